@@ -1,0 +1,189 @@
+"""Python binding of libkq (include/kq.h): block-quantized GEMM for MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+libkq.so; there is no CPU fallback.  If the library is missing the first call
+raises.  The kq_* functions mirror the C ABI one to one and accept torch
+tensors (their data_ptr() is passed) or plain integer addresses.  `stream`
+defaults to torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkq.so")
+
+KQ_Q4_K, KQ_Q6_K, KQ_TQ = 1, 2, 3
+KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
+KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS = 0, 1, 2
+KQ_OK = 0
+KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
+    -1, -2, -3, -4, -5, -6)
+
+# Every symbol include/kq.h declares, with its ctypes signature.
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "kq_weight_bytes": (_SZ, [_I, _I64, _I64]),
+    "kq_act_bytes": (_SZ, [_I, _I64, _I64]),
+    "kq_act_section_offset": (_I64, [_I, _I, _I64, _I64]),
+    "kq_act_fmt_for": (_I, [_I]),
+    "kq_quantize_act": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "kq_gemm": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "kq_gemm_subsums": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "kq_num_variants": (_I, []),
+    "kq_variant_name": (ctypes.c_char_p, [_I]),
+    "kq_dispatch_count": (ctypes.c_uint64, [_I]),
+    "kq_dispatch_reset": (None, []),
+    "kq_select_variant": (_I, [_I, _I64, _I64, _I64]),
+    "kq_strerror": (ctypes.c_char_p, [_I]),
+    "kq_version": (_I, []),
+}
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kq_strerror(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libkq.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> int:
+    if status != KQ_OK:
+        raise KQError(status, where)
+    return status
+
+
+# ---------------------------------------------------------------- C ABI mirror
+
+def kq_weight_bytes(fmt, N, K):
+    return lib().kq_weight_bytes(fmt, N, K)
+
+
+def kq_act_bytes(act_fmt, M, K):
+    return lib().kq_act_bytes(act_fmt, M, K)
+
+
+def kq_act_section_offset(act_fmt, section, M, K):
+    return lib().kq_act_section_offset(act_fmt, section, M, K)
+
+
+def kq_act_fmt_for(fmt):
+    return lib().kq_act_fmt_for(fmt)
+
+
+def kq_quantize_act(act_fmt, x, M, K, a_q8, stream=None):
+    return _check(lib().kq_quantize_act(act_fmt, _ptr(x), M, K, _ptr(a_q8), _stream(stream)),
+                  "kq_quantize_act")
+
+
+def kq_gemm(fmt, W, a_q8, M, N, K, out, stream=None):
+    return _check(lib().kq_gemm(fmt, _ptr(W), _ptr(a_q8), M, N, K, _ptr(out), _stream(stream)),
+                  "kq_gemm")
+
+
+def kq_gemm_subsums(fmt, W, a_q8, M, N, K, sums, stream=None):
+    return _check(lib().kq_gemm_subsums(fmt, _ptr(W), _ptr(a_q8), M, N, K, _ptr(sums),
+                                        _stream(stream)), "kq_gemm_subsums")
+
+
+def kq_num_variants():
+    return lib().kq_num_variants()
+
+
+def kq_variant_name(v):
+    s = lib().kq_variant_name(v)
+    return s.decode() if s else None
+
+
+def kq_dispatch_count(v):
+    return lib().kq_dispatch_count(v)
+
+
+def kq_dispatch_reset():
+    lib().kq_dispatch_reset()
+
+
+def kq_select_variant(fmt, M, N, K):
+    return lib().kq_select_variant(fmt, M, N, K)
+
+
+def kq_strerror(status):
+    return lib().kq_strerror(status).decode()
+
+
+def kq_version():
+    return lib().kq_version()
+
+
+# ------------------------------------------------- torch conveniences (allocation)
+
+def dispatch_counts() -> dict:
+    return {kq_variant_name(v): kq_dispatch_count(v) for v in range(kq_num_variants())}
+
+
+def quantize_act(x, act_fmt=KQ_ACT_Q8_K, stream=None):
+    """fp32 [M][K] device tensor -> uint8 device tensor holding the activation buffer."""
+    import torch
+    M, K = x.shape
+    a_q8 = torch.empty(kq_act_bytes(act_fmt, M, K), dtype=torch.uint8, device=x.device)
+    kq_quantize_act(act_fmt, x, M, K, a_q8, stream)
+    return a_q8
+
+
+def act_views(a_q8, act_fmt, M, K):
+    """(qs int8 [M][K], d fp32 [M][K/bs], bsums int16 [M][K/16] or None) views of a buffer."""
+    import torch
+    bs = 256 if act_fmt == KQ_ACT_Q8_K else 128
+    od = kq_act_section_offset(act_fmt, KQ_SEC_D, M, K)
+    qs = a_q8[:M * K].view(torch.int8).view(M, K)
+    d = a_q8[od:od + M * (K // bs) * 4].view(torch.float32).view(M, K // bs)
+    bsums = None
+    if act_fmt == KQ_ACT_Q8_K:
+        ob = kq_act_section_offset(act_fmt, KQ_SEC_BSUMS, M, K)
+        bsums = a_q8[ob:ob + M * (K // 16) * 2].view(torch.int16).view(M, K // 16)
+    return qs, d, bsums
+
+
+def gemm(fmt, W, a_q8, M, N, K, out=None, stream=None):
+    """out fp32 [M][N] = W x A (device tensors)."""
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_q8.device)
+    kq_gemm(fmt, W, a_q8, M, N, K, out, stream)
+    return out

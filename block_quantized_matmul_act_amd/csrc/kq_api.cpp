@@ -1,0 +1,215 @@
+// kq_api.cpp -- the C ABI of include/kq.h: host-side validation, size
+// queries, variant selection and launch.  Every argument check happens before
+// the first HIP call, so invalid calls return a status without touching the
+// runtime (and can be tested on a machine without a GPU).
+#include "../../include/kq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+namespace kq {
+hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_t *bsums,
+                            int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
+                       const int16_t *bsums, float *out, int M, int N, int K,
+                       hipStream_t stream);
+hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
+                          int K, hipStream_t stream);
+}  // namespace kq
+
+namespace {
+
+enum Variant {
+    V_QUANT_Q8K = 0,
+    V_QUANT_Q8_128,
+    V_GEMM_Q4K_128x128,
+    V_GEMM_Q6K_128x128,
+    V_GEMM_TQ_128x128,
+    V_SUBSUMS_Q4K,
+    V_SUBSUMS_Q6K,
+    V_SUBSUMS_TQ,
+    V_COUNT
+};
+
+const char *const kVariantNames[V_COUNT] = {
+    "quant_q8_k",        "quant_q8_128",      "gemm_q4_k_128x128", "gemm_q6_k_128x128",
+    "gemm_tq_128x128",   "subsums_q4_k",      "subsums_q6_k",      "subsums_tq",
+};
+
+std::atomic<uint64_t> g_count[V_COUNT];
+
+constexpr int64_t kMaxDim = INT32_MAX;  // kernels index rows and columns with int
+constexpr int64_t kMaxBytes = (int64_t)1 << 46;
+
+int qk_of(int fmt) {
+    return fmt == KQ_Q4_K || fmt == KQ_Q6_K ? 256 : fmt == KQ_TQ ? 128 : 0;
+}
+int bb_of(int fmt) {
+    return fmt == KQ_Q4_K ? 144 : fmt == KQ_Q6_K ? 210 : fmt == KQ_TQ ? 28 : 0;
+}
+int bs_of(int act_fmt) {
+    return act_fmt == KQ_ACT_Q8_K ? 256 : act_fmt == KQ_ACT_Q8_128 ? 128 : 0;
+}
+int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Section offsets of an activation buffer; false when invalid.
+bool act_layout(int act_fmt, int64_t M, int64_t K, int64_t *off_d, int64_t *off_bs,
+                int64_t *total) {
+    const int bs = bs_of(act_fmt);
+    if (!bs || M < 0 || K < 0 || K % bs || M > kMaxDim || K > kMaxDim) return false;
+    if (M != 0 && K > kMaxBytes / M) return false;
+    const int64_t qs_bytes = align256(M * K);
+    const int64_t d_bytes = align256(M * (K / bs) * 4);
+    *off_d = qs_bytes;
+    if (act_fmt == KQ_ACT_Q8_K) {
+        *off_bs = qs_bytes + d_bytes;
+        *total = *off_bs + align256(M * (K / 16) * 2);
+    } else {
+        *off_bs = -1;
+        *total = qs_bytes + d_bytes;
+    }
+    return true;
+}
+
+// Shared validation of kq_gemm / kq_gemm_subsums arguments.
+int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
+               const void *out) {
+    if (!qk_of(fmt)) return KQ_ERR_FMT;
+    if (M < 0 || N < 0 || K < 0 || K % qk_of(fmt)) return KQ_ERR_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return KQ_ERR_SHAPE;
+    if ((M && K > kMaxBytes / M) || (N && K > kMaxBytes / N) || (M && N > kMaxBytes / M))
+        return KQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return KQ_OK;
+    if (!W || !a_q8 || !out) return KQ_ERR_NULL;
+    if (!aligned16(W) || !aligned16(a_q8) || !aligned16(out)) return KQ_ERR_ALIGN;
+    // grid limits: tiles must fit a 1-D grid
+    const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
+    if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    return 1;  // proceed
+}
+
+int variant_for(int fmt) {
+    return fmt == KQ_Q4_K ? V_GEMM_Q4K_128x128 : fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128
+                                                                 : V_GEMM_TQ_128x128;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kq_weight_bytes(int fmt, int64_t N, int64_t K) {
+    const int qk = qk_of(fmt);
+    if (!qk || N < 0 || K < 0 || K % qk || N > kMaxDim || K > kMaxDim) return 0;
+    if (N && K > kMaxBytes / N) return 0;
+    return (size_t)(N * (K / qk) * bb_of(fmt));
+}
+
+size_t kq_act_bytes(int act_fmt, int64_t M, int64_t K) {
+    int64_t od, ob, total;
+    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return 0;
+    return (size_t)total;
+}
+
+int64_t kq_act_section_offset(int act_fmt, int section, int64_t M, int64_t K) {
+    int64_t od, ob, total;
+    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return -1;
+    if (section == KQ_SEC_QS) return 0;
+    if (section == KQ_SEC_D) return od;
+    if (section == KQ_SEC_BSUMS) return ob;
+    return -1;
+}
+
+int kq_act_fmt_for(int fmt) {
+    if (fmt == KQ_Q4_K || fmt == KQ_Q6_K) return KQ_ACT_Q8_K;
+    if (fmt == KQ_TQ) return KQ_ACT_Q8_128;
+    return KQ_ERR_FMT;
+}
+
+int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q8,
+                    hipStream_t stream) {
+    const int bs = bs_of(act_fmt);
+    if (!bs) return KQ_ERR_FMT;
+    int64_t od, ob, total;
+    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return KQ_ERR_SHAPE;
+    if (M == 0 || K == 0) return KQ_OK;
+    if (!x || !a_q8) return KQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(a_q8)) return KQ_ERR_ALIGN;
+    if ((M * (K / bs) * (bs / 4) + 255) / 256 > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    char *base = static_cast<char *>(a_q8);
+    hipError_t e = kq::launch_quant_act(bs, x, reinterpret_cast<int8_t *>(base),
+                                        reinterpret_cast<float *>(base + od),
+                                        ob >= 0 ? reinterpret_cast<int16_t *>(base + ob) : nullptr,
+                                        M, K, stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    g_count[act_fmt == KQ_ACT_Q8_K ? V_QUANT_Q8K : V_QUANT_Q8_128].fetch_add(1);
+    return KQ_OK;
+}
+
+int kq_select_variant(int fmt, int64_t M, int64_t N, int64_t K) {
+    if (!qk_of(fmt)) return KQ_ERR_FMT;
+    if (M < 0 || N < 0 || K < 0 || K % qk_of(fmt)) return KQ_ERR_SHAPE;
+    return variant_for(fmt);
+}
+
+int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
+            float *out, hipStream_t stream) {
+    int rc = check_gemm(fmt, W, a_q8, M, N, K, out);
+    if (rc <= 0) return rc;
+    int64_t od, ob, total;
+    act_layout(kq_act_fmt_for(fmt), M, K, &od, &ob, &total);
+    const char *base = static_cast<const char *>(a_q8);
+    hipError_t e = kq::launch_gemm(fmt, W, reinterpret_cast<const int8_t *>(base),
+                                   reinterpret_cast<const float *>(base + od),
+                                   ob >= 0 ? reinterpret_cast<const int16_t *>(base + ob) : nullptr,
+                                   out, (int)M, (int)N, (int)K, stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    g_count[variant_for(fmt)].fetch_add(1);
+    return KQ_OK;
+}
+
+int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
+                    int32_t *sums, hipStream_t stream) {
+    int rc = check_gemm(fmt, W, a_q8, M, N, K, sums);
+    if (rc <= 0) return rc;
+    const char *base = static_cast<const char *>(a_q8);
+    hipError_t e = kq::launch_subsums(fmt, W, reinterpret_cast<const int8_t *>(base), sums,
+                                      (int)M, (int)N, (int)K, stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    g_count[fmt == KQ_Q4_K ? V_SUBSUMS_Q4K : fmt == KQ_Q6_K ? V_SUBSUMS_Q6K : V_SUBSUMS_TQ]
+        .fetch_add(1);
+    return KQ_OK;
+}
+
+int kq_num_variants(void) { return V_COUNT; }
+
+const char *kq_variant_name(int variant) {
+    return (variant >= 0 && variant < V_COUNT) ? kVariantNames[variant] : nullptr;
+}
+
+uint64_t kq_dispatch_count(int variant) {
+    return (variant >= 0 && variant < V_COUNT) ? g_count[variant].load() : 0;
+}
+
+void kq_dispatch_reset(void) {
+    for (auto &c : g_count) c.store(0);
+}
+
+const char *kq_strerror(int status) {
+    switch (status) {
+        case KQ_OK: return "ok";
+        case KQ_ERR_FMT: return "unknown weight or activation format";
+        case KQ_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of the block, or size overflow)";
+        case KQ_ERR_NULL: return "null pointer with nonzero work";
+        case KQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case KQ_ERR_UNSUPPORTED: return "no verified kernel variant for this case";
+        case KQ_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int kq_version(void) { return KQ_VERSION; }
+
+}  // extern "C"

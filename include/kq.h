@@ -1,0 +1,169 @@
+/*
+ * kq.h -- C ABI of the block-quantized weight x quantized-activation GEMM
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The path (vllm.cpp PR 3036 "cooperative-tile WMMA kernels -- Shared
+ * rejected, BigTile accepted": activation-quant scratch, then a tile GEMM over
+ * Q4_K/Q6_K weights and BlockQ8_K activations; PrismML llama.cpp PR 214
+ * "branch-free PTQ1_0 MMQ tile loader": the ternary MMQ path):
+ *
+ *   1. kq_quantize_act: fp32 activations -> int8 blocks with an fp32 scale
+ *      (Q8_K: 256 per block plus int16 sums per 16; Q8_128: 128 per block).
+ *   2. kq_gemm: out[m][n] = sum_k W^[n][k] * A^[m][k], where W^ is the
+ *      dequantized stored weight and A^[m][k] = d[m][block] * qs[m][k].
+ *      The contraction runs on int8 matrix cores; block scales and mins are
+ *      folded in afterwards.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument is a DEVICE pointer except where noted.  The
+ *     caller allocates and frees all memory; the library allocates nothing,
+ *     keeps no handles and needs no scratch.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream).  Device faults surface at the caller's next synchronization.
+ *   - Arguments are validated on the host before any HIP call.  On any error
+ *     nothing is launched and a negative KQ_ERR_* code is returned; a shape
+ *     with no verified kernel variant is declined with KQ_ERR_UNSUPPORTED
+ *     rather than computed wrongly.  M == 0 or N == 0 returns KQ_OK with no
+ *     launch.
+ *   - Output buffers must not overlap inputs.  Calls are thread-safe; the only
+ *     global state is a set of atomic per-variant dispatch counters.
+ *
+ * Data layouts (this library's own; the pages fix only the block sizes:
+ * 292 bytes per 256 activations for BlockQ8_K in vllm.cpp PR 3036, a 28-byte
+ * block per 128 ternary weights in llama.cpp PR 214):
+ *
+ *   Q8_K activations (KQ_ACT_Q8_K), one buffer of kq_act_bytes() bytes with
+ *   three sections, each at a 256-byte-aligned offset from the start:
+ *     qs    int8  [M][K]        quantized values
+ *     d     fp32  [M][K/256]    block scales
+ *     bsums int16 [M][K/16]     sums of qs over each 16 consecutive values
+ *   Q8_128 activations (KQ_ACT_Q8_128): sections qs int8 [M][K] and
+ *   d fp32 [M][K/128]; no bsums.
+ *   Quantization rule per block, in fp32: amax = max|x|; if amax == 0 or
+ *   127/amax is not finite then d = 0 and qs = 0; otherwise d = amax/127,
+ *   s = 127/amax, qs = clamp(rint(x*s), -127, 127) (round half to even, one
+ *   fp32 multiply).  Inputs must be finite.
+ *
+ *   Weights W: row n (output feature) is K/QK consecutive blocks, rows are
+ *   consecutive, so W is [N][K/QK] blocks.
+ *   KQ_Q4_K, 144 bytes per 256 weights (8 sub-blocks of 32):
+ *     [0,2) fp16 d; [2,4) fp16 dmin; [4,16) a little-endian 96-bit integer
+ *     whose bits [6f, 6f+6) hold field f: f < 8 scale sc_f, f >= 8 min m_(f-8);
+ *     [16,144) byte 32c+t (c < 4, t < 32) holds weight 64c+t in its low nibble
+ *     and weight 64c+32+t in its high nibble.
+ *     W^_k = d * sc_j * q_k - dmin * m_j, j = k/32.
+ *   KQ_Q6_K, 210 bytes per 256 weights (16 sub-blocks of 16):
+ *     [0,128) byte 64h+t (h < 2, t < 64): low 4 bits of weight 128h+t (bits
+ *     0..3) and of weight 128h+64+t (bits 4..7); [128,192) bits 2u..2u+1 of
+ *     byte 128+32h+t (t < 32, u < 4) are the high 2 bits of weight
+ *     128h+32u+t; [192,208) int8 scales; [208,210) fp16 d.
+ *     W^_k = d * sc_j * (q_k - 32), j = k/16.
+ *   KQ_TQ (ternary), 28 bytes per 128 weights:
+ *     [0,26) weight k is base-3 digit t_k+1 at position k mod 5 of byte k/5
+ *     (least significant digit first; the two spare digits of byte 25 must
+ *     be 1, so every byte is <= 242); [26,28) fp16 d.  W^_k = d * t_k.
+ *     Bytes 24..27 read as a little-endian word are qh0 | qh1<<8 | d<<16,
+ *     the word layout of llama.cpp PR 214's loader.
+ *   Q4_K and Q6_K weights take Q8_K activations; ternary takes Q8_128.
+ *
+ *   out: fp32 [M][N] row-major, fully overwritten (never accumulated).
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KQ_VERSION 1
+
+/* weight formats */
+#define KQ_Q4_K 1
+#define KQ_Q6_K 2
+#define KQ_TQ 3
+
+/* activation formats */
+#define KQ_ACT_Q8_K 1
+#define KQ_ACT_Q8_128 2
+
+/* activation buffer sections */
+#define KQ_SEC_QS 0
+#define KQ_SEC_D 1
+#define KQ_SEC_BSUMS 2
+
+/* status codes */
+#define KQ_OK 0
+#define KQ_ERR_FMT (-1)         /* unknown format */
+#define KQ_ERR_SHAPE (-2)       /* negative size, K not a multiple of the block, size overflow */
+#define KQ_ERR_NULL (-3)        /* NULL pointer with nonzero work */
+#define KQ_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define KQ_ERR_UNSUPPORTED (-5) /* no verified kernel variant for this case */
+#define KQ_ERR_HIP (-6)         /* the HIP runtime reported an error at launch */
+
+/* Size queries.  Return 0 for invalid arguments. */
+size_t kq_weight_bytes(int fmt, int64_t N, int64_t K);
+size_t kq_act_bytes(int act_fmt, int64_t M, int64_t K);
+/* Byte offset of a section (KQ_SEC_*) inside an activation buffer; -1 when the
+ * section does not exist for this format or the arguments are invalid. */
+int64_t kq_act_section_offset(int act_fmt, int section, int64_t M, int64_t K);
+/* The activation format a weight format consumes; KQ_ERR_FMT if unknown. */
+int kq_act_fmt_for(int fmt);
+
+/*
+ * Quantize fp32 activations x [M][K] (device, row-major, contiguous, 16-byte
+ * aligned) into a_q8 (device, kq_act_bytes(act_fmt, M, K) bytes, 16-byte
+ * aligned) in the layout above.  K must be a multiple of 256 (Q8_K) or 128
+ * (Q8_128).  Defined by the activation-quant step of vllm.cpp PR 3036
+ * (EnsureQuantScratch filling qact with BlockQ8_K rows; no padding rows).
+ */
+int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q8,
+                    hipStream_t stream);
+
+/*
+ * out [M][N] = product of the quantized activations a_q8 (from
+ * kq_quantize_act with kq_act_fmt_for(fmt); exactly M rows, no padding) and
+ * the stored weights W [N][K/QK blocks].  K must be a multiple of 256 (Q4_K,
+ * Q6_K) or 128 (ternary).  All pointers device, 16-byte aligned.  Defined by
+ * the tile GEMM of vllm.cpp PR 3036 (per-sub-block int8 dot products with the
+ * Q4_K/Q6_K scales and mins folded in) and the PTQ1_0 MMQ path of llama.cpp
+ * PR 214.  The fp32 result agrees with the exact product of the dequantized
+ * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.
+ */
+int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
+            float *out, hipStream_t stream);
+
+/*
+ * Test hook: per-sub-block integer dot sums through the same weight loaders
+ * and int8 matrix-core code as kq_gemm, with the scale fold disabled.
+ * sums (device, int32 [M][N][K/SB]) receives
+ *   S[m][n][j] = sum_{k in sub-block j} qint[n][k] * qs[m][k]
+ * with SB = 32 and qint = q (Q4_K), SB = 16 and qint = q - 32 (Q6_K),
+ * SB = 128 and qint = t (ternary).
+ */
+int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N,
+                    int64_t K, int32_t *sums, hipStream_t stream);
+
+/* Per-variant dispatch counters (incremented on each successful launch) and
+ * their names, so tests can prove which kernel variant ran (vllm.cpp PR 3036
+ * added such counters after finding tests that never reached a variant). */
+int kq_num_variants(void);
+const char *kq_variant_name(int variant);
+uint64_t kq_dispatch_count(int variant);
+void kq_dispatch_reset(void);
+
+/* The variant kq_gemm would launch for this case, or a negative KQ_ERR_*. */
+int kq_select_variant(int fmt, int64_t M, int64_t N, int64_t K);
+
+const char *kq_strerror(int status);
+int kq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

@@ -1,0 +1,150 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and rejects invalid arguments with its status codes before any HIP
+call (so they run without a GPU)."""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import block_quantized_matmul_act_amd as kq
+    if not os.path.exists(kq.LIB_PATH):
+        from block_quantized_matmul_act_amd import build
+        build.build()
+    kq.lib()
+    return kq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kq_quantize_act", "kq_gemm", "kq_weight_bytes", "kq_act_bytes",
+                     "kq_gemm_subsums", "kq_dispatch_count", "kq_strerror", "kq_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(kq):
+    L = kq.lib()
+    names = declared_functions()
+    assert set(names) == set(kq.SIGNATURES), "binding and header disagree"
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_strings(kq):
+    assert kq.kq_version() == 1
+    for st in (kq.KQ_OK, kq.KQ_ERR_FMT, kq.KQ_ERR_SHAPE, kq.KQ_ERR_NULL, kq.KQ_ERR_ALIGN,
+               kq.KQ_ERR_UNSUPPORTED, kq.KQ_ERR_HIP):
+        s = kq.kq_strerror(st)
+        assert s and s != "unknown status"
+    assert kq.kq_strerror(12345) == "unknown status"
+
+
+def _a256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (8, 512), (7, 768), (513, 4096), (0, 256)])
+def test_act_layout_q8k(kq, M, K):
+    # three sections at 256-byte-aligned offsets: qs [M][K], d [M][K/256], bsums [M][K/16]
+    off_d = _a256(M * K)
+    off_b = off_d + _a256(M * (K // 256) * 4)
+    total = off_b + _a256(M * (K // 16) * 2)
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_QS, M, K) == 0
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_D, M, K) == off_d
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_BSUMS, M, K) == off_b
+    assert kq.kq_act_bytes(kq.KQ_ACT_Q8_K, M, K) == total
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (9, 384), (2048, 5120)])
+def test_act_layout_q8_128(kq, M, K):
+    off_d = _a256(M * K)
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_128, kq.KQ_SEC_D, M, K) == off_d
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_128, kq.KQ_SEC_BSUMS, M, K) == -1
+    assert kq.kq_act_bytes(kq.KQ_ACT_Q8_128, M, K) == off_d + _a256(M * (K // 128) * 4)
+
+
+def test_size_queries(kq):
+    assert kq.kq_weight_bytes(kq.KQ_Q4_K, 14336, 4096) == 14336 * 16 * 144 == 33030144
+    assert kq.kq_weight_bytes(kq.KQ_Q6_K, 4096, 14336) == 4096 * 56 * 210 == 48168960
+    assert kq.kq_weight_bytes(kq.KQ_TQ, 17408, 5120) == 17408 * 40 * 28 == 19496960
+    assert kq.kq_weight_bytes(kq.KQ_Q4_K, 10, 100) == 0          # K not a multiple of 256
+    assert kq.kq_weight_bytes(kq.KQ_TQ, 10, 384) == 10 * 3 * 28
+    assert kq.kq_weight_bytes(99, 10, 256) == 0
+    assert kq.kq_weight_bytes(kq.KQ_Q4_K, -1, 256) == 0
+    assert kq.kq_act_bytes(kq.KQ_ACT_Q8_K, 4, 128) == 0           # K not a multiple of 256
+    assert kq.kq_act_bytes(7, 4, 256) == 0
+    assert kq.kq_act_fmt_for(kq.KQ_Q4_K) == kq.KQ_ACT_Q8_K
+    assert kq.kq_act_fmt_for(kq.KQ_Q6_K) == kq.KQ_ACT_Q8_K
+    assert kq.kq_act_fmt_for(kq.KQ_TQ) == kq.KQ_ACT_Q8_128
+    assert kq.kq_act_fmt_for(0) == kq.KQ_ERR_FMT
+
+
+def _raw(kq):
+    return kq.lib()
+
+
+def test_gemm_validation_without_hip(kq):
+    L = _raw(kq)
+    A = 1 << 20   # a fake, aligned "device address": never dereferenced on these paths
+    s = None
+    assert L.kq_gemm(0, A, A, 8, 8, 256, A, s) == kq.KQ_ERR_FMT
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 300, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_TQ, A, A, 8, 8, 200, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, -1, 8, 256, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, -3, 256, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, -256, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 1 << 33, 8, 256, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 1 << 30, 1 << 30, 1 << 20, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm(kq.KQ_Q4_K, None, A, 8, 8, 256, A, s) == kq.KQ_ERR_NULL
+    assert L.kq_gemm(kq.KQ_Q4_K, A, None, 8, 8, 256, A, s) == kq.KQ_ERR_NULL
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 256, None, s) == kq.KQ_ERR_NULL
+    assert L.kq_gemm(kq.KQ_Q4_K, A + 4, A, 8, 8, 256, A, s) == kq.KQ_ERR_ALIGN
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A + 8, 8, 8, 256, A, s) == kq.KQ_ERR_ALIGN
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 256, A + 2, s) == kq.KQ_ERR_ALIGN
+    # empty problems are a no-op that succeeds, even with null pointers
+    assert L.kq_gemm(kq.KQ_Q4_K, None, None, 0, 8, 256, None, s) == kq.KQ_OK
+    assert L.kq_gemm(kq.KQ_Q6_K, None, None, 8, 0, 256, None, s) == kq.KQ_OK
+    assert L.kq_gemm_subsums(kq.KQ_TQ, None, None, 0, 0, 128, None, s) == kq.KQ_OK
+    assert L.kq_gemm_subsums(kq.KQ_TQ, A, A, 4, 4, 100, A, s) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemm_subsums(9, A, A, 4, 4, 128, A, s) == kq.KQ_ERR_FMT
+
+
+def test_quantize_validation_without_hip(kq):
+    L = _raw(kq)
+    A = 1 << 20
+    assert L.kq_quantize_act(3, A, 4, 256, A, None) == kq.KQ_ERR_FMT
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, A, 4, 128, A, None) == kq.KQ_ERR_SHAPE
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_128, A, 4, 64, A, None) == kq.KQ_ERR_SHAPE
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, A, -4, 256, A, None) == kq.KQ_ERR_SHAPE
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, None, 4, 256, A, None) == kq.KQ_ERR_NULL
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, A, 4, 256, None, None) == kq.KQ_ERR_NULL
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, A + 4, 4, 256, A, None) == kq.KQ_ERR_ALIGN
+    assert L.kq_quantize_act(kq.KQ_ACT_Q8_K, None, 0, 256, None, None) == kq.KQ_OK
+
+
+def test_variants_and_counters(kq):
+    n = kq.kq_num_variants()
+    names = [kq.kq_variant_name(v) for v in range(n)]
+    assert len(set(names)) == n and all(names)
+    assert kq.kq_variant_name(n) is None and kq.kq_variant_name(-1) is None
+    kq.kq_dispatch_reset()
+    assert all(kq.kq_dispatch_count(v) == 0 for v in range(n))
+    for fmt in (kq.KQ_Q4_K, kq.KQ_Q6_K, kq.KQ_TQ):
+        for M in (1, 8, 64, 65, 2048):
+            v = kq.kq_select_variant(fmt, M, 4096, 4096 if fmt != kq.KQ_TQ else 5120)
+            assert 0 <= v < n
+    assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT
+    assert kq.kq_select_variant(kq.KQ_Q4_K, 1, 1, 100) == kq.KQ_ERR_SHAPE

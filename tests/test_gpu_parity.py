@@ -1,0 +1,370 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integers are compared bit for bit (quantized activations, their scales and
+sums, per-sub-block dot sums); fp32 outputs must satisfy
+|out - ref| <= 1e-4 * sum_k |W^ A^| + 1e-6 on every element checked.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import datagen
+from oracle import kqref
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+Q4_K, Q6_K, TQ = 1, 2, 3
+FMTS = (Q4_K, Q6_K, TQ)
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
+SUB = {Q4_K: 32, Q6_K: 16, TQ: 128}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def kq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_matmul_act_amd as kq
+    kq.lib()
+    return kq
+
+
+DEV = "cuda:0"
+
+
+def dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_quant(kq, act_fmt, x):
+    M, K = x.shape
+    a_q8 = kq.quantize_act(dev(x), act_fmt)
+    torch.cuda.synchronize()
+    return a_q8
+
+
+def check_act_exact(kq, act_fmt, x, a_q8):
+    M, K = x.shape
+    qs, d, bs = kqref.quantize_act(act_fmt, x)
+    gq, gd, gb = kq.act_views(a_q8, act_fmt, M, K)
+    assert np.array_equal(gq.cpu().numpy(), qs)
+    assert np.array_equal(gd.cpu().numpy().view(np.uint32), d.view(np.uint32))
+    if bs is not None:
+        assert np.array_equal(gb.cpu().numpy(), bs)
+    return qs, d, bs
+
+
+def run_gemm(kq, fmt, W, a_q8, M, N, K):
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    kq.kq_gemm(fmt, dev(W) if isinstance(W, np.ndarray) else W, a_q8, M, N, K, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_within_tol(out, ref, tol, what):
+    assert np.all(np.isfinite(out)), what + ": non-finite output"
+    err = np.abs(out.astype(np.float64) - ref.astype(np.float64))
+    ratio = err / tol
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert np.all(err <= tol), f"{what}: max err/tol {ratio.max():.3g} at {worst}"
+    return float(ratio.max())
+
+
+# ---------------------------------------------------------------- activations
+
+@pytest.mark.parametrize("act_fmt,M,K", [(1, 8, 512), (1, 37, 4096), (1, 3, 14336),
+                                         (2, 5, 5120), (2, 64, 384)])
+def test_quantize_bit_exact(kq, act_fmt, M, K):
+    say(f"quantize act_fmt={act_fmt} M={M} K={K}")
+    x = datagen.draw_activations(M, K, 1000 + K, "outlier_lognormal" if M % 2 else "plain")
+    a_q8 = run_quant(kq, act_fmt, x)
+    check_act_exact(kq, act_fmt, x, a_q8)
+
+
+def test_quantize_special_blocks(kq):
+    say("quantize special blocks")
+    K = 1024
+    x = np.random.default_rng(3).standard_normal((6, K)).astype(np.float32)
+    x[0] = 0.0                                         # all-zero row
+    x[1, :256] = np.float32(1e-45)                     # subnormal amax: zero block
+    x[2, :256] = 0.0
+    x[2, 0] = 127.0
+    x[2, 1:8] = [0.5, 1.5, 2.5, -2.5, 126.5, -0.5, 3.5]   # ties
+    x[3] *= np.float32(2.0 ** 60)                      # large but finite
+    x[4] *= np.float32(2.0 ** -60)                     # tiny but normal
+    x[5, 256:512] = -x[5, 256:512]
+    for act_fmt in (1, 2):
+        a_q8 = run_quant(kq, act_fmt, x)
+        check_act_exact(kq, act_fmt, x, a_q8)
+
+
+# ---------------------------------------------------------------- sub-sums
+
+def run_subsums(kq, fmt, W, a_q8, M, N, K):
+    S = torch.full((M, N, K // SUB[fmt]), -7, dtype=torch.int32, device=DEV)
+    kq.kq_gemm_subsums(fmt, dev(W), a_q8, M, N, K, S)
+    torch.cuda.synchronize()
+    return S.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(Q4_K, 8, 256, 512), (Q4_K, 33, 70, 768),
+                                       (Q6_K, 8, 96, 512), (Q6_K, 40, 33, 256),
+                                       (TQ, 8, 64, 384), (TQ, 35, 50, 640)])
+def test_subsums_bit_exact(kq, fmt, M, N, K):
+    say(f"subsums fmt={fmt} M={M} N={N} K={K}")
+    W = datagen.make_weights(fmt, N, K, 1001)
+    x = datagen.draw_activations(M, K, 1001)
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    a_q8 = run_quant(kq, act_fmt, x)
+    qs, d, bs = check_act_exact(kq, act_fmt, x, a_q8)
+    S = run_subsums(kq, fmt, W, a_q8, M, N, K)
+    assert np.array_equal(S, kqref.subsums(fmt, W, qs, K))
+
+
+@pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_2048", "ffn_down_q6k_2048",
+                                  "tern_5120_2048"])
+def test_subsums_workload_slices(kq, workloads, name):
+    """First 64 tokens x 256 rows x all K of each large workload."""
+    say(f"subsums slice {name}")
+    wl = datagen.WORKLOADS[name]
+    W, x = workloads(name)
+    W = np.ascontiguousarray(W[:256])
+    x = np.ascontiguousarray(x[:64])
+    act_fmt = kq.kq_act_fmt_for(wl.fmt)
+    a_q8 = run_quant(kq, act_fmt, x)
+    qs, _, _ = check_act_exact(kq, act_fmt, x, a_q8)
+    S = run_subsums(kq, wl.fmt, W, a_q8, 64, 256, wl.K)
+    assert np.array_equal(S, kqref.subsums(wl.fmt, W, qs, wl.K))
+
+
+# ---------------------------------------------------------------- GEMM parity
+
+@pytest.fixture(scope="module")
+def workloads():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            say(f"generating {name}")
+            cache[name] = datagen.make_workload(name)
+        return cache[name]
+    return get
+
+
+def gemm_vs_oracle(kq, fmt, W, x, M, N, K, rows=None, what=""):
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    a_q8 = run_quant(kq, act_fmt, x)
+    qs, d, _ = check_act_exact(kq, act_fmt, x, a_q8)
+    out = run_gemm(kq, fmt, W, a_q8, M, N, K)
+    ref, tol = kqref.gemm(fmt, W, qs, d, K, rows=rows)
+    got = out if rows is None else out[:, rows]
+    return assert_within_tol(got, ref, tol, what or f"fmt={fmt} M={M} N={N} K={K}")
+
+
+def test_tiny_workload_full(kq, workloads):
+    say("gemm tiny_q4k full")
+    wl = datagen.WORKLOADS["tiny_q4k"]
+    W, x = workloads("tiny_q4k")
+    gemm_vs_oracle(kq, wl.fmt, W, x, wl.M, wl.N, wl.K)
+
+
+SWEEP_M = (1, 7, 8, 63, 64, 65, 80, 128, 129, 300)
+SWEEP_N = (48, 128, 200, 256)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_shape_sweep(kq, fmt):
+    Ks = (256, 512, 768) if fmt != TQ else (128, 384, 640)
+    rng = np.random.default_rng(fmt)
+    for K in Ks:
+        Wfull = datagen.make_weights(fmt, max(SWEEP_N), K, 2000 + K)
+        xfull = datagen.draw_activations(max(SWEEP_M), K, 3000 + K)
+        for M in SWEEP_M:
+            for N in SWEEP_N:
+                if rng.random() < 0.5 and not (M in (1, 65) or N == 200):
+                    continue
+                say(f"sweep fmt={fmt} M={M} N={N} K={K}")
+                gemm_vs_oracle(kq, fmt, np.ascontiguousarray(Wfull[:N]),
+                               np.ascontiguousarray(xfull[:M]), M, N, K)
+
+
+@pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_64", "ffn_up_q4k_2048",
+                                  "ffn_down_q6k_2048", "tern_5120_2048"])
+def test_workload_full_size_sampled(kq, workloads, name):
+    """Full-size problem in the benchmarked launch; the oracle checks a sample
+    of output rows (all tokens) spread over every tile position."""
+    wl = datagen.WORKLOADS[name]
+    W, x = workloads(name)
+    rng = np.random.default_rng(77)
+    nrows = 48
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, wl.N - 1],
+                                     rng.choice(wl.N, nrows, replace=False)]))
+    say(f"gemm full-size {name} (M={wl.M} N={wl.N} K={wl.K}), {len(rows)} sampled rows")
+    r = gemm_vs_oracle(kq, wl.fmt, W, x, wl.M, wl.N, wl.K, rows=rows, what=name)
+    say(f"  max err/tol {r:.3g}")
+
+
+def test_other_reading_of_distributions(kq):
+    """Config text 'same value distributions as config 1' read 0-based: outlier
+    weights and LogNormal channel scales on the FFN shape (sliced)."""
+    say("gemm ffn shape under the outlier/LogNormal distributions")
+    M, N, K = 256, 512, 4096
+    W = datagen.make_weights(Q4_K, N, K, 1003, "outlier_lognormal")
+    x = datagen.draw_activations(M, K, 1003, "outlier_lognormal")
+    gemm_vs_oracle(kq, Q4_K, W, x, M, N, K)
+    W6 = datagen.make_weights(Q6_K, 256, 2048, 1004, "outlier_lognormal")
+    x6 = datagen.draw_activations(200, 2048, 1004, "outlier_lognormal")
+    gemm_vs_oracle(kq, Q6_K, W6, x6, 200, 256, 2048)
+
+
+# ------------------------------------------------- exact special cases of the real kernel
+
+def hand_act_q8k(kq, qs):
+    """Q8_K buffer with unit scales and consistent sums, built on the host."""
+    M, K = qs.shape
+    buf = np.zeros(kq.kq_act_bytes(1, M, K), np.uint8)
+    od = kq.kq_act_section_offset(1, 1, M, K)
+    ob = kq.kq_act_section_offset(1, 2, M, K)
+    buf[:M * K] = qs.view(np.uint8).reshape(-1)
+    buf[od:od + M * (K // 256) * 4] = np.ones((M, K // 256), np.float32).view(np.uint8).reshape(-1)
+    bs = qs.astype(np.int32).reshape(M, K // 16, 16).sum(axis=2).astype(np.int16)
+    buf[ob:ob + M * (K // 16) * 2] = bs.view(np.uint8).reshape(-1)
+    return dev(buf)
+
+
+def hand_act_q8_128(kq, qs):
+    M, K = qs.shape
+    buf = np.zeros(kq.kq_act_bytes(2, M, K), np.uint8)
+    od = kq.kq_act_section_offset(2, 1, M, K)
+    buf[:M * K] = qs.view(np.uint8).reshape(-1)
+    buf[od:od + M * (K // 128) * 4] = np.ones((M, K // 128), np.float32).view(np.uint8).reshape(-1)
+    return dev(buf)
+
+
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K))
+def test_onehot_scales_expose_subsums(kq, fmt):
+    """d = d_a = 1, no mins, scale vector e_j: the production kernel's output is
+    exactly the sub-block sum S[:, :, j]."""
+    rng = np.random.default_rng(31 + fmt)
+    M, N, K = 70, 96, 512
+    qs = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    a_q8 = hand_act_q8k(kq, qs)
+    nsub = 8 if fmt == Q4_K else 16
+    for j in range(nsub):
+        say(f"one-hot fmt={fmt} j={j}")
+        B = N * (K // 256)
+        one = np.zeros((B, nsub), np.int64)
+        one[:, j] = 1
+        if fmt == Q4_K:
+            q = rng.integers(0, 16, size=(B, 256))
+            mn = rng.integers(0, 64, size=(B, 8))
+            W = datagen.pack_q4k(np.ones(B, np.float16), np.zeros(B, np.float16), one, mn, q)
+        else:
+            q = rng.integers(0, 64, size=(B, 256))
+            W = datagen.pack_q6k(np.ones(B, np.float16), one, q)
+        W = W.reshape(N, -1)
+        out = run_gemm(kq, fmt, W, a_q8, M, N, K)
+        S = kqref.subsums(fmt, W, qs, K)
+        want = np.stack([S[:, :, j + nsub * s] for s in range(K // 256)]).sum(axis=0)
+        assert np.array_equal(out, want.astype(np.float32)), f"one-hot j={j}"
+
+
+def test_unit_scale_ternary_is_integer_matmul(kq):
+    say("ternary unit scales")
+    rng = np.random.default_rng(41)
+    M, N, K = 67, 90, 640
+    qs = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(N, K))
+    W = datagen.encode_tq(t.astype(np.int8), np.ones((N, K // 128), np.float16))
+    out = run_gemm(kq, TQ, W, hand_act_q8_128(kq, qs), M, N, K)
+    want = qs.astype(np.int64) @ t.astype(np.int64).T
+    assert np.array_equal(out, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_and_negated_activations(kq, fmt):
+    say(f"x=0 and x->-x fmt={fmt}")
+    M, N, K = 96, 160, 768 if fmt != TQ else 640
+    W = datagen.make_weights(fmt, N, K, 55)
+    x = datagen.draw_activations(M, K, 56)
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    out = run_gemm(kq, fmt, W, run_quant(kq, act_fmt, x), M, N, K)
+    neg = run_gemm(kq, fmt, W, run_quant(kq, act_fmt, -x), M, N, K)
+    if fmt == Q4_K:
+        # The Q4_K min term goes through a bf16 MFMA whose internal fp32
+        # accumulation is not exactly sign-symmetric (measured: differences of
+        # about one ulp of the partial sums); everything else negates exactly.
+        qs, d, _ = kqref.quantize_act(act_fmt, x)
+        _, tol = kqref.gemm(fmt, W, qs, d, K)
+        assert np.all(np.abs(neg.astype(np.float64) + out) <= 0.01 * tol)
+    else:
+        assert np.array_equal(neg, -out)
+    zero = run_gemm(kq, fmt, W, run_quant(kq, act_fmt, np.zeros_like(x)), M, N, K)
+    assert np.all(zero == 0)
+
+
+# ------------------------------------------------- out-of-bounds canaries
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_canaries_and_poisoned_tails(kq, fmt):
+    """Inputs end at the last valid byte of larger buffers whose tails hold
+    garbage; the output is a view followed by NaN canaries.  Results must equal
+    the clean run and the canaries must be untouched."""
+    say(f"canaries fmt={fmt}")
+    M, N, K = 77, 131, 512 if fmt != TQ else 384
+    W = datagen.make_weights(fmt, N, K, 91)
+    x = datagen.draw_activations(M, K, 92)
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    a_clean = run_quant(kq, act_fmt, x)
+    ref = run_gemm(kq, fmt, W, a_clean, M, N, K)
+
+    pad = 4096
+    wb = np.full(W.nbytes + pad, 0xFF, np.uint8)
+    wb[:W.nbytes] = W.reshape(-1)
+    Wd = dev(wb)
+    ab = torch.full((a_clean.numel() + pad,), 0x7F, dtype=torch.uint8, device=DEV)
+    ab[:a_clean.numel()] = a_clean
+    ob = torch.full((M * N + pad,), float("nan"), dtype=torch.float32, device=DEV)
+    ob[M * N:] = 12345.0
+    kq.kq_gemm(fmt, Wd, ab, M, N, K, ob)
+    torch.cuda.synchronize()
+    got = ob[:M * N].cpu().numpy().reshape(M, N)
+    assert np.array_equal(got, ref)
+    assert torch.all(ob[M * N:] == 12345.0).item()
+
+
+def test_empty_problems_are_noops(kq):
+    say("empty problems")
+    out = torch.full((4, 4), 7.0, device=DEV)
+    a = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    kq.kq_gemm(Q4_K, a, a, 0, 4, 256, out)
+    kq.kq_gemm(Q4_K, a, a, 4, 0, 256, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0).item()
+
+
+def test_zero_k_gives_zero(kq):
+    say("K = 0")
+    out = torch.full((5, 6), 7.0, device=DEV)
+    a = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    for fmt in FMTS:
+        out.fill_(7.0)
+        kq.kq_gemm(fmt, a, a, 5, 6, 0, out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0.0).item()
+
+
+def test_zz_every_variant_dispatched(kq):
+    """Runs last in this file: every kernel variant in the table was launched by
+    the tests above (the counters prove which kernel ran)."""
+    counts = kq.dispatch_counts()
+    say(f"dispatch counts: {counts}")
+    missing = [name for name, c in counts.items() if c == 0]
+    assert not missing, f"variants never dispatched: {missing}"
