@@ -32,6 +32,8 @@
 //     a weight tile is fetched from HBM once per XCD L2.
 #include "kq_device.hpp"
 
+#include <type_traits>
+
 namespace kq {
 
 enum { FMT_Q4K = 1, FMT_Q6K = 2, FMT_TQ = 3 };
@@ -285,250 +287,421 @@ __device__ __forceinline__ v4i load_act_piece(const GemmArgs &a, int m, int c, i
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel
+// Main kernel.
+//
+// Workgroup: 512 threads (8 waves, two per SIMD), output tile 128 x 128.
+// Wave w computes rows 64*(w/4) .. +64 and columns 32*(w%4) .. +32 as two
+// 32x32 MFMA tiles.  K advances in chunks of 128 (half a Q4_K/Q6_K
+// superblock, one ternary block).  Everything a chunk needs lives in one of
+// two LDS buffers (activation tile, unpacked weight digit planes, scales), so
+// the staging of chunk c+1 (global->register prefetch, unpack, LDS writes)
+// and the MFMA work of chunk c run in the same iteration with one barrier.
+// The two waves that share a SIMD take the two phases in opposite order, so
+// one wave's unpack VALU work issues under the other wave's MFMAs.
+//
+// LDS rows are padded to 144 bytes: row r starts 36*r banks (mod 64) into
+// the 64 four-byte banks, so the fragment reads of 16 consecutive rows hit 16
+// different bank groups, and the piece for K-step ks is a constant offset.
+//
+// Q4_K / Q6_K keep two int32 accumulators per tile (high and low digit
+// plane) across both halves of a superblock and fold once per superblock:
+//   out += float((hi << SHIFT) + lo) * d_w[n] * d_a[m].
+// Rows past M or N are clamped to the last valid row on load (their results
+// are computed and never stored).
 // ---------------------------------------------------------------------------
 
+constexpr int MBM = 128, MBN = 128, MNT = 512, MKC = 128;
+constexpr int MPITCH = MKC + 16;
+
+// LDS byte offset of 16-byte piece c of row r (144-byte rows)
+__device__ __forceinline__ int swz(int r, int c) { return r * MPITCH + 16 * c; }
+
 template <int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
-    GemmArgs a) {
-    constexpr int BM = 128, BN = 128, NT = 256;
+struct WStage;
+template <>
+struct WStage<FMT_Q4K> {
+    v4i hdr;
+    v4i q;  // 16 nibble bytes
+};
+template <>
+struct WStage<FMT_Q6K> {
+    uint32_t ql[9], qh[9];
+    uint32_t scbits, dbits, shift;
+};
+template <>
+struct WStage<FMT_TQ> {
+    uint32_t w[7];
+};
+
+// Ternary: trits [32*Q, 32*Q+32) of a block -> two 16-byte pieces.
+template <int Q>
+__device__ __forceinline__ void tq_unpack_part(const uint32_t *w, v4i *out) {
+    constexpr int B0 = (32 * Q) / 5, B1 = (32 * Q + 31) / 5;
+    uint32_t f[B1 - B0 + 1];
+#pragma unroll
+    for (int b = B0; b <= B1; ++b) f[b - B0] = tq_fixed((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int k = 32 * Q + 16 * qq + 4 * e + bb;
+                const int byte = k / 5 - B0, pos = k % 5;
+                uint32_t dig;
+                switch (pos) {
+                    case 0: dig = tq_digit<0>(f[byte]); break;
+                    case 1: dig = tq_digit<1>(f[byte]); break;
+                    case 2: dig = tq_digit<2>(f[byte]); break;
+                    case 3: dig = tq_digit<3>(f[byte]); break;
+                    default: dig = tq_digit<4>(f[byte]); break;
+                }
+                word |= dig << (8 * bb);
+            }
+            out[qq][e] = (int)digits_to_trits(word);
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
+    constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
-    constexpr int NSC = (FMT == FMT_TQ) ? 2 : 1;  // scale sets per chunk
-    constexpr int APIECES = BM * (KC / 16) / NT;  // 16-byte activation pieces per thread
+    constexpr bool Q4 = FMT == FMT_Q4K;
+    constexpr int CPS = (FMT == FMT_TQ) ? 1 : 2;  // chunks per scale block
+    constexpr int ABUF = BM * MPITCH, WBUF = NDIG * BN * MPITCH;
 
-    __shared__ __attribute__((aligned(16))) int8_t s_a[BM * PITCH];
-    __shared__ __attribute__((aligned(16))) int8_t s_w[NDIG * BN * PITCH];
-    __shared__ __attribute__((aligned(16))) float s_da[NSC * BM];
-    __shared__ __attribute__((aligned(16))) float s_dw[NSC * BN];
-    __shared__ v8bf s_alpha[(FMT == FMT_Q4K) ? 2 * BM * 2 : 1];
-    __shared__ v8bf s_beta[(FMT == FMT_Q4K) ? 2 * BN * 2 : 1];
+    __shared__ __attribute__((aligned(16))) int8_t s_a[2 * ABUF];
+    __shared__ __attribute__((aligned(16))) int8_t s_w[2 * WBUF];
+    __shared__ __attribute__((aligned(16))) float s_da[2 * BM];
+    __shared__ __attribute__((aligned(16))) float s_dw[2 * BN];
+    // Q4_K min-term operands: [pair ring 2][hi/lo 2][row][superblock parity 2]
+    __shared__ v8bf s_alpha[Q4 ? 2 * 2 * BM * 2 : 1];
+    __shared__ v8bf s_beta[Q4 ? 2 * 2 * BN * 2 : 1];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // XCD-aware tile order: blocks are dealt round-robin over 8 XCDs, so give
-    // XCD x the contiguous tile range [x*q, (x+1)*q); M-tiles vary fastest.
-    const int nwg = gridDim.x;
-    const int wg = blockIdx.x;
-    const int q8 = nwg >> 3;
+    // XCD-aware tile order: workgroups are dealt round-robin to 8 XCDs, so
+    // XCD x gets the contiguous tile range [x*q, (x+1)*q); M-tiles vary
+    // fastest, so the workgroups sharing a weight tile share an L2.
+    const int nwg = gridDim.x, wg = blockIdx.x, q8 = nwg >> 3;
     const int tile = (wg < 8 * q8) ? ((wg & 7) * q8 + (wg >> 3)) : wg;
-    const int tm = tile % a.tiles_m;
-    const int tn = tile / a.tiles_m;
+    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
+    const int M = a.M, N = a.N, K = a.K;
+    const int nch = (K + KCH - 1) / KCH;  // chunks
+    const int nsa = (FMT == FMT_TQ) ? a.nblk : a.nchunks;  // activation scale blocks per row
 
-    // staging roles
-    const int wn_row = tid >> 1, wpart = tid & 1;
-    const bool wvalid = (n0 + wn_row) < a.N;
-    const int wn_glob = wvalid ? (n0 + wn_row) : 0;
-
-    // compute roles
-    const int wm = wave >> 1, wnn = wave & 1;
     const int lrow = lane & 31, kgrp = lane >> 5;
+    const int wm = wave >> 2, wn = wave & 3;
 
-    v16f acc_f[2][2];
+    // ---- staging roles --------------------------------------------------
+    // activations: two 16-byte pieces per thread (row a_r0 + 64 i, piece a_pc)
+    const int a_pc = tid & 7, a_r0 = tid >> 3;
+    const int8_t *a_tile = a.qs + (int64_t)m0 * K;
+    uint32_t a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        a_off[i] = (uint32_t)(min(m0 + a_r0 + 64 * i, M - 1) - m0) * (uint32_t)K + 16u * a_pc;
+    // scales / sums: threads < BM own row tid
+    const float *da_tile = a.da + (int64_t)m0 * nsa;
+    const uint32_t s_ml = (uint32_t)(min(m0 + (tid & (BM - 1)), M - 1) - m0);
+    const uint32_t da_off = s_ml * (uint32_t)nsa;
+    const int16_t *bs_tile = Q4 ? a.bsums + (int64_t)m0 * (K / 16) : nullptr;
+    const uint32_t bs_off = s_ml * (uint32_t)(K / 16);
+    // weights: four threads per row; ternary uses a wave-uniform quarter
+    const int wq = (FMT == FMT_TQ) ? (tid >> 7) : (tid & 3);
+    const int w_nl = (FMT == FMT_TQ) ? (tid & 127) : (tid >> 2);
+    const int w_n = min(n0 + w_nl, N - 1);
+    const int64_t w_rowbytes = (int64_t)a.nblk * Fmt<FMT>::BB;
+    const uint8_t *w_tile = a.W + (int64_t)n0 * w_rowbytes;
+    const uint32_t w_off = (uint32_t)(w_n - n0) * (uint32_t)w_rowbytes;
+
+    // ---- prefetched chunks in registers: chunk j lives in set j % 2; it is
+    // loaded at the start of iteration j-2 and staged in iteration j-1.
+    constexpr int RING = 2;
+    struct Regs {
+        v4i act[2];
+        float da_v;
+        v4i bs_v;
+        WStage<FMT> ws;
+    };
+    Regs rg[RING];
+
+    auto prefetch = [&](Regs &R, int c) {
+        v4i(&act)[2] = R.act;
+        float &da_v = R.da_v;
+        v4i &bs_v = R.bs_v;
+        WStage<FMT> &ws = R.ws;
+        const int8_t *ab = a_tile + (int64_t)c * KCH;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) act[i] = *reinterpret_cast<const v4i *>(ab + a_off[i]);
+        const int sblk = c / CPS;   // scale block of this chunk
+        const int half = c % CPS;   // which half of the superblock
+        // every thread loads (rows >= BM re-read a clamped row) so that all
+        // paths issue the same number of loads and waits stay precise
+        da_v = da_tile[da_off + sblk];
+        if constexpr (Q4) bs_v = *reinterpret_cast<const v4i *>(bs_tile + bs_off + 16 * sblk + 8 * half);
+        const uint8_t *blk = w_tile + w_off + (int64_t)sblk * Fmt<FMT>::BB;
+        if constexpr (FMT == FMT_Q4K) {
+            ws.hdr = *reinterpret_cast<const v4i *>(blk);
+            ws.q = *reinterpret_cast<const v4i *>(blk + 16 + 64 * half + 16 * wq);
+        } else if constexpr (FMT == FMT_Q6K) {
+            const int64_t o = (int64_t)n0 * w_rowbytes + w_off + (int64_t)sblk * 210;
+            const uint32_t sh = (uint32_t)(o & 3);
+            const uint8_t *base = a.W + (o - sh);
+            const int u = wq;
+            ws.shift = sh;
+            // nine dwords cover the 32 bytes for either alignment, and stay
+            // inside the block (the ninth ends at byte 132 or 196 at most)
+#pragma unroll
+            for (int i = 0; i < 9; ++i) ws.ql[i] = ld_u32(base + 64 * half + 32 * (u & 1) + 4 * i);
+#pragma unroll
+            for (int i = 0; i < 9; ++i) ws.qh[i] = ld_u32(base + 128 + 32 * half + 4 * i);
+            ws.scbits = *reinterpret_cast<const unsigned short *>(a.W + o + 192 + 8 * half + 2 * u);
+            ws.dbits = *reinterpret_cast<const unsigned short *>(a.W + o + 208);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 7; ++i) ws.w[i] = ld_u32(blk + 4 * i);
+        }
+    };
+
+    // stage chunk c (c & 1 == P) from register set R into LDS buffer P
+    auto stage = [&](auto PP, const Regs &R, int c) {
+        constexpr int buf = decltype(PP)::value;
+        const v4i(&act)[2] = R.act;
+        const float &da_v = R.da_v;
+        const v4i &bs_v = R.bs_v;
+        const WStage<FMT> &ws = R.ws;
+        int8_t *sa = s_a + buf * ABUF;
+        int8_t *p0 = s_w + buf * WBUF;
+        int8_t *p1 = p0 + (NDIG - 1) * BN * MPITCH;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(sa + swz(a_r0 + 64 * i, a_pc)) = act[i];
+        if (tid < BM) s_da[buf * BM + tid] = da_v;
+        const int sblk = c / CPS;
+        constexpr int half = (CPS == 2) ? buf : 0;
+        if constexpr (Q4) {
+            const int pair = sblk >> 1, par = sblk & 1, ring = pair & 1;
+            const bool zero_odd = (par == 0) && (sblk == a.nchunks - 1);
+            if (tid < BM) {
+                // alpha_j = d_a * (bsums[2j] + bsums[2j+1]) for j = 4*half .. +3
+                __bf16 *ah = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + tid) * 2 + par]) + 4 * half;
+                __bf16 *al = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + tid) * 2 + par]) + 4 * half;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t wv = (uint32_t)bs_v[i];
+                    const int b = (int)(int16_t)(wv & 0xFFFF) + (int)(int16_t)(wv >> 16);
+                    __bf16 hi, lo;
+                    split_bf16(da_v * (float)b, hi, lo);
+                    ah[i] = hi;
+                    al[i] = lo;
+                }
+                if (zero_odd) {
+                    __bf16 *zh = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + tid) * 2 + 1]) + 4 * half;
+                    __bf16 *zl = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + tid) * 2 + 1]) + 4 * half;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) zh[i] = zl[i] = (__bf16)0.0f;
+                }
+            }
+            // weights: this thread's 16 nibble bytes hold column cl = 2*half + (wq>>1)
+            const int cl = 2 * half + (wq >> 1);
+            uint32_t sc[2], mn[2];
+            q4k_fields((uint32_t)ws.hdr[1], (uint32_t)ws.hdr[2], (uint32_t)ws.hdr[3], 2 * cl, 2, sc, mn);
+            v4i hl, ll, hh, lh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t word = (uint32_t)ws.q[e];
+                uint32_t dh, dl;
+                q4k_digits(word & 0x0F0F0F0Fu, sc[0], dh, dl);
+                hl[e] = (int)dh;
+                ll[e] = (int)dl;
+                q4k_digits((word >> 4) & 0x0F0F0F0Fu, sc[1], dh, dl);
+                hh[e] = (int)dh;
+                lh[e] = (int)dl;
+            }
+            const int pl = 4 * (wq >> 1) + (wq & 1);   // piece of the low nibbles
+            *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl)) = hl;
+            *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl)) = ll;
+            *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl + 2)) = hh;
+            *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl + 2)) = lh;
+            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32((uint32_t)ws.hdr[0]);
+            if ((wq & 1) == 0) {
+                const float dmin = f16_bits_to_f32((uint32_t)ws.hdr[0] >> 16);
+                __bf16 *bh = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 0) * BN + w_nl) * 2 + par]) + 2 * cl;
+                __bf16 *bl = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 1) * BN + w_nl) * 2 + par]) + 2 * cl;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    __bf16 hi, lo;
+                    split_bf16(-dmin * (float)mn[i], hi, lo);
+                    bh[i] = hi;
+                    bl[i] = lo;
+                }
+                if (zero_odd) {
+                    __bf16 *zh = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 0) * BN + w_nl) * 2 + 1]) + 2 * cl;
+                    __bf16 *zl = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 1) * BN + w_nl) * 2 + 1]) + 2 * cl;
+                    zh[0] = zh[1] = zl[0] = zl[1] = (__bf16)0.0f;
+                }
+            }
+        } else if constexpr (FMT == FMT_Q6K) {
+            const int u = wq;
+            const uint32_t sh = ws.shift;
+            const int sc_lo = (int)(int8_t)(ws.scbits & 0xFF), sc_hi = (int)(int8_t)(ws.scbits >> 8);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int sc = g ? sc_hi : sc_lo;
+                v4i vh, vl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t4 = 4 * g + e;
+                    const uint32_t qlw = sh ? __builtin_amdgcn_alignbyte(ws.ql[t4 + 1], ws.ql[t4], 2) : ws.ql[t4];
+                    const uint32_t qhw = sh ? __builtin_amdgcn_alignbyte(ws.qh[t4 + 1], ws.qh[t4], 2) : ws.qh[t4];
+                    const uint32_t lo4 = (qlw >> (4 * (u >> 1))) & 0x0F0F0F0Fu;
+                    const uint32_t hi2 = (qhw >> (2 * u)) & 0x03030303u;
+                    uint32_t dh, dl;
+                    q6k_digits(lo4 | (hi2 << 4), sc, dh, dl);
+                    vh[e] = (int)dh;
+                    vl[e] = (int)dl;
+                }
+                *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * u + g)) = vh;
+                *reinterpret_cast<v4i *>(p1 + swz(w_nl, 2 * u + g)) = vl;
+            }
+            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32(ws.dbits);
+        } else {
+            v4i pieces[2];
+            switch (__builtin_amdgcn_readfirstlane(wq)) {  // wave-uniform
+                case 0: tq_unpack_part<0>(ws.w, pieces); break;
+                case 1: tq_unpack_part<1>(ws.w, pieces); break;
+                case 2: tq_unpack_part<2>(ws.w, pieces); break;
+                default: tq_unpack_part<3>(ws.w, pieces); break;
+            }
+            *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * wq)) = pieces[0];
+            *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * wq + 1)) = pieces[1];
+            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32(ws.w[6] >> 16);
+        }
+    };
+
+    v16f acc_f[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_f[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc_f[i][r] = 0.0f;
+    v16i acc[NDIG][2];
 
-    // register prefetch of one chunk
-    v4i act[APIECES];
-    float da_reg[NSC];
-    v4i bs_reg;  // Q4_K: this thread's 8 int16 bsums
-    float da_bs = 0.f;
-    WRaw<FMT> wr;
-
-    auto prefetch = [&](int c) {
+    // compute chunk c (c & 1 == P) from LDS buffer P
+    auto compute = [&](auto PP, int c) {
+        constexpr int buf = decltype(PP)::value;
+        const int8_t *sa = s_a + buf * ABUF;
+        const int8_t *sw = s_w + buf * WBUF;
+        constexpr bool first = (CPS == 1) || (buf == 0);
+        constexpr bool last = (CPS == 1) || (buf == 1);
 #pragma unroll
-        for (int i = 0; i < APIECES; ++i) {
-            const int p = tid + NT * i;
-            const int row = p >> 4, piece = p & 15;
-            const int m = m0 + row;
-            act[i] = load_act_piece(a, m, c, piece);
+        for (int ks = 0; ks < KCH / 32; ++ks) {
+            const int pc = 2 * ks + kgrp;
+            v4i A[2], B[NDIG];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                A[i] = *reinterpret_cast<const v4i *>(sa + swz(64 * wm + 32 * i + lrow, pc));
+#pragma unroll
+            for (int dg = 0; dg < NDIG; ++dg)
+                B[dg] = *reinterpret_cast<const v4i *>(sw + dg * BN * MPITCH + swz(32 * wn + lrow, pc));
+#pragma unroll
+            for (int dg = 0; dg < NDIG; ++dg)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[dg][i] = (first && ks == 0) ? mfma_i8_32x32x32(A[i], B[dg], v16i{})
+                                                    : mfma_i8_32x32x32(A[i], B[dg], acc[dg][i]);
         }
-        if (tid < BM) {
-            const int m = m0 + tid;
-            if constexpr (FMT == FMT_TQ) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int b = 2 * c + s;
-                    da_reg[s] = (m < a.M && b < a.nblk) ? a.da[(int64_t)m * a.nblk + b] : 0.0f;
-                }
-            } else {
-                da_reg[0] = (m < a.M) ? a.da[(int64_t)m * a.nchunks + c] : 0.0f;
-            }
-        }
-        if constexpr (FMT == FMT_Q4K) {
-            const int row = tid >> 1, half = tid & 1;
-            const int m = m0 + row;
-            if (m < a.M) {
-                bs_reg = *reinterpret_cast<const v4i *>(a.bsums + (int64_t)m * (a.K / 16) +
-                                                        16 * c + 8 * half);
-                da_bs = a.da[(int64_t)m * a.nchunks + c];
-            } else {
-                bs_reg = v4i{0, 0, 0, 0};
-                da_bs = 0.f;
-            }
-        }
-        load_w<FMT>(wr, a, wn_glob, wpart, c);
-    };
-
-    auto stage = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < APIECES; ++i) {
-            const int p = tid + NT * i;
-            const int row = p >> 4, piece = p & 15;
-            *reinterpret_cast<v4i *>(s_a + row * PITCH + 16 * piece) = act[i];
-        }
-        if (tid < BM) {
-#pragma unroll
-            for (int s = 0; s < NSC; ++s) s_da[s * BM + tid] = da_reg[s];
-        }
-        const int parity = c & 1;
-        const bool zero_odd = (parity == 0) && (c == a.nchunks - 1);
-        if constexpr (FMT == FMT_Q4K) {
-            // alpha_j = d_a * (bsums[2j] + bsums[2j+1]) for this thread's 4 sub-blocks
-            const int row = tid >> 1, half = tid & 1;
-            __bf16 *ah = reinterpret_cast<__bf16 *>(&s_alpha[(0 * BM + row) * 2 + parity]) + 4 * half;
-            __bf16 *al = reinterpret_cast<__bf16 *>(&s_alpha[(1 * BM + row) * 2 + parity]) + 4 * half;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t wv = (uint32_t)bs_reg[i];
-                const int b = (int)(int16_t)(wv & 0xFFFF) + (int)(int16_t)(wv >> 16);
-                __bf16 hi, lo;
-                split_bf16(da_bs * (float)b, hi, lo);
-                ah[i] = hi;
-                al[i] = lo;
-            }
-            if (zero_odd) {
-                __bf16 *zh = reinterpret_cast<__bf16 *>(&s_alpha[(0 * BM + row) * 2 + 1]) + 4 * half;
-                __bf16 *zl = reinterpret_cast<__bf16 *>(&s_alpha[(1 * BM + row) * 2 + 1]) + 4 * half;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    zh[i] = (__bf16)0.0f;
-                    zl[i] = (__bf16)0.0f;
-                }
-            }
-        }
-        unpack_w<FMT, false>(wr, wvalid, s_w, BN * PITCH, wn_row, wpart, s_dw, BN,
-                             (FMT == FMT_Q4K) ? s_beta : nullptr, parity, zero_odd);
-    };
-
-    // int32 accumulators for the digit planes
-    v16i acc_i[NDIG][2][2];
-
-    auto fold = [&](int s) {
-        // out += (T as fp32) * d_a[m] * d_w[n], T = (plane0 << SHIFT) + plane1
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float dwv = s_dw[s * BN + 64 * wnn + 32 * j + lrow];
+        if constexpr (last) {
+            // fold: out += float(T) * d_w[n] * d_a[m]
+            const float dwv = s_dw[buf * BN + 32 * wn + lrow];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const v4f dav = *reinterpret_cast<const v4f *>(
-                        &s_da[s * BM + 64 * wm + 32 * i + 8 * r4 + 4 * kgrp]);
+                    const v4f dav = *reinterpret_cast<const v4f *>(&s_da[buf * BM + 64 * wm + 32 * i + 8 * r4 + 4 * kgrp]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * r4 + e;
                         int T;
                         if constexpr (NDIG == 2)
-                            T = (acc_i[0][i][j][r] << Fmt<FMT>::SHIFT) + acc_i[1][i][j][r];
+                            T = (acc[0][i][r] << Fmt<FMT>::SHIFT) + acc[1][i][r];
                         else
-                            T = acc_i[0][i][j][r];
-                        acc_f[i][j][r] = fmaf((float)T, dav[e] * dwv, acc_f[i][j][r]);
+                            T = acc[0][i][r];
+                        acc_f[i][r] = fmaf((float)T * dwv, dav[e], acc_f[i][r]);
                     }
+                }
+            }
+        }
+        if constexpr (Q4) {
+            const int sblk = c / CPS;
+            // after the last chunk of each superblock pair (or of the row)
+            if (last && ((sblk & 1) || sblk == a.nchunks - 1)) {
+                const int ring = (sblk >> 1) & 1;
+                const int col = 32 * wn + lrow;
+                const v8bf bh = s_beta[((ring * 2 + 0) * BN + col) * 2 + kgrp];
+                const v8bf bl = s_beta[((ring * 2 + 1) * BN + col) * 2 + kgrp];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int row = 64 * wm + 32 * i + lrow;
+                    const v8bf ah = s_alpha[((ring * 2 + 0) * BM + row) * 2 + kgrp];
+                    const v8bf al = s_alpha[((ring * 2 + 1) * BM + row) * 2 + kgrp];
+                    acc_f[i] = mfma_bf16_32x32x16(ah, bh, acc_f[i]);
+                    acc_f[i] = mfma_bf16_32x32x16(ah, bl, acc_f[i]);
+                    acc_f[i] = mfma_bf16_32x32x16(al, bh, acc_f[i]);
                 }
             }
         }
     };
 
-    if (a.nchunks > 0) prefetch(0);
-
-    for (int c = 0; c < a.nchunks; ++c) {
-        __syncthreads();
-        stage(c);
-        __syncthreads();
-        if (c + 1 < a.nchunks) prefetch(c + 1);
-
-        constexpr int KSTEPS = KC / 32;
-        constexpr int FOLD_EVERY = (FMT == FMT_TQ) ? 4 : KSTEPS;  // K-steps per scale block
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            v4i A[2], B[NDIG][2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                A[i] = *reinterpret_cast<const v4i *>(
-                    s_a + (64 * wm + 32 * i + lrow) * PITCH + 32 * ks + 16 * kgrp);
-#pragma unroll
-            for (int dg = 0; dg < NDIG; ++dg)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    B[dg][j] = *reinterpret_cast<const v4i *>(
-                        s_w + dg * BN * PITCH + (64 * wnn + 32 * j + lrow) * PITCH + 32 * ks +
-                        16 * kgrp);
-            const bool first = (ks % FOLD_EVERY) == 0;
-#pragma unroll
-            for (int dg = 0; dg < NDIG; ++dg)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        v16i cin;
-                        if (first) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) cin[r] = 0;
-                        } else {
-                            cin = acc_i[dg][i][j];
-                        }
-                        acc_i[dg][i][j] = mfma_i8_32x32x32(A[i], B[dg][j], cin);
-                    }
-            if ((ks % FOLD_EVERY) == FOLD_EVERY - 1) fold((FMT == FMT_TQ) ? (ks / 4) : 0);
+    // prologue: chunks 0..RING-1 in flight, chunk 0 staged
+    // prefetches past the last chunk re-load the last chunk (harmless) so the
+    // number of loads in flight is the same on every path
+    const int clast = max(nch - 1, 0);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (nch > 0) {
+        prefetch(rg[0], 0);
+        prefetch(rg[1], min(1, clast));
+        stage(P0{}, rg[0], 0);
+    }
+    __syncthreads();
+    const bool stage_first = (wm == 0);
+    // one iteration (c & 1 == P): refill the register set that held chunk c
+    // with chunk c+2, stage chunk c+1 into the other LDS buffer, compute
+    // chunk c, barrier.  The two waves of a SIMD take stage and compute in
+    // opposite order.
+    auto iteration = [&](auto PP, int c) {
+        constexpr int P = decltype(PP)::value;
+        using Q = std::integral_constant<int, 1 - P>;
+        prefetch(rg[P], min(c + 2, clast));
+        if (stage_first) {
+            if (c + 1 < nch) stage(Q{}, rg[1 - P], c + 1);
+            compute(PP, c);
+        } else {
+            compute(PP, c);
+            if (c + 1 < nch) stage(Q{}, rg[1 - P], c + 1);
         }
-
-        if constexpr (FMT == FMT_Q4K) {
-            if ((c & 1) || c == a.nchunks - 1) {
-                v8bf ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = 64 * wm + 32 * i + lrow;
-                    ah[i] = s_alpha[(0 * BM + row) * 2 + kgrp];
-                    al[i] = s_alpha[(1 * BM + row) * 2 + kgrp];
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = 64 * wnn + 32 * j + lrow;
-                    bh[j] = s_beta[(0 * BN + col) * 2 + kgrp];
-                    bl[j] = s_beta[(1 * BN + col) * 2 + kgrp];
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        acc_f[i][j] = mfma_bf16_32x32x16(ah[i], bh[j], acc_f[i][j]);
-                        acc_f[i][j] = mfma_bf16_32x32x16(ah[i], bl[j], acc_f[i][j]);
-                        acc_f[i][j] = mfma_bf16_32x32x16(al[i], bh[j], acc_f[i][j]);
-                    }
-            }
-        }
+        __syncthreads();
+    };
+    for (int c = 0; c < nch; c += 2) {
+        iteration(P0{}, c);
+        if (c + 1 < nch) iteration(P1{}, c + 1);
     }
 
-    // epilogue: masked fp32 stores
+    // ---- epilogue: fp32 stores (unmasked when the whole tile is inside) ----
     float *out = reinterpret_cast<float *>(a.out);
+    const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+    const int n = n0 + 32 * wn + lrow;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wnn + 32 * j + lrow;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + 64 * wm + 32 * i + mfma32_row(r, lane);
-                if (m < a.M && n < a.N) out[(int64_t)m * a.N + n] = acc_f[i][j][r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int m = m0 + 64 * wm + 32 * i + mfma32_row(r, lane);
+            if (full || (m < M && n < N)) out[(int64_t)m * N + n] = acc_f[i][r];
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -670,17 +843,17 @@ static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float 
 hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
                        const int16_t *bsums, float *out, int M, int N, int K,
                        hipStream_t stream) {
-    GemmArgs a = make_args(fmt, W, qs, da, bsums, out, M, N, K, 128, 128);
+    GemmArgs a = make_args(fmt, W, qs, da, bsums, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {
         case FMT_Q4K:
-            hipLaunchKernelGGL(gemm_kernel<FMT_Q4K>, dim3(grid), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(gemm_kernel<FMT_Q4K>, dim3(grid), dim3(MNT), 0, stream, a);
             break;
         case FMT_Q6K:
-            hipLaunchKernelGGL(gemm_kernel<FMT_Q6K>, dim3(grid), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(gemm_kernel<FMT_Q6K>, dim3(grid), dim3(MNT), 0, stream, a);
             break;
         default:
-            hipLaunchKernelGGL(gemm_kernel<FMT_TQ>, dim3(grid), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(gemm_kernel<FMT_TQ>, dim3(grid), dim3(MNT), 0, stream, a);
             break;
     }
     return hipGetLastError();
