@@ -285,26 +285,32 @@ __device__ __forceinline__ v4i load_act_piece(const GemmArgs &a, int m, int c, i
     if (m >= a.M || k >= a.K) return v4i{0, 0, 0, 0};
     return *reinterpret_cast<const v4i *>(a.qs + (int64_t)m * a.K + k);
 }
-
 // ---------------------------------------------------------------------------
 // Main kernel.
 //
 // Workgroup: 512 threads (8 waves, two per SIMD), output tile 128 x 128.
 // Wave w computes rows 64*(w/4) .. +64 and columns 32*(w%4) .. +32 as two
 // 32x32 MFMA tiles.  K advances in chunks of 128 (half a Q4_K/Q6_K
-// superblock, one ternary block).  Everything a chunk needs lives in one of
-// two LDS buffers (activation tile, unpacked weight digit planes, scales), so
-// the staging of chunk c+1 (global->register prefetch, unpack, LDS writes)
-// and the MFMA work of chunk c run in the same iteration with one barrier.
-// The two waves that share a SIMD take the two phases in opposite order, so
-// one wave's unpack VALU work issues under the other wave's MFMAs.
+// superblock, one ternary block).  Each chunk has its own LDS buffer pair
+// (activation tile, unpacked weight digit planes); scales live in a ring of
+// four scale-block slots.  One iteration = one chunk, one barrier:
+//   * global loads of chunk c+2 into one register set,
+//   * unpack of chunk c+1 (loaded one iteration earlier) into the other LDS
+//     buffer,
+//   * the MFMAs of chunk c,
+//   * the fold of one m-tile: at a superblock's last chunk, tile 0 is folded
+//     right after its MFMAs (while tile 1's MFMAs run); tile 1 is folded at
+//     the next chunk, before its accumulators restart (while tile 0's run).
+// The body of an iteration is one basic block (compile-time chunk phase,
+// clamped loads past the end, no divergent stores), so the scheduler can
+// interleave the unpack and fold VALU work with the MFMAs.
 //
 // LDS rows are padded to 144 bytes: row r starts 36*r banks (mod 64) into
 // the 64 four-byte banks, so the fragment reads of 16 consecutive rows hit 16
-// different bank groups, and the piece for K-step ks is a constant offset.
+// different bank groups.
 //
 // Q4_K / Q6_K keep two int32 accumulators per tile (high and low digit
-// plane) across both halves of a superblock and fold once per superblock:
+// plane) across both chunks of a superblock and fold once per superblock:
 //   out += float((hi << SHIFT) + lo) * d_w[n] * d_a[m].
 // Rows past M or N are clamped to the last valid row on load (their results
 // are computed and never stored).
@@ -316,69 +322,85 @@ constexpr int MPITCH = MKC + 16;
 // LDS byte offset of 16-byte piece c of row r (144-byte rows)
 __device__ __forceinline__ int swz(int r, int c) { return r * MPITCH + 16 * c; }
 
-template <int FMT>
-struct WStage;
-template <>
-struct WStage<FMT_Q4K> {
-    v4i hdr;
-    v4i q;  // 16 nibble bytes
-};
-template <>
-struct WStage<FMT_Q6K> {
-    uint32_t ql[9], qh[9];
-    uint32_t scbits, dbits, shift;
-};
-template <>
-struct WStage<FMT_TQ> {
-    uint32_t w[7];
-};
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x020, SG_DSR = 0x100, SG_DSW = 0x200 };
 
-// Ternary: trits [32*Q, 32*Q+32) of a block -> two 16-byte pieces.
-template <int Q>
-__device__ __forceinline__ void tq_unpack_part(const uint32_t *w, v4i *out) {
-    constexpr int B0 = (32 * Q) / 5, B1 = (32 * Q + 31) / 5;
-    uint32_t f[B1 - B0 + 1];
-#pragma unroll
-    for (int b = B0; b <= B1; ++b) f[b - B0] = tq_fixed((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const int k = 32 * Q + 16 * qq + 4 * e + bb;
-                const int byte = k / 5 - B0, pos = k % 5;
-                uint32_t dig;
-                switch (pos) {
-                    case 0: dig = tq_digit<0>(f[byte]); break;
-                    case 1: dig = tq_digit<1>(f[byte]); break;
-                    case 2: dig = tq_digit<2>(f[byte]); break;
-                    case 3: dig = tq_digit<3>(f[byte]); break;
-                    default: dig = tq_digit<4>(f[byte]); break;
-                }
-                word |= dig << (8 * bb);
-            }
-            out[qq][e] = (int)digits_to_trits(word);
-        }
+#define KQ_INLINE __attribute__((always_inline))
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{})
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
     }
 }
 
+// Per-thread registers of one chunk between its global loads and its unpack.
 template <int FMT>
-__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
+struct ChunkRegs;
+template <>
+struct ChunkRegs<FMT_Q4K> {
+    v4i act[2];
+    float da;
+    uint32_t bs;  // the two int16 activation sums of this thread's 32-sub-block
+    v4i hdr;      // d, dmin, 12 scale bytes
+    v4i q;        // 16 nibble bytes
+};
+template <>
+struct ChunkRegs<FMT_Q6K> {
+    v4i act[2];
+    float da;
+    uint32_t ql[6];  // two 8-byte runs of ql, each in 3 aligned dwords
+    uint32_t qh[3];  // one 8-byte run of qh
+    uint32_t sc[3];  // 8 scale bytes
+    uint32_t d;
+};
+template <>
+struct ChunkRegs<FMT_TQ> {
+    v4i act[2];
+    float da;
+    uint32_t w[2];  // 8 trit bytes
+};
+
+// Ternary decode table entry for byte v: its five base-3 digits minus one as
+// int8 in bytes 0..4, zero bytes 5..7.  Digit p is floor(v / 3^p) mod 3, so
+// bytes above 242 decode exactly as the plain digit definition gives.
+__device__ __forceinline__ void tq_lut_entry(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    uint32_t t[5];
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+        t[p] = (uint32_t)(int8_t)((int)(v % 3u) - 1) & 0xFFu;
+        v /= 3u;
+    }
+    lo = t[0] | (t[1] << 8) | (t[2] << 16) | (t[3] << 24);
+    hi = t[4];
+}
+
+template <int FMT>
+__global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
-    constexpr bool Q4 = FMT == FMT_Q4K;
-    constexpr int CPS = (FMT == FMT_TQ) ? 1 : 2;  // chunks per scale block
-    constexpr int ABUF = BM * MPITCH, WBUF = NDIG * BN * MPITCH;
+    constexpr bool Q4 = FMT == FMT_Q4K, Q6 = FMT == FMT_Q6K, TQ = FMT == FMT_TQ;
+    constexpr int CPS = TQ ? 1 : 2;  // chunks per scale block
+    constexpr int PLANE = BN * MPITCH;
 
-    __shared__ __attribute__((aligned(16))) int8_t s_a[2 * ABUF];
-    __shared__ __attribute__((aligned(16))) int8_t s_w[2 * WBUF];
-    __shared__ __attribute__((aligned(16))) float s_da[2 * BM];
-    __shared__ __attribute__((aligned(16))) float s_dw[2 * BN];
+    // one array per buffer, so the compiler sees that staging writes and
+    // fragment reads never alias
+    __shared__ __attribute__((aligned(16))) int8_t s_a0[BM * MPITCH];
+    __shared__ __attribute__((aligned(16))) int8_t s_a1[BM * MPITCH];
+    __shared__ __attribute__((aligned(16))) int8_t s_w0[NDIG * PLANE];
+    __shared__ __attribute__((aligned(16))) int8_t s_w1[NDIG * PLANE];
+    // block scales: a ring of 4 scale-block slots
+    __shared__ __attribute__((aligned(16))) float s_da[4 * BM];
+    __shared__ __attribute__((aligned(16))) float s_dw[4 * BN + 64];  // + a junk row
     // Q4_K min-term operands: [pair ring 2][hi/lo 2][row][superblock parity 2]
     __shared__ v8bf s_alpha[Q4 ? 2 * 2 * BM * 2 : 1];
     __shared__ v8bf s_beta[Q4 ? 2 * 2 * BN * 2 : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t s_lut[TQ ? 2 * 256 : 2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -390,8 +412,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = a.M, N = a.N, K = a.K;
-    const int nch = (K + KCH - 1) / KCH;  // chunks
-    const int nsa = (FMT == FMT_TQ) ? a.nblk : a.nchunks;  // activation scale blocks per row
+    const int nch = (K + KCH - 1) / KCH;                    // chunks
+    const int nsa = TQ ? a.nblk : a.nchunks;                // activation scale blocks per row
 
     const int lrow = lane & 31, kgrp = lane >> 5;
     const int wm = wave >> 2, wn = wave & 3;
@@ -404,291 +426,460 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         a_off[i] = (uint32_t)(min(m0 + a_r0 + 64 * i, M - 1) - m0) * (uint32_t)K + 16u * a_pc;
-    // scales / sums: threads < BM own row tid
+    // activation scales / sums: thread t owns row t/4 and, for Q4_K, 32-sub-block t%4 of the chunk
+    const int s_row = tid >> 2, s_j = tid & 3;
     const float *da_tile = a.da + (int64_t)m0 * nsa;
-    const uint32_t s_ml = (uint32_t)(min(m0 + (tid & (BM - 1)), M - 1) - m0);
+    const uint32_t s_ml = (uint32_t)(min(m0 + s_row, M - 1) - m0);
     const uint32_t da_off = s_ml * (uint32_t)nsa;
     const int16_t *bs_tile = Q4 ? a.bsums + (int64_t)m0 * (K / 16) : nullptr;
-    const uint32_t bs_off = s_ml * (uint32_t)(K / 16);
-    // weights: four threads per row; ternary uses a wave-uniform quarter
-    const int wq = (FMT == FMT_TQ) ? (tid >> 7) : (tid & 3);
-    const int w_nl = (FMT == FMT_TQ) ? (tid & 127) : (tid >> 2);
+    const uint32_t bs_off = s_ml * (uint32_t)(K / 16) + 2 * s_j;
+    // weights: four threads per row
+    const int wq = tid & 3, w_nl = tid >> 2;
     const int w_n = min(n0 + w_nl, N - 1);
     const int64_t w_rowbytes = (int64_t)a.nblk * Fmt<FMT>::BB;
     const uint8_t *w_tile = a.W + (int64_t)n0 * w_rowbytes;
     const uint32_t w_off = (uint32_t)(w_n - n0) * (uint32_t)w_rowbytes;
+    // ternary: this thread's 8 trit bytes start at byte 8*wq of the block
+    // (20 for the last quarter, which decodes bytes 20..27 into row bytes
+    // 100..139; bytes 128.. land in the row padding)
+    const int tq_off = (wq == 3) ? 20 : 8 * wq;
 
-    // ---- prefetched chunks in registers: chunk j lives in set j % 2; it is
-    // loaded at the start of iteration j-2 and staged in iteration j-1.
-    constexpr int RING = 2;
-    struct Regs {
-        v4i act[2];
-        float da_v;
-        v4i bs_v;
-        WStage<FMT> ws;
+    const int clast = max(nch - 1, 0);
+    // chunk x, or past the end the last chunk with x's parity (the same half
+    // of a superblock), so repeated loads and stages rewrite identical values
+    auto clampc = [&](int x) KQ_INLINE {
+        if (x <= clast) return x;
+        return (CPS == 1) ? clast : clast - ((x - clast) & 1);
     };
-    Regs rg[RING];
 
-    auto prefetch = [&](Regs &R, int c) {
-        v4i(&act)[2] = R.act;
-        float &da_v = R.da_v;
-        v4i &bs_v = R.bs_v;
-        WStage<FMT> &ws = R.ws;
+    ChunkRegs<FMT> rg[2];
+
+    // global loads of chunk c (c % 2 == H) into R
+    auto prefetch = [&](auto HH, ChunkRegs<FMT> &R, int c) KQ_INLINE {
+        constexpr int H = decltype(HH)::value;
         const int8_t *ab = a_tile + (int64_t)c * KCH;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) act[i] = *reinterpret_cast<const v4i *>(ab + a_off[i]);
-        const int sblk = c / CPS;   // scale block of this chunk
-        const int half = c % CPS;   // which half of the superblock
-        // every thread loads (rows >= BM re-read a clamped row) so that all
-        // paths issue the same number of loads and waits stay precise
-        da_v = da_tile[da_off + sblk];
-        if constexpr (Q4) bs_v = *reinterpret_cast<const v4i *>(bs_tile + bs_off + 16 * sblk + 8 * half);
+        for (int i = 0; i < 2; ++i) R.act[i] = *reinterpret_cast<const v4i *>(ab + a_off[i]);
+        const int sblk = c / CPS;
+        R.da = da_tile[da_off + sblk];
         const uint8_t *blk = w_tile + w_off + (int64_t)sblk * Fmt<FMT>::BB;
-        if constexpr (FMT == FMT_Q4K) {
-            ws.hdr = *reinterpret_cast<const v4i *>(blk);
-            ws.q = *reinterpret_cast<const v4i *>(blk + 16 + 64 * half + 16 * wq);
-        } else if constexpr (FMT == FMT_Q6K) {
-            const int64_t o = (int64_t)n0 * w_rowbytes + w_off + (int64_t)sblk * 210;
-            const uint32_t sh = (uint32_t)(o & 3);
-            const uint8_t *base = a.W + (o - sh);
-            const int u = wq;
-            ws.shift = sh;
-            // nine dwords cover the 32 bytes for either alignment, and stay
-            // inside the block (the ninth ends at byte 132 or 196 at most)
+        if constexpr (Q4) {
+            R.bs = *reinterpret_cast<const uint32_t *>(bs_tile + bs_off + 16 * sblk + 8 * H);
+            R.hdr = *reinterpret_cast<const v4i *>(blk);
+            R.q = *reinterpret_cast<const v4i *>(blk + 16 + 64 * H + 16 * wq);
+        } else if constexpr (Q6) {
+            // the 210-byte block starts 0 or 2 bytes past a dword boundary;
+            // every window below lies inside the block or the block before it
+            const uint32_t sh = (uint32_t)(uintptr_t)blk & 3u;
+            const uint8_t *base = blk - sh;
 #pragma unroll
-            for (int i = 0; i < 9; ++i) ws.ql[i] = ld_u32(base + 64 * half + 32 * (u & 1) + 4 * i);
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 9; ++i) ws.qh[i] = ld_u32(base + 128 + 32 * half + 4 * i);
-            ws.scbits = *reinterpret_cast<const unsigned short *>(a.W + o + 192 + 8 * half + 2 * u);
-            ws.dbits = *reinterpret_cast<const unsigned short *>(a.W + o + 208);
+                for (int i = 0; i < 3; ++i)
+                    R.ql[3 * j + i] = ld_u32(base + 64 * H + 32 * j + 8 * wq + 4 * i);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) R.qh[i] = ld_u32(base + 128 + 32 * H + 8 * wq + 4 * i);
+            R.sc[0] = ld_u32(base + 192 + 8 * H);
+            R.sc[1] = ld_u32(base + 196 + 8 * H);
+            // third dword only needed when sh == 2; otherwise re-read the second
+            R.sc[2] = ld_u32(base + 200 + 8 * H - (sh ? 0 : 4));
+            R.d = *reinterpret_cast<const unsigned short *>(blk + 208);
         } else {
-#pragma unroll
-            for (int i = 0; i < 7; ++i) ws.w[i] = ld_u32(blk + 4 * i);
+            R.w[0] = ld_u32(blk + tq_off);
+            R.w[1] = ld_u32(blk + tq_off + 4);
         }
     };
 
-    // stage chunk c (c & 1 == P) from register set R into LDS buffer P
-    auto stage = [&](auto PP, const Regs &R, int c) {
-        constexpr int buf = decltype(PP)::value;
-        const v4i(&act)[2] = R.act;
-        const float &da_v = R.da_v;
-        const v4i &bs_v = R.bs_v;
-        const WStage<FMT> &ws = R.ws;
-        int8_t *sa = s_a + buf * ABUF;
-        int8_t *p0 = s_w + buf * WBUF;
-        int8_t *p1 = p0 + (NDIG - 1) * BN * MPITCH;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(sa + swz(a_r0 + 64 * i, a_pc)) = act[i];
-        if (tid < BM) s_da[buf * BM + tid] = da_v;
+    // ---- unpack of chunk c (c % 2 == B) from R into LDS buffer B, in eight
+    // pieces that ride along the eight MFMA slots of one m-tile ------------
+    struct StageTmp {
+        uint32_t sc[2], mn[2];   // Q4_K sub-block scales / mins of this thread
+        v4i hl, ll, hh, lh;      // Q4_K digit planes (low / high nibbles)
+        uint32_t ql[2][2], qh[2], S0, S1, vh[2], vl[2];  // Q6_K
+        uint32_t lo[8], hi[8];   // ternary table entries
+    };
+    auto stage_piece = [&](auto BB_, auto SS, const ChunkRegs<FMT> &R, int c, StageTmp &T) KQ_INLINE {
+        constexpr int B = decltype(BB_)::value;
+        constexpr int S = decltype(SS)::value;
+        int8_t *sa = B ? s_a1 : s_a0;
+        int8_t *p0 = B ? s_w1 : s_w0;
+        int8_t *p1 = p0 + (NDIG - 1) * PLANE;
         const int sblk = c / CPS;
-        constexpr int half = (CPS == 2) ? buf : 0;
+        const int slot = sblk & 3;
+        if constexpr (S == 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<v4i *>(sa + swz(a_r0 + 64 * i, a_pc)) = R.act[i];
+            s_da[slot * BM + s_row] = R.da;  // the four threads of a row store the same value
+        }
         if constexpr (Q4) {
-            const int pair = sblk >> 1, par = sblk & 1, ring = pair & 1;
-            const bool zero_odd = (par == 0) && (sblk == a.nchunks - 1);
-            if (tid < BM) {
-                // alpha_j = d_a * (bsums[2j] + bsums[2j+1]) for j = 4*half .. +3
-                __bf16 *ah = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + tid) * 2 + par]) + 4 * half;
-                __bf16 *al = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + tid) * 2 + par]) + 4 * half;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t wv = (uint32_t)bs_v[i];
-                    const int b = (int)(int16_t)(wv & 0xFFFF) + (int)(int16_t)(wv >> 16);
-                    __bf16 hi, lo;
-                    split_bf16(da_v * (float)b, hi, lo);
-                    ah[i] = hi;
-                    al[i] = lo;
-                }
-                if (zero_odd) {
-                    __bf16 *zh = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + tid) * 2 + 1]) + 4 * half;
-                    __bf16 *zl = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + tid) * 2 + 1]) + 4 * half;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) zh[i] = zl[i] = (__bf16)0.0f;
-                }
-            }
-            // weights: this thread's 16 nibble bytes hold column cl = 2*half + (wq>>1)
-            const int cl = 2 * half + (wq >> 1);
-            uint32_t sc[2], mn[2];
-            q4k_fields((uint32_t)ws.hdr[1], (uint32_t)ws.hdr[2], (uint32_t)ws.hdr[3], 2 * cl, 2, sc, mn);
-            v4i hl, ll, hh, lh;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t word = (uint32_t)ws.q[e];
+            constexpr int H = B;  // half of the superblock
+            const int par = sblk & 1, ring = (sblk >> 1) & 1;
+            const int cl = 2 * H + (wq >> 1);  // nibble column: 32-sub-blocks 2cl (low), 2cl+1 (high)
+            if constexpr (S == 0) {
+                // alpha_j = d_a * (bsums[2j] + bsums[2j+1]), j = 4*H + s_j.  An
+                // even superblock also clears its odd partner's entry (which
+                // stays zero if the row ends there); an odd one rewrites its own.
+                const int b = (int)(int16_t)(R.bs & 0xFFFF) + (int)(int16_t)(R.bs >> 16);
+                __bf16 hi, lo;
+                split_bf16(R.da * (float)b, hi, lo);
+                const int e = 4 * H + s_j;
+                __bf16 *ah = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + s_row) * 2]);
+                __bf16 *al = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + s_row) * 2]);
+                ah[8 * par + e] = hi;
+                al[8 * par + e] = lo;
+                ah[8 + e] = par ? hi : (__bf16)0.0f;
+                al[8 + e] = par ? lo : (__bf16)0.0f;
+            } else if constexpr (S == 1) {
+                q4k_fields((uint32_t)R.hdr[1], (uint32_t)R.hdr[2], (uint32_t)R.hdr[3], 2 * cl, 2, T.sc, T.mn);
+            } else if constexpr (S >= 2 && S <= 5) {
+                constexpr int e = S - 2;
+                const uint32_t word = (uint32_t)R.q[e];
                 uint32_t dh, dl;
-                q4k_digits(word & 0x0F0F0F0Fu, sc[0], dh, dl);
-                hl[e] = (int)dh;
-                ll[e] = (int)dl;
-                q4k_digits((word >> 4) & 0x0F0F0F0Fu, sc[1], dh, dl);
-                hh[e] = (int)dh;
-                lh[e] = (int)dl;
+                q4k_digits(word & 0x0F0F0F0Fu, T.sc[0], dh, dl);
+                T.hl[e] = (int)dh;
+                T.ll[e] = (int)dl;
+                q4k_digits((word >> 4) & 0x0F0F0F0Fu, T.sc[1], dh, dl);
+                T.hh[e] = (int)dh;
+                T.lh[e] = (int)dl;
+            } else if constexpr (S == 6) {
+                const int pl = 4 * (wq >> 1) + (wq & 1);  // piece of the low nibbles
+                *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl)) = T.hl;
+                *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl)) = T.ll;
+                *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl + 2)) = T.hh;
+                *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl + 2)) = T.lh;
+                s_dw[slot * BN + w_nl] = f16_bits_to_f32((uint32_t)R.hdr[0]);
+            } else {
+                // beta_j = -dmin * m_j for j = 4*H + wq (field 2*cl + (wq & 1))
+                const float dmin = f16_bits_to_f32((uint32_t)R.hdr[0] >> 16);
+                const uint32_t mj = (wq & 1) ? T.mn[1] : T.mn[0];
+                __bf16 hi, lo;
+                split_bf16(-dmin * (float)mj, hi, lo);
+                const int e = 4 * H + wq;
+                __bf16 *bh = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 0) * BN + w_nl) * 2]);
+                __bf16 *bl = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 1) * BN + w_nl) * 2]);
+                bh[8 * par + e] = hi;
+                bl[8 * par + e] = lo;
+                bh[8 + e] = par ? hi : (__bf16)0.0f;
+                bl[8 + e] = par ? lo : (__bf16)0.0f;
             }
-            const int pl = 4 * (wq >> 1) + (wq & 1);   // piece of the low nibbles
-            *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl)) = hl;
-            *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl)) = ll;
-            *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl + 2)) = hh;
-            *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl + 2)) = lh;
-            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32((uint32_t)ws.hdr[0]);
-            if ((wq & 1) == 0) {
-                const float dmin = f16_bits_to_f32((uint32_t)ws.hdr[0] >> 16);
-                __bf16 *bh = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 0) * BN + w_nl) * 2 + par]) + 2 * cl;
-                __bf16 *bl = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 1) * BN + w_nl) * 2 + par]) + 2 * cl;
+        } else if constexpr (Q6) {
+            // piece S unpacks dword e = S & 1 of quarter u = S >> 1: weights
+            // 128H + 32u + 8wq + 4e .. +4, sub-block scale 8H + 2u + (wq >> 1)
+            constexpr int u = S >> 1, e = S & 1;
+            if constexpr (S == 0) {
+                const uint32_t sh = (uint32_t)(uintptr_t)(w_tile + w_off + (int64_t)sblk * 210) & 3u;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    __bf16 hi, lo;
-                    split_bf16(-dmin * (float)mn[i], hi, lo);
-                    bh[i] = hi;
-                    bl[i] = lo;
-                }
-                if (zero_odd) {
-                    __bf16 *zh = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 0) * BN + w_nl) * 2 + 1]) + 2 * cl;
-                    __bf16 *zl = reinterpret_cast<__bf16 *>(&s_beta[((ring * 2 + 1) * BN + w_nl) * 2 + 1]) + 2 * cl;
-                    zh[0] = zh[1] = zl[0] = zl[1] = (__bf16)0.0f;
-                }
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        T.ql[j][k] = __builtin_amdgcn_alignbyte(R.ql[3 * j + k + 1], R.ql[3 * j + k], sh);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) T.qh[k] = __builtin_amdgcn_alignbyte(R.qh[k + 1], R.qh[k], sh);
+                T.S0 = __builtin_amdgcn_alignbyte(R.sc[1], R.sc[0], sh);
+                T.S1 = __builtin_amdgcn_alignbyte(R.sc[2], R.sc[1], sh);
             }
-        } else if constexpr (FMT == FMT_Q6K) {
-            const int u = wq;
-            const uint32_t sh = ws.shift;
-            const int sc_lo = (int)(int8_t)(ws.scbits & 0xFF), sc_hi = (int)(int8_t)(ws.scbits >> 8);
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int sc = g ? sc_hi : sc_lo;
-                v4i vh, vl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t4 = 4 * g + e;
-                    const uint32_t qlw = sh ? __builtin_amdgcn_alignbyte(ws.ql[t4 + 1], ws.ql[t4], 2) : ws.ql[t4];
-                    const uint32_t qhw = sh ? __builtin_amdgcn_alignbyte(ws.qh[t4 + 1], ws.qh[t4], 2) : ws.qh[t4];
-                    const uint32_t lo4 = (qlw >> (4 * (u >> 1))) & 0x0F0F0F0Fu;
-                    const uint32_t hi2 = (qhw >> (2 * u)) & 0x03030303u;
-                    uint32_t dh, dl;
-                    q6k_digits(lo4 | (hi2 << 4), sc, dh, dl);
-                    vh[e] = (int)dh;
-                    vl[e] = (int)dl;
-                }
-                *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * u + g)) = vh;
-                *reinterpret_cast<v4i *>(p1 + swz(w_nl, 2 * u + g)) = vl;
+            const uint32_t Sw = (u < 2) ? T.S0 : T.S1;
+            const int sc = __builtin_amdgcn_sbfe((int)Sw, (int)(16u * (u & 1) + 8u * (uint32_t)(wq >> 1)), 8);
+            const uint32_t qlw = T.ql[u & 1][e];
+            const uint32_t lo4 = (u < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
+            const uint32_t hi2 = (T.qh[e] >> (2 * u)) & 0x03030303u;
+            q6k_digits(lo4 | (hi2 << 4), sc, T.vh[e], T.vl[e]);
+            if constexpr (e == 1) {
+                const int off = w_nl * MPITCH + 32 * u + 8 * wq;
+                *reinterpret_cast<uint2 *>(p0 + off) = make_uint2(T.vh[0], T.vh[1]);
+                *reinterpret_cast<uint2 *>(p1 + off) = make_uint2(T.vl[0], T.vl[1]);
             }
-            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32(ws.dbits);
+            if constexpr (S == 7) s_dw[slot * BN + w_nl] = f16_bits_to_f32(R.d);
         } else {
-            v4i pieces[2];
-            switch (__builtin_amdgcn_readfirstlane(wq)) {  // wave-uniform
-                case 0: tq_unpack_part<0>(ws.w, pieces); break;
-                case 1: tq_unpack_part<1>(ws.w, pieces); break;
-                case 2: tq_unpack_part<2>(ws.w, pieces); break;
-                default: tq_unpack_part<3>(ws.w, pieces); break;
+            // trit byte v -> five int8 trits from the table; byte b of this
+            // thread's window fills row bytes 5*(tq_off + b) .. +5
+            if constexpr (S <= 1) {
+#pragma unroll
+                for (int b = 4 * S; b < 4 * S + 4; ++b) {
+                    const uint32_t v = (R.w[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+                    const uint2 t = *reinterpret_cast<const uint2 *>(&s_lut[2 * v]);
+                    T.lo[b] = t.x;
+                    T.hi[b] = t.y;
+                }
+            } else if constexpr (S == 3 || S == 4) {
+                constexpr int g = S - 3, b = 4 * g;
+                uint32_t o[5];
+                o[0] = T.lo[b];
+                o[1] = perm_b32(T.lo[b + 1], T.hi[b], 0x06050400u);
+                o[2] = __builtin_amdgcn_alignbyte(T.hi[b + 1], T.lo[b + 1], 3) | (T.lo[b + 2] << 16);
+                o[3] = __builtin_amdgcn_alignbyte(T.hi[b + 2], T.lo[b + 2], 2) | (T.lo[b + 3] << 24);
+                o[4] = __builtin_amdgcn_alignbyte(T.hi[b + 3], T.lo[b + 3], 1);
+                uint32_t *dst = reinterpret_cast<uint32_t *>(p0 + w_nl * MPITCH + 5 * tq_off) + 5 * g;
+#pragma unroll
+                for (int i = 0; i < 5; ++i) dst[i] = o[i];
+            } else if constexpr (S == 5) {
+                // d is bytes 26..27, the high half of the last quarter's second dword
+                float *dwp = (wq == 3) ? &s_dw[slot * BN + w_nl] : &s_dw[4 * BN + lane];
+                *dwp = f16_bits_to_f32(R.w[1] >> 16);
             }
-            *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * wq)) = pieces[0];
-            *reinterpret_cast<v4i *>(p0 + swz(w_nl, 2 * wq + 1)) = pieces[1];
-            if (wq == 0) s_dw[buf * BN + w_nl] = f16_bits_to_f32(ws.w[6] >> 16);
         }
     };
 
     v16f acc_f[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_f[i][r] = 0.0f;
     v16i acc[NDIG][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        acc_f[i] = v16f{};
+#pragma unroll
+        for (int dg = 0; dg < NDIG; ++dg) acc[dg][i] = v16i{};
+    }
 
-    // compute chunk c (c & 1 == P) from LDS buffer P
-    auto compute = [&](auto PP, int c) {
-        constexpr int buf = decltype(PP)::value;
-        const int8_t *sa = s_a + buf * ABUF;
-        const int8_t *sw = s_w + buf * WBUF;
-        constexpr bool first = (CPS == 1) || (buf == 0);
-        constexpr bool last = (CPS == 1) || (buf == 1);
+    constexpr int KS = KCH / 32;  // MFMA K-steps per chunk
+    // weight fragments of K-step ks (shared by both m-tiles)
+    auto ld_b = [&](auto BB_, v4i (&Bv)[KS][NDIG], int ks) KQ_INLINE {
+        constexpr int B = decltype(BB_)::value;
+        const int8_t *sw = B ? s_w1 : s_w0;
 #pragma unroll
-        for (int ks = 0; ks < KCH / 32; ++ks) {
-            const int pc = 2 * ks + kgrp;
-            v4i A[2], B[NDIG];
+        for (int dg = 0; dg < NDIG; ++dg)
+            Bv[ks][dg] = *reinterpret_cast<const v4i *>(sw + dg * PLANE + swz(32 * wn + lrow, 2 * ks + kgrp));
+    };
+    // activation fragment of m-tile I, K-step ks
+    auto ld_a = [&](auto BB_, v4i (&Av)[2][KS], int I, int ks) KQ_INLINE {
+        constexpr int B = decltype(BB_)::value;
+        const int8_t *sa = B ? s_a1 : s_a0;
+        Av[I][ks] = *reinterpret_cast<const v4i *>(sa + swz(64 * wm + 32 * I + lrow, 2 * ks + kgrp));
+    };
+    // one int8 MFMA: m-tile I, K-step ks, digit plane dg; ks == 0 of a
+    // restarting chunk starts from zero
+    auto mfma_one = [&](auto II, auto KK, auto DD, auto FF, const v4i (&Av)[2][KS],
+                        const v4i (&Bv)[KS][NDIG]) KQ_INLINE {
+        constexpr int I = decltype(II)::value, ks = decltype(KK)::value, dg = decltype(DD)::value;
+        constexpr bool ZERO = decltype(FF)::value && ks == 0;
+        acc[dg][I] = ZERO ? mfma_i8_32x32x32(Av[I][ks], Bv[ks][dg], v16i{})
+                          : mfma_i8_32x32x32(Av[I][ks], Bv[ks][dg], acc[dg][I]);
+    };
+
+    // ---- fold of m-tile I of scale block sb: out += float(T) * d_w[n] * d_a[m]
+    struct FoldTmp {
+        float dw;
+        v4f da[4];
+    };
+    struct MinTmp {
+        v8bf ah, al, bh, bl;  // Q4_K min-term operands
+    };
+    auto fold_load = [&](auto II, int sb, FoldTmp &F) KQ_INLINE {
+        constexpr int I = decltype(II)::value;
+        const int slot = sb & 3;
+        F.dw = s_dw[slot * BN + 32 * wn + lrow];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                A[i] = *reinterpret_cast<const v4i *>(sa + swz(64 * wm + 32 * i + lrow, pc));
+        for (int r4 = 0; r4 < 4; ++r4)
+            F.da[r4] = *reinterpret_cast<const v4f *>(&s_da[slot * BM + 64 * wm + 32 * I + 8 * r4 + 4 * kgrp]);
+    };
+    auto min_load = [&](auto II, int sb, MinTmp &Mt) KQ_INLINE {
+        constexpr int I = decltype(II)::value;
+        const int ring = (sb >> 1) & 1;
+        const int col = 32 * wn + lrow;
+        const int row = 64 * wm + 32 * I + lrow;
+        Mt.bh = s_beta[((ring * 2 + 0) * BN + col) * 2 + kgrp];
+        Mt.bl = s_beta[((ring * 2 + 1) * BN + col) * 2 + kgrp];
+        Mt.ah = s_alpha[((ring * 2 + 0) * BM + row) * 2 + kgrp];
+        Mt.al = s_alpha[((ring * 2 + 1) * BM + row) * 2 + kgrp];
+    };
+    // piece S of NP: outputs r in [S*16/NP, (S+1)*16/NP)
+    auto fold_piece = [&](auto II, auto SS, auto NPC, const FoldTmp &F) KQ_INLINE {
+        constexpr int I = decltype(II)::value, S = decltype(SS)::value, NP = decltype(NPC)::value;
 #pragma unroll
-            for (int dg = 0; dg < NDIG; ++dg)
-                B[dg] = *reinterpret_cast<const v4i *>(sw + dg * BN * MPITCH + swz(32 * wn + lrow, pc));
-#pragma unroll
-            for (int dg = 0; dg < NDIG; ++dg)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    acc[dg][i] = (first && ks == 0) ? mfma_i8_32x32x32(A[i], B[dg], v16i{})
-                                                    : mfma_i8_32x32x32(A[i], B[dg], acc[dg][i]);
+        for (int r = S * 16 / NP; r < (S + 1) * 16 / NP; ++r) {
+            int T;
+            if constexpr (NDIG == 2)
+                T = (acc[0][I][r] << Fmt<FMT>::SHIFT) + acc[1][I][r];
+            else
+                T = acc[0][I][r];
+            acc_f[I][r] = fmaf((float)T * F.dw, F.da[r >> 2][r & 3], acc_f[I][r]);
         }
-        if constexpr (last) {
-            // fold: out += float(T) * d_w[n] * d_a[m]
-            const float dwv = s_dw[buf * BN + 32 * wn + lrow];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const v4f dav = *reinterpret_cast<const v4f *>(&s_da[buf * BM + 64 * wm + 32 * i + 8 * r4 + 4 * kgrp]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * r4 + e;
-                        int T;
-                        if constexpr (NDIG == 2)
-                            T = (acc[0][i][r] << Fmt<FMT>::SHIFT) + acc[1][i][r];
-                        else
-                            T = acc[0][i][r];
-                        acc_f[i][r] = fmaf((float)T * dwv, dav[e], acc_f[i][r]);
-                    }
-                }
-            }
-        }
-        if constexpr (Q4) {
-            const int sblk = c / CPS;
-            // after the last chunk of each superblock pair (or of the row)
-            if (last && ((sblk & 1) || sblk == a.nchunks - 1)) {
-                const int ring = (sblk >> 1) & 1;
-                const int col = 32 * wn + lrow;
-                const v8bf bh = s_beta[((ring * 2 + 0) * BN + col) * 2 + kgrp];
-                const v8bf bl = s_beta[((ring * 2 + 1) * BN + col) * 2 + kgrp];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = 64 * wm + 32 * i + lrow;
-                    const v8bf ah = s_alpha[((ring * 2 + 0) * BM + row) * 2 + kgrp];
-                    const v8bf al = s_alpha[((ring * 2 + 1) * BM + row) * 2 + kgrp];
-                    acc_f[i] = mfma_bf16_32x32x16(ah, bh, acc_f[i]);
-                    acc_f[i] = mfma_bf16_32x32x16(ah, bl, acc_f[i]);
-                    acc_f[i] = mfma_bf16_32x32x16(al, bh, acc_f[i]);
-                }
-            }
+    };
+    // Q4_K min term of a superblock pair: out += alpha . beta (hi/lo split)
+    auto fold_min = [&](auto II, const MinTmp &Mt) KQ_INLINE {
+        constexpr int I = decltype(II)::value;
+        acc_f[I] = mfma_bf16_32x32x16(Mt.ah, Mt.bh, acc_f[I]);
+        acc_f[I] = mfma_bf16_32x32x16(Mt.ah, Mt.bl, acc_f[I]);
+        acc_f[I] = mfma_bf16_32x32x16(Mt.al, Mt.bh, acc_f[I]);
+    };
+    auto fold_all = [&](auto II, int sb, auto MINC) KQ_INLINE {
+        FoldTmp F;
+        fold_load(II, sb, F);
+        static_for<0, 4>([&](auto S) KQ_INLINE { fold_piece(II, S, IC<4>{}, F); });
+        if constexpr (decltype(MINC)::value) {
+            MinTmp Mt;
+            min_load(II, sb, Mt);
+            fold_min(II, Mt);
         }
     };
 
-    // prologue: chunks 0..RING-1 in flight, chunk 0 staged
-    // prefetches past the last chunk re-load the last chunk (harmless) so the
-    // number of loads in flight is the same on every path
-    const int clast = max(nch - 1, 0);
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
+    // ---- prologue ---------------------------------------------------------
+    // slot 3 and the min-term operands start zeroed: the first iteration
+    // folds tile 1 of a "scale block -1" whose accumulators are zero
+    for (int i = tid; i < BM; i += MNT) s_da[3 * BM + i] = 0.0f;
+    for (int i = tid; i < BN; i += MNT) s_dw[3 * BN + i] = 0.0f;
+    if constexpr (Q4) {
+        for (int i = tid; i < 2 * 2 * BM * 2; i += MNT) s_alpha[i] = v8bf{};
+        for (int i = tid; i < 2 * 2 * BN * 2; i += MNT) s_beta[i] = v8bf{};
+    }
+    if constexpr (TQ) {
+        if (tid < 256) {
+            uint32_t lo, hi;
+            tq_lut_entry((uint32_t)tid, lo, hi);
+            *reinterpret_cast<uint2 *>(&s_lut[2 * tid]) = make_uint2(lo, hi);
+        }
+    }
     if (nch > 0) {
-        prefetch(rg[0], 0);
-        prefetch(rg[1], min(1, clast));
-        stage(P0{}, rg[0], 0);
+        prefetch(IC<0>{}, rg[0], 0);
+        prefetch(IC<1>{}, rg[1], clampc(1));
     }
     __syncthreads();
-    const bool stage_first = (wm == 0);
-    // one iteration (c & 1 == P): refill the register set that held chunk c
-    // with chunk c+2, stage chunk c+1 into the other LDS buffer, compute
-    // chunk c, barrier.  The two waves of a SIMD take stage and compute in
-    // opposite order.
-    auto iteration = [&](auto PP, int c) {
-        constexpr int P = decltype(PP)::value;
-        using Q = std::integral_constant<int, 1 - P>;
-        prefetch(rg[P], min(c + 2, clast));
-        if (stage_first) {
-            if (c + 1 < nch) stage(Q{}, rg[1 - P], c + 1);
-            compute(PP, c);
+    if (nch > 0) {
+        StageTmp T;
+        static_for<0, 8>([&](auto S) KQ_INLINE { stage_piece(IC<0>{}, S, rg[0], 0, T); });
+    }
+    __syncthreads();
+
+    // ---- one iteration, chunk c with compile-time phase U (c % 4 for
+    // Q4_K/Q6_K, c % 2 for ternary).  The body is a fixed sequence of slots
+    // separated by scheduling fences: each slot issues one MFMA plus a share
+    // of the unpack or fold work and of the fragment reads for later slots.
+    auto iteration = [&](auto UU, int c) KQ_INLINE {
+        constexpr int U = decltype(UU)::value;
+        constexpr int P = U & 1;  // LDS buffer and register set of chunk c
+        using BP = IC<P>;
+        using BQ = IC<1 - P>;
+        const int cs = clampc(c + 1);
+        const ChunkRegs<FMT> &Rs = rg[1 - P];
+        prefetch(BP{}, rg[P], clampc(c + 2));
+        v4i Bv[KS][NDIG], Av[2][KS];
+        StageTmp T;
+        ld_b(BP{}, Bv, 0);
+        ld_b(BP{}, Bv, 1);
+        ld_a(BP{}, Av, 0, 0);
+        ld_a(BP{}, Av, 0, 1);
+        if constexpr (TQ) {
+            FoldTmp F1, F0;
+            fold_load(IC<1>{}, c - 1, F1);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 4>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<0>{}, S, IC<0>{}, std::true_type{}, Av, Bv);
+                if constexpr (s == 0) { ld_b(BP{}, Bv, 2); ld_b(BP{}, Bv, 3); }
+                if constexpr (s == 1) ld_a(BP{}, Av, 0, 2);
+                if constexpr (s == 2) ld_a(BP{}, Av, 0, 3);
+                if constexpr (s == 3) {
+                    ld_a(BP{}, Av, 1, 0);
+                    ld_a(BP{}, Av, 1, 1);
+                    fold_load(IC<0>{}, c, F0);
+                }
+                stage_piece(BQ{}, S, Rs, cs, T);
+                fold_piece(IC<1>{}, S, IC<4>{}, F1);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            static_for<0, 4>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<1>{}, S, IC<0>{}, std::true_type{}, Av, Bv);
+                if constexpr (s < 2) ld_a(BP{}, Av, 1, 2 + s);
+                stage_piece(BQ{}, IC<4 + s>{}, Rs, cs, T);
+                fold_piece(IC<0>{}, S, IC<4>{}, F0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else if constexpr (P == 0) {
+            // first chunk of superblock c/2: fold tile 1 of the superblock
+            // before it (odd when U == 0) under tile 0's MFMAs, then restart
+            // tile 1 under the unpack
+            constexpr bool MIN = Q4 && U == 0;
+            FoldTmp F;
+            MinTmp Mt;
+            fold_load(IC<1>{}, c / 2 - 1, F);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 8>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<0>{}, IC<(s >> 1)>{}, IC<(s & 1)>{}, std::true_type{}, Av, Bv);
+                if constexpr (s == 0) ld_b(BP{}, Bv, 2);
+                if constexpr (s == 1) ld_a(BP{}, Av, 0, 2);
+                if constexpr (s == 2) ld_b(BP{}, Bv, 3);
+                if constexpr (s == 3) ld_a(BP{}, Av, 0, 3);
+                if constexpr (s >= 4) ld_a(BP{}, Av, 1, s - 4);
+                if constexpr (MIN && s == 5) min_load(IC<1>{}, c / 2 - 1, Mt);
+                fold_piece(IC<1>{}, S, IC<8>{}, F);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (MIN) {
+                fold_min(IC<1>{}, Mt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            static_for<0, 8>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<1>{}, IC<(s >> 1)>{}, IC<(s & 1)>{}, std::true_type{}, Av, Bv);
+                stage_piece(BQ{}, S, Rs, cs, T);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else {
-            compute(PP, c);
-            if (c + 1 < nch) stage(Q{}, rg[1 - P], c + 1);
+            // second chunk: tile 0's MFMAs under the unpack, then fold tile 0
+            // (min term when the superblock is odd, U == 3) under tile 1's
+            constexpr bool MIN = Q4 && U == 3;
+            FoldTmp F;
+            MinTmp Mt;
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 8>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<0>{}, IC<(s >> 1)>{}, IC<(s & 1)>{}, std::false_type{}, Av, Bv);
+                if constexpr (s == 0) ld_b(BP{}, Bv, 2);
+                if constexpr (s == 1) ld_a(BP{}, Av, 0, 2);
+                if constexpr (s == 2) ld_b(BP{}, Bv, 3);
+                if constexpr (s == 3) ld_a(BP{}, Av, 0, 3);
+                if constexpr (s >= 4) ld_a(BP{}, Av, 1, s - 4);
+                if constexpr (s == 5) fold_load(IC<0>{}, c / 2, F);
+                stage_piece(BQ{}, S, Rs, cs, T);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            static_for<0, 8>([&](auto S) KQ_INLINE {
+                constexpr int s = decltype(S)::value;
+                mfma_one(IC<1>{}, IC<(s >> 1)>{}, IC<(s & 1)>{}, std::false_type{}, Av, Bv);
+                if constexpr (MIN && s == 5) min_load(IC<0>{}, c / 2, Mt);
+                fold_piece(IC<0>{}, S, IC<8>{}, F);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (MIN) fold_min(IC<0>{}, Mt);
         }
         __syncthreads();
     };
-    for (int c = 0; c < nch; c += 2) {
-        iteration(P0{}, c);
-        if (c + 1 < nch) iteration(P1{}, c + 1);
+
+    if constexpr (CPS == 2) {
+        int c = 0;
+        for (; c + 4 <= nch; c += 4) {
+            iteration(IC<0>{}, c);
+            iteration(IC<1>{}, c + 1);
+            iteration(IC<2>{}, c + 2);
+            iteration(IC<3>{}, c + 3);
+        }
+        if (c < nch) {  // nch is even
+            iteration(IC<0>{}, c);
+            iteration(IC<1>{}, c + 1);
+        }
+        if (nch > 0) {
+            const int lastb = nch / 2 - 1;
+            fold_all(IC<1>{}, lastb, std::integral_constant<bool, Q4>{});
+            if constexpr (Q4) {
+                if ((lastb & 1) == 0) {
+                    // an even last superblock: its pair's min term is still due for tile 0
+                    MinTmp Mt;
+                    min_load(IC<0>{}, lastb, Mt);
+                    fold_min(IC<0>{}, Mt);
+                }
+            }
+        }
+    } else {
+        int c = 0;
+        for (; c + 2 <= nch; c += 2) {
+            iteration(IC<0>{}, c);
+            iteration(IC<1>{}, c + 1);
+        }
+        if (c < nch) iteration(IC<0>{}, c);
+        if (nch > 0) fold_all(IC<1>{}, nch - 1, std::false_type{});
     }
+
 
     // ---- epilogue: fp32 stores (unmasked when the whole tile is inside) ----
     float *out = reinterpret_cast<float *>(a.out);
