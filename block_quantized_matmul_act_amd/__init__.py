@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libkq.so")
 
 KQ_Q4_K, KQ_Q6_K, KQ_TQ = 1, 2, 3
 KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
-KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS = 0, 1, 2
+KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
 KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
     -1, -2, -3, -4, -5, -6)
@@ -167,17 +167,26 @@ def quantize_act(x, act_fmt=KQ_ACT_Q8_K, stream=None):
 
 
 def act_views(a_q8, act_fmt, M, K):
-    """(qs int8 [M][K], d fp32 [M][K/bs], bsums int16 [M][K/16] or None) views of a buffer."""
+    """(qs int8 [M][K], d fp32 [M][K/bs], bsums int16 [M][K/16] or None) views of a
+    buffer.  d is stored block-major ([K/bs][M]); the view is its transpose."""
     import torch
     bs = 256 if act_fmt == KQ_ACT_Q8_K else 128
     od = kq_act_section_offset(act_fmt, KQ_SEC_D, M, K)
     qs = a_q8[:M * K].view(torch.int8).view(M, K)
-    d = a_q8[od:od + M * (K // bs) * 4].view(torch.float32).view(M, K // bs)
+    d = a_q8[od:od + M * (K // bs) * 4].view(torch.float32).view(K // bs, M).t()
     bsums = None
     if act_fmt == KQ_ACT_Q8_K:
         ob = kq_act_section_offset(act_fmt, KQ_SEC_BSUMS, M, K)
         bsums = a_q8[ob:ob + M * (K // 16) * 2].view(torch.int16).view(M, K // 16)
     return qs, d, bsums
+
+
+def alpha_view(a_q8, M, K):
+    """The Q8_K alpha section as int16 bit patterns of bf16 values, [K/256][2][M][8]."""
+    import torch
+    oa = kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, M, K)
+    n = (K // 256) * 2 * M * 8
+    return a_q8[oa:oa + 2 * n].view(torch.int16).view(K // 256, 2, M, 8)
 
 
 def gemm(fmt, W, a_q8, M, N, K, out=None, stream=None):

@@ -11,9 +11,9 @@
 
 namespace kq {
 hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_t *bsums,
-                            int64_t M, int64_t K, hipStream_t stream);
+                            uint16_t *alpha, int64_t M, int64_t K, hipStream_t stream);
 hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
-                       const int16_t *bsums, float *out, int M, int N, int K,
+                       const uint16_t *alpha, float *out, int M, int N, int K,
                        hipStream_t stream);
 hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
                           int K, hipStream_t stream);
@@ -56,20 +56,24 @@ int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Section offsets of an activation buffer; false when invalid.
-bool act_layout(int act_fmt, int64_t M, int64_t K, int64_t *off_d, int64_t *off_bs,
-                int64_t *total) {
+struct ActLayout {
+    int64_t d, bsums, alpha, total;  // byte offsets; -1 for absent sections
+};
+bool act_layout(int act_fmt, int64_t M, int64_t K, ActLayout *L) {
     const int bs = bs_of(act_fmt);
     if (!bs || M < 0 || K < 0 || K % bs || M > kMaxDim || K > kMaxDim) return false;
     if (M != 0 && K > kMaxBytes / M) return false;
     const int64_t qs_bytes = align256(M * K);
     const int64_t d_bytes = align256(M * (K / bs) * 4);
-    *off_d = qs_bytes;
+    L->d = qs_bytes;
     if (act_fmt == KQ_ACT_Q8_K) {
-        *off_bs = qs_bytes + d_bytes;
-        *total = *off_bs + align256(M * (K / 16) * 2);
+        L->bsums = qs_bytes + d_bytes;
+        L->alpha = L->bsums + align256(M * (K / 16) * 2);
+        L->total = L->alpha + align256((K / 256) * 2 * M * 8 * 2);
     } else {
-        *off_bs = -1;
-        *total = qs_bytes + d_bytes;
+        L->bsums = -1;
+        L->alpha = -1;
+        L->total = qs_bytes + d_bytes;
     }
     return true;
 }
@@ -88,6 +92,12 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     // grid limits: tiles must fit a 1-D grid
     const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    // the GEMM kernel addresses a 128-row tile of qs or W, the d section and
+    // the alpha section with 32-bit buffer offsets
+    const int64_t lim = (int64_t)1 << 31;
+    if (128 * K >= lim || 128 * (K / qk_of(fmt)) * bb_of(fmt) >= lim ||
+        (K / qk_of(fmt)) * M * 4 >= lim || (K / 256) * 2 * M * 16 >= lim)
+        return KQ_ERR_UNSUPPORTED;
     return 1;  // proceed
 }
 
@@ -108,17 +118,18 @@ size_t kq_weight_bytes(int fmt, int64_t N, int64_t K) {
 }
 
 size_t kq_act_bytes(int act_fmt, int64_t M, int64_t K) {
-    int64_t od, ob, total;
-    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return 0;
-    return (size_t)total;
+    ActLayout L;
+    if (!act_layout(act_fmt, M, K, &L)) return 0;
+    return (size_t)L.total;
 }
 
 int64_t kq_act_section_offset(int act_fmt, int section, int64_t M, int64_t K) {
-    int64_t od, ob, total;
-    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return -1;
+    ActLayout L;
+    if (!act_layout(act_fmt, M, K, &L)) return -1;
     if (section == KQ_SEC_QS) return 0;
-    if (section == KQ_SEC_D) return od;
-    if (section == KQ_SEC_BSUMS) return ob;
+    if (section == KQ_SEC_D) return L.d;
+    if (section == KQ_SEC_BSUMS) return L.bsums;
+    if (section == KQ_SEC_ALPHA) return L.alpha;
     return -1;
 }
 
@@ -132,17 +143,17 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
                     hipStream_t stream) {
     const int bs = bs_of(act_fmt);
     if (!bs) return KQ_ERR_FMT;
-    int64_t od, ob, total;
-    if (!act_layout(act_fmt, M, K, &od, &ob, &total)) return KQ_ERR_SHAPE;
+    ActLayout L;
+    if (!act_layout(act_fmt, M, K, &L)) return KQ_ERR_SHAPE;
     if (M == 0 || K == 0) return KQ_OK;
     if (!x || !a_q8) return KQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(a_q8)) return KQ_ERR_ALIGN;
     if ((M * (K / bs) * (bs / 4) + 255) / 256 > INT32_MAX) return KQ_ERR_UNSUPPORTED;
     char *base = static_cast<char *>(a_q8);
-    hipError_t e = kq::launch_quant_act(bs, x, reinterpret_cast<int8_t *>(base),
-                                        reinterpret_cast<float *>(base + od),
-                                        ob >= 0 ? reinterpret_cast<int16_t *>(base + ob) : nullptr,
-                                        M, K, stream);
+    hipError_t e = kq::launch_quant_act(
+        bs, x, reinterpret_cast<int8_t *>(base), reinterpret_cast<float *>(base + L.d),
+        L.bsums >= 0 ? reinterpret_cast<int16_t *>(base + L.bsums) : nullptr,
+        L.alpha >= 0 ? reinterpret_cast<uint16_t *>(base + L.alpha) : nullptr, M, K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
     g_count[act_fmt == KQ_ACT_Q8_K ? V_QUANT_Q8K : V_QUANT_Q8_128].fetch_add(1);
     return KQ_OK;
@@ -158,13 +169,13 @@ int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int6
             float *out, hipStream_t stream) {
     int rc = check_gemm(fmt, W, a_q8, M, N, K, out);
     if (rc <= 0) return rc;
-    int64_t od, ob, total;
-    act_layout(kq_act_fmt_for(fmt), M, K, &od, &ob, &total);
+    ActLayout L;
+    act_layout(kq_act_fmt_for(fmt), M, K, &L);
     const char *base = static_cast<const char *>(a_q8);
-    hipError_t e = kq::launch_gemm(fmt, W, reinterpret_cast<const int8_t *>(base),
-                                   reinterpret_cast<const float *>(base + od),
-                                   ob >= 0 ? reinterpret_cast<const int16_t *>(base + ob) : nullptr,
-                                   out, (int)M, (int)N, (int)K, stream);
+    hipError_t e = kq::launch_gemm(
+        fmt, W, reinterpret_cast<const int8_t *>(base), reinterpret_cast<const float *>(base + L.d),
+        L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr, out, (int)M,
+        (int)N, (int)K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
     g_count[variant_for(fmt)].fetch_add(1);
     return KQ_OK;

@@ -21,6 +21,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 
 // Row of the 32x32 MFMA result held by register r of lane l.
 __device__ __forceinline__ int mfma32_row(int r, int lane) {

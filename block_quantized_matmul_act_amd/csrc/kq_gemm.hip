@@ -19,11 +19,12 @@
 //     Two MFMA streams accumulate the two planes over the whole superblock
 //     in int32, so the fp32 fold runs once per superblock per output instead
 //     of once per sub-block.
-//   * Q4_K mins: sum_j m_j * B_j (B_j = sub-block sums of the activations,
-//     from the stored int16 bsums) is folded as -dmin*m_j x d_a*B_j through a
-//     bf16 MFMA with hi/lo-split operands (~16 significant bits each),
-//     accumulating straight into the fp32 output registers; two superblocks
-//     share one K=16 MFMA (one per k-group).
+//   * Q4_K mins: sum_j m_j * B_j (B_j = sub-block sums of the activations)
+//     is folded as -dmin*m_j x d_a*B_j through a bf16 MFMA with hi/lo-split
+//     operands (~16 significant bits each), accumulating straight into the
+//     fp32 output registers; two superblocks share one K=16 MFMA (one per
+//     k-group).  The activation operand d_a*B_j comes precomputed from the
+//     quantizer (the alpha section).
 //   * Rows >= M and >= N are never read: their LDS rows are zero-filled and
 //     the epilogue masks the stores (the ragged-tail staging clamp of
 //     vllm.cpp PR 3036).  No wave leaves before a barrier.
@@ -59,8 +60,8 @@ constexpr int PITCH = KC + 16;  // LDS row pitch in bytes (16-byte skew against 
 struct GemmArgs {
     const uint8_t *W;
     const int8_t *qs;       // activation values  [M][K]
-    const float *da;        // activation scales  [M][K/ABS]
-    const int16_t *bsums;   // activation sums    [M][K/16]  (Q8_K only)
+    const float *da;        // activation scales  [K/ABS][M] (block-major)
+    const uint16_t *alpha;  // Q4_K min operand   [K/256][2][M][8] bf16 (Q8_K only)
     void *out;              // fp32 [M][N], or int32 [M][N][K/SUB] for the sub-sum kernel
     int M, N, K;
     int nchunks;            // K / KC (ternary: K / 128 blocks rounded up to chunks)
@@ -346,8 +347,8 @@ template <>
 struct ChunkRegs<FMT_Q4K> {
     v4i act[2];
     float da;
-    uint32_t bs;  // the two int16 activation sums of this thread's 32-sub-block
-    v4i hdr;      // d, dmin, 12 scale bytes
+    uint32_t al;  // 4 bytes of the alpha section
+    v4i hdr;      // d, dmin, 12 scale bytes (loaded with the superblock's first chunk)
     v4i q;        // 16 nibble bytes
 };
 template <>
@@ -358,6 +359,7 @@ struct ChunkRegs<FMT_Q6K> {
     uint32_t qh[3];  // one 8-byte run of qh
     uint32_t sc[3];  // 8 scale bytes
     uint32_t d;
+    uint32_t sh;     // block start mod 4 (0 or 2)
 };
 template <>
 struct ChunkRegs<FMT_TQ> {
@@ -419,26 +421,37 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     const int wm = wave >> 2, wn = wave & 3;
 
     // ---- staging roles --------------------------------------------------
+    // Every global read goes through a buffer resource of this tile (base in
+    // SGPRs, 32-bit lane offsets fixed for the whole loop, the chunk advance
+    // as a scalar offset), so the loads cost no per-iteration address
+    // arithmetic.  Reads past a resource's end return zero: rows >= M or >= N
+    // of a ragged tile read zeros and their results are never stored.
+    constexpr int RSRC_FLAGS = 0x00020000;  // raw 32-bit dwords, gfx9 family
     // activations: two 16-byte pieces per thread (row a_r0 + 64 i, piece a_pc)
     const int a_pc = tid & 7, a_r0 = tid >> 3;
-    const int8_t *a_tile = a.qs + (int64_t)m0 * K;
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.qs + (int64_t)m0 * K), (short)0, min(M - m0, BM) * K, RSRC_FLAGS);
     uint32_t a_off[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        a_off[i] = (uint32_t)(min(m0 + a_r0 + 64 * i, M - 1) - m0) * (uint32_t)K + 16u * a_pc;
-    // activation scales / sums: thread t owns row t/4 and, for Q4_K, 32-sub-block t%4 of the chunk
+    for (int i = 0; i < 2; ++i) a_off[i] = (uint32_t)(a_r0 + 64 * i) * (uint32_t)K + 16u * a_pc;
+    // activation scales (block-major [nsa][M]) and, for Q4_K, the alpha
+    // section: thread t owns row t/4; of alpha it copies 4 bytes: part
+    // (t%4)/2 (hi/lo), sub-blocks 2*(t%2) .. +1 of the chunk's four
     const int s_row = tid >> 2, s_j = tid & 3;
-    const float *da_tile = a.da + (int64_t)m0 * nsa;
-    const uint32_t s_ml = (uint32_t)(min(m0 + s_row, M - 1) - m0);
-    const uint32_t da_off = s_ml * (uint32_t)nsa;
-    const int16_t *bs_tile = Q4 ? a.bsums + (int64_t)m0 * (K / 16) : nullptr;
-    const uint32_t bs_off = s_ml * (uint32_t)(K / 16) + 2 * s_j;
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)(a.da + m0), (short)0,
+                                                        (nsa * M - m0) * 4, RSRC_FLAGS);
+    const uint32_t d_off = 4u * s_row;
+    const auto rs_al = __builtin_amdgcn_make_buffer_rsrc(
+        Q4 ? (void *)(a.alpha + (int64_t)m0 * 8) : (void *)a.da, (short)0,
+        Q4 ? (a.nchunks * 2 * M - m0) * 16 : 0, RSRC_FLAGS);
+    const uint32_t al_off = (uint32_t)(((s_j >> 1) * M + s_row) * 16 + 4 * (s_j & 1));
     // weights: four threads per row
     const int wq = tid & 3, w_nl = tid >> 2;
-    const int w_n = min(n0 + w_nl, N - 1);
-    const int64_t w_rowbytes = (int64_t)a.nblk * Fmt<FMT>::BB;
-    const uint8_t *w_tile = a.W + (int64_t)n0 * w_rowbytes;
-    const uint32_t w_off = (uint32_t)(w_n - n0) * (uint32_t)w_rowbytes;
+    const int w_rowbytes = a.nblk * Fmt<FMT>::BB;
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.W + (int64_t)n0 * w_rowbytes), (short)0, min(N - n0, BN) * w_rowbytes,
+        RSRC_FLAGS);
+    const uint32_t w_off = (uint32_t)(w_nl * w_rowbytes);
     // ternary: this thread's 8 trit bytes start at byte 8*wq of the block
     // (20 for the last quarter, which decodes bytes 20..27 into row bytes
     // 100..139; bytes 128.. land in the row padding)
@@ -457,36 +470,49 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     // global loads of chunk c (c % 2 == H) into R
     auto prefetch = [&](auto HH, ChunkRegs<FMT> &R, int c) KQ_INLINE {
         constexpr int H = decltype(HH)::value;
-        const int8_t *ab = a_tile + (int64_t)c * KCH;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) R.act[i] = *reinterpret_cast<const v4i *>(ab + a_off[i]);
         const int sblk = c / CPS;
-        R.da = da_tile[da_off + sblk];
-        const uint8_t *blk = w_tile + w_off + (int64_t)sblk * Fmt<FMT>::BB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            R.act[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (int)a_off[i], c * KCH, 0));
+        R.da = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_d, (int)d_off, sblk * M * 4, 0));
+        const int wsoff = sblk * Fmt<FMT>::BB;
         if constexpr (Q4) {
-            R.bs = *reinterpret_cast<const uint32_t *>(bs_tile + bs_off + 16 * sblk + 8 * H);
-            R.hdr = *reinterpret_cast<const v4i *>(blk);
-            R.q = *reinterpret_cast<const v4i *>(blk + 16 + 64 * H + 16 * wq);
+            R.al = __builtin_amdgcn_raw_buffer_load_b32(rs_al, (int)al_off, sblk * 32 * M + 8 * H, 0);
+            if constexpr (H == 0)  // the second chunk reuses the first chunk's header
+                R.hdr = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, (int)w_off, wsoff, 0));
+            R.q = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, (int)(w_off + 16 + 64 * H + 16 * wq), wsoff, 0));
         } else if constexpr (Q6) {
             // the 210-byte block starts 0 or 2 bytes past a dword boundary;
             // every window below lies inside the block or the block before it
-            const uint32_t sh = (uint32_t)(uintptr_t)blk & 3u;
-            const uint8_t *base = blk - sh;
+            // (few wide loads: the address unit's cost is per instruction)
+            const uint32_t o = w_off + (uint32_t)wsoff;
+            const uint32_t sh = o & 3u;
+            const int base = (int)(o - sh);
+            const int bq = base + 8 * wq;
+            R.sh = sh;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-                    R.ql[3 * j + i] = ld_u32(base + 64 * H + 32 * j + 8 * wq + 4 * i);
-#pragma unroll
-            for (int i = 0; i < 3; ++i) R.qh[i] = ld_u32(base + 128 + 32 * H + 8 * wq + 4 * i);
-            R.sc[0] = ld_u32(base + 192 + 8 * H);
-            R.sc[1] = ld_u32(base + 196 + 8 * H);
+            for (int j = 0; j < 2; ++j) {
+                const v3u w3 = __builtin_amdgcn_raw_buffer_load_b96(rs_w, bq, 64 * H + 32 * j, 0);
+                R.ql[3 * j + 0] = w3.x;
+                R.ql[3 * j + 1] = w3.y;
+                R.ql[3 * j + 2] = w3.z;
+            }
+            {
+                const v3u w3 = __builtin_amdgcn_raw_buffer_load_b96(rs_w, bq, 128 + 32 * H, 0);
+                R.qh[0] = w3.x;
+                R.qh[1] = w3.y;
+                R.qh[2] = w3.z;
+            }
+            const v2u s2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, base, 192 + 8 * H, 0);
+            R.sc[0] = s2.x;
+            R.sc[1] = s2.y;
             // third dword only needed when sh == 2; otherwise re-read the second
-            R.sc[2] = ld_u32(base + 200 + 8 * H - (sh ? 0 : 4));
-            R.d = *reinterpret_cast<const unsigned short *>(blk + 208);
+            R.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(rs_w, base + (sh ? 4 : 0), 196 + 8 * H, 0);
+            R.d = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)o, 208, 0);
         } else {
-            R.w[0] = ld_u32(blk + tq_off);
-            R.w[1] = ld_u32(blk + tq_off + 4);
+            const v2u w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(w_off + tq_off), wsoff, 0);
+            R.w[0] = w2.x;
+            R.w[1] = w2.y;
         }
     };
 
@@ -498,7 +524,9 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
         uint32_t ql[2][2], qh[2], S0, S1, vh[2], vl[2];  // Q6_K
         uint32_t lo[8], hi[8];   // ternary table entries
     };
-    auto stage_piece = [&](auto BB_, auto SS, const ChunkRegs<FMT> &R, int c, StageTmp &T) KQ_INLINE {
+    // hdr: the Q4_K header of the chunk's superblock (held from its first chunk)
+    auto stage_piece = [&](auto BB_, auto SS, const ChunkRegs<FMT> &R, const v4i &hdr, int c,
+                           StageTmp &T) KQ_INLINE {
         constexpr int B = decltype(BB_)::value;
         constexpr int S = decltype(SS)::value;
         int8_t *sa = B ? s_a1 : s_a0;
@@ -517,21 +545,16 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
             const int par = sblk & 1, ring = (sblk >> 1) & 1;
             const int cl = 2 * H + (wq >> 1);  // nibble column: 32-sub-blocks 2cl (low), 2cl+1 (high)
             if constexpr (S == 0) {
-                // alpha_j = d_a * (bsums[2j] + bsums[2j+1]), j = 4*H + s_j.  An
-                // even superblock also clears its odd partner's entry (which
-                // stays zero if the row ends there); an odd one rewrites its own.
-                const int b = (int)(int16_t)(R.bs & 0xFFFF) + (int)(int16_t)(R.bs >> 16);
-                __bf16 hi, lo;
-                split_bf16(R.da * (float)b, hi, lo);
-                const int e = 4 * H + s_j;
-                __bf16 *ah = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 0) * BM + s_row) * 2]);
-                __bf16 *al = reinterpret_cast<__bf16 *>(&s_alpha[((ring * 2 + 1) * BM + s_row) * 2]);
-                ah[8 * par + e] = hi;
-                al[8 * par + e] = lo;
-                ah[8 + e] = par ? hi : (__bf16)0.0f;
-                al[8 + e] = par ? lo : (__bf16)0.0f;
+                // alpha: this thread's 4 bytes (part s_j/2, sub-blocks 4H + 2(s_j%2) .. +1)
+                // go to the superblock's parity slot.  An even superblock also
+                // clears its odd partner's slot (which stays zero if the row ends
+                // there); an odd one writes its own slot twice.
+                char *arow = reinterpret_cast<char *>(&s_alpha[(((ring * 2) + (s_j >> 1)) * BM + s_row) * 2]) +
+                             8 * H + 4 * (s_j & 1);
+                *reinterpret_cast<uint32_t *>(arow + 16 * par) = R.al;
+                *reinterpret_cast<uint32_t *>(arow + 16) = par ? R.al : 0u;
             } else if constexpr (S == 1) {
-                q4k_fields((uint32_t)R.hdr[1], (uint32_t)R.hdr[2], (uint32_t)R.hdr[3], 2 * cl, 2, T.sc, T.mn);
+                q4k_fields((uint32_t)hdr[1], (uint32_t)hdr[2], (uint32_t)hdr[3], 2 * cl, 2, T.sc, T.mn);
             } else if constexpr (S >= 2 && S <= 5) {
                 constexpr int e = S - 2;
                 const uint32_t word = (uint32_t)R.q[e];
@@ -548,10 +571,10 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
                 *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl)) = T.ll;
                 *reinterpret_cast<v4i *>(p0 + swz(w_nl, pl + 2)) = T.hh;
                 *reinterpret_cast<v4i *>(p1 + swz(w_nl, pl + 2)) = T.lh;
-                s_dw[slot * BN + w_nl] = f16_bits_to_f32((uint32_t)R.hdr[0]);
+                s_dw[slot * BN + w_nl] = f16_bits_to_f32((uint32_t)hdr[0]);
             } else {
                 // beta_j = -dmin * m_j for j = 4*H + wq (field 2*cl + (wq & 1))
-                const float dmin = f16_bits_to_f32((uint32_t)R.hdr[0] >> 16);
+                const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
                 const uint32_t mj = (wq & 1) ? T.mn[1] : T.mn[0];
                 __bf16 hi, lo;
                 split_bf16(-dmin * (float)mj, hi, lo);
@@ -568,7 +591,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
             // 128H + 32u + 8wq + 4e .. +4, sub-block scale 8H + 2u + (wq >> 1)
             constexpr int u = S >> 1, e = S & 1;
             if constexpr (S == 0) {
-                const uint32_t sh = (uint32_t)(uintptr_t)(w_tile + w_off + (int64_t)sblk * 210) & 3u;
+                const uint32_t sh = R.sh;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -735,7 +758,9 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     __syncthreads();
     if (nch > 0) {
         StageTmp T;
-        static_for<0, 8>([&](auto S) KQ_INLINE { stage_piece(IC<0>{}, S, rg[0], 0, T); });
+        v4i hdr = v4i{};
+        if constexpr (Q4) hdr = rg[0].hdr;
+        static_for<0, 8>([&](auto S) KQ_INLINE { stage_piece(IC<0>{}, S, rg[0], hdr, 0, T); });
     }
     __syncthreads();
 
@@ -750,6 +775,11 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
         using BQ = IC<1 - P>;
         const int cs = clampc(c + 1);
         const ChunkRegs<FMT> &Rs = rg[1 - P];
+        // Q4_K header of the staged chunk's superblock: in register set 0 either
+        // way (when P == 0 the staged chunk is the superblock's second and set
+        // 0 holds its first, which the prefetch below overwrites)
+        v4i hdr = v4i{};
+        if constexpr (Q4) hdr = rg[0].hdr;
         prefetch(BP{}, rg[P], clampc(c + 2));
         v4i Bv[KS][NDIG], Av[2][KS];
         StageTmp T;
@@ -772,7 +802,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
                     ld_a(BP{}, Av, 1, 1);
                     fold_load(IC<0>{}, c, F0);
                 }
-                stage_piece(BQ{}, S, Rs, cs, T);
+                stage_piece(BQ{}, S, Rs, hdr, cs, T);
                 fold_piece(IC<1>{}, S, IC<4>{}, F1);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -780,7 +810,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
                 constexpr int s = decltype(S)::value;
                 mfma_one(IC<1>{}, S, IC<0>{}, std::true_type{}, Av, Bv);
                 if constexpr (s < 2) ld_a(BP{}, Av, 1, 2 + s);
-                stage_piece(BQ{}, IC<4 + s>{}, Rs, cs, T);
+                stage_piece(BQ{}, IC<4 + s>{}, Rs, hdr, cs, T);
                 fold_piece(IC<0>{}, S, IC<4>{}, F0);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -812,7 +842,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
             static_for<0, 8>([&](auto S) KQ_INLINE {
                 constexpr int s = decltype(S)::value;
                 mfma_one(IC<1>{}, IC<(s >> 1)>{}, IC<(s & 1)>{}, std::true_type{}, Av, Bv);
-                stage_piece(BQ{}, S, Rs, cs, T);
+                stage_piece(BQ{}, S, Rs, hdr, cs, T);
                 __builtin_amdgcn_sched_barrier(0);
             });
         } else {
@@ -831,7 +861,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
                 if constexpr (s == 3) ld_a(BP{}, Av, 0, 3);
                 if constexpr (s >= 4) ld_a(BP{}, Av, 1, s - 4);
                 if constexpr (s == 5) fold_load(IC<0>{}, c / 2, F);
-                stage_piece(BQ{}, S, Rs, cs, T);
+                stage_piece(BQ{}, S, Rs, hdr, cs, T);
                 __builtin_amdgcn_sched_barrier(0);
             });
             static_for<0, 8>([&](auto S) KQ_INLINE {
@@ -1013,13 +1043,13 @@ __global__ __launch_bounds__(64) void subsums_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float *da,
-                          const int16_t *bsums, void *out, int M, int N, int K, int bm,
+                          const uint16_t *alpha, void *out, int M, int N, int K, int bm,
                           int bn) {
     GemmArgs a;
     a.W = (const uint8_t *)W;
     a.qs = qs;
     a.da = da;
-    a.bsums = bsums;
+    a.alpha = alpha;
     a.out = out;
     a.M = M;
     a.N = N;
@@ -1032,9 +1062,9 @@ static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float 
 }
 
 hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
-                       const int16_t *bsums, float *out, int M, int N, int K,
+                       const uint16_t *alpha, float *out, int M, int N, int K,
                        hipStream_t stream) {
-    GemmArgs a = make_args(fmt, W, qs, da, bsums, out, M, N, K, MBM, MBN);
+    GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {
         case FMT_Q4K:

@@ -10,7 +10,11 @@
 // Layout: one block per group of BS/4 lanes, four consecutive values per lane
 // (one 16-byte load), so a 64-lane wave covers one Q8_K block or two Q8_128
 // blocks.  amax is a max-reduction across the group (exact, order-free).
-// The kernel is bound by HBM bandwidth: it reads 4 bytes and writes ~1.14
+// Scales are stored block-major (d[s][m]) so that the GEMM reads the scales
+// of a 128-row tile as one contiguous run.  For Q8_K the kernel also writes
+// the Q4_K min-term operand alpha = d * (sum of 32 qs) as a bf16 hi/lo pair
+// per 32-value sub-block, once per activation instead of once per GEMM tile.
+// The kernel is bound by HBM bandwidth: it reads 4 bytes and writes ~1.2
 // bytes per value.
 #include "kq_device.hpp"
 
@@ -21,8 +25,10 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict_
                                                         int8_t *__restrict__ qs,
                                                         float *__restrict__ d,
                                                         int16_t *__restrict__ bsums,
+                                                        uint16_t *__restrict__ alpha,
                                                         int64_t nblocks_total,
-                                                        int64_t blocks_per_row, int64_t K) {
+                                                        int64_t blocks_per_row, int64_t M,
+                                                        int64_t K) {
     constexpr int LANES = BS / 4;  // lanes per block
     const int lane = threadIdx.x & (LANES - 1);
     const int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
@@ -52,20 +58,32 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict_
         uint32_t packed = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
                           ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
         *reinterpret_cast<uint32_t *>(qs + row * K + col) = packed;
-        if (lane == 0) d[b] = zero ? 0.0f : amax / 127.0f;
     }
+    const int64_t sblk = b % blocks_per_row;
+    const float dv = zero ? 0.0f : amax / 127.0f;
+    if (valid && lane == 0) d[sblk * M + row] = dv;
     if constexpr (BSUMS) {
         // 16 values = 4 lanes; reduce within aligned groups of 4 lanes
         int sum = q0 + q1 + q2 + q3;
         sum += __shfl_xor(sum, 1, 64);
         sum += __shfl_xor(sum, 2, 64);
         if (valid && (lane & 3) == 0) bsums[row * (K / 16) + col / 16] = (int16_t)sum;
+        // 32 values = 8 lanes: alpha_j = d * sum32 in fp32, then a bf16 hi/lo pair
+        const int sum32 = sum + __shfl_xor(sum, 4, 64);
+        const float av = dv * (float)sum32;
+        const __bf16 hi = (__bf16)av;
+        const __bf16 lo = (__bf16)(av - (float)hi);
+        if (valid && (lane & 7) == 0) {
+            const int j = lane >> 3;
+            alpha[((sblk * 2 + 0) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, hi);
+            alpha[((sblk * 2 + 1) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, lo);
+        }
     }
 }
 
 // Host-side launchers (called from kq_api.cpp after validation).
 hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_t *bsums,
-                            int64_t M, int64_t K, hipStream_t stream) {
+                            uint16_t *alpha, int64_t M, int64_t K, hipStream_t stream) {
     const int64_t blocks_per_row = K / bs;
     const int64_t nblocks = M * blocks_per_row;
     const int lanes = bs / 4;
@@ -73,10 +91,10 @@ hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_
     const int64_t grid = (threads + 255) / 256;
     if (bs == 256)
         hipLaunchKernelGGL((quant_act_kernel<256, true>), dim3((unsigned)grid), dim3(256), 0,
-                           stream, x, qs, d, bsums, nblocks, blocks_per_row, K);
+                           stream, x, qs, d, bsums, alpha, nblocks, blocks_per_row, M, K);
     else
         hipLaunchKernelGGL((quant_act_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0,
-                           stream, x, qs, d, bsums, nblocks, blocks_per_row, K);
+                           stream, x, qs, d, bsums, alpha, nblocks, blocks_per_row, M, K);
     return hipGetLastError();
 }
 

@@ -33,12 +33,21 @@
  * block per 128 ternary weights in llama.cpp PR 214):
  *
  *   Q8_K activations (KQ_ACT_Q8_K), one buffer of kq_act_bytes() bytes with
- *   three sections, each at a 256-byte-aligned offset from the start:
+ *   four sections, each at a 256-byte-aligned offset from the start:
  *     qs    int8  [M][K]        quantized values
- *     d     fp32  [M][K/256]    block scales
+ *     d     fp32  [K/256][M]    block scales, block-major: the scales of block
+ *                               s of all M rows are contiguous
  *     bsums int16 [M][K/16]     sums of qs over each 16 consecutive values
+ *     alpha bf16  [K/256][2][M][8]
+ *                               per block s, row m and 32-value sub-block j:
+ *                               a = d * (float)(sum of the 32 qs), one fp32
+ *                               multiply; part 0 = bf16(a), part 1 =
+ *                               bf16(a - part 0), both round-to-nearest-even.
+ *                               This is the activation operand of the Q4_K
+ *                               min term, kept in hi/lo form so that the GEMM
+ *                               reads it instead of recomputing it per tile.
  *   Q8_128 activations (KQ_ACT_Q8_128): sections qs int8 [M][K] and
- *   d fp32 [M][K/128]; no bsums.
+ *   d fp32 [K/128][M] (block-major); no bsums, no alpha.
  *   Quantization rule per block, in fp32: amax = max|x|; if amax == 0 or
  *   127/amax is not finite then d = 0 and qs = 0; otherwise d = amax/127,
  *   s = 127/amax, qs = clamp(rint(x*s), -127, 127) (round half to even, one
@@ -80,7 +89,7 @@
 extern "C" {
 #endif
 
-#define KQ_VERSION 1
+#define KQ_VERSION 2
 
 /* weight formats */
 #define KQ_Q4_K 1
@@ -95,6 +104,7 @@ extern "C" {
 #define KQ_SEC_QS 0
 #define KQ_SEC_D 1
 #define KQ_SEC_BSUMS 2
+#define KQ_SEC_ALPHA 3
 
 /* status codes */
 #define KQ_OK 0
@@ -132,7 +142,10 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
  * the tile GEMM of vllm.cpp PR 3036 (per-sub-block int8 dot products with the
  * Q4_K/Q6_K scales and mins folded in) and the PTQ1_0 MMQ path of llama.cpp
  * PR 214.  The fp32 result agrees with the exact product of the dequantized
- * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.
+ * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.  The kernels
+ * address each 128-row tile and each activation section with 32-bit
+ * offsets: shapes where 128*K, 128 weight rows, the d section or the alpha
+ * section reach 2^31 bytes are declined with KQ_ERR_UNSUPPORTED.
  */
 int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
             float *out, hipStream_t stream);

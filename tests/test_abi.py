@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(kq):
 
 
 def test_version_and_strings(kq):
-    assert kq.kq_version() == 1
+    assert kq.kq_version() == 2
     for st in (kq.KQ_OK, kq.KQ_ERR_FMT, kq.KQ_ERR_SHAPE, kq.KQ_ERR_NULL, kq.KQ_ERR_ALIGN,
                kq.KQ_ERR_UNSUPPORTED, kq.KQ_ERR_HIP):
         s = kq.kq_strerror(st)
@@ -58,13 +58,17 @@ def _a256(v):
 
 @pytest.mark.parametrize("M,K", [(1, 256), (8, 512), (7, 768), (513, 4096), (0, 256)])
 def test_act_layout_q8k(kq, M, K):
-    # three sections at 256-byte-aligned offsets: qs [M][K], d [M][K/256], bsums [M][K/16]
+    # four sections at 256-byte-aligned offsets: qs [M][K], d [K/256][M],
+    # bsums [M][K/16], alpha bf16 [K/256][2][M][8]
     off_d = _a256(M * K)
     off_b = off_d + _a256(M * (K // 256) * 4)
-    total = off_b + _a256(M * (K // 16) * 2)
+    off_a = off_b + _a256(M * (K // 16) * 2)
+    total = off_a + _a256((K // 256) * 2 * M * 8 * 2)
     assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_QS, M, K) == 0
     assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_D, M, K) == off_d
     assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_BSUMS, M, K) == off_b
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, kq.KQ_SEC_ALPHA, M, K) == off_a
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_K, 4, M, K) == -1
     assert kq.kq_act_bytes(kq.KQ_ACT_Q8_K, M, K) == total
 
 
@@ -73,6 +77,7 @@ def test_act_layout_q8_128(kq, M, K):
     off_d = _a256(M * K)
     assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_128, kq.KQ_SEC_D, M, K) == off_d
     assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_128, kq.KQ_SEC_BSUMS, M, K) == -1
+    assert kq.kq_act_section_offset(kq.KQ_ACT_Q8_128, kq.KQ_SEC_ALPHA, M, K) == -1
     assert kq.kq_act_bytes(kq.KQ_ACT_Q8_128, M, K) == off_d + _a256(M * (K // 128) * 4)
 
 
@@ -114,6 +119,8 @@ def test_gemm_validation_without_hip(kq):
     assert L.kq_gemm(kq.KQ_Q4_K, A + 4, A, 8, 8, 256, A, s) == kq.KQ_ERR_ALIGN
     assert L.kq_gemm(kq.KQ_Q4_K, A, A + 8, 8, 8, 256, A, s) == kq.KQ_ERR_ALIGN
     assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 256, A + 2, s) == kq.KQ_ERR_ALIGN
+    # 32-bit tile offsets: 128*K must stay below 2^31 bytes
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 1 << 24, A, s) == kq.KQ_ERR_UNSUPPORTED
     # empty problems are a no-op that succeeds, even with null pointers
     assert L.kq_gemm(kq.KQ_Q4_K, None, None, 0, 8, 256, None, s) == kq.KQ_OK
     assert L.kq_gemm(kq.KQ_Q6_K, None, None, 8, 0, 256, None, s) == kq.KQ_OK

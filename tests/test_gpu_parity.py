@@ -50,6 +50,25 @@ def run_quant(kq, act_fmt, x):
     return a_q8
 
 
+def bf16_bits_rne(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    b = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def expected_alpha(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """The alpha section [K/256][2][M][8] (bf16 bits) that the Q8_K layout
+    defines: a = d * (sum of the 32 qs of each sub-block) in fp32, then
+    hi = bf16(a), lo = bf16(a - hi)."""
+    M, K = qs.shape
+    s32 = qs.astype(np.int64).reshape(M, K // 256, 8, 32).sum(-1)          # [M][S][8]
+    a = (d.astype(np.float32)[:, :, None] * s32.astype(np.float32)).astype(np.float32)
+    hi = bf16_bits_rne(a)
+    hi_f = (hi.astype(np.uint32) << 16).view(np.float32)
+    lo = bf16_bits_rne((a - hi_f).astype(np.float32))
+    return np.stack([hi, lo], 0).transpose(2, 0, 1, 3).view(np.int16)     # [S][2][M][8]
+
+
 def check_act_exact(kq, act_fmt, x, a_q8):
     M, K = x.shape
     qs, d, bs = kqref.quantize_act(act_fmt, x)
@@ -58,6 +77,8 @@ def check_act_exact(kq, act_fmt, x, a_q8):
     assert np.array_equal(gd.cpu().numpy().view(np.uint32), d.view(np.uint32))
     if bs is not None:
         assert np.array_equal(gb.cpu().numpy(), bs)
+        ga = kq.alpha_view(a_q8, M, K).cpu().numpy()
+        assert np.array_equal(ga, expected_alpha(qs, d)), "alpha section differs"
     return qs, d, bs
 
 
@@ -236,6 +257,9 @@ def hand_act_q8k(kq, qs):
     buf[od:od + M * (K // 256) * 4] = np.ones((M, K // 256), np.float32).view(np.uint8).reshape(-1)
     bs = qs.astype(np.int32).reshape(M, K // 16, 16).sum(axis=2).astype(np.int16)
     buf[ob:ob + M * (K // 16) * 2] = bs.view(np.uint8).reshape(-1)
+    oa = kq.kq_act_section_offset(1, 3, M, K)
+    al = expected_alpha(qs, np.ones((M, K // 256), np.float32))
+    buf[oa:oa + al.nbytes] = al.view(np.uint8).reshape(-1)
     return dev(buf)
 
 
