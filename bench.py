@@ -9,18 +9,26 @@ headline metric is quoted on.  Inputs are resident in HBM before timing; the
 weight, activation and output buffers rotate over enough copies that
 consecutive steps touch more than 512 MB, twice the 256 MB Infinity Cache.
 
-Prints ONE JSON line.  `roofline` describes the GEMM kernel: algorithmic int8
-ops per launch over its mean launch time (HIP events on the launch stream)
-against the 5.0 POP/s dense int8 MFMA peak.  `cpu_baseline` is the plain CPU
+Prints ONE JSON line.  `roofline` describes the GEMM kernel (the dominant
+one): algorithmic int8 ops per launch (2*M*N*K) over its mean launch time,
+measured with HIP events recorded on the stream the kernel is launched on,
+against the 5.0 POP/s dense int8 MFMA peak (for M < 256 the kernel is bound by
+streaming the weights: algorithmic bytes per launch over HBM's 8 TB/s).
+`traffic` is the HBM traffic per launch measured with rocprofv3 counters for
+the current kernel source (profiles/*_traffic.md), or null when those counters
+were taken on a different kernel source.  `cpu_baseline` is the plain CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--cpu-seconds S] [--copy-mib N]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,10 +39,34 @@ METRIC = "effective int8 TOPS + prefill tok/s, Q4_K x Q8_K 4096x14336 GEMM; % of
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
+GEMM_SOURCE = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc", "kq_gemm.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from profiles/<...>_<workload>_traffic.md, if
+    that file was measured on the current kernel source; else None."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    want = kernel_source_hash()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(f"{workload}_traffic.md"):
+            continue
+        text = open(os.path.join(pdir, name)).read()
+        h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+        b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+        if h and b and h.group(1) == want:
+            return float(b.group(1))
+    return None
 
 
 def main():
@@ -46,6 +78,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(the reference kernel for scaling profiler byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +139,16 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy of {args.copy_mib} MiB done")
 
     quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
@@ -114,6 +159,7 @@ def main():
     quant_mean_s = float(quant_ms.mean()) * 1e-3
     value_tops = ops / (step_ms * 1e-3) / 1e12
     gemm_tops = ops / gemm_mean_s / 1e12
+    gemm_alg_bytes = w_bytes + a_bytes + o_bytes
 
     result = {
         "metric": METRIC,
@@ -138,24 +184,26 @@ def main():
                  "tok_per_s": round(M / gemm_mean_s, 1),
                  "frac_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
                  "weight_gbs": round(w_bytes / gemm_mean_s / 1e9, 1),
-                 "frac_hbm_on_weights": round(w_bytes / gemm_mean_s / 1e9 / PEAK_HBM_GBS, 4)},
+                 "frac_hbm_on_weights": round(w_bytes / gemm_mean_s / 1e9 / PEAK_HBM_GBS, 4),
+                 "algorithmic_bytes": gemm_alg_bytes},
         "quantize": {"mean_us": round(quant_mean_s * 1e6, 2),
                      "gbs": round((x_bytes + a_bytes) / quant_mean_s / 1e9, 1),
                      "frac_hbm": round((x_bytes + a_bytes) / quant_mean_s / 1e9 / PEAK_HBM_GBS,
                                        4)},
-        "roofline": {"bound": "mfma" if M >= 256 else "hbm",
-                     "kernel": kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)),
-                     "achieved": None, "peak": None, "unit": None, "frac": None,
-                     "traffic": None},
         "dispatch": kq.dispatch_counts(),
+        "kernel_source_sha256_16": kernel_source_hash(),
     }
+    traffic = measured_traffic(wl.name)
     if M >= 256:
-        result["roofline"].update({"achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
-                                   "unit": "TOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)})
+        result["roofline"] = {"bound": "mfma", "achieved": round(gemm_tops, 2),
+                              "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                              "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic}
     else:
-        gbs = (w_bytes + a_bytes + o_bytes) / gemm_mean_s / 1e9
-        result["roofline"].update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        gbs = gemm_alg_bytes / gemm_mean_s / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "traffic": traffic}
+    result["roofline"]["kernel"] = kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, W_np, x_np, Os[(args.steps - 1) % ncopy],
@@ -164,9 +212,11 @@ def main():
 
 
 def cpu_baseline(wl, W_np, x_np, out_dev, target_s):
-    """The plain CPU oracle (quantize + fp64 dequantize-and-multiply) on a
-    bounded sample of the workload: all tokens, a subset of weight rows.  Also
-    re-checks the GPU output on those rows."""
+    """The plain CPU oracle (fp32 Q8 quantize, fp64 dequantize-and-multiply) on
+    a bounded sample of the workload: all tokens against a random subset of
+    weight rows, sized to about target_s seconds of CPU time.  The quantize
+    cost is charged to the sample in proportion to its share of the rows.  The
+    GPU output of the last step is re-checked on a few of those rows."""
     import numpy as np
 
     from oracle import kqref
@@ -177,33 +227,37 @@ def cpu_baseline(wl, W_np, x_np, out_dev, target_s):
     qs, d, _ = kqref.quantize_act(act_fmt, x_np)
     tq = time.perf_counter() - t
     rng = np.random.default_rng(5)
-    # calibrate on a few rows, then size the sample to ~target_s
-    probe = np.sort(rng.choice(wl.N, 8, replace=False))
-    t = time.perf_counter()
-    kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=probe)
-    per_row = max((time.perf_counter() - t) / len(probe), 1e-6)
-    nrows = int(min(wl.N, max(8, (target_s - tq) / per_row)))
+    # calibrate: double the sample until one run takes >= 1 s, then scale
+    n, per_row = 16, None
+    while n <= wl.N:
+        rows = np.sort(rng.choice(wl.N, n, replace=False))
+        t = time.perf_counter()
+        kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=rows, want_tol=False)
+        dt = time.perf_counter() - t
+        per_row = dt / n
+        if dt >= 1.0:
+            break
+        n *= 2
+    nrows = int(min(wl.N, max(16, (target_s - tq) / per_row)))
     rows = np.sort(rng.choice(wl.N, nrows, replace=False))
+    log(f"[bench] cpu baseline: {nrows} weight rows (~{nrows * per_row:.1f} s)")
     t = time.perf_counter()
-    ref, tol = kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=rows)
+    kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=rows, want_tol=False)
     tg = time.perf_counter() - t
     ops = 2.0 * wl.M * nrows * wl.K
-    # quantize cost attributed to the sample in proportion to its share of rows
     t_sample = tg + tq * nrows / wl.N
-    got = out_dev[:, torch_index(rows, out_dev)].cpu().numpy().astype(np.float64)
-    ratio = float((np.abs(got - ref) / tol).max())
+    check = rows[:: max(1, nrows // 8)][:8]
+    ref, tol = kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=check)
+    import torch
+    got = out_dev[:, torch.from_numpy(check).to(out_dev.device)].cpu().numpy()
+    ratio = float((np.abs(got.astype(np.float64) - ref) / tol).max())
     return {"value": round(ops / t_sample / 1e12, 6), "unit": "TOPS", "cores": cores,
             "kind": "oracle",
-            "sample": f"{wl.name}: all {wl.M} tokens x {nrows} of {wl.N} weight rows, K={wl.K}; "
-                      f"plain C oracle (fp32 Q8 quantize + fp64 dequantize-and-multiply), "
-                      f"gcc -O2 -fopenmp; quantize {tq:.2f} s for all rows, "
-                      f"multiply {tg:.2f} s",
+            "sample": f"{wl.name}: all {wl.M} tokens x {nrows} of {wl.N} weight rows (random), "
+                      f"K={wl.K}; plain C oracle (fp32 Q8 quantize + fp64 "
+                      f"dequantize-and-multiply), gcc -O2 -fopenmp; quantize {tq:.2f} s for all "
+                      f"rows (charged pro rata), multiply {tg:.2f} s",
             "gpu_vs_oracle_max_err_over_tol": round(ratio, 4)}
-
-
-def torch_index(rows, t):
-    import torch
-    return torch.from_numpy(rows).to(t.device)
 
 
 if __name__ == "__main__":
