@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kq_api.cpp", "kq_quant.hip", "kq_gemm.hip"]
+SOURCES = ["kq_api.cpp", "kq_quant.hip", "kq_gemm.hip", "kq_gemm_q4k.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -23,6 +23,9 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    # MFMA accumulators in ordinary VGPRs: the fold reads and writes them with
+    # VALU instructions, and AGPR placement would add a copy per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

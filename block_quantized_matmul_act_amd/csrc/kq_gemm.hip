@@ -1069,9 +1069,14 @@ static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float 
     return a;
 }
 
+hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
+                           const uint16_t *alpha, float *out, int M, int N, int K,
+                           hipStream_t stream);
+
 hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
                        const uint16_t *alpha, float *out, int M, int N, int K,
                        hipStream_t stream) {
+    if (fmt == FMT_Q4K) return launch_gemm_q4k(W, qs, da, alpha, out, M, N, K, stream);
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {

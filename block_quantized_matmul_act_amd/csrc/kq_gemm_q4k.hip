@@ -1,0 +1,425 @@
+// kq_gemm_q4k.hip -- Q4_K x Q8_K GEMM on gfx950 int8 MFMA, weights unpacked
+// straight into matrix-core operand registers.
+//
+// out[m][n] = sum_sb d_a[m,sb] * ( d[n,sb] * sum_k sc_j q_k a_k
+//                                  - dmin[n,sb] * sum_j m_j * B_j[m,sb] )
+// where B_j is the sum of the 32 quantized activations of sub-block j
+// (the Q4_K dequantization w = d*sc_j*q - dmin*m_j, multiplied out).
+//
+// Work split (prior art: the BigTile kernel of vllm.cpp PR 3036 and
+// llama.cpp's mul_mat_q share one staged activation tile among all warps of
+// a block; here the weight side is not staged at all):
+//   * A workgroup of 4 waves (one per SIMD) computes 128 x 128 output tiles,
+//     persistently: the grid is one workgroup per CU and each walks a list
+//     of tiles with one flat (tile, superblock) loop, so prefetching runs
+//     across tile boundaries.
+//   * Wave w owns 32 weight rows (output columns) and all 128 activation
+//     rows.  Every weight is fetched and unpacked once per tile, by the wave
+//     that multiplies it, directly into v_mfma_i32_32x32x32_i8 operand
+//     registers: no LDS round trip for weights.
+//   * Each 256-wide superblock of activations (values, scales) is copied
+//     global -> LDS by the buffer unit (no registers), two superblocks ahead,
+//     into a ring of three slots; rows are 256 bytes with 16-byte pieces
+//     XOR-swizzled by the row, which keeps fragment reads conflict-free.
+//   * The 6-bit sub-block scale rides in the int8 operand as two digit
+//     planes, sc = 8*sh + sl with sh, sl in [0,7]:
+//         sc*q = 8*(sh*q) + (sl*q),   sh*q, sl*q <= 105,
+//     so two MFMA streams accumulate a whole superblock in int32 and the
+//     fp32 fold runs once per superblock and output.
+//   * The min term is a rank-8 product per superblock.  Its activation
+//     operand d_a*B_j comes precomputed from the quantizer (alpha section, a
+//     bf16 hi/lo pair); the weight operand -dmin*m_j is split the same way;
+//     three bf16 MFMAs (hi*hi + hi*lo + lo*hi) per pair of superblocks fold
+//     it straight into the fp32 accumulators.
+//   * Reads past the last activation row or weight row return zero (buffer
+//     resources sized to the tile); the epilogue masks the stores.
+//
+// MFMA operand convention (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_bf16):
+// lane l supplies row (l % 32) of A and column (l % 32) of B with k-group
+// l / 32; the contraction sums over every (k-group, element) pair, so any K
+// order works as long as both operands use the same one.  The 32x32 result
+// is 16 registers per lane: register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+#include "kq_device.hpp"
+
+#include <type_traits>
+
+namespace kq {
+namespace q4w {
+
+constexpr int BM = 128, BN = 128, NWAVE = 4, NT = 64 * NWAVE;
+constexpr int MT = BM / 32;           // 32-row m-tiles per wave
+constexpr int ROW = 256;              // LDS bytes per staged activation row
+constexpr int ABUF = BM * ROW;        // staged activation values of one superblock
+constexpr int BB = 144;               // Q4_K block bytes
+constexpr int LBUF = 2 * BM * 16;     // staged min-term operands (hi, lo) of one superblock
+constexpr int WG_PER_CU = 2;          // two workgroups (eight waves) share a CU
+constexpr int RSRC_FLAGS = 0x00020000;
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+struct Args {
+    const uint8_t *W;
+    const int8_t *qs;
+    const float *da;         // [nsb][M]
+    const uint16_t *alpha;   // [nsb][2][M][8] bf16
+    float *out;
+    int M, N, K, nsb, tiles_m, tiles_n, ntiles;
+};
+
+__device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mma_bf16(v8bf a, v8bf b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// four nibble bytes times a scale digit s < 8, bytewise (products < 128)
+__device__ __forceinline__ int mul_digit(uint32_t nib4, uint32_t s) {
+    v2u16 x = __builtin_bit_cast(v2u16, nib4);
+    const unsigned short s16 = (unsigned short)s;
+    return (int)__builtin_bit_cast(uint32_t, (v2u16)(x * (v2u16){s16, s16}));
+}
+// s_waitcnt on the vector-memory counter only (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// copies in flight).  LDS filled by buffer->LDS copies is made visible by the
+// vmcnt wait each wave performs before it.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rs, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rs, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ v4i ld16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+
+// Tile t of the grouped order: GM M-tiles down, then across N.
+struct TileXY {
+    int m0, n0;
+};
+__device__ __forceinline__ TileXY tile_xy(const Args &a, int t) {
+    constexpr int GM = 4;
+    const int per_group = GM * a.tiles_n;
+    const int first_m = (t / per_group) * GM;
+    const int gsize = min(a.tiles_m - first_m, GM);
+    const int r = t % per_group;
+    return {(first_m + r % gsize) * BM, (r / gsize) * BN};
+}
+
+// One staging slot: distinct LDS arrays per slot, so the compiler can tell
+// the copies into one slot from the reads of the other.
+struct Slot {
+    int8_t *a;      // [BM rows][256]: 16-byte piece p of row r at ((p ^ (r % 16)) * 16)
+    float *d;       // [BM] activation scales
+    int8_t *l;      // [2][BM][16]: min-term operands, hi then lo
+};
+
+// This lane's raw weight block: header and its 64 nibble bytes.
+struct WRaw {
+    v4i hdr, q[4];
+};
+
+__global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) int8_t s_a0[ABUF], s_a1[ABUF];
+    __shared__ __attribute__((aligned(16))) float s_d0[BM], s_d1[BM];
+    __shared__ __attribute__((aligned(16))) int8_t s_l0[LBUF], s_l1[LBUF];
+    const Slot slots[2] = {{s_a0, s_d0, s_l0}, {s_a1, s_d1, s_l1}};
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int ln = lane & 31, g = lane >> 5;
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+
+    // ---- persistent tile list ----------------------------------------------
+    // Workgroups are dealt round-robin to the 8 XCDs.  At step k the grid
+    // covers grouped-order tiles [k*G, (k+1)*G); the workgroups of one XCD
+    // take a contiguous run of them, so they share activation and weight
+    // rows in that XCD's L2.
+    const int G = gridDim.x, b = blockIdx.x;
+    const int per_xcd = G >> 3;
+    const int slot_in_step = (per_xcd > 0 && b < 8 * per_xcd) ? ((b & 7) * per_xcd + (b >> 3)) : b;
+    const int my_tiles = (a.ntiles - slot_in_step + G - 1) / G;  // tiles slot, slot+G, ...
+    const int total = my_tiles * nsb;                            // flat iterations
+    const int rowbytes = nsb * BB;
+    if (total <= 0) return;  // uniform: no barrier is ever reached
+
+    auto tile_sb = [&](int itx, TileXY &T, int &sbx) {
+        const int kx = itx / nsb;
+        sbx = itx - kx * nsb;
+        T = tile_xy(a, slot_in_step + kx * G);
+    };
+
+    // ---- staging of one superblock of activations: buffer -> LDS copies ----
+    // Values: 1 KiB copy c holds rows 4c..4c+3; lane l fills position l%16 of
+    // row 4c + l/16 with piece (l%16) ^ (row%16).  Wave w copies c = 8w..8w+7.
+    // Wave 0 also copies the scales (two 256-byte copies), waves 1..3 and 0
+    // the min-term operands (four 1 KiB copies: part c/2, rows 64*(c%2)..).
+    const int st_row = lane >> 4, st_pos = lane & 15;
+    // copy i covers rows 32w + 4i + l/16: its piece index is
+    // (l%16) ^ (4i + l/16), i.e. base ^ (64*(i%4)) in bytes (K is a multiple
+    // of 256, so the XOR stays inside the row), and copies i, i+4 are 16 rows
+    // (16*K bytes) apart
+    const int a_vbase = (32 * wave + st_row) * K + 16 * (st_pos ^ st_row);
+    auto stage = [&](const Slot &S, TileXY T, int sbx) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.qs + (int64_t)T.m0 * K), (short)0, min(M - T.m0, BM) * K, RSRC_FLAGS);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            copy16(rs, S.a + (8 * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
+                   sbx * ROW + (4 * (i & 3) + 16 * (i >> 2)) * K);
+        if (wave == 0) {
+            const auto rd = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.da + T.m0), (short)0, (nsb * M - T.m0) * 4, RSRC_FLAGS);
+            copy4(rd, S.d, 4 * lane, sbx * M * 4);
+            copy4(rd, S.d + 64, 4 * lane + 256, sbx * M * 4);
+        }
+        const auto ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.alpha + (int64_t)T.m0 * 8), (short)0, (nsb * 2 * M - T.m0) * 16, RSRC_FLAGS);
+        const int c = wave;  // part c/2, rows 64*(c%2) .. +64
+        copy16(ra, S.l + c * 1024, 16 * lane + (c & 1) * 1024, (sbx * 2 + (c >> 1)) * M * 16);
+    };
+
+    // ---- weights of this lane: row n0 + 32*wave + ln, straight to registers --
+    const int w_row = (32 * wave + ln) * rowbytes;
+    auto load_w = [&](TileXY T, int sbx, WRaw &R) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.W + (int64_t)T.n0 * rowbytes), (short)0, min(N - T.n0, BN) * rowbytes,
+            RSRC_FLAGS);
+        const int so = sbx * BB;
+        R.hdr = ld16(rs, w_row, so);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs, w_row + 16 + 64 * g + 16 * i, so);
+    };
+
+    // ---- fragment addressing: row 32t + ln, piece p(g, s) swizzled by row ----
+    // k-group g takes nibble bytes [64g, 64g+64) of the block: sub-blocks
+    // 4g..4g+3.  K-step s uses the 16 bytes at 64g + 16*(s%4): their low
+    // nibbles (s < 4) are weights 128g + 64*((s%4)/2) + 16*(s%2) + i of the
+    // superblock, their high nibbles (s >= 4) the same plus 32.
+    int frag[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int p = 8 * g + 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
+        frag[s] = ln * ROW + ((p ^ (ln & 15)) << 4);
+    }
+
+    v16i acc[MT];
+    v16f out[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = v16f{};
+
+    WRaw wc;
+
+    // ---- one superblock; P = slot parity (compile-time) -----------------------
+    auto iteration = [&](auto PP, int it) {
+        constexpr int P = decltype(PP)::value;
+        const Slot &S = slots[P];
+        // everything this wave copied for iteration it has landed; after the
+        // barrier, so has every other wave's, and every read of the other
+        // slot (iteration it-1) is done.  Only this iteration's weights
+        // (issued after those copies, one iteration ago) may be in flight.
+        wait_vmcnt<5>();
+        barrier_nofence();
+        TileXY T;
+        int sb;
+        tile_sb(it, T, sb);
+        const bool more = it + 1 < total;
+        TileXY Tn;
+        int sbn = 0;
+        if (more) {
+            tile_sb(it + 1, Tn, sbn);
+            stage(slots[1 - P], Tn, sbn);
+        }
+
+        // scale digits of sub-blocks 4g..4g+3 (fields 4g.. of the 96-bit word)
+        const uint32_t w1 = (uint32_t)wc.hdr[1], w2 = (uint32_t)wc.hdr[2], w3 = (uint32_t)wc.hdr[3];
+        const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
+        const float dw = f16_bits_to_f32((uint32_t)wc.hdr[0]);
+        const float dmin = f16_bits_to_f32((uint32_t)wc.hdr[0] >> 16);
+
+        // pass 1: high digits (sc >> 3) over the whole superblock; pass 2: low
+        // digits (sc & 7) into the same accumulators after a shift by 3.  The
+        // fragments of K-step s+1 are read while K-step s multiplies.
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            v4i av[2][MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[0]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                if (s + 1 < 8) {
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[s + 1]);
+                }
+                const int si = 2 * ((s & 3) >> 1) + (s >> 2);  // sub-block 4g + si
+                const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
+                const v4i raw = wc.q[s & 3];
+                v4i bq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t nib = (s < 4) ? ((uint32_t)raw[e] & 0x0F0F0F0Fu)
+                                                 : (((uint32_t)raw[e] >> 4) & 0x0F0F0F0Fu);
+                    bq[e] = mul_digit(nib, dig);
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[t] = (pass == 0 && s == 0) ? mma_i8(av[s & 1][t], bq, v16i{})
+                                                   : mma_i8(av[s & 1][t], bq, acc[t]);
+            }
+            if (pass == 0) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[t][r] <<= 3;
+                // re-read the operands in pass 2 rather than keeping all of
+                // pass 1's live (registers are the scarcer unit)
+                asm volatile("" ::: "memory");
+            }
+        }
+        // the next superblock's weights: issued after the passes, so they
+        // and this superblock's nibbles are never live at the same time
+        WRaw wn;
+        if (more) load_w(Tn, sbn, wn);
+        // fold: out += float(sum_k sc*q*a) * d_a[m] * d[n]
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            v4f da4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                da4[q] = *reinterpret_cast<const v4f *>(S.d + 32 * t + 8 * q + 4 * g);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * q + i;
+                    out[t][r] = fmaf((float)acc[t][r], da4[q][i] * dw, out[t][r]);
+                }
+            }
+        }
+        // min term: k-group g carries sub-blocks 4g..4g+3.  A row m: alpha_hi
+        // and alpha_lo of those; B: beta_hi twice, then beta_lo and zeros, so
+        // two bf16 MFMAs give sum_j (a_hi + a_lo) b_hi + a_hi b_lo.
+        {
+            // mins m_j: bits 48 + 6j of the 96-bit word (words w1, w2, w3)
+            const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);  // bits 32..95
+            const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));      // fields 4g..4g+3
+            v8bf b1, b2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
+                __bf16 h, l;
+                split_bf16(beta, h, l);
+                b1[i] = h;
+                b1[4 + i] = h;
+                b2[i] = l;
+                b2[4 + i] = (__bf16)0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int8_t *lp = S.l + (32 * t + ln) * 16 + 8 * g;
+                const v2u ahi = *reinterpret_cast<const v2u *>(lp);
+                const v2u alo = *reinterpret_cast<const v2u *>(lp + BM * 16);
+                const v4i avv = {(int)ahi.x, (int)ahi.y, (int)alo.x, (int)alo.y};
+                const v8bf am = __builtin_bit_cast(v8bf, avv);
+                out[t] = mma_bf16(am, b1, out[t]);
+                out[t] = mma_bf16(am, b2, out[t]);
+            }
+        }
+
+        if (sb + 1 == nsb) {
+            // epilogue of tile T: fp32 stores through a buffer resource sized
+            // to the tile's valid rows; columns past N are sent out of range
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.out + (int64_t)T.m0 * N), (short)0, min(M - T.m0, BM) * N * 4, RSRC_FLAGS);
+            const int n = T.n0 + 32 * wave + ln;
+            const int voff = n < N ? (4 * g * N + n) * 4 : 0x7FFFFFF0;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                // cast the whole vector: storing a bit-cast of one element
+                // directly miscompiles to a store of element 0 (ROCm 7.2 clang)
+                const v16i bits = __builtin_bit_cast(v16i, out[t]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
+                    __builtin_amdgcn_raw_buffer_store_b32(bits[r], ro, voff, row * N * 4, 0);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) out[t] = v16f{};
+        }
+        if (more) wc = wn;
+    };
+
+    // prologue: stage iteration 0, its weights
+    {
+        TileXY T0;
+        int sb0;
+        tile_sb(0, T0, sb0);
+        stage(slots[0], T0, sb0);
+        load_w(T0, sb0, wc);
+    }
+    for (int it = 0; it < total; it += 2) {
+        iteration(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < total) iteration(std::integral_constant<int, 1>{}, it + 1);
+    }
+}
+
+// out[0, n) = 0 (the product over an empty K); a kernel rather than a memset
+// so that the call stays capturable in a graph
+__global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = 0.0f;
+}
+
+}  // namespace q4w
+
+static int g_num_cus = 0;
+
+hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
+                           const uint16_t *alpha, float *out, int M, int N, int K,
+                           hipStream_t stream) {
+    if (g_num_cus <= 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        g_num_cus = cus;
+    }
+    if (K == 0) {
+        const int64_t n = (int64_t)M * N;
+        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, out, n);
+        return hipGetLastError();
+    }
+    q4w::Args a;
+    a.W = static_cast<const uint8_t *>(W);
+    a.qs = qs;
+    a.da = da;
+    a.alpha = alpha;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nsb = K / 256;
+    a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
+    a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
+    a.ntiles = a.tiles_m * a.tiles_n;
+    const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
+    hipLaunchKernelGGL(q4w::gemm_q4k_kernel, dim3(grid), dim3(q4w::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kq
