@@ -96,6 +96,7 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     // the alpha section with 32-bit buffer offsets
     const int64_t lim = (int64_t)1 << 31;
     if (128 * K >= lim || 128 * (K / qk_of(fmt)) * bb_of(fmt) >= lim || 128 * N * 4 >= lim ||
+        M * K >= lim || N * (K / qk_of(fmt)) * bb_of(fmt) >= lim || M * N * 4 >= lim ||
         (K / qk_of(fmt)) * M * 4 >= lim || (K / 256) * 2 * M * 16 >= lim)
         return KQ_ERR_UNSUPPORTED;
     return 1;  // proceed

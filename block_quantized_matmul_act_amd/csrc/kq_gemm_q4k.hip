@@ -16,23 +16,26 @@
 //   * Wave w owns 32 weight rows (output columns) and all 128 activation
 //     rows.  Every weight is fetched and unpacked once per tile, by the wave
 //     that multiplies it, directly into v_mfma_i32_32x32x32_i8 operand
-//     registers: no LDS round trip for weights.
-//   * Each 256-wide superblock of activations (values, scales) is copied
-//     global -> LDS by the buffer unit (no registers), two superblocks ahead,
-//     into a ring of three slots; rows are 256 bytes with 16-byte pieces
-//     XOR-swizzled by the row, which keeps fragment reads conflict-free.
-//   * The 6-bit sub-block scale rides in the int8 operand as two digit
-//     planes, sc = 8*sh + sl with sh, sl in [0,7]:
-//         sc*q = 8*(sh*q) + (sl*q),   sh*q, sl*q <= 105,
-//     so two MFMA streams accumulate a whole superblock in int32 and the
-//     fp32 fold runs once per superblock and output.
+//     registers (loaded one superblock ahead): no LDS round trip for weights.
+//   * Each 256-wide superblock of activations (values, scales, min-term
+//     operands) is copied global -> LDS by the buffer unit (no registers)
+//     one superblock ahead, into the other of two slots; rows are 256 bytes
+//     with 16-byte pieces XOR-swizzled by the row, which keeps fragment reads
+//     conflict-free.
+//   * The 6-bit sub-block scale rides in the int8 operand as two digits,
+//     sc = 8*sh + sl with sh, sl in [0,7]:
+//         sc*q = 8*(sh*q) + (sl*q),   sh*q, sl*q <= 105.
+//     Pass 1 accumulates the sh digits over the whole superblock, the int32
+//     sums are shifted left by 3, pass 2 adds the sl digits; the fp32 fold
+//     then runs once per superblock and output.
 //   * The min term is a rank-8 product per superblock.  Its activation
 //     operand d_a*B_j comes precomputed from the quantizer (alpha section, a
 //     bf16 hi/lo pair); the weight operand -dmin*m_j is split the same way;
-//     three bf16 MFMAs (hi*hi + hi*lo + lo*hi) per pair of superblocks fold
-//     it straight into the fp32 accumulators.
-//   * Reads past the last activation row or weight row return zero (buffer
-//     resources sized to the tile); the epilogue masks the stores.
+//     two bf16 MFMAs per superblock (hi*hi + lo*hi, then hi*lo) fold it
+//     straight into the fp32 accumulators.
+//   * Reads past the last activation row or weight row return zero and
+//     stores past the last output row are dropped (buffer resources over the
+//     whole tensors); columns past N are sent out of range.
 //
 // MFMA operand convention (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_bf16):
 // lane l supplies row (l % 32) of A and column (l % 32) of B with k-group
@@ -55,6 +58,9 @@ constexpr int BB = 144;               // Q4_K block bytes
 constexpr int LBUF = 2 * BM * 16;     // staged min-term operands (hi, lo) of one superblock
 constexpr int WG_PER_CU = 2;          // two workgroups (eight waves) share a CU
 constexpr int RSRC_FLAGS = 0x00020000;
+// A store offset the buffer range check always drops: outputs hold fewer than
+// 2^31 bytes, and a row offset (< 2^30) added to it cannot wrap 2^32.
+constexpr int OOB_VOFF = (int)0x80000000u;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -153,11 +159,15 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     const int rowbytes = nsb * BB;
     if (total <= 0) return;  // uniform: no barrier is ever reached
 
-    auto tile_sb = [&](int itx, TileXY &T, int &sbx) {
-        const int kx = itx / nsb;
-        sbx = itx - kx * nsb;
-        T = tile_xy(a, slot_in_step + kx * G);
-    };
+    // Buffer resources over whole tensors (built once): reads past the last
+    // activation or weight row return zero and stores past the last output
+    // row are dropped.  Every offset below stays under 2^31 (checked on the
+    // host).
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
 
     // ---- staging of one superblock of activations: buffer -> LDS copies ----
     // Values: 1 KiB copy c holds rows 4c..4c+3; lane l fills position l%16 of
@@ -171,34 +181,25 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     // (16*K bytes) apart
     const int a_vbase = (32 * wave + st_row) * K + 16 * (st_pos ^ st_row);
     auto stage = [&](const Slot &S, TileXY T, int sbx) {
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.qs + (int64_t)T.m0 * K), (short)0, min(M - T.m0, BM) * K, RSRC_FLAGS);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            copy16(rs, S.a + (8 * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
-                   sbx * ROW + (4 * (i & 3) + 16 * (i >> 2)) * K);
+            copy16(rs_a, S.a + (8 * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
+                   (T.m0 + 4 * (i & 3) + 16 * (i >> 2)) * K + sbx * ROW);
         if (wave == 0) {
-            const auto rd = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a.da + T.m0), (short)0, (nsb * M - T.m0) * 4, RSRC_FLAGS);
-            copy4(rd, S.d, 4 * lane, sbx * M * 4);
-            copy4(rd, S.d + 64, 4 * lane + 256, sbx * M * 4);
+            copy4(rs_d, S.d, 4 * lane, (sbx * M + T.m0) * 4);
+            copy4(rs_d, S.d + 64, 4 * lane + 256, (sbx * M + T.m0) * 4);
         }
-        const auto ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.alpha + (int64_t)T.m0 * 8), (short)0, (nsb * 2 * M - T.m0) * 16, RSRC_FLAGS);
-        const int c = wave;  // part c/2, rows 64*(c%2) .. +64
-        copy16(ra, S.l + c * 1024, 16 * lane + (c & 1) * 1024, (sbx * 2 + (c >> 1)) * M * 16);
+        const int c = wave;  // min-term operands: part c/2, rows 64*(c%2) .. +64
+        copy16(rs_l, S.l + c * 1024, 16 * lane + (c & 1) * 1024, ((sbx * 2 + (c >> 1)) * M + T.m0) * 16);
     };
 
     // ---- weights of this lane: row n0 + 32*wave + ln, straight to registers --
     const int w_row = (32 * wave + ln) * rowbytes;
     auto load_w = [&](TileXY T, int sbx, WRaw &R) {
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.W + (int64_t)T.n0 * rowbytes), (short)0, min(N - T.n0, BN) * rowbytes,
-            RSRC_FLAGS);
-        const int so = sbx * BB;
-        R.hdr = ld16(rs, w_row, so);
+        const int so = T.n0 * rowbytes + sbx * BB;
+        R.hdr = ld16(rs_w, w_row, so);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs, w_row + 16 + 64 * g + 16 * i, so);
+        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs_w, w_row + 16 + 64 * g + 16 * i, so);
     };
 
     // ---- fragment addressing: row 32t + ln, piece p(g, s) swizzled by row ----
@@ -221,6 +222,11 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     WRaw wc;
 
     // ---- one superblock; P = slot parity (compile-time) -----------------------
+    // (k, sb): tile index in this workgroup's list and superblock of the
+    // current iteration; T = tile k, TN = tile k+1 (computed once per tile)
+    int k = 0, sb = 0;
+    TileXY T = tile_xy(a, slot_in_step), TN = tile_xy(a, slot_in_step + G);
+
     auto iteration = [&](auto PP, int it) {
         constexpr int P = decltype(PP)::value;
         const Slot &S = slots[P];
@@ -230,17 +236,21 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
         // (issued after those copies, one iteration ago) may be in flight.
         wait_vmcnt<5>();
         barrier_nofence();
-        TileXY T;
-        int sb;
-        tile_sb(it, T, sb);
         const bool more = it + 1 < total;
-        TileXY Tn;
-        int sbn = 0;
-        if (more) {
-            tile_sb(it + 1, Tn, sbn);
-            stage(slots[1 - P], Tn, sbn);
-        }
+        const bool last_sb = sb + 1 == nsb;
+        const TileXY Tn = last_sb ? TN : T;
+        const int sbn = last_sb ? 0 : sb + 1;
+        if (more) stage(slots[1 - P], Tn, sbn);
 
+        // nibble dwords of K-steps 0..7 (low nibbles, then high nibbles)
+        uint32_t nib[8][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nib[i][e] = (uint32_t)wc.q[i][e] & 0x0F0F0F0Fu;
+                nib[i + 4][e] = ((uint32_t)wc.q[i][e] >> 4) & 0x0F0F0F0Fu;
+            }
         // scale digits of sub-blocks 4g..4g+3 (fields 4g.. of the 96-bit word)
         const uint32_t w1 = (uint32_t)wc.hdr[1], w2 = (uint32_t)wc.hdr[2], w3 = (uint32_t)wc.hdr[3];
         const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
@@ -250,6 +260,9 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
         // pass 1: high digits (sc >> 3) over the whole superblock; pass 2: low
         // digits (sc & 7) into the same accumulators after a shift by 3.  The
         // fragments of K-step s+1 are read while K-step s multiplies.
+        // (scheduling fences pin the reads of K-step s+1 ahead of the MFMAs
+        // of K-step s; left alone, the scheduler sinks each read to just
+        // before its MFMA and every MFMA waits out a full LDS latency)
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             v4i av[2][MT];
@@ -258,21 +271,18 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
                 av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[0]);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
+                __builtin_amdgcn_sched_barrier(0);
                 if (s + 1 < 8) {
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
                         av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[s + 1]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
                 const int si = 2 * ((s & 3) >> 1) + (s >> 2);  // sub-block 4g + si
                 const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
-                const v4i raw = wc.q[s & 3];
                 v4i bq;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t nib = (s < 4) ? ((uint32_t)raw[e] & 0x0F0F0F0Fu)
-                                                 : (((uint32_t)raw[e] >> 4) & 0x0F0F0F0Fu);
-                    bq[e] = mul_digit(nib, dig);
-                }
+                for (int e = 0; e < 4; ++e) bq[e] = mul_digit(nib[s][e], dig);
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                     acc[t] = (pass == 0 && s == 0) ? mma_i8(av[s & 1][t], bq, v16i{})
@@ -338,13 +348,11 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
             }
         }
 
-        if (sb + 1 == nsb) {
-            // epilogue of tile T: fp32 stores through a buffer resource sized
-            // to the tile's valid rows; columns past N are sent out of range
-            const auto ro = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a.out + (int64_t)T.m0 * N), (short)0, min(M - T.m0, BM) * N * 4, RSRC_FLAGS);
+        if (last_sb) {
+            // epilogue of tile T: rows past M fall outside the resource and
+            // are dropped; columns past N are sent out of range
             const int n = T.n0 + 32 * wave + ln;
-            const int voff = n < N ? (4 * g * N + n) * 4 : 0x7FFFFFF0;
+            const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 // cast the whole vector: storing a bit-cast of one element
@@ -353,26 +361,213 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
-                    __builtin_amdgcn_raw_buffer_store_b32(bits[r], ro, voff, row * N * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, (T.m0 + row) * N * 4, 0);
                 }
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) out[t] = v16f{};
         }
         if (more) wc = wn;
+        // advance (k, sb); entering tile k+1 computes tile k+2 once
+        if (last_sb) {
+            ++k;
+            sb = 0;
+            T = TN;
+            TN = tile_xy(a, slot_in_step + (k + 1) * G);
+        } else {
+            ++sb;
+        }
     };
 
     // prologue: stage iteration 0, its weights
-    {
-        TileXY T0;
-        int sb0;
-        tile_sb(0, T0, sb0);
-        stage(slots[0], T0, sb0);
-        load_w(T0, sb0, wc);
-    }
+    stage(slots[0], T, 0);
+    load_w(T, 0, wc);
     for (int it = 0; it < total; it += 2) {
         iteration(std::integral_constant<int, 0>{}, it);
         if (it + 1 < total) iteration(std::integral_constant<int, 1>{}, it + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Few tokens (M <= 64): the product is bound by streaming the weights from
+// HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
+// weight rows and runs 4 waves: wave (h, t) takes m-tile t (32 tokens) over
+// superblock half h.  Vector memory completes in issue order, so each
+// superblock's operands (8 activation fragments and the weight block of the
+// lane's row) are issued as one batch, two superblocks ahead, and consumed in
+// that same order: a wait for a near operand never queues behind a far one.
+// The activation scales and min-term operands of the wave's superblocks are
+// copied to LDS once, ahead of the first batch.  The two scale digits share
+// one int32 accumulator (shift by 3 between the passes, the fragments stay in
+// registers for both).  The two K-halves of a tile are summed in LDS.
+// ---------------------------------------------------------------------------
+constexpr int SMT = 2;                // 32-row m-tiles (64 tokens)
+constexpr int SKH = 2;                // K-split: superblock halves
+constexpr int SWAVES = SMT * SKH;
+constexpr int SMAXSB = 32;            // superblocks per wave held in LDS
+constexpr int SBATCH = 13;            // vector loads per superblock batch
+
+__global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) {
+    // per wave: scales [sb][32 rows], min-term operands [sb][hi/lo][32 rows][16 B]
+    __shared__ __attribute__((aligned(16))) float s_dd[SWAVES][SMAXSB][32];
+    __shared__ __attribute__((aligned(16))) int8_t s_ll[SWAVES][SMAXSB][2][32 * 16];
+    __shared__ __attribute__((aligned(16))) float s_red[SMT][16][64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = wave & 1, h = wave >> 1;
+    const int ln = lane & 31, g = lane >> 5;
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int n0 = blockIdx.x * 32;
+    const int rowbytes = nsb * BB;
+    const int sb0 = h * nsb / SKH, sb1 = (h + 1) * nsb / SKH;
+    const int nk = 32 * t < M ? sb1 - sb0 : 0;  // a tile past M has no work
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+
+    // this tile's scales (two superblocks per dword copy: lane -> sb 2i + g,
+    // row ln) and min-term operands (lane -> plane g, row ln) -> LDS
+    for (int j = 0; j < nk; j += 2)
+        copy4(rs_d, &s_dd[wave][j][0], ((sb0 + j + g) * M + 32 * t + ln) * 4, 0);
+    for (int j = 0; j < nk; ++j)
+        copy16(rs_l, &s_ll[wave][j][0][0], (((sb0 + j) * 2 + g) * M + 32 * t + ln) * 16, 0);
+
+    // one superblock's operands: activation fragments per K-step and the
+    // weight block of this lane's row
+    struct Batch {
+        v4i af[8];
+        WRaw w;
+    };
+    const int w_row = (n0 + ln) * rowbytes;
+    const int a_row = (32 * t + ln) * K;
+    auto issue = [&](int j, Batch &B) {
+        const int sb = sb0 + min(j, nk - 1);  // past the end: re-read the last (unused)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int k0 = 128 * g + 64 * ((s & 3) >> 1) + 16 * (s & 1) + 32 * (s >> 2);
+            B.af[s] = ld16(rs_a, a_row + k0, sb * ROW);
+        }
+        const int so = sb * BB;
+        B.w.hdr = ld16(rs_w, w_row, so);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) B.w.q[i] = ld16(rs_w, w_row + 16 + 64 * g + 16 * i, so);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    v16f out = v16f{};
+
+    auto superblock = [&](int j, const Batch &B) {
+        const v4i hdr = B.w.hdr;
+        const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2], w3 = (uint32_t)hdr[3];
+        const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
+        const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
+        const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
+        v16i acc;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int si = 2 * ((s & 3) >> 1) + (s >> 2);
+                const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
+                v4i bq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t q = (uint32_t)B.w.q[s & 3][e];
+                    bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
+                }
+                acc = (pass == 0 && s == 0) ? mma_i8(B.af[s], bq, v16i{}) : mma_i8(B.af[s], bq, acc);
+            }
+            if (pass == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] <<= 3;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4f da4 = *reinterpret_cast<const v4f *>(&s_dd[wave][j & ~1][32 * (j & 1) + 8 * q + 4 * g]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q + i;
+                out[r] = fmaf((float)acc[r], da4[i] * dw, out[r]);
+            }
+        }
+        const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
+        const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
+        v8bf b1, b2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
+            __bf16 hb, lb;
+            split_bf16(beta, hb, lb);
+            b1[i] = hb;
+            b1[4 + i] = hb;
+            b2[i] = lb;
+            b2[4 + i] = (__bf16)0.0f;
+        }
+        const int8_t *lp = &s_ll[wave][j][0][ln * 16 + 8 * g];
+        const v2u ahi = *reinterpret_cast<const v2u *>(lp);
+        const v2u alo = *reinterpret_cast<const v2u *>(lp + 32 * 16);
+        const v4i avv = {(int)ahi.x, (int)ahi.y, (int)alo.x, (int)alo.y};
+        const v8bf am = __builtin_bit_cast(v8bf, avv);
+        out = mma_bf16(am, b1, out);
+        out = mma_bf16(am, b2, out);
+    };
+
+    if (nk > 0) {
+        // The LDS copies sit ahead of batch 0 in the vector-memory queue, so
+        // the wait for batch 0 also covers them.  The loop body is three
+        // whole superblocks with no exit, so every path into its head leaves
+        // the same two batches in flight; batches issued past the end re-read
+        // the last superblock and are drained unused.
+        Batch b0, b1, b2;
+        issue(0, b0);
+        issue(1, b1);
+        int j = 0;
+        for (; j + 3 <= nk; j += 3) {
+            issue(j + 2, b2);
+            wait_vmcnt<2 * SBATCH>();
+            superblock(j, b0);
+            issue(j + 3, b0);
+            wait_vmcnt<2 * SBATCH>();
+            superblock(j + 1, b1);
+            issue(j + 4, b1);
+            wait_vmcnt<2 * SBATCH>();
+            superblock(j + 2, b2);
+        }
+        if (j < nk) {
+            wait_vmcnt<SBATCH>();
+            superblock(j, b0);
+            if (j + 1 < nk) {
+                wait_vmcnt<0>();
+                superblock(j + 1, b1);
+            }
+        }
+        wait_vmcnt<0>();
+    }
+
+    // sum the two K-halves in a fixed order: the h = 1 waves park theirs in LDS
+    if (h == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_red[t][r][lane] = out[r];
+    }
+    __syncthreads();
+    if (h == 0 && 32 * t < M) {
+        const int n = n0 + ln;
+        const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
+        v16f sum = out;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] += s_red[t][r][lane];
+        const v16i bits = __builtin_bit_cast(v16i, sum);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
+            __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, row * N * 4, 0);
+        }
     }
 }
 
@@ -417,6 +612,11 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
+    if (M <= 32 * q4w::SMT && a.nsb <= q4w::SKH * q4w::SMAXSB) {
+        hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
+                           dim3(64 * q4w::SWAVES), 0, stream, a);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
     hipLaunchKernelGGL(q4w::gemm_q4k_kernel, dim3(grid), dim3(q4w::NT), 0, stream, a);
     return hipGetLastError();
