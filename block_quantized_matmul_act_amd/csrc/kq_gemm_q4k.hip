@@ -109,6 +109,28 @@ __device__ __forceinline__ v4i ld16(__amdgpu_buffer_rsrc_t rs, int voff, int sof
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
 }
 
+// LDS reads of staged data, written as instructions of our own: the
+// compiler's wait insertion tracks only a few buffer -> LDS copies at a time
+// and, past that, makes every LDS read wait for the newest copy in flight.
+// The caller orders these reads after the copies they need with an explicit
+// vmcnt wait and makes each result usable with lds_wait.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+template <int OFF>
+__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+    v4i r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// s_waitcnt lgkmcnt(N), tied to a register it guards so that no use of that
+// register is scheduled above it
+template <int N>
+__device__ __forceinline__ void lds_wait(v4i &r) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+
 // Tile t of the grouped order: GM M-tiles down, then across N.
 struct TileXY {
     int m0, n0;
@@ -137,7 +159,7 @@ struct WRaw {
 
 __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) int8_t s_a0[ABUF], s_a1[ABUF];
-    __shared__ __attribute__((aligned(16))) float s_d0[BM], s_d1[BM];
+    __shared__ __attribute__((aligned(16))) float s_d0[2 * BM], s_d1[2 * BM];
     __shared__ __attribute__((aligned(16))) int8_t s_l0[LBUF], s_l1[LBUF];
     const Slot slots[2] = {{s_a0, s_d0, s_l0}, {s_a1, s_d1, s_l1}};
 
@@ -172,34 +194,35 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     // ---- staging of one superblock of activations: buffer -> LDS copies ----
     // Values: 1 KiB copy c holds rows 4c..4c+3; lane l fills position l%16 of
     // row 4c + l/16 with piece (l%16) ^ (row%16).  Wave w copies c = 8w..8w+7.
-    // Wave 0 also copies the scales (two 256-byte copies), waves 1..3 and 0
-    // the min-term operands (four 1 KiB copies: part c/2, rows 64*(c%2)..).
+    // Each wave also copies a quarter of the min-term operands (1 KiB: part
+    // w/2, rows 64*(w%2)..), and wave 0 the scales (one 1 KiB copy).
     const int st_row = lane >> 4, st_pos = lane & 15;
     // copy i covers rows 32w + 4i + l/16: its piece index is
     // (l%16) ^ (4i + l/16), i.e. base ^ (64*(i%4)) in bytes (K is a multiple
     // of 256, so the XOR stays inside the row), and copies i, i+4 are 16 rows
     // (16*K bytes) apart
     const int a_vbase = (32 * wave + st_row) * K + 16 * (st_pos ^ st_row);
+    const int l_voff = 16 * lane + (wave & 1) * 1024;  // 16 * lane for wave 0
     auto stage = [&](const Slot &S, TileXY T, int sbx) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             copy16(rs_a, S.a + (8 * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
                    (T.m0 + 4 * (i & 3) + 16 * (i >> 2)) * K + sbx * ROW);
-        if (wave == 0) {
-            copy4(rs_d, S.d, 4 * lane, (sbx * M + T.m0) * 4);
-            copy4(rs_d, S.d + 64, 4 * lane + 256, (sbx * M + T.m0) * 4);
-        }
         const int c = wave;  // min-term operands: part c/2, rows 64*(c%2) .. +64
-        copy16(rs_l, S.l + c * 1024, 16 * lane + (c & 1) * 1024, ((sbx * 2 + (c >> 1)) * M + T.m0) * 16);
+        copy16(rs_l, S.l + c * 1024, l_voff, ((sbx * 2 + (c >> 1)) * M + T.m0) * 16);
+        // scales of rows m0..m0+127 (lanes 32..63 fill an unused upper half)
+        if (wave == 0) copy16(rs_d, S.d, l_voff, (sbx * M + T.m0) * 4);
     };
 
     // ---- weights of this lane: row n0 + 32*wave + ln, straight to registers --
+    // (constant offsets go to the scalar operand: one address register per lane)
     const int w_row = (32 * wave + ln) * rowbytes;
+    const int w_nib = w_row + 64 * g;
     auto load_w = [&](TileXY T, int sbx, WRaw &R) {
         const int so = T.n0 * rowbytes + sbx * BB;
         R.hdr = ld16(rs_w, w_row, so);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs_w, w_row + 16 + 64 * g + 16 * i, so);
+        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs_w, w_nib, so + 16 + 16 * i);
     };
 
     // ---- fragment addressing: row 32t + ln, piece p(g, s) swizzled by row ----
@@ -207,19 +230,21 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     // 4g..4g+3.  K-step s uses the 16 bytes at 64g + 16*(s%4): their low
     // nibbles (s < 4) are weights 128g + 64*((s%4)/2) + 16*(s%2) + i of the
     // superblock, their high nibbles (s >= 4) the same plus 32.
-    int frag[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int p = 8 * g + 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
-        frag[s] = ln * ROW + ((p ^ (ln & 15)) << 4);
-    }
+    // p = 8g + c(s) with c < 8, so p ^ (ln % 16) splits into bit 3 (fixed
+    // per lane) and bits 0..2: one XOR with a constant per K-step.
+    const int frag_base = ln * ROW + (((8 * g) ^ (ln & 8)) << 4);
+    const int frag_x = (ln & 7) << 4;
+    auto frag = [&](int s) {
+        const int c = 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
+        return frag_base + ((c << 4) ^ frag_x);
+    };
 
     v16i acc[MT];
     v16f out[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) out[t] = v16f{};
 
-    WRaw wc;
+    WRaw wring[2];  // weights of iterations with slot parity 0 / 1
 
     // ---- one superblock; P = slot parity (compile-time) -----------------------
     // (k, sb): tile index in this workgroup's list and superblock of the
@@ -230,27 +255,24 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     auto iteration = [&](auto PP, int it) {
         constexpr int P = decltype(PP)::value;
         const Slot &S = slots[P];
-        // everything this wave copied for iteration it has landed; after the
-        // barrier, so has every other wave's, and every read of the other
-        // slot (iteration it-1) is done.  Only this iteration's weights
-        // (issued after those copies, one iteration ago) may be in flight.
-        wait_vmcnt<5>();
+        // everything this wave copied or loaded for iteration it (one
+        // iteration ago) has landed; after the barrier, so has every other
+        // wave's, and every read of the other slot (iteration it-1) is done.
+        wait_vmcnt<0>();
         barrier_nofence();
         const bool more = it + 1 < total;
         const bool last_sb = sb + 1 == nsb;
         const TileXY Tn = last_sb ? TN : T;
         const int sbn = last_sb ? 0 : sb + 1;
-        if (more) stage(slots[1 - P], Tn, sbn);
-
-        // nibble dwords of K-steps 0..7 (low nibbles, then high nibbles)
-        uint32_t nib[8][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                nib[i][e] = (uint32_t)wc.q[i][e] & 0x0F0F0F0Fu;
-                nib[i + 4][e] = ((uint32_t)wc.q[i][e] >> 4) & 0x0F0F0F0Fu;
-            }
+        // the next superblock's activations and weights, a whole iteration
+        // ahead of their use
+        const WRaw &wc = wring[P];
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            stage(slots[1 - P], Tn, sbn);
+            load_w(Tn, sbn, wring[1 - P]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // scale digits of sub-blocks 4g..4g+3 (fields 4g.. of the 96-bit word)
         const uint32_t w1 = (uint32_t)wc.hdr[1], w2 = (uint32_t)wc.hdr[2], w3 = (uint32_t)wc.hdr[3];
         const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
@@ -263,26 +285,33 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
         // (scheduling fences pin the reads of K-step s+1 ahead of the MFMAs
         // of K-step s; left alone, the scheduler sinks each read to just
         // before its MFMA and every MFMA waits out a full LDS latency)
+        // The two workgroups on a CU put one wave on each SIMD.  While this
+        // wave multiplies it takes issue priority, so the other wave's fold
+        // and unpacking fill the issue slots between its MFMAs.
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             v4i av[2][MT];
 #pragma unroll
             for (int t = 0; t < MT; ++t)
-                av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[0]);
+                av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(0));
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (s + 1 < 8) {
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
-                        av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag[s + 1]);
+                        av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(s + 1));
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 const int si = 2 * ((s & 3) >> 1) + (s >> 2);  // sub-block 4g + si
                 const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
                 v4i bq;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bq[e] = mul_digit(nib[s][e], dig);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t q = (uint32_t)wc.q[s & 3][e];
+                    bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
+                }
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                     acc[t] = (pass == 0 && s == 0) ? mma_i8(av[s & 1][t], bq, v16i{})
@@ -298,10 +327,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
                 asm volatile("" ::: "memory");
             }
         }
-        // the next superblock's weights: issued after the passes, so they
-        // and this superblock's nibbles are never live at the same time
-        WRaw wn;
-        if (more) load_w(Tn, sbn, wn);
+        __builtin_amdgcn_s_setprio(0);
         // fold: out += float(sum_k sc*q*a) * d_a[m] * d[n]
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -367,7 +393,6 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 #pragma unroll
             for (int t = 0; t < MT; ++t) out[t] = v16f{};
         }
-        if (more) wc = wn;
         // advance (k, sb); entering tile k+1 computes tile k+2 once
         if (last_sb) {
             ++k;
@@ -381,7 +406,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 
     // prologue: stage iteration 0, its weights
     stage(slots[0], T, 0);
-    load_w(T, 0, wc);
+    load_w(T, 0, wring[0]);
     for (int it = 0; it < total; it += 2) {
         iteration(std::integral_constant<int, 0>{}, it);
         if (it + 1 < total) iteration(std::integral_constant<int, 1>{}, it + 1);
@@ -391,27 +416,32 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // Few tokens (M <= 64): the product is bound by streaming the weights from
 // HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
-// weight rows and runs 4 waves: wave (h, t) takes m-tile t (32 tokens) over
-// superblock half h.  Vector memory completes in issue order, so each
-// superblock's operands (8 activation fragments and the weight block of the
-// lane's row) are issued as one batch, two superblocks ahead, and consumed in
-// that same order: a wait for a near operand never queues behind a far one.
-// The activation scales and min-term operands of the wave's superblocks are
-// copied to LDS once, ahead of the first batch.  The two scale digits share
-// one int32 accumulator (shift by 3 between the passes, the fragments stay in
-// registers for both).  The two K-halves of a tile are summed in LDS.
+// weight rows and runs 4 independent waves: wave (h, t) takes m-tile t (32
+// tokens) over superblock half h.  Each wave stages its own operands through
+// LDS with coalesced buffer -> LDS copies (consecutive lanes read consecutive
+// bytes of one row, so a copy touches 8 to 14 cache lines instead of one per
+// lane), three superblocks deep, and reads them back in MFMA layout.  The
+// activation scales and min-term operands ride in registers with the same
+// batch.  No barrier is needed until the two K-halves of a tile are summed in
+// LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int SMT = 2;                // 32-row m-tiles (64 tokens)
-constexpr int SKH = 2;                // K-split: superblock halves
+constexpr int SMT = 2;                 // 32-row m-tiles (64 tokens)
+constexpr int SKH = 2;                 // K-split: superblock halves
 constexpr int SWAVES = SMT * SKH;
-constexpr int SMAXSB = 32;            // superblocks per wave held in LDS
-constexpr int SBATCH = 13;            // vector loads per superblock batch
+constexpr int SA = 32 * ROW;           // staged activations of one superblock (32 rows)
+constexpr int SW = 5 * 1024;           // staged weight blocks of 32 rows (4608 B used)
+constexpr int SBATCH = 8 + 5 + 4 + 2;  // vector-memory instructions per superblock
+
+struct SRegs {           // a superblock's register operands
+    v4f da[4];           // activation scales of rows 8q + 4g .. +3
+    v2u ahi, alo;        // min-term operands of row ln, sub-blocks 4g..4g+3
+};
 
 __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) {
-    // per wave: scales [sb][32 rows], min-term operands [sb][hi/lo][32 rows][16 B]
-    __shared__ __attribute__((aligned(16))) float s_dd[SWAVES][SMAXSB][32];
-    __shared__ __attribute__((aligned(16))) int8_t s_ll[SWAVES][SMAXSB][2][32 * 16];
-    __shared__ __attribute__((aligned(16))) float s_red[SMT][16][64];
+    // one array per stage and operand, so that copies into one stage are
+    // never mistaken for writes to the stage being read
+    __shared__ __attribute__((aligned(16))) int8_t s_a0[SWAVES][SA], s_a1[SWAVES][SA], s_a2[SWAVES][SA];
+    __shared__ __attribute__((aligned(16))) int8_t s_w0[SWAVES][SW], s_w1[SWAVES][SW], s_w2[SWAVES][SW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -422,6 +452,10 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
     const int rowbytes = nsb * BB;
     const int sb0 = h * nsb / SKH, sb1 = (h + 1) * nsb / SKH;
     const int nk = 32 * t < M ? sb1 - sb0 : 0;  // a tile past M has no work
+    struct Stage {
+        int8_t *a, *w;
+    };
+    const Stage st[3] = {{s_a0[wave], s_w0[wave]}, {s_a1[wave], s_w1[wave]}, {s_a2[wave], s_w2[wave]}};
 
     const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
     const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
@@ -429,40 +463,73 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
 
-    // this tile's scales (two superblocks per dword copy: lane -> sb 2i + g,
-    // row ln) and min-term operands (lane -> plane g, row ln) -> LDS
-    for (int j = 0; j < nk; j += 2)
-        copy4(rs_d, &s_dd[wave][j][0], ((sb0 + j + g) * M + 32 * t + ln) * 4, 0);
-    for (int j = 0; j < nk; ++j)
-        copy16(rs_l, &s_ll[wave][j][0][0], (((sb0 + j) * 2 + g) * M + 32 * t + ln) * 16, 0);
+    // Activation copy i (1 KiB) covers rows 4i .. 4i+3 of the tile: lane l
+    // fills position l%16 of row 4i + l/16 with piece (l%16) ^ (row%16), so
+    // that the MFMA-layout reads below are free of bank conflicts.  With
+    // r0 = l/16 the piece index is ((l%16) ^ r0) ^ 4(i%4): the i-dependent
+    // part is an XOR of 64*(i%4) on the byte offset.
+    const int r0 = lane >> 4;
+    const int a_vb = (32 * t + r0) * K + 16 * ((lane & 15) ^ r0);
+    // Weight copy i: flat 16-byte piece f = 64i + l is piece f%9 of row f/9
+    // (nine pieces per 144-byte block, rows laid end to end in LDS).  Pieces
+    // past row 31 land in the unused tail of the stage.
+    int w_vb[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int f = 64 * i + lane;
+        w_vb[i] = (n0 + f / 9) * rowbytes + 16 * (f % 9);
+    }
+    const int d_row = 32 * t + 8 * 0 + 4 * g;  // + 8q below
+    const int l_row = 32 * t + ln;
 
-    // one superblock's operands: activation fragments per K-step and the
-    // weight block of this lane's row
-    struct Batch {
-        v4i af[8];
-        WRaw w;
-    };
-    const int w_row = (n0 + ln) * rowbytes;
-    const int a_row = (32 * t + ln) * K;
-    auto issue = [&](int j, Batch &B) {
+    auto issue = [&](int j, const Stage &S, SRegs &R) {
         const int sb = sb0 + min(j, nk - 1);  // past the end: re-read the last (unused)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int k0 = 128 * g + 64 * ((s & 3) >> 1) + 16 * (s & 1) + 32 * (s >> 2);
-            B.af[s] = ld16(rs_a, a_row + k0, sb * ROW);
-        }
-        const int so = sb * BB;
-        B.w.hdr = ld16(rs_w, w_row, so);
+        for (int i = 0; i < 8; ++i)
+            copy16(rs_a, S.a + 1024 * i, a_vb ^ (64 * (i & 3)), 4 * i * K + sb * ROW);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) B.w.q[i] = ld16(rs_w, w_row + 16 + 64 * g + 16 * i, so);
+        for (int i = 0; i < 5; ++i) copy16(rs_w, S.w + 1024 * i, w_vb[i], sb * BB);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            R.da[q] = __builtin_bit_cast(v4f, ld16(rs_d, (d_row + 8 * q) * 4, sb * M * 4));
+        R.ahi = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, sb * 2 * M * 16, 0));
+        R.alo = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, (sb * 2 + 1) * M * 16, 0));
         __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // MFMA-layout reads: K-step s of lane (ln, g) is piece p = 8g + c(s) of
+    // row ln; as in the big tile, p ^ (ln % 16) splits into bit 3 and bits 0..2
+    const int frag_base = ln * ROW + (((8 * g) ^ (ln & 8)) << 4);
+    const int frag_x = (ln & 7) << 4;
+    auto frag = [&](int s) {
+        const int c = 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
+        return frag_base + ((c << 4) ^ frag_x);
     };
 
     v16f out = v16f{};
 
-    auto superblock = [&](int j, const Batch &B) {
-        const v4i hdr = B.w.hdr;
+    auto superblock = [&](const Stage &S, const SRegs &R) {
+        // weights (header, then this lane's 64 nibble bytes), then the eight
+        // activation fragments; 13 reads in flight, consumed in order
+        const uint32_t wrow = lds_addr(S.w) + BB * ln;
+        const uint32_t wnib = wrow + 64 * g;
+        const uint32_t abase = lds_addr(S.a);
+        v4i hdr = lds_read16<0>(wrow);
+        v4i wq[4];
+        wq[0] = lds_read16<16>(wnib);
+        wq[1] = lds_read16<32>(wnib);
+        wq[2] = lds_read16<48>(wnib);
+        wq[3] = lds_read16<64>(wnib);
+        v4i af[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) af[s] = lds_read16<0>(abase + frag(s));
+        lds_wait<12>(hdr);
+        lds_wait<8>(wq[0]);
+        lds_wait<8>(wq[1]);
+        lds_wait<8>(wq[2]);
+        lds_wait<8>(wq[3]);
+
         const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2], w3 = (uint32_t)hdr[3];
         const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
         const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
@@ -477,10 +544,21 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
                 v4i bq;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t q = (uint32_t)B.w.q[s & 3][e];
+                    const uint32_t q = (uint32_t)wq[s & 3][e];
                     bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
                 }
-                acc = (pass == 0 && s == 0) ? mma_i8(B.af[s], bq, v16i{}) : mma_i8(B.af[s], bq, acc);
+                if (pass == 0) {
+                    // fragment s is the (s+6)-th of the 13 reads
+                    if (s == 0) lds_wait<7>(af[0]);
+                    if (s == 1) lds_wait<6>(af[1]);
+                    if (s == 2) lds_wait<5>(af[2]);
+                    if (s == 3) lds_wait<4>(af[3]);
+                    if (s == 4) lds_wait<3>(af[4]);
+                    if (s == 5) lds_wait<2>(af[5]);
+                    if (s == 6) lds_wait<1>(af[6]);
+                    if (s == 7) lds_wait<0>(af[7]);
+                }
+                acc = (pass == 0 && s == 0) ? mma_i8(af[s], bq, v16i{}) : mma_i8(af[s], bq, acc);
             }
             if (pass == 0) {
 #pragma unroll
@@ -488,14 +566,12 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const v4f da4 = *reinterpret_cast<const v4f *>(&s_dd[wave][j & ~1][32 * (j & 1) + 8 * q + 4 * g]);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * q + i;
-                out[r] = fmaf((float)acc[r], da4[i] * dw, out[r]);
+                out[r] = fmaf((float)acc[r], R.da[q][i] * dw, out[r]);
             }
-        }
         const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
         const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
         v8bf b1, b2;
@@ -509,51 +585,50 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
             b2[i] = lb;
             b2[4 + i] = (__bf16)0.0f;
         }
-        const int8_t *lp = &s_ll[wave][j][0][ln * 16 + 8 * g];
-        const v2u ahi = *reinterpret_cast<const v2u *>(lp);
-        const v2u alo = *reinterpret_cast<const v2u *>(lp + 32 * 16);
-        const v4i avv = {(int)ahi.x, (int)ahi.y, (int)alo.x, (int)alo.y};
+        const v4i avv = {(int)R.ahi.x, (int)R.ahi.y, (int)R.alo.x, (int)R.alo.y};
         const v8bf am = __builtin_bit_cast(v8bf, avv);
         out = mma_bf16(am, b1, out);
         out = mma_bf16(am, b2, out);
     };
 
     if (nk > 0) {
-        // The LDS copies sit ahead of batch 0 in the vector-memory queue, so
-        // the wait for batch 0 also covers them.  The loop body is three
-        // whole superblocks with no exit, so every path into its head leaves
-        // the same two batches in flight; batches issued past the end re-read
-        // the last superblock and are drained unused.
-        Batch b0, b1, b2;
-        issue(0, b0);
-        issue(1, b1);
+        // The loop body is three whole superblocks with no exit, so every
+        // path into its head leaves the same two batches in flight; batches
+        // issued past the end re-read the last superblock and are drained
+        // unused.
+        SRegs r0s, r1s, r2s;
+        issue(0, st[0], r0s);
+        issue(1, st[1], r1s);
         int j = 0;
         for (; j + 3 <= nk; j += 3) {
-            issue(j + 2, b2);
+            issue(j + 2, st[2], r2s);
             wait_vmcnt<2 * SBATCH>();
-            superblock(j, b0);
-            issue(j + 3, b0);
+            superblock(st[0], r0s);
+            issue(j + 3, st[0], r0s);
             wait_vmcnt<2 * SBATCH>();
-            superblock(j + 1, b1);
-            issue(j + 4, b1);
+            superblock(st[1], r1s);
+            issue(j + 4, st[1], r1s);
             wait_vmcnt<2 * SBATCH>();
-            superblock(j + 2, b2);
+            superblock(st[2], r2s);
         }
         if (j < nk) {
             wait_vmcnt<SBATCH>();
-            superblock(j, b0);
+            superblock(st[0], r0s);
             if (j + 1 < nk) {
                 wait_vmcnt<0>();
-                superblock(j + 1, b1);
+                superblock(st[1], r1s);
             }
         }
-        wait_vmcnt<0>();
     }
+    // no copy may still be writing this wave's stages
+    wait_vmcnt<0>();
 
-    // sum the two K-halves in a fixed order: the h = 1 waves park theirs in LDS
+    // sum the two K-halves in a fixed order: the h = 1 waves park theirs in
+    // their own (now idle) first stage
+    float *const red = reinterpret_cast<float *>(s_a0[2 + t]);  // wave (h = 1, t)
     if (h == 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s_red[t][r][lane] = out[r];
+        for (int r = 0; r < 16; ++r) red[64 * r + lane] = out[r];
     }
     __syncthreads();
     if (h == 0 && 32 * t < M) {
@@ -561,7 +636,7 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
         const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
         v16f sum = out;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] += s_red[t][r][lane];
+        for (int r = 0; r < 16; ++r) sum[r] += red[64 * r + lane];
         const v16i bits = __builtin_bit_cast(v16i, sum);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -612,7 +687,7 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
-    if (M <= 32 * q4w::SMT && a.nsb <= q4w::SKH * q4w::SMAXSB) {
+    if (M <= 32 * q4w::SMT) {
         hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
                            dim3(64 * q4w::SWAVES), 0, stream, a);
         return hipGetLastError();
