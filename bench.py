@@ -39,7 +39,8 @@ METRIC = "effective int8 TOPS + prefill tok/s, Q4_K x Q8_K 4096x14336 GEMM; % of
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
-GEMM_SOURCE = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc", "kq_gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc", f)
+                for f in ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp")]
 
 
 def log(*a):
@@ -47,8 +48,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) over the GEMM kernel sources, in order."""
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
