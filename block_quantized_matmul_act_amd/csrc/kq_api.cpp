@@ -92,8 +92,8 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     // grid limits: tiles must fit a 1-D grid
     const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
-    // the GEMM kernel addresses a 128-row tile of qs or W, the d section and
-    // the alpha section with 32-bit buffer offsets
+    // the GEMM kernels address whole tensors (W, the qs, d and alpha sections,
+    // out) and 128-row tiles of them with 32-bit buffer offsets
     const int64_t lim = (int64_t)1 << 31;
     if (128 * K >= lim || 128 * (K / qk_of(fmt)) * bb_of(fmt) >= lim || 128 * N * 4 >= lim ||
         M * K >= lim || N * (K / qk_of(fmt)) * bb_of(fmt) >= lim || M * N * 4 >= lim ||

@@ -143,9 +143,10 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
  * Q4_K/Q6_K scales and mins folded in) and the PTQ1_0 MMQ path of llama.cpp
  * PR 214.  The fp32 result agrees with the exact product of the dequantized
  * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.  The kernels
- * address each 128-row tile and each activation section with 32-bit
- * offsets: shapes where 128*K, 128 weight rows, the d section or the alpha
- * section reach 2^31 bytes are declined with KQ_ERR_UNSUPPORTED.
+ * address every operand with 32-bit byte offsets: shapes where the weight
+ * tensor, an activation section (qs, d, alpha), the output, or a 128-row
+ * tile of qs, W or out reaches 2^31 bytes are declined with
+ * KQ_ERR_UNSUPPORTED.
  */
 int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
             float *out, hipStream_t stream);
