@@ -417,31 +417,41 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // Few tokens (M <= 64): the product is bound by streaming the weights from
 // HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
 // weight rows and runs 4 independent waves: wave (h, t) takes m-tile t (32
-// tokens) over superblock half h.  Each wave stages its own operands through
-// LDS with coalesced buffer -> LDS copies (consecutive lanes read consecutive
-// bytes of one row, so a copy touches 8 to 14 cache lines instead of one per
-// lane), three superblocks deep, and reads them back in MFMA layout.  The
-// activation scales and min-term operands ride in registers with the same
-// batch.  No barrier is needed until the two K-halves of a tile are summed in
-// LDS at the end.
+// tokens) over superblock half h; two workgroups share a CU.  Each wave
+// stages its own operands through LDS in half-superblocks (128 values: 4 KiB
+// of activations, the 64 nibble bytes and the 16-byte header of 32 weight
+// blocks), three stages deep, with coalesced buffer -> LDS copies
+// (consecutive lanes read consecutive bytes of a row, so a copy touches a
+// handful of cache lines instead of one per lane).  Both scale digits are
+// multiplied as soon as a fragment arrives, into two int32 planes combined
+// at the superblock's end.  No barrier is needed until the two K-halves of a
+// tile are summed in LDS.
+//
+// K-step s (0..3) of half H uses nibble half n = s/2 of chunk pair cp = s%2:
+// lane group g holds weight chunk c = 2cp + g (nibble bytes 64H + 16c ..
+// +16), i.e. values k = 128H + 64cp + 32n + 16g + i, all of sub-block
+// j = 4H + 2cp + n; the activation fragment is the same 16 values of the
+// lane's row, piece p = 4cp + 2n + g of the half-row.
 // ---------------------------------------------------------------------------
-constexpr int SMT = 2;                 // 32-row m-tiles (64 tokens)
-constexpr int SKH = 2;                 // K-split: superblock halves
+constexpr int SMT = 2;                      // 32-row m-tiles (64 tokens)
+constexpr int SKH = 2;                      // K-split: superblock halves
 constexpr int SWAVES = SMT * SKH;
-constexpr int SA = 32 * ROW;           // staged activations of one superblock (32 rows)
-constexpr int SW = 5 * 1024;           // staged weight blocks of 32 rows (4608 B used)
-constexpr int SBATCH = 8 + 5 + 4 + 2;  // vector-memory instructions per superblock
+constexpr int SA = 32 * 128;                // half-row activations of 32 rows
+constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 blocks
+constexpr int SHD = 32 * 16;                // block headers of 32 rows
+constexpr int SSLOT = SA + SWN + SHD;       // one stage
+constexpr int SNST = 3;                     // stages per wave
+constexpr int SDA = 4 + 2;                  // activation scale and min-operand loads per superblock
+constexpr int SCOPY0 = 4 + 2 + 2;           // copies of a first-half stage (with headers)
+constexpr int SCOPY1 = 4 + 2;               // copies of a second-half stage
 
 struct SRegs {           // a superblock's register operands
     v4f da[4];           // activation scales of rows 8q + 4g .. +3
     v2u ahi, alo;        // min-term operands of row ln, sub-blocks 4g..4g+3
 };
 
-__global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) {
-    // one array per stage and operand, so that copies into one stage are
-    // never mistaken for writes to the stage being read
-    __shared__ __attribute__((aligned(16))) int8_t s_a0[SWAVES][SA], s_a1[SWAVES][SA], s_a2[SWAVES][SA];
-    __shared__ __attribute__((aligned(16))) int8_t s_w0[SWAVES][SW], s_w1[SWAVES][SW], s_w2[SWAVES][SW];
+__global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[SWAVES][SNST][SSLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,10 +462,6 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
     const int rowbytes = nsb * BB;
     const int sb0 = h * nsb / SKH, sb1 = (h + 1) * nsb / SKH;
     const int nk = 32 * t < M ? sb1 - sb0 : 0;  // a tile past M has no work
-    struct Stage {
-        int8_t *a, *w;
-    };
-    const Stage st[3] = {{s_a0[wave], s_w0[wave]}, {s_a1[wave], s_w1[wave]}, {s_a2[wave], s_w2[wave]}};
 
     const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
     const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
@@ -463,169 +469,171 @@ __global__ __launch_bounds__(64 * SWAVES, 1) void gemm_q4k_small_kernel(Args a) 
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
 
-    // Activation copy i (1 KiB) covers rows 4i .. 4i+3 of the tile: lane l
-    // fills position l%16 of row 4i + l/16 with piece (l%16) ^ (row%16), so
-    // that the MFMA-layout reads below are free of bank conflicts.  With
-    // r0 = l/16 the piece index is ((l%16) ^ r0) ^ 4(i%4): the i-dependent
-    // part is an XOR of 64*(i%4) on the byte offset.
-    const int r0 = lane >> 4;
-    const int a_vb = (32 * t + r0) * K + 16 * ((lane & 15) ^ r0);
-    // Weight copy i: flat 16-byte piece f = 64i + l is piece f%9 of row f/9
-    // (nine pieces per 144-byte block, rows laid end to end in LDS).  Pieces
-    // past row 31 land in the unused tail of the stage.
-    int w_vb[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int f = 64 * i + lane;
-        w_vb[i] = (n0 + f / 9) * rowbytes + 16 * (f % 9);
-    }
-    const int d_row = 32 * t + 8 * 0 + 4 * g;  // + 8q below
+    // Activation copy i (1 KiB) covers rows 8i .. 8i+7 of the tile (128 bytes
+    // each); lane l fills position l%8 of row 8i + l/8 with piece
+    // (l%8) ^ ((row/2) % 8) = ((l%8) ^ (l/16)) ^ 4(i%2): the i-dependent part
+    // is an XOR of 64*(i%2) on the byte offset.  The reads below are then free
+    // of bank conflicts.
+    const int a_vb = (32 * t + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 4));
+    // Nibble copy i: piece f = 64i + l is piece f%4 of row f/4 (64 bytes per
+    // row); header copy i: dword e = 64i + l is dword e%4 of row e/4.
+    // (unsigned: rows past N in the last strip may pass 2^31; the buffer
+    // range check drops them)
+    const uint32_t wr0 = (uint32_t)(n0 + (lane >> 2)) * (uint32_t)rowbytes;
+    const uint32_t wr1 = wr0 + 16u * (uint32_t)rowbytes;
+    const int w_vb0 = (int)(wr0 + 16 + 16 * (lane & 3));
+    const int w_vb1 = (int)(wr1 + 16 + 16 * (lane & 3));
+    const int h_vb0 = (int)(wr0 + 4 * (lane & 3));
+    const int h_vb1 = (int)(wr1 + 4 * (lane & 3));
+    const int d_row = 32 * t + 4 * g;  // + 8q below
     const int l_row = 32 * t + ln;
 
-    auto issue = [&](int j, const Stage &S, SRegs &R) {
-        const int sb = sb0 + min(j, nk - 1);  // past the end: re-read the last (unused)
-        __builtin_amdgcn_sched_barrier(0);
+    int8_t *const my = &s_lds[wave][0][0];
+    // stage j: superblock sb0 + j/2 (clamped: past the end re-reads the last,
+    // unused), half j%2 (a compile-time H in every caller)
+    auto issue = [&](int j, int H) {
+        const int sb = sb0 + min(j >> 1, nk - 1);
+        int8_t *S = my + (j % SNST) * SSLOT;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            copy16(rs_a, S.a + 1024 * i, a_vb ^ (64 * (i & 3)), 4 * i * K + sb * ROW);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) copy16(rs_w, S.w + 1024 * i, w_vb[i], sb * BB);
+        for (int i = 0; i < 4; ++i)
+            copy16(rs_a, S + 1024 * i, a_vb ^ (64 * (i & 1)), 8 * i * K + sb * ROW + 128 * H);
+        copy16(rs_w, S + SA, w_vb0, sb * BB + 64 * H);
+        copy16(rs_w, S + SA + 1024, w_vb1, sb * BB + 64 * H);
+        if (H == 0) {
+            copy4(rs_w, S + SA + SWN, h_vb0, sb * BB);
+            copy4(rs_w, S + SA + SWN + 256, h_vb1, sb * BB);
+        }
+    };
+    SRegs R0, R1;  // scales of even and odd superblocks, two superblocks ahead
+    auto issue_scales = [&](int sbx, SRegs &R) {
+        const int sb = sb0 + min(sbx, nk - 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             R.da[q] = __builtin_bit_cast(v4f, ld16(rs_d, (d_row + 8 * q) * 4, sb * M * 4));
         R.ahi = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, sb * 2 * M * 16, 0));
         R.alo = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, (sb * 2 + 1) * M * 16, 0));
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // MFMA-layout reads: K-step s of lane (ln, g) is piece p = 8g + c(s) of
-    // row ln; as in the big tile, p ^ (ln % 16) splits into bit 3 and bits 0..2
-    const int frag_base = ln * ROW + (((8 * g) ^ (ln & 8)) << 4);
-    const int frag_x = (ln & 7) << 4;
-    auto frag = [&](int s) {
-        const int c = 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
-        return frag_base + ((c << 4) ^ frag_x);
-    };
-
+    const int afx = (ln >> 1) & 7;
     v16f out = v16f{};
+    v16i acc_h, acc_l;
+    v4i hdr;
 
-    auto superblock = [&](const Stage &S, const SRegs &R) {
-        // weights (header, then this lane's 64 nibble bytes), then the eight
-        // activation fragments; 13 reads in flight, consumed in order
-        const uint32_t wrow = lds_addr(S.w) + BB * ln;
-        const uint32_t wnib = wrow + 64 * g;
-        const uint32_t abase = lds_addr(S.a);
-        v4i hdr = lds_read16<0>(wrow);
-        v4i wq[4];
-        wq[0] = lds_read16<16>(wnib);
-        wq[1] = lds_read16<32>(wnib);
-        wq[2] = lds_read16<48>(wnib);
-        wq[3] = lds_read16<64>(wnib);
-        v4i af[8];
+    // one half-superblock: H compile-time, slot runtime; R the superblock's
+    // scales, fold = false for the phantom superblock that rounds nk up to even
+    auto half = [&](auto HH, int j, const SRegs &R, bool fold) {
+        constexpr int H = decltype(HH)::value;
+        const uint32_t S = lds_addr(my + (j % SNST) * SSLOT);
+        const uint32_t arow = S + 128 * ln;
+        const uint32_t wrow = S + 64 * ln + 16 * g;  // + SA in the read offset
+        if (H == 0) hdr = lds_read16<SA + SWN>(S + 16 * ln);
+        v4i wq0 = lds_read16<SA>(wrow);
+        v4i wq1 = lds_read16<SA + 32>(wrow);
+        v4i af[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) af[s] = lds_read16<0>(abase + frag(s));
-        lds_wait<12>(hdr);
-        lds_wait<8>(wq[0]);
-        lds_wait<8>(wq[1]);
-        lds_wait<8>(wq[2]);
-        lds_wait<8>(wq[3]);
-
-        const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2], w3 = (uint32_t)hdr[3];
-        const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
-        const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
-        const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
-        v16i acc;
+        for (int s = 0; s < 4; ++s) {
+            const int p = 4 * (s & 1) + 2 * (s >> 1) + g;
+            af[s] = lds_read16<0>(arow + 16 * (p ^ afx));
+        }
+        if (H == 0) lds_wait<6>(hdr);
+        lds_wait<5>(wq0);
+        lds_wait<4>(wq1);
+        // scale digits of the four sub-blocks of this half
+        const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2];
+        const uint32_t x = H == 0 ? w1 : __builtin_amdgcn_alignbit(w2, w1, 24);
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int s = 0; s < 4; ++s) {
+            const int cp = s & 1, n = s >> 1;
+            const uint32_t sc = (x >> (6 * (2 * cp + n))) & 63u;
+            const v4i &wq = cp ? wq1 : wq0;
+            v4i bh, bl;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int si = 2 * ((s & 3) >> 1) + (s >> 2);
-                const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
-                v4i bq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t q = (uint32_t)wq[s & 3][e];
-                    bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
-                }
-                if (pass == 0) {
-                    // fragment s is the (s+6)-th of the 13 reads
-                    if (s == 0) lds_wait<7>(af[0]);
-                    if (s == 1) lds_wait<6>(af[1]);
-                    if (s == 2) lds_wait<5>(af[2]);
-                    if (s == 3) lds_wait<4>(af[3]);
-                    if (s == 4) lds_wait<3>(af[4]);
-                    if (s == 5) lds_wait<2>(af[5]);
-                    if (s == 6) lds_wait<1>(af[6]);
-                    if (s == 7) lds_wait<0>(af[7]);
-                }
-                acc = (pass == 0 && s == 0) ? mma_i8(af[s], bq, v16i{}) : mma_i8(af[s], bq, acc);
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t q = (uint32_t)wq[e];
+                const uint32_t nib = n ? (q >> 4) & 0x0F0F0F0Fu : q & 0x0F0F0F0Fu;
+                bh[e] = mul_digit(nib, sc >> 3);
+                bl[e] = mul_digit(nib, sc & 7u);
             }
-            if (pass == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] <<= 3;
+            if (s == 0) lds_wait<3>(af[0]);
+            if (s == 1) lds_wait<2>(af[1]);
+            if (s == 2) lds_wait<1>(af[2]);
+            if (s == 3) lds_wait<0>(af[3]);
+            if (H == 0 && s == 0) {
+                acc_h = mma_i8(af[s], bh, v16i{});
+                acc_l = mma_i8(af[s], bl, v16i{});
+            } else {
+                acc_h = mma_i8(af[s], bh, acc_h);
+                acc_l = mma_i8(af[s], bl, acc_l);
             }
         }
+        if (H == 1 && fold) {
+            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n]
+            const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
+            const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * q + i;
+                    const int T = (acc_h[r] << 3) + acc_l[r];
+                    out[r] = fmaf((float)T, R.da[q][i] * dw, out[r]);
+                }
+            // min term, as in the large tile
+            const uint32_t w3 = (uint32_t)hdr[3];
+            const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
+            const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
+            v8bf b1, b2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 4 * q + i;
-                out[r] = fmaf((float)acc[r], R.da[q][i] * dw, out[r]);
+                const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
+                __bf16 hb, lb;
+                split_bf16(beta, hb, lb);
+                b1[i] = hb;
+                b1[4 + i] = hb;
+                b2[i] = lb;
+                b2[4 + i] = (__bf16)0.0f;
             }
-        const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
-        const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
-        v8bf b1, b2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
-            __bf16 hb, lb;
-            split_bf16(beta, hb, lb);
-            b1[i] = hb;
-            b1[4 + i] = hb;
-            b2[i] = lb;
-            b2[4 + i] = (__bf16)0.0f;
+            const v4i avv = {(int)R.ahi.x, (int)R.ahi.y, (int)R.alo.x, (int)R.alo.y};
+            const v8bf am = __builtin_bit_cast(v8bf, avv);
+            out = mma_bf16(am, b1, out);
+            out = mma_bf16(am, b2, out);
         }
-        const v4i avv = {(int)R.ahi.x, (int)R.ahi.y, (int)R.alo.x, (int)R.alo.y};
-        const v8bf am = __builtin_bit_cast(v8bf, avv);
-        out = mma_bf16(am, b1, out);
-        out = mma_bf16(am, b2, out);
     };
 
     if (nk > 0) {
-        // The loop body is three whole superblocks with no exit, so every
-        // path into its head leaves the same two batches in flight; batches
-        // issued past the end re-read the last superblock and are drained
-        // unused.
-        SRegs r0s, r1s, r2s;
-        issue(0, st[0], r0s);
-        issue(1, st[1], r1s);
-        int j = 0;
-        for (; j + 3 <= nk; j += 3) {
-            issue(j + 2, st[2], r2s);
-            wait_vmcnt<2 * SBATCH>();
-            superblock(st[0], r0s);
-            issue(j + 3, st[0], r0s);
-            wait_vmcnt<2 * SBATCH>();
-            superblock(st[1], r1s);
-            issue(j + 4, st[1], r1s);
-            wait_vmcnt<2 * SBATCH>();
-            superblock(st[2], r2s);
-        }
-        if (j < nk) {
-            wait_vmcnt<SBATCH>();
-            superblock(st[0], r0s);
-            if (j + 1 < nk) {
-                wait_vmcnt<0>();
-                superblock(st[1], r1s);
-            }
+        // Every iteration is two superblocks (four halves) with no exit, so
+        // each wait below sees the same loads in flight on every pass.  In
+        // issue order a superblock k queues the copies of stages 2k+2 (a first
+        // half: SCOPY0) and 2k+3 (SCOPY1), then the scales of superblock k+2
+        // (SDA).  At a first half, stage 2k's copies are followed by stage
+        // 2k+1's and superblock k+1's scales; at a second half, stage 2k+1's
+        // by those scales and stage 2k+2's copies.  Stages and scales issued
+        // past the end re-read the last superblock and are drained unused.
+        auto superblock = [&](int k, SRegs &R) {
+            const int j = 2 * k;
+            wait_vmcnt<SCOPY1 + SDA>();
+            issue(j + 2, 0);
+            half(std::integral_constant<int, 0>{}, j, R, k < nk);
+            wait_vmcnt<SDA + SCOPY0>();
+            issue(j + 3, 1);
+            half(std::integral_constant<int, 1>{}, j + 1, R, k < nk);
+            issue_scales(k + 2, R);
+        };
+        issue_scales(0, R0);
+        issue(0, 0);
+        issue(1, 1);
+        issue_scales(1, R1);
+        for (int k = 0; k < nk; k += 2) {
+            superblock(k, R0);
+            superblock(k + 1, R1);
         }
     }
     // no copy may still be writing this wave's stages
     wait_vmcnt<0>();
 
     // sum the two K-halves in a fixed order: the h = 1 waves park theirs in
-    // their own (now idle) first stage
-    float *const red = reinterpret_cast<float *>(s_a0[2 + t]);  // wave (h = 1, t)
+    // their own (now idle) stages
+    float *const red = reinterpret_cast<float *>(&s_lds[2 + t][0][0]);  // wave (h = 1, t)
     if (h == 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[64 * r + lane] = out[r];
