@@ -43,7 +43,7 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
 GEMM_SOURCES = [os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc", f)
-                for f in ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp")]
+                for f in ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp")]
 
 
 def log(*a):

@@ -9,21 +9,14 @@
 #include <atomic>
 #include <cstdint>
 
-namespace kq {
-hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_t *bsums,
-                            uint16_t *alpha, int64_t M, int64_t K, hipStream_t stream);
-hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
-                       const uint16_t *alpha, float *out, int M, int N, int K,
-                       hipStream_t stream);
-hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
-                          int K, hipStream_t stream);
-}  // namespace kq
+#include "kq_launch.hpp"
 
 namespace {
 
 enum Variant {
     V_QUANT_Q8K = 0,
     V_QUANT_Q8_128,
+    V_GEMM_Q4K_M64,
     V_GEMM_Q4K_128x128,
     V_GEMM_Q6K_128x128,
     V_GEMM_TQ_128x128,
@@ -34,8 +27,9 @@ enum Variant {
 };
 
 const char *const kVariantNames[V_COUNT] = {
-    "quant_q8_k",        "quant_q8_128",      "gemm_q4_k_128x128", "gemm_q6_k_128x128",
-    "gemm_tq_128x128",   "subsums_q4_k",      "subsums_q6_k",      "subsums_tq",
+    "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128",
+    "gemm_q6_k_128x128", "gemm_tq_128x128", "subsums_q4_k",  "subsums_q6_k",
+    "subsums_tq",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -93,18 +87,23 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
     // the GEMM kernels address whole tensors (W, the qs, d and alpha sections,
-    // out) and 128-row tiles of them with 32-bit buffer offsets
+    // out) with 32-bit buffer offsets, including the rows and columns a last
+    // tile hangs past M (up to 128) and N (up to 256): every such offset stays
+    // below 2^31, so adding the 2^31 "drop this store" offset cannot wrap
     const int64_t lim = (int64_t)1 << 31;
-    if (128 * K >= lim || 128 * (K / qk_of(fmt)) * bb_of(fmt) >= lim || 128 * N * 4 >= lim ||
-        M * K >= lim || N * (K / qk_of(fmt)) * bb_of(fmt) >= lim || M * N * 4 >= lim ||
-        (K / qk_of(fmt)) * M * 4 >= lim || (K / 256) * 2 * M * 16 >= lim)
+    const int64_t rowbytes = (K / qk_of(fmt)) * bb_of(fmt);
+    if ((M + 128) * K >= lim || (N + 256) * rowbytes >= lim || (M + 128) * N * 4 >= lim ||
+        (K / qk_of(fmt)) * (M + 256) * 4 >= lim || (K / 256) * 2 * (M + 256) * 16 >= lim)
         return KQ_ERR_UNSUPPORTED;
     return 1;  // proceed
 }
 
-int variant_for(int fmt) {
-    return fmt == KQ_Q4_K ? V_GEMM_Q4K_128x128 : fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128
-                                                                 : V_GEMM_TQ_128x128;
+int variant_for(int fmt, int64_t M, int64_t N) {
+    if (fmt == KQ_Q4_K) {
+        return kq::q4k_kernel_choice((int)M, (int)N) == kq::Q4K_FEW_TOKENS ? V_GEMM_Q4K_M64
+                                                                             : V_GEMM_Q4K_128x128;
+    }
+    return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
 }
 
 }  // namespace
@@ -163,7 +162,8 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
 int kq_select_variant(int fmt, int64_t M, int64_t N, int64_t K) {
     if (!qk_of(fmt)) return KQ_ERR_FMT;
     if (M < 0 || N < 0 || K < 0 || K % qk_of(fmt)) return KQ_ERR_SHAPE;
-    return variant_for(fmt);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return KQ_ERR_SHAPE;
+    return variant_for(fmt, M, N);
 }
 
 int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
@@ -178,7 +178,7 @@ int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int6
         L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr, out, (int)M,
         (int)N, (int)K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
-    g_count[variant_for(fmt)].fetch_add(1);
+    g_count[variant_for(fmt, M, N)].fetch_add(1);
     return KQ_OK;
 }
 

@@ -44,6 +44,7 @@
 // is 16 registers per lane: register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 #include "kq_device.hpp"
+#include "kq_launch.hpp"
 
 #include <type_traits>
 
@@ -58,8 +59,9 @@ constexpr int BB = 144;               // Q4_K block bytes
 constexpr int LBUF = 2 * BM * 16;     // staged min-term operands (hi, lo) of one superblock
 constexpr int WG_PER_CU = 2;          // two workgroups (eight waves) share a CU
 constexpr int RSRC_FLAGS = 0x00020000;
-// A store offset the buffer range check always drops: outputs hold fewer than
-// 2^31 bytes, and a row offset (< 2^30) added to it cannot wrap 2^32.
+// A store offset the buffer range check always drops: the host checks that
+// every row offset, overhanging tile rows included, stays below 2^31, so
+// adding this cannot wrap 2^32 and always lands past the output.
 constexpr int OOB_VOFF = (int)0x80000000u;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -665,6 +667,13 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
 
 static int g_num_cus = 0;
 
+// Which Q4_K kernel a shape gets: few tokens -> the K-split weight-streaming
+// kernel; otherwise the 128 x 128 persistent kernel (two per CU).
+int q4k_kernel_choice(int M, int N) {
+    (void)N;
+    return M <= 32 * q4w::SMT ? Q4K_FEW_TOKENS : Q4K_TILE128;
+}
+
 hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                            const uint16_t *alpha, float *out, int M, int N, int K,
                            hipStream_t stream) {
@@ -695,13 +704,17 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
-    if (M <= 32 * q4w::SMT) {
-        hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
-                           dim3(64 * q4w::SWAVES), 0, stream, a);
-        return hipGetLastError();
+    switch (q4k_kernel_choice(M, N)) {
+        case Q4K_FEW_TOKENS:
+            hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
+                               dim3(64 * q4w::SWAVES), 0, stream, a);
+            break;
+        default: {
+            const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
+            hipLaunchKernelGGL(q4w::gemm_q4k_kernel, dim3(grid), dim3(q4w::NT), 0, stream, a);
+            break;
+        }
     }
-    const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
-    hipLaunchKernelGGL(q4w::gemm_q4k_kernel, dim3(grid), dim3(q4w::NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,23 @@
+// kq_launch.hpp -- host-side launchers of the kernels, and the shape rule
+// that picks the Q4_K kernel (shared by the launcher and the variant query).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+hipError_t launch_quant_act(int bs, const float *x, int8_t *qs, float *d, int16_t *bsums,
+                            uint16_t *alpha, int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
+                       const uint16_t *alpha, float *out, int M, int N, int K,
+                       hipStream_t stream);
+hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
+                          int K, hipStream_t stream);
+
+// Q4_K kernels: M <= 64 -> few-token kernel; otherwise the 128 x 128
+// persistent kernel.
+enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1 };
+int q4k_kernel_choice(int M, int N);
+
+}  // namespace kq

@@ -144,8 +144,8 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
  * PR 214.  The fp32 result agrees with the exact product of the dequantized
  * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.  The kernels
  * address every operand with 32-bit byte offsets: shapes where the weight
- * tensor, an activation section (qs, d, alpha), the output, or a 128-row
- * tile of qs, W or out reaches 2^31 bytes are declined with
+ * tensor plus 256 rows, or an activation section (qs, d, alpha) or the
+ * output plus 128 (scales: 256) rows, reaches 2^31 bytes are declined with
  * KQ_ERR_UNSUPPORTED.
  */
 int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,

@@ -121,6 +121,14 @@ def test_gemm_validation_without_hip(kq):
     assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 256, A + 2, s) == kq.KQ_ERR_ALIGN
     # 32-bit tile offsets: 128*K must stay below 2^31 bytes
     assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, 8, 1 << 24, A, s) == kq.KQ_ERR_UNSUPPORTED
+    # ... and so must the output plus the 128 rows a last tile hangs past M:
+    # 131000 x 4096 fp32 is below 2^31 bytes, 131128 x 4096 is not
+    assert 131000 * 4096 * 4 < 1 << 31 <= (131000 + 128) * 4096 * 4
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 131000, 4096, 256, A, s) == kq.KQ_ERR_UNSUPPORTED
+    # ... and the weights plus 256 overhanging rows (Q4_K, K = 4096: 2304 B a row)
+    n = (1 << 31) // 2304 - 100
+    assert n * 2304 < 1 << 31 <= (n + 256) * 2304
+    assert L.kq_gemm(kq.KQ_Q4_K, A, A, 8, n, 4096, A, s) == kq.KQ_ERR_UNSUPPORTED
     # empty problems are a no-op that succeeds, even with null pointers
     assert L.kq_gemm(kq.KQ_Q4_K, None, None, 0, 8, 256, None, s) == kq.KQ_OK
     assert L.kq_gemm(kq.KQ_Q6_K, None, None, 8, 0, 256, None, s) == kq.KQ_OK

@@ -232,6 +232,27 @@ def test_workload_full_size_sampled(kq, workloads, name):
     say(f"  max err/tol {r:.3g}")
 
 
+def test_large_ragged_tiles(kq, workloads):
+    """The persistent 128 x 128 kernel on a large shape ragged in both M (2000
+    = 15 tiles + 80 rows) and N (13999 = 109 tiles + 47 columns, odd), sliced
+    from the FFN draw; sampled output columns cover the first, last and
+    tile-edge columns."""
+    wl = datagen.WORKLOADS["ffn_up_q4k_2048"]
+    W, x = workloads("ffn_up_q4k_2048")
+    M, N, K = 2000, 13999, wl.K
+    v = kq.kq_select_variant(Q4_K, M, N, K)
+    assert kq.kq_variant_name(v) == "gemm_q4_k_128x128"
+    rng = np.random.default_rng(78)
+    edges = [0, 1, 31, 32, 127, 128, 255, 256, 13823, 13824, 13951, 13952, N - 1]
+    rows = np.unique(np.concatenate([edges, rng.choice(N, 40, replace=False)]))
+    say(f"gemm large ragged M={M} N={N} K={K}, {len(rows)} sampled columns")
+    before = kq.kq_dispatch_count(v)
+    r = gemm_vs_oracle(kq, Q4_K, np.ascontiguousarray(W[:N]), np.ascontiguousarray(x[:M]),
+                       M, N, K, rows=rows, what="large ragged")
+    assert kq.kq_dispatch_count(v) == before + 1
+    say(f"  max err/tol {r:.3g}")
+
+
 def test_other_reading_of_distributions(kq):
     """Config text 'same value distributions as config 1' read 0-based: outlier
     weights and LogNormal channel scales on the FFN shape (sliced)."""
