@@ -418,16 +418,17 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // Few tokens (M <= 64): the product is bound by streaming the weights from
 // HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
-// weight rows and runs 4 independent waves: wave (h, t) takes m-tile t (32
-// tokens) over superblock half h; two workgroups share a CU.  Each wave
-// stages its own operands through LDS in half-superblocks (128 values: 4 KiB
-// of activations, the 64 nibble bytes and the 16-byte header of 32 weight
-// blocks), three stages deep, with coalesced buffer -> LDS copies
-// (consecutive lanes read consecutive bytes of a row, so a copy touches a
-// handful of cache lines instead of one per lane).  Both scale digits are
-// multiplied as soon as a fragment arrives, into two int32 planes combined
-// at the superblock's end.  No barrier is needed until the two K-halves of a
-// tile are summed in LDS.
+// weight rows and runs 2 independent waves, wave h taking superblock half h
+// for all 64 token rows (two 32-row m-tiles, so each weight nibble is
+// unpacked once for both); two workgroups share a CU, one wave per SIMD.
+// Each wave stages its own operands through LDS in half-superblocks (128
+// values: 8 KiB of activations, the 64 nibble bytes and the 16-byte header
+// of 32 weight blocks), three stages deep, with coalesced buffer -> LDS
+// copies (consecutive lanes read consecutive bytes of a row, so a copy
+// touches a handful of cache lines instead of one per lane).  Both scale
+// digits are multiplied as soon as a fragment arrives, into two int32 planes
+// combined at the superblock's end.  No barrier is needed until the two
+// K-halves are summed in LDS.
 //
 // K-step s (0..3) of half H uses nibble half n = s/2 of chunk pair cp = s%2:
 // lane group g holds weight chunk c = 2cp + g (nibble bytes 64H + 16c ..
@@ -436,34 +437,32 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // lane's row, piece p = 4cp + 2n + g of the half-row.
 // ---------------------------------------------------------------------------
 constexpr int SMT = 2;                      // 32-row m-tiles (64 tokens)
-constexpr int SKH = 2;                      // K-split: superblock halves
-constexpr int SWAVES = SMT * SKH;
-constexpr int SA = 32 * 128;                // half-row activations of 32 rows
+constexpr int SKH = 2;                      // K-split: superblock halves (one wave each)
+constexpr int SA = 64 * 128;                // half-row activations of 64 rows
 constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 blocks
 constexpr int SHD = 32 * 16;                // block headers of 32 rows
 constexpr int SSLOT = SA + SWN + SHD;       // one stage
 constexpr int SNST = 3;                     // stages per wave
-constexpr int SDA = 4 + 2;                  // activation scale and min-operand loads per superblock
-constexpr int SCOPY0 = 4 + 2 + 2;           // copies of a first-half stage (with headers)
-constexpr int SCOPY1 = 4 + 2;               // copies of a second-half stage
+constexpr int SDA = SMT * (4 + 2);          // activation scale and min-operand loads per superblock
+constexpr int SCOPY0 = 8 + 2 + 2;           // copies of a first-half stage (with headers)
+constexpr int SCOPY1 = 8 + 2;               // copies of a second-half stage
 
-struct SRegs {           // a superblock's register operands
-    v4f da[4];           // activation scales of rows 8q + 4g .. +3
-    v2u ahi, alo;        // min-term operands of row ln, sub-blocks 4g..4g+3
+struct SRegs {             // a superblock's register operands, per m-tile
+    v4f da[SMT][4];        // activation scales of rows 32t + 8q + 4g .. +3
+    v2u ahi[SMT], alo[SMT];  // min-term operands of row 32t + ln, sub-blocks 4g..4g+3
 };
 
-__global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) int8_t s_lds[SWAVES][SNST][SSLOT];
+__global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][SNST][SSLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = wave & 1, h = wave >> 1;
+    const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31, g = lane >> 5;
     const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
     const int n0 = blockIdx.x * 32;
     const int rowbytes = nsb * BB;
     const int sb0 = h * nsb / SKH, sb1 = (h + 1) * nsb / SKH;
-    const int nk = 32 * t < M ? sb1 - sb0 : 0;  // a tile past M has no work
+    const int nk = sb1 - sb0;
 
     const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
     const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
@@ -471,12 +470,12 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
 
-    // Activation copy i (1 KiB) covers rows 8i .. 8i+7 of the tile (128 bytes
-    // each); lane l fills position l%8 of row 8i + l/8 with piece
+    // Activation copy i (1 KiB) covers rows 8i .. 8i+7 (128 bytes each);
+    // lane l fills position l%8 of row 8i + l/8 with piece
     // (l%8) ^ ((row/2) % 8) = ((l%8) ^ (l/16)) ^ 4(i%2): the i-dependent part
     // is an XOR of 64*(i%2) on the byte offset.  The reads below are then free
     // of bank conflicts.
-    const int a_vb = (32 * t + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 4));
+    const int a_vb = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 4));
     // Nibble copy i: piece f = 64i + l is piece f%4 of row f/4 (64 bytes per
     // row); header copy i: dword e = 64i + l is dword e%4 of row e/4.
     // (unsigned: rows past N in the last strip may pass 2^31; the buffer
@@ -487,17 +486,15 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
     const int w_vb1 = (int)(wr1 + 16 + 16 * (lane & 3));
     const int h_vb0 = (int)(wr0 + 4 * (lane & 3));
     const int h_vb1 = (int)(wr1 + 4 * (lane & 3));
-    const int d_row = 32 * t + 4 * g;  // + 8q below
-    const int l_row = 32 * t + ln;
 
-    int8_t *const my = &s_lds[wave][0][0];
+    int8_t *const my = &s_lds[h][0][0];
     // stage j: superblock sb0 + j/2 (clamped: past the end re-reads the last,
     // unused), half j%2 (a compile-time H in every caller)
-    auto issue = [&](int j, int H) {
+    auto issue = [&](int j, int H) __attribute__((always_inline)) {
         const int sb = sb0 + min(j >> 1, nk - 1);
         int8_t *S = my + (j % SNST) * SSLOT;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
             copy16(rs_a, S + 1024 * i, a_vb ^ (64 * (i & 1)), 8 * i * K + sb * ROW + 128 * H);
         copy16(rs_w, S + SA, w_vb0, sb * BB + 64 * H);
         copy16(rs_w, S + SA + 1024, w_vb1, sb * BB + 64 * H);
@@ -507,23 +504,29 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
         }
     };
     SRegs R0, R1;  // scales of even and odd superblocks, two superblocks ahead
-    auto issue_scales = [&](int sbx, SRegs &R) {
+    auto issue_scales = [&](int sbx, SRegs &R) __attribute__((always_inline)) {
         const int sb = sb0 + min(sbx, nk - 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            R.da[q] = __builtin_bit_cast(v4f, ld16(rs_d, (d_row + 8 * q) * 4, sb * M * 4));
-        R.ahi = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, sb * 2 * M * 16, 0));
-        R.alo = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, l_row * 16 + 8 * g, (sb * 2 + 1) * M * 16, 0));
+        for (int t = 0; t < SMT; ++t) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                R.da[t][q] = __builtin_bit_cast(v4f, ld16(rs_d, (32 * t + 8 * q + 4 * g) * 4, sb * M * 4));
+            const int lrow = (32 * t + ln) * 16 + 8 * g;
+            R.ahi[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, lrow, sb * 2 * M * 16, 0));
+            R.alo[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, lrow, (sb * 2 + 1) * M * 16, 0));
+        }
     };
 
     const int afx = (ln >> 1) & 7;
-    v16f out = v16f{};
-    v16i acc_h, acc_l;
+    v16f out[SMT];
+#pragma unroll
+    for (int t = 0; t < SMT; ++t) out[t] = v16f{};
+    v16i acc_h[SMT], acc_l[SMT];
     v4i hdr;
 
     // one half-superblock: H compile-time, slot runtime; R the superblock's
     // scales, fold = false for the phantom superblock that rounds nk up to even
-    auto half = [&](auto HH, int j, const SRegs &R, bool fold) {
+    auto half = [&](auto HH, int j, const SRegs &R, bool fold) __attribute__((always_inline)) {
         constexpr int H = decltype(HH)::value;
         const uint32_t S = lds_addr(my + (j % SNST) * SSLOT);
         const uint32_t arow = S + 128 * ln;
@@ -531,15 +534,18 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
         if (H == 0) hdr = lds_read16<SA + SWN>(S + 16 * ln);
         v4i wq0 = lds_read16<SA>(wrow);
         v4i wq1 = lds_read16<SA + 32>(wrow);
-        v4i af[4];
+        // fragments in K-step order, tile 0 then tile 1 within a step
+        v4i af[4][SMT];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int p = 4 * (s & 1) + 2 * (s >> 1) + g;
-            af[s] = lds_read16<0>(arow + 16 * (p ^ afx));
+            const uint32_t ad = arow + 16 * (p ^ afx);
+            af[s][0] = lds_read16<0>(ad);
+            af[s][1] = lds_read16<32 * 128>(ad);
         }
-        if (H == 0) lds_wait<6>(hdr);
-        lds_wait<5>(wq0);
-        lds_wait<4>(wq1);
+        if (H == 0) lds_wait<10>(hdr);
+        lds_wait<9>(wq0);
+        lds_wait<8>(wq1);
         // scale digits of the four sub-blocks of this half
         const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2];
         const uint32_t x = H == 0 ? w1 : __builtin_amdgcn_alignbit(w2, w1, 24);
@@ -556,31 +562,30 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
                 bh[e] = mul_digit(nib, sc >> 3);
                 bl[e] = mul_digit(nib, sc & 7u);
             }
-            if (s == 0) lds_wait<3>(af[0]);
-            if (s == 1) lds_wait<2>(af[1]);
-            if (s == 2) lds_wait<1>(af[2]);
-            if (s == 3) lds_wait<0>(af[3]);
-            if (H == 0 && s == 0) {
-                acc_h = mma_i8(af[s], bh, v16i{});
-                acc_l = mma_i8(af[s], bl, v16i{});
-            } else {
-                acc_h = mma_i8(af[s], bh, acc_h);
-                acc_l = mma_i8(af[s], bl, acc_l);
+#pragma unroll
+            for (int t = 0; t < SMT; ++t) {
+                // reads newer than fragment (s, t): the 2*(3 - s) + (1 - t) after it
+                if (s == 0 && t == 0) lds_wait<7>(af[0][0]);
+                if (s == 0 && t == 1) lds_wait<6>(af[0][1]);
+                if (s == 1 && t == 0) lds_wait<5>(af[1][0]);
+                if (s == 1 && t == 1) lds_wait<4>(af[1][1]);
+                if (s == 2 && t == 0) lds_wait<3>(af[2][0]);
+                if (s == 2 && t == 1) lds_wait<2>(af[2][1]);
+                if (s == 3 && t == 0) lds_wait<1>(af[3][0]);
+                if (s == 3 && t == 1) lds_wait<0>(af[3][1]);
+                if (H == 0 && s == 0) {
+                    acc_h[t] = mma_i8(af[s][t], bh, v16i{});
+                    acc_l[t] = mma_i8(af[s][t], bl, v16i{});
+                } else {
+                    acc_h[t] = mma_i8(af[s][t], bh, acc_h[t]);
+                    acc_l[t] = mma_i8(af[s][t], bl, acc_l[t]);
+                }
             }
         }
         if (H == 1 && fold) {
-            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n]
+            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n], then the min term
             const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
             const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * q + i;
-                    const int T = (acc_h[r] << 3) + acc_l[r];
-                    out[r] = fmaf((float)T, R.da[q][i] * dw, out[r]);
-                }
-            // min term, as in the large tile
             const uint32_t w3 = (uint32_t)hdr[3];
             const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
             const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
@@ -595,10 +600,21 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
                 b2[i] = lb;
                 b2[4 + i] = (__bf16)0.0f;
             }
-            const v4i avv = {(int)R.ahi.x, (int)R.ahi.y, (int)R.alo.x, (int)R.alo.y};
-            const v8bf am = __builtin_bit_cast(v8bf, avv);
-            out = mma_bf16(am, b1, out);
-            out = mma_bf16(am, b2, out);
+#pragma unroll
+            for (int t = 0; t < SMT; ++t) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * q + i;
+                        const int T = (acc_h[t][r] << 3) + acc_l[t][r];
+                        out[t][r] = fmaf((float)T, R.da[t][q][i] * dw, out[t][r]);
+                    }
+                const v4i avv = {(int)R.ahi[t].x, (int)R.ahi[t].y, (int)R.alo[t].x, (int)R.alo[t].y};
+                const v8bf am = __builtin_bit_cast(v8bf, avv);
+                out[t] = mma_bf16(am, b1, out[t]);
+                out[t] = mma_bf16(am, b2, out[t]);
+            }
         }
     };
 
@@ -611,7 +627,7 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
         // 2k+1's and superblock k+1's scales; at a second half, stage 2k+1's
         // by those scales and stage 2k+2's copies.  Stages and scales issued
         // past the end re-read the last superblock and are drained unused.
-        auto superblock = [&](int k, SRegs &R) {
+        auto superblock = [&](int k, SRegs &R) __attribute__((always_inline)) {
             const int j = 2 * k;
             wait_vmcnt<SCOPY1 + SDA>();
             issue(j + 2, 0);
@@ -633,25 +649,30 @@ __global__ __launch_bounds__(64 * SWAVES, 2) void gemm_q4k_small_kernel(Args a) 
     // no copy may still be writing this wave's stages
     wait_vmcnt<0>();
 
-    // sum the two K-halves in a fixed order: the h = 1 waves park theirs in
-    // their own (now idle) stages
-    float *const red = reinterpret_cast<float *>(&s_lds[2 + t][0][0]);  // wave (h = 1, t)
+    // sum the two K-halves in a fixed order: wave 1 parks its sums in its own
+    // (now idle) stages
+    float *const red = reinterpret_cast<float *>(&s_lds[1][0][0]);
     if (h == 1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[64 * r + lane] = out[r];
+        for (int t = 0; t < SMT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(16 * t + r) * 64 + lane] = out[t][r];
     }
     __syncthreads();
-    if (h == 0 && 32 * t < M) {
+    if (h == 0) {
         const int n = n0 + ln;
         const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
-        v16f sum = out;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] += red[64 * r + lane];
-        const v16i bits = __builtin_bit_cast(v16i, sum);
+        for (int t = 0; t < SMT; ++t) {
+            v16f sum = out[t];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
-            __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, row * N * 4, 0);
+            for (int r = 0; r < 16; ++r) sum[r] += red[(16 * t + r) * 64 + lane];
+            const v16i bits = __builtin_bit_cast(v16i, sum);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
+                __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, row * N * 4, 0);
+            }
         }
     }
 }
@@ -707,7 +728,7 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     switch (q4k_kernel_choice(M, N)) {
         case Q4K_FEW_TOKENS:
             hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
-                               dim3(64 * q4w::SWAVES), 0, stream, a);
+                               dim3(64 * q4w::SKH), 0, stream, a);
             break;
         default: {
             const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
