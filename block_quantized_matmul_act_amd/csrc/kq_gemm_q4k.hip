@@ -125,10 +125,26 @@ __device__ __forceinline__ v4i lds_read16(uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
+template <int OFF>
+__device__ __forceinline__ v2u lds_read8(uint32_t addr) {
+    v2u r;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
 // s_waitcnt lgkmcnt(N), tied to a register it guards so that no use of that
 // register is scheduled above it
 template <int N>
 __device__ __forceinline__ void lds_wait(v4i &r) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(v4f &r) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(v2u &r) {
     static_assert(N >= 0 && N < 16, "lgkmcnt range");
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
 }
@@ -423,8 +439,9 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // unpacked once for both); two workgroups share a CU, one wave per SIMD.
 // Each wave stages its own operands through LDS in half-superblocks (128
 // values: 8 KiB of activations, the 64 nibble bytes and the 16-byte header
-// of 32 weight blocks), three stages deep, with coalesced buffer -> LDS
-// copies (consecutive lanes read consecutive bytes of a row, so a copy
+// of 32 weight blocks; a second half also brings the superblock's activation
+// scales and min-term operands), three stages deep, with coalesced buffer ->
+// LDS copies (consecutive lanes read consecutive bytes of a row, so a copy
 // touches a handful of cache lines instead of one per lane).  Both scale
 // digits are multiplied as soon as a fragment arrives, into two int32 planes
 // combined at the superblock's end.  No barrier is needed until the two
@@ -441,16 +458,12 @@ constexpr int SKH = 2;                      // K-split: superblock halves (one w
 constexpr int SA = 64 * 128;                // half-row activations of 64 rows
 constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 blocks
 constexpr int SHD = 32 * 16;                // block headers of 32 rows
-constexpr int SSLOT = SA + SWN + SHD;       // one stage
+constexpr int SDS = 64 * 4;                 // activation scales of 64 rows
+constexpr int SLS = 2 * 64 * 16;            // min-term operands (hi, lo) of 64 rows
+constexpr int SSLOT = SA + SWN + SHD + SDS + SLS;  // one stage
 constexpr int SNST = 3;                     // stages per wave
-constexpr int SDA = SMT * (4 + 2);          // activation scale and min-operand loads per superblock
 constexpr int SCOPY0 = 8 + 2 + 2;           // copies of a first-half stage (with headers)
-constexpr int SCOPY1 = 8 + 2;               // copies of a second-half stage
-
-struct SRegs {             // a superblock's register operands, per m-tile
-    v4f da[SMT][4];        // activation scales of rows 32t + 8q + 4g .. +3
-    v2u ahi[SMT], alo[SMT];  // min-term operands of row 32t + ln, sub-blocks 4g..4g+3
-};
+constexpr int SCOPY1 = 8 + 2 + 1 + 2;       // copies of a second-half stage (with scales)
 
 __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][SNST][SSLOT];
@@ -501,19 +514,11 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
         if (H == 0) {
             copy4(rs_w, S + SA + SWN, h_vb0, sb * BB);
             copy4(rs_w, S + SA + SWN + 256, h_vb1, sb * BB);
-        }
-    };
-    SRegs R0, R1;  // scales of even and odd superblocks, two superblocks ahead
-    auto issue_scales = [&](int sbx, SRegs &R) __attribute__((always_inline)) {
-        const int sb = sb0 + min(sbx, nk - 1);
-#pragma unroll
-        for (int t = 0; t < SMT; ++t) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                R.da[t][q] = __builtin_bit_cast(v4f, ld16(rs_d, (32 * t + 8 * q + 4 * g) * 4, sb * M * 4));
-            const int lrow = (32 * t + ln) * 16 + 8 * g;
-            R.ahi[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, lrow, sb * 2 * M * 16, 0));
-            R.alo[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs_l, lrow, (sb * 2 + 1) * M * 16, 0));
+        } else {
+            // scales of rows 0..63 (lane = row) and min operands (lane = row)
+            copy4(rs_d, S + SA + SWN + SHD, 4 * lane, sb * M * 4);
+            copy16(rs_l, S + SA + SWN + SHD + SDS, 16 * lane, sb * 2 * M * 16);
+            copy16(rs_l, S + SA + SWN + SHD + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
         }
     };
 
@@ -524,9 +529,8 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
     v16i acc_h[SMT], acc_l[SMT];
     v4i hdr;
 
-    // one half-superblock: H compile-time, slot runtime; R the superblock's
-    // scales, fold = false for the phantom superblock that rounds nk up to even
-    auto half = [&](auto HH, int j, const SRegs &R, bool fold) __attribute__((always_inline)) {
+    // one half-superblock: H compile-time, slot runtime
+    auto half = [&](auto HH, int j) __attribute__((always_inline)) {
         constexpr int H = decltype(HH)::value;
         const uint32_t S = lds_addr(my + (j % SNST) * SSLOT);
         const uint32_t arow = S + 128 * ln;
@@ -582,8 +586,31 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
                 }
             }
         }
-        if (H == 1 && fold) {
-            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n], then the min term
+        if (H == 1) {
+            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n], then the min
+            // term; scales and min operands from this stage
+            const uint32_t sd = S + SA + SWN + SHD + 16 * g;
+            const uint32_t sl = S + SA + SWN + SHD + SDS + 16 * ln + 8 * g;
+            v4f da[SMT][4];
+            v2u ahi[SMT], alo[SMT];
+            da[0][0] = __builtin_bit_cast(v4f, lds_read16<0>(sd));
+            da[0][1] = __builtin_bit_cast(v4f, lds_read16<32>(sd));
+            da[0][2] = __builtin_bit_cast(v4f, lds_read16<64>(sd));
+            da[0][3] = __builtin_bit_cast(v4f, lds_read16<96>(sd));
+            ahi[0] = lds_read8<0>(sl);
+            alo[0] = lds_read8<1024>(sl);
+            da[1][0] = __builtin_bit_cast(v4f, lds_read16<128>(sd));
+            da[1][1] = __builtin_bit_cast(v4f, lds_read16<160>(sd));
+            da[1][2] = __builtin_bit_cast(v4f, lds_read16<192>(sd));
+            da[1][3] = __builtin_bit_cast(v4f, lds_read16<224>(sd));
+            ahi[1] = lds_read8<512>(sl);
+            alo[1] = lds_read8<1536>(sl);
+            lds_wait<6>(da[0][0]);
+            lds_wait<6>(da[0][1]);
+            lds_wait<6>(da[0][2]);
+            lds_wait<6>(da[0][3]);
+            lds_wait<6>(ahi[0]);
+            lds_wait<6>(alo[0]);
             const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
             const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
             const uint32_t w3 = (uint32_t)hdr[3];
@@ -608,9 +635,17 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
                     for (int i = 0; i < 4; ++i) {
                         const int r = 4 * q + i;
                         const int T = (acc_h[t][r] << 3) + acc_l[t][r];
-                        out[t][r] = fmaf((float)T, R.da[t][q][i] * dw, out[t][r]);
+                        out[t][r] = fmaf((float)T, da[t][q][i] * dw, out[t][r]);
                     }
-                const v4i avv = {(int)R.ahi[t].x, (int)R.ahi[t].y, (int)R.alo[t].x, (int)R.alo[t].y};
+                if (t == 0) {
+                    lds_wait<0>(da[1][0]);
+                    lds_wait<0>(da[1][1]);
+                    lds_wait<0>(da[1][2]);
+                    lds_wait<0>(da[1][3]);
+                    lds_wait<0>(ahi[1]);
+                    lds_wait<0>(alo[1]);
+                }
+                const v4i avv = {(int)ahi[t].x, (int)ahi[t].y, (int)alo[t].x, (int)alo[t].y};
                 const v8bf am = __builtin_bit_cast(v8bf, avv);
                 out[t] = mma_bf16(am, b1, out[t]);
                 out[t] = mma_bf16(am, b2, out[t]);
@@ -619,31 +654,21 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
     };
 
     if (nk > 0) {
-        // Every iteration is two superblocks (four halves) with no exit, so
-        // each wait below sees the same loads in flight on every pass.  In
-        // issue order a superblock k queues the copies of stages 2k+2 (a first
-        // half: SCOPY0) and 2k+3 (SCOPY1), then the scales of superblock k+2
-        // (SDA).  At a first half, stage 2k's copies are followed by stage
-        // 2k+1's and superblock k+1's scales; at a second half, stage 2k+1's
-        // by those scales and stage 2k+2's copies.  Stages and scales issued
-        // past the end re-read the last superblock and are drained unused.
-        auto superblock = [&](int k, SRegs &R) __attribute__((always_inline)) {
-            const int j = 2 * k;
-            wait_vmcnt<SCOPY1 + SDA>();
-            issue(j + 2, 0);
-            half(std::integral_constant<int, 0>{}, j, R, k < nk);
-            wait_vmcnt<SDA + SCOPY0>();
-            issue(j + 3, 1);
-            half(std::integral_constant<int, 1>{}, j + 1, R, k < nk);
-            issue_scales(k + 2, R);
-        };
-        issue_scales(0, R0);
+        // Every iteration is one superblock (two halves) with no exit, so each
+        // wait below sees the same copies in flight on every pass: at a first
+        // half, the next stage's (a second half: SCOPY1); at a second half,
+        // the next stage's (a first half: SCOPY0).  Stages issued past the end
+        // re-read the last superblock and are drained unused.
         issue(0, 0);
         issue(1, 1);
-        issue_scales(1, R1);
-        for (int k = 0; k < nk; k += 2) {
-            superblock(k, R0);
-            superblock(k + 1, R1);
+        for (int k = 0; k < nk; ++k) {
+            const int j = 2 * k;
+            wait_vmcnt<SCOPY1>();
+            issue(j + 2, 0);
+            half(std::integral_constant<int, 0>{}, j);
+            wait_vmcnt<SCOPY0>();
+            issue(j + 3, 1);
+            half(std::integral_constant<int, 1>{}, j + 1);
         }
     }
     // no copy may still be writing this wave's stages
