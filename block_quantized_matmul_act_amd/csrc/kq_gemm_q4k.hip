@@ -503,7 +503,12 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
     int8_t *const my = &s_lds[h][0][0];
     // stage j: superblock sb0 + j/2 (clamped: past the end re-reads the last,
     // unused), half j%2 (a compile-time H in every caller)
+    // The copies are pinned between compiler memory barriers: the LDS reads
+    // are asm statements the compiler does not see as memory accesses, so
+    // without them a copy into a stage could be moved above the last reads
+    // of that stage.
     auto issue = [&](int j, int H) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
         const int sb = sb0 + min(j >> 1, nk - 1);
         int8_t *S = my + (j % SNST) * SSLOT;
 #pragma unroll
@@ -520,6 +525,7 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
             copy16(rs_l, S + SA + SWN + SHD + SDS, 16 * lane, sb * 2 * M * 16);
             copy16(rs_l, S + SA + SWN + SHD + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
         }
+        asm volatile("" ::: "memory");
     };
 
     const int afx = (ln >> 1) & 7;
@@ -673,6 +679,7 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
     }
     // no copy may still be writing this wave's stages
     wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
 
     // sum the two K-halves in a fixed order: wave 1 parks its sums in its own
     // (now idle) stages
