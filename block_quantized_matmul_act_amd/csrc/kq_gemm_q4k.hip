@@ -131,6 +131,9 @@ __device__ __forceinline__ v2u lds_read8(uint32_t addr) {
     asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
+// lgkmcnt wait with a count known only after unrolling (folds to one case)
+template <typename R>
+__device__ __forceinline__ void lds_wait_n(int n, R &r);
 // s_waitcnt lgkmcnt(N), tied to a register it guards so that no use of that
 // register is scheduled above it
 template <int N>
@@ -147,6 +150,27 @@ template <int N>
 __device__ __forceinline__ void lds_wait(v2u &r) {
     static_assert(N >= 0 && N < 16, "lgkmcnt range");
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <typename R>
+__device__ __forceinline__ void lds_wait_n(int n, R &r) {
+    switch (n) {
+        case 0: lds_wait<0>(r); break;
+        case 1: lds_wait<1>(r); break;
+        case 2: lds_wait<2>(r); break;
+        case 3: lds_wait<3>(r); break;
+        case 4: lds_wait<4>(r); break;
+        case 5: lds_wait<5>(r); break;
+        case 6: lds_wait<6>(r); break;
+        case 7: lds_wait<7>(r); break;
+        case 8: lds_wait<8>(r); break;
+        case 9: lds_wait<9>(r); break;
+        case 10: lds_wait<10>(r); break;
+        case 11: lds_wait<11>(r); break;
+        case 12: lds_wait<12>(r); break;
+        case 13: lds_wait<13>(r); break;
+        case 14: lds_wait<14>(r); break;
+        default: lds_wait<15>(r); break;
+    }
 }
 
 // Tile t of the grouped order: GM M-tiles down, then across N.
@@ -435,10 +459,11 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // Few tokens (M <= 64): the product is bound by streaming the weights from
 // HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
 // weight rows and runs 2 independent waves, wave h taking superblock half h
-// for all 64 token rows (two 32-row m-tiles, so each weight nibble is
-// unpacked once for both); two workgroups share a CU, one wave per SIMD.
+// for all token rows: SMT 32-row m-tiles (2 for M <= 64, so each weight
+// nibble is unpacked once for both; 1 for M <= 32).  Two (SMT = 2) or three
+// (SMT = 1) workgroups share a CU.
 // Each wave stages its own operands through LDS in half-superblocks (128
-// values: 8 KiB of activations, the 64 nibble bytes and the 16-byte header
+// values: 4 KiB of activations per m-tile, the 64 nibble bytes and the 16-byte header
 // of 32 weight blocks; a second half also brings the superblock's activation
 // scales and min-term operands), three stages deep, with coalesced buffer ->
 // LDS copies (consecutive lanes read consecutive bytes of a row, so a copy
@@ -453,19 +478,26 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // j = 4H + 2cp + n; the activation fragment is the same 16 values of the
 // lane's row, piece p = 4cp + 2n + g of the half-row.
 // ---------------------------------------------------------------------------
-constexpr int SMT = 2;                      // 32-row m-tiles (64 tokens)
 constexpr int SKH = 2;                      // K-split: superblock halves (one wave each)
-constexpr int SA = 64 * 128;                // half-row activations of 64 rows
 constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 blocks
 constexpr int SHD = 32 * 16;                // block headers of 32 rows
 constexpr int SDS = 64 * 4;                 // activation scales of 64 rows
 constexpr int SLS = 2 * 64 * 16;            // min-term operands (hi, lo) of 64 rows
-constexpr int SSLOT = SA + SWN + SHD + SDS + SLS;  // one stage
 constexpr int SNST = 3;                     // stages per wave
-constexpr int SCOPY0 = 8 + 2 + 2;           // copies of a first-half stage (with headers)
-constexpr int SCOPY1 = 8 + 2 + 1 + 2;       // copies of a second-half stage (with scales)
+// per number of 32-token m-tiles SMT (1: M <= 32, 2: M <= 64)
+template <int SMT>
+struct SmallCfg {
+    static constexpr int SA = 32 * SMT * 128;                   // half-row activations
+    static constexpr int SSLOT = SA + SWN + SHD + SDS + SLS;    // one stage
+    static constexpr int COPY0 = 4 * SMT + 2 + 2;               // copies of a first-half stage
+    static constexpr int COPY1 = 4 * SMT + 2 + 1 + 2;           // copies of a second-half stage
+    static constexpr int WG_PER_CU = SMT == 1 ? 3 : 2;          // workgroups sharing a CU's LDS
+};
 
-__global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
+template <int SMT>
+__global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_small_kernel(Args a) {
+    constexpr int SA = SmallCfg<SMT>::SA, SSLOT = SmallCfg<SMT>::SSLOT;
+    constexpr int SCOPY0 = SmallCfg<SMT>::COPY0, SCOPY1 = SmallCfg<SMT>::COPY1;
     __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][SNST][SSLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -512,7 +544,7 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
         const int sb = sb0 + min(j >> 1, nk - 1);
         int8_t *S = my + (j % SNST) * SSLOT;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4 * SMT; ++i)
             copy16(rs_a, S + 1024 * i, a_vb ^ (64 * (i & 1)), 8 * i * K + sb * ROW + 128 * H);
         copy16(rs_w, S + SA, w_vb0, sb * BB + 64 * H);
         copy16(rs_w, S + SA + 1024, w_vb1, sb * BB + 64 * H);
@@ -551,11 +583,12 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
             const int p = 4 * (s & 1) + 2 * (s >> 1) + g;
             const uint32_t ad = arow + 16 * (p ^ afx);
             af[s][0] = lds_read16<0>(ad);
-            af[s][1] = lds_read16<32 * 128>(ad);
+            if constexpr (SMT == 2) af[s][1] = lds_read16<32 * 128>(ad);
         }
-        if (H == 0) lds_wait<10>(hdr);
-        lds_wait<9>(wq0);
-        lds_wait<8>(wq1);
+        // reads in flight after each: header, two weight reads, 4*SMT fragments
+        if (H == 0) lds_wait_n(2 + 4 * SMT, hdr);
+        lds_wait_n(1 + 4 * SMT, wq0);
+        lds_wait_n(4 * SMT, wq1);
         // scale digits of the four sub-blocks of this half
         const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2];
         const uint32_t x = H == 0 ? w1 : __builtin_amdgcn_alignbit(w2, w1, 24);
@@ -574,15 +607,8 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
             }
 #pragma unroll
             for (int t = 0; t < SMT; ++t) {
-                // reads newer than fragment (s, t): the 2*(3 - s) + (1 - t) after it
-                if (s == 0 && t == 0) lds_wait<7>(af[0][0]);
-                if (s == 0 && t == 1) lds_wait<6>(af[0][1]);
-                if (s == 1 && t == 0) lds_wait<5>(af[1][0]);
-                if (s == 1 && t == 1) lds_wait<4>(af[1][1]);
-                if (s == 2 && t == 0) lds_wait<3>(af[2][0]);
-                if (s == 2 && t == 1) lds_wait<2>(af[2][1]);
-                if (s == 3 && t == 0) lds_wait<1>(af[3][0]);
-                if (s == 3 && t == 1) lds_wait<0>(af[3][1]);
+                // reads newer than fragment (s, t): SMT*(3 - s) + (SMT - 1 - t)
+                lds_wait_n(SMT * (3 - s) + (SMT - 1 - t), af[s][t]);
                 if (H == 0 && s == 0) {
                     acc_h[t] = mma_i8(af[s][t], bh, v16i{});
                     acc_l[t] = mma_i8(af[s][t], bl, v16i{});
@@ -605,18 +631,21 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
             da[0][3] = __builtin_bit_cast(v4f, lds_read16<96>(sd));
             ahi[0] = lds_read8<0>(sl);
             alo[0] = lds_read8<1024>(sl);
-            da[1][0] = __builtin_bit_cast(v4f, lds_read16<128>(sd));
-            da[1][1] = __builtin_bit_cast(v4f, lds_read16<160>(sd));
-            da[1][2] = __builtin_bit_cast(v4f, lds_read16<192>(sd));
-            da[1][3] = __builtin_bit_cast(v4f, lds_read16<224>(sd));
-            ahi[1] = lds_read8<512>(sl);
-            alo[1] = lds_read8<1536>(sl);
-            lds_wait<6>(da[0][0]);
-            lds_wait<6>(da[0][1]);
-            lds_wait<6>(da[0][2]);
-            lds_wait<6>(da[0][3]);
-            lds_wait<6>(ahi[0]);
-            lds_wait<6>(alo[0]);
+            if constexpr (SMT == 2) {
+                da[SMT - 1][0] = __builtin_bit_cast(v4f, lds_read16<128>(sd));
+                da[SMT - 1][1] = __builtin_bit_cast(v4f, lds_read16<160>(sd));
+                da[SMT - 1][2] = __builtin_bit_cast(v4f, lds_read16<192>(sd));
+                da[SMT - 1][3] = __builtin_bit_cast(v4f, lds_read16<224>(sd));
+                ahi[SMT - 1] = lds_read8<512>(sl);
+                alo[SMT - 1] = lds_read8<1536>(sl);
+            }
+            // tile 0's six reads are followed by tile 1's six (if any)
+            lds_wait_n(6 * (SMT - 1), da[0][0]);
+            lds_wait_n(6 * (SMT - 1), da[0][1]);
+            lds_wait_n(6 * (SMT - 1), da[0][2]);
+            lds_wait_n(6 * (SMT - 1), da[0][3]);
+            lds_wait_n(6 * (SMT - 1), ahi[0]);
+            lds_wait_n(6 * (SMT - 1), alo[0]);
             const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
             const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
             const uint32_t w3 = (uint32_t)hdr[3];
@@ -643,13 +672,15 @@ __global__ __launch_bounds__(64 * SKH, 2) void gemm_q4k_small_kernel(Args a) {
                         const int T = (acc_h[t][r] << 3) + acc_l[t][r];
                         out[t][r] = fmaf((float)T, da[t][q][i] * dw, out[t][r]);
                     }
-                if (t == 0) {
-                    lds_wait<0>(da[1][0]);
-                    lds_wait<0>(da[1][1]);
-                    lds_wait<0>(da[1][2]);
-                    lds_wait<0>(da[1][3]);
-                    lds_wait<0>(ahi[1]);
-                    lds_wait<0>(alo[1]);
+                if constexpr (SMT == 2) {
+                    if (t == 0) {
+                        lds_wait<0>(da[SMT - 1][0]);
+                        lds_wait<0>(da[SMT - 1][1]);
+                        lds_wait<0>(da[SMT - 1][2]);
+                        lds_wait<0>(da[SMT - 1][3]);
+                        lds_wait<0>(ahi[SMT - 1]);
+                        lds_wait<0>(alo[SMT - 1]);
+                    }
                 }
                 const v4i avv = {(int)ahi[t].x, (int)ahi[t].y, (int)alo[t].x, (int)alo[t].y};
                 const v8bf am = __builtin_bit_cast(v8bf, avv);
@@ -724,7 +755,7 @@ static int g_num_cus = 0;
 // kernel; otherwise the 128 x 128 persistent kernel (two per CU).
 int q4k_kernel_choice(int M, int N) {
     (void)N;
-    return M <= 32 * q4w::SMT ? Q4K_FEW_TOKENS : Q4K_TILE128;
+    return M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
 }
 
 hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
@@ -759,8 +790,12 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.ntiles = a.tiles_m * a.tiles_n;
     switch (q4k_kernel_choice(M, N)) {
         case Q4K_FEW_TOKENS:
-            hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel, dim3((unsigned)((N + 31) / 32)),
-                               dim3(64 * q4w::SKH), 0, stream, a);
+            if (M <= 32)
+                hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel<1>, dim3((unsigned)((N + 31) / 32)),
+                                   dim3(64 * q4w::SKH), 0, stream, a);
+            else
+                hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel<2>, dim3((unsigned)((N + 31) / 32)),
+                                   dim3(64 * q4w::SKH), 0, stream, a);
             break;
         default: {
             const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
