@@ -483,22 +483,54 @@ constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 block
 constexpr int SHD = 32 * 16;                // block headers of 32 rows
 constexpr int SDS = 64 * 4;                 // activation scales of 64 rows
 constexpr int SLS = 2 * 64 * 16;            // min-term operands (hi, lo) of 64 rows
-constexpr int SNST = 3;                     // stages per wave
-// per number of 32-token m-tiles SMT (1: M <= 32, 2: M <= 64)
-template <int SMT>
+// staging depths (half-superblocks ahead) of the few-token kernel: at 64
+// tokens the kernel is bound by its VALU work and depth makes no difference;
+// at up to 32 tokens weights six halves ahead beat four (12.6 vs 14.5 us for
+// 8 x 14336 x 4096)
+#ifndef Q4S_DA1
+#define Q4S_DA1 1
+#endif
+#ifndef Q4S_DW1
+#define Q4S_DW1 6
+#endif
+#ifndef Q4S_DA2
+#define Q4S_DA2 1
+#endif
+#ifndef Q4S_DW2
+#define Q4S_DW2 4
+#endif
+// SMT 32-token m-tiles (1: M <= 32, 2: M <= 64); activations are staged DA
+// half-superblocks ahead (they come from L2), weights DW > DA ahead (they
+// stream from HBM), in rings of DA + 1 and DW + 1 slots.
+template <int SMT, int DA, int DW>
 struct SmallCfg {
+    static_assert(DW > DA && DA >= 1, "weights must run ahead of activations");
     static constexpr int SA = 32 * SMT * 128;                   // half-row activations
-    static constexpr int SSLOT = SA + SWN + SHD + SDS + SLS;    // one stage
-    static constexpr int COPY0 = 4 * SMT + 2 + 2;               // copies of a first-half stage
-    static constexpr int COPY1 = 4 * SMT + 2 + 1 + 2;           // copies of a second-half stage
-    static constexpr int WG_PER_CU = SMT == 1 ? 3 : 2;          // workgroups sharing a CU's LDS
+    static constexpr int SAS = SA + SDS + SLS;                   // activation slot (+ scales)
+    static constexpr int SWS = SWN + SHD;                        // weight slot (+ headers)
+    static constexpr int LDS = (DA + 1) * SAS + (DW + 1) * SWS;  // per wave
+    static constexpr int WG_PER_CU = 163840 / (SKH * LDS);       // workgroups sharing a CU's LDS
+    // copies of an activation stage (second halves add the scales) and of a
+    // weight stage (first halves add the headers)
+    static constexpr int szA(int H) { return 4 * SMT + 3 * H; }
+    static constexpr int szW(int H) { return 2 + 2 * (1 - H); }
+    // Copies that may still be in flight when half j (parity H) starts: each
+    // half i issues activation stage i + DA, then weight stage i + DW.  The
+    // newest copies half j needs are activation stage j's (issued at half
+    // j - DA); after them came weight stage j - DA + DW and all copies of
+    // halves j - DA + 1 .. j - 1.
+    static constexpr int in_flight(int H) {
+        int n = szW((H - DA + DW) & 1);
+        for (int d = 1; d < DA; ++d) n += szA((H + d) & 1) + szW((H - DA + d + DW) & 1);
+        return n;
+    }
 };
 
-template <int SMT>
-__global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_small_kernel(Args a) {
-    constexpr int SA = SmallCfg<SMT>::SA, SSLOT = SmallCfg<SMT>::SSLOT;
-    constexpr int SCOPY0 = SmallCfg<SMT>::COPY0, SCOPY1 = SmallCfg<SMT>::COPY1;
-    __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][SNST][SSLOT];
+template <int SMT, int DA, int DW>
+__global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void gemm_q4k_small_kernel(Args a) {
+    using C = SmallCfg<SMT, DA, DW>;
+    constexpr int SA = C::SA, SAS = C::SAS, SWS = C::SWS;
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][C::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -532,30 +564,39 @@ __global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_s
     const int h_vb0 = (int)(wr0 + 4 * (lane & 3));
     const int h_vb1 = (int)(wr1 + 4 * (lane & 3));
 
-    int8_t *const my = &s_lds[h][0][0];
-    // stage j: superblock sb0 + j/2 (clamped: past the end re-reads the last,
-    // unused), half j%2 (a compile-time H in every caller)
-    // The copies are pinned between compiler memory barriers: the LDS reads
-    // are asm statements the compiler does not see as memory accesses, so
-    // without them a copy into a stage could be moved above the last reads
-    // of that stage.
-    auto issue = [&](int j, int H) __attribute__((always_inline)) {
+    int8_t *const myA = &s_lds[h][0];                    // activation ring
+    int8_t *const myW = &s_lds[h][(DA + 1) * SAS];       // weight ring
+    // Stage x: superblock sb0 + x/2 (clamped: past the end re-reads the last,
+    // unused), half x%2.  The copies are pinned between compiler memory
+    // barriers: the LDS reads are asm statements the compiler does not see as
+    // memory accesses, so without them a copy into a slot could be moved
+    // above the last reads of that slot.
+    auto issueA = [&](int x) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
-        const int sb = sb0 + min(j >> 1, nk - 1);
-        int8_t *S = my + (j % SNST) * SSLOT;
+        const int H = x & 1;
+        const int sb = sb0 + min(x >> 1, nk - 1);
+        int8_t *S = myA + (x % (DA + 1)) * SAS;
 #pragma unroll
         for (int i = 0; i < 4 * SMT; ++i)
             copy16(rs_a, S + 1024 * i, a_vb ^ (64 * (i & 1)), 8 * i * K + sb * ROW + 128 * H);
-        copy16(rs_w, S + SA, w_vb0, sb * BB + 64 * H);
-        copy16(rs_w, S + SA + 1024, w_vb1, sb * BB + 64 * H);
-        if (H == 0) {
-            copy4(rs_w, S + SA + SWN, h_vb0, sb * BB);
-            copy4(rs_w, S + SA + SWN + 256, h_vb1, sb * BB);
-        } else {
+        if (H == 1) {
             // scales of rows 0..63 (lane = row) and min operands (lane = row)
-            copy4(rs_d, S + SA + SWN + SHD, 4 * lane, sb * M * 4);
-            copy16(rs_l, S + SA + SWN + SHD + SDS, 16 * lane, sb * 2 * M * 16);
-            copy16(rs_l, S + SA + SWN + SHD + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
+            copy4(rs_d, S + SA, 4 * lane, sb * M * 4);
+            copy16(rs_l, S + SA + SDS, 16 * lane, sb * 2 * M * 16);
+            copy16(rs_l, S + SA + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
+        }
+        asm volatile("" ::: "memory");
+    };
+    auto issueW = [&](int x) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        const int H = x & 1;
+        const int sb = sb0 + min(x >> 1, nk - 1);
+        int8_t *S = myW + (x % (DW + 1)) * SWS;
+        copy16(rs_w, S, w_vb0, sb * BB + 64 * H);
+        copy16(rs_w, S + 1024, w_vb1, sb * BB + 64 * H);
+        if (H == 0) {
+            copy4(rs_w, S + SWN, h_vb0, sb * BB);
+            copy4(rs_w, S + SWN + 256, h_vb1, sb * BB);
         }
         asm volatile("" ::: "memory");
     };
@@ -567,15 +608,16 @@ __global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_s
     v16i acc_h[SMT], acc_l[SMT];
     v4i hdr;
 
-    // one half-superblock: H compile-time, slot runtime
+    // one half-superblock: H compile-time, slots runtime
     auto half = [&](auto HH, int j) __attribute__((always_inline)) {
         constexpr int H = decltype(HH)::value;
-        const uint32_t S = lds_addr(my + (j % SNST) * SSLOT);
+        const uint32_t S = lds_addr(myA + (j % (DA + 1)) * SAS);
+        const uint32_t SW = lds_addr(myW + (j % (DW + 1)) * SWS);
         const uint32_t arow = S + 128 * ln;
-        const uint32_t wrow = S + 64 * ln + 16 * g;  // + SA in the read offset
-        if (H == 0) hdr = lds_read16<SA + SWN>(S + 16 * ln);
-        v4i wq0 = lds_read16<SA>(wrow);
-        v4i wq1 = lds_read16<SA + 32>(wrow);
+        const uint32_t wrow = SW + 64 * ln + 16 * g;
+        if (H == 0) hdr = lds_read16<SWN>(SW + 16 * ln);
+        v4i wq0 = lds_read16<0>(wrow);
+        v4i wq1 = lds_read16<32>(wrow);
         // fragments in K-step order, tile 0 then tile 1 within a step
         v4i af[4][SMT];
 #pragma unroll
@@ -621,8 +663,8 @@ __global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_s
         if (H == 1) {
             // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n], then the min
             // term; scales and min operands from this stage
-            const uint32_t sd = S + SA + SWN + SHD + 16 * g;
-            const uint32_t sl = S + SA + SWN + SHD + SDS + 16 * ln + 8 * g;
+            const uint32_t sd = S + SA + 16 * g;
+            const uint32_t sl = S + SA + SDS + 16 * ln + 8 * g;
             v4f da[SMT][4];
             v2u ahi[SMT], alo[SMT];
             da[0][0] = __builtin_bit_cast(v4f, lds_read16<0>(sd));
@@ -692,19 +734,24 @@ __global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_s
 
     if (nk > 0) {
         // Every iteration is one superblock (two halves) with no exit, so each
-        // wait below sees the same copies in flight on every pass: at a first
-        // half, the next stage's (a second half: SCOPY1); at a second half,
-        // the next stage's (a first half: SCOPY0).  Stages issued past the end
-        // re-read the last superblock and are drained unused.
-        issue(0, 0);
-        issue(1, 1);
+        // wait below sees the same copies in flight on every pass
+        // (C::in_flight).  The prologue issues what halves -DW .. -1 would
+        // have, so half 0 starts in the same state.  Stages issued past the
+        // end re-read the last superblock and are drained unused.
+#pragma unroll
+        for (int i = -DW; i < 0; ++i) {
+            if (i + DA >= 0) issueA(i + DA);
+            issueW(i + DW);
+        }
         for (int k = 0; k < nk; ++k) {
             const int j = 2 * k;
-            wait_vmcnt<SCOPY1>();
-            issue(j + 2, 0);
+            wait_vmcnt<C::in_flight(0)>();
+            issueA(j + DA);
+            issueW(j + DW);
             half(std::integral_constant<int, 0>{}, j);
-            wait_vmcnt<SCOPY0>();
-            issue(j + 3, 1);
+            wait_vmcnt<C::in_flight(1)>();
+            issueA(j + 1 + DA);
+            issueW(j + 1 + DW);
             half(std::integral_constant<int, 1>{}, j + 1);
         }
     }
@@ -714,7 +761,7 @@ __global__ __launch_bounds__(64 * SKH, SmallCfg<SMT>::WG_PER_CU) void gemm_q4k_s
 
     // sum the two K-halves in a fixed order: wave 1 parks its sums in its own
     // (now idle) stages
-    float *const red = reinterpret_cast<float *>(&s_lds[1][0][0]);
+    float *const red = reinterpret_cast<float *>(&s_lds[1][0]);
     if (h == 1) {
 #pragma unroll
         for (int t = 0; t < SMT; ++t)
@@ -791,11 +838,11 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     switch (q4k_kernel_choice(M, N)) {
         case Q4K_FEW_TOKENS:
             if (M <= 32)
-                hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel<1>, dim3((unsigned)((N + 31) / 32)),
-                                   dim3(64 * q4w::SKH), 0, stream, a);
+                hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<1, Q4S_DA1, Q4S_DW1>),
+                                   dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
             else
-                hipLaunchKernelGGL(q4w::gemm_q4k_small_kernel<2>, dim3((unsigned)((N + 31) / 32)),
-                                   dim3(64 * q4w::SKH), 0, stream, a);
+                hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<2, Q4S_DA2, Q4S_DW2>),
+                                   dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
             break;
         default: {
             const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
