@@ -42,30 +42,36 @@ METRIC = "effective int8 TOPS + prefill tok/s, Q4_K x Q8_K 4096x14336 GEMM; % of
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
-GEMM_SOURCES = [os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc", f)
-                for f in ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp")]
+CSRC = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc")
+# the sources each format's GEMM kernels are built from
+GEMM_SOURCES = {
+    "q4_k": ("kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "q6_k": ("kq_gemm.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "tq": ("kq_gemm.hip", "kq_device.hpp", "kq_launch.hpp"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) over the GEMM kernel sources, in order."""
+def kernel_source_hash(fmt_name: str) -> str:
+    """sha256 (first 16 hex digits) over the sources of one format's GEMM
+    kernels, in order."""
     h = hashlib.sha256()
-    for path in GEMM_SOURCES:
-        with open(path, "rb") as f:
+    for name in GEMM_SOURCES[fmt_name]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, fmt_name: str):
     """HBM bytes per GEMM launch from profiles/<...>_<workload>_traffic.md, if
     that file was measured on the current kernel source; else None."""
     pdir = os.path.join(ROOT, "profiles")
     if not os.path.isdir(pdir):
         return None
-    want = kernel_source_hash()
+    want = kernel_source_hash(fmt_name)
     for name in sorted(os.listdir(pdir)):
         if not name.endswith(f"{workload}_traffic.md"):
             continue
@@ -212,9 +218,9 @@ def main():
                      "frac_hbm": round((x_bytes + a_bytes) / quant_mean_s / 1e9 / PEAK_HBM_GBS,
                                        4)},
         "dispatch": kq.dispatch_counts(),
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(datagen.FMT_NAMES[fmt]),
     }
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, datagen.FMT_NAMES[fmt])
     if M >= 256:
         tops = ops / gemm_b2b_s / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": round(tops, 2),

@@ -10,7 +10,7 @@
 // llama.cpp's mul_mat_q share one staged activation tile among all warps of
 // a block; here the weight side is not staged at all):
 //   * A workgroup of 4 waves (one per SIMD) computes 128 x 128 output tiles,
-//     persistently: the grid is one workgroup per CU and each walks a list
+//     persistently: the grid is two workgroups per CU and each walks a list
 //     of tiles with one flat (tile, superblock) loop, so prefetching runs
 //     across tile boundaries.
 //   * Wave w owns 32 weight rows (output columns) and all 128 activation
@@ -463,11 +463,12 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
 // nibble is unpacked once for both; 1 for M <= 32).  Two (SMT = 2) or three
 // (SMT = 1) workgroups share a CU.
 // Each wave stages its own operands through LDS in half-superblocks (128
-// values: 4 KiB of activations per m-tile, the 64 nibble bytes and the 16-byte header
-// of 32 weight blocks; a second half also brings the superblock's activation
-// scales and min-term operands), three stages deep, with coalesced buffer ->
-// LDS copies (consecutive lanes read consecutive bytes of a row, so a copy
-// touches a handful of cache lines instead of one per lane).  Both scale
+// values), with coalesced buffer -> LDS copies (consecutive lanes read
+// consecutive bytes of a row, so a copy touches a handful of cache lines
+// instead of one per lane).  Activations (4 KiB per m-tile; the second half
+// also brings the superblock's scales and min-term operands) and weights
+// (the 64 nibble bytes of the half and the 16-byte headers of 32 blocks)
+// sit in separate rings, the weights staged further ahead.  Both scale
 // digits are multiplied as soon as a fragment arrives, into two int32 planes
 // combined at the superblock's end.  No barrier is needed until the two
 // K-halves are summed in LDS.
