@@ -19,11 +19,16 @@ timed steps; `gemm.mean_us` is the per-step event pair around each launch,
 which also holds the dispatch gap after the quantize kernel.
 `traffic` is the HBM traffic per launch measured with rocprofv3 counters for
 the current kernel source (profiles/*_traffic.md), or null when those counters
-were taken on a different kernel source.  `cpu_baseline` is the plain CPU
+were taken on a different kernel source.  `calibration` holds the device's
+own rates measured in the same run by the library's calibration kernels
+(int8 MFMA with constant operands, with operands changing every iteration, and
+with 4-10 VALU instructions per MFMA; fp32 VALU; HBM read over 1 GiB);
+`roofline.frac_measured` is `achieved` over the measured rate (changing-operand
+MFMA when compute-bound, HBM read for few tokens).  `cpu_baseline` is the plain CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--cpu-seconds S] [--copy-mib N]
+                       [--no-cpu-baseline] [--no-calib] [--cpu-seconds S] [--copy-mib N]
 """
 from __future__ import annotations
 
@@ -42,6 +47,7 @@ METRIC = "effective int8 TOPS + prefill tok/s, Q4_K x Q8_K 4096x14336 GEMM; % of
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 ROTATE_BYTES = 512 << 20
+CALIB_READ_BYTES = 1 << 30   # HBM read calibration buffer, 4x the Infinity Cache
 CSRC = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc")
 # the sources each format's GEMM kernels are built from
 GEMM_SOURCES = {
@@ -90,6 +96,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ffn_up_q4k_2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the calibration kernels (measured peak rates)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -233,10 +241,56 @@ def main():
                               "traffic": traffic}
     result["roofline"]["kernel"] = kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K))
 
+    if not args.no_calib:
+        # the device's own rates, measured now: the GEMM's fraction of them
+        # sits beside the fraction of the published peak
+        cal = calibrate(kq, stream)
+        result["calibration"] = cal
+        rl = result["roofline"]
+        measured = cal["mfma_i8_toggle_tops"] if rl["bound"] == "mfma" else cal["hbm_read_gbs"]
+        rl["measured_peak"] = measured
+        rl["frac_measured"] = round(rl["achieved"] / measured, 4)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, W_np, x_np, Os[(args.steps - 1) % ncopy],
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def calibrate(kq, stream):
+    """Calibration kernels of the library, each timed with HIP events on the
+    stream it runs on (one warm-up launch, then the best of three)."""
+    import torch
+
+    def rate(kind, param=0, buf=None, nbytes=0):
+        kq.kq_calib_launch(kind, param, buf, nbytes, stream.cuda_stream)
+        best = None
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            work = kq.kq_calib_launch(kind, param, buf, nbytes, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            r = work / (e0.elapsed_time(e1) * 1e-3)
+            best = r if best is None else max(best, r)
+        return best
+
+    nbytes = CALIB_READ_BYTES
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    cal = {
+        "mfma_i8_tops": round(rate(kq.KQ_CALIB_MFMA_I8) / 1e12, 1),
+        "mfma_i8_toggle_tops": round(rate(kq.KQ_CALIB_MFMA_I8_TOGGLE) / 1e12, 1),
+        "mfma_i8_tops_with_valu_per_mfma": {
+            str(p + 2): round(rate(kq.KQ_CALIB_MFMA_I8_VALU, p) / 1e12, 1) for p in (2, 4, 6, 8)},
+        "valu_f32_tflops": round(rate(kq.KQ_CALIB_VALU_F32) / 1e12, 2),
+        "hbm_read_gbs": round(rate(kq.KQ_CALIB_HBM_READ, 0, buf, nbytes) / 1e9, 1),
+        "hbm_read_bytes": nbytes,
+    }
+    del buf
+    log(f"[bench] calibration: {cal}")
+    return cal
 
 
 def cpu_baseline(wl, W_np, x_np, out_dev, target_s):

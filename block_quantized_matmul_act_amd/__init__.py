@@ -20,6 +20,8 @@ KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
 KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
     -1, -2, -3, -4, -5, -6)
+(KQ_CALIB_MFMA_I8, KQ_CALIB_MFMA_I8_TOGGLE, KQ_CALIB_VALU_F32, KQ_CALIB_MFMA_I8_VALU,
+ KQ_CALIB_HBM_READ) = 0, 1, 2, 3, 4
 
 # Every symbol include/kq.h declares, with its ctypes signature.
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -36,6 +38,7 @@ SIGNATURES = {
     "kq_dispatch_count": (ctypes.c_uint64, [_I]),
     "kq_dispatch_reset": (None, []),
     "kq_select_variant": (_I, [_I, _I64, _I64, _I64]),
+    "kq_calib_launch": (_I, [_I, _I, _P, _I64, ctypes.POINTER(ctypes.c_double), _P]),
     "kq_strerror": (ctypes.c_char_p, [_I]),
     "kq_version": (_I, []),
 }
@@ -141,6 +144,15 @@ def kq_dispatch_reset():
 
 def kq_select_variant(fmt, M, N, K):
     return lib().kq_select_variant(fmt, M, N, K)
+
+
+def kq_calib_launch(kind, param=0, buf=None, nbytes=0, stream=None):
+    """Launch one calibration kernel; returns the work it does (int8 ops, fp32
+    flops or bytes)."""
+    work = ctypes.c_double(0.0)
+    _check(lib().kq_calib_launch(kind, param, _ptr(buf), nbytes, ctypes.byref(work), _stream(stream)),
+           "kq_calib_launch")
+    return work.value
 
 
 def kq_strerror(status):

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstdint>
 
+#include "kq_calib.hpp"
 #include "kq_launch.hpp"
 
 namespace {
@@ -193,6 +194,25 @@ int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t
     g_count[fmt == KQ_Q4_K ? V_SUBSUMS_Q4K : fmt == KQ_Q6_K ? V_SUBSUMS_Q6K : V_SUBSUMS_TQ]
         .fetch_add(1);
     return KQ_OK;
+}
+
+int kq_calib_launch(int kind, int param, const void *buf, int64_t bytes, double *work,
+                    hipStream_t stream) {
+    if (kind < KQ_CALIB_MFMA_I8 || kind > KQ_CALIB_HBM_READ) return KQ_ERR_FMT;
+    if (!work) return KQ_ERR_NULL;
+    if (kind == KQ_CALIB_MFMA_I8_VALU && param != 2 && param != 4 && param != 6 && param != 8)
+        return KQ_ERR_SHAPE;
+    if (kind == KQ_CALIB_HBM_READ) {
+        if (!buf) return KQ_ERR_NULL;
+        if (bytes < 16 || bytes % 16 || bytes > kMaxBytes) return KQ_ERR_SHAPE;
+        if (!aligned16(buf)) return KQ_ERR_ALIGN;
+    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return KQ_ERR_HIP;
+    return kq::launch_calib(kind, param, buf, bytes, cus, work, stream) == hipSuccess ? KQ_OK
+                                                                                      : KQ_ERR_HIP;
 }
 
 int kq_num_variants(void) { return V_COUNT; }

@@ -170,6 +170,36 @@ const char *kq_variant_name(int variant);
 uint64_t kq_dispatch_count(int variant);
 void kq_dispatch_reset(void);
 
+/*
+ * Calibration kernels (measurement hooks): the device's own int8 matrix-core,
+ * fp32 VALU and HBM read rates, against which the GEMM's fractions of peak are
+ * also reported (the published peaks assume a clock the chip does not hold
+ * under load).  One call launches one kernel on `stream` that does a fixed
+ * amount of work and stores *work (host pointer): int8 ops for the matrix-core
+ * kinds, fp32 flops for KQ_CALIB_VALU_F32, bytes read for KQ_CALIB_HBM_READ.
+ * The caller times the launch with events on the same stream.
+ *   KQ_CALIB_MFMA_I8        independent v_mfma_i32_32x32x32_i8 chains, two
+ *                           waves per SIMD, constant operands
+ *   KQ_CALIB_MFMA_I8_TOGGLE the same with operands that change every iteration
+ *                           (two VALU adds per MFMA)
+ *   KQ_CALIB_VALU_F32       independent v_fma_f32 chains (not packed)
+ *   KQ_CALIB_MFMA_I8_VALU   KQ_CALIB_MFMA_I8_TOGGLE plus `param` (2, 4, 6 or
+ *                           8) v_fma_f32 between consecutive MFMAs
+ *   KQ_CALIB_HBM_READ       16-byte loads over buf [bytes] (device, 16-byte
+ *                           aligned, bytes a positive multiple of 16); use a
+ *                           buffer well beyond the 256 MB Infinity Cache
+ * Errors: unknown kind -> KQ_ERR_FMT; work NULL, or buf NULL for the read ->
+ * KQ_ERR_NULL; bad param or bytes -> KQ_ERR_SHAPE; misaligned buf ->
+ * KQ_ERR_ALIGN; a launch failure -> KQ_ERR_HIP.
+ */
+#define KQ_CALIB_MFMA_I8 0
+#define KQ_CALIB_MFMA_I8_TOGGLE 1
+#define KQ_CALIB_VALU_F32 2
+#define KQ_CALIB_MFMA_I8_VALU 3
+#define KQ_CALIB_HBM_READ 4
+int kq_calib_launch(int kind, int param, const void *buf, int64_t bytes, double *work,
+                    hipStream_t stream);
+
 /* The variant kq_gemm would launch for this case, or a negative KQ_ERR_*. */
 int kq_select_variant(int fmt, int64_t M, int64_t N, int64_t K);
 

@@ -163,3 +163,19 @@ def test_variants_and_counters(kq):
             assert 0 <= v < n
     assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT
     assert kq.kq_select_variant(kq.KQ_Q4_K, 1, 1, 100) == kq.KQ_ERR_SHAPE
+
+
+def test_calib_rejects_bad_arguments(kq):
+    L = kq.lib()
+    import ctypes
+    w = ctypes.c_double(0.0)
+    assert L.kq_calib_launch(5, 0, None, 0, ctypes.byref(w), None) == kq.KQ_ERR_FMT
+    assert L.kq_calib_launch(-1, 0, None, 0, ctypes.byref(w), None) == kq.KQ_ERR_FMT
+    assert L.kq_calib_launch(kq.KQ_CALIB_MFMA_I8, 0, None, 0, None, None) == kq.KQ_ERR_NULL
+    for p in (0, 1, 3, 10):
+        assert L.kq_calib_launch(kq.KQ_CALIB_MFMA_I8_VALU, p, None, 0, ctypes.byref(w), None) == kq.KQ_ERR_SHAPE
+    R = kq.KQ_CALIB_HBM_READ
+    assert L.kq_calib_launch(R, 0, None, 1024, ctypes.byref(w), None) == kq.KQ_ERR_NULL
+    assert L.kq_calib_launch(R, 0, 4096, 0, ctypes.byref(w), None) == kq.KQ_ERR_SHAPE
+    assert L.kq_calib_launch(R, 0, 4096, 24, ctypes.byref(w), None) == kq.KQ_ERR_SHAPE
+    assert L.kq_calib_launch(R, 0, 4104, 1024, ctypes.byref(w), None) == kq.KQ_ERR_ALIGN

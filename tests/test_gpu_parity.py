@@ -196,7 +196,7 @@ def test_tiny_workload_full(kq, workloads):
     gemm_vs_oracle(kq, wl.fmt, W, x, wl.M, wl.N, wl.K)
 
 
-SWEEP_M = (1, 7, 8, 63, 64, 65, 80, 128, 129, 300)
+SWEEP_M = (1, 7, 8, 24, 40, 63, 64, 65, 80, 128, 129, 300)
 SWEEP_N = (48, 128, 200, 256)
 
 
