@@ -19,6 +19,7 @@ enum Variant {
     V_QUANT_Q8_128,
     V_GEMM_Q4K_M64,
     V_GEMM_Q4K_128x128,
+    V_GEMM_Q4K_MATVEC,
     V_GEMM_Q6K_128x128,
     V_GEMM_TQ_128x128,
     V_SUBSUMS_Q4K,
@@ -28,7 +29,7 @@ enum Variant {
 };
 
 const char *const kVariantNames[V_COUNT] = {
-    "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128",
+    "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
     "gemm_q6_k_128x128", "gemm_tq_128x128", "subsums_q4_k",  "subsums_q6_k",
     "subsums_tq",
 };
@@ -99,10 +100,13 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     return 1;  // proceed
 }
 
-int variant_for(int fmt, int64_t M, int64_t N) {
+int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
     if (fmt == KQ_Q4_K) {
-        return kq::q4k_kernel_choice((int)M, (int)N) == kq::Q4K_FEW_TOKENS ? V_GEMM_Q4K_M64
-                                                                             : V_GEMM_Q4K_128x128;
+        switch (kq::q4k_kernel_choice((int)M, (int)N, (int)K)) {
+            case kq::Q4K_MATVEC: return V_GEMM_Q4K_MATVEC;
+            case kq::Q4K_FEW_TOKENS: return V_GEMM_Q4K_M64;
+            default: return V_GEMM_Q4K_128x128;
+        }
     }
     return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
 }
@@ -164,7 +168,7 @@ int kq_select_variant(int fmt, int64_t M, int64_t N, int64_t K) {
     if (!qk_of(fmt)) return KQ_ERR_FMT;
     if (M < 0 || N < 0 || K < 0 || K % qk_of(fmt)) return KQ_ERR_SHAPE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return KQ_ERR_SHAPE;
-    return variant_for(fmt, M, N);
+    return variant_for(fmt, M, N, K);
 }
 
 int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int64_t K,
@@ -179,7 +183,7 @@ int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int6
         L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr, out, (int)M,
         (int)N, (int)K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
-    g_count[variant_for(fmt, M, N)].fetch_add(1);
+    g_count[variant_for(fmt, M, N, K)].fetch_add(1);
     return KQ_OK;
 }
 

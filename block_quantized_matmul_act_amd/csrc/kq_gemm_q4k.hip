@@ -788,6 +788,184 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-vector kernel for one or two tokens (decode): the product is a stream of
+// 33 MB of weights for a handful of dot products each, so it needs many waves
+// with loads in flight rather than matrix cores.  Workgroups of 4 waves each
+// own 16 weight rows (4 per wave); the activation buffer (values, scales,
+// min-term operands of the few tokens) is copied once per workgroup into LDS.
+//
+// Load instruction i of a wave covers 8 consecutive superblocks of one of its
+// rows (K is a multiple of 2048, so a row is a whole number of them); lane l
+// takes 16-byte nibble chunk c8 = l % 8 of superblock l / 8 of them, a
+// contiguous 1 KiB run apart from the block headers, which a second load
+// brings (each lane its superblock's 16-byte header).  Chunk c8 holds the low
+// nibbles of weights 64c + 16h + i (sub-block 2c) and the high nibbles of
+// weights 64c + 32 + 16h + i (sub-block 2c + 1), c = c8 / 2, h = c8 % 2,
+// i < 16.  Per token the lane forms the integer sums of those 32 products
+// with v_dot4, scales them by the two sub-block scales, and folds
+//   acc += float(sc0 S0 + sc1 S1) * d_a * d - dmin * m_c8 * alpha_c8,
+// the min term of sub-block c8 (one sub-block per lane covers all eight).
+// A row's total is the sum over the 64 lanes of its load instructions, in a
+// fixed butterfly order, stored by lane 0.
+// ---------------------------------------------------------------------------
+namespace mv {
+constexpr int NW = 4;          // waves per workgroup
+constexpr int RPW = 4;         // weight rows per wave
+constexpr int RPG = NW * RPW;  // weight rows per workgroup
+// Up to two tokens: measured on 14336 x 4096 weights, 8.9 and 10.6 us
+// against 14.6 us for the few-token kernel; at three and four tokens the two
+// kernels tie, beyond that the per-token LDS reads and dot products lose.
+constexpr int MAX_TOKENS = 2;
+
+// LDS bytes of the staged activations for MT tokens (MT >= M); sections at
+// 1 KiB multiples so every copy stays inside its own section
+__host__ __device__ constexpr int lds_qs(int MT, int K) { return MT * K; }
+__host__ __device__ constexpr int lds_d(int M, int nsb) { return (nsb * M * 4 + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int lds_al(int M, int nsb) { return (nsb * 2 * M * 16 + 1023) / 1024 * 1024; }
+// total, with room for the reads of token rows past M (never stored)
+__host__ __device__ constexpr int lds_bytes(int MT, int M, int K, int nsb) {
+    return lds_qs(MT, K) + lds_d(M, nsb) + lds_al(M, nsb) + 256;
+}
+}  // namespace mv
+
+template <int MT>
+__global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
+    extern __shared__ __attribute__((aligned(16))) int8_t s_mv[];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int rowbytes = nsb * BB;
+    const int ipr = nsb >> 3;                  // load instructions per row
+    const int row0 = blockIdx.x * mv::RPG + w * mv::RPW;
+
+    int8_t *const s_qs = s_mv;
+    float *const s_d = reinterpret_cast<float *>(s_mv + mv::lds_qs(MT, K));
+    int8_t *const s_al = s_mv + mv::lds_qs(MT, K) + mv::lds_d(M, nsb);
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+
+    // ---- activations -> LDS, shared by the workgroup's waves ----------------
+    // (M*K is a multiple of 2048; the last scale and min-operand copies read
+    // past their sections as zeros and stay inside their LDS sections)
+    {
+        const int nq = (M * K) >> 10, nd = (nsb * M * 4 + 255) >> 8, nl = (nsb * 2 * M * 16 + 1023) >> 10;
+        // copy c holds superblocks 4c'..4c'+3 of one token row; lane l fills
+        // slot l%16 of superblock l/16 with piece (l%16) ^ 2(sb%2), which
+        // spreads the two superblocks one read instruction touches over
+        // different banks
+        const int aq = 16 * (lane ^ (2 * ((lane >> 4) & 1)));
+        for (int c = w; c < nq; c += mv::NW) copy16(rs_a, s_qs + 1024 * c, 1024 * c + aq, 0);
+        for (int c = w; c < nd; c += mv::NW) copy4(rs_d, reinterpret_cast<int8_t *>(s_d) + 256 * c, 256 * c + 4 * lane, 0);
+        for (int c = w; c < nl; c += mv::NW) copy16(rs_l, s_al + 1024 * c, 1024 * c + 16 * lane, 0);
+    }
+
+    // ---- weights: one load instruction in flight per row ----------------------
+    // Instruction (r, j) reads superblocks 8j .. 8j+7 of the wave's row r; the
+    // wave walks j = 0 .. ipr-1 over its RPW rows in turn, keeping one
+    // instruction per row in flight (the next group of that row), and past the
+    // last group re-reads it (unused, drained at the end).
+    const int c8 = lane & 7, sbl = lane >> 3;
+    const int cq = c8 >> 1, hq = c8 & 1;
+    v4i wq[mv::RPW], wh[mv::RPW];
+    auto issue = [&](int r, int j, v4i &q, v4i &h) __attribute__((always_inline)) {
+        const int off = (row0 + r) * rowbytes + (8 * min(j, ipr - 1) + sbl) * BB;  // < (N + 256) rows
+        q = ld16(rs_w, off + 16 + 16 * c8, 0);
+        h = ld16(rs_w, off, 0);
+    };
+#pragma unroll
+    for (int r = 0; r < mv::RPW; ++r) issue(r, 0, wq[r], wh[r]);
+    // this wave's activation copies have landed once at most the weight loads
+    // are in flight; the barrier covers the other waves' copies
+    wait_vmcnt<2 * mv::RPW>();
+    barrier_nofence();
+
+    float acc[mv::RPW][MT];
+#pragma unroll
+    for (int r = 0; r < mv::RPW; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+    auto compute = [&](int j, const v4i &q, const v4i &h, float (&ac)[MT]) __attribute__((always_inline)) {
+        const int sb = 8 * j + sbl;
+        // header: d, dmin, scales sc_j (bits 6j) and mins m_j (bits 48 + 6j)
+        const uint32_t w0 = (uint32_t)h[0], w1 = (uint32_t)h[1], w2 = (uint32_t)h[2], w3 = (uint32_t)h[3];
+        const uint64_t lo64 = (uint64_t)w1 | ((uint64_t)w2 << 32);
+        const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
+        const uint32_t scs = (uint32_t)(lo64 >> (12 * cq));
+        const int sc0 = (int)(scs & 63u), sc1 = (int)((scs >> 6) & 63u);
+        const float mn = (float)((uint32_t)(hi64 >> (16 + 6 * c8)) & 63u);
+        const float dw = f16_bits_to_f32(w0);
+        const float cmin = -f16_bits_to_f32(w0 >> 16) * mn;
+        int lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo[e] = q[e] & 0x0F0F0F0F;
+            hi[e] = (int)(((uint32_t)q[e] >> 4) & 0x0F0F0F0Fu);
+        }
+        // pieces 4cq + hq (low nibbles' weights) and + 2 (high), swizzled
+        const int sw = 2 * (sb & 1);
+        const int k0 = sb * ROW + 16 * ((4 * cq + hq) ^ sw);
+        const int k1 = sb * ROW + 16 * ((4 * cq + hq + 2) ^ sw);
+        // every token's operands first, so the reads overlap
+        v4i a0[MT], a1[MT];
+        float da[MT];
+        uint16_t ah[MT], al[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            a0[m] = *reinterpret_cast<const v4i *>(s_qs + m * K + k0);
+            a1[m] = *reinterpret_cast<const v4i *>(s_qs + m * K + k1);
+            da[m] = s_d[sb * M + m];
+            ah[m] = *reinterpret_cast<const uint16_t *>(s_al + ((sb * 2) * M + m) * 16 + 2 * c8);
+            al[m] = *reinterpret_cast<const uint16_t *>(s_al + ((sb * 2 + 1) * M + m) * 16 + 2 * c8);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s0 = __builtin_amdgcn_sdot4(lo[e], a0[m][e], s0, false);
+                s1 = __builtin_amdgcn_sdot4(hi[e], a1[m][e], s1, false);
+            }
+            const int u = sc0 * s0 + sc1 * s1;
+            ac[m] = fmaf((float)u, da[m] * dw, ac[m]);
+            ac[m] = fmaf(__builtin_bit_cast(float, (uint32_t)ah[m] << 16), cmin, ac[m]);
+            ac[m] = fmaf(__builtin_bit_cast(float, (uint32_t)al[m] << 16), cmin, ac[m]);
+        }
+    };
+
+    for (int j = 0; j < ipr; ++j) {
+#pragma unroll
+        for (int r = 0; r < mv::RPW; ++r) {
+            // row r's instruction j has landed once the RPW - 1 issued after
+            // it may still be in flight
+            wait_vmcnt<2 * (mv::RPW - 1)>();
+            compute(j, wq[r], wh[r], acc[r]);
+            issue(r, j + 1, wq[r], wh[r]);
+        }
+    }
+
+    // Each row's total: its 64 lanes summed in a fixed butterfly order (all
+    // rows and tokens step together), stored by lane 0.
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int r = 0; r < mv::RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], o, 64);
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < mv::RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < M && row0 + r < N) a.out[(int64_t)m * N + row0 + r] = acc[r][m];
+    }
+    wait_vmcnt<0>();
+}
+
 // out[0, n) = 0 (the product over an empty K); a kernel rather than a memset
 // so that the call stays capturable in a graph
 __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
@@ -799,10 +977,17 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
 
 static int g_num_cus = 0;
 
-// Which Q4_K kernel a shape gets: few tokens -> the K-split weight-streaming
-// kernel; otherwise the 128 x 128 persistent kernel (two per CU).
-int q4k_kernel_choice(int M, int N) {
+static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
+constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
+
+// Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
+// kernel; up to 64 -> the K-split weight-streaming kernel; otherwise the
+// 128 x 128 persistent kernel (two per CU).
+int q4k_kernel_choice(int M, int N, int K) {
     (void)N;
+    if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
+        q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
+        return Q4K_MATVEC;
     return M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
 }
 
@@ -836,7 +1021,17 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
-    switch (q4k_kernel_choice(M, N)) {
+    switch (q4k_kernel_choice(M, N, K)) {
+        case Q4K_MATVEC: {
+            const dim3 grid((unsigned)((N + q4w::mv::RPG - 1) / q4w::mv::RPG)), block(64 * q4w::mv::NW);
+            const int mt = mv_tokens(M);
+            const size_t lds = (size_t)q4w::mv::lds_bytes(mt, M, K, a.nsb);
+            switch (mt) {
+                case 1: hipLaunchKernelGGL(q4w::gemv_q4k_kernel<1>, grid, block, lds, stream, a); break;
+                default: hipLaunchKernelGGL(q4w::gemv_q4k_kernel<2>, grid, block, lds, stream, a); break;
+            }
+            break;
+        }
         case Q4K_FEW_TOKENS:
             if (M <= 32)
                 hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<1, Q4S_DA1, Q4S_DW1>),

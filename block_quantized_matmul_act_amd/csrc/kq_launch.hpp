@@ -15,9 +15,10 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
 hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
                           int K, hipStream_t stream);
 
-// Q4_K kernels: M <= 64 -> few-token kernel; otherwise the 128 x 128
-// persistent kernel.
-enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1 };
-int q4k_kernel_choice(int M, int N);
+// Q4_K kernels: one or two tokens with K a multiple of 2048 (and the staged
+// activations within the LDS budget) -> matrix-vector kernel; M <= 64 ->
+// few-token kernel; otherwise the 128 x 128 persistent kernel.
+enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1, Q4K_MATVEC = 2 };
+int q4k_kernel_choice(int M, int N, int K);
 
 }  // namespace kq

@@ -63,6 +63,9 @@ WORKLOADS = {
     "ffn_up_q4k_64": Workload("ffn_up_q4k_64", Q4_K, 64, 14336, 4096, 1003,
                               "plain", "Q4_K x Q8_K FFN gate/up, 64 tokens "
                               "(first 64 token rows of the 2048-token draw)"),
+    "ffn_up_q4k_1": Workload("ffn_up_q4k_1", Q4_K, 1, 14336, 4096, 1003,
+                             "plain", "Q4_K x Q8_K FFN gate/up, one token (decode; "
+                             "first token row of the 2048-token draw)"),
     "ffn_down_q6k_2048": Workload("ffn_down_q6k_2048", Q6_K, 2048, 4096, 14336, 1004,
                                   "plain", "Q6_K x Q8_K FFN down, 2048 tokens"),
     "tern_5120_2048": Workload("tern_5120_2048", TQ, 2048, 17408, 5120, 1005,
