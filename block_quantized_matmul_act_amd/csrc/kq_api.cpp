@@ -153,7 +153,6 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
     if (M == 0 || K == 0) return KQ_OK;
     if (!x || !a_q8) return KQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(a_q8)) return KQ_ERR_ALIGN;
-    if ((M * (K / bs) * (bs / 4) + 255) / 256 > INT32_MAX) return KQ_ERR_UNSUPPORTED;
     char *base = static_cast<char *>(a_q8);
     hipError_t e = kq::launch_quant_act(
         bs, x, reinterpret_cast<int8_t *>(base), reinterpret_cast<float *>(base + L.d),
