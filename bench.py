@@ -52,8 +52,8 @@ CSRC = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc")
 # the sources each format's GEMM kernels are built from
 GEMM_SOURCES = {
     "q4_k": ("kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp"),
-    "q6_k": ("kq_gemm.hip", "kq_device.hpp", "kq_launch.hpp"),
-    "tq": ("kq_gemm.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "q6_k": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "tq": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
 }
 
 

@@ -32,6 +32,7 @@
 //     land on the same XCD (blocks are dealt round-robin to the 8 XCDs), so
 //     a weight tile is fetched from HBM once per XCD L2.
 #include "kq_device.hpp"
+#include "kq_launch.hpp"
 
 #include <type_traits>
 
@@ -1077,6 +1078,7 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
                        const uint16_t *alpha, float *out, int M, int N, int K,
                        hipStream_t stream) {
     if (fmt == FMT_Q4K) return launch_gemm_q4k(W, qs, da, alpha, out, M, N, K, stream);
+    if (gemv_choice(fmt, M, N, K)) return launch_gemv(fmt, W, qs, da, out, M, N, K, stream);
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {

@@ -1,0 +1,247 @@
+// kq_gemv.hip -- matrix-vector kernels for Q6_K weights (a handful of tokens,
+// decode).
+//
+// A token's product with a weight row is a stream of the row's blocks: a
+// handful of tokens need many waves with loads in flight, not matrix cores.
+// Workgroups of 4 waves own 8 weight rows (2 per wave); the tokens'
+// activation values and scales are copied once per workgroup into LDS.  A
+// load instruction covers 8 consecutive superblocks of one row, one 32-value
+// piece per lane; each wave keeps one instruction per row in flight and walks
+// its rows in turn (two rows per wave beat one and four: 12.5 against 13.1
+// and 16.3 us for one token on 4096 x 14336).  Every lane keeps its rows'
+// sums in registers, and one butterfly over the 64 lanes at the end (a fixed
+// order) gives each row's total, which lane 0 stores.  Integer sums come from
+// v_dot4_i32_i8 and are folded per 16-value sub-block with the block scales.
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+
+namespace kq {
+namespace gv {
+
+constexpr int NW = 4;          // waves per workgroup
+#ifndef GV_RPW
+#define GV_RPW 2
+#endif
+constexpr int RPW = GV_RPW;    // weight rows per wave
+constexpr int RPG = NW * RPW;  // weight rows per workgroup
+constexpr int RSRC_FLAGS = 0x00020000;
+constexpr int Q6B = 210;       // Q6_K block bytes
+// staged activations: values of MT tokens, then the scales (1 KiB multiple so
+// the last 256-byte scale copy stays inside)
+__host__ __device__ constexpr int lds_qs(int MT, int K) { return MT * K; }
+__host__ __device__ constexpr int lds_d(int M, int nsb) { return (nsb * M * 4 + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int lds_bytes(int MT, int M, int K) {
+    return lds_qs(MT, K) + lds_d(M, K / 256) + 256;  // + room for reads of token rows past M
+}
+constexpr int LDS_BUDGET = 120 * 1024;  // one workgroup per CU at most
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+struct Args {
+    const uint8_t *W;
+    const int8_t *qs;  // [M][K]
+    const float *da;   // [K/256][M]
+    float *out;        // [M][N]
+    int M, N, K;
+};
+
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rs, void *lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rs, void *lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
+}
+__device__ __forceinline__ v4i ld16(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
+// Stage the activations of a workgroup (values [M][K], scales [K/256][M]).
+// The 16-byte pieces of odd superblocks are stored with their index's low bit
+// flipped, which puts the two superblocks a read instruction touches on
+// different banks.
+__device__ __forceinline__ void stage_acts(const Args &a, int8_t *s_qs, float *s_d, int w, int lane) {
+    const int M = a.M, K = a.K, nsb = K / 256;
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const int nq = (M * K) >> 10, nd = (nsb * M * 4 + 255) >> 8;
+    const int aq = 16 * (lane ^ ((lane >> 4) & 1));
+    for (int c = w; c < nq; c += NW) copy16(rs_a, s_qs + 1024 * c, 1024 * c + aq);
+    for (int c = w; c < nd; c += NW) copy4(rs_d, reinterpret_cast<int8_t *>(s_d) + 256 * c, 256 * c + 4 * lane);
+}
+
+// ---------------------------------------------------------------------------
+// Q6_K.  Lane l of a load instruction takes superblock l/8 of the instruction's
+// eight and, within it, the 32 values 128h + 32u + t (t < 32) with h = (l%8)/4,
+// u = l%4: low 4 bits from ql[64h + 32(u%2) + t] (low nibble for u < 2, high
+// for u >= 2), high 2 bits from bits 2u of qh[32h + t], sub-blocks 8h + 2u
+// and 8h + 2u + 1.  Blocks are 210 bytes, so a block is 2-byte aligned: the
+// lane loads whole aligned dwords and shifts them into place with v_alignbit.
+// q - 32 is formed per byte without borrows: (q | 0x80) - 0x20, then bit 7
+// flipped back.
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
+    extern __shared__ __attribute__((aligned(16))) int8_t s_gv[];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int M = a.M, N = a.N, K = a.K, nsb = K / 256;
+    const int rowbytes = nsb * Q6B;
+    const int ipr = nsb >> 3;  // load instructions per row
+    const int row0 = blockIdx.x * RPG + w * RPW;
+    int8_t *const s_qs = s_gv;
+    float *const s_d = reinterpret_cast<float *>(s_gv + lds_qs(MT, K));
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+
+    stage_acts(a, s_qs, s_d, w, lane);
+
+    const int sbl = lane >> 3, h = (lane >> 2) & 1, u = lane & 3;
+    struct Raw {
+        v4i ql0, ql1;
+        uint32_t ql2;
+        v4i qh0, qh1;
+        uint32_t qh2, sc, dd;
+    };
+    // (rows past N: offsets stay below (N + 256) rows, the host's limit)
+    auto issue = [&](int r, int j, Raw &R) __attribute__((always_inline)) {
+        const int base = (row0 + r) * rowbytes + (8 * min(j, ipr - 1) + sbl) * Q6B;
+        const int b4 = base & ~3;
+        const int oq = b4 + 64 * h + 32 * (u & 1), oh = b4 + 128 + 32 * h;
+        R.ql0 = ld16(rs_w, oq);
+        R.ql1 = ld16(rs_w, oq + 16);
+        R.ql2 = ld4(rs_w, oq + 32);
+        R.qh0 = ld16(rs_w, oh);
+        R.qh1 = ld16(rs_w, oh + 16);
+        R.qh2 = ld4(rs_w, oh + 32);
+        R.sc = ld4(rs_w, (base + 192 + 8 * h + 2 * u) & ~3);
+        R.dd = ld4(rs_w, (base + 208) & ~3);
+    };
+    constexpr int LOADS = 8;  // per issue
+    Raw raw[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) issue(r, 0, raw[r]);
+    // this wave's activation copies have landed once at most the weight loads
+    // are in flight; the barrier covers the other waves' copies
+    wait_vmcnt<LOADS * RPW>();
+    __builtin_amdgcn_s_barrier();
+
+    float acc[RPW][MT];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+    auto compute = [&](int j, const Raw &R, float (&ac)[MT]) __attribute__((always_inline)) {
+        const int sb = 8 * j + sbl;
+        const int mis = (2 * sb) & 3;  // block offset mod 4 (rows are 16-byte multiples)
+        const uint32_t sh = 8 * mis;
+        const uint32_t ql[9] = {(uint32_t)R.ql0[0], (uint32_t)R.ql0[1], (uint32_t)R.ql0[2], (uint32_t)R.ql0[3],
+                                (uint32_t)R.ql1[0], (uint32_t)R.ql1[1], (uint32_t)R.ql1[2], (uint32_t)R.ql1[3], R.ql2};
+        const uint32_t qh[9] = {(uint32_t)R.qh0[0], (uint32_t)R.qh0[1], (uint32_t)R.qh0[2], (uint32_t)R.qh0[3],
+                                (uint32_t)R.qh1[0], (uint32_t)R.qh1[1], (uint32_t)R.qh1[2], (uint32_t)R.qh1[3], R.qh2};
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t l4 = (__builtin_amdgcn_alignbit(ql[i + 1], ql[i], sh) >> (4 * (u >> 1))) & 0x0F0F0F0Fu;
+            const uint32_t h2 = (__builtin_amdgcn_alignbit(qh[i + 1], qh[i], sh) >> (2 * u)) & 0x03030303u;
+            const uint32_t v = l4 | (h2 << 4);
+            q[i] = (int)(((v | 0x80808080u) - 0x20202020u) ^ 0x80808080u);
+        }
+        const uint32_t scw = R.sc >> (8 * ((mis + 2 * u) & 3));
+        const int sc0 = (int)(int8_t)(scw & 0xFFu), sc1 = (int)(int8_t)((scw >> 8) & 0xFFu);
+        const float dw = f16_bits_to_f32(R.dd >> (8 * mis));
+        // values 128h + 32u + t: pieces 8h + 2u (t < 16) and 8h + 2u + 1, swizzled
+        const int sw = sb & 1;
+        const int k0 = sb * 256 + 16 * ((8 * h + 2 * u) ^ sw);
+        const int k1 = sb * 256 + 16 * ((8 * h + 2 * u + 1) ^ sw);
+        v4i a0[MT], a1[MT];
+        float da[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            a0[m] = *reinterpret_cast<const v4i *>(s_qs + m * K + k0);
+            a1[m] = *reinterpret_cast<const v4i *>(s_qs + m * K + k1);
+            da[m] = s_d[sb * M + m];
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s0 = __builtin_amdgcn_sdot4(q[e], a0[m][e], s0, false);
+                s1 = __builtin_amdgcn_sdot4(q[4 + e], a1[m][e], s1, false);
+            }
+            ac[m] = fmaf((float)(sc0 * s0 + sc1 * s1), da[m] * dw, ac[m]);
+        }
+    };
+
+    for (int j = 0; j < ipr; ++j) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            // row r's loads for group j have landed once the RPW - 1 issued
+            // after them may still be in flight
+            wait_vmcnt<LOADS * (RPW - 1)>();
+            compute(j, raw[r], acc[r]);
+            issue(r, j + 1, raw[r]);
+        }
+    }
+
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], o, 64);
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < M && row0 + r < N) a.out[(int64_t)m * N + row0 + r] = acc[r][m];
+    }
+    wait_vmcnt<0>();
+}
+
+}  // namespace gv
+
+static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+// Which Q6_K / ternary shapes the matrix-vector kernels take: up to 8 tokens,
+// K a multiple of 2048 (a row is a whole number of load instructions) and the
+// staged activations within the LDS budget.
+bool gemv_choice(int fmt, int M, int N, int K) {
+    (void)N;
+    if (fmt != 2 || M < 1 || M > 8 || K % 2048) return false;
+    return gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+}
+
+hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da, float *out,
+                       int M, int N, int K, hipStream_t stream) {
+    (void)fmt;
+    gv::Args a;
+    a.W = static_cast<const uint8_t *>(W);
+    a.qs = qs;
+    a.da = da;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    const dim3 grid((unsigned)((N + gv::RPG - 1) / gv::RPG)), block(64 * gv::NW);
+    const int mt = gv_tokens(M);
+    const size_t lds = (size_t)gv::lds_bytes(mt, M, K);
+    switch (mt) {
+        case 1: hipLaunchKernelGGL(gv::gemv_q6k_kernel<1>, grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(gv::gemv_q6k_kernel<2>, grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(gv::gemv_q6k_kernel<4>, grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL(gv::gemv_q6k_kernel<8>, grid, block, lds, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kq

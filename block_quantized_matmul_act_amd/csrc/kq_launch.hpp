@@ -15,6 +15,11 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
 hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
                           int K, hipStream_t stream);
 
+// Q6_K shapes the matrix-vector kernel takes (kq_gemv.hip), and its launcher.
+bool gemv_choice(int fmt, int M, int N, int K);
+hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da, float *out,
+                       int M, int N, int K, hipStream_t stream);
+
 // Q4_K kernels: one or two tokens with K a multiple of 2048 (and the staged
 // activations within the LDS budget) -> matrix-vector kernel; M <= 64 ->
 // few-token kernel; otherwise the 128 x 128 persistent kernel.

@@ -70,6 +70,12 @@ WORKLOADS = {
                                   "plain", "Q6_K x Q8_K FFN down, 2048 tokens"),
     "tern_5120_2048": Workload("tern_5120_2048", TQ, 2048, 17408, 5120, 1005,
                                "plain", "ternary x Q8_128, 2048 tokens, 17408x5120"),
+    "ffn_down_q6k_1": Workload("ffn_down_q6k_1", Q6_K, 1, 4096, 14336, 1004,
+                               "plain", "Q6_K x Q8_K FFN down, one token (decode; first "
+                               "token row of the 2048-token draw)"),
+    "tern_5120_1": Workload("tern_5120_1", TQ, 1, 17408, 5120, 1005,
+                            "plain", "ternary x Q8_128, one token (decode; first token row "
+                            "of the 2048-token draw), 17408x5120"),
 }
 
 
@@ -267,6 +273,10 @@ def make_weights(fmt: int, N: int, K: int, seed: int, dist: str = "plain") -> np
     raise ValueError(f"unknown format {fmt}")
 
 
+# token-prefix workloads: their activations are the first rows of the 2048-token draw
+_PREFIX_OF_2048 = ("ffn_up_q4k_2048", "ffn_up_q4k_64", "ffn_up_q4k_1", "ffn_down_q6k_1", "tern_5120_1")
+
+
 def make_workload(wl: Workload | str, n_rows: int | None = None, m_rows: int | None = None):
     """(W blocks, x fp32) for a named workload.  n_rows / m_rows take a prefix
     of the output rows / tokens (the draws are made at full size, so a prefix
@@ -274,7 +284,7 @@ def make_workload(wl: Workload | str, n_rows: int | None = None, m_rows: int | N
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     W = make_weights(wl.fmt, wl.N, wl.K, wl.seed, wl.dist)
-    full_rows = 2048 if wl.name.startswith("ffn_up_q4k") else wl.M
+    full_rows = 2048 if wl.name in _PREFIX_OF_2048 else wl.M
     x = draw_activations(wl.M, wl.K, wl.seed, wl.dist, rows=full_rows)
     if n_rows is not None:
         W = np.ascontiguousarray(W[:n_rows])

@@ -217,6 +217,7 @@ def test_shape_sweep(kq, fmt):
 
 
 @pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_1", "ffn_up_q4k_64", "ffn_up_q4k_2048",
+                                  "ffn_down_q6k_1",
                                   "ffn_down_q6k_2048", "tern_5120_2048"])
 def test_workload_full_size_sampled(kq, workloads, name):
     """Full-size problem in the benchmarked launch; the oracle checks a sample
@@ -253,27 +254,32 @@ def test_large_ragged_tiles(kq, workloads):
     say(f"  max err/tol {r:.3g}")
 
 
+MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 5, 8))}
+
+
+@pytest.mark.parametrize("fmt", sorted(MATVEC))
 @pytest.mark.parametrize("K", [2048, 4096])
-def test_matvec_path(kq, K):
-    """The matrix-vector kernel (one or two tokens, K a multiple of 2048):
-    both token counts it is built for, N ragged against its 16-row
+def test_matvec_path(kq, fmt, K):
+    """The matrix-vector kernels (a handful of tokens, K a multiple of 2048):
+    every token count each is built for, N ragged against their 16-row
     workgroups, full output against the oracle."""
-    Wfull = datagen.make_weights(Q4_K, 1000, K, 4000 + K)
-    xfull = datagen.draw_activations(2, K, 5000 + K)
-    for M in (1, 2):
+    name, tokens = MATVEC[fmt]
+    Wfull = datagen.make_weights(fmt, 1000, K, 4000 + K)
+    xfull = datagen.draw_activations(max(tokens), K, 5000 + K)
+    for M in tokens:
         for N in (16, 40, 1000):
-            v = kq.kq_select_variant(Q4_K, M, N, K)
-            assert kq.kq_variant_name(v) == "gemm_q4_k_matvec"
-            say(f"matvec M={M} N={N} K={K}")
+            v = kq.kq_select_variant(fmt, M, N, K)
+            assert kq.kq_variant_name(v) == name
+            say(f"matvec fmt={fmt} M={M} N={N} K={K}")
             before = kq.kq_dispatch_count(v)
-            gemm_vs_oracle(kq, Q4_K, np.ascontiguousarray(Wfull[:N]),
+            gemm_vs_oracle(kq, fmt, np.ascontiguousarray(Wfull[:N]),
                            np.ascontiguousarray(xfull[:M]), M, N, K)
             assert kq.kq_dispatch_count(v) == before + 1
 
 
 def test_matvec_boundaries(kq):
-    """Shapes just outside the matrix-vector kernel's rule go to the
-    few-token kernel; inside it the long-K projection still takes it."""
+    """Shapes just outside the matrix-vector kernels' rules go to the
+    tile kernels; inside them the long-K projection still takes them."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
     assert name(3, 4096, 4096) == "gemm_q4_k_m64"
     assert name(2, 4096, 1792) == "gemm_q4_k_m64"      # K not a multiple of 2048
@@ -283,6 +289,14 @@ def test_matvec_boundaries(kq):
     x = datagen.draw_activations(2, 14336, 4343)
     say("matvec M=2 N=48 K=14336")
     gemm_vs_oracle(kq, Q4_K, W, x, 2, 48, 14336)
+    q6 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q6_K, M, N, K))
+    assert q6(9, 4096, 14336) == "gemm_q6_k_128x128"
+    assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_128x128"  # K not a multiple of 2048
+    assert q6(8, 4096, 14336) == "gemm_q6_k_matvec"
+    W6 = datagen.make_weights(Q6_K, 40, 14336, 4444)
+    x6 = datagen.draw_activations(8, 14336, 4545)
+    say("matvec Q6_K M=8 N=40 K=14336")
+    gemm_vs_oracle(kq, Q6_K, W6, x6, 8, 40, 14336)
 
 
 def test_other_reading_of_distributions(kq):
