@@ -23,6 +23,7 @@ enum Variant {
     V_GEMM_Q6K_128x128,
     V_GEMM_Q6K_MATVEC,
     V_GEMM_TQ_128x128,
+    V_GEMM_TQ_MATVEC,
     V_SUBSUMS_Q4K,
     V_SUBSUMS_Q6K,
     V_SUBSUMS_TQ,
@@ -31,7 +32,7 @@ enum Variant {
 
 const char *const kVariantNames[V_COUNT] = {
     "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
-    "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "subsums_q4_k",  "subsums_q6_k",
+    "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
     "subsums_tq",
 };
 
@@ -109,7 +110,8 @@ int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
             default: return V_GEMM_Q4K_128x128;
         }
     }
-    if (kq::gemv_choice(fmt, (int)M, (int)N, (int)K)) return V_GEMM_Q6K_MATVEC;
+    if (kq::gemv_choice(fmt, (int)M, (int)N, (int)K))
+        return fmt == KQ_Q6_K ? V_GEMM_Q6K_MATVEC : V_GEMM_TQ_MATVEC;
     return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
 }
 

@@ -1,5 +1,5 @@
-// kq_gemv.hip -- matrix-vector kernels for Q6_K weights (a handful of tokens,
-// decode).
+// kq_gemv.hip -- matrix-vector kernels for Q6_K and ternary weights (a
+// handful of tokens, decode).
 //
 // A token's product with a weight row is a stream of the row's blocks: a
 // handful of tokens need many waves with loads in flight, not matrix cores.
@@ -208,22 +208,183 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
     wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Ternary.  Blocks are 28 bytes (26 trit bytes, fp16 scale), 4-byte aligned.
+// A load instruction covers 8 consecutive blocks of each of the wave's 8 rows:
+// lane l takes block l%8 of row l/8, all 128 values.  Byte b holds the digits
+// e = t + 1 of values 5b .. 5b+4 (value 5b + p at base-3 position p).  The
+// trits come from an LDS table with four phases: entry (phi, v) holds the five
+// trits of byte value v as int8 at byte offsets phi .. phi+4 of 8 bytes.  Byte
+// b's values start at byte 5b of the block's natural order, i.e. at offset
+// 5b mod 4 = b mod 4 of dword floor(5b/4), so the phase-(b mod 4) entry ORs
+// straight into natural-order dwords 5b/4 and 5b/4 + 1 (the two padding
+// positions past value 127 are dropped).  Then 32 v_dot4 per token, one fold
+// per block with the block scale.  The 8 lanes of a row are summed at the
+// end in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int TQB = 28;         // ternary block bytes
+constexpr int TRPW = 8;         // rows per wave
+constexpr int TRPG = NW * TRPW; // rows per workgroup
+constexpr int TQ_DEPTH = 2;     // load instructions in flight per wave
+constexpr int LUT_BYTES = 4 * 256 * 8;
+__host__ __device__ constexpr int tq_lds_d(int M, int nblk) { return (nblk * M * 4 + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int tq_lds_bytes(int MT, int M, int K) {
+    return MT * K + tq_lds_d(M, K / 128) + LUT_BYTES + 256;
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
+    extern __shared__ __attribute__((aligned(16))) int8_t s_gv[];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int M = a.M, N = a.N, K = a.K, nblk = K / 128;
+    const int rowbytes = nblk * TQB;
+    const int ipr = nblk >> 3;  // load instructions per row
+    const int r = lane >> 3, bl = lane & 7;
+    const int row = blockIdx.x * TRPG + w * TRPW + r;
+    int8_t *const s_qs = s_gv;
+    float *const s_d = reinterpret_cast<float *>(s_gv + MT * K);
+    int8_t *const s_lut = s_gv + MT * K + tq_lds_d(M, nblk);
+
+    // ---- activations -> LDS (piece i of block b at slot i ^ (b % 8): the 8
+    // blocks one read instruction touches fall on different banks) ----------
+    {
+        const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+        const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nblk * M * 4, RSRC_FLAGS);
+        const int nq = (M * K) >> 10, nd = (nblk * M * 4 + 255) >> 8;
+        const int aq = 128 * (lane >> 3) + 16 * ((lane & 7) ^ (lane >> 3));
+        for (int c = w; c < nq; c += NW) copy16(rs_a, s_qs + 1024 * c, 1024 * c + aq);
+        for (int c = w; c < nd; c += NW) copy4(rs_d, reinterpret_cast<int8_t *>(s_d) + 256 * c, 256 * c + 4 * lane);
+    }
+    // ---- weights: TQ_DEPTH instructions in flight (7 dwords per lane) ---------
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    struct Raw {
+        v4i w0;
+        v3u w1;
+    };
+    // (rows past N: offsets stay below (N + 256) rows, the host's limit)
+    auto issue = [&](int j, Raw &R) __attribute__((always_inline)) {
+        const int off = row * rowbytes + (8 * min(j, ipr - 1) + bl) * TQB;
+        R.w0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0));
+        R.w1 = __builtin_bit_cast(v3u, __builtin_amdgcn_raw_buffer_load_b96(rs_w, off + 16, 0, 0));
+    };
+    Raw raw[TQ_DEPTH];
+#pragma unroll
+    for (int s = 0; s < TQ_DEPTH; ++s) issue(s, raw[s]);
+
+    // ---- the trit table: entry (phi, v), 8 bytes, at 8 * (256 phi + v) ----
+    for (int e = threadIdx.x; e < 4 * 256; e += 64 * NW) {
+        const int phi = e >> 8, v = e & 255;
+        uint64_t ent = 0;
+        if (v < 243) {
+            int x = v;
+#pragma unroll
+            for (int p = 0; p < 5; ++p) {
+                const int t = x % 3 - 1;
+                x /= 3;
+                ent |= (uint64_t)(uint8_t)(int8_t)t << (8 * (phi + p));
+            }
+        }
+        *reinterpret_cast<uint64_t *>(s_lut + 8 * e) = ent;
+    }
+    // this wave's activation copies have landed once at most the weight loads
+    // are in flight, and its table entries once its LDS writes are done; the
+    // barrier covers the other waves'
+    wait_vmcnt<2 * TQ_DEPTH>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    const uint32_t lut = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)s_lut;
+
+    auto compute = [&](int j, const Raw &R) __attribute__((always_inline)) {
+        const int b = 8 * j + bl;
+        const uint32_t wv[7] = {(uint32_t)R.w0[0], (uint32_t)R.w0[1], (uint32_t)R.w0[2], (uint32_t)R.w0[3],
+                                R.w1[0], R.w1[1], R.w1[2]};
+        // table lookups for the 26 trit bytes
+        uint64_t ent[26];
+#pragma unroll
+        for (int by = 0; by < 26; ++by) {
+            const uint32_t v = (wv[by >> 2] >> (8 * (by & 3))) & 0xFFu;
+            const uint32_t addr = lut + 2048u * (uint32_t)(by & 3) + 8u * v;
+            ent[by] = *reinterpret_cast<const __attribute__((address_space(3))) uint64_t *>(
+                (__attribute__((address_space(3))) void *)(uintptr_t)addr);
+        }
+        // natural-order int8 trits: byte by ORs into dwords 5by/4 and 5by/4 + 1
+        int nat[32];
+#pragma unroll
+        for (int d = 0; d < 32; ++d) nat[d] = 0;
+#pragma unroll
+        for (int by = 0; by < 26; ++by) {
+            const int d0 = (5 * by) >> 2;
+            nat[d0] |= (int)(uint32_t)ent[by];
+            if (d0 + 1 < 32) nat[d0 + 1] |= (int)(uint32_t)(ent[by] >> 32);
+        }
+        const float dw = f16_bits_to_f32(wv[6] >> 16);
+        const int kb = b * 128;
+        v4i av[MT][8];
+        float da[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                av[m][i] = *reinterpret_cast<const v4i *>(s_qs + m * K + kb + 16 * (i ^ (b & 7)));
+            da[m] = s_d[b * M + m];
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            int sacc = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc = __builtin_amdgcn_sdot4(nat[4 * i + e], av[m][i][e], sacc, false);
+            acc[m] = fmaf((float)sacc, da[m] * dw, acc[m]);
+        }
+    };
+
+    for (int j0 = 0; j0 < ipr; j0 += TQ_DEPTH) {
+#pragma unroll
+        for (int s = 0; s < TQ_DEPTH; ++s) {
+            // instruction j0 + s has landed once the TQ_DEPTH - 1 issued after
+            // it may still be in flight (past the last, re-reads are harmless)
+            wait_vmcnt<2 * (TQ_DEPTH - 1)>();
+            if (j0 + s < ipr) compute(j0 + s, raw[s]);
+            issue(j0 + s + TQ_DEPTH, raw[s]);
+        }
+    }
+    // a row's total: its 8 lanes summed in a fixed order, stored by lane 8r
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] += __shfl_xor(acc[m], o, 64);
+    if (bl == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < M && row < N) a.out[(int64_t)m * N + row] = acc[m];
+    }
+    wait_vmcnt<0>();
+}
+
 }  // namespace gv
 
 static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 // Which Q6_K / ternary shapes the matrix-vector kernels take: up to 8 tokens,
-// K a multiple of 2048 (a row is a whole number of load instructions) and the
-// staged activations within the LDS budget.
+// K a multiple of 2048 (Q6_K) or 1024 (ternary), so that a row is a whole
+// number of load instructions, and the staged activations within the LDS
+// budget.
 bool gemv_choice(int fmt, int M, int N, int K) {
     (void)N;
-    if (fmt != 2 || M < 1 || M > 8 || K % 2048) return false;
-    return gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    if (M < 1 || M > 8) return false;
+    if (fmt == 2) return K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    if (fmt == 3) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    return false;
 }
 
 hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da, float *out,
                        int M, int N, int K, hipStream_t stream) {
-    (void)fmt;
     gv::Args a;
     a.W = static_cast<const uint8_t *>(W);
     a.qs = qs;
@@ -232,8 +393,20 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
     a.M = M;
     a.N = N;
     a.K = K;
-    const dim3 grid((unsigned)((N + gv::RPG - 1) / gv::RPG)), block(64 * gv::NW);
+    const dim3 block(64 * gv::NW);
     const int mt = gv_tokens(M);
+    if (fmt == 3) {
+        const dim3 grid((unsigned)((N + gv::TRPG - 1) / gv::TRPG));
+        const size_t lds = (size_t)gv::tq_lds_bytes(mt, M, K);
+        switch (mt) {
+            case 1: hipLaunchKernelGGL(gv::gemv_tq_kernel<1>, grid, block, lds, stream, a); break;
+            case 2: hipLaunchKernelGGL(gv::gemv_tq_kernel<2>, grid, block, lds, stream, a); break;
+            case 4: hipLaunchKernelGGL(gv::gemv_tq_kernel<4>, grid, block, lds, stream, a); break;
+            default: hipLaunchKernelGGL(gv::gemv_tq_kernel<8>, grid, block, lds, stream, a); break;
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((N + gv::RPG - 1) / gv::RPG));
     const size_t lds = (size_t)gv::lds_bytes(mt, M, K);
     switch (mt) {
         case 1: hipLaunchKernelGGL(gv::gemv_q6k_kernel<1>, grid, block, lds, stream, a); break;

@@ -15,7 +15,8 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
 hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sums, int M, int N,
                           int K, hipStream_t stream);
 
-// Q6_K shapes the matrix-vector kernel takes (kq_gemv.hip), and its launcher.
+// Q6_K and ternary shapes the matrix-vector kernels take (kq_gemv.hip), and
+// their launcher.
 bool gemv_choice(int fmt, int M, int N, int K);
 hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da, float *out,
                        int M, int N, int K, hipStream_t stream);

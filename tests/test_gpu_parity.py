@@ -217,7 +217,7 @@ def test_shape_sweep(kq, fmt):
 
 
 @pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_1", "ffn_up_q4k_64", "ffn_up_q4k_2048",
-                                  "ffn_down_q6k_1",
+                                  "ffn_down_q6k_1", "tern_5120_1",
                                   "ffn_down_q6k_2048", "tern_5120_2048"])
 def test_workload_full_size_sampled(kq, workloads, name):
     """Full-size problem in the benchmarked launch; the oracle checks a sample
@@ -254,7 +254,8 @@ def test_large_ragged_tiles(kq, workloads):
     say(f"  max err/tol {r:.3g}")
 
 
-MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 5, 8))}
+MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 5, 8)),
+          TQ: ("gemm_tq_matvec", (1, 2, 3, 5, 8))}
 
 
 @pytest.mark.parametrize("fmt", sorted(MATVEC))
@@ -293,6 +294,14 @@ def test_matvec_boundaries(kq):
     assert q6(9, 4096, 14336) == "gemm_q6_k_128x128"
     assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_128x128"  # K not a multiple of 2048
     assert q6(8, 4096, 14336) == "gemm_q6_k_matvec"
+    tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
+    assert tq(9, 17408, 5120) == "gemm_tq_128x128"
+    assert tq(8, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024
+    assert tq(8, 17408, 5120) == "gemm_tq_matvec"
+    Wt = datagen.make_weights(TQ, 40, 5120, 4646)
+    xt = datagen.draw_activations(8, 5120, 4747)
+    say("matvec ternary M=8 N=40 K=5120")
+    gemm_vs_oracle(kq, TQ, Wt, xt, 8, 40, 5120)
     W6 = datagen.make_weights(Q6_K, 40, 14336, 4444)
     x6 = datagen.draw_activations(8, 14336, 4545)
     say("matvec Q6_K M=8 N=40 K=14336")
