@@ -3,6 +3,11 @@
 // out[m][n] = sum_k W^[n][k] * A^[m][k] for Q4_K / Q6_K weights against Q8_K
 // activations and ternary weights against Q8_128 activations.
 //
+// Launched for Q6_K and ternary weights (shapes the matrix-vector kernels of
+// kq_gemv.hip do not take); Q4_K runs on the kernels of kq_gemm_q4k.hip.  The
+// Q4_K branches below are not instantiated by launch_gemm; the sub-sum test
+// hook (subsums_kernel) uses this file's loaders for all three formats.
+//
 // Design (MI355X-first; prior art: the BigTile kernel of vllm.cpp PR 3036,
 // which reuses staged activation rows across warps, and llama.cpp's
 // mul_mat_q, which P1 describes as sharing one cooperatively loaded 128x128
@@ -1082,9 +1087,6 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {
-        case FMT_Q4K:
-            hipLaunchKernelGGL(gemm_kernel<FMT_Q4K>, dim3(grid), dim3(MNT), 0, stream, a);
-            break;
         case FMT_Q6K:
             hipLaunchKernelGGL(gemm_kernel<FMT_Q6K>, dim3(grid), dim3(MNT), 0, stream, a);
             break;

@@ -792,7 +792,8 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 // Matrix-vector kernel for one or two tokens (decode): the product is a stream of
 // 33 MB of weights for a handful of dot products each, so it needs many waves
 // with loads in flight rather than matrix cores.  Workgroups of 4 waves each
-// own 16 weight rows (4 per wave); the activation buffer (values, scales,
+// own 8 weight rows (2 per wave: 8.4 us for one token on 14336 x 4096, against
+// 8.9 and 9.0 with four and one); the activation buffer (values, scales,
 // min-term operands of the few tokens) is copied once per workgroup into LDS.
 //
 // Load instruction i of a wave covers 8 consecutive superblocks of one of its
@@ -811,7 +812,10 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 // ---------------------------------------------------------------------------
 namespace mv {
 constexpr int NW = 4;          // waves per workgroup
-constexpr int RPW = 4;         // weight rows per wave
+#ifndef MV_RPW
+#define MV_RPW 2
+#endif
+constexpr int RPW = MV_RPW;    // weight rows per wave
 constexpr int RPG = NW * RPW;  // weight rows per workgroup
 // Up to two tokens: measured on 14336 x 4096 weights, 8.9 and 10.6 us
 // against 14.6 us for the few-token kernel; at three and four tokens the two

@@ -225,7 +225,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
 constexpr int TQB = 28;         // ternary block bytes
 constexpr int TRPW = 8;         // rows per wave
 constexpr int TRPG = NW * TRPW; // rows per workgroup
-constexpr int TQ_DEPTH = 2;     // load instructions in flight per wave
+#ifndef GV_TQ_DEPTH
+#define GV_TQ_DEPTH 2
+#endif
+constexpr int TQ_DEPTH = GV_TQ_DEPTH;  // load instructions in flight per wave
 constexpr int LUT_BYTES = 4 * 256 * 8;
 __host__ __device__ constexpr int tq_lds_d(int M, int nblk) { return (nblk * M * 4 + 1023) / 1024 * 1024; }
 __host__ __device__ constexpr int tq_lds_bytes(int MT, int M, int K) {
