@@ -18,6 +18,7 @@ KQ_Q4_K, KQ_Q6_K, KQ_TQ = 1, 2, 3
 KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
 KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
+KQ_DEBUG_UNPACK_MAX_BLOCKS = 1 << 24
 KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
     -1, -2, -3, -4, -5, -6)
 (KQ_CALIB_MFMA_I8, KQ_CALIB_MFMA_I8_TOGGLE, KQ_CALIB_VALU_F32, KQ_CALIB_MFMA_I8_VALU,
@@ -33,6 +34,7 @@ SIGNATURES = {
     "kq_quantize_act": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "kq_gemm": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kq_gemm_subsums": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "kq_debug_unpack": (_I, [_I, _P, _I64, _P, _P, _P]),
     "kq_num_variants": (_I, []),
     "kq_variant_name": (ctypes.c_char_p, [_I]),
     "kq_dispatch_count": (ctypes.c_uint64, [_I]),
@@ -146,6 +148,11 @@ def kq_select_variant(fmt, M, N, K):
     return lib().kq_select_variant(fmt, M, N, K)
 
 
+def kq_debug_unpack(fmt, W, nblocks, q, scales, stream=None):
+    return _check(lib().kq_debug_unpack(fmt, _ptr(W), nblocks, _ptr(q), _ptr(scales),
+                                        _stream(stream)), "kq_debug_unpack")
+
+
 def kq_calib_launch(kind, param=0, buf=None, nbytes=0, stream=None):
     """Launch one calibration kernel; returns the work it does (int8 ops, fp32
     flops or bytes)."""
@@ -208,3 +215,14 @@ def gemm(fmt, W, a_q8, M, N, K, out=None, stream=None):
         out = torch.empty((M, N), dtype=torch.float32, device=a_q8.device)
     kq_gemm(fmt, W, a_q8, M, N, K, out, stream)
     return out
+
+
+def debug_unpack(fmt, W, nblocks, stream=None):
+    """Decode nblocks weight blocks (uint8 device tensor) with the tile kernel's
+    loaders: (q int8 [nblocks][QK], scales int32 [nblocks][16] or None)."""
+    import torch
+    qk = 128 if fmt == KQ_TQ else 256
+    q = torch.empty((nblocks, qk), dtype=torch.int8, device=W.device)
+    scales = None if fmt == KQ_TQ else torch.empty((nblocks, 16), dtype=torch.int32, device=W.device)
+    kq_debug_unpack(fmt, W, nblocks, q, scales, stream)
+    return q, scales

@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include "kq_calib.hpp"
+#include "kq_hooks.hpp"
 #include "kq_launch.hpp"
 
 namespace {
@@ -201,6 +202,19 @@ int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t
     g_count[fmt == KQ_Q4_K ? V_SUBSUMS_Q4K : fmt == KQ_Q6_K ? V_SUBSUMS_Q6K : V_SUBSUMS_TQ]
         .fetch_add(1);
     return KQ_OK;
+}
+
+int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
+                    hipStream_t stream) {
+    if (!qk_of(fmt)) return KQ_ERR_FMT;
+    if (nblocks < 0 || nblocks > KQ_DEBUG_UNPACK_MAX_BLOCKS) return KQ_ERR_SHAPE;
+    if (nblocks == 0) return KQ_OK;
+    if (!W || !q || (fmt != KQ_TQ && !scales)) return KQ_ERR_NULL;
+    if (!aligned16(W) || !aligned16(q) || ((uintptr_t)scales & 3u)) return KQ_ERR_ALIGN;
+    return kq::launch_debug_unpack(fmt, W, nblocks, q, fmt == KQ_TQ ? nullptr : scales, stream) ==
+                   hipSuccess
+               ? KQ_OK
+               : KQ_ERR_HIP;
 }
 
 int kq_calib_launch(int kind, int param, const void *buf, int64_t bytes, double *work,

@@ -5,8 +5,9 @@
 //
 // Launched for Q6_K and ternary weights (shapes the matrix-vector kernels of
 // kq_gemv.hip do not take); Q4_K runs on the kernels of kq_gemm_q4k.hip.  The
-// Q4_K branches below are not instantiated by launch_gemm; the sub-sum test
-// hook (subsums_kernel) uses this file's loaders for all three formats.
+// Q4_K branches below are not instantiated by launch_gemm; the two test hooks
+// (subsums_kernel, debug_unpack_kernel) use this file's loaders for all three
+// formats.
 //
 // Design (MI355X-first; prior art: the BigTile kernel of vllm.cpp PR 3036,
 // which reuses staged activation rows across warps, and llama.cpp's
@@ -37,6 +38,7 @@
 //     land on the same XCD (blocks are dealt round-robin to the 8 XCDs), so
 //     a weight tile is fetched from HBM once per XCD L2.
 #include "kq_device.hpp"
+#include "kq_hooks.hpp"
 #include "kq_launch.hpp"
 
 #include <type_traits>
@@ -101,6 +103,12 @@ struct WRaw<FMT_TQ> {
 
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) {
     return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// A Q6_K block starts 0 or 2 bytes into the dword its loads begin at; word i
+// of the block is bytes [2, 4) of loaded word i and [0, 2) of word i + 1.
+__device__ __forceinline__ uint32_t q6k_realign(uint32_t lo, uint32_t hi, uint32_t shift) {
+    return shift ? __builtin_amdgcn_alignbyte(hi, lo, 2) : lo;
 }
 
 // Load this thread's part of weight row `n` (global row index, < N) for chunk c.
@@ -219,11 +227,11 @@ __device__ __forceinline__ void unpack_w(const WRaw<FMT> &r, bool valid, int8_t 
         // realign to the block's byte 0
         uint32_t ql[16], qh[8], scw[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ql[i] = sh ? __builtin_amdgcn_alignbyte(r.ql[i + 1], r.ql[i], 2) : r.ql[i];
+        for (int i = 0; i < 16; ++i) ql[i] = q6k_realign(r.ql[i], r.ql[i + 1], sh);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qh[i] = sh ? __builtin_amdgcn_alignbyte(r.qh[i + 1], r.qh[i], 2) : r.qh[i];
+        for (int i = 0; i < 8; ++i) qh[i] = q6k_realign(r.qh[i], r.qh[i + 1], sh);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) scw[i] = sh ? __builtin_amdgcn_alignbyte(r.sc[i + 1], r.sc[i], 2) : r.sc[i];
+        for (int i = 0; i < 2; ++i) scw[i] = q6k_realign(r.sc[i], r.sc[i + 1], sh);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -1092,6 +1100,97 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
             break;
         default:
             hipLaunchKernelGGL(gemm_kernel<FMT_TQ>, dim3(grid), dim3(MNT), 0, stream, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Loader test hook: nblocks consecutive blocks of W, read as one weight row,
+// go through load_w and unpack_w (unit scales) -- the loaders of the tile
+// kernel above -- and the integer operand of every value is rebuilt from the
+// digit planes as the MFMA accumulation does (high plane << SHIFT plus low
+// plane).  The scale fields come from the same words the loader fetched:
+// q4k_fields for the Q4_K 6-bit scales and mins, the realigned scale bytes for
+// Q6_K.  One thread per chunk half (Q4_K, Q6_K: 128 values of a superblock;
+// ternary: one 128-value block), 32 chunks per 64-thread workgroup.
+// ---------------------------------------------------------------------------
+constexpr int DBG_CHUNKS = 32;
+
+template <int FMT>
+__global__ __launch_bounds__(64) void debug_unpack_kernel(GemmArgs a, int8_t *q, int32_t *scales) {
+    constexpr int NDIG = Fmt<FMT>::NDIG, SHIFT = Fmt<FMT>::SHIFT;
+    __shared__ __attribute__((aligned(16))) int8_t s_w[NDIG * DBG_CHUNKS * PITCH];
+    __shared__ float s_dw[2 * DBG_CHUNKS];
+    const int nl = threadIdx.x >> 1, part = threadIdx.x & 1;
+    const int c = blockIdx.x * DBG_CHUNKS + nl;
+    // block holding this thread's values
+    const int64_t b = FMT == FMT_TQ ? 2 * (int64_t)c + part : c;
+    const bool valid = b < a.nblk;
+    WRaw<FMT> wr;
+    // past the end: Q4_K/Q6_K read block 0 instead (nothing is stored); the
+    // ternary loader fills blocks past nblk itself without reading
+    load_w<FMT>(wr, a, 0, part, (valid || FMT == FMT_TQ) ? c : 0);
+    unpack_w<FMT, true>(wr, valid, s_w, DBG_CHUNKS * PITCH, nl, part, s_dw, DBG_CHUNKS, nullptr, 0,
+                        false);
+    __syncthreads();
+    if (!valid) return;
+
+    const int8_t *hi = s_w + nl * PITCH + 128 * part;
+    int8_t *dst = q + (FMT == FMT_TQ ? b * 128 : b * 256 + 128 * part);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v4i h = *reinterpret_cast<const v4i *>(hi + 16 * i), v;
+        if constexpr (NDIG == 2) {
+            const v4i l = *reinterpret_cast<const v4i *>(hi + DBG_CHUNKS * PITCH + 16 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int hv = (int8_t)(h[e] >> (8 * bb)), lv = (int8_t)(l[e] >> (8 * bb));
+                    w |= (uint32_t)((hv * (1 << SHIFT) + lv) & 0xFF) << (8 * bb);
+                }
+                v[e] = (int)w;
+            }
+        } else {
+            v = h;
+        }
+        *reinterpret_cast<v4i *>(dst + 16 * i) = v;
+    }
+    if constexpr (FMT == FMT_Q4K) {
+        uint32_t sc[4], mn[4];
+        q4k_fields((uint32_t)wr.hdr[1], (uint32_t)wr.hdr[2], (uint32_t)wr.hdr[3], 4 * part, 4, sc, mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            scales[b * 16 + 4 * part + i] = (int32_t)sc[i];
+            scales[b * 16 + 8 + 4 * part + i] = (int32_t)mn[i];
+        }
+    } else if constexpr (FMT == FMT_Q6K) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t w = q6k_realign(wr.sc[j >> 2], wr.sc[(j >> 2) + 1], wr.shift);
+            scales[b * 16 + 8 * part + j] = (int32_t)(int8_t)(w >> (8 * (j & 3)));
+        }
+    }
+}
+
+hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
+                               hipStream_t stream) {
+    GemmArgs a{};
+    a.W = (const uint8_t *)W;
+    a.nblk = (int)nblocks;
+    const int64_t chunks = fmt == FMT_TQ ? (nblocks + 1) / 2 : nblocks;
+    const unsigned grid = (unsigned)((chunks + DBG_CHUNKS - 1) / DBG_CHUNKS);
+    switch (fmt) {
+        case FMT_Q4K:
+            hipLaunchKernelGGL(debug_unpack_kernel<FMT_Q4K>, dim3(grid), dim3(64), 0, stream, a, q, scales);
+            break;
+        case FMT_Q6K:
+            hipLaunchKernelGGL(debug_unpack_kernel<FMT_Q6K>, dim3(grid), dim3(64), 0, stream, a, q, scales);
+            break;
+        default:
+            hipLaunchKernelGGL(debug_unpack_kernel<FMT_TQ>, dim3(grid), dim3(64), 0, stream, a, q, scales);
             break;
     }
     return hipGetLastError();

@@ -162,6 +162,26 @@ int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int6
 int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N,
                     int64_t K, int32_t *sums, hipStream_t stream);
 
+/*
+ * Test hook: decode nblocks consecutive weight blocks of W (device, 16-byte
+ * aligned, kq_weight_bytes(fmt, 1, nblocks * QK) bytes) with the weight
+ * loaders of the tile GEMM kernel (the loader fuzz test of llama.cpp PR 214,
+ * which ran its unpack on thousands of random packed blocks against the
+ * scalar codec).  Writes, for block b:
+ *   q [b][QK] int8 (device, 16-byte aligned): the integer operand of every
+ *     value in storage order, q in [0,15] (Q4_K), q - 32 (Q6_K), t (ternary);
+ *   scales [b][16] int32 (device, 4-byte aligned): Q4_K sc_0..sc_7 then
+ *     m_0..m_7 (the 6-bit fields); Q6_K the 16 int8 scales, sign-extended.
+ *     Not written for ternary, where scales may be NULL.
+ * The fp16 d / dmin fields are not decoded here.  nblocks may be at most
+ * KQ_DEBUG_UNPACK_MAX_BLOCKS (KQ_ERR_SHAPE beyond, or when negative); 0 returns
+ * KQ_OK with no launch.  Unknown fmt -> KQ_ERR_FMT; W or q NULL (or scales for
+ * Q4_K / Q6_K) -> KQ_ERR_NULL; misaligned pointers -> KQ_ERR_ALIGN.
+ */
+#define KQ_DEBUG_UNPACK_MAX_BLOCKS (1 << 24)
+int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
+                    hipStream_t stream);
+
 /* Per-variant dispatch counters (incremented on each successful launch) and
  * their names, so tests can prove which kernel variant ran (vllm.cpp PR 3036
  * added such counters after finding tests that never reached a variant). */

@@ -179,3 +179,25 @@ def test_calib_rejects_bad_arguments(kq):
     assert L.kq_calib_launch(R, 0, 4096, 0, ctypes.byref(w), None) == kq.KQ_ERR_SHAPE
     assert L.kq_calib_launch(R, 0, 4096, 24, ctypes.byref(w), None) == kq.KQ_ERR_SHAPE
     assert L.kq_calib_launch(R, 0, 4104, 1024, ctypes.byref(w), None) == kq.KQ_ERR_ALIGN
+
+
+def test_debug_unpack_rejects_bad_arguments(kq):
+    L = kq.lib()
+    Q4, Q6, TQ = kq.KQ_Q4_K, kq.KQ_Q6_K, kq.KQ_TQ
+    # unknown format, bad counts, zero work
+    assert L.kq_debug_unpack(0, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
+    assert L.kq_debug_unpack(4, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
+    assert L.kq_debug_unpack(Q4, 4096, -1, 8192, 16384, None) == kq.KQ_ERR_SHAPE
+    assert L.kq_debug_unpack(Q4, 4096, kq.KQ_DEBUG_UNPACK_MAX_BLOCKS + 1, 8192, 16384,
+                             None) == kq.KQ_ERR_SHAPE
+    for fmt in (Q4, Q6, TQ):
+        assert L.kq_debug_unpack(fmt, None, 0, None, None, None) == kq.KQ_OK
+    # null pointers: scales may be NULL only for ternary
+    assert L.kq_debug_unpack(Q4, None, 1, 8192, 16384, None) == kq.KQ_ERR_NULL
+    assert L.kq_debug_unpack(Q6, 4096, 1, None, 16384, None) == kq.KQ_ERR_NULL
+    assert L.kq_debug_unpack(Q4, 4096, 1, 8192, None, None) == kq.KQ_ERR_NULL
+    assert L.kq_debug_unpack(Q6, 4096, 1, 8192, None, None) == kq.KQ_ERR_NULL
+    # alignment: W and q 16 bytes, scales 4 bytes
+    assert L.kq_debug_unpack(Q4, 4100, 1, 8192, 16384, None) == kq.KQ_ERR_ALIGN
+    assert L.kq_debug_unpack(TQ, 4096, 1, 8200, None, None) == kq.KQ_ERR_ALIGN
+    assert L.kq_debug_unpack(Q6, 4096, 1, 8192, 16386, None) == kq.KQ_ERR_ALIGN

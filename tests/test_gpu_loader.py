@@ -1,0 +1,240 @@
+"""GPU tests of the weight loaders against the oracle's codec.
+
+1. kq_debug_unpack runs the tile kernel's loaders on fuzzed blocks (the loader
+   fuzz test of llama.cpp PR 214: thousands of arbitrary packed blocks through
+   the unpack, compared value by value with the scalar codec) and on blocks
+   built so that every field position takes every value.  Integer results must
+   match bit for bit.
+2. Identity activations through every GEMM kernel variant: with unit
+   activation scales and qs = I, row m of the product is column m of the
+   dequantized weights, so each kernel's own loader (registers, LDS digit
+   planes, trit table) is checked at every K position.  Q6_K and ternary
+   results are exact in fp32; Q4_K's min term goes through bf16 hi/lo operands
+   (16 significant bits), so it is checked against a bound derived from that
+   split instead.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import kqref
+
+pytestmark = pytest.mark.gpu
+
+Q4_K, Q6_K, TQ = 1, 2, 3
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
+BB = {Q4_K: 144, Q6_K: 210, TQ: 28}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def kq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_matmul_act_amd as kq
+    kq.lib()
+    return kq
+
+
+def dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# ------------------------------------------------------------ block sets
+
+def fuzz_blocks(fmt: int, n: int, seed: int) -> np.ndarray:
+    """n arbitrary blocks: every byte pattern is a valid Q4_K / Q6_K block; a
+    ternary block takes digit bytes <= 242 and a last digit byte whose two
+    spare digits are 1 (108..134)."""
+    rng = np.random.default_rng(seed)
+    if fmt != TQ:
+        return rng.integers(0, 256, size=(n, BB[fmt]), dtype=np.uint8)
+    b = np.empty((n, 28), np.uint8)
+    b[:, :25] = rng.integers(0, 243, size=(n, 25))
+    b[:, 25] = 108 + rng.integers(0, 27, size=n)
+    b[:, 26:] = rng.integers(0, 256, size=(n, 2))
+    return b
+
+
+def exhaustive_blocks(fmt: int) -> np.ndarray:
+    """Blocks in which every field position takes every value it can hold."""
+    if fmt == Q4_K:
+        # 6-bit scale/min fields: field f of block b is (b + 5f) mod 64; nibble
+        # bytes: byte i of block b is (b + i) mod 256
+        B = 256
+        b = np.arange(B)[:, None]
+        fields = (b + 5 * np.arange(16)[None, :]) % 64
+        bits = ((fields[:, :, None] >> np.arange(6)) & 1).reshape(B, 96).astype(np.uint8)
+        out = np.zeros((B, 144), np.uint8)
+        out[:, 0:4] = (b + np.arange(4)) % 256
+        out[:, 4:16] = np.packbits(bits, axis=1, bitorder="little")
+        out[:, 16:] = (b + np.arange(128)) % 256
+        return out
+    if fmt == Q6_K:
+        # every byte of the block, quant and scale bytes alike, takes all 256
+        # values across the set (byte i of block b is (b + 3i) mod 256)
+        b = np.arange(256)[:, None]
+        return ((b + 3 * np.arange(210)[None, :]) % 256).astype(np.uint8)
+    # ternary: digit byte i of block b is (b + 7i) mod 243; the last digit byte
+    # runs through its 27 valid values
+    b = np.arange(243)[:, None]
+    out = np.zeros((243, 28), np.uint8)
+    out[:, :25] = (b + 7 * np.arange(25)[None, :]) % 243
+    out[:, 25] = 108 + (np.arange(243) % 27)
+    out[:, 26:] = (b + np.arange(2)) % 256
+    return out
+
+
+def oracle_scales(fmt: int, blocks: np.ndarray) -> np.ndarray:
+    out = np.zeros((blocks.shape[0], 16), np.int32)
+    for i, blk in enumerate(blocks):
+        if fmt == Q4_K:
+            _, _, sc, mn, _ = kqref.decode_q4k(blk)
+            out[i, :8], out[i, 8:] = sc, mn
+        else:
+            _, sc, _ = kqref.decode_q6k(blk)
+            out[i] = sc
+    return out
+
+
+# ------------------------------------------------------------ 1. kq_debug_unpack
+
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ))
+def test_debug_unpack_matches_codec(kq, fmt):
+    blocks = np.concatenate([exhaustive_blocks(fmt), fuzz_blocks(fmt, 10007, 900 + fmt)])
+    B = blocks.shape[0]
+    say(f"debug_unpack fmt={fmt} blocks={B}")
+    q, scales = kq.debug_unpack(fmt, dev(blocks.reshape(-1)), B)
+    torch.cuda.synchronize()
+    want_q = kqref.int_operands(fmt, blocks.reshape(1, -1), B * QK[fmt]).reshape(B, QK[fmt])
+    got_q = q.cpu().numpy().astype(np.int32)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, f"{len(bad)} values differ, first at block/value {tuple(bad[0])}"
+    if fmt != TQ:
+        got_s = scales.cpu().numpy()
+        want_s = oracle_scales(fmt, blocks)
+        bad = np.argwhere(got_s != want_s)
+        assert bad.size == 0, f"{len(bad)} scale fields differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ))
+@pytest.mark.parametrize("B", [1, 2, 31, 33, 65])
+def test_debug_unpack_ragged_counts(kq, fmt, B):
+    """Counts that leave workgroups partly empty; bytes past the last block are
+    never written (canaries after q and scales stay intact)."""
+    blocks = fuzz_blocks(fmt, B, 77 + B)
+    q = torch.full((B + 4, QK[fmt]), 99, dtype=torch.int8, device=DEV)
+    sc = torch.full((B + 4, 16), -7, dtype=torch.int32, device=DEV)
+    kq.kq_debug_unpack(fmt, dev(blocks.reshape(-1)), B, q, sc)
+    torch.cuda.synchronize()
+    want = kqref.int_operands(fmt, blocks.reshape(1, -1), B * QK[fmt]).reshape(B, QK[fmt])
+    qn = q.cpu().numpy()
+    assert np.array_equal(qn[:B].astype(np.int32), want)
+    assert np.all(qn[B:] == 99)
+    scn = sc.cpu().numpy()
+    if fmt != TQ:
+        assert np.array_equal(scn[:B], oracle_scales(fmt, blocks))
+    assert np.all(scn[B:] == -7) and (fmt != TQ or np.all(scn == -7))
+
+
+# ------------------------------------------------------------ 2. identity activations
+
+def unit_act(kq, fmt, qs):
+    """Activation buffer with unit scales (and, for Q8_K, the sums and min
+    operands that go with qs), built on the host."""
+    M, K = qs.shape
+    act = kq.kq_act_fmt_for(fmt)
+    bs = 256 if act == kq.KQ_ACT_Q8_K else 128
+    buf = np.zeros(kq.kq_act_bytes(act, M, K), np.uint8)
+    buf[:M * K] = qs.view(np.uint8).reshape(-1)
+    od = kq.kq_act_section_offset(act, kq.KQ_SEC_D, M, K)
+    buf[od:od + M * (K // bs) * 4] = np.ones(M * (K // bs), np.float32).view(np.uint8)
+    if act == kq.KQ_ACT_Q8_K:
+        ob = kq.kq_act_section_offset(act, kq.KQ_SEC_BSUMS, M, K)
+        bsums = qs.astype(np.int32).reshape(M, K // 16, 16).sum(-1).astype(np.int16)
+        buf[ob:ob + bsums.nbytes] = bsums.view(np.uint8).reshape(-1)
+        # alpha = 1 * (sum of 32 qs): small integers, exact in bf16 (hi), lo = 0
+        s32 = qs.astype(np.int32).reshape(M, K // 256, 8, 32).sum(-1).astype(np.float32)
+        hi = (s32.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal((hi.astype(np.uint32) << 16).view(np.float32), s32)
+        al = np.stack([hi, np.zeros_like(hi)], 0).transpose(2, 0, 1, 3)   # [S][2][M][8]
+        oa = kq.kq_act_section_offset(act, kq.KQ_SEC_ALPHA, M, K)
+        buf[oa:oa + al.nbytes] = np.ascontiguousarray(al).view(np.uint8).reshape(-1)
+    return dev(buf)
+
+
+def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
+    """Fuzzed fields with finite fp16 scales, packed as [N][K/QK] blocks."""
+    rng = np.random.default_rng(seed)
+    B = N * K // QK[fmt]
+    if fmt == Q4_K:
+        W = datagen.pack_q4k(*datagen.random_fields_q4k(rng, B))
+    elif fmt == Q6_K:
+        W = datagen.pack_q6k(*datagen.random_fields_q6k(rng, B))
+    else:
+        d, t = datagen.random_fields_tq(rng, B)
+        W = datagen.pack_tq(t, d)
+    return W.reshape(N, -1)
+
+
+def q4k_term_sizes(W: np.ndarray, N: int, K: int) -> np.ndarray:
+    """|d*sc_j*q_k| + |dmin*m_j| per weight, fp64 [N][K], from the oracle codec."""
+    out = np.zeros((N, K))
+    blocks = W.reshape(N, K // 256, 144)
+    for n in range(N):
+        for s in range(K // 256):
+            d, dm, sc, mn, q = kqref.decode_q4k(blocks[n, s])
+            j = np.arange(256) // 32
+            out[n, 256 * s:256 * (s + 1)] = np.abs(d * sc[j] * q) + np.abs(dm * mn[j])
+    return out
+
+
+# (fmt, K, variant, token rows per launch)
+IDENTITY_CASES = [
+    (Q4_K, 2048, "gemm_q4_k_matvec", 2),
+    (Q4_K, 2048, "gemm_q4_k_m64", 64),
+    (Q4_K, 2048, "gemm_q4_k_128x128", 2048),
+    (Q6_K, 2048, "gemm_q6_k_matvec", 8),
+    (Q6_K, 2048, "gemm_q6_k_128x128", 2048),
+    (TQ, 1024, "gemm_tq_matvec", 8),
+    (TQ, 1024, "gemm_tq_128x128", 1024),
+]
+
+
+@pytest.mark.parametrize("fmt,K,variant,MT", IDENTITY_CASES,
+                         ids=[c[2] for c in IDENTITY_CASES])
+def test_identity_activations_decode_every_position(kq, fmt, K, variant, MT):
+    N = 72                       # two and a bit 32-row groups: a ragged column tile
+    W = finite_weights(fmt, N, K, 300 + fmt)
+    ref = kqref.dequant_rows(fmt, W, K).T            # out[m][n] = W^[n][m]
+    Wd = dev(W)
+    out = np.empty((K, N), np.float32)
+    names = [kq.kq_variant_name(v) for v in range(kq.kq_num_variants())]
+    assert kq.kq_variant_name(kq.kq_select_variant(fmt, MT, N, K)) == variant
+    kq.kq_dispatch_reset()
+    say(f"identity {variant}: K={K} N={N}, {K // MT} launches of {MT} rows")
+    for m0 in range(0, K, MT):
+        qs = np.zeros((MT, K), np.int8)
+        qs[np.arange(MT), m0 + np.arange(MT)] = 1
+        o = torch.full((MT, N), float("nan"), dtype=torch.float32, device=DEV)
+        kq.kq_gemm(fmt, Wd, unit_act(kq, fmt, qs), MT, N, K, o)
+        out[m0:m0 + MT] = o.cpu().numpy()
+    assert kq.kq_dispatch_count(names.index(variant)) == K // MT
+    assert np.all(np.isfinite(out))
+    if fmt == Q4_K:
+        # main term exact (an fp16 d times an integer below 2^10); the min term
+        # -dmin*m_j is carried as bf16 hi + lo (at least 16 significant bits)
+        bound = 2.0 ** -15 * q4k_term_sizes(W, N, K).T + 1e-30
+        err = np.abs(out.astype(np.float64) - ref)
+        worst = np.unravel_index(np.argmax(err / bound), err.shape)
+        assert np.all(err <= bound), f"{variant}: err/bound {(err / bound).max():.3g} at k,n={worst}"
+    else:
+        bad = np.argwhere(out != ref.astype(np.float32))
+        assert bad.size == 0, f"{variant}: {len(bad)} values differ, first at k,n={tuple(bad[0])}"
