@@ -410,6 +410,54 @@ def test_zero_and_negated_activations(kq, fmt):
     assert np.all(zero == 0)
 
 
+# ------------------------------------------------- the gate is not vacuous
+
+# (fmt, field, byte offset inside the block, xor mask): one stored field of
+# one block changed in the copy of the weights the GPU gets
+MUTATIONS = [
+    (Q4_K, "nibble", 16 + 40, 0x08),            # bit 3 of a 4-bit quant
+    (Q4_K, "scale", 4 + 2, 0x02),               # bit 5 of the 6-bit scale field 2
+    (Q4_K, "min", 4 + 8, 0x40),                 # bit 4 of the 6-bit min field 3
+    (Q6_K, "low bits", 10, 0x08),               # bit 3 of a quant's low nibble
+    (Q6_K, "high bits", 128 + 5, 0x02),         # the high bit of a quant's top pair
+    (Q6_K, "scale", 192 + 3, 0x40),             # bit 6 of an int8 scale
+    (TQ, "trit", 7, None),                      # one base-3 digit of byte 7
+]
+
+
+@pytest.mark.parametrize("fmt,field,off,mask", MUTATIONS,
+                         ids=[f"{f}-{w}" for f, w, _, _ in MUTATIONS])
+def test_gate_fails_on_a_flipped_field(kq, fmt, field, off, mask):
+    """One field flipped in the GPU's copy of the weights must fail the
+    comparison with the oracle run on the original, in exactly the output
+    column of the changed weight row."""
+    say(f"mutation fmt={fmt} {field}")
+    M, N = 64, 96
+    K = 384 if fmt == TQ else 512
+    W = datagen.make_weights(fmt, N, K, 71)
+    x = datagen.draw_activations(M, K, 72)
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    qs, d, _ = kqref.quantize_act(act_fmt, x)
+    ref, tol = kqref.gemm(fmt, W, qs, d, K)
+    a_q8 = run_quant(kq, act_fmt, x)
+    assert_within_tol(run_gemm(kq, fmt, W, a_q8, M, N, K), ref, tol, "unmutated")
+
+    n, bb = 37, {Q4_K: 144, Q6_K: 210, TQ: 28}[fmt]
+    Wm = W.copy()
+    i = bb + off                                   # second block of row n
+    if mask is None:                               # next base-3 value of the lowest digit
+        v = int(Wm[n, i])
+        Wm[n, i] = v + 1 if v % 3 != 2 else v - 2
+    else:
+        Wm[n, i] ^= mask
+    changed = np.argwhere(kqref.dequant_rows(fmt, Wm, K) != kqref.dequant_rows(fmt, W, K))
+    assert changed.size and set(changed[:, 0]) == {n}, "the mutation must change row n only"
+    out = run_gemm(kq, fmt, Wm, a_q8, M, N, K)
+    bad = np.abs(out.astype(np.float64) - ref) > tol
+    assert bad.any(), f"{field} flip not caught by the gate"
+    assert set(np.nonzero(bad)[1]) == {n}
+
+
 # ------------------------------------------------- out-of-bounds canaries
 
 @pytest.mark.parametrize("fmt", FMTS)
