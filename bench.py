@@ -15,8 +15,10 @@ against the 5.0 POP/s dense int8 MFMA peak (for M < 256 the kernel is bound by
 streaming the weights: algorithmic bytes per launch over HBM's 8 TB/s).  The
 launch time comes from HIP events recorded on the stream the kernel is
 launched on, around the same K launches issued back to back right after the
-timed steps; `gemm.mean_us` is the per-step event pair around each launch,
-which also holds the dispatch gap after the quantize kernel.
+timed steps; `gemm.mean_us` and `quantize.mean_us` come from event pairs
+around each launch in a separate, untimed pass of the same steps (they include
+the dispatch gap after the preceding kernel).  The timed steps themselves carry
+no events.
 `traffic` is the HBM traffic per launch measured with rocprofv3 counters for
 the current kernel source (profiles/*_traffic.md), or null when those counters
 were taken on a different kernel source.  `calibration` holds the device's
@@ -92,8 +94,8 @@ def measured_traffic(workload: str, fmt_name: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ffn_up_q4k_2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calib", action="store_true",
@@ -154,14 +156,22 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps: nothing but the two launches per step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    # per-kernel breakdown, in a separate pass of the same steps with events
+    # around each launch (the event packets cost a few microseconds per step,
+    # so they stay out of the timed steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
 
     # The roofline's launch duration: the same GEMM launches back to back on
     # the same stream (no quantize in between), so the events bracket kernel
