@@ -33,10 +33,10 @@ import dataclasses
 
 import numpy as np
 
-Q4_K, Q6_K, TQ = 1, 2, 3
-FMT_NAMES = {Q4_K: "q4_k", Q6_K: "q6_k", TQ: "tq"}
-QK = {Q4_K: 256, Q6_K: 256, TQ: 128}            # weights per block
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, TQ: 28}     # bytes per block
+Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
+FMT_NAMES = {Q4_K: "q4_k", Q6_K: "q6_k", TQ: "tq", TQ2: "tq2"}
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}             # weights per block
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, TQ: 28, TQ2: 34}      # bytes per block
 
 
 @dataclasses.dataclass(frozen=True)
@@ -76,6 +76,9 @@ WORKLOADS = {
     "tern_5120_1": Workload("tern_5120_1", TQ, 1, 17408, 5120, 1005,
                             "plain", "ternary x Q8_128, one token (decode; first token row "
                             "of the 2048-token draw), 17408x5120"),
+    "tern2_5120_2048": Workload("tern2_5120_2048", TQ2, 2048, 17408, 5120, 1005,
+                                "plain", "ternary at two bits per weight x Q8_128, 2048 "
+                                "tokens, 17408x5120 (the same trits as tern_5120_2048)"),
 }
 
 
@@ -188,6 +191,20 @@ def pack_tq(t: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out
 
 
+def pack_tq2(t: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Pack ternary blocks at two bits per weight: t int [B][128] in {-1,0,1},
+    d fp16 [B] -> uint8 [B][34]; byte j holds the codes t+1 of weights j,
+    j+32, j+64, j+96 from its low bits up."""
+    t = np.asarray(t).astype(np.int64)
+    B = t.shape[0]
+    assert t.shape[1] == 128 and t.min(initial=0) >= -1 and t.max(initial=0) <= 1
+    c = (t + 1).reshape(B, 4, 32)
+    out = np.zeros((B, 34), dtype=np.uint8)
+    out[:, 0:32] = (c[:, 0] | (c[:, 1] << 2) | (c[:, 2] << 4) | (c[:, 3] << 6)).astype(np.uint8)
+    out[:, 32:34] = np.asarray(d, dtype=np.float16).reshape(B, 1).view(np.uint8)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Weight encoders: fp32 weights -> block bytes (fp64 arithmetic)
 # ----------------------------------------------------------------------------
@@ -257,6 +274,14 @@ def encode_tq(t: np.ndarray, d: np.ndarray) -> np.ndarray:
     return pack_tq(t.reshape(B, 128), d.reshape(B)).reshape(N, (K // 128) * 28)
 
 
+def encode_tq2(t: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Two-bit ternary encoder. t int8 [N][K], d fp16 [N][K/128] -> uint8 [N][K/128*34]."""
+    N, K = t.shape
+    assert K % 128 == 0
+    B = N * (K // 128)
+    return pack_tq2(t.reshape(B, 128), d.reshape(B)).reshape(N, (K // 128) * 34)
+
+
 # ----------------------------------------------------------------------------
 # Whole workloads
 # ----------------------------------------------------------------------------
@@ -270,6 +295,9 @@ def make_weights(fmt: int, N: int, K: int, seed: int, dist: str = "plain") -> np
     if fmt == TQ:
         t, d = draw_ternary(N, K, seed)
         return encode_tq(t, d)
+    if fmt == TQ2:
+        t, d = draw_ternary(N, K, seed)
+        return encode_tq2(t, d)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -312,6 +340,12 @@ def random_fields_q6k(rng: np.random.Generator, B: int):
 
 
 def random_fields_tq(rng: np.random.Generator, B: int):
+    d = rng.uniform(-2.0, 2.0, size=B).astype(np.float16)
+    t = rng.integers(-1, 2, size=(B, 128))
+    return d, t
+
+
+def random_fields_tq2(rng: np.random.Generator, B: int):
     d = rng.uniform(-2.0, 2.0, size=B).astype(np.float16)
     t = rng.integers(-1, 2, size=(B, 128))
     return d, t

@@ -24,8 +24,9 @@
  *
  * Block layouts are this project's own (the pages fix only block sizes:
  * 292 bytes per 256 activations for the Q8_K block in the vllm.cpp PR, a
- * 28-byte block per 128 ternary weights in the llama.cpp PR).  The decoders
- * below state each layout in full.
+ * 28-byte block per 128 ternary weights in the llama.cpp PR, which also
+ * names PQ2_0, the same trits at two bits each).  The decoders below state
+ * each layout in full.
  *
  * Every routine is written for clarity: bit-by-bit field extraction, plain
  * loops, no blocking.  Build: gcc -O2 -fopenmp -ffp-contract=off (no
@@ -39,6 +40,7 @@
 #define KQREF_Q4_K 1
 #define KQREF_Q6_K 2
 #define KQREF_TQ 3
+#define KQREF_TQ2 4
 #define KQREF_ACT_Q8_K 1
 #define KQREF_ACT_Q8_128 2
 
@@ -137,14 +139,31 @@ void kqref_decode_tq(const uint8_t *b, double *d, int32_t t[128])
     *d = kqref_f16_to_f64(rd16(b + 26));
 }
 
-static int qk_of(int fmt) { return fmt == KQREF_TQ ? 128 : 256; }
+/* Ternary block at two bits per weight (the PQ2_0 packing the llama.cpp PR
+ * names: the same trits as above, two bits each), 34 bytes, 128 weights.
+ *   [0,32): weight k has code c_k = t_k + 1 in bits 2*(k/32) .. 2*(k/32)+1
+ *   of byte k % 32, i.e. byte j holds weights j, j+32, j+64, j+96 from its
+ *   low bits up.  Code 3 is not a valid trit.  [32,34): fp16 d.
+ *   W^_k = d * t_k.                                                        */
+void kqref_decode_tq2(const uint8_t *b, double *d, int32_t t[128])
+{
+    for (int k = 0; k < 128; k++) {
+        int c = (b[k % 32] >> (2 * (k / 32))) & 3;
+        t[k] = c - 1;
+    }
+    *d = kqref_f16_to_f64(rd16(b + 32));
+}
+
+static int ternary(int fmt) { return fmt == KQREF_TQ || fmt == KQREF_TQ2; }
+static int qk_of(int fmt) { return ternary(fmt) ? 128 : 256; }
 static int bb_of(int fmt)
 {
-    return fmt == KQREF_Q4_K ? 144 : fmt == KQREF_Q6_K ? 210 : fmt == KQREF_TQ ? 28 : 0;
+    return fmt == KQREF_Q4_K ? 144 : fmt == KQREF_Q6_K ? 210 : fmt == KQREF_TQ ? 28
+         : fmt == KQREF_TQ2 ? 34 : 0;
 }
 static int sub_of(int fmt)
 {
-    return fmt == KQREF_Q4_K ? 32 : fmt == KQREF_Q6_K ? 16 : fmt == KQREF_TQ ? 128 : 0;
+    return fmt == KQREF_Q4_K ? 32 : fmt == KQREF_Q6_K ? 16 : ternary(fmt) ? 128 : 0;
 }
 
 /* Dequantize one block to fp64 (QK values), plus the integer operand that the
@@ -169,7 +188,10 @@ static void dequant_block(int fmt, const uint8_t *b, double *w, int32_t *qint)
             if (qint) qint[k] = q[k] - 32;
         }
     } else {
-        kqref_decode_tq(b, &d, q);
+        if (fmt == KQREF_TQ2)
+            kqref_decode_tq2(b, &d, q);
+        else
+            kqref_decode_tq(b, &d, q);
         for (int k = 0; k < 128; k++) {
             if (w) w[k] = d * q[k];
             if (qint) qint[k] = q[k];
@@ -264,7 +286,7 @@ int kqref_gemm_rows(int fmt, const uint8_t *W, const int8_t *qs, const float *d_
                     float *out, double *tol)
 {
     int qk = qk_of(fmt), bb = bb_of(fmt);
-    int abs_ = fmt == KQREF_TQ ? 128 : 256;       /* activation block size */
+    int abs_ = ternary(fmt) ? 128 : 256;          /* activation block size */
     if (!bb || K % qk) return -1;
     int64_t nb = K / qk, na = K / abs_;
     int64_t ncols = rows ? n_rows : N;

@@ -16,12 +16,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kqref.c")
 LIB = os.path.join(HERE, "libkqref.so")
 
-Q4_K, Q6_K, TQ = 1, 2, 3
+Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
 ACT_Q8_K, ACT_Q8_128 = 1, 2
-QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, TQ: 28}
-SUB = {Q4_K: 32, Q6_K: 16, TQ: 128}
-ACT_FOR = {Q4_K: ACT_Q8_K, Q6_K: ACT_Q8_K, TQ: ACT_Q8_128}
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, TQ: 28, TQ2: 34}
+SUB = {Q4_K: 32, Q6_K: 16, TQ: 128, TQ2: 128}
+ACT_FOR = {Q4_K: ACT_Q8_K, Q6_K: ACT_Q8_K, TQ: ACT_Q8_128, TQ2: ACT_Q8_128}
 ACT_BS = {ACT_Q8_K: 256, ACT_Q8_128: 128}
 
 CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-Wall"]
@@ -75,6 +75,7 @@ def _bind(L):
     L.kqref_decode_q4k.argtypes = [P, P, P, P, P, P]
     L.kqref_decode_q6k.argtypes = [P, P, P, P]
     L.kqref_decode_tq.argtypes = [P, P, P]
+    L.kqref_decode_tq2.argtypes = [P, P, P]
     L.kqref_dequant_rows.argtypes = [ctypes.c_int, P, I64, I64, P]
     L.kqref_int_operands.argtypes = [ctypes.c_int, P, I64, I64, P]
     L.kqref_quantize_act.argtypes = [ctypes.c_int, P, I64, I64, P, P, P]
@@ -111,6 +112,13 @@ def decode_tq(block: np.ndarray):
     b = np.ascontiguousarray(block, dtype=np.uint8)
     d = np.zeros(1, np.float64); t = np.zeros(128, np.int32)
     lib().kqref_decode_tq(_p(b), _p(d), _p(t))
+    return float(d[0]), t
+
+
+def decode_tq2(block: np.ndarray):
+    b = np.ascontiguousarray(block, dtype=np.uint8)
+    d = np.zeros(1, np.float64); t = np.zeros(128, np.int32)
+    lib().kqref_decode_tq2(_p(b), _p(d), _p(t))
     return float(d[0]), t
 
 

@@ -16,6 +16,7 @@ void kqref_decode_q4k(const uint8_t *b, double *d, double *dmin, int32_t sc[8], 
                       int32_t q[256]);
 void kqref_decode_q6k(const uint8_t *b, double *d, int32_t sc[16], int32_t q[256]);
 void kqref_decode_tq(const uint8_t *b, double *d, int32_t t[128]);
+void kqref_decode_tq2(const uint8_t *b, double *d, int32_t t[128]);
 int kqref_dequant_rows(int fmt, const uint8_t *W, int64_t N, int64_t K, double *out);
 int kqref_int_operands(int fmt, const uint8_t *W, int64_t N, int64_t K, int32_t *out);
 int kqref_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, int8_t *qs, float *d,
@@ -34,8 +35,9 @@ static uint32_t rnd(void) {
     return (uint32_t)(rs >> 16);
 }
 
-static const int QK[4] = {0, 256, 256, 128}, BB[4] = {0, 144, 210, 28}, SUB[4] = {0, 32, 16, 128};
-static const int ACT[4] = {0, 1, 1, 2}, ABS_[4] = {0, 256, 256, 128};
+static const int QK[5] = {0, 256, 256, 128, 128}, BB[5] = {0, 144, 210, 28, 34};
+static const int SUB[5] = {0, 32, 16, 128, 128};
+static const int ACT[5] = {0, 1, 1, 2, 2}, ABS_[5] = {0, 256, 256, 128, 128};
 
 static int failures = 0;
 #define EXPECT(c)                                                   \
@@ -61,6 +63,13 @@ static void fill_blocks(int fmt, uint8_t *W, int64_t nblocks) {
             memcpy(b + 2, &d, 2);
         } else if (fmt == 2) {
             memcpy(b + 208, &d, 2);
+        } else if (fmt == 4) {
+            for (int j = 0; j < 32; j++) {
+                uint32_t v = 0;
+                for (int p = 0; p < 4; p++) v |= (rnd() % 3) << (2 * p);
+                b[j] = (uint8_t)v;
+            }
+            memcpy(b + 32, &d, 2);
         } else {
             for (int j = 0; j < 25; j++) b[j] = (uint8_t)(rnd() % 243);
             b[25] = (uint8_t)(108 + rnd() % 27);
@@ -94,6 +103,10 @@ int main(void) {
         kqref_decode_q6k(b6, &d, sc, q);
         for (int k = 0; k < 256; k++) EXPECT(q[k] >= 0 && q[k] <= 63);
         kqref_decode_tq(bt, &d, q);
+        uint8_t b2[34];
+        for (int j = 0; j < 34; j++) b2[j] = (uint8_t)rnd();
+        kqref_decode_tq2(b2, &d, q);
+        for (int k = 0; k < 128; k++) EXPECT(q[k] >= -1 && q[k] <= 2);
     }
     for (uint32_t h = 0; h < 65536; h++) {
         double v = kqref_f16_to_f64((uint16_t)h);
@@ -102,7 +115,7 @@ int main(void) {
 
     /* every entry point on ragged shapes; exact-size buffers */
     static const int64_t Ms[] = {1, 3, 33}, Ns[] = {1, 2, 7};
-    for (int fmt = 1; fmt <= 3; fmt++) {
+    for (int fmt = 1; fmt <= 4; fmt++) {
         for (int kk = 1; kk <= 3; kk++) {
             const int64_t K = kk * QK[fmt];
             for (int mi = 0; mi < 3; mi++) {

@@ -30,7 +30,7 @@ import numpy as np
 import datagen
 from oracle import kqref
 
-Q4_K, Q6_K, TQ = kqref.Q4_K, kqref.Q6_K, kqref.TQ
+Q4_K, Q6_K, TQ, TQ2 = kqref.Q4_K, kqref.Q6_K, kqref.TQ, kqref.TQ2
 ACT_Q8_K, ACT_Q8_128 = kqref.ACT_Q8_K, kqref.ACT_Q8_128
 
 
@@ -79,6 +79,15 @@ def tq_by_hand(d_bits: int, t) -> np.ndarray:
     for i in range(26):
         b[i] = sum(e[5 * i + p] * 3 ** p for p in range(5))
     b[26:28] = d_bits.to_bytes(2, "little")
+    return np.frombuffer(bytes(b), dtype=np.uint8).copy()
+
+
+def tq2_by_hand(d_bits: int, t) -> np.ndarray:
+    # byte j: codes t+1 of weights j, j+32, j+64, j+96, from the low bits up
+    b = bytearray(34)
+    for j in range(32):
+        b[j] = sum((int(t[j + 32 * p]) + 1) << (2 * p) for p in range(4))
+    b[32:34] = d_bits.to_bytes(2, "little")
     return np.frombuffer(bytes(b), dtype=np.uint8).copy()
 
 
@@ -215,6 +224,53 @@ def check_tq_block():
         assert np.array_equal(w, d * t.astype(np.float64))
 
 
+def check_tq2_codes():
+    # every code at every position, the other weights at code 1 (zero)
+    one = f16_bits(1.0)
+    for k in range(128):
+        for c in range(3):
+            t = [0] * 128
+            t[k] = c - 1
+            blk = tq2_by_hand(one, t)
+            assert (int(blk[k % 32]) >> (2 * (k // 32))) & 3 == c
+            d, dt = kqref.decode_tq2(blk)
+            assert d == 1.0
+            assert list(dt) == t, (k, c)
+
+
+def check_tq2_block():
+    rng = np.random.default_rng(8)
+    for _ in range(50):
+        t = rng.integers(-1, 2, size=128)
+        dval = float(rng.uniform(-0.05, 0.05))
+        blk = tq2_by_hand(f16_bits(dval), t)
+        d, dt = kqref.decode_tq2(blk)
+        assert d == float(np.float16(dval))
+        assert np.array_equal(dt, t)
+        w = kqref.dequant_rows(TQ2, blk[None], 128)[0]
+        assert np.array_equal(w, d * t.astype(np.float64))
+
+
+def check_tq2_same_trits_as_tq():
+    # the two packings of the same trits and scales are the same weights:
+    # dequantized values, products and integer sub-sums all agree exactly
+    rng = np.random.default_rng(9)
+    N, K, M = 5, 640, 4
+    t = rng.integers(-1, 2, size=(N, K // 128, 128))
+    d = rng.uniform(-0.1, 0.1, size=(N, K // 128))
+    W3 = np.stack([np.concatenate([tq_by_hand(f16_bits(float(d[n, s])), t[n, s]) for s in range(K // 128)])
+                   for n in range(N)])
+    W4 = np.stack([np.concatenate([tq2_by_hand(f16_bits(float(d[n, s])), t[n, s]) for s in range(K // 128)])
+                   for n in range(N)])
+    assert W4.shape == (N, (K // 128) * 34)
+    assert np.array_equal(kqref.dequant_rows(TQ, W3, K), kqref.dequant_rows(TQ2, W4, K))
+    qs, d_a = _random_acts(rng, M, K, 128)
+    o3, t3 = kqref.gemm(TQ, W3, qs, d_a, K)
+    o4, t4 = kqref.gemm(TQ2, W4, qs, d_a, K)
+    assert np.array_equal(o3, o4) and np.array_equal(t3, t4)
+    assert np.array_equal(kqref.subsums(TQ, W3, qs, K), kqref.subsums(TQ2, W4, qs, K))
+
+
 # ---------------------------------------------------------------------------
 # Q8 activation rule
 # ---------------------------------------------------------------------------
@@ -305,15 +361,16 @@ def _fields_to_blocks(fmt, fields):
         return np.concatenate([q6k_by_hand(f16_bits(float(d[b])), sc[b], q[b])
                                for b in range(len(d))])
     d, t = fields
-    return np.concatenate([tq_by_hand(f16_bits(float(d[b])), t[b]) for b in range(len(d))])
+    pack = tq2_by_hand if fmt == TQ2 else tq_by_hand
+    return np.concatenate([pack(f16_bits(float(d[b])), t[b]) for b in range(len(d))])
 
 
 def _exact_factored(fmt, fields_rows, qs, d_a):
     """Exact value of each output via the factored form, and exact sub-sums."""
     M, K = qs.shape
     N = len(fields_rows)
-    Q = {Q4_K: 256, Q6_K: 256, TQ: 128}[fmt]
-    sub = {Q4_K: 32, Q6_K: 16, TQ: 128}[fmt]
+    Q = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}[fmt]
+    sub = {Q4_K: 32, Q6_K: 16, TQ: 128, TQ2: 128}[fmt]
     exact = [[Fraction(0)] * N for _ in range(M)]
     mag = [[Fraction(0)] * N for _ in range(M)]
     S = np.zeros((M, N, K // sub), np.int64)
@@ -354,7 +411,7 @@ def _exact_factored(fmt, fields_rows, qs, d_a):
 
 
 def _tiny_case(fmt, rng, M, N, K):
-    Q = {Q4_K: 256, Q6_K: 256, TQ: 128}[fmt]
+    Q = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}[fmt]
     nb = K // Q
     rows = []
     for _ in range(N):
@@ -366,13 +423,13 @@ def _tiny_case(fmt, rng, M, N, K):
             d, t = datagen.random_fields_tq(rng, nb)
             rows.append((d, t))
     W = np.stack([_fields_to_blocks(fmt, f) for f in rows])
-    qs, d_a = _random_acts(rng, M, K, 128 if fmt == TQ else 256)
+    qs, d_a = _random_acts(rng, M, K, 128 if fmt in (TQ, TQ2) else 256)
     return rows, W, qs, d_a
 
 
 def check_bruteforce_exact():
     rng = np.random.default_rng(2024)
-    for fmt, Ks in ((Q4_K, (256, 512)), (Q6_K, (256, 512)), (TQ, (128, 384))):
+    for fmt, Ks in ((Q4_K, (256, 512)), (Q6_K, (256, 512)), (TQ, (128, 384)), (TQ2, (128, 384))):
         for K in Ks:
             M, N = 3, 4
             rows, W, qs, d_a = _tiny_case(fmt, rng, M, N, K)
@@ -418,6 +475,11 @@ def check_integer_special_case():
     outT, _ = kqref.gemm(TQ, WT, qs, np.ones((M, K // 128), np.float32), K)
     wantT = qs.astype(np.int64) @ tt.reshape(N, K).astype(np.int64).T
     assert np.array_equal(outT, wantT.astype(np.float32))
+    # ternary at two bits per weight
+    W2 = np.stack([np.concatenate([tq2_by_hand(f16_bits(1.0), tt[n, s]) for s in range(4)])
+                   for n in range(N)])
+    out2, _ = kqref.gemm(TQ2, W2, qs, np.ones((M, K // 128), np.float32), K)
+    assert np.array_equal(out2, wantT.astype(np.float32))
 
 
 def check_onehot_scales():
@@ -541,6 +603,10 @@ def check_packers_agree():
     at = datagen.pack_tq(tt, dt)
     bt = np.stack([tq_by_hand(f16_bits(float(dt[i])), tt[i]) for i in range(6)])
     assert np.array_equal(at, bt)
+    d2, t2 = datagen.random_fields_tq2(rng, 6)
+    a2 = datagen.pack_tq2(t2, d2)
+    b2 = np.stack([tq2_by_hand(f16_bits(float(d2[i])), t2[i]) for i in range(6)])
+    assert np.array_equal(a2, b2)
 
 
 ALL_CHECKS = [
@@ -552,6 +618,9 @@ ALL_CHECKS = [
     check_q6k_positions,
     check_tq_bytes,
     check_tq_block,
+    check_tq2_codes,
+    check_tq2_block,
+    check_tq2_same_trits_as_tq,
     check_q8_ties,
     check_q8_zero_and_tiny,
     check_q8_properties,

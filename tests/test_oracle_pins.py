@@ -77,8 +77,15 @@ MUTANTS = [
      "A[m * K + k] = (double)d_a[m * na] * (double)qs[m * K + k];"),
     ("gemm activation reversed along K", "double p = w[k] * a[k];",
      "double p = w[k] * a[K - 1 - k];"),
-    ("ternary with 256-wide activation scales", "int abs_ = fmt == KQREF_TQ ? 128 : 256;",
+    ("ternary with 256-wide activation scales", "int abs_ = ternary(fmt) ? 128 : 256;",
      "int abs_ = 256;"),
+    ("tq2 code planes in reverse", "int c = (b[k % 32] >> (2 * (k / 32))) & 3;",
+     "int c = (b[k % 32] >> (6 - 2 * (k / 32))) & 3;"),
+    ("tq2 codes of consecutive weights in one byte", "int c = (b[k % 32] >> (2 * (k / 32))) & 3;",
+     "int c = (b[k / 4] >> (2 * (k % 4))) & 3;"),
+    ("tq2 code not centred", "        t[k] = c - 1;\n", "        t[k] = c - (k != 5);\n"),
+    ("tq2 scale read from the code bytes", "*d = kqref_f16_to_f64(rd16(b + 32));",
+     "*d = kqref_f16_to_f64(rd16(b + 30));"),
     ("tolerance without abs", "mag += fabs(p);", "mag += p;"),
     ("subsums activation index restarts per sub-block",
      "acc += (int64_t)qi[k] * (int64_t)qs[m * K + k];",
