@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkq.so")
 
-KQ_Q4_K, KQ_Q6_K, KQ_TQ = 1, 2, 3
+KQ_Q4_K, KQ_Q6_K, KQ_TQ, KQ_TQ2 = 1, 2, 3, 4
 KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
 KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
@@ -221,8 +221,9 @@ def debug_unpack(fmt, W, nblocks, stream=None):
     """Decode nblocks weight blocks (uint8 device tensor) with the tile kernel's
     loaders: (q int8 [nblocks][QK], scales int32 [nblocks][16] or None)."""
     import torch
-    qk = 128 if fmt == KQ_TQ else 256
+    ternary = fmt in (KQ_TQ, KQ_TQ2)
+    qk = 128 if ternary else 256
     q = torch.empty((nblocks, qk), dtype=torch.int8, device=W.device)
-    scales = None if fmt == KQ_TQ else torch.empty((nblocks, 16), dtype=torch.int32, device=W.device)
+    scales = None if ternary else torch.empty((nblocks, 16), dtype=torch.int32, device=W.device)
     kq_debug_unpack(fmt, W, nblocks, q, scales, stream)
     return q, scales

@@ -28,13 +28,15 @@ enum Variant {
     V_SUBSUMS_Q4K,
     V_SUBSUMS_Q6K,
     V_SUBSUMS_TQ,
+    V_GEMM_TQ2_128x128,
+    V_SUBSUMS_TQ2,
     V_COUNT
 };
 
 const char *const kVariantNames[V_COUNT] = {
     "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
     "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
-    "subsums_tq",
+    "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -43,10 +45,10 @@ constexpr int64_t kMaxDim = INT32_MAX;  // kernels index rows and columns with i
 constexpr int64_t kMaxBytes = (int64_t)1 << 46;
 
 int qk_of(int fmt) {
-    return fmt == KQ_Q4_K || fmt == KQ_Q6_K ? 256 : fmt == KQ_TQ ? 128 : 0;
+    return fmt == KQ_Q4_K || fmt == KQ_Q6_K ? 256 : fmt == KQ_TQ || fmt == KQ_TQ2 ? 128 : 0;
 }
 int bb_of(int fmt) {
-    return fmt == KQ_Q4_K ? 144 : fmt == KQ_Q6_K ? 210 : fmt == KQ_TQ ? 28 : 0;
+    return fmt == KQ_Q4_K ? 144 : fmt == KQ_Q6_K ? 210 : fmt == KQ_TQ ? 28 : fmt == KQ_TQ2 ? 34 : 0;
 }
 int bs_of(int act_fmt) {
     return act_fmt == KQ_ACT_Q8_K ? 256 : act_fmt == KQ_ACT_Q8_128 ? 128 : 0;
@@ -111,6 +113,7 @@ int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
             default: return V_GEMM_Q4K_128x128;
         }
     }
+    if (fmt == KQ_TQ2) return V_GEMM_TQ2_128x128;
     if (kq::gemv_choice(fmt, (int)M, (int)N, (int)K))
         return fmt == KQ_Q6_K ? V_GEMM_Q6K_MATVEC : V_GEMM_TQ_MATVEC;
     return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
@@ -145,7 +148,7 @@ int64_t kq_act_section_offset(int act_fmt, int section, int64_t M, int64_t K) {
 
 int kq_act_fmt_for(int fmt) {
     if (fmt == KQ_Q4_K || fmt == KQ_Q6_K) return KQ_ACT_Q8_K;
-    if (fmt == KQ_TQ) return KQ_ACT_Q8_128;
+    if (fmt == KQ_TQ || fmt == KQ_TQ2) return KQ_ACT_Q8_128;
     return KQ_ERR_FMT;
 }
 
@@ -199,7 +202,8 @@ int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t
     hipError_t e = kq::launch_subsums(fmt, W, reinterpret_cast<const int8_t *>(base), sums,
                                       (int)M, (int)N, (int)K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
-    g_count[fmt == KQ_Q4_K ? V_SUBSUMS_Q4K : fmt == KQ_Q6_K ? V_SUBSUMS_Q6K : V_SUBSUMS_TQ]
+    g_count[fmt == KQ_Q4_K ? V_SUBSUMS_Q4K : fmt == KQ_Q6_K ? V_SUBSUMS_Q6K
+            : fmt == KQ_TQ ? V_SUBSUMS_TQ : V_SUBSUMS_TQ2]
         .fetch_add(1);
     return KQ_OK;
 }
@@ -209,9 +213,10 @@ int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t 
     if (!qk_of(fmt)) return KQ_ERR_FMT;
     if (nblocks < 0 || nblocks > KQ_DEBUG_UNPACK_MAX_BLOCKS) return KQ_ERR_SHAPE;
     if (nblocks == 0) return KQ_OK;
-    if (!W || !q || (fmt != KQ_TQ && !scales)) return KQ_ERR_NULL;
+    const bool ternary = fmt == KQ_TQ || fmt == KQ_TQ2;  // no scale fields
+    if (!W || !q || (!ternary && !scales)) return KQ_ERR_NULL;
     if (!aligned16(W) || !aligned16(q) || ((uintptr_t)scales & 3u)) return KQ_ERR_ALIGN;
-    return kq::launch_debug_unpack(fmt, W, nblocks, q, fmt == KQ_TQ ? nullptr : scales, stream) ==
+    return kq::launch_debug_unpack(fmt, W, nblocks, q, ternary ? nullptr : scales, stream) ==
                    hipSuccess
                ? KQ_OK
                : KQ_ERR_HIP;

@@ -1,13 +1,14 @@
 // kq_gemm.hip -- cooperative-tile block-quantized GEMM on gfx950 int8 MFMA.
 //
 // out[m][n] = sum_k W^[n][k] * A^[m][k] for Q4_K / Q6_K weights against Q8_K
-// activations and ternary weights against Q8_128 activations.
+// activations and ternary weights (base-3 at 1.6 bits per weight, or two bits
+// per weight) against Q8_128 activations.
 //
 // Launched for Q6_K and ternary weights (shapes the matrix-vector kernels of
-// kq_gemv.hip do not take); Q4_K runs on the kernels of kq_gemm_q4k.hip.  The
-// Q4_K branches below are not instantiated by launch_gemm; the two test hooks
-// (subsums_kernel, debug_unpack_kernel) use this file's loaders for all three
-// formats.
+// kq_gemv.hip do not take; two-bit ternary always); Q4_K runs on the kernels
+// of kq_gemm_q4k.hip.  The Q4_K branches below are not instantiated by
+// launch_gemm; the two test hooks (subsums_kernel, debug_unpack_kernel) use
+// this file's loaders for every format.
 //
 // Design (MI355X-first; prior art: the BigTile kernel of vllm.cpp PR 3036,
 // which reuses staged activation rows across warps, and llama.cpp's
@@ -45,7 +46,7 @@
 
 namespace kq {
 
-enum { FMT_Q4K = 1, FMT_Q6K = 2, FMT_TQ = 3 };
+enum { FMT_Q4K = 1, FMT_Q6K = 2, FMT_TQ = 3, FMT_TQ2 = 4 };
 
 template <int FMT>
 struct Fmt;
@@ -61,6 +62,12 @@ template <>
 struct Fmt<FMT_TQ> {
     static constexpr int QK = 128, BB = 28, NDIG = 1, SHIFT = 0, SUB = 128;
 };
+template <>
+struct Fmt<FMT_TQ2> {
+    static constexpr int QK = 128, BB = 34, NDIG = 1, SHIFT = 0, SUB = 128;
+};
+// formats whose scales cover 128 values (one block per 128-wide chunk half)
+constexpr bool tri(int fmt) { return fmt == FMT_TQ || fmt == FMT_TQ2; }
 
 constexpr int KC = 256;         // K values per chunk
 constexpr int PITCH = KC + 16;  // LDS row pitch in bytes (16-byte skew against bank conflicts)
@@ -100,6 +107,18 @@ template <>
 struct WRaw<FMT_TQ> {
     uint32_t w[7];
 };
+template <>
+struct WRaw<FMT_TQ2> {
+    uint32_t w[9];   // the block from its dword boundary: 8 (aligned) or 9 dwords
+    uint32_t dbits;  // fp16 d (aligned blocks; otherwise the top half of w[8])
+    uint32_t shift;  // block start mod 4 (0 or 2)
+};
+
+// Four int8 trits t = c - 1 from four two-bit codes c <= 2, one per byte
+// (adding 0x7F never carries out of a byte and flipping bit 7 gives c - 1).
+__device__ __forceinline__ uint32_t codes_to_trits(uint32_t c4) {
+    return (c4 + 0x7F7F7F7Fu) ^ 0x80808080u;
+}
 
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) {
     return *reinterpret_cast<const uint32_t *>(p);
@@ -135,6 +154,24 @@ __device__ __forceinline__ void load_w(WRaw<FMT> &r, const GemmArgs &a, int n, i
 #pragma unroll
         for (int i = 0; i < 3; ++i) r.sc[i] = i < ns ? ld_u32(base + 192 + 8 * h + 4 * i) : 0u;
         r.dbits = *reinterpret_cast<const unsigned short *>(a.W + o + 208);
+    } else if constexpr (FMT == FMT_TQ2) {
+        // one 34-byte block per part; it starts 0 or 2 bytes past a dword
+        // boundary, and no load reaches past its last byte
+        const int blkidx = 2 * c + part;
+        if (blkidx < a.nblk) {
+            const int64_t o = ((int64_t)n * a.nblk + blkidx) * 34;
+            const uint32_t sh = (uint32_t)(o & 3);
+            const uint8_t *base = a.W + (o - sh);
+            r.shift = sh;
+#pragma unroll
+            for (int i = 0; i < 9; ++i) r.w[i] = (i < 8 || sh) ? ld_u32(base + 4 * i) : 0u;
+            r.dbits = sh ? (r.w[8] >> 16) : *reinterpret_cast<const unsigned short *>(a.W + o + 32);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 9; ++i) r.w[i] = 0x55555555u;  // code 1 everywhere: zero trits
+            r.dbits = 0;
+            r.shift = 0;
+        }
     } else {
         const int blkidx = 2 * c + part;
         if (blkidx < a.nblk) {
@@ -259,6 +296,20 @@ __device__ __forceinline__ void unpack_w(const WRaw<FMT> &r, bool valid, int8_t 
             }
         }
         if (part == 0) dw[nl] = valid ? (UNIT ? 1.0f : f16_bits_to_f32(r.dbits)) : 0.0f;
+    } else if constexpr (FMT == FMT_TQ2) {
+        // two-bit ternary: this part is one 128-block; plane p of code dword i
+        // is weights 4i .. 4i+3 + 32p
+        int8_t *dst = row0 + 128 * part;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t cw = __builtin_amdgcn_alignbyte(r.w[i + 1], r.w[i], r.shift);
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl) {
+                const uint32_t v = codes_to_trits((cw >> (2 * pl)) & 0x03030303u);
+                *reinterpret_cast<uint32_t *>(dst + 32 * pl + 4 * i) = valid ? v : 0u;
+            }
+        }
+        dw[part * rows + nl] = valid ? (UNIT ? 1.0f : f16_bits_to_f32(r.dbits)) : 0.0f;
     } else {
         // ternary: 26 digit bytes + fp16 d; this part is one 128-block
         uint32_t f[26];
@@ -381,6 +432,14 @@ struct ChunkRegs<FMT_TQ> {
     float da;
     uint32_t w[2];  // 8 trit bytes
 };
+template <>
+struct ChunkRegs<FMT_TQ2> {
+    v4i act[2];
+    float da;
+    uint32_t w[3];  // 8 code bytes from their dword boundary
+    uint32_t sh;    // block start mod 4 (0 or 2)
+    uint32_t d;     // fp16 d
+};
 
 // Ternary decode table entry for byte v: its five base-3 digits minus one as
 // int8 in bytes 0..4, zero bytes 5..7.  Digit p is floor(v / 3^p) mod 3, so
@@ -400,8 +459,9 @@ template <int FMT>
 __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
-    constexpr bool Q4 = FMT == FMT_Q4K, Q6 = FMT == FMT_Q6K, TQ = FMT == FMT_TQ;
-    constexpr int CPS = TQ ? 1 : 2;  // chunks per scale block
+    constexpr bool Q4 = FMT == FMT_Q4K, Q6 = FMT == FMT_Q6K, TQ = FMT == FMT_TQ, TQ2 = FMT == FMT_TQ2;
+    constexpr bool TRI = tri(FMT);    // scales per 128 values, one block per chunk
+    constexpr int CPS = TRI ? 1 : 2;  // chunks per scale block
     constexpr int PLANE = BN * MPITCH;
 
     // one array per buffer, so the compiler sees that staging writes and
@@ -437,7 +497,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = a.M, N = a.N, K = a.K;
     const int nch = (K + KCH - 1) / KCH;                    // chunks
-    const int nsa = TQ ? a.nblk : a.nchunks;                // activation scale blocks per row
+    const int nsa = TRI ? a.nblk : a.nchunks;               // activation scale blocks per row
 
     const int lrow = lane & 31, kgrp = lane >> 5;
     const int wm = wave >> 2, wn = wave & 3;
@@ -531,10 +591,23 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
             // third dword only needed when sh == 2; otherwise re-read the second
             R.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(rs_w, base + (sh ? 4 : 0), 196 + 8 * H, 0);
             R.d = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)o, 208, 0);
-        } else {
+        } else if constexpr (TQ) {
             const v2u w2 = __builtin_amdgcn_raw_buffer_load_b64(rs_w, (int)(w_off + tq_off), wsoff, 0);
             R.w[0] = w2.x;
             R.w[1] = w2.y;
+        } else {
+            // code bytes 8wq .. 8wq+7 of the 34-byte block, from their dword
+            // boundary (the block starts 0 or 2 bytes past one; a window may
+            // run two bytes into the next block, or past the end, which reads
+            // zero)
+            const uint32_t o = w_off + (uint32_t)wsoff;
+            const uint32_t sh = o & 3u;
+            const v3u w3 = __builtin_amdgcn_raw_buffer_load_b96(rs_w, (int)(o - sh) + 8 * wq, 0, 0);
+            R.w[0] = w3.x;
+            R.w[1] = w3.y;
+            R.w[2] = w3.z;
+            R.sh = sh;
+            R.d = __builtin_amdgcn_raw_buffer_load_b16(rs_w, (int)o, 32, 0);
         }
     };
 
@@ -636,6 +709,22 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
                 *reinterpret_cast<uint2 *>(p1 + off) = make_uint2(T.vl[0], T.vl[1]);
             }
             if constexpr (S == 7) s_dw[slot * BN + w_nl] = f16_bits_to_f32(R.d);
+        } else if constexpr (TQ2) {
+            // code bytes 8wq .. 8wq+7: piece S (1..4) writes plane p = S - 1,
+            // weights 32p + 8wq .. +8; piece 5 the block scale
+            if constexpr (S >= 1 && S <= 4) {
+                constexpr int pl = S - 1;
+                uint32_t v[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t cw = __builtin_amdgcn_alignbyte(R.w[e + 1], R.w[e], R.sh);
+                    v[e] = codes_to_trits((cw >> (2 * pl)) & 0x03030303u);
+                }
+                *reinterpret_cast<uint2 *>(p0 + w_nl * MPITCH + 32 * pl + 8 * wq) = make_uint2(v[0], v[1]);
+            } else if constexpr (S == 5) {
+                float *dwp = (wq == 0) ? &s_dw[slot * BN + w_nl] : &s_dw[4 * BN + lane];
+                *dwp = f16_bits_to_f32(R.d);
+            }
         } else {
             // trit byte v -> five int8 trits from the table; byte b of this
             // thread's window fills row bytes 5*(tq_off + b) .. +5
@@ -809,7 +898,7 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
         ld_b(BP{}, Bv, 1);
         ld_a(BP{}, Av, 0, 0);
         ld_a(BP{}, Av, 0, 1);
-        if constexpr (TQ) {
+        if constexpr (TRI) {
             FoldTmp F1, F0;
             fold_load(IC<1>{}, c - 1, F1);
             __builtin_amdgcn_sched_barrier(0);
@@ -1077,7 +1166,7 @@ static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float 
     a.N = N;
     a.K = K;
     a.nchunks = (K + KC - 1) / KC;
-    a.nblk = (fmt == FMT_TQ) ? K / 128 : K / 256;
+    a.nblk = (fmt == FMT_TQ || fmt == FMT_TQ2) ? K / 128 : K / 256;
     a.tiles_m = (M + bm - 1) / bm;
     a.tiles_n = (N + bn - 1) / bn;
     return a;
@@ -1097,6 +1186,9 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
     switch (fmt) {
         case FMT_Q6K:
             hipLaunchKernelGGL(gemm_kernel<FMT_Q6K>, dim3(grid), dim3(MNT), 0, stream, a);
+            break;
+        case FMT_TQ2:
+            hipLaunchKernelGGL(gemm_kernel<FMT_TQ2>, dim3(grid), dim3(MNT), 0, stream, a);
             break;
         default:
             hipLaunchKernelGGL(gemm_kernel<FMT_TQ>, dim3(grid), dim3(MNT), 0, stream, a);
@@ -1125,19 +1217,19 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(GemmArgs a, int8_t *q,
     const int nl = threadIdx.x >> 1, part = threadIdx.x & 1;
     const int c = blockIdx.x * DBG_CHUNKS + nl;
     // block holding this thread's values
-    const int64_t b = FMT == FMT_TQ ? 2 * (int64_t)c + part : c;
+    const int64_t b = tri(FMT) ? 2 * (int64_t)c + part : c;
     const bool valid = b < a.nblk;
     WRaw<FMT> wr;
     // past the end: Q4_K/Q6_K read block 0 instead (nothing is stored); the
     // ternary loader fills blocks past nblk itself without reading
-    load_w<FMT>(wr, a, 0, part, (valid || FMT == FMT_TQ) ? c : 0);
+    load_w<FMT>(wr, a, 0, part, (valid || tri(FMT)) ? c : 0);
     unpack_w<FMT, true>(wr, valid, s_w, DBG_CHUNKS * PITCH, nl, part, s_dw, DBG_CHUNKS, nullptr, 0,
                         false);
     __syncthreads();
     if (!valid) return;
 
     const int8_t *hi = s_w + nl * PITCH + 128 * part;
-    int8_t *dst = q + (FMT == FMT_TQ ? b * 128 : b * 256 + 128 * part);
+    int8_t *dst = q + (tri(FMT) ? b * 128 : b * 256 + 128 * part);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         v4i h = *reinterpret_cast<const v4i *>(hi + 16 * i), v;
@@ -1180,7 +1272,7 @@ hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *
     GemmArgs a{};
     a.W = (const uint8_t *)W;
     a.nblk = (int)nblocks;
-    const int64_t chunks = fmt == FMT_TQ ? (nblocks + 1) / 2 : nblocks;
+    const int64_t chunks = (fmt == FMT_TQ || fmt == FMT_TQ2) ? (nblocks + 1) / 2 : nblocks;
     const unsigned grid = (unsigned)((chunks + DBG_CHUNKS - 1) / DBG_CHUNKS);
     switch (fmt) {
         case FMT_Q4K:
@@ -1188,6 +1280,9 @@ hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *
             break;
         case FMT_Q6K:
             hipLaunchKernelGGL(debug_unpack_kernel<FMT_Q6K>, dim3(grid), dim3(64), 0, stream, a, q, scales);
+            break;
+        case FMT_TQ2:
+            hipLaunchKernelGGL(debug_unpack_kernel<FMT_TQ2>, dim3(grid), dim3(64), 0, stream, a, q, scales);
             break;
         default:
             hipLaunchKernelGGL(debug_unpack_kernel<FMT_TQ>, dim3(grid), dim3(64), 0, stream, a, q, scales);
@@ -1206,6 +1301,9 @@ hipError_t launch_subsums(int fmt, const void *W, const int8_t *qs, int32_t *sum
             break;
         case FMT_Q6K:
             hipLaunchKernelGGL(subsums_kernel<FMT_Q6K>, dim3(grid), dim3(64), 0, stream, a);
+            break;
+        case FMT_TQ2:
+            hipLaunchKernelGGL(subsums_kernel<FMT_TQ2>, dim3(grid), dim3(64), 0, stream, a);
             break;
         default:
             hipLaunchKernelGGL(subsums_kernel<FMT_TQ>, dim3(grid), dim3(64), 0, stream, a);

@@ -73,7 +73,13 @@
  *     be 1, so every byte is <= 242); [26,28) fp16 d.  W^_k = d * t_k.
  *     Bytes 24..27 read as a little-endian word are qh0 | qh1<<8 | d<<16,
  *     the word layout of llama.cpp PR 214's loader.
- *   Q4_K and Q6_K weights take Q8_K activations; ternary takes Q8_128.
+ *   KQ_TQ2 (ternary at two bits per weight: the PQ2_0 packing llama.cpp PR
+ *   214 names, the same trits), 34 bytes per 128 weights:
+ *     [0,32) byte j holds the codes c = t + 1 of weights j, j+32, j+64 and
+ *     j+96 in bits 0-1, 2-3, 4-5 and 6-7 (code 3 must not occur); [32,34)
+ *     fp16 d.  W^_k = d * t_k.  Blocks start 2-byte aligned only.
+ *   Q4_K and Q6_K weights take Q8_K activations; both ternary formats take
+ *   Q8_128.
  *
  *   out: fp32 [M][N] row-major, fully overwritten (never accumulated).
  */
@@ -95,6 +101,7 @@ extern "C" {
 #define KQ_Q4_K 1
 #define KQ_Q6_K 2
 #define KQ_TQ 3
+#define KQ_TQ2 4
 
 /* activation formats */
 #define KQ_ACT_Q8_K 1
@@ -172,7 +179,7 @@ int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t
  *     value in storage order, q in [0,15] (Q4_K), q - 32 (Q6_K), t (ternary);
  *   scales [b][16] int32 (device, 4-byte aligned): Q4_K sc_0..sc_7 then
  *     m_0..m_7 (the 6-bit fields); Q6_K the 16 int8 scales, sign-extended.
- *     Not written for ternary, where scales may be NULL.
+ *     Not written for the ternary formats, where scales may be NULL.
  * The fp16 d / dmin fields are not decoded here.  nblocks may be at most
  * KQ_DEBUG_UNPACK_MAX_BLOCKS (KQ_ERR_SHAPE beyond, or when negative); 0 returns
  * KQ_OK with no launch.  Unknown fmt -> KQ_ERR_FMT; W or q NULL (or scales for

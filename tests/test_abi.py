@@ -94,6 +94,9 @@ def test_size_queries(kq):
     assert kq.kq_act_fmt_for(kq.KQ_Q4_K) == kq.KQ_ACT_Q8_K
     assert kq.kq_act_fmt_for(kq.KQ_Q6_K) == kq.KQ_ACT_Q8_K
     assert kq.kq_act_fmt_for(kq.KQ_TQ) == kq.KQ_ACT_Q8_128
+    assert kq.kq_act_fmt_for(kq.KQ_TQ2) == kq.KQ_ACT_Q8_128
+    assert kq.kq_weight_bytes(kq.KQ_TQ2, 17408, 5120) == 17408 * 40 * 34
+    assert kq.kq_weight_bytes(kq.KQ_TQ2, 3, 200) == 0             # K not a multiple of 128
     assert kq.kq_act_fmt_for(0) == kq.KQ_ERR_FMT
 
 
@@ -157,10 +160,13 @@ def test_variants_and_counters(kq):
     assert kq.kq_variant_name(n) is None and kq.kq_variant_name(-1) is None
     kq.kq_dispatch_reset()
     assert all(kq.kq_dispatch_count(v) == 0 for v in range(n))
-    for fmt in (kq.KQ_Q4_K, kq.KQ_Q6_K, kq.KQ_TQ):
+    for fmt in (kq.KQ_Q4_K, kq.KQ_Q6_K, kq.KQ_TQ, kq.KQ_TQ2):
         for M in (1, 8, 64, 65, 2048):
-            v = kq.kq_select_variant(fmt, M, 4096, 4096 if fmt != kq.KQ_TQ else 5120)
+            v = kq.kq_select_variant(fmt, M, 4096, 4096 if fmt < kq.KQ_TQ else 5120)
             assert 0 <= v < n
+    # two-bit ternary always runs on the tile kernel
+    for M in (1, 8, 2048):
+        assert kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, 4096, 5120)) == "gemm_tq2_128x128"
     assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT
     assert kq.kq_select_variant(kq.KQ_Q4_K, 1, 1, 100) == kq.KQ_ERR_SHAPE
 
@@ -186,7 +192,6 @@ def test_debug_unpack_rejects_bad_arguments(kq):
     Q4, Q6, TQ = kq.KQ_Q4_K, kq.KQ_Q6_K, kq.KQ_TQ
     # unknown format, bad counts, zero work
     assert L.kq_debug_unpack(0, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
-    assert L.kq_debug_unpack(4, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
     assert L.kq_debug_unpack(Q4, 4096, -1, 8192, 16384, None) == kq.KQ_ERR_SHAPE
     assert L.kq_debug_unpack(Q4, 4096, kq.KQ_DEBUG_UNPACK_MAX_BLOCKS + 1, 8192, 16384,
                              None) == kq.KQ_ERR_SHAPE
@@ -201,3 +206,5 @@ def test_debug_unpack_rejects_bad_arguments(kq):
     assert L.kq_debug_unpack(Q4, 4100, 1, 8192, 16384, None) == kq.KQ_ERR_ALIGN
     assert L.kq_debug_unpack(TQ, 4096, 1, 8200, None, None) == kq.KQ_ERR_ALIGN
     assert L.kq_debug_unpack(Q6, 4096, 1, 8192, 16386, None) == kq.KQ_ERR_ALIGN
+    assert L.kq_debug_unpack(5, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
+    assert L.kq_debug_unpack(kq.KQ_TQ2, 4096, 0, None, None, None) == kq.KQ_OK

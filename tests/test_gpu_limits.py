@@ -17,9 +17,9 @@ from oracle import kqref
 
 pytestmark = pytest.mark.gpu
 
-Q4_K, Q6_K, TQ = 1, 2, 3
-QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
-BB = {Q4_K: 144, Q6_K: 210, TQ: 28}
+Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}
+BB = {Q4_K: 144, Q6_K: 210, TQ: 28, TQ2: 34}
 DEV = "cuda:0"
 LIMIT = 1 << 31
 
@@ -46,6 +46,9 @@ def random_blocks(fmt: int, nblocks: int, seed: int) -> np.ndarray:
         b[:, 2:4] = np.array([0.002], np.float16).view(np.uint8)
     elif fmt == Q6_K:
         b[:, 208:210] = np.array([0.003], np.float16).view(np.uint8)
+    elif fmt == TQ2:
+        b[:, :32] &= 0x55  # codes 0 or 1 in every field: valid
+        b[:, 32:34] = np.array([0.01], np.float16).view(np.uint8)
     else:
         b[:, :25] %= 243
         b[:, 25] = 108 + b[:, 25] % 27
@@ -72,10 +75,11 @@ WEIGHT_CASES = [
     (Q4_K, 4096, (1, 40, 200)),     # matrix-vector, few-token, 128 x 128
     (Q6_K, 4096, (1, 40)),          # matrix-vector, 128 x 128 tile
     (TQ, 5120, (1, 40)),            # matrix-vector, 128 x 128 tile
+    (TQ2, 5120, (1, 40)),           # 128 x 128 tile
 ]
 
 
-@pytest.mark.parametrize("fmt,K,Ms", WEIGHT_CASES, ids=["q4_k", "q6_k", "tq"])
+@pytest.mark.parametrize("fmt,K,Ms", WEIGHT_CASES, ids=["q4_k", "q6_k", "tq", "tq2"])
 def test_weights_just_below_2gib(kq, fmt, K, Ms):
     rowbytes = (K // QK[fmt]) * BB[fmt]
     N = LIMIT // rowbytes - 256           # largest N with (N + 256) * rowbytes < 2^31
@@ -101,7 +105,7 @@ def test_weights_just_below_2gib(kq, fmt, K, Ms):
         del out
 
 
-@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ), ids=["q4_k", "q6_k", "tq"])
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ, TQ2), ids=["q4_k", "q6_k", "tq", "tq2"])
 def test_output_just_below_2gib(kq, fmt):
     M, K = 4096, 256
     N = LIMIT // (4 * (M + 128))          # largest N with (M + 128) * N * 4 < 2^31

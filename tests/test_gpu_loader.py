@@ -24,9 +24,10 @@ from oracle import kqref
 
 pytestmark = pytest.mark.gpu
 
-Q4_K, Q6_K, TQ = 1, 2, 3
-QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
-BB = {Q4_K: 144, Q6_K: 210, TQ: 28}
+Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}
+BB = {Q4_K: 144, Q6_K: 210, TQ: 28, TQ2: 34}
+TERNARY = (TQ, TQ2)
 DEV = "cuda:0"
 
 
@@ -54,6 +55,12 @@ def fuzz_blocks(fmt: int, n: int, seed: int) -> np.ndarray:
     ternary block takes digit bytes <= 242 and a last digit byte whose two
     spare digits are 1 (108..134)."""
     rng = np.random.default_rng(seed)
+    if fmt == TQ2:  # two-bit codes 0..2 only
+        b = np.empty((n, 34), np.uint8)
+        c = rng.integers(0, 3, size=(n, 32, 4))
+        b[:, :32] = (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+        b[:, 32:] = rng.integers(0, 256, size=(n, 2))
+        return b
     if fmt != TQ:
         return rng.integers(0, 256, size=(n, BB[fmt]), dtype=np.uint8)
     b = np.empty((n, 28), np.uint8)
@@ -76,6 +83,17 @@ def exhaustive_blocks(fmt: int) -> np.ndarray:
         out[:, 0:4] = (b + np.arange(4)) % 256
         out[:, 4:16] = np.packbits(bits, axis=1, bitorder="little")
         out[:, 16:] = (b + np.arange(128)) % 256
+        return out
+    if fmt == TQ2:
+        # every code byte of the block takes all 81 values made of valid
+        # codes (byte i of block b is the (b + 7i) mod 81-th of them)
+        valid = np.array([v for v in range(256) if all((v >> (2 * p)) & 3 != 3 for p in range(4))],
+                         np.uint8)
+        assert len(valid) == 81
+        b = np.arange(81)[:, None]
+        out = np.zeros((81, 34), np.uint8)
+        out[:, :32] = valid[(b + 7 * np.arange(32)[None, :]) % 81]
+        out[:, 32:] = (b + np.arange(2)) % 256
         return out
     if fmt == Q6_K:
         # every byte of the block, quant and scale bytes alike, takes all 256
@@ -106,7 +124,7 @@ def oracle_scales(fmt: int, blocks: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------ 1. kq_debug_unpack
 
-@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ))
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ, TQ2))
 def test_debug_unpack_matches_codec(kq, fmt):
     blocks = np.concatenate([exhaustive_blocks(fmt), fuzz_blocks(fmt, 10007, 900 + fmt)])
     B = blocks.shape[0]
@@ -117,14 +135,14 @@ def test_debug_unpack_matches_codec(kq, fmt):
     got_q = q.cpu().numpy().astype(np.int32)
     bad = np.argwhere(got_q != want_q)
     assert bad.size == 0, f"{len(bad)} values differ, first at block/value {tuple(bad[0])}"
-    if fmt != TQ:
+    if fmt not in TERNARY:
         got_s = scales.cpu().numpy()
         want_s = oracle_scales(fmt, blocks)
         bad = np.argwhere(got_s != want_s)
         assert bad.size == 0, f"{len(bad)} scale fields differ, first at {tuple(bad[0])}"
 
 
-@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ))
+@pytest.mark.parametrize("fmt", (Q4_K, Q6_K, TQ, TQ2))
 @pytest.mark.parametrize("B", [1, 2, 31, 33, 65])
 def test_debug_unpack_ragged_counts(kq, fmt, B):
     """Counts that leave workgroups partly empty; bytes past the last block are
@@ -139,9 +157,9 @@ def test_debug_unpack_ragged_counts(kq, fmt, B):
     assert np.array_equal(qn[:B].astype(np.int32), want)
     assert np.all(qn[B:] == 99)
     scn = sc.cpu().numpy()
-    if fmt != TQ:
+    if fmt not in TERNARY:
         assert np.array_equal(scn[:B], oracle_scales(fmt, blocks))
-    assert np.all(scn[B:] == -7) and (fmt != TQ or np.all(scn == -7))
+    assert np.all(scn[B:] == -7) and (fmt not in TERNARY or np.all(scn == -7))
 
 
 # ------------------------------------------------------------ 2. identity activations
@@ -178,6 +196,9 @@ def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
         W = datagen.pack_q4k(*datagen.random_fields_q4k(rng, B))
     elif fmt == Q6_K:
         W = datagen.pack_q6k(*datagen.random_fields_q6k(rng, B))
+    elif fmt == TQ2:
+        d, t = datagen.random_fields_tq2(rng, B)
+        W = datagen.pack_tq2(t, d)
     else:
         d, t = datagen.random_fields_tq(rng, B)
         W = datagen.pack_tq(t, d)
@@ -205,6 +226,8 @@ IDENTITY_CASES = [
     (Q6_K, 2048, "gemm_q6_k_128x128", 2048),
     (TQ, 1024, "gemm_tq_matvec", 8),
     (TQ, 1024, "gemm_tq_128x128", 1024),
+    (TQ2, 1024, "gemm_tq2_128x128", 8),
+    (TQ2, 1024, "gemm_tq2_128x128", 1024),
 ]
 
 

@@ -17,10 +17,10 @@ from oracle import kqref
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-Q4_K, Q6_K, TQ = 1, 2, 3
-FMTS = (Q4_K, Q6_K, TQ)
-QK = {Q4_K: 256, Q6_K: 256, TQ: 128}
-SUB = {Q4_K: 32, Q6_K: 16, TQ: 128}
+Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
+FMTS = (Q4_K, Q6_K, TQ, TQ2)
+QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}
+SUB = {Q4_K: 32, Q6_K: 16, TQ: 128, TQ2: 128}
 
 
 def say(*a):
@@ -137,7 +137,8 @@ def run_subsums(kq, fmt, W, a_q8, M, N, K):
 
 @pytest.mark.parametrize("fmt,M,N,K", [(Q4_K, 8, 256, 512), (Q4_K, 33, 70, 768),
                                        (Q6_K, 8, 96, 512), (Q6_K, 40, 33, 256),
-                                       (TQ, 8, 64, 384), (TQ, 35, 50, 640)])
+                                       (TQ, 8, 64, 384), (TQ, 35, 50, 640),
+                                       (TQ2, 8, 64, 384), (TQ2, 35, 50, 640)])
 def test_subsums_bit_exact(kq, fmt, M, N, K):
     say(f"subsums fmt={fmt} M={M} N={N} K={K}")
     W = datagen.make_weights(fmt, N, K, 1001)
@@ -202,7 +203,7 @@ SWEEP_N = (48, 128, 200, 256)
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_shape_sweep(kq, fmt):
-    Ks = (256, 512, 768) if fmt != TQ else (128, 384, 640)
+    Ks = (256, 512, 768) if fmt not in (TQ, TQ2) else (128, 384, 640)
     rng = np.random.default_rng(fmt)
     for K in Ks:
         Wfull = datagen.make_weights(fmt, max(SWEEP_N), K, 2000 + K)
@@ -391,7 +392,7 @@ def test_unit_scale_ternary_is_integer_matmul(kq):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_zero_and_negated_activations(kq, fmt):
     say(f"x=0 and x->-x fmt={fmt}")
-    M, N, K = 96, 160, 768 if fmt != TQ else 640
+    M, N, K = 96, 160, 768 if fmt not in (TQ, TQ2) else 640
     W = datagen.make_weights(fmt, N, K, 55)
     x = datagen.draw_activations(M, K, 56)
     act_fmt = kq.kq_act_fmt_for(fmt)
@@ -422,6 +423,7 @@ MUTATIONS = [
     (Q6_K, "high bits", 128 + 5, 0x02),         # the high bit of a quant's top pair
     (Q6_K, "scale", 192 + 3, 0x40),             # bit 6 of an int8 scale
     (TQ, "trit", 7, None),                      # one base-3 digit of byte 7
+    (TQ2, "code", 9, 0x30),                     # the code of weight 73 (bits 4-5 of byte 9)
 ]
 
 
@@ -433,7 +435,7 @@ def test_gate_fails_on_a_flipped_field(kq, fmt, field, off, mask):
     column of the changed weight row."""
     say(f"mutation fmt={fmt} {field}")
     M, N = 64, 96
-    K = 384 if fmt == TQ else 512
+    K = 384 if fmt in (TQ, TQ2) else 512
     W = datagen.make_weights(fmt, N, K, 71)
     x = datagen.draw_activations(M, K, 72)
     act_fmt = kq.kq_act_fmt_for(fmt)
@@ -442,12 +444,15 @@ def test_gate_fails_on_a_flipped_field(kq, fmt, field, off, mask):
     a_q8 = run_quant(kq, act_fmt, x)
     assert_within_tol(run_gemm(kq, fmt, W, a_q8, M, N, K), ref, tol, "unmutated")
 
-    n, bb = 37, {Q4_K: 144, Q6_K: 210, TQ: 28}[fmt]
+    n, bb = 37, {Q4_K: 144, Q6_K: 210, TQ: 28, TQ2: 34}[fmt]
     Wm = W.copy()
     i = bb + off                                   # second block of row n
     if mask is None:                               # next base-3 value of the lowest digit
         v = int(Wm[n, i])
         Wm[n, i] = v + 1 if v % 3 != 2 else v - 2
+    elif fmt == TQ2:                               # next valid code (0 -> 1 -> 2 -> 0)
+        c = (int(Wm[n, i]) >> 4) & 3
+        Wm[n, i] = (int(Wm[n, i]) & ~0x30) | (((c + 1) % 3) << 4)
     else:
         Wm[n, i] ^= mask
     changed = np.argwhere(kqref.dequant_rows(fmt, Wm, K) != kqref.dequant_rows(fmt, W, K))
@@ -466,7 +471,7 @@ def test_canaries_and_poisoned_tails(kq, fmt):
     garbage; the output is a view followed by NaN canaries.  Results must equal
     the clean run and the canaries must be untouched."""
     say(f"canaries fmt={fmt}")
-    M, N, K = 77, 131, 512 if fmt != TQ else 384
+    M, N, K = 77, 131, 512 if fmt not in (TQ, TQ2) else 384
     W = datagen.make_weights(fmt, N, K, 91)
     x = datagen.draw_activations(M, K, 92)
     act_fmt = kq.kq_act_fmt_for(fmt)
