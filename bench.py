@@ -56,6 +56,7 @@ GEMM_SOURCES = {
     "q4_k": ("kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp"),
     "q6_k": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     "tq": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "tq2": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
 }
 
 
