@@ -19,6 +19,7 @@ KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
 KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
 KQ_DEBUG_UNPACK_MAX_BLOCKS = 1 << 24
+KQ_GEMM_ID_MAX_EXPERTS = 65536
 KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
     -1, -2, -3, -4, -5, -6)
 (KQ_CALIB_MFMA_I8, KQ_CALIB_MFMA_I8_TOGGLE, KQ_CALIB_VALU_F32, KQ_CALIB_MFMA_I8_VALU,
@@ -35,6 +36,7 @@ SIGNATURES = {
     "kq_gemm": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kq_gemm_subsums": (_I, [_I, _P, _P, _I64, _I64, _I64, _P, _P]),
     "kq_debug_unpack": (_I, [_I, _P, _I64, _P, _P, _P]),
+    "kq_gemm_id": (_I, [_I, _P, _I64, _P, _I64, _I64, _I64, _P, _P, _I64, _P, _P]),
     "kq_num_variants": (_I, []),
     "kq_variant_name": (ctypes.c_char_p, [_I]),
     "kq_dispatch_count": (ctypes.c_uint64, [_I]),
@@ -153,6 +155,11 @@ def kq_debug_unpack(fmt, W, nblocks, q, scales, stream=None):
                                         _stream(stream)), "kq_debug_unpack")
 
 
+def kq_gemm_id(fmt, W, n_experts, a_q8, M, N, K, expert_offsets, rows, R, out, stream=None):
+    return _check(lib().kq_gemm_id(fmt, _ptr(W), n_experts, _ptr(a_q8), M, N, K, _ptr(expert_offsets),
+                                   _ptr(rows), R, _ptr(out), _stream(stream)), "kq_gemm_id")
+
+
 def kq_calib_launch(kind, param=0, buf=None, nbytes=0, stream=None):
     """Launch one calibration kernel; returns the work it does (int8 ops, fp32
     flops or bytes)."""
@@ -227,3 +234,14 @@ def debug_unpack(fmt, W, nblocks, stream=None):
     scales = None if ternary else torch.empty((nblocks, 16), dtype=torch.int32, device=W.device)
     kq_debug_unpack(fmt, W, nblocks, q, scales, stream)
     return q, scales
+
+
+def gemm_id(fmt, W, n_experts, a_q8, M, N, K, expert_offsets, rows, out=None, stream=None):
+    """out fp32 [R][N]: routed row r = expert e's weights x token rows[r]
+    (expert_offsets int32 [n_experts + 1], rows int32 [R]; device tensors)."""
+    import torch
+    R = rows.numel()
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.float32, device=a_q8.device)
+    kq_gemm_id(fmt, W, n_experts, a_q8, M, N, K, expert_offsets, rows, R, out, stream)
+    return out

@@ -30,13 +30,14 @@ enum Variant {
     V_SUBSUMS_TQ,
     V_GEMM_TQ2_128x128,
     V_SUBSUMS_TQ2,
+    V_GEMM_ID_128x128,
     V_COUNT
 };
 
 const char *const kVariantNames[V_COUNT] = {
     "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
     "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
-    "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",
+    "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",   "gemm_id_128x128",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -220,6 +221,44 @@ int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t 
                    hipSuccess
                ? KQ_OK
                : KQ_ERR_HIP;
+}
+
+int kq_gemm_id(int fmt, const void *W, int64_t n_experts, const void *a_q8, int64_t M, int64_t N,
+               int64_t K, const int32_t *expert_offsets, const int32_t *rows, int64_t R, float *out,
+               hipStream_t stream) {
+    if (!qk_of(fmt)) return KQ_ERR_FMT;
+    if (M < 0 || N < 0 || K < 0 || R < 0 || K % qk_of(fmt)) return KQ_ERR_SHAPE;
+    if (n_experts < 1 || n_experts > KQ_GEMM_ID_MAX_EXPERTS) return KQ_ERR_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || R > kMaxDim) return KQ_ERR_SHAPE;
+    if ((M && K > kMaxBytes / M) || (N && K > kMaxBytes / N) || (R && N > kMaxBytes / R))
+        return KQ_ERR_SHAPE;
+    const int64_t rowbytes = (K / qk_of(fmt)) * bb_of(fmt);
+    if (N && rowbytes && n_experts > kMaxBytes / (N * rowbytes)) return KQ_ERR_SHAPE;
+    if (R == 0 || N == 0) return KQ_OK;
+    if (M == 0) return KQ_ERR_SHAPE;  // routed rows but no token to read
+    if (!W || !a_q8 || !expert_offsets || !rows || !out) return KQ_ERR_NULL;
+    if (!aligned16(W) || !aligned16(a_q8) || !aligned16(out) || ((uintptr_t)expert_offsets & 3u) ||
+        ((uintptr_t)rows & 3u))
+        return KQ_ERR_ALIGN;
+    // the tile kernel addresses one expert's weights and the activation
+    // sections with 32-bit offsets (activation rows are gathered, never past M)
+    const int64_t lim = (int64_t)1 << 31;
+    if ((N + 256) * rowbytes >= lim || M * K >= lim || (K / qk_of(fmt)) * M * 4 >= lim ||
+        (K / 256) * 2 * M * 16 >= lim)
+        return KQ_ERR_UNSUPPORTED;
+    const int64_t tiles = ((R + 127) / 128 + n_experts) * ((N + 127) / 128);
+    if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    ActLayout L;
+    act_layout(kq_act_fmt_for(fmt), M, K, &L);
+    const char *base = static_cast<const char *>(a_q8);
+    hipError_t e = kq::launch_gemm_id(
+        fmt, W, (int)n_experts, N * rowbytes, reinterpret_cast<const int8_t *>(base),
+        reinterpret_cast<const float *>(base + L.d),
+        L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr, expert_offsets, rows,
+        (int)R, out, (int)M, (int)N, (int)K, stream);
+    if (e != hipSuccess) return KQ_ERR_HIP;
+    g_count[V_GEMM_ID_128x128].fetch_add(1);
+    return KQ_OK;
 }
 
 int kq_calib_launch(int kind, int param, const void *buf, int64_t bytes, double *work,

@@ -82,6 +82,13 @@ struct GemmArgs {
     int nchunks;            // K / KC (ternary: K / 128 blocks rounded up to chunks)
     int nblk;               // weight blocks per row = K / QK
     int tiles_m, tiles_n;
+    // expert-indexed product (gather mode of the tile kernel): routed row r of
+    // expert e, r in [exp_off[e], exp_off[e+1]), is token rows[r]; expert e's
+    // weights start expert_bytes * e bytes into W
+    const int32_t *exp_off;
+    const int32_t *rows;
+    int n_experts, n_routed;
+    int64_t expert_bytes;
 };
 
 // ---------------------------------------------------------------------------
@@ -455,7 +462,7 @@ __device__ __forceinline__ void tq_lut_entry(uint32_t v, uint32_t &lo, uint32_t 
     hi = t[4];
 }
 
-template <int FMT>
+template <int FMT, bool GATHER = false>
 __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
@@ -494,8 +501,47 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     const int first_m = (tile / per_group) * GM;
     const int gsize = min(a.tiles_m - first_m, GM);
     const int tm = first_m + (tile % per_group) % gsize, tn = (tile % per_group) / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int n0 = tn * BN;
     const int M = a.M, N = a.N, K = a.K;
+    // m0: first activation row of the tile; mrows: tile rows holding data;
+    // orow0: first output row; Wx: the weights this tile multiplies
+    int m0, mrows, grb = 0;
+    int64_t orow0;
+    const uint8_t *Wx = a.W;
+    if constexpr (!GATHER) {
+        m0 = tm * BM;
+        mrows = min(M - m0, BM);
+        orow0 = m0;
+    } else {
+        // expert-indexed: M-tile tm is tile mt of expert e, counting each
+        // expert's ceil(rows / BM) tiles in expert order; tiles past the last
+        // one (the grid is an upper bound) leave before any barrier
+        int e = -1, mt = 0, acc = 0;
+        for (int x = 0; x < a.n_experts; ++x) {
+            const int cnt = max(a.exp_off[x + 1] - a.exp_off[x], 0);
+            const int te = (cnt + BM - 1) / BM;
+            if (e < 0 && tm < acc + te) {
+                e = x;
+                mt = tm - acc;
+            }
+            acc += te;
+        }
+        if (e < 0) return;
+        // (clamped, so that routing arrays that break their contract give
+        // wrong values but never an access outside rows[] or out)
+        grb = a.exp_off[e] + mt * BM;
+        mrows = (grb < 0 || grb >= a.n_routed) ? 0 : min(min(a.exp_off[e + 1], a.n_routed) - grb, BM);
+        m0 = 0;
+        orow0 = grb;
+        Wx = a.W + (int64_t)e * a.expert_bytes;
+    }
+    // token row of tile row r when gathering (rows past the expert's last
+    // repeat it; indices are clamped into the activation buffer)
+    auto token = [&](int r) KQ_INLINE {
+        const int idx = min(max(grb + min(r, mrows - 1), 0), a.n_routed - 1);
+        const int t = a.rows[idx];
+        return min(max(t, 0), M - 1);
+    };
     const int nch = (K + KCH - 1) / KCH;                    // chunks
     const int nsa = TRI ? a.nblk : a.nchunks;               // activation scale blocks per row
 
@@ -512,26 +558,28 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     // activations: two 16-byte pieces per thread (row a_r0 + 64 i, piece a_pc)
     const int a_pc = tid & 7, a_r0 = tid >> 3;
     const auto rs_a = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.qs + (int64_t)m0 * K), (short)0, min(M - m0, BM) * K, RSRC_FLAGS);
+        (void *)(a.qs + (int64_t)m0 * K), (short)0, (GATHER ? M : min(M - m0, BM)) * K, RSRC_FLAGS);
     uint32_t a_off[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a_off[i] = (uint32_t)(a_r0 + 64 * i) * (uint32_t)K + 16u * a_pc;
+    for (int i = 0; i < 2; ++i)
+        a_off[i] = (uint32_t)(GATHER ? token(a_r0 + 64 * i) : a_r0 + 64 * i) * (uint32_t)K + 16u * a_pc;
     // activation scales (block-major [nsa][M]) and, for Q4_K, the alpha
     // section: thread t owns row t/4; of alpha it copies 4 bytes: part
     // (t%4)/2 (hi/lo), sub-blocks 2*(t%2) .. +1 of the chunk's four
     const int s_row = tid >> 2, s_j = tid & 3;
     const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)(a.da + m0), (short)0,
                                                         (nsa * M - m0) * 4, RSRC_FLAGS);
-    const uint32_t d_off = 4u * s_row;
+    const int s_tok = GATHER ? token(s_row) : s_row;  // activation row whose scales this thread stages
+    const uint32_t d_off = 4u * s_tok;
     const auto rs_al = __builtin_amdgcn_make_buffer_rsrc(
         Q4 ? (void *)(a.alpha + (int64_t)m0 * 8) : (void *)a.da, (short)0,
         Q4 ? (a.nchunks * 2 * M - m0) * 16 : 0, RSRC_FLAGS);
-    const uint32_t al_off = (uint32_t)(((s_j >> 1) * M + s_row) * 16 + 4 * (s_j & 1));
+    const uint32_t al_off = (uint32_t)(((s_j >> 1) * M + s_tok) * 16 + 4 * (s_j & 1));
     // weights: four threads per row
     const int wq = tid & 3, w_nl = tid >> 2;
     const int w_rowbytes = a.nblk * Fmt<FMT>::BB;
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.W + (int64_t)n0 * w_rowbytes), (short)0, min(N - n0, BN) * w_rowbytes,
+        (void *)(Wx + (int64_t)n0 * w_rowbytes), (short)0, min(N - n0, BN) * w_rowbytes,
         RSRC_FLAGS);
     const uint32_t w_off = (uint32_t)(w_nl * w_rowbytes);
     // ternary: this thread's 8 trit bytes start at byte 8*wq of the block
@@ -1024,14 +1072,14 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
 
     // ---- epilogue: fp32 stores (unmasked when the whole tile is inside) ----
     float *out = reinterpret_cast<float *>(a.out);
-    const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+    const bool full = (mrows == BM) && (n0 + BN <= N);
     const int n = n0 + 32 * wn + lrow;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = m0 + 64 * wm + 32 * i + mfma32_row(r, lane);
-            if (full || (m < M && n < N)) out[(int64_t)m * N + n] = acc_f[i][r];
+            const int ml = 64 * wm + 32 * i + mfma32_row(r, lane);
+            if (full || (ml < mrows && n < N)) out[(orow0 + ml) * N + n] = acc_f[i][r];
         }
     }
 }
@@ -1169,6 +1217,11 @@ static GemmArgs make_args(int fmt, const void *W, const int8_t *qs, const float 
     a.nblk = (fmt == FMT_TQ || fmt == FMT_TQ2) ? K / 128 : K / 256;
     a.tiles_m = (M + bm - 1) / bm;
     a.tiles_n = (N + bn - 1) / bn;
+    a.exp_off = nullptr;
+    a.rows = nullptr;
+    a.n_experts = 0;
+    a.n_routed = 0;
+    a.expert_bytes = 0;
     return a;
 }
 
@@ -1286,6 +1339,38 @@ hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *
             break;
         default:
             hipLaunchKernelGGL(debug_unpack_kernel<FMT_TQ>, dim3(grid), dim3(64), 0, stream, a, q, scales);
+            break;
+    }
+    return hipGetLastError();
+}
+
+// Expert-indexed product on the tile kernel (gather mode): out [R][N], row r =
+// W[e(r)] x A[rows[r]].  The grid covers an upper bound of the M-tiles,
+// ceil(R / BM) + n_experts; surplus workgroups return at once.
+hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_bytes,
+                          const int8_t *qs, const float *da, const uint16_t *alpha,
+                          const int32_t *exp_off, const int32_t *rows, int R, float *out, int M,
+                          int N, int K, hipStream_t stream) {
+    GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
+    a.tiles_m = (R + MBM - 1) / MBM + n_experts;
+    a.exp_off = exp_off;
+    a.rows = rows;
+    a.n_experts = n_experts;
+    a.n_routed = R;
+    a.expert_bytes = expert_bytes;
+    const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
+    switch (fmt) {
+        case FMT_Q4K:
+            hipLaunchKernelGGL((gemm_kernel<FMT_Q4K, true>), dim3(grid), dim3(MNT), 0, stream, a);
+            break;
+        case FMT_Q6K:
+            hipLaunchKernelGGL((gemm_kernel<FMT_Q6K, true>), dim3(grid), dim3(MNT), 0, stream, a);
+            break;
+        case FMT_TQ2:
+            hipLaunchKernelGGL((gemm_kernel<FMT_TQ2, true>), dim3(grid), dim3(MNT), 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_kernel<FMT_TQ, true>), dim3(grid), dim3(MNT), 0, stream, a);
             break;
     }
     return hipGetLastError();

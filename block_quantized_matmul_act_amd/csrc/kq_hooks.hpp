@@ -1,5 +1,5 @@
-// kq_hooks.hpp -- host-side launchers of test hooks that have no place in the
-// GEMM launch path.
+// kq_hooks.hpp -- host-side launchers outside the plain GEMM launch path: the
+// loader test hook and the expert-indexed product.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,5 +12,11 @@ namespace kq {
 // (Q4_K: 8 scales then 8 mins; Q6_K: 16 scales; ternary: not written).
 hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
                                hipStream_t stream);
+
+// Expert-indexed product (kq_gemm_id) on the tile kernel of kq_gemm.hip.
+hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_bytes,
+                          const int8_t *qs, const float *da, const uint16_t *alpha,
+                          const int32_t *exp_off, const int32_t *rows, int R, float *out, int M,
+                          int N, int K, hipStream_t stream);
 
 }  // namespace kq

@@ -189,6 +189,34 @@ int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t
 int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
                     hipStream_t stream);
 
+/*
+ * Expert-indexed product (a mixture-of-experts layer's GEMM; llama.cpp's
+ * MUL_MAT_ID, which the pages test next to MUL_MAT): every routed row r
+ * multiplies one expert's weights with one token's quantized activations,
+ *   out[r][n] = sum_k W^_e[n][k] * A^[rows[r]][k],  e the expert of row r,
+ * through the same loaders and tile kernel as kq_gemm.
+ *   W               device, n_experts consecutive weight tensors of N rows of
+ *                   K/QK blocks (expert e starts e * kq_weight_bytes(fmt, N, K)
+ *                   bytes in), 16-byte aligned
+ *   a_q8            device, M tokens from kq_quantize_act (kq_act_fmt_for(fmt))
+ *   expert_offsets  device int32 [n_experts + 1], non-decreasing, [0] = 0,
+ *                   [n_experts] = R: the routed rows of expert e are
+ *                   [expert_offsets[e], expert_offsets[e + 1])
+ *   rows            device int32 [R]: the token (row of a_q8, 0 <= t < M) of
+ *                   each routed row; a token may appear any number of times
+ *   out             device fp32 [R][N], fully overwritten
+ * The routing arrays live on the device and are not checked on the host:
+ * arrays that break the contract give undefined values in out, but every
+ * access stays inside W, a_q8, rows and out.  R == 0 or N == 0 returns KQ_OK
+ * with no launch; M == 0 with R > 0 is KQ_ERR_SHAPE; n_experts must be in
+ * 1 .. KQ_GEMM_ID_MAX_EXPERTS.  Other errors and limits as kq_gemm (one
+ * expert's weights and the activation sections within 2^31 bytes).
+ */
+#define KQ_GEMM_ID_MAX_EXPERTS 65536
+int kq_gemm_id(int fmt, const void *W, int64_t n_experts, const void *a_q8, int64_t M, int64_t N,
+               int64_t K, const int32_t *expert_offsets, const int32_t *rows, int64_t R, float *out,
+               hipStream_t stream);
+
 /* Per-variant dispatch counters (incremented on each successful launch) and
  * their names, so tests can prove which kernel variant ran (vllm.cpp PR 3036
  * added such counters after finding tests that never reached a variant). */

@@ -31,7 +31,7 @@ struct Rec {
     int calls = 0;
     const void *p[4] = {};
     int64_t n[3] = {};
-} rq, rg, rs, rd;
+} rq, rg, rs, rd, ri;
 }  // namespace
 
 namespace kq {
@@ -69,6 +69,20 @@ hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *
 int q4k_kernel_choice(int M, int, int) { return M <= 2 ? Q4K_MATVEC : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128; }
 hipError_t launch_calib(int, int, const void *, int64_t, int, double *work, hipStream_t) {
     *work = 1.0;
+    return hipSuccess;
+}
+hipError_t launch_gemm_id(int, const void *, int n_experts, int64_t expert_bytes, const int8_t *qs,
+                          const float *da, const uint16_t *alpha, const int32_t *, const int32_t *, int R,
+                          float *, int M, int N, int K, hipStream_t) {
+    ++ri.calls;
+    ri.p[0] = qs;
+    ri.p[1] = da;
+    ri.p[2] = alpha;
+    ri.n[0] = n_experts;
+    ri.n[1] = expert_bytes;
+    ri.n[2] = (int64_t)R * 1000000 + M;
+    (void)N;
+    (void)K;
     return hipSuccess;
 }
 hipError_t launch_debug_unpack(int, const void *, int64_t nblocks, int8_t *, int32_t *, hipStream_t) {
@@ -111,6 +125,11 @@ int main() {
                         EXPECT((M + 128) * K < ((int64_t)1 << 31));
                     }
                     (void)kq_gemm_subsums(fmt, A, A, M, N, K, reinterpret_cast<int32_t *>(A), s);
+                    for (int64_t E : {(int64_t)-1, (int64_t)0, (int64_t)1, (int64_t)8, (int64_t)65537, INT64_MAX}) {
+                        const int rc2 = kq_gemm_id(fmt, A, E, A, M, N, K, reinterpret_cast<int32_t *>(A),
+                                                   reinterpret_cast<int32_t *>(A), K, reinterpret_cast<float *>(A), s);
+                        EXPECT(rc2 == KQ_OK || rc2 == KQ_ERR_FMT || rc2 == KQ_ERR_SHAPE || rc2 == KQ_ERR_UNSUPPORTED);
+                    }
                     (void)kq_quantize_act(fmt, reinterpret_cast<float *>(A), M, K, A, s);
                 }
     for (int fmt = -1; fmt <= 4; ++fmt)
@@ -141,6 +160,14 @@ int main() {
             EXPECT(kq_gemm(KQ_TQ, A, A, M, 96, K, reinterpret_cast<float *>(A), s) == KQ_OK);
             EXPECT(rg.p[2] == nullptr);
         }
+    // the expert-indexed product hands the launcher the documented sections
+    // and the byte stride of one expert's weights
+    ri = Rec{};
+    EXPECT(kq_gemm_id(KQ_Q6_K, A, 8, A, 100, 96, 512, reinterpret_cast<int32_t *>(A),
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
+    EXPECT(ri.calls == 1 && ri.n[0] == 8 && ri.n[1] == 96 * 2 * 210 && ri.n[2] == 300 * 1000000 + 100);
+    EXPECT(ri.p[1] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_D, 100, 512));
+    EXPECT(ri.p[2] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, 100, 512));
     // the loader hook reaches its launcher only with a valid count
     rd = Rec{};
     EXPECT(kq_debug_unpack(KQ_Q4_K, A, 10, reinterpret_cast<int8_t *>(A), reinterpret_cast<int32_t *>(A), s) == KQ_OK);

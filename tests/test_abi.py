@@ -208,3 +208,26 @@ def test_debug_unpack_rejects_bad_arguments(kq):
     assert L.kq_debug_unpack(Q6, 4096, 1, 8192, 16386, None) == kq.KQ_ERR_ALIGN
     assert L.kq_debug_unpack(5, 4096, 1, 8192, 16384, None) == kq.KQ_ERR_FMT
     assert L.kq_debug_unpack(kq.KQ_TQ2, 4096, 0, None, None, None) == kq.KQ_OK
+
+
+def test_gemm_id_rejects_bad_arguments(kq):
+    L = kq.lib()
+    A, P4 = 1 << 20, (1 << 20) + 4096   # fake aligned addresses, never dereferenced
+    Q4, TQ2 = kq.KQ_Q4_K, kq.KQ_TQ2
+    f = lambda *a: L.kq_gemm_id(*a, None)
+    assert f(0, A, 8, A, 10, 64, 256, P4, P4, 20, A) == kq.KQ_ERR_FMT
+    assert f(Q4, A, 8, A, 10, 64, 300, P4, P4, 20, A) == kq.KQ_ERR_SHAPE     # K % 256
+    assert f(Q4, A, 0, A, 10, 64, 256, P4, P4, 20, A) == kq.KQ_ERR_SHAPE     # no expert
+    assert f(Q4, A, kq.KQ_GEMM_ID_MAX_EXPERTS + 1, A, 10, 64, 256, P4, P4, 20, A) == kq.KQ_ERR_SHAPE
+    assert f(Q4, A, 8, A, 10, 64, 256, P4, P4, -1, A) == kq.KQ_ERR_SHAPE
+    assert f(Q4, A, 8, A, 0, 64, 256, P4, P4, 20, A) == kq.KQ_ERR_SHAPE      # rows but no token
+    assert f(Q4, None, 8, None, 10, 64, 256, None, None, 0, None) == kq.KQ_OK  # R == 0
+    assert f(TQ2, None, 8, None, 10, 0, 256, None, None, 20, None) == kq.KQ_OK  # N == 0
+    assert f(Q4, A, 8, A, 10, 64, 256, None, P4, 20, A) == kq.KQ_ERR_NULL
+    assert f(Q4, A, 8, A, 10, 64, 256, P4, None, 20, A) == kq.KQ_ERR_NULL
+    assert f(Q4, A + 8, 8, A, 10, 64, 256, P4, P4, 20, A) == kq.KQ_ERR_ALIGN
+    assert f(Q4, A, 8, A, 10, 64, 256, P4 + 2, P4, 20, A) == kq.KQ_ERR_ALIGN
+    assert f(Q4, A, 8, A, 10, 64, 256, P4, P4, 20, A + 4) == kq.KQ_ERR_ALIGN
+    # one expert's weights must stay within 2^31 bytes
+    n = (1 << 31) // 2304
+    assert f(Q4, A, 2, A, 10, n, 4096, P4, P4, 20, A) == kq.KQ_ERR_UNSUPPORTED

@@ -411,6 +411,74 @@ def test_zero_and_negated_activations(kq, fmt):
     assert np.all(zero == 0)
 
 
+# ------------------------------------------------- expert-indexed product
+
+def routing(rng, M, counts):
+    """Synthetic routing: expert e takes counts[e] routed rows of random tokens
+    (repeats allowed); returns int32 offsets [E+1] and rows [R]."""
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = np.concatenate([rng.integers(0, M, size=c) for c in counts]).astype(np.int32)
+    return off, rows
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_id_matches_oracle(kq, fmt):
+    """Every routed row against the oracle on its expert and token; experts
+    with no row, one row, and more rows than a tile; canaries after out."""
+    E, M, N = 8, 97, 200
+    K = 640 if fmt in (TQ, TQ2) else 512
+    rng = np.random.default_rng(60 + fmt)
+    counts = [0, 1, 129, 7, 40, 0, 64, 33]
+    off, rows = routing(rng, M, counts)
+    R = int(off[-1])
+    Ws = [datagen.make_weights(fmt, N, K, 900 + e) for e in range(E)]
+    W = np.concatenate([w.reshape(-1) for w in Ws])
+    x = datagen.draw_activations(M, K, 61)
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    a_q8 = run_quant(kq, act_fmt, x)
+    qs, d, _ = check_act_exact(kq, act_fmt, x, a_q8)
+    say(f"gemm_id fmt={fmt} E={E} M={M} N={N} K={K} R={R}")
+    ob = torch.full((R + 3, N), 12345.0, dtype=torch.float32, device=DEV)
+    before = kq.dispatch_counts()["gemm_id_128x128"]
+    kq.kq_gemm_id(fmt, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, ob)
+    torch.cuda.synchronize()
+    assert kq.dispatch_counts()["gemm_id_128x128"] == before + 1
+    out = ob.cpu().numpy()
+    assert np.all(out[R:] == 12345.0), "rows past R written"
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r0 == r1:
+            continue
+        toks = rows[r0:r1]
+        ref, tol = kqref.gemm(fmt, Ws[e], np.ascontiguousarray(qs[toks]), np.ascontiguousarray(d[toks]), K)
+        assert_within_tol(out[r0:r1], ref, tol, f"gemm_id fmt={fmt} expert {e}")
+        if fmt != Q4_K and r1 - r0 > 8:
+            # the plain product of the same tile kernel on the gathered tokens:
+            # identical arithmetic, identical bits
+            xg = np.ascontiguousarray(x[toks])
+            plain = run_gemm(kq, fmt, Ws[e], run_quant(kq, act_fmt, xg), r1 - r0, N, K)
+            assert np.array_equal(out[r0:r1], plain), f"expert {e} differs from kq_gemm"
+
+
+def test_gemm_id_routing_out_of_contract_stays_in_bounds(kq):
+    """Offsets past R, decreasing offsets and token indices past M give
+    undefined values but no access outside the buffers: canaries around out
+    stay intact and the call completes."""
+    E, M, N, K = 4, 20, 64, 256
+    rng = np.random.default_rng(77)
+    W = np.concatenate([datagen.make_weights(Q6_K, N, K, 70 + e).reshape(-1) for e in range(E)])
+    a_q8 = run_quant(kq, kq.KQ_ACT_Q8_K, datagen.draw_activations(M, K, 71))
+    R = 50
+    off = np.array([0, 30, 10, 60, 1000], np.int32)     # decreasing, then past R
+    rows = rng.integers(-5, M + 5, size=R).astype(np.int32)
+    pad = 4096
+    ob = torch.full((R * N + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
+    view = ob[pad:pad + R * N].view(R, N)
+    kq.kq_gemm_id(Q6_K, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, view)
+    torch.cuda.synchronize()
+    assert torch.all(ob[:pad] == 7.0).item() and torch.all(ob[pad + R * N:] == 7.0).item()
+
+
 # ------------------------------------------------- the gate is not vacuous
 
 # (fmt, field, byte offset inside the block, xor mask): one stored field of
