@@ -3,7 +3,8 @@
 
 A step is one pass of the whole path over one batch: kq_quantize_act (fp32
 activations -> Q8_K blocks) then kq_gemm (Q4_K weights x Q8_K activations ->
-fp32 out).  The default workload is the 4096 -> 14336 FFN gate/up projection
+fp32 out), or for an expert-indexed workload kq_gemm_id over a seeded top-k
+routing (throughput counts 2 * routed rows * N * K).  The default workload is the 4096 -> 14336 FFN gate/up projection
 at 2048 tokens (M=2048, N=14336, K=4096, seeded synthetic data), the shape the
 headline metric is quoted on.  Inputs are resident in HBM before timing; the
 weight, activation and output buffers rotate over enough copies that
@@ -57,6 +58,8 @@ GEMM_SOURCES = {
     "q6_k": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     "tq": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     "tq2": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
+    # expert-indexed workloads (any format) run the tile kernel of kq_gemm.hip
+    "moe": ("kq_gemm.hip", "kq_device.hpp", "kq_hooks.hpp"),
 }
 
 
@@ -127,20 +130,35 @@ def main():
 
     log(f"[bench] generating {wl.name} M={M} N={N} K={K}")
     W_np, x_np = datagen.make_workload(wl)
+    # an expert-indexed workload routes M tokens to topk of E experts: R
+    # routed rows, each one expert's N x K product
+    E = max(wl.experts, 1)
+    src_key = "moe" if wl.experts else datagen.FMT_NAMES[fmt]  # sources of the GEMM kernel
+    R = M * wl.topk if wl.experts else M
+    if wl.experts:
+        off_np, rows_np = datagen.draw_routing(M, wl.experts, wl.topk, wl.seed)
+        off_d = torch.from_numpy(off_np).to(dev)
+        rows_d = torch.from_numpy(rows_np).to(dev)
 
-    w_bytes = kq.kq_weight_bytes(fmt, N, K)
+    w_bytes = kq.kq_weight_bytes(fmt, N, K) * E
     a_bytes = kq.kq_act_bytes(act_fmt, M, K)
     x_bytes = M * K * 4
-    o_bytes = M * N * 4
+    o_bytes = R * N * 4
     per_step = w_bytes + a_bytes + x_bytes + o_bytes
     ncopy = max(1, min(16, -(-ROTATE_BYTES // per_step)))
     log(f"[bench] {ncopy} rotating buffer sets of {per_step / 2**20:.1f} MiB")
     Ws = [torch.from_numpy(W_np).to(dev) for _ in range(ncopy)]
     xs = [torch.from_numpy(x_np).to(dev) for _ in range(ncopy)]
     As = [torch.empty(a_bytes, dtype=torch.uint8, device=dev) for _ in range(ncopy)]
-    Os = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(ncopy)]
+    Os = [torch.empty((R, N), dtype=torch.float32, device=dev) for _ in range(ncopy)]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+
+    def gemm(j):
+        if wl.experts:
+            kq.kq_gemm_id(fmt, Ws[j], E, As[j], M, N, K, off_d, rows_d, R, Os[j], sp)
+        else:
+            kq.kq_gemm(fmt, Ws[j], As[j], M, N, K, Os[j], sp)
 
     def step(i, ev=None):
         j = i % ncopy
@@ -149,7 +167,7 @@ def main():
         kq.kq_quantize_act(act_fmt, xs[j], M, K, As[j], sp)
         if ev is not None:
             ev[1].record(stream)
-        kq.kq_gemm(fmt, Ws[j], As[j], M, N, K, Os[j], sp)
+        gemm(j)
         if ev is not None:
             ev[2].record(stream)
 
@@ -180,8 +198,7 @@ def main():
     b2b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     b2b[0].record(stream)
     for i in range(args.steps):
-        j = i % ncopy
-        kq.kq_gemm(fmt, Ws[j], As[j], M, N, K, Os[j], sp)
+        gemm(i % ncopy)
     b2b[1].record(stream)
     torch.cuda.synchronize()
     gemm_b2b_s = b2b[0].elapsed_time(b2b[1]) * 1e-3 / args.steps
@@ -198,7 +215,7 @@ def main():
     quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     step_ms = wall * 1e3 / args.steps
-    ops = 2.0 * M * N * K
+    ops = 2.0 * R * N * K
 
     gemm_mean_s = float(gemm_ms.mean()) * 1e-3
     quant_mean_s = float(quant_ms.mean()) * 1e-3
@@ -220,6 +237,7 @@ def main():
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": wl.name, "fmt": datagen.FMT_NAMES[fmt], "M": M, "N": N, "K": K,
+                   **({"experts": wl.experts, "topk": wl.topk, "routed_rows": R} if wl.experts else {}),
                    "seed": wl.seed, "note": wl.note},
         "tok_per_s": round(M / (step_ms * 1e-3), 1),
         "gemm": {"mean_us": round(gemm_mean_s * 1e6, 2),
@@ -237,10 +255,10 @@ def main():
                      "frac_hbm": round((x_bytes + a_bytes) / quant_mean_s / 1e9 / PEAK_HBM_GBS,
                                        4)},
         "dispatch": kq.dispatch_counts(),
-        "kernel_source_sha256_16": kernel_source_hash(datagen.FMT_NAMES[fmt]),
+        "kernel_source_sha256_16": kernel_source_hash(src_key),
     }
-    traffic = measured_traffic(wl.name, datagen.FMT_NAMES[fmt])
-    if M >= 256:
+    traffic = measured_traffic(wl.name, src_key)
+    if R >= 256:
         tops = ops / gemm_b2b_s / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": round(tops, 2),
                               "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
@@ -250,7 +268,8 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                               "traffic": traffic}
-    result["roofline"]["kernel"] = kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K))
+    result["roofline"]["kernel"] = ("gemm_id_128x128" if wl.experts
+                                    else kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)))
 
     if not args.no_calib:
         # the device's own rates, measured now: the GEMM's fraction of them
@@ -305,6 +324,18 @@ def calibrate(kq, stream):
 
 
 def cpu_baseline(wl, W_np, x_np, out_dev, target_s):
+    import datagen
+    if wl.experts:
+        # expert-indexed: the sample is expert 0 (its tokens and its weights),
+        # against the GPU's routed rows of expert 0
+        off, toks = datagen.draw_routing(wl.M, wl.experts, wl.topk, wl.seed)
+        t0 = toks[off[0]:off[1]]
+        return _cpu_baseline(wl, wl.name + " expert 0", W_np[:wl.N], x_np[t0],
+                             out_dev[int(off[0]):int(off[1])], target_s)
+    return _cpu_baseline(wl, wl.name, W_np, x_np, out_dev, target_s)
+
+
+def _cpu_baseline(wl, label, W_np, x_np, out_dev, target_s):
     """The plain CPU oracle (fp32 Q8 quantize, fp64 dequantize-and-multiply) on
     a bounded sample of the workload: all tokens against a random subset of
     weight rows, sized to about target_s seconds of CPU time.  The quantize
@@ -337,7 +368,8 @@ def cpu_baseline(wl, W_np, x_np, out_dev, target_s):
     t = time.perf_counter()
     kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=rows, want_tol=False)
     tg = time.perf_counter() - t
-    ops = 2.0 * wl.M * nrows * wl.K
+    Mx = x_np.shape[0]
+    ops = 2.0 * Mx * nrows * wl.K
     t_sample = tg + tq * nrows / wl.N
     check = rows[:: max(1, nrows // 8)][:8]
     ref, tol = kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=check)
@@ -346,7 +378,7 @@ def cpu_baseline(wl, W_np, x_np, out_dev, target_s):
     ratio = float((np.abs(got.astype(np.float64) - ref) / tol).max())
     return {"value": round(ops / t_sample / 1e12, 6), "unit": "TOPS", "cores": cores,
             "kind": "oracle",
-            "sample": f"{wl.name}: all {wl.M} tokens x {nrows} of {wl.N} weight rows (random), "
+            "sample": f"{label}: all {Mx} tokens x {nrows} of {wl.N} weight rows (random), "
                       f"K={wl.K}; plain C oracle (fp32 Q8 quantize + fp64 "
                       f"dequantize-and-multiply), gcc -O2 -fopenmp; quantize {tq:.2f} s for all "
                       f"rows (charged pro rata), multiply {tg:.2f} s",

@@ -49,6 +49,8 @@ class Workload:
     seed: int
     dist: str          # "plain" or "outlier_lognormal"
     note: str
+    experts: int = 0   # > 0: an expert-indexed product over this many experts
+    topk: int = 0      # experts per token
 
 
 WORKLOADS = {
@@ -76,6 +78,10 @@ WORKLOADS = {
     "tern_5120_1": Workload("tern_5120_1", TQ, 1, 17408, 5120, 1005,
                             "plain", "ternary x Q8_128, one token (decode; first token row "
                             "of the 2048-token draw), 17408x5120"),
+    "moe_q4k_8x2_512": Workload("moe_q4k_8x2_512", Q4_K, 512, 14336, 4096, 1006, "plain",
+                                "Q4_K x Q8_K expert-indexed FFN gate/up: 8 experts of 14336x4096, "
+                                "512 tokens routed to 2 experts each (1024 routed rows)",
+                                experts=8, topk=2),
     "tern2_5120_2048": Workload("tern2_5120_2048", TQ2, 2048, 17408, 5120, 1005,
                                 "plain", "ternary at two bits per weight x Q8_128, 2048 "
                                 "tokens, 17408x5120 (the same trits as tern_5120_2048)"),
@@ -286,6 +292,21 @@ def encode_tq2(t: np.ndarray, d: np.ndarray) -> np.ndarray:
 # Whole workloads
 # ----------------------------------------------------------------------------
 
+def draw_routing(M: int, experts: int, topk: int, seed: int):
+    """Synthetic top-k routing: each token picks topk distinct experts
+    uniformly.  Returns int32 expert offsets [experts + 1] and the token of
+    each routed row [M * topk], grouped by expert (tokens ascending within an
+    expert)."""
+    _, _, gx = _streams(seed)
+    choice = np.argsort(gx.random((M, experts)), axis=1)[:, :topk]     # [M][topk]
+    tok = np.repeat(np.arange(M), topk)
+    exp = choice.reshape(-1)
+    order = np.lexsort((tok, exp))
+    counts = np.bincount(exp, minlength=experts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return off, tok[order].astype(np.int32)
+
+
 def make_weights(fmt: int, N: int, K: int, seed: int, dist: str = "plain") -> np.ndarray:
     """Stored weight blocks uint8 [N][K/QK*block_bytes] for a seeded draw."""
     if fmt == Q4_K:
@@ -311,7 +332,8 @@ def make_workload(wl: Workload | str, n_rows: int | None = None, m_rows: int | N
     equals the same rows of the full problem)."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
-    W = make_weights(wl.fmt, wl.N, wl.K, wl.seed, wl.dist)
+    # an expert-indexed workload: experts x N consecutive weight rows
+    W = make_weights(wl.fmt, wl.N * max(wl.experts, 1), wl.K, wl.seed, wl.dist)
     full_rows = 2048 if wl.name in _PREFIX_OF_2048 else wl.M
     x = draw_activations(wl.M, wl.K, wl.seed, wl.dist, rows=full_rows)
     if n_rows is not None:
