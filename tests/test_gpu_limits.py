@@ -130,3 +130,35 @@ def test_output_just_below_2gib(kq, fmt):
     # the last output row, every column: the end of the buffer
     last = out[M - 1].cpu().numpy()
     assert np.all(np.isfinite(last))
+
+
+def test_gemm_id_experts_beyond_2gib(kq):
+    """Four Q4_K experts of about 0.9 GiB each: the last ones start past 2^31
+    bytes into W (the per-expert base is 64-bit; each expert's own offsets stay
+    32-bit).  A few routed rows per expert, sampled weight rows checked."""
+    fmt, E, K = Q4_K, 4, 4096
+    rowbytes = (K // 256) * 144
+    N = 400_000
+    assert E * N * rowbytes > LIMIT and (N + 256) * rowbytes < LIMIT
+    say(f"gemm_id: {E} experts x {N * rowbytes / 2**30:.2f} GiB")
+    W = random_blocks(fmt, E * N * (K // 256), 900).reshape(E * N, rowbytes)
+    rng = np.random.default_rng(901)
+    M = 12
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    a_q8, qs, d = quantize(kq, fmt, x)
+    counts = [3, 5, 4, 6]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = rng.integers(0, M, size=int(off[-1])).astype(np.int32)
+    R = int(off[-1])
+    out = torch.full((R, N), float("nan"), dtype=torch.float32, device=DEV)
+    kq.kq_gemm_id(fmt, torch.from_numpy(W).to(DEV), E, a_q8, M, N, K,
+                  torch.from_numpy(off).to(DEV), torch.from_numpy(rows).to(DEV), R, out)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 6, replace=False)]))
+    got = out[:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        toks = rows[r0:r1]
+        ref, tol = kqref.gemm(fmt, W[e * N:(e + 1) * N], np.ascontiguousarray(qs[toks]),
+                              np.ascontiguousarray(d[toks]), K, rows=cols)
+        check_columns(got[r0:r1], ref, tol, f"gemm_id expert {e}")
