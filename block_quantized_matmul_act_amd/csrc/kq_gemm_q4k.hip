@@ -51,13 +51,19 @@
 namespace kq {
 namespace q4w {
 
-constexpr int BM = 128, BN = 128, NWAVE = 4, NT = 64 * NWAVE;
-constexpr int MT = BM / 32;           // 32-row m-tiles per wave
+constexpr int BN = 128, NWAVE = 4, NT = 64 * NWAVE;
 constexpr int ROW = 256;              // LDS bytes per staged activation row
-constexpr int ABUF = BM * ROW;        // staged activation values of one superblock
 constexpr int BB = 144;               // Q4_K block bytes
-constexpr int LBUF = 2 * BM * 16;     // staged min-term operands (hi, lo) of one superblock
-constexpr int WG_PER_CU = 2;          // two workgroups (eight waves) share a CU
+// Tile heights: 128 rows (four 32-row m-tiles per wave), or 64 rows for
+// shapes whose 128-row tiles would leave CUs idle.
+template <int BM>
+struct TileCfg {
+    static constexpr int MT = BM / 32;                   // 32-row m-tiles per wave
+    static constexpr int ABUF = BM * ROW;                // staged activation values of one superblock
+    static constexpr int DBUF = 2 * BM > 256 ? 2 * BM : 256;  // staged scales (a 1 KiB copy lands here)
+    static constexpr int LBUF = 2 * BM * 16;             // staged min-term operands (hi, lo)
+    static constexpr int WG_PER_CU = 2;                   // workgroups sharing a CU
+};
 constexpr int RSRC_FLAGS = 0x00020000;
 // A store offset the buffer range check always drops: the host checks that
 // every row offset, overhanging tile rows included, stays below 2^31, so
@@ -177,6 +183,7 @@ __device__ __forceinline__ void lds_wait_n(int n, R &r) {
 struct TileXY {
     int m0, n0;
 };
+template <int BM>
 __device__ __forceinline__ TileXY tile_xy(const Args &a, int t) {
     constexpr int GM = 4;
     const int per_group = GM * a.tiles_n;
@@ -199,10 +206,13 @@ struct WRaw {
     v4i hdr, q[4];
 };
 
-__global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) int8_t s_a0[ABUF], s_a1[ABUF];
-    __shared__ __attribute__((aligned(16))) float s_d0[2 * BM], s_d1[2 * BM];
-    __shared__ __attribute__((aligned(16))) int8_t s_l0[LBUF], s_l1[LBUF];
+template <int BM>
+__global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Args a) {
+    using TC = TileCfg<BM>;
+    constexpr int MT = TC::MT;
+    __shared__ __attribute__((aligned(16))) int8_t s_a0[TC::ABUF], s_a1[TC::ABUF];
+    __shared__ __attribute__((aligned(16))) float s_d0[TC::DBUF], s_d1[TC::DBUF];
+    __shared__ __attribute__((aligned(16))) int8_t s_l0[TC::LBUF], s_l1[TC::LBUF];
     const Slot slots[2] = {{s_a0, s_d0, s_l0}, {s_a1, s_d1, s_l1}};
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -239,20 +249,27 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     // Each wave also copies a quarter of the min-term operands (1 KiB: part
     // w/2, rows 64*(w%2)..), and wave 0 the scales (one 1 KiB copy).
     const int st_row = lane >> 4, st_pos = lane & 15;
-    // copy i covers rows 32w + 4i + l/16: its piece index is
-    // (l%16) ^ (4i + l/16), i.e. base ^ (64*(i%4)) in bytes (K is a multiple
-    // of 256, so the XOR stays inside the row), and copies i, i+4 are 16 rows
-    // (16*K bytes) apart
-    const int a_vbase = (32 * wave + st_row) * K + 16 * (st_pos ^ st_row);
-    const int l_voff = 16 * lane + (wave & 1) * 1024;  // 16 * lane for wave 0
+    // copy i covers rows (BM/4)w + 4(i%4) + 16(i/4) + l/16: its piece index
+    // is (l%16) ^ (4(i%4) + l/16), i.e. base ^ (64*(i%4)) in bytes (K is a
+    // multiple of 256, so the XOR stays inside the row), and copies i, i+4 are
+    // 16 rows (16*K bytes) apart
+    constexpr int CPW = BM / 16;  // value copies per wave
+    const int a_vbase = ((BM / 4) * wave + st_row) * K + 16 * (st_pos ^ st_row);
+    const int l_voff = 16 * lane + (BM == 128 ? (wave & 1) * 1024 : 0);  // 16 * lane for wave 0
     auto stage = [&](const Slot &S, TileXY T, int sbx) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            copy16(rs_a, S.a + (8 * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
+        for (int i = 0; i < CPW; ++i)
+            copy16(rs_a, S.a + (CPW * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
                    (T.m0 + 4 * (i & 3) + 16 * (i >> 2)) * K + sbx * ROW);
-        const int c = wave;  // min-term operands: part c/2, rows 64*(c%2) .. +64
-        copy16(rs_l, S.l + c * 1024, l_voff, ((sbx * 2 + (c >> 1)) * M + T.m0) * 16);
-        // scales of rows m0..m0+127 (lanes 32..63 fill an unused upper half)
+        if constexpr (BM == 128) {
+            const int c = wave;  // min-term operands: part c/2, rows 64*(c%2) .. +64
+            copy16(rs_l, S.l + c * 1024, l_voff, ((sbx * 2 + (c >> 1)) * M + T.m0) * 16);
+        } else if (wave < 2) {
+            // min-term operands: part w, all 64 rows
+            copy16(rs_l, S.l + wave * 1024, l_voff, ((sbx * 2 + wave) * M + T.m0) * 16);
+        }
+        // scales of rows m0..m0+BM-1 (the rest of the 1 KiB copy fills an
+        // unused part of the slot)
         if (wave == 0) copy16(rs_d, S.d, l_voff, (sbx * M + T.m0) * 4);
     };
 
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
     // (k, sb): tile index in this workgroup's list and superblock of the
     // current iteration; T = tile k, TN = tile k+1 (computed once per tile)
     int k = 0, sb = 0;
-    TileXY T = tile_xy(a, slot_in_step), TN = tile_xy(a, slot_in_step + G);
+    TileXY T = tile_xy<BM>(a, slot_in_step), TN = tile_xy<BM>(a, slot_in_step + G);
 
     auto iteration = [&](auto PP, int it) {
         constexpr int P = decltype(PP)::value;
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void gemm_q4k_kernel(Args a) {
             ++k;
             sb = 0;
             T = TN;
-            TN = tile_xy(a, slot_in_step + (k + 1) * G);
+            TN = tile_xy<BM>(a, slot_in_step + (k + 1) * G);
         } else {
             ++sb;
         }
@@ -986,13 +1003,18 @@ constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
 
 // Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
 // kernel; up to 64 -> the K-split weight-streaming kernel; otherwise the
-// 128 x 128 persistent kernel (two per CU).
+// persistent tile kernel (two workgroups per CU), 128 x 128 when that tiling
+// has more tiles than the chip has CUs (256), else 64 x 128: below that the
+// taller tile leaves CUs idle, above it the shorter tile's extra unpacking
+// (twice the weight work per output) and tail cost more than they gain.
+constexpr int TILE64_MAX_TILES128 = 256;
 int q4k_kernel_choice(int M, int N, int K) {
-    (void)N;
     if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
-    return M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
+    if (M <= 64) return Q4K_FEW_TOKENS;
+    const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    return tiles128 > TILE64_MAX_TILES128 ? Q4K_TILE128 : Q4K_TILE64;
 }
 
 hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
@@ -1022,10 +1044,12 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.N = N;
     a.K = K;
     a.nsb = K / 256;
-    a.tiles_m = (M + q4w::BM - 1) / q4w::BM;
+    const int choice = q4k_kernel_choice(M, N, K);
+    const int bm = choice == Q4K_TILE64 ? 64 : 128;
+    a.tiles_m = (M + bm - 1) / bm;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
-    switch (q4k_kernel_choice(M, N, K)) {
+    switch (choice) {
         case Q4K_MATVEC: {
             const dim3 grid((unsigned)((N + q4w::mv::RPG - 1) / q4w::mv::RPG)), block(64 * q4w::mv::NW);
             const int mt = mv_tokens(M);
@@ -1044,9 +1068,14 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                 hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<2, Q4S_DA2, Q4S_DW2>),
                                    dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
             break;
+        case Q4K_TILE64: {
+            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * g_num_cus);
+            hipLaunchKernelGGL(q4w::gemm_q4k_kernel<64>, dim3(grid), dim3(q4w::NT), 0, stream, a);
+            break;
+        }
         default: {
-            const unsigned grid = (unsigned)min(a.ntiles, q4w::WG_PER_CU * g_num_cus);
-            hipLaunchKernelGGL(q4w::gemm_q4k_kernel, dim3(grid), dim3(q4w::NT), 0, stream, a);
+            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<128>::WG_PER_CU * g_num_cus);
+            hipLaunchKernelGGL(q4w::gemm_q4k_kernel<128>, dim3(grid), dim3(q4w::NT), 0, stream, a);
             break;
         }
     }

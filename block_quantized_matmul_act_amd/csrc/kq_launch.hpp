@@ -23,8 +23,9 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
 
 // Q4_K kernels: one or two tokens with K a multiple of 2048 (and the staged
 // activations within the LDS budget) -> matrix-vector kernel; M <= 64 ->
-// few-token kernel; otherwise the 128 x 128 persistent kernel.
-enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1, Q4K_MATVEC = 2 };
+// few-token kernel; otherwise the persistent tile kernel, 128 x 128 or (for
+// shapes of at most 256 such tiles) 64 x 128.
+enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1, Q4K_MATVEC = 2, Q4K_TILE64 = 3 };
 int q4k_kernel_choice(int M, int N, int K);
 
 }  // namespace kq

@@ -217,24 +217,27 @@ def q4k_term_sizes(W: np.ndarray, N: int, K: int) -> np.ndarray:
     return out
 
 
-# (fmt, K, variant, token rows per launch)
+# (fmt, K, variant, token rows per launch, weight rows); the 128 x 128 Q4_K
+# kernel takes shapes of more than 256 such tiles, hence its 2100 weight rows
 IDENTITY_CASES = [
-    (Q4_K, 2048, "gemm_q4_k_matvec", 2),
-    (Q4_K, 2048, "gemm_q4_k_m64", 64),
-    (Q4_K, 2048, "gemm_q4_k_128x128", 2048),
-    (Q6_K, 2048, "gemm_q6_k_matvec", 8),
-    (Q6_K, 2048, "gemm_q6_k_128x128", 2048),
-    (TQ, 1024, "gemm_tq_matvec", 8),
-    (TQ, 1024, "gemm_tq_128x128", 1024),
-    (TQ2, 1024, "gemm_tq2_128x128", 8),
-    (TQ2, 1024, "gemm_tq2_128x128", 1024),
+    (Q4_K, 2048, "gemm_q4_k_matvec", 2, 72),
+    (Q4_K, 2048, "gemm_q4_k_m64", 64, 72),
+    (Q4_K, 2048, "gemm_q4_k_64x128", 2048, 72),
+    (Q4_K, 2048, "gemm_q4_k_128x128", 2048, 2100),
+    (Q6_K, 2048, "gemm_q6_k_matvec", 8, 72),
+    (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 72),
+    (TQ, 1024, "gemm_tq_matvec", 8, 72),
+    (TQ, 1024, "gemm_tq_128x128", 1024, 72),
+    (TQ2, 1024, "gemm_tq2_128x128", 8, 72),
+    (TQ2, 1024, "gemm_tq2_128x128", 1024, 72),
 ]
 
 
-@pytest.mark.parametrize("fmt,K,variant,MT", IDENTITY_CASES,
+@pytest.mark.parametrize("fmt,K,variant,MT,N", IDENTITY_CASES,
                          ids=[c[2] for c in IDENTITY_CASES])
-def test_identity_activations_decode_every_position(kq, fmt, K, variant, MT):
-    N = 72                       # two and a bit 32-row groups: a ragged column tile
+def test_identity_activations_decode_every_position(kq, fmt, K, variant, MT, N):
+    # N = 72: two and a bit 32-row groups, a ragged column tile; N = 2100:
+    # 16 full column tiles and a ragged one
     W = finite_weights(fmt, N, K, 300 + fmt)
     ref = kqref.dequant_rows(fmt, W, K).T            # out[m][n] = W^[n][m]
     Wd = dev(W)

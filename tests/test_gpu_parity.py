@@ -255,6 +255,23 @@ def test_large_ragged_tiles(kq, workloads):
     say(f"  max err/tol {r:.3g}")
 
 
+def test_q4k_tile_heights(kq):
+    """The Q4_K tile kernel in both heights at shapes ragged in M and N: 128 x
+    128 (a shape of more than 256 such tiles: 3 x 86) and 64 x 128 just below
+    that count (3 x 85), with a short K so the full output is compared."""
+    K = 512
+    W = datagen.make_weights(Q4_K, 11000, K, 4848)
+    x = datagen.draw_activations(300, K, 4949)
+    for M, N, name in ((300, 11000, "gemm_q4_k_128x128"), (300, 10880, "gemm_q4_k_64x128"),
+                       (65, 4000, "gemm_q4_k_64x128"), (129, 200, "gemm_q4_k_64x128")):
+        v = kq.kq_select_variant(Q4_K, M, N, K)
+        assert kq.kq_variant_name(v) == name, (M, N)
+        say(f"q4k tile {name} M={M} N={N} K={K}")
+        before = kq.kq_dispatch_count(v)
+        gemm_vs_oracle(kq, Q4_K, np.ascontiguousarray(W[:N]), np.ascontiguousarray(x[:M]), M, N, K)
+        assert kq.kq_dispatch_count(v) == before + 1
+
+
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 5, 8)),
           TQ: ("gemm_tq_matvec", (1, 2, 3, 5, 8))}
 
