@@ -58,8 +58,9 @@ GEMM_SOURCES = {
     "q6_k": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     "tq": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     "tq2": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
-    # expert-indexed workloads (any format) run the tile kernel of kq_gemm.hip
-    "moe": ("kq_gemm.hip", "kq_device.hpp", "kq_hooks.hpp"),
+    # expert-indexed workloads: the gather mode of the Q4_K tile kernel
+    # (kq_gemm_q4k.hip) or of the other formats' tile kernel (kq_gemm.hip)
+    "moe": ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp", "kq_hooks.hpp"),
 }
 
 
@@ -268,8 +269,11 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                               "traffic": traffic}
-    result["roofline"]["kernel"] = ("gemm_id_128x128" if wl.experts
-                                    else kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)))
+    if wl.experts:  # the expert-indexed variant this run dispatched
+        disp = kq.dispatch_counts()
+        result["roofline"]["kernel"] = max((v for v in disp if v.startswith("gemm_id")), key=disp.get)
+    else:
+        result["roofline"]["kernel"] = kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K))
 
     if not args.no_calib:
         # the device's own rates, measured now: the GEMM's fraction of them

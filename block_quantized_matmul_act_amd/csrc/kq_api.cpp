@@ -32,6 +32,7 @@ enum Variant {
     V_SUBSUMS_TQ2,
     V_GEMM_ID_128x128,
     V_GEMM_Q4K_64x128,
+    V_GEMM_ID_Q4K_64x128,
     V_COUNT
 };
 
@@ -39,6 +40,7 @@ const char *const kVariantNames[V_COUNT] = {
     "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
     "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
     "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",   "gemm_id_128x128", "gemm_q4_k_64x128",
+    "gemm_id_q4_k_64x128",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -248,18 +250,23 @@ int kq_gemm_id(int fmt, const void *W, int64_t n_experts, const void *a_q8, int6
     if ((N + 256) * rowbytes >= lim || M * K >= lim || (K / qk_of(fmt)) * M * 4 >= lim ||
         (K / 256) * 2 * M * 16 >= lim)
         return KQ_ERR_UNSUPPORTED;
-    const int64_t tiles = ((R + 127) / 128 + n_experts) * ((N + 127) / 128);
+    const int64_t tiles = ((R + 63) / 64 + n_experts) * ((N + 127) / 128);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
     ActLayout L;
     act_layout(kq_act_fmt_for(fmt), M, K, &L);
     const char *base = static_cast<const char *>(a_q8);
-    hipError_t e = kq::launch_gemm_id(
-        fmt, W, (int)n_experts, N * rowbytes, reinterpret_cast<const int8_t *>(base),
-        reinterpret_cast<const float *>(base + L.d),
-        L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr, expert_offsets, rows,
-        (int)R, out, (int)M, (int)N, (int)K, stream);
+    const int8_t *qs = reinterpret_cast<const int8_t *>(base);
+    const float *da = reinterpret_cast<const float *>(base + L.d);
+    const uint16_t *alpha = L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr;
+    const bool q4k_tile = fmt == KQ_Q4_K && kq::q4k_id_tile_ok((int)N, (int)K);
+    hipError_t e = q4k_tile ? kq::launch_gemm_q4k_id(W, (int)n_experts, N * rowbytes, qs, da, alpha,
+                                                     expert_offsets, rows, (int)R, out, (int)M, (int)N,
+                                                     (int)K, stream)
+                            : kq::launch_gemm_id(fmt, W, (int)n_experts, N * rowbytes, qs, da, alpha,
+                                                 expert_offsets, rows, (int)R, out, (int)M, (int)N,
+                                                 (int)K, stream);
     if (e != hipSuccess) return KQ_ERR_HIP;
-    g_count[V_GEMM_ID_128x128].fetch_add(1);
+    g_count[q4k_tile ? V_GEMM_ID_Q4K_64x128 : V_GEMM_ID_128x128].fetch_add(1);
     return KQ_OK;
 }
 

@@ -44,6 +44,7 @@
 // is 16 registers per lane: register r of lane l holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 #include "kq_device.hpp"
+#include "kq_hooks.hpp"
 #include "kq_launch.hpp"
 
 #include <type_traits>
@@ -79,6 +80,13 @@ struct Args {
     const uint16_t *alpha;   // [nsb][2][M][8] bf16
     float *out;
     int M, N, K, nsb, tiles_m, tiles_n, ntiles;
+    // expert-indexed product only: out has n_routed rows, routed row r
+    // multiplies token rows[r] by the weights of the expert e with
+    // exp_off[e] <= r < exp_off[e+1] (at W + e * expert_bytes); tiles_m is an
+    // upper bound, the kernel counts the real M-tiles
+    const int32_t *exp_off, *rows;
+    int n_experts, n_routed;
+    int64_t expert_bytes;
 };
 
 __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
@@ -180,17 +188,52 @@ __device__ __forceinline__ void lds_wait_n(int n, R &r) {
 }
 
 // Tile t of the grouped order: GM M-tiles down, then across N.
+// Expert-indexed tiles also carry the expert e, the first routed row grb
+// and the number of routed rows mrows (0..BM) the tile holds.
 struct TileXY {
-    int m0, n0;
+    int m0, n0, e, grb, mrows;
 };
-template <int BM>
-__device__ __forceinline__ TileXY tile_xy(const Args &a, int t) {
+// rows routed to expert x (clamped: routing that breaks its contract gives
+// wrong values, never an access outside the buffers)
+__device__ __forceinline__ int expert_rows(const Args &a, int x) {
+    const int64_t c = (int64_t)a.exp_off[x + 1] - a.exp_off[x];
+    return (int)min(max(c, (int64_t)0), (int64_t)a.n_routed);
+}
+template <int BM, bool GATHER>
+__device__ __forceinline__ TileXY tile_xy(const Args &a, int tiles_m, int t) {
     constexpr int GM = 4;
     const int per_group = GM * a.tiles_n;
     const int first_m = (t / per_group) * GM;
-    const int gsize = min(a.tiles_m - first_m, GM);
+    const int gsize = min(tiles_m - first_m, GM);
     const int r = t % per_group;
-    return {(first_m + r % gsize) * BM, (r / gsize) * BN};
+    const int tm = first_m + r % gsize, n0 = (r / gsize) * BN;
+    if constexpr (!GATHER) {
+        return {tm * BM, n0, 0, 0, 0};
+    } else {
+        // M-tile tm is tile mt of expert e, counting each expert's
+        // ceil(rows / BM) tiles in expert order
+        int e = 0, mt = 0, acc = 0;
+        bool found = false;
+        for (int x = 0; x < a.n_experts; ++x) {
+            const int te = (expert_rows(a, x) + BM - 1) / BM;
+            if (tm < acc + te) {
+                e = x;
+                mt = tm - acc;
+                found = true;
+                break;
+            }
+            acc += te;
+        }
+        int grb = a.exp_off[e] + mt * BM;
+        int mrows = 0;
+        if (found && grb >= 0 && grb < a.n_routed)
+            mrows = min(min(a.exp_off[e + 1], a.n_routed) - grb, BM);
+        if (mrows <= 0) {
+            mrows = 0;
+            grb = 0;
+        }
+        return {0, n0, e, grb, mrows};
+    }
 }
 
 // One staging slot: distinct LDS arrays per slot, so the compiler can tell
@@ -206,8 +249,9 @@ struct WRaw {
     v4i hdr, q[4];
 };
 
-template <int BM>
+template <int BM, bool GATHER = false>
 __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Args a) {
+    static_assert(!GATHER || BM == 64, "gather mode stages one routed row per lane");
     using TC = TileCfg<BM>;
     constexpr int MT = TC::MT;
     __shared__ __attribute__((aligned(16))) int8_t s_a0[TC::ABUF], s_a1[TC::ABUF];
@@ -228,7 +272,14 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     const int G = gridDim.x, b = blockIdx.x;
     const int per_xcd = G >> 3;
     const int slot_in_step = (per_xcd > 0 && b < 8 * per_xcd) ? ((b & 7) * per_xcd + (b >> 3)) : b;
-    const int my_tiles = (a.ntiles - slot_in_step + G - 1) / G;  // tiles slot, slot+G, ...
+    int tiles_m = a.tiles_m;
+    if constexpr (GATHER) {
+        int acc = 0;
+        for (int x = 0; x < a.n_experts; ++x) acc += (expert_rows(a, x) + BM - 1) / BM;
+        tiles_m = min(acc, a.tiles_m);
+    }
+    const int ntiles = tiles_m * a.tiles_n;
+    const int my_tiles = (ntiles - slot_in_step + G - 1) / G;    // tiles slot, slot+G, ...
     const int total = my_tiles * nsb;                            // flat iterations
     const int rowbytes = nsb * BB;
     if (total <= 0) return;  // uniform: no barrier is ever reached
@@ -242,6 +293,20 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+    // expert-indexed: the weights of the tile's expert, and its output rows
+    // (the range ends at the tile's last routed row, so stores past it drop)
+    auto rs_w_of = [&](const TileXY &T) {
+        if constexpr (!GATHER) return rs_w;
+        else
+            return __builtin_amdgcn_make_buffer_rsrc((void *)(a.W + (int64_t)T.e * a.expert_bytes), (short)0,
+                                                     N * rowbytes, RSRC_FLAGS);
+    };
+    auto rs_o_of = [&](const TileXY &T) {
+        if constexpr (!GATHER) return rs_o;
+        else
+            return __builtin_amdgcn_make_buffer_rsrc((void *)(a.out + (int64_t)T.grb * N), (short)0,
+                                                     T.mrows * N * 4, RSRC_FLAGS);
+    };
 
     // ---- staging of one superblock of activations: buffer -> LDS copies ----
     // Values: 1 KiB copy c holds rows 4c..4c+3; lane l fills position l%16 of
@@ -256,7 +321,34 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     constexpr int CPW = BM / 16;  // value copies per wave
     const int a_vbase = ((BM / 4) * wave + st_row) * K + 16 * (st_pos ^ st_row);
     const int l_voff = 16 * lane + (BM == 128 ? (wave & 1) * 1024 : 0);  // 16 * lane for wave 0
-    auto stage = [&](const Slot &S, TileXY T, int sbx) {
+    // Expert-indexed: the same copies with per-lane offsets of gathered token
+    // rows: ga[i] for value copy i (row 16w + 4i + l/16, piece as above), gd
+    // = 4 * token of tile row l (scales: one 4-byte copy per row; min-term
+    // operands: 16 bytes per row).  Rows past the tile's last routed row
+    // repeat it; indices are clamped into rows[] and the activation buffer.
+    struct GOff {
+        int ga[CPW], gd;
+    };
+    auto token = [&](const TileXY &T, int r) {
+        const int idx = min(max(T.grb + min(r, T.mrows - 1), 0), a.n_routed - 1);
+        return min(max(a.rows[idx], 0), M - 1);
+    };
+    auto goffs = [&](const TileXY &T, GOff &o) {
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+                o.ga[i] = token(T, (BM / 4) * wave + 4 * i + st_row) * K + 16 * (st_pos ^ (4 * i + st_row));
+            o.gd = 4 * token(T, lane);
+        }
+    };
+    auto stage = [&](const Slot &S, TileXY T, int sbx, const GOff &o) {
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) copy16(rs_a, S.a + (CPW * wave + i) * 1024, o.ga[i], sbx * ROW);
+            if (wave < 2) copy16(rs_l, S.l + wave * 1024, 4 * o.gd, (sbx * 2 + wave) * M * 16);
+            if (wave == 0) copy4(rs_d, S.d, o.gd, sbx * M * 4);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
             copy16(rs_a, S.a + (CPW * wave + i) * 1024, a_vbase ^ (64 * (i & 3)),
@@ -279,9 +371,10 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     const int w_nib = w_row + 64 * g;
     auto load_w = [&](TileXY T, int sbx, WRaw &R) {
         const int so = T.n0 * rowbytes + sbx * BB;
-        R.hdr = ld16(rs_w, w_row, so);
+        const auto rw = rs_w_of(T);
+        R.hdr = ld16(rw, w_row, so);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rs_w, w_nib, so + 16 + 16 * i);
+        for (int i = 0; i < 4; ++i) R.q[i] = ld16(rw, w_nib, so + 16 + 16 * i);
     };
 
     // ---- fragment addressing: row 32t + ln, piece p(g, s) swizzled by row ----
@@ -309,7 +402,11 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     // (k, sb): tile index in this workgroup's list and superblock of the
     // current iteration; T = tile k, TN = tile k+1 (computed once per tile)
     int k = 0, sb = 0;
-    TileXY T = tile_xy<BM>(a, slot_in_step), TN = tile_xy<BM>(a, slot_in_step + G);
+    TileXY T = tile_xy<BM, GATHER>(a, tiles_m, slot_in_step);
+    TileXY TN = tile_xy<BM, GATHER>(a, tiles_m, slot_in_step + G);
+    GOff oT, oN;  // gathered offsets of tiles T and TN (expert-indexed only)
+    goffs(T, oT);
+    goffs(TN, oN);
 
     auto iteration = [&](auto PP, int it) {
         constexpr int P = decltype(PP)::value;
@@ -328,7 +425,13 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
         const WRaw &wc = wring[P];
         __builtin_amdgcn_sched_barrier(0);
         if (more) {
-            stage(slots[1 - P], Tn, sbn);
+            GOff on;
+            if constexpr (GATHER) {
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) on.ga[i] = last_sb ? oN.ga[i] : oT.ga[i];
+                on.gd = last_sb ? oN.gd : oT.gd;
+            }
+            stage(slots[1 - P], Tn, sbn, on);
             load_w(Tn, sbn, wring[1 - P]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -438,6 +541,8 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
             // are dropped; columns past N are sent out of range
             const int n = T.n0 + 32 * wave + ln;
             const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
+            const auto ro = rs_o_of(T);
+            const int orow0 = GATHER ? 0 : T.m0;
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 // cast the whole vector: storing a bit-cast of one element
@@ -446,7 +551,7 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
-                    __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, (T.m0 + row) * N * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(bits[r], ro, voff, (orow0 + row) * N * 4, 0);
                 }
             }
 #pragma unroll
@@ -457,14 +562,18 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
             ++k;
             sb = 0;
             T = TN;
-            TN = tile_xy<BM>(a, slot_in_step + (k + 1) * G);
+            TN = tile_xy<BM, GATHER>(a, tiles_m, slot_in_step + (k + 1) * G);
+            if constexpr (GATHER) {
+                oT = oN;
+                goffs(TN, oN);
+            }
         } else {
             ++sb;
         }
     };
 
     // prologue: stage iteration 0, its weights
-    stage(slots[0], T, 0);
+    stage(slots[0], T, 0, oT);
     load_w(T, 0, wring[0]);
     for (int it = 0; it < total; it += 2) {
         iteration(std::integral_constant<int, 0>{}, it);
@@ -1017,9 +1126,7 @@ int q4k_kernel_choice(int M, int N, int K) {
     return tiles128 > TILE64_MAX_TILES128 ? Q4K_TILE128 : Q4K_TILE64;
 }
 
-hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
-                           const uint16_t *alpha, float *out, int M, int N, int K,
-                           hipStream_t stream) {
+static void init_num_cus() {
     if (g_num_cus <= 0) {
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -1028,6 +1135,46 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             cus = 256;
         g_num_cus = cus;
     }
+}
+
+bool q4k_id_tile_ok(int N, int K) {
+    // per-tile output offsets (64 rows of N floats) stay below 2^31
+    return K > 0 && (int64_t)64 * N * 4 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes, const int8_t *qs,
+                              const float *da, const uint16_t *alpha, const int32_t *exp_off,
+                              const int32_t *rows, int R, float *out, int M, int N, int K,
+                              hipStream_t stream) {
+    init_num_cus();
+    q4w::Args a;
+    a.W = static_cast<const uint8_t *>(W);
+    a.qs = qs;
+    a.da = da;
+    a.alpha = alpha;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nsb = K / 256;
+    // upper bound on the M-tiles: each expert's count rounded up to 64 rows
+    a.tiles_m = (R + 63) / 64 + n_experts;
+    a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
+    a.ntiles = a.tiles_m * a.tiles_n;
+    a.exp_off = exp_off;
+    a.rows = rows;
+    a.n_experts = n_experts;
+    a.n_routed = R;
+    a.expert_bytes = expert_bytes;
+    const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * g_num_cus);
+    hipLaunchKernelGGL((q4w::gemm_q4k_kernel<64, true>), dim3(grid), dim3(q4w::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
+                           const uint16_t *alpha, float *out, int M, int N, int K,
+                           hipStream_t stream) {
+    init_num_cus();
     if (K == 0) {
         const int64_t n = (int64_t)M * N;
         hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,

@@ -19,4 +19,13 @@ hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_
                           const int32_t *exp_off, const int32_t *rows, int R, float *out, int M,
                           int N, int K, hipStream_t stream);
 
+// Q4_K expert-indexed product on the register-unpack tile kernel
+// (kq_gemm_q4k.hip, 64-row tiles in gather mode), for shapes where
+// q4k_id_tile_ok(N, K) holds; other shapes take launch_gemm_id.
+bool q4k_id_tile_ok(int N, int K);
+hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes, const int8_t *qs,
+                              const float *da, const uint16_t *alpha, const int32_t *exp_off,
+                              const int32_t *rows, int R, float *out, int M, int N, int K,
+                              hipStream_t stream);
+
 }  // namespace kq

@@ -194,7 +194,11 @@ int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t 
  * MUL_MAT_ID, which the pages test next to MUL_MAT): every routed row r
  * multiplies one expert's weights with one token's quantized activations,
  *   out[r][n] = sum_k W^_e[n][k] * A^[rows[r]][k],  e the expert of row r,
- * through the same loaders and tile kernel as kq_gemm.
+ * through the same loaders and tile kernels as kq_gemm: Q4_K (K > 0 and
+ * N < 2^23) on the register-unpack tile kernel with 64-row tiles, the other
+ * formats and shapes on the 128 x 128 tile kernel, each gathering the token
+ * rows of one expert per tile.  Every routed row gets the bits kq_gemm gives
+ * its token where kq_gemm runs the same tile kernel.
  *   W               device, n_experts consecutive weight tensors of N rows of
  *                   K/QK blocks (expert e starts e * kq_weight_bytes(fmt, N, K)
  *                   bytes in), 16-byte aligned

@@ -31,7 +31,7 @@ struct Rec {
     int calls = 0;
     const void *p[4] = {};
     int64_t n[3] = {};
-} rq, rg, rs, rd, ri;
+} rq, rg, rs, rd, ri, rx;
 }  // namespace
 
 namespace kq {
@@ -83,6 +83,19 @@ hipError_t launch_gemm_id(int, const void *, int n_experts, int64_t expert_bytes
     ri.n[2] = (int64_t)R * 1000000 + M;
     (void)N;
     (void)K;
+    return hipSuccess;
+}
+bool q4k_id_tile_ok(int N, int K) { return K > 0 && (int64_t)64 * N * 4 < ((int64_t)1 << 31); }
+hipError_t launch_gemm_q4k_id(const void *, int n_experts, int64_t expert_bytes, const int8_t *qs, const float *da,
+                              const uint16_t *alpha, const int32_t *, const int32_t *, int R, float *, int M, int,
+                              int, hipStream_t) {
+    ++rx.calls;
+    rx.p[0] = qs;
+    rx.p[1] = da;
+    rx.p[2] = alpha;
+    rx.n[0] = n_experts;
+    rx.n[1] = expert_bytes;
+    rx.n[2] = (int64_t)R * 1000000 + M;
     return hipSuccess;
 }
 hipError_t launch_debug_unpack(int, const void *, int64_t nblocks, int8_t *, int32_t *, hipStream_t) {
@@ -168,6 +181,19 @@ int main() {
     EXPECT(ri.calls == 1 && ri.n[0] == 8 && ri.n[1] == 96 * 2 * 210 && ri.n[2] == 300 * 1000000 + 100);
     EXPECT(ri.p[1] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_D, 100, 512));
     EXPECT(ri.p[2] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, 100, 512));
+    // Q4_K goes to the register-unpack tile kernel's gather mode, with the same
+    // sections; K = 0 stays on the generic path (it writes the zeros)
+    ri = Rec{};
+    rx = Rec{};
+    EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, 96, 512, reinterpret_cast<int32_t *>(A),
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
+    EXPECT(ri.calls == 0 && rx.calls == 1 && rx.n[0] == 8 && rx.n[1] == 96 * 2 * 144 &&
+           rx.n[2] == 300 * 1000000 + 100);
+    EXPECT(rx.p[1] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_D, 100, 512));
+    EXPECT(rx.p[2] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, 100, 512));
+    EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, 96, 0, reinterpret_cast<int32_t *>(A),
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
+    EXPECT(ri.calls == 1 && rx.calls == 1);
     // the loader hook reaches its launcher only with a valid count
     rd = Rec{};
     EXPECT(kq_debug_unpack(KQ_Q4_K, A, 10, reinterpret_cast<int8_t *>(A), reinterpret_cast<int32_t *>(A), s) == KQ_OK);

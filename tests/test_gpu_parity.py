@@ -456,10 +456,11 @@ def test_gemm_id_matches_oracle(kq, fmt):
     qs, d, _ = check_act_exact(kq, act_fmt, x, a_q8)
     say(f"gemm_id fmt={fmt} E={E} M={M} N={N} K={K} R={R}")
     ob = torch.full((R + 3, N), 12345.0, dtype=torch.float32, device=DEV)
-    before = kq.dispatch_counts()["gemm_id_128x128"]
+    variant = "gemm_id_q4_k_64x128" if fmt == Q4_K else "gemm_id_128x128"
+    before = kq.dispatch_counts()[variant]
     kq.kq_gemm_id(fmt, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, ob)
     torch.cuda.synchronize()
-    assert kq.dispatch_counts()["gemm_id_128x128"] == before + 1
+    assert kq.dispatch_counts()[variant] == before + 1
     out = ob.cpu().numpy()
     assert np.all(out[R:] == 12345.0), "rows past R written"
     for e in range(E):
@@ -469,21 +470,23 @@ def test_gemm_id_matches_oracle(kq, fmt):
         toks = rows[r0:r1]
         ref, tol = kqref.gemm(fmt, Ws[e], np.ascontiguousarray(qs[toks]), np.ascontiguousarray(d[toks]), K)
         assert_within_tol(out[r0:r1], ref, tol, f"gemm_id fmt={fmt} expert {e}")
-        if fmt != Q4_K and r1 - r0 > 8:
-            # the plain product of the same tile kernel on the gathered tokens:
+        if r1 - r0 > (64 if fmt == Q4_K else 8):
+            # the plain product of the same tile kernel on the gathered tokens
+            # (Q4_K: a tile kernel from 65 tokens on, either height):
             # identical arithmetic, identical bits
             xg = np.ascontiguousarray(x[toks])
             plain = run_gemm(kq, fmt, Ws[e], run_quant(kq, act_fmt, xg), r1 - r0, N, K)
             assert np.array_equal(out[r0:r1], plain), f"expert {e} differs from kq_gemm"
 
 
-def test_gemm_id_routing_out_of_contract_stays_in_bounds(kq):
+@pytest.mark.parametrize("fmt", (Q6_K, Q4_K))
+def test_gemm_id_routing_out_of_contract_stays_in_bounds(kq, fmt):
     """Offsets past R, decreasing offsets and token indices past M give
     undefined values but no access outside the buffers: canaries around out
-    stay intact and the call completes."""
+    stay intact and the call completes (both gather kernels)."""
     E, M, N, K = 4, 20, 64, 256
     rng = np.random.default_rng(77)
-    W = np.concatenate([datagen.make_weights(Q6_K, N, K, 70 + e).reshape(-1) for e in range(E)])
+    W = np.concatenate([datagen.make_weights(fmt, N, K, 70 + e).reshape(-1) for e in range(E)])
     a_q8 = run_quant(kq, kq.KQ_ACT_Q8_K, datagen.draw_activations(M, K, 71))
     R = 50
     off = np.array([0, 30, 10, 60, 1000], np.int32)     # decreasing, then past R
@@ -491,7 +494,7 @@ def test_gemm_id_routing_out_of_contract_stays_in_bounds(kq):
     pad = 4096
     ob = torch.full((R * N + 2 * pad,), 7.0, dtype=torch.float32, device=DEV)
     view = ob[pad:pad + R * N].view(R, N)
-    kq.kq_gemm_id(Q6_K, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, view)
+    kq.kq_gemm_id(fmt, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, view)
     torch.cuda.synchronize()
     assert torch.all(ob[:pad] == 7.0).item() and torch.all(ob[pad + R * N:] == 7.0).item()
 
