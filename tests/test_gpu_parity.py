@@ -479,6 +479,39 @@ def test_gemm_id_matches_oracle(kq, fmt):
             assert np.array_equal(out[r0:r1], plain), f"expert {e} differs from kq_gemm"
 
 
+def test_gemm_id_many_experts(kq):
+    """Q4_K gather kernel with 300 experts, most of them empty and a few
+    spanning several 64-row tiles (the kernel counts the tiles and finds
+    each tile's expert from the offsets): sampled experts against the oracle,
+    every expert's rows finite, canaries after out."""
+    E, M, N, K = 300, 150, 96, 256
+    rng = np.random.default_rng(303)
+    counts = np.zeros(E, np.int64)
+    busy = rng.choice(E, 12, replace=False)
+    counts[busy] = rng.integers(1, 200, size=12)
+    counts[busy[0]], counts[E - 1] = 129, 64
+    off, rows = routing(rng, M, counts)
+    R = int(off[-1])
+    W = datagen.make_weights(Q4_K, E * N, K, 304)
+    x = datagen.draw_activations(M, K, 305)
+    a_q8 = run_quant(kq, kq.KQ_ACT_Q8_K, x)
+    qs, d, _ = check_act_exact(kq, kq.KQ_ACT_Q8_K, x, a_q8)
+    say(f"gemm_id many experts E={E} R={R}")
+    ob = torch.full((R + 2, N), 12345.0, dtype=torch.float32, device=DEV)
+    before = kq.dispatch_counts()["gemm_id_q4_k_64x128"]
+    kq.kq_gemm_id(Q4_K, dev(W), E, a_q8, M, N, K, dev(off), dev(rows), R, ob)
+    torch.cuda.synchronize()
+    assert kq.dispatch_counts()["gemm_id_q4_k_64x128"] == before + 1
+    out = ob.cpu().numpy()
+    assert np.all(out[R:] == 12345.0) and np.all(np.isfinite(out[:R]))
+    for e in sorted(set(busy[:6].tolist()) | {E - 1}):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        toks = rows[r0:r1]
+        ref, tol = kqref.gemm(Q4_K, W[e * N:(e + 1) * N], np.ascontiguousarray(qs[toks]),
+                              np.ascontiguousarray(d[toks]), K)
+        assert_within_tol(out[r0:r1], ref, tol, f"gemm_id many experts: expert {e}")
+
+
 @pytest.mark.parametrize("fmt", (Q6_K, Q4_K))
 def test_gemm_id_routing_out_of_contract_stays_in_bounds(kq, fmt):
     """Offsets past R, decreasing offsets and token indices past M give
