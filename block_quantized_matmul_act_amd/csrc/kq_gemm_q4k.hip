@@ -204,7 +204,9 @@ __device__ __forceinline__ TileXY tile_xy(const Args &a, int tiles_m, int t) {
     constexpr int GM = 4;
     const int per_group = GM * a.tiles_n;
     const int first_m = (t / per_group) * GM;
-    const int gsize = min(tiles_m - first_m, GM);
+    // (at least 1: the look-ahead tile of a workgroup's last tile may lie
+    // past the list; its coordinates are then never used)
+    const int gsize = max(min(tiles_m - first_m, GM), 1);
     const int r = t % per_group;
     const int tm = first_m + r % gsize, n0 = (r / gsize) * BN;
     if constexpr (!GATHER) {
