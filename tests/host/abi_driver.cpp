@@ -194,6 +194,13 @@ int main() {
     EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, 96, 0, reinterpret_cast<int32_t *>(A),
                       reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
     EXPECT(ri.calls == 1 && rx.calls == 1);
+    // so does N >= 2^23 (64 output rows of N floats past 2^31 bytes)
+    EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, (int64_t)1 << 23, 256, reinterpret_cast<int32_t *>(A),
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
+    EXPECT(ri.calls == 2 && rx.calls == 1);
+    EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, ((int64_t)1 << 23) - 1, 256, reinterpret_cast<int32_t *>(A),
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
+    EXPECT(ri.calls == 2 && rx.calls == 2);
     // the loader hook reaches its launcher only with a valid count
     rd = Rec{};
     EXPECT(kq_debug_unpack(KQ_Q4_K, A, 10, reinterpret_cast<int8_t *>(A), reinterpret_cast<int32_t *>(A), s) == KQ_OK);
