@@ -36,6 +36,11 @@
 //   * Reads past the last activation row or weight row return zero and
 //     stores past the last output row are dropped (buffer resources over the
 //     whole tensors); columns past N are sent out of range.
+//   * The same kernel is built with 64-row tiles (two m-tiles per wave) for
+//     shapes whose 128-row tiling would leave CUs idle, and, at that height,
+//     in a gather mode for the expert-indexed product: a tile holds routed
+//     rows of one expert, the copies take per-lane offsets of the gathered
+//     token rows, and the weight and output resources are set per tile.
 //
 // MFMA operand convention (v_mfma_i32_32x32x32_i8, v_mfma_f32_32x32x16_bf16):
 // lane l supplies row (l % 32) of A and column (l % 32) of B with k-group
