@@ -19,7 +19,7 @@ KQ_ACT_Q8_K, KQ_ACT_Q8_128 = 1, 2
 KQ_SEC_QS, KQ_SEC_D, KQ_SEC_BSUMS, KQ_SEC_ALPHA = 0, 1, 2, 3
 KQ_OK = 0
 KQ_DEBUG_UNPACK_MAX_BLOCKS = 1 << 24
-KQ_GEMM_ID_MAX_EXPERTS = 65536
+KQ_GEMM_ID_MAX_EXPERTS = 1024
 KQ_ERR_FMT, KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_ALIGN, KQ_ERR_UNSUPPORTED, KQ_ERR_HIP = (
     -1, -2, -3, -4, -5, -6)
 (KQ_CALIB_MFMA_I8, KQ_CALIB_MFMA_I8_TOGGLE, KQ_CALIB_VALU_F32, KQ_CALIB_MFMA_I8_VALU,
@@ -96,6 +96,28 @@ def _check(status: int, where: str) -> int:
     return status
 
 
+def _need(t, nbytes, what, dtype=None):
+    """Host-side check of a torch tensor argument before its address goes to the
+    library (plain integer addresses are passed through unchecked): a
+    contiguous device tensor of the right element type holding at least
+    nbytes bytes.  Raises ValueError; nothing is launched."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise ValueError(f"{what}: expected dtype {dtype}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, {nbytes} needed")
+
+
+def _sub_block(fmt):
+    return {KQ_Q4_K: 32, KQ_Q6_K: 16}.get(fmt, 128)
+
+
 # ---------------------------------------------------------------- C ABI mirror
 
 def kq_weight_bytes(fmt, N, K):
@@ -115,16 +137,29 @@ def kq_act_fmt_for(fmt):
 
 
 def kq_quantize_act(act_fmt, x, M, K, a_q8, stream=None):
+    _need(x, 4 * max(M, 0) * max(K, 0), "kq_quantize_act x", "float32")
+    _need(a_q8, kq_act_bytes(act_fmt, M, K), "kq_quantize_act a_q8")
     return _check(lib().kq_quantize_act(act_fmt, _ptr(x), M, K, _ptr(a_q8), _stream(stream)),
                   "kq_quantize_act")
 
 
+def _need_gemm_inputs(fmt, W, a_q8, M, N, K, where, n_experts=1):
+    _need(W, n_experts * kq_weight_bytes(fmt, N, K), where + " W")
+    act = kq_act_fmt_for(fmt)
+    if act > 0:
+        _need(a_q8, kq_act_bytes(act, M, K), where + " a_q8")
+
+
 def kq_gemm(fmt, W, a_q8, M, N, K, out, stream=None):
+    _need_gemm_inputs(fmt, W, a_q8, M, N, K, "kq_gemm")
+    _need(out, 4 * max(M, 0) * max(N, 0), "kq_gemm out", "float32")
     return _check(lib().kq_gemm(fmt, _ptr(W), _ptr(a_q8), M, N, K, _ptr(out), _stream(stream)),
                   "kq_gemm")
 
 
 def kq_gemm_subsums(fmt, W, a_q8, M, N, K, sums, stream=None):
+    _need_gemm_inputs(fmt, W, a_q8, M, N, K, "kq_gemm_subsums")
+    _need(sums, 4 * max(M, 0) * max(N, 0) * max(K, 0) // _sub_block(fmt), "kq_gemm_subsums sums", "int32")
     return _check(lib().kq_gemm_subsums(fmt, _ptr(W), _ptr(a_q8), M, N, K, _ptr(sums),
                                         _stream(stream)), "kq_gemm_subsums")
 
@@ -156,6 +191,11 @@ def kq_debug_unpack(fmt, W, nblocks, q, scales, stream=None):
 
 
 def kq_gemm_id(fmt, W, n_experts, a_q8, M, N, K, expert_offsets, rows, R, out, stream=None):
+    if 1 <= n_experts <= KQ_GEMM_ID_MAX_EXPERTS:
+        _need_gemm_inputs(fmt, W, a_q8, M, N, K, "kq_gemm_id", n_experts)
+        _need(expert_offsets, 4 * (n_experts + 1), "kq_gemm_id expert_offsets", "int32")
+    _need(rows, 4 * max(R, 0), "kq_gemm_id rows", "int32")
+    _need(out, 4 * max(R, 0) * max(N, 0), "kq_gemm_id out", "float32")
     return _check(lib().kq_gemm_id(fmt, _ptr(W), n_experts, _ptr(a_q8), M, N, K, _ptr(expert_offsets),
                                    _ptr(rows), R, _ptr(out), _stream(stream)), "kq_gemm_id")
 

@@ -97,6 +97,10 @@ int check_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, i
     // grid limits: tiles must fit a 1-D grid
     const int64_t tiles = ((M + 31) / 32) * ((N + 31) / 32);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    // the Q4_K persistent kernels count (tile, superblock) steps per
+    // workgroup in int32 (64-row tiles at the most)
+    if (fmt == KQ_Q4_K && ((M + 63) / 64) * ((N + 127) / 128) * (K / 256) > INT32_MAX)
+        return KQ_ERR_UNSUPPORTED;
     // the GEMM kernels address whole tensors (W, the qs, d and alpha sections,
     // out) with 32-bit buffer offsets, including the rows and columns a last
     // tile hangs past M (up to 128) and N (up to 256): every such offset stays
@@ -252,13 +256,19 @@ int kq_gemm_id(int fmt, const void *W, int64_t n_experts, const void *a_q8, int6
         return KQ_ERR_UNSUPPORTED;
     const int64_t tiles = ((R + 63) / 64 + n_experts) * ((N + 127) / 128);
     if (tiles > INT32_MAX) return KQ_ERR_UNSUPPORTED;
+    // the Q4_K persistent kernel counts (tile, superblock) steps per
+    // workgroup in int32; a workgroup may own every tile
+    if (fmt == KQ_Q4_K && tiles * (K / 256) > INT32_MAX) return KQ_ERR_UNSUPPORTED;
     ActLayout L;
     act_layout(kq_act_fmt_for(fmt), M, K, &L);
     const char *base = static_cast<const char *>(a_q8);
     const int8_t *qs = reinterpret_cast<const int8_t *>(base);
     const float *da = reinterpret_cast<const float *>(base + L.d);
     const uint16_t *alpha = L.alpha >= 0 ? reinterpret_cast<const uint16_t *>(base + L.alpha) : nullptr;
-    const bool q4k_tile = fmt == KQ_Q4_K && kq::q4k_id_tile_ok((int)N, (int)K);
+    // Q4_K runs only on the register-unpack tile kernel (per-tile output
+    // offsets within 2^31 bytes); wider Q4_K shapes are declined
+    if (fmt == KQ_Q4_K && !kq::q4k_id_tile_ok((int)N, (int)K)) return KQ_ERR_UNSUPPORTED;
+    const bool q4k_tile = fmt == KQ_Q4_K;
     hipError_t e = q4k_tile ? kq::launch_gemm_q4k_id(W, (int)n_experts, N * rowbytes, qs, da, alpha,
                                                      expert_offsets, rows, (int)R, out, (int)M, (int)N,
                                                      (int)K, stream)

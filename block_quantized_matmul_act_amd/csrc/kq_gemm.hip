@@ -6,9 +6,11 @@
 //
 // Launched for Q6_K and ternary weights (shapes the matrix-vector kernels of
 // kq_gemv.hip do not take; two-bit ternary always); Q4_K runs on the kernels
-// of kq_gemm_q4k.hip.  The Q4_K branches below are not instantiated by
-// launch_gemm; the two test hooks (subsums_kernel, debug_unpack_kernel) use
-// this file's loaders for every format.
+// of kq_gemm_q4k.hip, and gemm_kernel refuses to compile for it.  The two
+// test hooks (subsums_kernel, debug_unpack_kernel) are a separate decoder:
+// their own loaders (load_w / unpack_w) and a small 32 x 32 MFMA loop, for
+// every format; the production kernels are checked exactly by the one-hot
+// and unit-scale products of the tests instead.
 //
 // Design (MI355X-first; prior art: the BigTile kernel of vllm.cpp PR 3036,
 // which reuses staged activation rows across warps, and llama.cpp's
@@ -466,6 +468,10 @@ template <int FMT, bool GATHER = false>
 __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
+    // Q4_K runs on the register-unpack kernels of kq_gemm_q4k.hip; this
+    // kernel's Q4_K branches (min term through the older alpha operand) are
+    // never compiled
+    static_assert(FMT != FMT_Q4K, "Q4_K products run on kq_gemm_q4k.hip");
     constexpr bool Q4 = FMT == FMT_Q4K, Q6 = FMT == FMT_Q6K, TQ = FMT == FMT_TQ, TQ2 = FMT == FMT_TQ2;
     constexpr bool TRI = tri(FMT);    // scales per 128 values, one block per chunk
     constexpr int CPS = TRI ? 1 : 2;  // chunks per scale block
@@ -1360,9 +1366,6 @@ hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_
     a.expert_bytes = expert_bytes;
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {
-        case FMT_Q4K:
-            hipLaunchKernelGGL((gemm_kernel<FMT_Q4K, true>), dim3(grid), dim3(MNT), 0, stream, a);
-            break;
         case FMT_Q6K:
             hipLaunchKernelGGL((gemm_kernel<FMT_Q6K, true>), dim3(grid), dim3(MNT), 0, stream, a);
             break;

@@ -28,11 +28,13 @@
 //     Pass 1 accumulates the sh digits over the whole superblock, the int32
 //     sums are shifted left by 3, pass 2 adds the sl digits; the fp32 fold
 //     then runs once per superblock and output.
-//   * The min term is a rank-8 product per superblock.  Its activation
-//     operand d_a*B_j comes precomputed from the quantizer (alpha section, a
-//     bf16 hi/lo pair); the weight operand -dmin*m_j is split the same way;
-//     two bf16 MFMAs per superblock (hi*hi + lo*hi, then hi*lo) fold it
-//     straight into the fp32 accumulators.
+//   * The min term is a rank-8 product per superblock, computed exactly:
+//     M = sum_j m_j * B_j, with B_j the sum of a sub-block's 32 quantized
+//     activations.  The quantizer stores B_j as two parts bf16 holds exactly
+//     (the alpha section), so one bf16 MFMA against the 6-bit mins gives M
+//     with every product and partial sum an integer below 2^24.  The fold is
+//     then out += d_a * (d * T - dmin * M) in fp32, T the integer superblock
+//     sum of sc*q*a.
 //   * Reads past the last activation row or weight row return zero and
 //     stores past the last output row are dropped (buffer resources over the
 //     whole tensors); columns past N are sent out of range.
@@ -52,6 +54,7 @@
 #include "kq_hooks.hpp"
 #include "kq_launch.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace kq {
@@ -82,7 +85,7 @@ struct Args {
     const uint8_t *W;
     const int8_t *qs;
     const float *da;         // [nsb][M]
-    const uint16_t *alpha;   // [nsb][2][M][8] bf16
+    const uint16_t *alpha;   // [nsb][2][M][8] bf16: exact parts of the sub-block sums B_j
     float *out;
     int M, N, K, nsb, tiles_m, tiles_n, ntiles;
     // expert-indexed product only: out has n_routed rows, routed row r
@@ -497,49 +500,44 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // fold: out += float(sum_k sc*q*a) * d_a[m] * d[n]
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            v4f da4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                da4[q] = *reinterpret_cast<const v4f *>(S.d + 32 * t + 8 * q + 4 * g);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * q + i;
-                    out[t][r] = fmaf((float)acc[t][r], da4[q][i] * dw, out[t][r]);
-                }
-            }
-        }
-        // min term: k-group g carries sub-blocks 4g..4g+3.  A row m: alpha_hi
-        // and alpha_lo of those; B: beta_hi twice, then beta_lo and zeros, so
-        // two bf16 MFMAs give sum_j (a_hi + a_lo) b_hi + a_hi b_lo.
+        // min term, exactly: M = sum_j m_j * B_j with B_j the sum of the
+        // sub-block's 32 quantized activations (staged as two bf16 parts that
+        // are exact, 64*floor(B_j/64) and B_j mod 64); one bf16 MFMA per
+        // m-tile, all products and partial sums integers below 2^24.  k-group
+        // g carries sub-blocks 4g..4g+3: A row m holds both parts of those, B
+        // the mins m_j twice.
+        // fold: out += d_a[m] * (d[n] * float(sum_k sc*q*a) - dmin[n] * M)
         {
             // mins m_j: bits 48 + 6j of the 96-bit word (words w1, w2, w3)
             const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);  // bits 32..95
             const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));      // fields 4g..4g+3
-            v8bf b1, b2;
+            v8bf bm;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
-                __bf16 h, l;
-                split_bf16(beta, h, l);
-                b1[i] = h;
-                b1[4 + i] = h;
-                b2[i] = l;
-                b2[4 + i] = (__bf16)0.0f;
+                const __bf16 m = (__bf16)(float)((mx >> (6 * i)) & 63u);
+                bm[i] = m;
+                bm[4 + i] = m;
             }
+            const float ndmin = -dmin;
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const int8_t *lp = S.l + (32 * t + ln) * 16 + 8 * g;
-                const v2u ahi = *reinterpret_cast<const v2u *>(lp);
-                const v2u alo = *reinterpret_cast<const v2u *>(lp + BM * 16);
-                const v4i avv = {(int)ahi.x, (int)ahi.y, (int)alo.x, (int)alo.y};
-                const v8bf am = __builtin_bit_cast(v8bf, avv);
-                out[t] = mma_bf16(am, b1, out[t]);
-                out[t] = mma_bf16(am, b2, out[t]);
+                const v2u ap0 = *reinterpret_cast<const v2u *>(lp);
+                const v2u ap1 = *reinterpret_cast<const v2u *>(lp + BM * 16);
+                const v4i avv = {(int)ap0.x, (int)ap0.y, (int)ap1.x, (int)ap1.y};
+                const v16f mt = mma_bf16(__builtin_bit_cast(v8bf, avv), bm, v16f{});
+                v4f da4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    da4[q] = *reinterpret_cast<const v4f *>(S.d + 32 * t + 8 * q + 4 * g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * q + i;
+                        out[t][r] = fmaf(fmaf((float)acc[t][r], dw, mt[r] * ndmin), da4[q][i], out[t][r]);
+                    }
+                }
             }
         }
 
@@ -795,48 +793,60 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
             }
         }
         if (H == 1) {
-            // fold: out += float(8*acc_h + acc_l) * d_a[m] * d[n], then the min
-            // term; scales and min operands from this stage
+            // fold: out += d_a[m] * (d[n] * float(8*acc_h + acc_l) - dmin[n] * M)
+            // with M = sum_j m_j B_j exact (one bf16 MFMA per m-tile on the
+            // exact parts of B_j, as in the tile kernel); scales and min
+            // operands from this stage
             const uint32_t sd = S + SA + 16 * g;
             const uint32_t sl = S + SA + SDS + 16 * ln + 8 * g;
             v4f da[SMT][4];
-            v2u ahi[SMT], alo[SMT];
+            v2u ap0[SMT], ap1[SMT];
             da[0][0] = __builtin_bit_cast(v4f, lds_read16<0>(sd));
             da[0][1] = __builtin_bit_cast(v4f, lds_read16<32>(sd));
             da[0][2] = __builtin_bit_cast(v4f, lds_read16<64>(sd));
             da[0][3] = __builtin_bit_cast(v4f, lds_read16<96>(sd));
-            ahi[0] = lds_read8<0>(sl);
-            alo[0] = lds_read8<1024>(sl);
+            ap0[0] = lds_read8<0>(sl);
+            ap1[0] = lds_read8<1024>(sl);
             if constexpr (SMT == 2) {
                 da[SMT - 1][0] = __builtin_bit_cast(v4f, lds_read16<128>(sd));
                 da[SMT - 1][1] = __builtin_bit_cast(v4f, lds_read16<160>(sd));
                 da[SMT - 1][2] = __builtin_bit_cast(v4f, lds_read16<192>(sd));
                 da[SMT - 1][3] = __builtin_bit_cast(v4f, lds_read16<224>(sd));
-                ahi[SMT - 1] = lds_read8<512>(sl);
-                alo[SMT - 1] = lds_read8<1536>(sl);
+                ap0[SMT - 1] = lds_read8<512>(sl);
+                ap1[SMT - 1] = lds_read8<1536>(sl);
             }
             // tile 0's six reads are followed by tile 1's six (if any)
             lds_wait_n(6 * (SMT - 1), da[0][0]);
             lds_wait_n(6 * (SMT - 1), da[0][1]);
             lds_wait_n(6 * (SMT - 1), da[0][2]);
             lds_wait_n(6 * (SMT - 1), da[0][3]);
-            lds_wait_n(6 * (SMT - 1), ahi[0]);
-            lds_wait_n(6 * (SMT - 1), alo[0]);
+            lds_wait_n(6 * (SMT - 1), ap0[0]);
+            lds_wait_n(6 * (SMT - 1), ap1[0]);
+            if constexpr (SMT == 2) {
+                lds_wait<0>(da[SMT - 1][0]);
+                lds_wait<0>(da[SMT - 1][1]);
+                lds_wait<0>(da[SMT - 1][2]);
+                lds_wait<0>(da[SMT - 1][3]);
+                lds_wait<0>(ap0[SMT - 1]);
+                lds_wait<0>(ap1[SMT - 1]);
+            }
             const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
-            const float dmin = f16_bits_to_f32((uint32_t)hdr[0] >> 16);
+            const float ndmin = -f16_bits_to_f32((uint32_t)hdr[0] >> 16);
             const uint32_t w3 = (uint32_t)hdr[3];
             const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
             const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
-            v8bf b1, b2;
+            v8bf bm;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float beta = -dmin * (float)((mx >> (6 * i)) & 63u);
-                __bf16 hb, lb;
-                split_bf16(beta, hb, lb);
-                b1[i] = hb;
-                b1[4 + i] = hb;
-                b2[i] = lb;
-                b2[4 + i] = (__bf16)0.0f;
+                const __bf16 m = (__bf16)(float)((mx >> (6 * i)) & 63u);
+                bm[i] = m;
+                bm[4 + i] = m;
+            }
+            v16f mt[SMT];
+#pragma unroll
+            for (int t = 0; t < SMT; ++t) {
+                const v4i avv = {(int)ap0[t].x, (int)ap0[t].y, (int)ap1[t].x, (int)ap1[t].y};
+                mt[t] = mma_bf16(__builtin_bit_cast(v8bf, avv), bm, v16f{});
             }
 #pragma unroll
             for (int t = 0; t < SMT; ++t) {
@@ -846,22 +856,8 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
                     for (int i = 0; i < 4; ++i) {
                         const int r = 4 * q + i;
                         const int T = (acc_h[t][r] << 3) + acc_l[t][r];
-                        out[t][r] = fmaf((float)T, da[t][q][i] * dw, out[t][r]);
+                        out[t][r] = fmaf(fmaf((float)T, dw, mt[t][r] * ndmin), da[t][q][i], out[t][r]);
                     }
-                if constexpr (SMT == 2) {
-                    if (t == 0) {
-                        lds_wait<0>(da[SMT - 1][0]);
-                        lds_wait<0>(da[SMT - 1][1]);
-                        lds_wait<0>(da[SMT - 1][2]);
-                        lds_wait<0>(da[SMT - 1][3]);
-                        lds_wait<0>(ahi[SMT - 1]);
-                        lds_wait<0>(alo[SMT - 1]);
-                    }
-                }
-                const v4i avv = {(int)ahi[t].x, (int)ahi[t].y, (int)alo[t].x, (int)alo[t].y};
-                const v8bf am = __builtin_bit_cast(v8bf, avv);
-                out[t] = mma_bf16(am, b1, out[t]);
-                out[t] = mma_bf16(am, b2, out[t]);
             }
         }
     };
@@ -938,7 +934,7 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 // weights 64c + 32 + 16h + i (sub-block 2c + 1), c = c8 / 2, h = c8 % 2,
 // i < 16.  Per token the lane forms the integer sums of those 32 products
 // with v_dot4, scales them by the two sub-block scales, and folds
-//   acc += float(sc0 S0 + sc1 S1) * d_a * d - dmin * m_c8 * alpha_c8,
+//   acc += d_a * (d * float(sc0 S0 + sc1 S1) - dmin * m_c8 * B_c8),
 // the min term of sub-block c8 (one sub-block per lane covers all eight).
 // A row's total is the sum over the 64 lanes of its load instructions, in a
 // fixed butterfly order, stored by lane 0.
@@ -1068,9 +1064,10 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
                 s1 = __builtin_amdgcn_sdot4(hi[e], a1[m][e], s1, false);
             }
             const int u = sc0 * s0 + sc1 * s1;
-            ac[m] = fmaf((float)u, da[m] * dw, ac[m]);
-            ac[m] = fmaf(__builtin_bit_cast(float, (uint32_t)ah[m] << 16), cmin, ac[m]);
-            ac[m] = fmaf(__builtin_bit_cast(float, (uint32_t)al[m] << 16), cmin, ac[m]);
+            // B of sub-block c8 from its two exact parts
+            const float bj = __builtin_bit_cast(float, (uint32_t)ah[m] << 16) +
+                             __builtin_bit_cast(float, (uint32_t)al[m] << 16);
+            ac[m] = fmaf(fmaf((float)u, dw, cmin * bj), da[m], ac[m]);
         }
     };
 
@@ -1112,7 +1109,6 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
 
 }  // namespace q4w
 
-static int g_num_cus = 0;
 
 static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
 constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
@@ -1133,27 +1129,42 @@ int q4k_kernel_choice(int M, int N, int K) {
     return tiles128 > TILE64_MAX_TILES128 ? Q4K_TILE128 : Q4K_TILE64;
 }
 
-static void init_num_cus() {
-    if (g_num_cus <= 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        g_num_cus = cus;
+// Compute units of the current device, cached per device (the persistent
+// grids are sized from it).  Concurrent first calls may both query; they
+// store the same value.
+static int num_cus() {
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < MAX_DEV) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < MAX_DEV) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 bool q4k_id_tile_ok(int N, int K) {
     // per-tile output offsets (64 rows of N floats) stay below 2^31
-    return K > 0 && (int64_t)64 * N * 4 < ((int64_t)1 << 31);
+    (void)K;
+    return (int64_t)64 * N * 4 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes, const int8_t *qs,
                               const float *da, const uint16_t *alpha, const int32_t *exp_off,
                               const int32_t *rows, int R, float *out, int M, int N, int K,
                               hipStream_t stream) {
-    init_num_cus();
+    const int cus = num_cus();
+    if (K == 0) {
+        const int64_t n = (int64_t)R * N;
+        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, out, n);
+        return hipGetLastError();
+    }
     q4w::Args a;
     a.W = static_cast<const uint8_t *>(W);
     a.qs = qs;
@@ -1173,7 +1184,7 @@ hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes
     a.n_experts = n_experts;
     a.n_routed = R;
     a.expert_bytes = expert_bytes;
-    const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * g_num_cus);
+    const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * cus);
     hipLaunchKernelGGL((q4w::gemm_q4k_kernel<64, true>), dim3(grid), dim3(q4w::NT), 0, stream, a);
     return hipGetLastError();
 }
@@ -1181,7 +1192,7 @@ hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes
 hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                            const uint16_t *alpha, float *out, int M, int N, int K,
                            hipStream_t stream) {
-    init_num_cus();
+    const int cus = num_cus();
     if (K == 0) {
         const int64_t n = (int64_t)M * N;
         hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
@@ -1223,12 +1234,12 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                                    dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
             break;
         case Q4K_TILE64: {
-            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * g_num_cus);
+            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * cus);
             hipLaunchKernelGGL(q4w::gemm_q4k_kernel<64>, dim3(grid), dim3(q4w::NT), 0, stream, a);
             break;
         }
         default: {
-            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<128>::WG_PER_CU * g_num_cus);
+            const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<128>::WG_PER_CU * cus);
             hipLaunchKernelGGL(q4w::gemm_q4k_kernel<128>, dim3(grid), dim3(q4w::NT), 0, stream, a);
             break;
         }

@@ -13,7 +13,8 @@ namespace kq {
 hipError_t launch_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t *scales,
                                hipStream_t stream);
 
-// Expert-indexed product (kq_gemm_id) on the tile kernel of kq_gemm.hip.
+// Expert-indexed product (kq_gemm_id) on the tile kernel of kq_gemm.hip
+// (Q6_K and ternary formats).
 hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_bytes,
                           const int8_t *qs, const float *da, const uint16_t *alpha,
                           const int32_t *exp_off, const int32_t *rows, int R, float *out, int M,
@@ -21,7 +22,8 @@ hipError_t launch_gemm_id(int fmt, const void *W, int n_experts, int64_t expert_
 
 // Q4_K expert-indexed product on the register-unpack tile kernel
 // (kq_gemm_q4k.hip, 64-row tiles in gather mode), for shapes where
-// q4k_id_tile_ok(N, K) holds; other shapes take launch_gemm_id.
+// q4k_id_tile_ok(N, K) holds (the API declines the others); K == 0 writes
+// zeros.
 bool q4k_id_tile_ok(int N, int K);
 hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes, const int8_t *qs,
                               const float *da, const uint16_t *alpha, const int32_t *exp_off,

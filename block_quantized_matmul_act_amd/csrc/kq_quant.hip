@@ -16,8 +16,10 @@
 // divides and no wave idles unless K is below 1024.
 // Scales are stored block-major (d[s][m]) so that the GEMM reads the scales of
 // a 128-row tile as one contiguous run.  For Q8_K the kernel also writes the
-// Q4_K min-term operand alpha = d * (sum of 32 qs) as a bf16 hi/lo pair per
-// 32-value sub-block, once per activation instead of once per GEMM tile.  The
+// Q4_K min-term operand: the sum B of the 32 qs of each sub-block, split into
+// two parts that bf16 holds exactly (64 * floor(B / 64) and B mod 64), so
+// that a bf16 matrix-core product with the 6-bit mins gives sum_j m_j B_j
+// exactly; written once per activation instead of once per GEMM tile.  The
 // kernel is bound by HBM bandwidth: it reads 4 bytes and writes ~1.2 bytes per
 // value.
 #include "kq_device.hpp"
@@ -101,15 +103,16 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict_
     if constexpr (BSUMS) {
         // this lane's 16 values are one bsums group
         if (valid) bsums[row * (K / 16) + col / 16] = (int16_t)sum;
-        // 32 values = lanes 2j, 2j+1: alpha_j = d * sum32 in fp32, then a bf16 hi/lo pair
+        // 32 values = lanes 2j, 2j+1: B_j = sum32 (|B_j| <= 4064), parts
+        // 64 * floor(B_j / 64) (a 7-bit integer times 64) and B_j mod 64, both
+        // exact in bf16
         const int sum32 = sum + (int)dpp<DPP_QUAD_XOR1>((uint32_t)sum);
-        const float av = dv * (float)sum32;
-        const __bf16 hi = (__bf16)av;
-        const __bf16 lo = (__bf16)(av - (float)hi);
+        const __bf16 p0 = (__bf16)(float)(sum32 & ~63);
+        const __bf16 p1 = (__bf16)(float)(sum32 & 63);
         if (valid && (gl & 1) == 0) {
             const int j = gl >> 1;
-            alpha[((sblk * 2 + 0) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, hi);
-            alpha[((sblk * 2 + 1) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, lo);
+            alpha[((sblk * 2 + 0) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, p0);
+            alpha[((sblk * 2 + 1) * M + row) * 8 + j] = __builtin_bit_cast(uint16_t, p1);
         }
     }
 }

@@ -39,13 +39,14 @@
  *                               s of all M rows are contiguous
  *     bsums int16 [M][K/16]     sums of qs over each 16 consecutive values
  *     alpha bf16  [K/256][2][M][8]
- *                               per block s, row m and 32-value sub-block j:
- *                               a = d * (float)(sum of the 32 qs), one fp32
- *                               multiply; part 0 = bf16(a), part 1 =
- *                               bf16(a - part 0), both round-to-nearest-even.
- *                               This is the activation operand of the Q4_K
- *                               min term, kept in hi/lo form so that the GEMM
- *                               reads it instead of recomputing it per tile.
+ *                               per block s, row m and 32-value sub-block j,
+ *                               with B the sum of the sub-block's 32 qs
+ *                               (|B| <= 4064): part 0 = 64 * floor(B / 64),
+ *                               part 1 = B - part 0 (in [0, 63]); both are
+ *                               integers bf16 represents exactly.  This is
+ *                               the activation operand of the Q4_K min term
+ *                               sum_j m_j * B_j, which the GEMM forms exactly
+ *                               from it instead of re-summing qs per tile.
  *   Q8_128 activations (KQ_ACT_Q8_128): sections qs int8 [M][K] and
  *   d fp32 [K/128][M] (block-major); no bsums, no alpha.
  *   Quantization rule per block, in fp32: amax = max|x|; if amax == 0 or
@@ -159,22 +160,28 @@ int kq_gemm(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N, int6
             float *out, hipStream_t stream);
 
 /*
- * Test hook: per-sub-block integer dot sums through the same weight loaders
- * and int8 matrix-core code as kq_gemm, with the scale fold disabled.
- * sums (device, int32 [M][N][K/SB]) receives
+ * Test hook: per-sub-block integer dot sums, written out.  sums (device,
+ * int32 [M][N][K/SB]) receives
  *   S[m][n][j] = sum_{k in sub-block j} qint[n][k] * qs[m][k]
  * with SB = 32 and qint = q (Q4_K), SB = 16 and qint = q - 32 (Q6_K),
- * SB = 128 and qint = t (ternary).
+ * SB = 128 and qint = t (ternary).  This runs a separate small decoder (its
+ * own weight loaders and a 32 x 32 int8 MFMA loop, for every format), not
+ * the kq_gemm kernels, which never materialize S: those are held to the same
+ * sums exactly by products whose scales expose them (unit scales, a single
+ * nonzero sub-block scale), so the hook is a reference implementation on the
+ * device rather than a view into production code.  Defined by the
+ * per-sub-block int8 dot products of vllm.cpp PR 3036's tile GEMM.
  */
 int kq_gemm_subsums(int fmt, const void *W, const void *a_q8, int64_t M, int64_t N,
                     int64_t K, int32_t *sums, hipStream_t stream);
 
 /*
  * Test hook: decode nblocks consecutive weight blocks of W (device, 16-byte
- * aligned, kq_weight_bytes(fmt, 1, nblocks * QK) bytes) with the weight
- * loaders of the tile GEMM kernel (the loader fuzz test of llama.cpp PR 214,
- * which ran its unpack on thousands of random packed blocks against the
- * scalar codec).  Writes, for block b:
+ * aligned, kq_weight_bytes(fmt, 1, nblocks * QK) bytes) with the loaders of
+ * the sub-sum hook above (the loader fuzz test of llama.cpp PR 214, which ran
+ * its unpack on thousands of random packed blocks against the scalar codec;
+ * the kq_gemm kernels' own unpacking is checked through identity activations
+ * and the exact-sum products instead).  Writes, for block b:
  *   q [b][QK] int8 (device, 16-byte aligned): the integer operand of every
  *     value in storage order, q in [0,15] (Q4_K), q - 32 (Q6_K), t (ternary);
  *   scales [b][16] int32 (device, 4-byte aligned): Q4_K sc_0..sc_7 then
@@ -194,11 +201,12 @@ int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t 
  * MUL_MAT_ID, which the pages test next to MUL_MAT): every routed row r
  * multiplies one expert's weights with one token's quantized activations,
  *   out[r][n] = sum_k W^_e[n][k] * A^[rows[r]][k],  e the expert of row r,
- * through the same loaders and tile kernels as kq_gemm: Q4_K (K > 0 and
- * N < 2^23) on the register-unpack tile kernel with 64-row tiles, the other
- * formats and shapes on the 128 x 128 tile kernel, each gathering the token
- * rows of one expert per tile.  Every routed row gets the bits kq_gemm gives
- * its token where kq_gemm runs the same tile kernel.
+ * through the same loaders and tile kernels as kq_gemm: Q4_K on the
+ * register-unpack tile kernel with 64-row tiles (N < 2^23; wider Q4_K shapes
+ * are declined with KQ_ERR_UNSUPPORTED), the other formats on the 128 x 128
+ * tile kernel, each gathering the token rows of one expert per tile.  Every
+ * routed row gets the bits kq_gemm gives its token where kq_gemm runs the
+ * same tile kernel.
  *   W               device, n_experts consecutive weight tensors of N rows of
  *                   K/QK blocks (expert e starts e * kq_weight_bytes(fmt, N, K)
  *                   bytes in), 16-byte aligned
@@ -213,10 +221,12 @@ int kq_debug_unpack(int fmt, const void *W, int64_t nblocks, int8_t *q, int32_t 
  * arrays that break the contract give undefined values in out, but every
  * access stays inside W, a_q8, rows and out.  R == 0 or N == 0 returns KQ_OK
  * with no launch; M == 0 with R > 0 is KQ_ERR_SHAPE; n_experts must be in
- * 1 .. KQ_GEMM_ID_MAX_EXPERTS.  Other errors and limits as kq_gemm (one
- * expert's weights and the activation sections within 2^31 bytes).
+ * 1 .. KQ_GEMM_ID_MAX_EXPERTS (each tile locates its expert by walking the
+ * offsets, so the walk is kept short).  Other errors and limits as kq_gemm
+ * (one expert's weights and the activation sections within 2^31 bytes, and
+ * the per-workgroup loop count of the persistent tile kernel within int32).
  */
-#define KQ_GEMM_ID_MAX_EXPERTS 65536
+#define KQ_GEMM_ID_MAX_EXPERTS 1024
 int kq_gemm_id(int fmt, const void *W, int64_t n_experts, const void *a_q8, int64_t M, int64_t N,
                int64_t K, const int32_t *expert_offsets, const int32_t *rows, int64_t R, float *out,
                hipStream_t stream);

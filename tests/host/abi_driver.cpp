@@ -85,7 +85,7 @@ hipError_t launch_gemm_id(int, const void *, int n_experts, int64_t expert_bytes
     (void)K;
     return hipSuccess;
 }
-bool q4k_id_tile_ok(int N, int K) { return K > 0 && (int64_t)64 * N * 4 < ((int64_t)1 << 31); }
+bool q4k_id_tile_ok(int N, int K) { (void)K; return (int64_t)64 * N * 4 < ((int64_t)1 << 31); }
 hipError_t launch_gemm_q4k_id(const void *, int n_experts, int64_t expert_bytes, const int8_t *qs, const float *da,
                               const uint16_t *alpha, const int32_t *, const int32_t *, int R, float *, int M, int,
                               int, hipStream_t) {
@@ -182,7 +182,7 @@ int main() {
     EXPECT(ri.p[1] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_D, 100, 512));
     EXPECT(ri.p[2] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, 100, 512));
     // Q4_K goes to the register-unpack tile kernel's gather mode, with the same
-    // sections; K = 0 stays on the generic path (it writes the zeros)
+    // sections, K = 0 included (its launcher writes the zeros)
     ri = Rec{};
     rx = Rec{};
     EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, 96, 512, reinterpret_cast<int32_t *>(A),
@@ -193,14 +193,14 @@ int main() {
     EXPECT(rx.p[2] == A + kq_act_section_offset(KQ_ACT_Q8_K, KQ_SEC_ALPHA, 100, 512));
     EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, 96, 0, reinterpret_cast<int32_t *>(A),
                       reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
-    EXPECT(ri.calls == 1 && rx.calls == 1);
-    // so does N >= 2^23 (64 output rows of N floats past 2^31 bytes)
+    EXPECT(ri.calls == 0 && rx.calls == 2);
+    // N >= 2^23 (64 output rows of N floats past 2^31 bytes) is declined
     EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, (int64_t)1 << 23, 256, reinterpret_cast<int32_t *>(A),
-                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
-    EXPECT(ri.calls == 2 && rx.calls == 1);
+                      reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_ERR_UNSUPPORTED);
+    EXPECT(ri.calls == 0 && rx.calls == 2);
     EXPECT(kq_gemm_id(KQ_Q4_K, A, 8, A, 100, ((int64_t)1 << 23) - 1, 256, reinterpret_cast<int32_t *>(A),
                       reinterpret_cast<int32_t *>(A), 300, reinterpret_cast<float *>(A), s) == KQ_OK);
-    EXPECT(ri.calls == 2 && rx.calls == 2);
+    EXPECT(ri.calls == 0 && rx.calls == 3);
     // the loader hook reaches its launcher only with a valid count
     rd = Rec{};
     EXPECT(kq_debug_unpack(KQ_Q4_K, A, 10, reinterpret_cast<int8_t *>(A), reinterpret_cast<int32_t *>(A), s) == KQ_OK);

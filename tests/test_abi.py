@@ -240,3 +240,52 @@ def test_gemm_id_rejects_bad_arguments(kq):
     # one expert's weights must stay within 2^31 bytes
     n = (1 << 31) // 2304
     assert f(Q4, A, 2, A, 10, n, 4096, P4, P4, 20, A) == kq.KQ_ERR_UNSUPPORTED
+
+
+def test_binding_checks_tensor_arguments(kq):
+    """The torch conveniences refuse host tensors, wrong element types,
+    non-contiguous tensors and buffers smaller than the size queries give,
+    before any address reaches the library."""
+    torch = pytest.importorskip("torch")
+    cpu = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device tensor"):
+        kq.kq_quantize_act(kq.KQ_ACT_Q8_K, cpu, 1, 256, cpu)
+    with pytest.raises(ValueError, match="device tensor"):
+        kq.kq_gemm(kq.KQ_Q4_K, cpu, 0, 1, 1, 256, 0)
+
+    class FakeDev:  # duck-typed device tensor for the size and type checks
+        is_cuda = True
+
+        def __init__(self, n, dtype="uint8", size=1, contiguous=True):
+            self.n, self.dtype, self.size, self.c = n, "torch." + dtype, size, contiguous
+
+        def is_contiguous(self):
+            return self.c
+
+        def numel(self):
+            return self.n
+
+        def element_size(self):
+            return self.size
+
+        def data_ptr(self):
+            raise AssertionError("an address escaped the check")
+
+    M, N, K = 3, 5, 256
+    wb, ab = kq.kq_weight_bytes(kq.KQ_Q4_K, N, K), kq.kq_act_bytes(kq.KQ_ACT_Q8_K, M, K)
+    W, A = FakeDev(wb), FakeDev(ab)
+    with pytest.raises(ValueError, match="W"):
+        kq.kq_gemm(kq.KQ_Q4_K, FakeDev(wb - 1), A, M, N, K, FakeDev(M * N, "float32", 4))
+    with pytest.raises(ValueError, match="a_q8"):
+        kq.kq_gemm(kq.KQ_Q4_K, W, FakeDev(ab - 16), M, N, K, FakeDev(M * N, "float32", 4))
+    with pytest.raises(ValueError, match="out"):
+        kq.kq_gemm(kq.KQ_Q4_K, W, A, M, N, K, FakeDev(M * N - 1, "float32", 4))
+    with pytest.raises(ValueError, match="dtype"):
+        kq.kq_gemm(kq.KQ_Q4_K, W, A, M, N, K, FakeDev(M * N, "float16", 2))
+    with pytest.raises(ValueError, match="contiguous"):
+        kq.kq_gemm(kq.KQ_Q4_K, W, A, M, N, K, FakeDev(M * N, "float32", 4, contiguous=False))
+    with pytest.raises(ValueError, match="dtype"):
+        kq.kq_quantize_act(kq.KQ_ACT_Q8_K, FakeDev(M * K, "float16", 2), M, K, A)
+    with pytest.raises(ValueError, match="rows"):
+        kq.kq_gemm_id(kq.KQ_Q4_K, FakeDev(2 * wb), 2, A, M, N, K, FakeDev(3, "int32", 4),
+                      FakeDev(6, "int32", 4), 7, FakeDev(7 * N, "float32", 4))

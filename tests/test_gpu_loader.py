@@ -178,11 +178,15 @@ def unit_act(kq, fmt, qs):
         ob = kq.kq_act_section_offset(act, kq.KQ_SEC_BSUMS, M, K)
         bsums = qs.astype(np.int32).reshape(M, K // 16, 16).sum(-1).astype(np.int16)
         buf[ob:ob + bsums.nbytes] = bsums.view(np.uint8).reshape(-1)
-        # alpha = 1 * (sum of 32 qs): small integers, exact in bf16 (hi), lo = 0
-        s32 = qs.astype(np.int32).reshape(M, K // 256, 8, 32).sum(-1).astype(np.float32)
-        hi = (s32.view(np.uint32) >> 16).astype(np.uint16)
-        assert np.array_equal((hi.astype(np.uint32) << 16).view(np.float32), s32)
-        al = np.stack([hi, np.zeros_like(hi)], 0).transpose(2, 0, 1, 3)   # [S][2][M][8]
+        # alpha: the sum B of each sub-block's 32 qs as 64 * floor(B / 64) and
+        # B mod 64, both exact in bf16 (the low 16 bits of their fp32 are 0)
+        s32 = qs.astype(np.int32).reshape(M, K // 256, 8, 32).sum(-1)
+        p0 = ((s32 // 64) * 64).astype(np.float32)
+        p1 = (s32 - (s32 // 64) * 64).astype(np.float32)
+        parts = [(p.view(np.uint32) >> 16).astype(np.uint16) for p in (p0, p1)]
+        for p, b in zip((p0, p1), parts):
+            assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), p)
+        al = np.stack(parts, 0).transpose(2, 0, 1, 3)                      # [S][2][M][8]
         oa = kq.kq_act_section_offset(act, kq.KQ_SEC_ALPHA, M, K)
         buf[oa:oa + al.nbytes] = np.ascontiguousarray(al).view(np.uint8).reshape(-1)
     return dev(buf)
@@ -203,18 +207,6 @@ def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
         d, t = datagen.random_fields_tq(rng, B)
         W = datagen.pack_tq(t, d)
     return W.reshape(N, -1)
-
-
-def q4k_term_sizes(W: np.ndarray, N: int, K: int) -> np.ndarray:
-    """|d*sc_j*q_k| + |dmin*m_j| per weight, fp64 [N][K], from the oracle codec."""
-    out = np.zeros((N, K))
-    blocks = W.reshape(N, K // 256, 144)
-    for n in range(N):
-        for s in range(K // 256):
-            d, dm, sc, mn, q = kqref.decode_q4k(blocks[n, s])
-            j = np.arange(256) // 32
-            out[n, 256 * s:256 * (s + 1)] = np.abs(d * sc[j] * q) + np.abs(dm * mn[j])
-    return out
 
 
 # (fmt, K, variant, token rows per launch, weight rows); the 128 x 128 Q4_K
@@ -255,12 +247,14 @@ def test_identity_activations_decode_every_position(kq, fmt, K, variant, MT, N):
     assert kq.kq_dispatch_count(names.index(variant)) == K // MT
     assert np.all(np.isfinite(out))
     if fmt == Q4_K:
-        # main term exact (an fp16 d times an integer below 2^10); the min term
-        # -dmin*m_j is carried as bf16 hi + lo (at least 16 significant bits)
-        bound = 2.0 ** -15 * q4k_term_sizes(W, N, K).T + 1e-30
+        # the bound the product is held to: 1e-4 * sum_k |W^ A^| + 1e-6, here
+        # 1e-4 * |W^[n][m]| + 1e-6 (one unit activation per row); the kernels
+        # form d * (sc*q) - dmin * m_j * 1 with two fp32 roundings
+        bound = 1e-4 * np.abs(ref) + 1e-6
         err = np.abs(out.astype(np.float64) - ref)
         worst = np.unravel_index(np.argmax(err / bound), err.shape)
-        assert np.all(err <= bound), f"{variant}: err/bound {(err / bound).max():.3g} at k,n={worst}"
+        say(f"  max err/tol {(err / bound).max():.3g}")
+        assert np.all(err <= bound), f"{variant}: err/tol {(err / bound).max():.3g} at k,n={worst}"
     else:
         bad = np.argwhere(out != ref.astype(np.float32))
         assert bad.size == 0, f"{variant}: {len(bad)} values differ, first at k,n={tuple(bad[0])}"

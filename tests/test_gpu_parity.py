@@ -56,17 +56,20 @@ def bf16_bits_rne(a: np.ndarray) -> np.ndarray:
     return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def expected_alpha(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+def expected_alpha(qs: np.ndarray, d=None) -> np.ndarray:
     """The alpha section [K/256][2][M][8] (bf16 bits) that the Q8_K layout
-    defines: a = d * (sum of the 32 qs of each sub-block) in fp32, then
-    hi = bf16(a), lo = bf16(a - hi)."""
+    defines: for the sum B of the 32 qs of each sub-block, part 0 = 64 *
+    floor(B / 64) and part 1 = B - part 0, both integers bf16 holds exactly
+    (the scales d do not enter)."""
     M, K = qs.shape
     s32 = qs.astype(np.int64).reshape(M, K // 256, 8, 32).sum(-1)          # [M][S][8]
-    a = (d.astype(np.float32)[:, :, None] * s32.astype(np.float32)).astype(np.float32)
-    hi = bf16_bits_rne(a)
-    hi_f = (hi.astype(np.uint32) << 16).view(np.float32)
-    lo = bf16_bits_rne((a - hi_f).astype(np.float32))
-    return np.stack([hi, lo], 0).transpose(2, 0, 1, 3).view(np.int16)     # [S][2][M][8]
+    p0 = (s32 // 64) * 64
+    p1 = s32 - p0
+    assert np.all((p1 >= 0) & (p1 < 64)) and np.all(np.abs(p0) <= 4096)
+    parts = [bf16_bits_rne(p.astype(np.float32)) for p in (p0, p1)]
+    for p, b in zip((p0, p1), parts):   # exact: the bits decode to the integer
+        assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), p.astype(np.float32))
+    return np.stack(parts, 0).transpose(2, 0, 1, 3).view(np.int16)         # [S][2][M][8]
 
 
 def check_act_exact(kq, act_fmt, x, a_q8):
