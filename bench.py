@@ -28,10 +28,18 @@ own rates measured in the same run by the library's calibration kernels
 with 4-10 VALU instructions per MFMA; fp32 VALU; HBM read over 1 GiB);
 `roofline.frac_measured` is `achieved` over the measured rate (changing-operand
 MFMA when compute-bound, HBM read for few tokens).  `cpu_baseline` is the plain CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload (with the host's CPU model).
+
+`configs` reports the other workloads in the same run (by default the 64-token
+FFN projection, the 512-token projection, the Q6_K down projection and the
+ternary projection): GEMM launches only, back to back between two events on
+the launch stream, each with its own roofline and the variant the dispatch
+counters saw run.  `device` holds the SMI's shader and memory clocks and
+package power before and after the run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--no-calib] [--cpu-seconds S] [--copy-mib N]
+                       [--side W1,W2,...] [--side-launches L]
 """
 from __future__ import annotations
 
@@ -62,6 +70,12 @@ GEMM_SOURCES = {
     # (kq_gemm_q4k.hip) or of the other formats' tile kernel (kq_gemm.hip)
     "moe": ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp", "kq_hooks.hpp"),
 }
+
+
+# the other configurations, reported beside the main one in the same line:
+# the 64-token case of the same FFN projection (bound by the weight stream),
+# the 512-token projection, the Q6_K down projection, the ternary projection
+SIDE_WORKLOADS = ("ffn_up_q4k_64", "proj_q4k_4096", "ffn_down_q6k_2048", "tern_5120_2048")
 
 
 def log(*a):
@@ -107,6 +121,10 @@ def main():
                     help="skip the calibration kernels (measured peak rates)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--side", default=",".join(SIDE_WORKLOADS),
+                    help="comma-separated workloads timed after the main one (GEMM launches "
+                         "only, each with its own roofline); empty for none")
+    ap.add_argument("--side-launches", type=int, default=50)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(the reference kernel for scaling profiler byte counters)")
@@ -129,6 +147,7 @@ def main():
     act_fmt = kq.kq_act_fmt_for(fmt)
     dev = torch.device("cuda:0")
 
+    dev_state0 = device_state()
     log(f"[bench] generating {wl.name} M={M} N={N} K={K}")
     W_np, x_np = datagen.make_workload(wl)
     # an expert-indexed workload routes M tokens to topk of E experts: R
@@ -285,10 +304,100 @@ def main():
         rl["measured_peak"] = measured
         rl["frac_measured"] = round(rl["achieved"] / measured, 4)
 
+    side = [w for w in args.side.split(",") if w and w != wl.name]
+    if side:
+        # free the main workload's rotation sets before the others allocate
+        cpu_out = Os[(args.steps - 1) % ncopy].cpu()
+        del Ws, xs, As, Os
+        torch.cuda.empty_cache()
+        result["configs"] = {w: side_config(kq, w, stream, args.side_launches) for w in side}
+    else:
+        cpu_out = Os[(args.steps - 1) % ncopy].cpu()
+    result["device"] = {"before": dev_state0, "after": device_state()}
+
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, W_np, x_np, Os[(args.steps - 1) % ncopy],
-                                              args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, W_np, x_np, cpu_out, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def device_state():
+    """Shader and memory clocks and package power as the SMI reports them
+    (rocm-smi, a few seconds at most); None where a value cannot be read."""
+    import subprocess
+    st = {"sclk_mhz": None, "mclk_mhz": None, "power_w": None}
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+    except Exception:
+        return st
+    for key, pat in (("sclk_mhz", r'"sclk clock speed:"\s*:\s*"\(?(\d+)\s*Mhz'),
+                     ("mclk_mhz", r'"mclk clock speed:"\s*:\s*"\(?(\d+)\s*Mhz'),
+                     ("power_w", r'Power[^"]*"\s*:\s*"([0-9.]+)')):
+        m = re.search(pat, txt, re.I)
+        if m:
+            st[key] = float(m.group(1))
+    return st
+
+
+def side_config(kq, name, stream, launches):
+    """One more workload, GEMM launches only: its activations quantized once
+    per rotating buffer set, then `launches` GEMM launches back to back
+    between two events on the launch stream (mean launch time), the variant
+    that ran taken from the dispatch counters, and its roofline: int8 ops
+    against the 5.0 POP/s peak for M >= 256, else algorithmic bytes against
+    8 TB/s (with the weight bytes alone beside them)."""
+    import torch
+
+    import datagen
+    wl = datagen.WORKLOADS[name]
+    M, N, K, fmt = wl.M, wl.N, wl.K, wl.fmt
+    act_fmt = kq.kq_act_fmt_for(fmt)
+    log(f"[bench] side config {name} M={M} N={N} K={K}")
+    W_np, x_np = datagen.make_workload(wl)
+    w_bytes = kq.kq_weight_bytes(fmt, N, K)
+    a_bytes = kq.kq_act_bytes(act_fmt, M, K)
+    o_bytes = M * N * 4
+    per = w_bytes + a_bytes + o_bytes
+    ncopy = max(1, min(16, -(-ROTATE_BYTES // per)))
+    dev = torch.device("cuda:0")
+    Ws = [torch.from_numpy(W_np).to(dev) for _ in range(ncopy)]
+    x = torch.from_numpy(x_np).to(dev)
+    As = [kq.quantize_act(x, act_fmt) for _ in range(ncopy)]
+    Os = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(ncopy)]
+    sp = stream.cuda_stream
+    for i in range(5):
+        kq.kq_gemm(fmt, Ws[i % ncopy], As[i % ncopy], M, N, K, Os[i % ncopy], sp)
+    torch.cuda.synchronize()
+    before = kq.dispatch_counts()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(launches):
+        kq.kq_gemm(fmt, Ws[i % ncopy], As[i % ncopy], M, N, K, Os[i % ncopy], sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / launches
+    ran = {k: v - before[k] for k, v in kq.dispatch_counts().items() if v != before[k]}
+    variant = max(ran, key=ran.get)
+    assert ran[variant] == launches, ran
+    ops = 2.0 * M * N * K
+    out = {"fmt": datagen.FMT_NAMES[fmt], "M": M, "N": N, "K": K, "seed": wl.seed,
+           "gemm_us": round(t * 1e6, 2), "tops": round(ops / t / 1e12, 2),
+           "tok_per_s": round(M / t, 1), "launches": launches}
+    if M >= 256:
+        tops = ops / t / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK_INT8_TOPS,
+                           "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4), "kernel": variant,
+                           "traffic": measured_traffic(name, datagen.FMT_NAMES[fmt])}
+    else:
+        gbs = per / t / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": variant,
+                           "weight_gbs": round(w_bytes / t / 1e9, 1),
+                           "frac_on_weights": round(w_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                           "traffic": measured_traffic(name, datagen.FMT_NAMES[fmt])}
+    del Ws, As, Os, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def calibrate(kq, stream):
@@ -378,10 +487,17 @@ def _cpu_baseline(wl, label, W_np, x_np, out_dev, target_s):
     check = rows[:: max(1, nrows // 8)][:8]
     ref, tol = kqref.gemm(wl.fmt, W_np, qs, d, wl.K, rows=check)
     import torch
-    got = out_dev[:, torch.from_numpy(check).to(out_dev.device)].cpu().numpy()
+    got = out_dev[:, torch.from_numpy(check)].numpy()
     ratio = float((np.abs(got.astype(np.float64) - ref) / tol).max())
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            m = re.search(r"^model name\s*:\s*(.+)$", f.read(), re.M)
+            model = m.group(1).strip() if m else None
+    except OSError:
+        pass
     return {"value": round(ops / t_sample / 1e12, 6), "unit": "TOPS", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{label}: all {Mx} tokens x {nrows} of {wl.N} weight rows (random), "
                       f"K={wl.K}; plain C oracle (fp32 Q8 quantize + fp64 "
                       f"dequantize-and-multiply), gcc -O2 -fopenmp; quantize {tq:.2f} s for all "
