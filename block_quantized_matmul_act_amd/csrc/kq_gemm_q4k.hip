@@ -259,20 +259,30 @@ struct WRaw {
     v4i hdr, q[4];
 };
 
-template <int BM, bool GATHER = false>
-__global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Args a) {
-    static_assert(!GATHER || BM == 64, "gather mode stages one routed row per lane");
+// KS = 2: one workgroup of 8 waves per CU instead of two of 4.  Waves 4h ..
+// 4h+3 (half h) take superblock 2i+h of superblock pair i, each half its own
+// region of the staging slot; at the end of a tile half 1 hands its sums to
+// half 0 through LDS.  A CU then owns whole tiles at twice the rate, so the
+// tile count balances over CUs rather than over twice as many workgroups.
+template <int BM, bool GATHER = false, int KS = 1>
+__global__ __launch_bounds__(NT * KS, KS == 1 ? TileCfg<BM>::WG_PER_CU : 1) void gemm_q4k_kernel(Args a) {
+    static_assert(!GATHER || (BM == 64 && KS == 1), "gather mode stages one routed row per lane");
+    static_assert(KS == 1 || KS == 2, "one or two superblocks per step");
     using TC = TileCfg<BM>;
     constexpr int MT = TC::MT;
-    __shared__ __attribute__((aligned(16))) int8_t s_a0[TC::ABUF], s_a1[TC::ABUF];
-    __shared__ __attribute__((aligned(16))) float s_d0[TC::DBUF], s_d1[TC::DBUF];
-    __shared__ __attribute__((aligned(16))) int8_t s_l0[TC::LBUF], s_l1[TC::LBUF];
+    // a slot holds KS superblocks, half h's at offset h * (ABUF, DBUF, LBUF)
+    __shared__ __attribute__((aligned(16))) int8_t s_a0[KS * TC::ABUF], s_a1[KS * TC::ABUF];
+    __shared__ __attribute__((aligned(16))) float s_d0[KS * TC::DBUF], s_d1[KS * TC::DBUF];
+    __shared__ __attribute__((aligned(16))) int8_t s_l0[KS * TC::LBUF], s_l1[KS * TC::LBUF];
     const Slot slots[2] = {{s_a0, s_d0, s_l0}, {s_a1, s_d1, s_l1}};
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    // weight strip of this wave (its 32 output columns) and its half
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & (NWAVE - 1));
+    const int half = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
     const int ln = lane & 31, g = lane >> 5;
     const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int npair = (nsb + KS - 1) / KS;  // steps per tile
 
     // ---- persistent tile list ----------------------------------------------
     // Workgroups are dealt round-robin to the 8 XCDs.  At step k the grid
@@ -290,7 +300,7 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     }
     const int ntiles = tiles_m * a.tiles_n;
     const int my_tiles = (ntiles - slot_in_step + G - 1) / G;    // tiles slot, slot+G, ...
-    const int total = my_tiles * nsb;                            // flat iterations
+    const int total = my_tiles * npair;                          // flat iterations
     const int rowbytes = nsb * BB;
     if (total <= 0) return;  // uniform: no barrier is ever reached
 
@@ -351,7 +361,11 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
             o.gd = 4 * token(T, lane);
         }
     };
-    auto stage = [&](const Slot &S, TileXY T, int sbx, const GOff &o) {
+    auto stage = [&](const Slot &S0, TileXY T, int px, const GOff &o) {
+        // this half's superblock of step px, into its region of the slot
+        const int sbx = KS * px + half;
+        if (KS > 1 && sbx >= nsb) return;  // uniform: an odd superblock count's last step
+        const Slot S = KS == 1 ? S0 : Slot{S0.a + half * TC::ABUF, S0.d + half * TC::DBUF, S0.l + half * TC::LBUF};
         if constexpr (GATHER) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) copy16(rs_a, S.a + (CPW * wave + i) * 1024, o.ga[i], sbx * ROW);
@@ -379,8 +393,9 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     // (constant offsets go to the scalar operand: one address register per lane)
     const int w_row = (32 * wave + ln) * rowbytes;
     const int w_nib = w_row + 64 * g;
-    auto load_w = [&](TileXY T, int sbx, WRaw &R) {
-        const int so = T.n0 * rowbytes + sbx * BB;
+    auto load_w = [&](TileXY T, int px, WRaw &R) {
+        // (past an odd count's last superblock: a repeat of it, unused)
+        const int so = T.n0 * rowbytes + (KS == 1 ? px : min(KS * px + half, nsb - 1)) * BB;
         const auto rw = rs_w_of(T);
         R.hdr = ld16(rw, w_row, so);
 #pragma unroll
@@ -394,7 +409,9 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
     // superblock, their high nibbles (s >= 4) the same plus 32.
     // p = 8g + c(s) with c < 8, so p ^ (ln % 16) splits into bit 3 (fixed
     // per lane) and bits 0..2: one XOR with a constant per K-step.
-    const int frag_base = ln * ROW + (((8 * g) ^ (ln & 8)) << 4);
+    const int frag_base = half * TC::ABUF + ln * ROW + (((8 * g) ^ (ln & 8)) << 4);
+    const int d_lane = half * TC::DBUF + 4 * g;          // this half's scales, + 32t + 8q
+    const int l_lane = half * TC::LBUF + ln * 16 + 8 * g;  // this half's min-term parts, + 32*16*t
     const int frag_x = (ln & 7) << 4;
     auto frag = [&](int s) {
         const int c = 4 * ((s & 3) >> 1) + (s & 1) + 2 * (s >> 2);
@@ -420,6 +437,8 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
 
     auto iteration = [&](auto PP, int it) {
         constexpr int P = decltype(PP)::value;
+        // (this half's region of the slot: its offsets ride in the per-lane
+        // read bases frag_base, d_lane and l_lane)
         const Slot &S = slots[P];
         // everything this wave copied or loaded for iteration it (one
         // iteration ago) has landed; after the barrier, so has every other
@@ -427,7 +446,8 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
         wait_vmcnt<0>();
         barrier_nofence();
         const bool more = it + 1 < total;
-        const bool last_sb = sb + 1 == nsb;
+        const bool last_sb = sb + 1 == npair;  // sb counts steps of KS superblocks
+        const bool mine = KS == 1 || KS * sb + half < nsb;  // this half has a superblock this step
         const TileXY Tn = last_sb ? TN : T;
         const int sbn = last_sb ? 0 : sb + 1;
         // the next superblock's activations and weights, a whole iteration
@@ -445,103 +465,129 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
             load_w(Tn, sbn, wring[1 - P]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // scale digits of sub-blocks 4g..4g+3 (fields 4g.. of the 96-bit word)
-        const uint32_t w1 = (uint32_t)wc.hdr[1], w2 = (uint32_t)wc.hdr[2], w3 = (uint32_t)wc.hdr[3];
-        const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
-        const float dw = f16_bits_to_f32((uint32_t)wc.hdr[0]);
-        const float dmin = f16_bits_to_f32((uint32_t)wc.hdr[0] >> 16);
+        if (mine) {  // uniform
+            // scale digits of sub-blocks 4g..4g+3 (fields 4g.. of the 96-bit word)
+            const uint32_t w1 = (uint32_t)wc.hdr[1], w2 = (uint32_t)wc.hdr[2], w3 = (uint32_t)wc.hdr[3];
+            const uint32_t x24 = g ? __builtin_amdgcn_alignbit(w2, w1, 24) : w1;
+            const float dw = f16_bits_to_f32((uint32_t)wc.hdr[0]);
+            const float dmin = f16_bits_to_f32((uint32_t)wc.hdr[0] >> 16);
 
-        // pass 1: high digits (sc >> 3) over the whole superblock; pass 2: low
-        // digits (sc & 7) into the same accumulators after a shift by 3.  The
-        // fragments of K-step s+1 are read while K-step s multiplies.
-        // (scheduling fences pin the reads of K-step s+1 ahead of the MFMAs
-        // of K-step s; left alone, the scheduler sinks each read to just
-        // before its MFMA and every MFMA waits out a full LDS latency)
-        // The two workgroups on a CU put one wave on each SIMD.  While this
-        // wave multiplies it takes issue priority, so the other wave's fold
-        // and unpacking fill the issue slots between its MFMAs.
-        __builtin_amdgcn_s_setprio(2);
+            // pass 1: high digits (sc >> 3) over the whole superblock; pass 2: low
+            // digits (sc & 7) into the same accumulators after a shift by 3.  The
+            // fragments of K-step s+1 are read while K-step s multiplies.
+            // (scheduling fences pin the reads of K-step s+1 ahead of the MFMAs
+            // of K-step s; left alone, the scheduler sinks each read to just
+            // before its MFMA and every MFMA waits out a full LDS latency)
+            // The two workgroups on a CU put one wave on each SIMD.  While this
+            // wave multiplies it takes issue priority, so the other wave's fold
+            // and unpacking fill the issue slots between its MFMAs.
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            v4i av[2][MT];
+            for (int pass = 0; pass < 2; ++pass) {
+                v4i av[2][MT];
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(0));
+                for (int t = 0; t < MT; ++t)
+                    av[0][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(0));
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < 8) {
+                for (int s = 0; s < 8; ++s) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s + 1 < 8) {
+#pragma unroll
+                        for (int t = 0; t < MT; ++t)
+                            av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(s + 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int si = 2 * ((s & 3) >> 1) + (s >> 2);  // sub-block 4g + si
+                    const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
+                    v4i bq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t q = (uint32_t)wc.q[s & 3][e];
+                        bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
+                    }
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
-                        av[(s + 1) & 1][t] = *reinterpret_cast<const v4i *>(S.a + t * 32 * ROW + frag(s + 1));
+                        acc[t] = (pass == 0 && s == 0) ? mma_i8(av[s & 1][t], bq, v16i{})
+                                                       : mma_i8(av[s & 1][t], bq, acc[t]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                const int si = 2 * ((s & 3) >> 1) + (s >> 2);  // sub-block 4g + si
-                const uint32_t dig = pass == 0 ? (x24 >> (6 * si + 3)) & 7u : (x24 >> (6 * si)) & 7u;
-                v4i bq;
+                if (pass == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t q = (uint32_t)wc.q[s & 3][e];
-                    bq[e] = mul_digit(s < 4 ? q & 0x0F0F0F0Fu : (q >> 4) & 0x0F0F0F0Fu, dig);
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[t][r] <<= 3;
+                    // re-read the operands in pass 2 rather than keeping all of
+                    // pass 1's live (registers are the scarcer unit)
+                    asm volatile("" ::: "memory");
                 }
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    acc[t] = (pass == 0 && s == 0) ? mma_i8(av[s & 1][t], bq, v16i{})
-                                                   : mma_i8(av[s & 1][t], bq, acc[t]);
             }
-            if (pass == 0) {
+            __builtin_amdgcn_s_setprio(0);
+            // min term, exactly: M = sum_j m_j * B_j with B_j the sum of the
+            // sub-block's 32 quantized activations (staged as two bf16 parts that
+            // are exact, 64*floor(B_j/64) and B_j mod 64); one bf16 MFMA per
+            // m-tile, all products and partial sums integers below 2^24.  k-group
+            // g carries sub-blocks 4g..4g+3: A row m holds both parts of those, B
+            // the mins m_j twice.
+            // fold: out += d_a[m] * (d[n] * float(sum_k sc*q*a) - dmin[n] * M)
+            {
+                // mins m_j: bits 48 + 6j of the 96-bit word (words w1, w2, w3)
+                const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);  // bits 32..95
+                const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));      // fields 4g..4g+3
+                v8bf bm;
 #pragma unroll
-                for (int t = 0; t < MT; ++t)
+                for (int i = 0; i < 4; ++i) {
+                    const __bf16 m = (__bf16)(float)((mx >> (6 * i)) & 63u);
+                    bm[i] = m;
+                    bm[4 + i] = m;
+                }
+                const float ndmin = -dmin;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[t][r] <<= 3;
-                // re-read the operands in pass 2 rather than keeping all of
-                // pass 1's live (registers are the scarcer unit)
-                asm volatile("" ::: "memory");
-            }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // min term, exactly: M = sum_j m_j * B_j with B_j the sum of the
-        // sub-block's 32 quantized activations (staged as two bf16 parts that
-        // are exact, 64*floor(B_j/64) and B_j mod 64); one bf16 MFMA per
-        // m-tile, all products and partial sums integers below 2^24.  k-group
-        // g carries sub-blocks 4g..4g+3: A row m holds both parts of those, B
-        // the mins m_j twice.
-        // fold: out += d_a[m] * (d[n] * float(sum_k sc*q*a) - dmin[n] * M)
-        {
-            // mins m_j: bits 48 + 6j of the 96-bit word (words w1, w2, w3)
-            const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);  // bits 32..95
-            const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));      // fields 4g..4g+3
-            v8bf bm;
+                for (int t = 0; t < MT; ++t) {
+                    const int8_t *lp = S.l + 32 * 16 * t + l_lane;
+                    const v2u ap0 = *reinterpret_cast<const v2u *>(lp);
+                    const v2u ap1 = *reinterpret_cast<const v2u *>(lp + BM * 16);
+                    const v4i avv = {(int)ap0.x, (int)ap0.y, (int)ap1.x, (int)ap1.y};
+                    const v16f mt = mma_bf16(__builtin_bit_cast(v8bf, avv), bm, v16f{});
+                    v4f da4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const __bf16 m = (__bf16)(float)((mx >> (6 * i)) & 63u);
-                bm[i] = m;
-                bm[4 + i] = m;
-            }
-            const float ndmin = -dmin;
+                    for (int q = 0; q < 4; ++q)
+                        da4[q] = *reinterpret_cast<const v4f *>(S.d + 32 * t + 8 * q + d_lane);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int8_t *lp = S.l + (32 * t + ln) * 16 + 8 * g;
-                const v2u ap0 = *reinterpret_cast<const v2u *>(lp);
-                const v2u ap1 = *reinterpret_cast<const v2u *>(lp + BM * 16);
-                const v4i avv = {(int)ap0.x, (int)ap0.y, (int)ap1.x, (int)ap1.y};
-                const v16f mt = mma_bf16(__builtin_bit_cast(v8bf, avv), bm, v16f{});
-                v4f da4[4];
+                    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    da4[q] = *reinterpret_cast<const v4f *>(S.d + 32 * t + 8 * q + 4 * g);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * q + i;
-                        out[t][r] = fmaf(fmaf((float)acc[t][r], dw, mt[r] * ndmin), da4[q][i], out[t][r]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * q + i;
+                            out[t][r] = fmaf(fmaf((float)acc[t][r], dw, mt[r] * ndmin), da4[q][i], out[t][r]);
+                        }
                     }
                 }
             }
         }
 
-        if (last_sb) {
+        if constexpr (KS == 2) {
+            if (last_sb) {
+                // half 1 hands its sums to half 0 through the activation
+                // region of this slot, once every wave is done reading it
+                // (the next step's copies into it wait for the next barrier)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                barrier_nofence();
+                float *red = reinterpret_cast<float *>(slots[P].a);
+                if (half == 1) {
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) red[((wave * MT + t) * 16 + r) * 64 + lane] = out[t][r];
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                barrier_nofence();
+                if (half == 0) {
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) out[t][r] += red[((wave * MT + t) * 16 + r) * 64 + lane];
+                }
+            }
+        }
+        if (last_sb && half == 0) {
             // epilogue of tile T: rows past M fall outside the resource and
             // are dropped; columns past N are sent out of range
             const int n = T.n0 + 32 * wave + ln;
@@ -559,6 +605,8 @@ __global__ __launch_bounds__(NT, TileCfg<BM>::WG_PER_CU) void gemm_q4k_kernel(Ar
                     __builtin_amdgcn_raw_buffer_store_b32(bits[r], ro, voff, (orow0 + row) * N * 4, 0);
                 }
             }
+        }
+        if (last_sb) {
 #pragma unroll
             for (int t = 0; t < MT; ++t) out[t] = v16f{};
         }
@@ -1109,26 +1157,6 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
 
 }  // namespace q4w
 
-
-static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
-constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
-
-// Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
-// kernel; up to 64 -> the K-split weight-streaming kernel; otherwise the
-// persistent tile kernel (two workgroups per CU), 128 x 128 when that tiling
-// has more tiles than the chip has CUs (256), else 64 x 128: below that the
-// taller tile leaves CUs idle, above it the shorter tile's extra unpacking
-// (twice the weight work per output) and tail cost more than they gain.
-constexpr int TILE64_MAX_TILES128 = 256;
-int q4k_kernel_choice(int M, int N, int K) {
-    if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
-        q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
-        return Q4K_MATVEC;
-    if (M <= 64) return Q4K_FEW_TOKENS;
-    const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    return tiles128 > TILE64_MAX_TILES128 ? Q4K_TILE128 : Q4K_TILE64;
-}
-
 // Compute units of the current device, cached per device (the persistent
 // grids are sized from it).  Concurrent first calls may both query; they
 // store the same value.
@@ -1146,6 +1174,44 @@ static int num_cus() {
         cus = 256;
     if (dev < MAX_DEV) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
+}
+
+static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
+constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
+
+// Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
+// kernel; up to 64 -> the K-split weight-streaming kernel; otherwise the
+// persistent tile kernel (two workgroups per CU), 128 x 128 when that tiling
+// has more tiles than the chip has CUs (256), else 64 x 128: below that the
+// taller tile leaves CUs idle, above it the shorter tile's extra unpacking
+// (twice the weight work per output) and tail cost more than they gain.
+constexpr int TILE64_MAX_TILES128 = 256;
+// Persistent grids: two 4-wave workgroups per CU (KS = 1) or one 8-wave
+// workgroup per CU that works on two superblocks at a time (KS = 2), which
+// finishes a tile in about half the time.  The tiles are dealt in rounds of
+// one tile per workgroup; the last round may be partly empty.  In units of
+// one KS = 1 tile time, KS = 1 takes ceil(tiles / 2c) and KS = 2 takes
+// ceil(tiles / c) / 2 for c CUs: KS = 2 wins when the tile count leaves the
+// last KS = 1 round at most half full.  Measured for the 64-row tile on
+// K = 4096: 512 x 4096 (256 tiles) 27.3 against 32.4 us, 200 x 4096 22.8
+// against 27.4 us; 1024 x 4096 and 256 x 14336 (448-512 tiles) keep KS = 1
+// (43.8 / 45.8 us against 50.3 / 52.5).  The 128-row tile at KS = 2 needs
+// more than 256 VGPRs per lane and spills: it ran 420 against 308 us on
+// 2048 x 14336, so that tile height keeps KS = 1 everywhere.
+static bool split_pays(int64_t tiles, int cus) {
+    const int64_t r1 = (tiles + 2 * cus - 1) / (2 * cus), r2 = (tiles + cus - 1) / cus;
+    return r2 < 2 * r1;
+}
+int q4k_kernel_choice(int M, int N, int K) {
+    if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
+        q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
+        return Q4K_MATVEC;
+    if (M <= 64) return Q4K_FEW_TOKENS;
+    const int cus = num_cus();
+    const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
+    const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+    return split_pays(tiles64, cus) ? Q4K_TILE64_K2 : Q4K_TILE64;
 }
 
 bool q4k_id_tile_ok(int N, int K) {
@@ -1210,7 +1276,7 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     a.K = K;
     a.nsb = K / 256;
     const int choice = q4k_kernel_choice(M, N, K);
-    const int bm = choice == Q4K_TILE64 ? 64 : 128;
+    const int bm = (choice == Q4K_TILE64 || choice == Q4K_TILE64_K2) ? 64 : 128;
     a.tiles_m = (M + bm - 1) / bm;
     a.tiles_n = (N + q4w::BN - 1) / q4w::BN;
     a.ntiles = a.tiles_m * a.tiles_n;
@@ -1238,6 +1304,12 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             hipLaunchKernelGGL(q4w::gemm_q4k_kernel<64>, dim3(grid), dim3(q4w::NT), 0, stream, a);
             break;
         }
+        case Q4K_TILE64_K2: {
+            const unsigned grid = (unsigned)min(a.ntiles, cus);
+            hipLaunchKernelGGL((q4w::gemm_q4k_kernel<64, false, 2>), dim3(grid), dim3(2 * q4w::NT), 0, stream, a);
+            break;
+        }
+
         default: {
             const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<128>::WG_PER_CU * cus);
             hipLaunchKernelGGL(q4w::gemm_q4k_kernel<128>, dim3(grid), dim3(q4w::NT), 0, stream, a);

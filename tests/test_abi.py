@@ -164,14 +164,17 @@ def test_variants_and_counters(kq):
         for M in (1, 8, 64, 65, 2048):
             v = kq.kq_select_variant(fmt, M, 4096, 4096 if fmt < kq.KQ_TQ else 5120)
             assert 0 <= v < n
-    # Q4_K tile heights: 128 x 128 above 256 such tiles, else 64 x 128
+    # Q4_K tile heights: 128 x 128 above 256 such tiles, else 64 x 128; the
+    # 8-wave 64 x 128 build when the 64-row tiles are at most one per CU
+    # (the CU count without a device is taken as 256)
     q4 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_Q4_K, M, N, K))
-    assert q4(2048, 2048, 4096) == "gemm_q4_k_64x128"    # 16 x 16 tiles
+    assert q4(2048, 2048, 4096) == "gemm_q4_k_64x128"    # 16 x 16 tiles (32 x 16 of 64 rows)
     assert q4(2048, 2049, 4096) == "gemm_q4_k_128x128"   # 16 x 17
     assert q4(1536, 4096, 4096) == "gemm_q4_k_128x128"   # 12 x 32
-    assert q4(512, 4096, 4096) == "gemm_q4_k_64x128"
+    assert q4(512, 4096, 4096) == "gemm_q4_k_64x128_k2"  # 8 x 32 tiles of 64 rows
+    assert q4(576, 4096, 4096) == "gemm_q4_k_64x128"     # 9 x 32
     assert q4(2048, 14336, 4096) == "gemm_q4_k_128x128"
-    assert q4(65, 4096, 4096) == "gemm_q4_k_64x128"
+    assert q4(65, 4096, 4096) == "gemm_q4_k_64x128_k2"
     assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
     # two-bit ternary always runs on the tile kernel
     for M in (1, 8, 2048):

@@ -107,12 +107,16 @@ def assert_exact(out, want, what):
 # ------------------------------------------------------------------ Q4_K
 
 # (variant, M, N, K): the 128 x 128 tile needs more than 256 such tiles
-# (3 x 86); the few-token kernel has a one- and a two-m-tile build; the
-# matrix-vector kernel takes one or two tokens with K a multiple of 2048
+# (3 x 86); the 4-wave 64 x 128 tile more than 256 of its own (3 x 100); the
+# 8-wave 64 x 128 build takes the smaller counts (K = 768: an odd number of
+# superblocks, so one half of its waves sits out the last step); the
+# few-token kernel has a one- and a two-m-tile build; the matrix-vector
+# kernel takes one or two tokens with K a multiple of 2048
 Q4K_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 256),
-    ("gemm_q4_k_64x128", 70, 96, 256),
-    ("gemm_q4_k_64x128", 129, 200, 512),
+    ("gemm_q4_k_64x128", 192, 12800, 256),
+    ("gemm_q4_k_64x128_k2", 70, 96, 256),
+    ("gemm_q4_k_64x128_k2", 129, 200, 768),
     ("gemm_q4_k_m64", 64, 200, 256),
     ("gemm_q4_k_m64", 20, 200, 512),
     ("gemm_q4_k_matvec", 1, 100, 2048),
@@ -285,7 +289,7 @@ def stress_weights(N, K, seed, kind):
 
 HEADROOM_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 512),
-    ("gemm_q4_k_64x128", 129, 640, 1024),
+    ("gemm_q4_k_64x128_k2", 129, 640, 1024),
     ("gemm_q4_k_m64", 64, 640, 1024),
     ("gemm_q4_k_matvec", 2, 640, 2048),
 ]

@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 Q4_K, Q6_K, TQ, TQ2 = 1, 2, 3, 4
 FMTS = (Q4_K, Q6_K, TQ, TQ2)
+FMT_NAME = {Q4_K: "q4_k", Q6_K: "q6_k", TQ: "tq", TQ2: "tq2"}
 QK = {Q4_K: 256, Q6_K: 256, TQ: 128, TQ2: 128}
 SUB = {Q4_K: 32, Q6_K: 16, TQ: 128, TQ2: 128}
 
@@ -260,13 +261,14 @@ def test_large_ragged_tiles(kq, workloads):
 
 def test_q4k_tile_heights(kq):
     """The Q4_K tile kernel in both heights at shapes ragged in M and N: 128 x
-    128 (a shape of more than 256 such tiles: 3 x 86) and 64 x 128 just below
-    that count (3 x 85), with a short K so the full output is compared."""
+    128 (a shape of more than 256 such tiles: 3 x 86), 64 x 128 just below
+    that count (3 x 85), and the 8-wave 64 x 128 build for shapes of at most
+    one 64 x 128 tile per CU, with a short K so the full output is compared."""
     K = 512
     W = datagen.make_weights(Q4_K, 11000, K, 4848)
     x = datagen.draw_activations(300, K, 4949)
     for M, N, name in ((300, 11000, "gemm_q4_k_128x128"), (300, 10880, "gemm_q4_k_64x128"),
-                       (65, 4000, "gemm_q4_k_64x128"), (129, 200, "gemm_q4_k_64x128")):
+                       (65, 4000, "gemm_q4_k_64x128_k2"), (129, 200, "gemm_q4_k_64x128_k2")):
         v = kq.kq_select_variant(Q4_K, M, N, K)
         assert kq.kq_variant_name(v) == name, (M, N)
         say(f"q4k tile {name} M={M} N={N} K={K}")
@@ -473,10 +475,12 @@ def test_gemm_id_matches_oracle(kq, fmt):
         toks = rows[r0:r1]
         ref, tol = kqref.gemm(fmt, Ws[e], np.ascontiguousarray(qs[toks]), np.ascontiguousarray(d[toks]), K)
         assert_within_tol(out[r0:r1], ref, tol, f"gemm_id fmt={fmt} expert {e}")
-        if r1 - r0 > (64 if fmt == Q4_K else 8):
+        same = {Q4_K: ("gemm_q4_k_64x128", "gemm_q4_k_128x128")}.get(fmt, (f"gemm_{FMT_NAME[fmt]}_128x128",))
+        if kq.kq_variant_name(kq.kq_select_variant(fmt, r1 - r0, N, K)) in same:
             # the plain product of the same tile kernel on the gathered tokens
-            # (Q4_K: a tile kernel from 65 tokens on, either height):
-            # identical arithmetic, identical bits
+            # (Q4_K: a 4-wave tile kernel, either height): identical
+            # arithmetic, identical bits (the 8-wave build adds its two
+            # superblock streams in another order)
             xg = np.ascontiguousarray(x[toks])
             plain = run_gemm(kq, fmt, Ws[e], run_quant(kq, act_fmt, xg), r1 - r0, N, K)
             assert np.array_equal(out[r0:r1], plain), f"expert {e} differs from kq_gemm"
