@@ -966,6 +966,316 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 }
 
 // ---------------------------------------------------------------------------
+// Few tokens, K split over the waves of a workgroup (M <= 16 in use).
+// A workgroup of KW waves owns 32 weight rows; wave w takes superblocks w,
+// w + KW, w + 2KW, ... for every token row (MT 16-row m-tiles), so the waves
+// of a workgroup read neighbouring bytes of the same weight rows.  At the end
+// the KW partial sums are added through LDS in a fixed order.  On 14336 x
+// 4096 weights that is 448 workgroups of 4 waves: two waves on most SIMDs,
+// where the two-wave kernel above leaves at most one.
+// Activation fragments go straight from memory into registers, half a
+// superblock ahead: every workgroup reads the same few token rows, so they
+// come from L2, and staging them in LDS per wave would cap the waves per CU.
+// The 16 x 16 x 64 int8 MFMA keeps the wasted rows of a few-token product
+// to one 16-row tile, and its A operand is 16 rows of 64 contiguous bytes: a
+// fragment load touches 16 64-byte pieces where a 32-row operand touches 64
+// half-used ones (a 32-row build measured three times the L1 accesses of
+// the two-wave kernel, with the address unit stalled on the L1 40% of the
+// time).
+// The weights and the fold data (activation scales and min-term operands of
+// a superblock) stream through a small per-wave LDS ring with coalesced
+// buffer -> LDS copies.  No barrier is needed until the final sum.
+// Past 16 tokens the kernel loses to the two-wave kernel: its waves spend
+// most of their time waiting on memory (the vector-memory counter counts in
+// issue order, so waiting for the next half's activation loads also waits
+// for every weight copy issued before them, and a weight stage gets at most
+// two halves to arrive), and the m-tile registers leave no room to load the
+// activations further ahead.
+//
+// v_mfma_i32_16x16x64_i8: lane l supplies row l % 16 of A and column l % 16
+// of B with k-group l / 16 (16 values each); register i of the 4-register
+// result holds row 4(l/16) + i, column l % 16.
+// K order: K-step s (0..3) of a superblock covers values 64s .. 64s+63, lane
+// group kg the 16 values k = 64s + 16kg + i, all in sub-block j = 2s + kg/2.
+// In the Q4_K nibble layout (32-byte group u holds weights 64u + o in its
+// low nibbles and 64u + 32 + o in its high nibbles, o = byte within the
+// group) those are the low (kg < 2) or high (kg >= 2) nibbles of bytes 32s +
+// 16(kg % 2) + i: piece 2(s % 2) + kg % 2 of the 64 nibble bytes of half s/2.
+// ---------------------------------------------------------------------------
+constexpr int KWS = SWN + SHD;  // weight stage: nibbles of one half of 32 blocks, their headers
+constexpr int KFS = SDS + SLS;  // fold data of one superblock: scales and min-term parts of 64 rows
+
+__device__ __forceinline__ v4i mma16_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mma16_bf16(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int MT, int KW, int DW>
+struct SplitCfg {
+    static_assert(MT == 1 || MT == 2 || MT == 4, "16-row m-tiles: up to 16, 32 or 64 tokens");
+    static_assert(DW >= 2, "a weight stage is waited for two halves after its copies are issued");
+    static_assert((8 * MT) % KW == 0, "the final sum deals output registers evenly over the waves");
+    static constexpr int RING = (DW + 1) * KWS;
+    static constexpr int LDS = RING + KFS;  // per wave
+    static_assert(LDS >= 8 * MT * 64 * 4, "the final sum reuses each wave's stages");
+    // buffer -> LDS copies of weight stage x: two of nibbles, plus two of
+    // headers for a first half
+    static constexpr int szW(int x) { return 2 + 2 * (1 - (x & 1)); }
+};
+
+template <int MT, int KW, int DW>
+__global__ __launch_bounds__(64 * KW, 8 / KW) void gemm_q4k_split_kernel(Args a) {
+    using C = SplitCfg<MT, KW, DW>;
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[KW][C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int n0 = blockIdx.x * 32;
+    const int rowbytes = nsb * BB;
+    const int nk = (nsb - w + KW - 1) / KW;  // superblocks of this wave (0 if nsb <= w)
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+
+    // activation fragment of m-tile t: row 16t + r16, bytes 64s + 16kg of the
+    // superblock (rows past M read as zero)
+    int a_vo[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_vo[t] = (16 * t + r16) * K + 16 * kg;
+    // Weight stage: nibble copy i puts piece (l%4) ^ ((l/8)%4) of the 64
+    // nibble bytes of row 16i + l/4 at LDS piece 64i + l, so that row r's
+    // piece p sits at 4r + (p ^ ((r/2)%4)) and the 16-byte reads below, eight
+    // consecutive rows at a time, hit all 32 banks; header copy i puts dword
+    // l%4 of row 16i + l/4 at dword 64i + l.  (Row offsets as unsigned: rows
+    // past N in the last strip may pass 2^31, and the range check drops them.)
+    const uint32_t wr0 = (uint32_t)(n0 + (lane >> 2)) * (uint32_t)rowbytes;
+    const uint32_t wr1 = wr0 + 16u * (uint32_t)rowbytes;
+    const int wsw = 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+    const int w_vb0 = (int)(wr0 + 16 + wsw), w_vb1 = (int)(wr1 + 16 + wsw);
+    const int h_vb0 = (int)(wr0 + 4 * (lane & 3)), h_vb1 = (int)(wr1 + 4 * (lane & 3));
+    // this lane's pieces (K-step 2H + ss, n-tile nt): row 16nt + r16, piece
+    // 2ss + kg%2
+    uint32_t wo[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            const int r = 16 * nt + r16;
+            wo[nt][ss] = 16 * (4 * r + ((2 * ss + (kg & 1)) ^ ((r >> 1) & 3)));
+        }
+    const uint32_t nib_sh = 4 * (kg >> 1);  // high nibbles for k-groups 2, 3
+
+    int8_t *const ring = &s_lds[w][0];
+    int8_t *const fold = &s_lds[w][C::RING];
+    const uint32_t ring_addr = lds_addr(ring), fold_addr = lds_addr(fold);
+    // stage x: superblock w + KW * min(x/2, nk - 1) (past the end: a repeat
+    // of the last, never used), half x % 2
+    auto sb_of = [&](int x) { return w + KW * min(x >> 1, nk - 1); };
+
+    v4i av[2][MT][2];  // activation fragments of the halves of parity 0 / 1
+    // A stage: the activation fragments of half x; an odd x also brings the
+    // superblock's fold data (the previous superblock's was read in full one
+    // half earlier).  Copies are pinned between compiler memory barriers
+    // (the LDS reads are asm the compiler does not see as memory accesses).
+    auto issueA = [&](auto PP, int x) __attribute__((always_inline)) {
+        constexpr int P = decltype(PP)::value;
+        asm volatile("" ::: "memory");
+        const int sb = sb_of(x);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) av[P][t][ss] = ld16(rs_a, a_vo[t], sb * ROW + 128 * P + 64 * ss);
+        if (P == 1) {
+            copy4(rs_d, fold, 4 * lane, sb * M * 4);
+            copy16(rs_l, fold + SDS, 16 * lane, sb * 2 * M * 16);
+            copy16(rs_l, fold + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
+        }
+        asm volatile("" ::: "memory");
+    };
+    auto issueW = [&](int x) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        const int H = x & 1;
+        const int sb = sb_of(x);
+        int8_t *S = ring + (x % (DW + 1)) * KWS;
+        copy16(rs_w, S, w_vb0, sb * BB + 64 * H);
+        copy16(rs_w, S + 1024, w_vb1, sb * BB + 64 * H);
+        if (H == 0) {
+            copy4(rs_w, S + SWN, h_vb0, sb * BB);
+            copy4(rs_w, S + SWN + 256, h_vb1, sb * BB);
+        }
+        asm volatile("" ::: "memory");
+    };
+
+    v4f out[2][MT];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) out[nt][t] = v4f{};
+    v4i acc_h[2][MT], acc_l[2][MT];
+    v4i hdr[2];
+
+    // half j (parity H): the weights of stage j landed DW halves after their
+    // copies were issued; this half's activation fragments and fold data were
+    // issued one half ago, followed only by the copies of weight stage
+    // j - 1 + DW
+    auto half = [&](auto HH, int j) __attribute__((always_inline)) {
+        constexpr int H = decltype(HH)::value;
+        // (scheduling fences keep each half's wait and copies in place: the
+        // scheduler would otherwise hoist the next half's wait into this
+        // half's multiplies, and the next activation loads ahead of this
+        // half's weight copies, which shortens what the waits leave in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::szW((H + 1 + DW) & 1)>();
+        issueA(std::integral_constant<int, 1 - H>{}, j + 1);
+        issueW(j + DW);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t SW = ring_addr + (uint32_t)((j % (DW + 1)) * KWS);
+        if (H == 0) {
+            hdr[0] = lds_read16<SWN>(SW + 16 * r16);
+            hdr[1] = lds_read16<SWN + 256>(SW + 16 * r16);
+        }
+        v4i wq[2][2];
+        wq[0][0] = lds_read16<0>(SW + wo[0][0]);
+        wq[0][1] = lds_read16<0>(SW + wo[0][1]);
+        wq[1][0] = lds_read16<0>(SW + wo[1][0]);
+        wq[1][1] = lds_read16<0>(SW + wo[1][1]);
+        if (H == 0) {
+            lds_wait<5>(hdr[0]);
+            lds_wait<4>(hdr[1]);
+        }
+        lds_wait<3>(wq[0][0]);
+        lds_wait<2>(wq[0][1]);
+        lds_wait<1>(wq[1][0]);
+        lds_wait<0>(wq[1][1]);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                // scale of sub-block j = 4H + 2ss + kg/2: field j, at bits
+                // 12ss + 6(kg/2) of the fields from 4H on
+                const uint32_t w1 = (uint32_t)hdr[nt][1], w2 = (uint32_t)hdr[nt][2];
+                const uint32_t x = H == 0 ? w1 : __builtin_amdgcn_alignbit(w2, w1, 24);
+                const uint32_t sc = (x >> (12 * ss + 6 * (kg >> 1))) & 63u;
+                v4i bh, bl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t nib = ((uint32_t)wq[nt][ss][e] >> nib_sh) & 0x0F0F0F0Fu;
+                    bh[e] = mul_digit(nib, sc >> 3);
+                    bl[e] = mul_digit(nib, sc & 7u);
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    if (H == 0 && ss == 0) {
+                        acc_h[nt][t] = mma16_i8(av[H][t][ss], bh, v4i{});
+                        acc_l[nt][t] = mma16_i8(av[H][t][ss], bl, v4i{});
+                    } else {
+                        acc_h[nt][t] = mma16_i8(av[H][t][ss], bh, acc_h[nt][t]);
+                        acc_l[nt][t] = mma16_i8(av[H][t][ss], bl, acc_l[nt][t]);
+                    }
+                }
+            }
+        }
+        if (H == 1) {
+            // fold: out += d_a[m] * (d[n] * float(8*acc_h + acc_l) - dmin[n] * M)
+            // with M = sum_j m_j B_j exact: one bf16 MFMA per output tile, A
+            // row m = both exact parts of B_0..B_7 (k-groups 0 and 1; k-groups
+            // 2 and 3 zero), B column n = m_0..m_7 (all products and partial
+            // sums integers below 2^24)
+            v4f da[MT];
+            v4i ap[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                da[t] = __builtin_bit_cast(v4f, lds_read16<0>(fold_addr + 64 * t + 16 * kg));
+                ap[t] = lds_read16<0>(fold_addr + SDS + 1024 * (kg & 1) + 16 * (16 * t + r16));
+            }
+            v8bf bm[2];
+            float dw[2], ndmin[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                dw[nt] = f16_bits_to_f32((uint32_t)hdr[nt][0]);
+                ndmin[nt] = -f16_bits_to_f32((uint32_t)hdr[nt][0] >> 16);
+                // mins m_j: bits 48 + 6j of the 96-bit word
+                const uint64_t hi64 = (uint64_t)(uint32_t)hdr[nt][2] | ((uint64_t)(uint32_t)hdr[nt][3] << 32);
+                const uint64_t mx = hi64 >> 16;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bm[nt][i] = (__bf16)(float)(uint32_t)((mx >> (6 * i)) & 63u);
+            }
+            // (reads in flight after da[t]: 2(MT-1-t) + 1; after ap[t]: one fewer)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                lds_wait_n(2 * (MT - 1 - t) + 1, da[t]);
+                lds_wait_n(2 * (MT - 1 - t), ap[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4i avv = kg < 2 ? ap[t] : v4i{};
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const v4f mt = mma16_bf16(__builtin_bit_cast(v8bf, avv), bm[nt], v4f{});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int T = (acc_h[nt][t][i] << 3) + acc_l[nt][t][i];
+                        out[nt][t][i] = fmaf(fmaf((float)T, dw[nt], mt[i] * ndmin[nt]), da[t][i], out[nt][t][i]);
+                    }
+                }
+            }
+        }
+    };
+
+    if (nk > 0) {
+        // Every loop pass is one superblock (two halves), so each wait sees
+        // the same copies in flight.  The prologue issues what halves -DW ..
+        // -1 would have: weight stages 0 .. DW-1 and, last but one, the
+        // activations of half 0.
+#pragma unroll
+        for (int x = 0; x + 1 < DW; ++x) issueW(x);
+        issueA(std::integral_constant<int, 0>{}, 0);
+        issueW(DW - 1);
+        for (int k = 0; k < nk; ++k) {
+            half(std::integral_constant<int, 0>{}, 2 * k);
+            half(std::integral_constant<int, 1>{}, 2 * k + 1);
+        }
+    }
+    // no copy may still be writing this wave's stages, no read still pending
+    wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // Sum the KW partials in wave order.  Each wave parks its sums in its own
+    // stages; wave w then adds and stores output registers w*PER .. +PER-1
+    // (register u = 4(MT*nt + t) + i).
+    constexpr int PER = 8 * MT / KW;
+    {
+        float *const mine = reinterpret_cast<float *>(&s_lds[w][0]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mine[(4 * (MT * nt + t) + i) * 64 + lane] = out[nt][t][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = w * PER + u;
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < KW; ++v) sum += reinterpret_cast<const float *>(&s_lds[v][0])[idx * 64 + lane];
+        const int nt = idx / (4 * MT), t = (idx >> 2) % MT, i = idx & 3;
+        const int n = n0 + 16 * nt + r16;
+        const int voff = n < N ? n * 4 : OOB_VOFF;
+        const int row = 16 * t + 4 * kg + i;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, sum), rs_o, voff, row * N * 4, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-vector kernel for one or two tokens (decode): the product is a stream of
 // 33 MB of weights for a handful of dot products each, so it needs many waves
 // with loads in flight rather than matrix cores.  Workgroups of 4 waves each
@@ -1180,7 +1490,10 @@ static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
 constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
 
 // Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
-// kernel; up to 64 -> the K-split weight-streaming kernel; otherwise the
+// kernel; up to 16 -> the four-wave K-split kernel; up to 64 -> the two-wave
+// few-token kernel (measured on 14336 x 4096 weights: 11.6 / 12.2 / 13.4 us
+// against 14.1 / 14.3 / 14.4 us at 4 / 8 / 16 tokens, but 17.5 and 26.6 us
+// against 15.1 and 19.0 us at 32 and 64 tokens); otherwise the
 // persistent tile kernel (two workgroups per CU), 128 x 128 when that tiling
 // has more tiles than the chip has CUs (256), else 64 x 128: below that the
 // taller tile leaves CUs idle, above it the shorter tile's extra unpacking
@@ -1206,6 +1519,7 @@ int q4k_kernel_choice(int M, int N, int K) {
     if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
+    if (M <= 16) return Q4K_FEW_SPLIT;
     if (M <= 64) return Q4K_FEW_TOKENS;
     const int cus = num_cus();
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
@@ -1291,6 +1605,10 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             }
             break;
         }
+        case Q4K_FEW_SPLIT:
+            hipLaunchKernelGGL((q4w::gemm_q4k_split_kernel<1, 4, 2>), dim3((unsigned)((N + 31) / 32)), dim3(64 * 4),
+                               0, stream, a);
+            break;
         case Q4K_FEW_TOKENS:
             if (M <= 32)
                 hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<1, Q4S_DA1, Q4S_DW1>),

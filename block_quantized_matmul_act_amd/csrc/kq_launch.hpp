@@ -22,12 +22,20 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
                        int M, int N, int K, hipStream_t stream);
 
 // Q4_K kernels: one or two tokens with K a multiple of 2048 (and the staged
-// activations within the LDS budget) -> matrix-vector kernel; M <= 64 ->
+// activations within the LDS budget) -> matrix-vector kernel; M <= 16 -> the
+// few-token kernel with K split over four waves; M <= 64 -> the two-wave
 // few-token kernel; otherwise the persistent tile kernel, 128 x 128 or (for
 // shapes of at most 256 such tiles) 64 x 128.
 // The 64-row tile also has an 8-wave build (one workgroup per CU, two
 // superblocks per step) for tile counts that balance better over CUs.
-enum Q4KKernel { Q4K_FEW_TOKENS = 0, Q4K_TILE128 = 1, Q4K_MATVEC = 2, Q4K_TILE64 = 3, Q4K_TILE64_K2 = 4 };
+enum Q4KKernel {
+    Q4K_FEW_TOKENS = 0,
+    Q4K_TILE128 = 1,
+    Q4K_MATVEC = 2,
+    Q4K_TILE64 = 3,
+    Q4K_TILE64_K2 = 4,
+    Q4K_FEW_SPLIT = 5
+};
 int q4k_kernel_choice(int M, int N, int K);
 
 }  // namespace kq

@@ -66,7 +66,9 @@ bool gemv_choice(int, int M, int, int) { return M <= 8; }
 hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
-int q4k_kernel_choice(int M, int, int) { return M <= 2 ? Q4K_MATVEC : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128; }
+int q4k_kernel_choice(int M, int, int) {
+    return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
+}
 hipError_t launch_calib(int, int, const void *, int64_t, int, double *work, hipStream_t) {
     *work = 1.0;
     return hipSuccess;

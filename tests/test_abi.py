@@ -176,6 +176,8 @@ def test_variants_and_counters(kq):
     assert q4(2048, 14336, 4096) == "gemm_q4_k_128x128"
     assert q4(65, 4096, 4096) == "gemm_q4_k_64x128_k2"
     assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
+    assert q4(17, 4096, 4096) == "gemm_q4_k_m64"
+    assert q4(16, 4096, 4096) == "gemm_q4_k_m16"
     # two-bit ternary always runs on the tile kernel
     for M in (1, 8, 2048):
         assert kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, 4096, 5120)) == "gemm_tq2_128x128"

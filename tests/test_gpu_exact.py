@@ -119,6 +119,7 @@ Q4K_CASES = [
     ("gemm_q4_k_64x128_k2", 129, 200, 768),
     ("gemm_q4_k_m64", 64, 200, 256),
     ("gemm_q4_k_m64", 20, 200, 512),
+    ("gemm_q4_k_m16", 16, 200, 512), ("gemm_q4_k_m16", 3, 100, 256), ("gemm_q4_k_m16", 9, 96, 1280),
     ("gemm_q4_k_matvec", 1, 100, 2048),
     ("gemm_q4_k_matvec", 2, 100, 2048),
 ]
@@ -291,6 +292,7 @@ HEADROOM_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 512),
     ("gemm_q4_k_64x128_k2", 129, 640, 1024),
     ("gemm_q4_k_m64", 64, 640, 1024),
+    ("gemm_q4_k_m16", 16, 640, 1024),
     ("gemm_q4_k_matvec", 2, 640, 2048),
 ]
 

@@ -305,9 +305,11 @@ def test_matvec_boundaries(kq):
     """Shapes just outside the matrix-vector kernels' rules go to the
     tile kernels; inside them the long-K projection still takes them."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
-    assert name(3, 4096, 4096) == "gemm_q4_k_m64"
-    assert name(2, 4096, 1792) == "gemm_q4_k_m64"      # K not a multiple of 2048
-    assert name(2, 4096, 2048 * 9) == "gemm_q4_k_m64"  # staged activations past the budget
+    assert name(3, 4096, 4096) == "gemm_q4_k_m16"
+    assert name(2, 4096, 1792) == "gemm_q4_k_m16"      # K not a multiple of 2048
+    assert name(2, 4096, 2048 * 9) == "gemm_q4_k_m16"  # staged activations past the budget
+    assert name(16, 4096, 4096) == "gemm_q4_k_m16"
+    assert name(17, 4096, 4096) == "gemm_q4_k_m64"
     assert name(2, 4096, 14336) == "gemm_q4_k_matvec"
     W = datagen.make_weights(Q4_K, 48, 14336, 4242)
     x = datagen.draw_activations(2, 14336, 4343)
