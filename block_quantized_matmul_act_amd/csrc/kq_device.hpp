@@ -143,4 +143,18 @@ __device__ __forceinline__ uint32_t digits_to_trits(uint32_t e4) {
     return (e4 + 0x7F7F7F7Fu) ^ 0x80808080u;
 }
 
+// Ternary decode table entry for byte v: its five base-3 digits minus one as
+// int8 in bytes 0..4, zero bytes 5..7.  Digit p is floor(v / 3^p) mod 3, so
+// bytes above 242 decode exactly as the plain digit definition gives.
+__device__ __forceinline__ void tq_lut_entry(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    uint32_t t[5];
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+        t[p] = (uint32_t)(int8_t)((int)(v % 3u) - 1) & 0xFFu;
+        v /= 3u;
+    }
+    lo = t[0] | (t[1] << 8) | (t[2] << 16) | (t[3] << 24);
+    hi = t[4];
+}
+
 }  // namespace kq

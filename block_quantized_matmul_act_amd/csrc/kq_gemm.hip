@@ -450,20 +450,6 @@ struct ChunkRegs<FMT_TQ2> {
     uint32_t d;     // fp16 d
 };
 
-// Ternary decode table entry for byte v: its five base-3 digits minus one as
-// int8 in bytes 0..4, zero bytes 5..7.  Digit p is floor(v / 3^p) mod 3, so
-// bytes above 242 decode exactly as the plain digit definition gives.
-__device__ __forceinline__ void tq_lut_entry(uint32_t v, uint32_t &lo, uint32_t &hi) {
-    uint32_t t[5];
-#pragma unroll
-    for (int p = 0; p < 5; ++p) {
-        t[p] = (uint32_t)(int8_t)((int)(v % 3u) - 1) & 0xFFu;
-        v /= 3u;
-    }
-    lo = t[0] | (t[1] << 8) | (t[2] << 16) | (t[3] << 24);
-    hi = t[4];
-}
-
 template <int FMT, bool GATHER = false>
 __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
@@ -1240,6 +1226,7 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
                        hipStream_t stream) {
     if (fmt == FMT_Q4K) return launch_gemm_q4k(W, qs, da, alpha, out, M, N, K, stream);
     if (gemv_choice(fmt, M, N, K)) return launch_gemv(fmt, W, qs, da, out, M, N, K, stream);
+    if (fmt == FMT_TQ && tq_tile_choice(M, N, K)) return launch_gemm_tq_tile(W, qs, da, out, M, N, K, stream);
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
     switch (fmt) {

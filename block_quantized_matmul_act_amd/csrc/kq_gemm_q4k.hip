@@ -53,12 +53,14 @@
 #include "kq_device.hpp"
 #include "kq_hooks.hpp"
 #include "kq_launch.hpp"
+#include "kq_tile.hpp"
 
 #include <atomic>
 #include <type_traits>
 
 namespace kq {
 namespace q4w {
+using namespace tl;
 
 constexpr int BN = 128, NWAVE = 4, NT = 64 * NWAVE;
 constexpr int ROW = 256;              // LDS bytes per staged activation row
@@ -73,14 +75,6 @@ struct TileCfg {
     static constexpr int LBUF = 2 * BM * 16;             // staged min-term operands (hi, lo)
     static constexpr int WG_PER_CU = 2;                   // workgroups sharing a CU
 };
-constexpr int RSRC_FLAGS = 0x00020000;
-// A store offset the buffer range check always drops: the host checks that
-// every row offset, overhanging tile rows included, stays below 2^31, so
-// adding this cannot wrap 2^32 and always lands past the output.
-constexpr int OOB_VOFF = (int)0x80000000u;
-
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
 struct Args {
     const uint8_t *W;
     const int8_t *qs;
@@ -97,104 +91,12 @@ struct Args {
     int64_t expert_bytes;
 };
 
-__device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v16f mma_bf16(v8bf a, v8bf b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 // four nibble bytes times a scale digit s < 8, bytewise (products < 128)
 __device__ __forceinline__ int mul_digit(uint32_t nib4, uint32_t s) {
     v2u16 x = __builtin_bit_cast(v2u16, nib4);
     const unsigned short s16 = (unsigned short)s;
     return (int)__builtin_bit_cast(uint32_t, (v2u16)(x * (v2u16){s16, s16}));
 }
-// s_waitcnt on the vector-memory counter only (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Workgroup barrier without a memory fence (a fence would also wait for the
-// copies in flight).  LDS filled by buffer->LDS copies is made visible by the
-// vmcnt wait each wave performs before it.
-__device__ __forceinline__ void barrier_nofence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rs, void *lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rs, void *lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
-}
-__device__ __forceinline__ v4i ld16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
-}
-
-// LDS reads of staged data, written as instructions of our own: the
-// compiler's wait insertion tracks only a few buffer -> LDS copies at a time
-// and, past that, makes every LDS read wait for the newest copy in flight.
-// The caller orders these reads after the copies they need with an explicit
-// vmcnt wait and makes each result usable with lds_wait.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-template <int OFF>
-__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
-    v4i r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-template <int OFF>
-__device__ __forceinline__ v2u lds_read8(uint32_t addr) {
-    v2u r;
-    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-// lgkmcnt wait with a count known only after unrolling (folds to one case)
-template <typename R>
-__device__ __forceinline__ void lds_wait_n(int n, R &r);
-// s_waitcnt lgkmcnt(N), tied to a register it guards so that no use of that
-// register is scheduled above it
-template <int N>
-__device__ __forceinline__ void lds_wait(v4i &r) {
-    static_assert(N >= 0 && N < 16, "lgkmcnt range");
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
-}
-template <int N>
-__device__ __forceinline__ void lds_wait(v4f &r) {
-    static_assert(N >= 0 && N < 16, "lgkmcnt range");
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
-}
-template <int N>
-__device__ __forceinline__ void lds_wait(v2u &r) {
-    static_assert(N >= 0 && N < 16, "lgkmcnt range");
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
-}
-template <typename R>
-__device__ __forceinline__ void lds_wait_n(int n, R &r) {
-    switch (n) {
-        case 0: lds_wait<0>(r); break;
-        case 1: lds_wait<1>(r); break;
-        case 2: lds_wait<2>(r); break;
-        case 3: lds_wait<3>(r); break;
-        case 4: lds_wait<4>(r); break;
-        case 5: lds_wait<5>(r); break;
-        case 6: lds_wait<6>(r); break;
-        case 7: lds_wait<7>(r); break;
-        case 8: lds_wait<8>(r); break;
-        case 9: lds_wait<9>(r); break;
-        case 10: lds_wait<10>(r); break;
-        case 11: lds_wait<11>(r); break;
-        case 12: lds_wait<12>(r); break;
-        case 13: lds_wait<13>(r); break;
-        case 14: lds_wait<14>(r); break;
-        default: lds_wait<15>(r); break;
-    }
-}
-
 // Tile t of the grouped order: GM M-tiles down, then across N.
 // Expert-indexed tiles also carry the expert e, the first routed row grb
 // and the number of routed rows mrows (0..BM) the tile holds.
@@ -1470,7 +1372,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
 // Compute units of the current device, cached per device (the persistent
 // grids are sized from it).  Concurrent first calls may both query; they
 // store the same value.
-static int num_cus() {
+int num_cus() {
     constexpr int MAX_DEV = 64;
     static std::atomic<int> cache[MAX_DEV];
     int dev = 0;

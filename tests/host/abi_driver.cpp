@@ -66,6 +66,11 @@ bool gemv_choice(int, int M, int, int) { return M <= 8; }
 hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
+bool tq_tile_choice(int M, int, int K) { return M > 8 && K % 256 == 0; }
+hipError_t launch_gemm_tq_tile(const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
+    return hipSuccess;
+}
+int num_cus() { return 256; }
 int q4k_kernel_choice(int M, int, int) {
     return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
 }

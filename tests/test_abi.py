@@ -178,6 +178,11 @@ def test_variants_and_counters(kq):
     assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(17, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(16, 4096, 4096) == "gemm_q4_k_m16"
+    # base-3 ternary: the register-unpack tile kernel when K is a multiple of
+    # 256, the digit-plane tile kernel otherwise
+    tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ, M, N, K))
+    assert tq(2048, 17408, 5120) == "gemm_tq_128x128_reg"
+    assert tq(2048, 17408, 5248) == "gemm_tq_128x128"
     # two-bit ternary always runs on the tile kernel
     for M in (1, 8, 2048):
         assert kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, 4096, 5120)) == "gemm_tq2_128x128"

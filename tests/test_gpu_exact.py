@@ -237,6 +237,7 @@ def test_q6k_subsums_exact_through_variant(kq, variant, M, N, K):
 
 TQ_CASES = [
     ("gemm_tq_128x128", TQ, 67, 90, 640),
+    ("gemm_tq_128x128_reg", TQ, 300, 11000, 512), ("gemm_tq_128x128_reg", TQ, 129, 16500, 256),
     ("gemm_tq_matvec", TQ, 1, 40, 1024),
     ("gemm_tq_matvec", TQ, 8, 40, 1024),
     ("gemm_tq2_128x128", TQ2, 67, 90, 640),

@@ -320,8 +320,9 @@ def test_matvec_boundaries(kq):
     assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_128x128"  # K not a multiple of 2048
     assert q6(8, 4096, 14336) == "gemm_q6_k_matvec"
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
-    assert tq(9, 17408, 5120) == "gemm_tq_128x128"
-    assert tq(8, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024
+    assert tq(9, 17408, 5120) == "gemm_tq_128x128"        # fewer 128 x 128 tiles than CUs
+    assert tq(256, 17408, 5120) == "gemm_tq_128x128_reg"
+    assert tq(8, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024 (nor of 256)
     assert tq(8, 17408, 5120) == "gemm_tq_matvec"
     Wt = datagen.make_weights(TQ, 40, 5120, 4646)
     xt = datagen.draw_activations(8, 5120, 4747)
