@@ -62,13 +62,13 @@ CALIB_READ_BYTES = 1 << 30   # HBM read calibration buffer, 4x the Infinity Cach
 CSRC = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc")
 # the sources each format's GEMM kernels are built from
 GEMM_SOURCES = {
-    "q4_k": ("kq_gemm_q4k.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "q4_k": ("kq_gemm_q4k.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
     "q6_k": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
-    "tq": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
+    "tq": ("kq_gemm.hip", "kq_gemm_tq.hip", "kq_gemv.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
     "tq2": ("kq_gemm.hip", "kq_gemv.hip", "kq_device.hpp", "kq_launch.hpp"),
     # expert-indexed workloads: the gather mode of the Q4_K tile kernel
     # (kq_gemm_q4k.hip) or of the other formats' tile kernel (kq_gemm.hip)
-    "moe": ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_device.hpp", "kq_hooks.hpp"),
+    "moe": ("kq_gemm.hip", "kq_gemm_q4k.hip", "kq_tile.hpp", "kq_device.hpp", "kq_hooks.hpp"),
 }
 
 
@@ -215,10 +215,15 @@ def main():
     # The roofline's launch duration: the same GEMM launches back to back on
     # the same stream (no quantize in between), so the events bracket kernel
     # time rather than the dispatch gap that follows each quantize.
+    # (Launched through the C ABI with the pointers resolved beforehand: the
+    # binding's argument checks take longer on the host than the shortest
+    # kernels run, and would time the host instead.)
+    launch = raw_gemm_launcher(kq, fmt, Ws, As, Os, M, N, K, sp,
+                               (E, off_d.data_ptr(), rows_d.data_ptr(), R) if wl.experts else None)
     b2b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     b2b[0].record(stream)
     for i in range(args.steps):
-        gemm(i % ncopy)
+        launch(i % ncopy)
     b2b[1].record(stream)
     torch.cuda.synchronize()
     gemm_b2b_s = b2b[0].elapsed_time(b2b[1]) * 1e-3 / args.steps
@@ -320,22 +325,74 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def device_state():
-    """Shader and memory clocks and package power as the SMI reports them
-    (rocm-smi, a few seconds at most); None where a value cannot be read."""
-    import subprocess
-    st = {"sclk_mhz": None, "mclk_mhz": None, "power_w": None}
+def raw_gemm_launcher(kq, fmt, Ws, As, Os, M, N, K, sp, routing):
+    """launch(j): kq_gemm (or kq_gemm_id with routing = (experts, off, rows,
+    routed rows)) on buffer set j, straight through the C ABI with the
+    device pointers taken once.  The buffers were checked by earlier calls
+    through the binding with the same arguments."""
+    L = kq.lib()
+    ptr = [(W.data_ptr(), A.data_ptr(), O.data_ptr()) for W, A, O in zip(Ws, As, Os)]
+    if routing is None:
+        f = L.kq_gemm
+
+        def launch(j):
+            w, a, o = ptr[j]
+            rc = f(fmt, w, a, M, N, K, o, sp)
+            if rc != 0:
+                raise RuntimeError(f"kq_gemm failed: {rc}")
+    else:
+        f = L.kq_gemm_id
+        E, off, rows, R = routing
+
+        def launch(j):
+            w, a, o = ptr[j]
+            rc = f(fmt, w, E, a, M, N, K, off, rows, R, o, sp)
+            if rc != 0:
+                raise RuntimeError(f"kq_gemm_id failed: {rc}")
+    return launch
+
+
+def _sysfs_device_dir():
+    """sysfs directory of cuda:0's PCI function, or None."""
     try:
-        txt = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
-                             text=True, timeout=20).stdout
+        import torch
+        p = torch.cuda.get_device_properties(0)
+        path = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        return path if os.path.isdir(path) else None
     except Exception:
+        return None
+
+
+def device_state():
+    """Shader and memory clocks (the current DPM levels) and package power
+    read from the driver's sysfs files of cuda:0; None where a value cannot
+    be read.  (No program is started for this: a process that has
+    initialised the GPU must not replace a child with another program.)"""
+    st = {"sclk_mhz": None, "mclk_mhz": None, "power_w": None}
+    d = _sysfs_device_dir()
+    if d is None:
         return st
-    for key, pat in (("sclk_mhz", r'"sclk clock speed:"\s*:\s*"\(?(\d+)\s*Mhz'),
-                     ("mclk_mhz", r'"mclk clock speed:"\s*:\s*"\(?(\d+)\s*Mhz'),
-                     ("power_w", r'Power[^"]*"\s*:\s*"([0-9.]+)')):
-        m = re.search(pat, txt, re.I)
-        if m:
-            st[key] = float(m.group(1))
+    for key, fname in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+        try:
+            for line in open(os.path.join(d, fname)):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    if m:
+                        st[key] = float(m.group(1))
+        except OSError:
+            pass
+    try:
+        hw = os.path.join(d, "hwmon")
+        for h in sorted(os.listdir(hw)):
+            for fname in ("power1_average", "power1_input"):
+                f = os.path.join(hw, h, fname)
+                if os.path.exists(f):
+                    st["power_w"] = round(int(open(f).read().strip()) / 1e6, 1)
+                    break
+            if st["power_w"] is not None:
+                break
+    except (OSError, ValueError):
+        pass
     return st
 
 
@@ -369,10 +426,11 @@ def side_config(kq, name, stream, launches):
         kq.kq_gemm(fmt, Ws[i % ncopy], As[i % ncopy], M, N, K, Os[i % ncopy], sp)
     torch.cuda.synchronize()
     before = kq.dispatch_counts()
+    launch = raw_gemm_launcher(kq, fmt, Ws, As, Os, M, N, K, sp, None)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(launches):
-        kq.kq_gemm(fmt, Ws[i % ncopy], As[i % ncopy], M, N, K, Os[i % ncopy], sp)
+        launch(i % ncopy)
     e1.record(stream)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / launches

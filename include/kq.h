@@ -26,7 +26,9 @@
  *     rather than computed wrongly.  M == 0 or N == 0 returns KQ_OK with no
  *     launch.
  *   - Output buffers must not overlap inputs.  Calls are thread-safe; the only
- *     global state is a set of atomic per-variant dispatch counters.
+ *     global state is a set of atomic per-variant dispatch counters and a
+ *     per-device cache of the compute-unit count (atomic; it sizes the
+ *     persistent grids).
  *
  * Data layouts (this library's own; the pages fix only the block sizes:
  * 292 bytes per 256 activations for BlockQ8_K in vllm.cpp PR 3036, a 28-byte

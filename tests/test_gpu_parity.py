@@ -645,6 +645,27 @@ def test_zero_k_gives_zero(kq):
         assert torch.all(out == 0.0).item()
 
 
+@pytest.mark.parametrize("M,N,K,variant", [
+    (512, 16384, 5120, "gemm_tq_128x128_reg"),       # 512 tiles: one full round of two per CU
+    (1024, 17408, 5376, "gemm_tq_128x128_reg"),      # 1088 tiles, 2.1 rounds; 21 steps per tile
+])
+def test_ternary_register_kernels(kq, M, N, K, variant):
+    """The ternary register-unpack tile kernel against the oracle on sampled
+    weight rows (the first, last and random ones)."""
+    assert kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K)) == variant
+    say(f"{variant}: M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    t = rng.choice(np.array([-1, 0, 1], np.int8), size=(N, K), p=[0.3, 0.4, 0.3])
+    d = rng.uniform(0.01, 0.05, size=(N, K // 128)).astype(np.float16)
+    W = datagen.encode_tq(t, d)
+    x = datagen.draw_activations(M, K, M + 7)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N - 2, N - 1], rng.choice(N, 24, replace=False)]))
+    names = [kq.kq_variant_name(v) for v in range(kq.kq_num_variants())]
+    before = kq.kq_dispatch_count(names.index(variant))
+    gemm_vs_oracle(kq, TQ, W, x, M, N, K, rows=rows, what=variant)
+    assert kq.kq_dispatch_count(names.index(variant)) == before + 1
+
+
 def test_zz_every_variant_dispatched(kq):
     """Runs last in this file: every kernel variant in the table was launched by
     the tests above (the counters prove which kernel ran)."""
