@@ -97,22 +97,21 @@ __device__ __forceinline__ void q4k_digits(uint32_t nib4, uint32_t sc, uint32_t 
 //
 // q dword (4 weights, bytes in [0,63]) and the sub-block scale sc (int8) ->
 // two int8 digit dwords of W = sc*(q-32) in [-4096, 4096]: W = 64*h + l with
-// l in [0,63], h in [-64,64].  Products are formed in packed 16-bit lanes.
+// l in [0,63], h in [-64,64].  Products are formed in packed 16-bit lanes as
+// 4*W = 256*h + 4*l (|4W| <= 16384 fits a signed 16-bit lane): the high byte
+// of each lane is h in two's complement and the low byte 4*l, a multiple of
+// 4, so the packed low bytes shifted right by 2 are the four l digits (the
+// bits that cross into a byte from its neighbour are zero).
 __device__ __forceinline__ void q6k_digits(uint32_t q4, int sc, uint32_t &dh, uint32_t &dl) {
-    uint32_t qe = perm_b32(0u, q4, 0x0c020c00u);   // bytes 0,2 -> 16-bit lanes
-    uint32_t qo = perm_b32(0u, q4, 0x0c030c01u);   // bytes 1,3 -> 16-bit lanes
-    v2i16 s2 = {(short)sc, (short)sc};
-    v2i16 off = {(short)(-32 * sc), (short)(-32 * sc)};
-    v2i16 we = __builtin_bit_cast(v2i16, qe) * s2 + off;
-    v2i16 wo = __builtin_bit_cast(v2i16, qo) * s2 + off;
-    uint32_t le = __builtin_bit_cast(uint32_t, we) & 0x003F003Fu;
-    uint32_t lo = __builtin_bit_cast(uint32_t, wo) & 0x003F003Fu;
-    v2i16 sh6 = {6, 6};
-    uint32_t he = __builtin_bit_cast(uint32_t, (v2i16)(we >> sh6));
-    uint32_t ho = __builtin_bit_cast(uint32_t, (v2i16)(wo >> sh6));
-    // interleave back: byte order e0, o0, e1, o1
-    dl = perm_b32(lo, le, 0x06020400u);
-    dh = perm_b32(ho, he, 0x06020400u);
+    const uint32_t qe = perm_b32(0u, q4, 0x0c020c00u);   // bytes 0,2 -> 16-bit lanes
+    const uint32_t qo = perm_b32(0u, q4, 0x0c030c01u);   // bytes 1,3 -> 16-bit lanes
+    const v2i16 s4 = {(short)(4 * sc), (short)(4 * sc)};
+    const v2i16 off = {(short)(-128 * sc), (short)(-128 * sc)};
+    const uint32_t we = __builtin_bit_cast(uint32_t, (v2i16)(__builtin_bit_cast(v2i16, qe) * s4 + off));
+    const uint32_t wo = __builtin_bit_cast(uint32_t, (v2i16)(__builtin_bit_cast(v2i16, qo) * s4 + off));
+    // byte order e0, o0, e1, o1: high bytes for h, low bytes for 4*l
+    dh = perm_b32(wo, we, 0x07030501u);
+    dl = perm_b32(wo, we, 0x06020400u) >> 2;
 }
 
 // ---------------------------------------------------------------------------
