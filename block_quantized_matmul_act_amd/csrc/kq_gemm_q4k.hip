@@ -1360,6 +1360,298 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
     wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (17..64): all tokens in one workgroup, K split in two halves.
+// A workgroup owns 64 weight rows as four 16-row strips; wave w takes strip
+// w % 4 over the superblocks of K-half w / 4, so two waves share each SIMD.
+// Step t multiplies superblock t (first half) and T + t (second half),
+// T = ceil(nsb / 2).  The activations of a step (values, scales, min-term
+// operands of both halves, all token rows) are copied global -> LDS into a
+// ring of 4 slots, RING_L = 3 steps ahead; each wave loads its strip's
+// weights for the same step into a register ring of 4 slots, in the same
+// issue.  Vector-memory loads complete in issue order, so the wait for a
+// step's copies is also a wait for the weights issued before them, but
+// those are the weights of the same step or earlier: nothing is held up
+// that is not needed.  (The kernels above stage activations one step ahead
+// while weights run further, and there the in-order wait stalls.)  The two
+// halves are summed through LDS at the end, in a fixed order.
+//
+// v_mfma_i32_16x16x64_i8 operands, in this kernel's K order: in K-step s of
+// a superblock, lane group kg (lane / 16) holds the 16 values k = 64kg + 16s
+// + i, sub-block j = 2kg + s/2.  Those are the low (s < 2) or high (s >= 2)
+// nibbles of nibble bytes 32kg + 16(s % 2) + i (byte 32c + t holds weights
+// 64c + t and 64c + 32 + t), so a lane loads 32 contiguous nibble bytes per
+// superblock and uses each byte twice.  The A operand of K-step s is the 16
+// contiguous activation bytes at 64kg + 16s of the token row.
+// ---------------------------------------------------------------------------
+constexpr int RING_L = 3;              // steps of lead
+constexpr int RING_S = RING_L + 1;     // LDS slots and weight registers sets
+constexpr int RING_ZERO = 1024;        // zero bytes read as the min-term operand of lanes 32..63
+
+template <int TM>
+struct RingCfg {
+    static_assert(TM == 32 || TM == 64, "32 or 64 token rows");
+    static constexpr int MT = TM / 16;             // 16-row m-tiles
+    static constexpr int ACTH = TM * ROW;          // values of one half: [row][256], swizzled
+    static constexpr int DAH = 256;                // scales of one half (a 64-lane 4-byte copy)
+    static constexpr int ALH = 2 * TM * 16;        // min-term operands of one half: [part][row][16]
+    static constexpr int O_DA = 2 * ACTH, O_AL = O_DA + 2 * DAH;
+    static constexpr int SLOT = O_AL + 2 * ALH;
+    static constexpr int LDS = RING_S * SLOT + RING_ZERO;
+    static constexpr int NA = ACTH / 1024;         // value copies per half
+    static constexpr int NL = ALH / 1024;          // operand copies per half
+    static_assert(NL <= 2 && NA % 4 == 0, "four value copies of a half per wave group, two operand parts");
+    static constexpr int CPW = NA / 4 + 1;         // copies per wave and step
+    static constexpr int LOADS = CPW + 3;          // vector-memory instructions per wave and step
+    static_assert(LOADS * (RING_L - 1) < 64, "vmcnt range");
+};
+
+struct RingW {
+    v4i hdr, q0, q1;  // block header; nibble bytes 32kg .. +15, 32kg + 16 .. +15
+};
+
+template <int TM>
+__global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
+    using C = RingCfg<TM>;
+    constexpr int MT = C::MT;
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int strip = w & 3, kh = w >> 2;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int T = (nsb + 1) >> 1;            // steps
+    const int n0 = blockIdx.x * 64 + 16 * strip;
+    const int rowbytes = nsb * BB;
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+    // no records: reads return zero without a memory access (copies and
+    // loads of steps past the end, so that every step issues the same)
+    const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
+
+    int8_t *const zero = s_lds + RING_S * C::SLOT;
+    for (int i = tid; i < RING_ZERO / 4; i += 512) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
+
+    // ---- copies of step x into slot x % RING_S.  Wave w copies for its own
+    // K-half kh: value copies CPV*(w%4) .. +CPV-1 (copy r: rows 4r .. 4r+3;
+    // lane l fills piece l%16 of row 4r + l/16 with piece (l%16) ^ row), and
+    // one more by w%4: the scales (lane l: token l), the min-term operands
+    // (TM = 64: part w%4 - 1, lane l token l; TM = 32: lane l part l/32,
+    // token l%32), or a repeat of the last operand copy (the same bytes to
+    // the same place).  Per-lane offsets are fixed; the superblock goes in
+    // the scalar offset.  Token rows past M read other rows' data or zero;
+    // their outputs are dropped.
+    constexpr int CPV = C::NA / 4;
+    const int wq = w & 3;
+    int a_vo[CPV];
+#pragma unroll
+    for (int i = 0; i < CPV; ++i) {
+        const int row = 4 * (CPV * wq + i) + (lane >> 4);
+        a_vo[i] = row * K + 16 * ((lane & 15) ^ (row & 15));
+    }
+    const int x_part = TM == 64 ? min(max(wq - 1, 0), 1) : (lane >> 5);
+    const int x_tok = TM == 64 ? lane : (lane & 31);
+    const int x_vo = wq == 0 ? 4 * lane : (x_part * M + x_tok) * 16;
+    const int x_lds = wq == 0 ? C::O_DA + kh * C::DAH
+                              : C::O_AL + kh * C::ALH + (TM == 64 ? min(max(wq - 1, 0), 1) * 1024 : 0);
+    auto copies = [&](int x) __attribute__((always_inline)) {
+        int8_t *S = s_lds + (x % RING_S) * C::SLOT;
+        const int sb = kh ? T + x : x;
+        const bool real = x < T && sb < nsb;
+        const int sbr = real ? sb : 0;
+        const auto ra = real ? rs_a : rs_nul;
+#pragma unroll
+        for (int i = 0; i < CPV; ++i)
+            copy16(ra, S + kh * C::ACTH + (CPV * wq + i) * 1024, a_vo[i], sbr * ROW);
+        if (wq == 0) copy4(real ? rs_d : rs_nul, S + x_lds, x_vo, sbr * M * 4);
+        else copy16(real ? rs_l : rs_nul, S + x_lds, x_vo, sbr * 2 * M * 16);
+    };
+    // ---- this lane's weights: row n0 + r16, header and 32 nibble bytes ----
+    // (row offsets as unsigned: rows past N may pass 2^31, and the range
+    // check drops them)
+    const int w_hdr = (int)((uint32_t)(n0 + r16) * (uint32_t)rowbytes);
+    const int w_nib = w_hdr + 16 + 32 * kg;
+    RingW ring[RING_S];
+    auto wload = [&](int x, RingW &R) __attribute__((always_inline)) {
+        const int sb = kh ? T + x : x;
+        const bool real = x < T && sb < nsb;
+        const auto rw = real ? rs_w : rs_nul;
+        const int so = (real ? sb : 0) * BB;
+        R.hdr = ld16(rw, w_hdr, so);
+        R.q0 = ld16(rw, w_nib, so);
+        R.q1 = ld16(rw, w_nib + 16, so);
+    };
+
+    v4f out[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = v4f{};
+    // LDS addresses (the reads are instructions of our own with explicit
+    // waits: the compiler's copy tracking would make them wait for every
+    // load in flight).  K-step s of m-tile t: row 16t + r16, piece
+    // (4kg + s) ^ r16; m-tile t is 16t rows (4096t bytes) on.
+    uint32_t a_ad[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a_ad[s] = lds_addr(s_lds) + kh * C::ACTH + r16 * ROW + (((4 * kg + s) ^ r16) << 4);
+    // min-term operands: part kg of row 16t + r16 for kg < 2, zeros above
+    const uint32_t l_ad = kg < 2 ? lds_addr(s_lds) + C::O_AL + kh * C::ALH + (kg & 1) * (TM * 16) + 16 * r16
+                                 : lds_addr(zero) + 16 * r16;
+    const uint32_t l_slot = kg < 2 ? 1u : 0u;  // slot offsets apply to real operands only
+    // scales of rows 4kg .. 4kg+3 of m-tile t
+    const uint32_t d_ad = lds_addr(s_lds) + C::O_DA + kh * C::DAH + 16 * kg;
+
+    auto compute = [&](const RingW &R, uint32_t so) __attribute__((always_inline)) {
+        // LDS reads of K-step s (one per m-tile), two K-steps in flight; the
+        // fold's reads go out under K-step 3
+        v4i av[2][MT];
+        auto rd = [&](int s, v4i(&dst)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                switch (t) {
+                    case 0: dst[t] = lds_read16<0>(a_ad[s] + so); break;
+                    case 1: dst[t] = lds_read16<16 * ROW>(a_ad[s] + so); break;
+                    case 2: dst[t] = lds_read16<32 * ROW>(a_ad[s] + so); break;
+                    default: dst[t] = lds_read16<48 * ROW>(a_ad[s] + so); break;
+                }
+            }
+        };
+        rd(0, av[0]);
+        rd(1, av[1]);
+        // scales of sub-blocks 2kg (K-steps 0, 1) and 2kg + 1 (2, 3):
+        // fields 2kg, 2kg+1 of the 96-bit word, bits 12kg ..
+        const uint64_t f64 = (uint64_t)(uint32_t)R.hdr[1] | ((uint64_t)(uint32_t)R.hdr[2] << 32);
+        const uint32_t x = (uint32_t)(f64 >> (12 * kg));
+        v4i acc_h[MT], acc_l[MT];
+        v4i ap[MT];
+        v4f da[MT];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t sc = (s < 2 ? x : x >> 6) & 63u;
+            const v4i qw = (s & 1) ? R.q1 : R.q0;
+            v4i bh, bl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t nib = s < 2 ? (uint32_t)qw[e] & 0x0F0F0F0Fu : ((uint32_t)qw[e] >> 4) & 0x0F0F0F0Fu;
+                bh[e] = mul_digit(nib, sc >> 3);
+                bl[e] = mul_digit(nib, sc & 7u);
+            }
+            // reads in flight behind m-tile t of K-step s: the rest of this
+            // K-step's, then the next K-step's (MT) or, under K-step 3, the
+            // fold's (2 MT)
+            v4i(&cur)[MT] = av[s & 1];
+            const int behind = s < 2 ? MT : (s == 2 ? MT : 2 * MT);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) lds_wait_n(MT - 1 - t + behind, cur[t]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                acc_h[t] = mma16_i8(cur[t], bh, s == 0 ? v4i{} : acc_h[t]);
+                acc_l[t] = mma16_i8(cur[t], bl, s == 0 ? v4i{} : acc_l[t]);
+            }
+            if (s < 2) {
+                rd(s + 2, av[s & 1]);
+            } else if (s == 2) {
+                // the fold's operands
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    switch (t) {
+                        case 0: ap[t] = lds_read16<0>(l_ad + l_slot * so); break;
+                        case 1: ap[t] = lds_read16<256>(l_ad + l_slot * so); break;
+                        case 2: ap[t] = lds_read16<512>(l_ad + l_slot * so); break;
+                        default: ap[t] = lds_read16<768>(l_ad + l_slot * so); break;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t) da[t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 64 * t));
+            }
+        }
+        // fold: out += d_a[m] * (d[n] * float(8*acc_h + acc_l) - dmin[n] * M),
+        // M = sum_j m_j B_j exact on one bf16 MFMA per m-tile (A row m =
+        // both exact parts of B_0..B_7 in k-groups 0 and 1, k-groups 2 and 3
+        // zero; B column n = m_0..m_7)
+        const float dw = f16_bits_to_f32((uint32_t)R.hdr[0]);
+        const float ndmin = -f16_bits_to_f32((uint32_t)R.hdr[0] >> 16);
+        const uint64_t hi64 = (uint64_t)(uint32_t)R.hdr[2] | ((uint64_t)(uint32_t)R.hdr[3] << 32);
+        const uint64_t mx = hi64 >> 16;  // mins m_j: bits 48 + 6j of the 96-bit word
+        v8bf bm;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bm[i] = (__bf16)(float)(uint32_t)((mx >> (6 * i)) & 63u);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            lds_wait_n(2 * MT - 1 - t, ap[t]);
+            lds_wait_n(MT - 1 - t, da[t]);
+            const v4f mt = mma16_bf16(__builtin_bit_cast(v8bf, ap[t]), bm, v4f{});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int Tq = (acc_h[t][i] << 3) + acc_l[t][i];
+                out[t][i] = fmaf(fmaf((float)Tq, dw, mt[i] * ndmin), da[t][i], out[t][i]);
+            }
+        }
+    };
+
+    // step x: the copies and loads of step x + RING_L go out once every wave
+    // is past step x - 1 (their slot's last reader), then step x multiplies
+    auto step = [&](auto KK, int x) __attribute__((always_inline)) {
+        constexpr int k = decltype(KK)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (RING_L - 1)>();
+        barrier_nofence();
+        copies(x + RING_L);
+        wload(x + RING_L, ring[(k + RING_L) % RING_S]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int sb = kh ? T + x : x;
+        if (x < T && sb < nsb) compute(ring[k], (uint32_t)(k * C::SLOT));  // uniform
+    };
+#pragma unroll
+    for (int x = 0; x < RING_L; ++x) {
+        copies(x);
+        wload(x, ring[x]);
+    }
+    // (a whole number of ring turns: every step issues the same loads, so
+    // the waits stay partial)
+    const int npass = (T + RING_S - 1) / RING_S * RING_S;
+    for (int x0 = 0; x0 < npass; x0 += RING_S) {
+        step(std::integral_constant<int, 0>{}, x0);
+        step(std::integral_constant<int, 1>{}, x0 + 1);
+        step(std::integral_constant<int, 2>{}, x0 + 2);
+        step(std::integral_constant<int, 3>{}, x0 + 3);
+    }
+    // the copies and loads past the end (reading nothing) drain; then the
+    // second half's sums go through LDS to the first half's waves
+    wait_vmcnt<0>();
+    barrier_nofence();
+    float *red = reinterpret_cast<float *>(s_lds);
+    if (kh == 1) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[((strip * MT + t) * 4 + i) * 64 + lane] = out[t][i];
+    }
+    barrier_nofence();
+    if (kh == 0) {
+        // rows past M fall outside the resource; columns past N are sent out
+        // of range
+        const int n = n0 + r16;
+        const int voff = n < N ? (4 * kg * N + n) * 4 : OOB_VOFF;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            v4f sum;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[i] = out[t][i] + red[((strip * MT + t) * 4 + i) * 64 + lane];
+            // (the whole vector is bit-cast: see the tile kernel's epilogue)
+            const v4i bits = __builtin_bit_cast(v4i, sum);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(bits[i], rs_o, voff, (16 * t + i) * N * 4, 0);
+        }
+    }
+}
+static_assert(RING_S == 4, "the step loop above is unrolled for four slots");
+
 // out[0, n) = 0 (the product over an empty K); a kernel rather than a memset
 // so that the call stays capturable in a graph
 __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
@@ -1422,8 +1714,15 @@ int q4k_kernel_choice(int M, int N, int K) {
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
     if (M <= 16) return Q4K_FEW_SPLIT;
-    if (M <= 64) return Q4K_FEW_TOKENS;
     const int cus = num_cus();
+    // the K-split ring kernel runs one 64-row workgroup per CU: it needs the
+    // weight rows to fill two thirds of the CUs.  Measured against the
+    // two-wave kernel (K = 4096): 14336 rows (224 workgroups) 12.5 against
+    // 14.6 us at 20 tokens, 13.9 against 15.7 at 32, 19.2 against 19.9 at
+    // 64; 11008 rows (172) 13.0 against 14.7 at 32, 17.6 against 18.1 at 64;
+    // 8192 rows (128) 12.7 against 11.4 at 32, 17.4 against 14.9 at 64
+    if (M <= 64 && 3 * ((N + 63) / 64) >= 2 * cus) return Q4K_FEW_RING;
+    if (M <= 64) return Q4K_FEW_TOKENS;
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
@@ -1518,6 +1817,14 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             else
                 hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<2, Q4S_DA2, Q4S_DW2>),
                                    dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
+            break;
+        case Q4K_FEW_RING:
+            if (M <= 32)
+                hipLaunchKernelGGL(q4w::gemm_q4k_ring_kernel<32>, dim3((unsigned)((N + 63) / 64)), dim3(512), 0,
+                                   stream, a);
+            else
+                hipLaunchKernelGGL(q4w::gemm_q4k_ring_kernel<64>, dim3((unsigned)((N + 63) / 64)), dim3(512), 0,
+                                   stream, a);
             break;
         case Q4K_TILE64: {
             const unsigned grid = (unsigned)min(a.ntiles, q4w::TileCfg<64>::WG_PER_CU * cus);

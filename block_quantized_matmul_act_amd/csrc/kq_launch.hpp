@@ -44,7 +44,8 @@ enum Q4KKernel {
     Q4K_MATVEC = 2,
     Q4K_TILE64 = 3,
     Q4K_TILE64_K2 = 4,
-    Q4K_FEW_SPLIT = 5
+    Q4K_FEW_SPLIT = 5,
+    Q4K_FEW_RING = 6
 };
 int q4k_kernel_choice(int M, int N, int K);
 
