@@ -1390,11 +1390,13 @@ constexpr int RING_ZERO = 1024;        // zero bytes read as the min-term operan
 
 template <int TM>
 struct RingCfg {
-    static_assert(TM == 32 || TM == 64, "32 or 64 token rows");
+    static_assert(TM == 16 || TM == 32 || TM == 64, "16, 32 or 64 token rows");
     static constexpr int MT = TM / 16;             // 16-row m-tiles
     static constexpr int ACTH = TM * ROW;          // values of one half: [row][256], swizzled
     static constexpr int DAH = 256;                // scales of one half (a 64-lane 4-byte copy)
-    static constexpr int ALH = 2 * TM * 16;        // min-term operands of one half: [part][row][16]
+    // min-term operands of one half: [part][row][16] (at TM = 16 the 1 KiB
+    // copy's second half lands in padding)
+    static constexpr int ALH = 2 * TM * 16 > 1024 ? 2 * TM * 16 : 1024;
     static constexpr int O_DA = 2 * ACTH, O_AL = O_DA + 2 * DAH;
     static constexpr int SLOT = O_AL + 2 * ALH;
     static constexpr int LDS = RING_S * SLOT + RING_ZERO;
@@ -1442,7 +1444,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     // lane l fills piece l%16 of row 4r + l/16 with piece (l%16) ^ row), and
     // one more by w%4: the scales (lane l: token l), the min-term operands
     // (TM = 64: part w%4 - 1, lane l token l; TM = 32: lane l part l/32,
-    // token l%32), or a repeat of the last operand copy (the same bytes to
+    // token l%32; TM = 16: lane l part (l/16)%2, token l%16, lanes 32..63
+    // into padding), or a repeat of the last operand copy (the same bytes to
     // the same place).  Per-lane offsets are fixed; the superblock goes in
     // the scalar offset.  Token rows past M read other rows' data or zero;
     // their outputs are dropped.
@@ -1454,8 +1457,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
         const int row = 4 * (CPV * wq + i) + (lane >> 4);
         a_vo[i] = row * K + 16 * ((lane & 15) ^ (row & 15));
     }
-    const int x_part = TM == 64 ? min(max(wq - 1, 0), 1) : (lane >> 5);
-    const int x_tok = TM == 64 ? lane : (lane & 31);
+    const int x_part = TM == 64 ? min(max(wq - 1, 0), 1) : TM == 32 ? (lane >> 5) : ((lane >> 4) & 1);
+    const int x_tok = TM == 64 ? lane : (lane & (TM - 1));
     const int x_vo = wq == 0 ? 4 * lane : (x_part * M + x_tok) * 16;
     const int x_lds = wq == 0 ? C::O_DA + kh * C::DAH
                               : C::O_AL + kh * C::ALH + (TM == 64 ? min(max(wq - 1, 0), 1) * 1024 : 0);
@@ -1713,15 +1716,18 @@ int q4k_kernel_choice(int M, int N, int K) {
     if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
-    if (M <= 16) return Q4K_FEW_SPLIT;
     const int cus = num_cus();
     // the K-split ring kernel runs one 64-row workgroup per CU: it needs the
     // weight rows to fill two thirds of the CUs.  Measured against the
     // two-wave kernel (K = 4096): 14336 rows (224 workgroups) 12.5 against
     // 14.6 us at 20 tokens, 13.9 against 15.7 at 32, 19.2 against 19.9 at
     // 64; 11008 rows (172) 13.0 against 14.7 at 32, 17.6 against 18.1 at 64;
-    // 8192 rows (128) 12.7 against 11.4 at 32, 17.4 against 14.9 at 64
+    // 8192 rows (128) 12.7 against 11.4 at 32, 17.4 against 14.9 at 64.
+    // Its 16-row build against the four-wave split kernel on 14336 rows:
+    // 11.3 against 13.6 us at 16 tokens, 10.7 against 12.2 at 8, 10.4
+    // against 11.5 at 3
     if (M <= 64 && 3 * ((N + 63) / 64) >= 2 * cus) return Q4K_FEW_RING;
+    if (M <= 16) return Q4K_FEW_SPLIT;
     if (M <= 64) return Q4K_FEW_TOKENS;
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
@@ -1819,7 +1825,10 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                                    dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
             break;
         case Q4K_FEW_RING:
-            if (M <= 32)
+            if (M <= 16)
+                hipLaunchKernelGGL(q4w::gemm_q4k_ring_kernel<16>, dim3((unsigned)((N + 63) / 64)), dim3(512), 0,
+                                   stream, a);
+            else if (M <= 32)
                 hipLaunchKernelGGL(q4w::gemm_q4k_ring_kernel<32>, dim3((unsigned)((N + 63) / 64)), dim3(512), 0,
                                    stream, a);
             else

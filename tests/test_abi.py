@@ -178,12 +178,13 @@ def test_variants_and_counters(kq):
     assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(17, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(16, 4096, 4096) == "gemm_q4_k_m16"
-    # 17 .. 64 tokens: the K-split ring kernel once its 64-row workgroups
+    # 3 .. 64 tokens: the K-split ring kernel once its 64-row workgroups
     # cover two thirds of the CUs
     assert q4(64, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert q4(17, 10944, 4096) == "gemm_q4_k_m64_ring"  # 171 workgroups
     assert q4(17, 10880, 4096) == "gemm_q4_k_m64"       # 170
-    assert q4(16, 14336, 4096) == "gemm_q4_k_m16"
+    assert q4(16, 14336, 4096) == "gemm_q4_k_m64_ring"  # its 16-row build
+    assert q4(3, 14336, 4096) == "gemm_q4_k_m64_ring"
     # base-3 ternary: the register-unpack tile kernel when K is a multiple of
     # 256, the digit-plane tile kernel otherwise
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ, M, N, K))

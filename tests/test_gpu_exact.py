@@ -111,9 +111,9 @@ def assert_exact(out, want, what):
 # 8-wave 64 x 128 build takes the smaller counts (K = 768: an odd number of
 # superblocks, so one half of its waves sits out the last step); the
 # few-token kernel has a one- and a two-m-tile build; the K-split ring
-# kernel takes 17 .. 64 tokens when N / 64 reaches two thirds of the CUs
-# (one superblock: the second K-half has none; three: its second step is
-# empty; 11016 columns: a ragged last workgroup); the matrix-vector kernel takes one
+# kernel takes 3 .. 64 tokens when N / 64 reaches two thirds of the CUs, in
+# 16-, 32- and 64-row builds (one superblock: the second K-half has none;
+# three: its second step is empty; 11016 columns: a ragged last workgroup); the matrix-vector kernel takes one
 # or two tokens with K a multiple of 2048
 Q4K_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 256),
@@ -124,6 +124,7 @@ Q4K_CASES = [
     ("gemm_q4_k_m64", 20, 200, 512),
     ("gemm_q4_k_m64_ring", 64, 11008, 256),
     ("gemm_q4_k_m64_ring", 20, 11016, 768),
+    ("gemm_q4_k_m64_ring", 9, 11008, 512),
     ("gemm_q4_k_m16", 16, 200, 512), ("gemm_q4_k_m16", 3, 100, 256), ("gemm_q4_k_m16", 9, 96, 1280),
     ("gemm_q4_k_matvec", 1, 100, 2048),
     ("gemm_q4_k_matvec", 2, 100, 2048),
@@ -299,6 +300,7 @@ HEADROOM_CASES = [
     ("gemm_q4_k_64x128_k2", 129, 640, 1024),
     ("gemm_q4_k_m64", 64, 640, 1024),
     ("gemm_q4_k_m64_ring", 64, 11008, 1024),
+    ("gemm_q4_k_m64_ring", 16, 11008, 1024),
     ("gemm_q4_k_m16", 16, 640, 1024),
     ("gemm_q4_k_matvec", 2, 640, 2048),
 ]

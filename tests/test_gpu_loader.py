@@ -217,6 +217,7 @@ IDENTITY_CASES = [
     (Q4_K, 2048, "gemm_q4_k_matvec", 2, 72),
     (Q4_K, 2048, "gemm_q4_k_m64", 64, 72),
     (Q4_K, 2048, "gemm_q4_k_m64_ring", 64, 11016),
+    (Q4_K, 2048, "gemm_q4_k_m64_ring", 16, 11016),
     (Q4_K, 2048, "gemm_q4_k_m16", 16, 72),
     (Q4_K, 2048, "gemm_q4_k_64x128_k2", 2048, 72),
     (Q4_K, 2048, "gemm_q4_k_64x128", 2048, 1100),

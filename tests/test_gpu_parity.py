@@ -278,20 +278,23 @@ def test_q4k_tile_heights(kq):
 
 
 def test_q4k_few_token_ring(kq):
-    """The K-split ring kernel of 17 .. 64 tokens: its choice rule, then
+    """The K-split ring kernel of 3 .. 64 tokens: its choice rule, then
     products in full against the oracle at a ragged width (11016 columns:
-    the last workgroup has two 16-row strips past N and 8 columns) for both
-    token-tile builds (32 and 64 rows) and odd and even superblock counts."""
+    the last workgroup has two 16-row strips past N and 8 columns) for all
+    three token-tile builds (16, 32 and 64 rows) and odd and even superblock
+    counts."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
     assert name(64, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert name(33, 10944, 1280) == "gemm_q4_k_m64_ring"
     assert name(64, 10880, 4096) == "gemm_q4_k_m64"
+    assert name(3, 14336, 4096) == "gemm_q4_k_m64_ring"
+    assert name(16, 10880, 4096) == "gemm_q4_k_m16"
     N = 11016
     v = kq.kq_select_variant(Q4_K, 64, N, 768)
     for K in (768, 1280):
         W = datagen.make_weights(Q4_K, N, K, 5100 + K)
         x = datagen.draw_activations(64, K, 5200 + K)
-        for M in (17, 32, 33, 64):
+        for M in (3, 16, 17, 32, 33, 64):
             say(f"ring M={M} N={N} K={K}")
             before = kq.kq_dispatch_count(v)
             gemm_vs_oracle(kq, Q4_K, W, np.ascontiguousarray(x[:M]), M, N, K, what=f"ring M={M} K={K}")
