@@ -51,7 +51,7 @@ def test_measured_traffic_needs_the_current_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     cur = bench.kernel_source_hash("q4_k")
     _fake_profiles(tmp_path, "gemm_q4k_ffn_up_q4k_2048_traffic.md", cur, "1.25e+08")
-    _fake_profiles(tmp_path, "gemm_q4k_small_ffn_up_q4k_64_traffic.md", "0" * 16, "3.4e+07")
+    _fake_profiles(tmp_path, "gemm_q4k_ring_ffn_up_q4k_64_traffic.md", "0" * 16, "3.4e+07")
     assert bench.measured_traffic("ffn_up_q4k_2048", "q4_k") == pytest.approx(1.25e8)
     # taken on another kernel source: not reported
     assert bench.measured_traffic("ffn_up_q4k_64", "q4_k") is None
