@@ -1361,7 +1361,9 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (17..64): all tokens in one workgroup, K split in two halves.
+// Few tokens (3..64, weights wide enough to fill the CUs with 64-row
+// workgroups): all tokens in one workgroup, K split in two halves.  The token
+// rows form one, two or four 16-row m-tiles (TM = 16, 32 or 64).
 // A workgroup owns 64 weight rows as four 16-row strips; wave w takes strip
 // w % 4 over the superblocks of K-half w / 4, so two waves share each SIMD.
 // Step t multiplies superblock t (first half) and T + t (second half),
