@@ -82,13 +82,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_tokens(text: str) -> str:
+    """The source with its comments removed and its whitespace collapsed, so
+    that an edit of comments or layout does not count as a kernel change (the
+    sources hold no string literal with a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(fmt_name: str) -> str:
-    """sha256 (first 16 hex digits) over the sources of one format's GEMM
-    kernels, in order."""
+    """sha256 (first 16 hex digits) over the code of one format's GEMM kernel
+    sources, in order (comments and layout excluded)."""
     h = hashlib.sha256()
     for name in GEMM_SOURCES[fmt_name]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 
