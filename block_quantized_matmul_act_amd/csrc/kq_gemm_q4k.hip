@@ -1206,6 +1206,11 @@ constexpr int NW = 4;          // waves per workgroup
 #endif
 constexpr int RPW = MV_RPW;    // weight rows per wave
 constexpr int RPG = NW * RPW;  // weight rows per workgroup
+// Load instructions in flight per row: two once a row has three or more
+// (K >= 6144).  One token on 4096 rows: 5.48 against 6.27 us at K = 8192,
+// 7.99 against 9.13 at 14336; at K = 4096 (two per row) the single one
+// stays (8.40 against 8.59 us on 14336 rows).
+__host__ __device__ constexpr int depth_for(int ipr) { return ipr >= 3 ? 2 : 1; }
 // Up to two tokens: measured on 14336 x 4096 weights, 8.9 and 10.6 us
 // against 14.6 us for the few-token kernel; at three and four tokens the two
 // kernels tie, beyond that the per-token LDS reads and dot products lose.
@@ -1222,7 +1227,7 @@ __host__ __device__ constexpr int lds_bytes(int MT, int M, int K, int nsb) {
 }
 }  // namespace mv
 
-template <int MT>
+template <int MT, int D>
 __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
     extern __shared__ __attribute__((aligned(16))) int8_t s_mv[];
     const int lane = threadIdx.x & 63;
@@ -1256,24 +1261,27 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
         for (int c = w; c < nl; c += mv::NW) copy16(rs_l, s_al + 1024 * c, 1024 * c + 16 * lane, 0);
     }
 
-    // ---- weights: one load instruction in flight per row ----------------------
+    // ---- weights: D load instructions in flight per row -----------------------
     // Instruction (r, j) reads superblocks 8j .. 8j+7 of the wave's row r; the
-    // wave walks j = 0 .. ipr-1 over its RPW rows in turn, keeping one
-    // instruction per row in flight (the next group of that row), and past the
-    // last group re-reads it (unused, drained at the end).
+    // wave walks j = 0 .. ipr-1 over its RPW rows in turn, keeping D
+    // instructions per row in flight, and past the last group re-reads it
+    // (unused, drained at the end), so every step has the same loads in
+    // flight.
     const int c8 = lane & 7, sbl = lane >> 3;
     const int cq = c8 >> 1, hq = c8 & 1;
-    v4i wq[mv::RPW], wh[mv::RPW];
+    v4i wq[mv::RPW][D], wh[mv::RPW][D];
     auto issue = [&](int r, int j, v4i &q, v4i &h) __attribute__((always_inline)) {
         const int off = (row0 + r) * rowbytes + (8 * min(j, ipr - 1) + sbl) * BB;  // < (N + 256) rows
         q = ld16(rs_w, off + 16 + 16 * c8, 0);
         h = ld16(rs_w, off, 0);
     };
 #pragma unroll
-    for (int r = 0; r < mv::RPW; ++r) issue(r, 0, wq[r], wh[r]);
+    for (int jj = 0; jj < D; ++jj)
+#pragma unroll
+        for (int r = 0; r < mv::RPW; ++r) issue(r, jj, wq[r][jj], wh[r][jj]);
     // this wave's activation copies have landed once at most the weight loads
     // are in flight; the barrier covers the other waves' copies
-    wait_vmcnt<2 * mv::RPW>();
+    wait_vmcnt<2 * mv::RPW * D>();
     barrier_nofence();
 
     float acc[mv::RPW][MT];
@@ -1331,14 +1339,17 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
         }
     };
 
-    for (int j = 0; j < ipr; ++j) {
+    for (int j0 = 0; j0 < ipr; j0 += D) {
 #pragma unroll
-        for (int r = 0; r < mv::RPW; ++r) {
-            // row r's instruction j has landed once the RPW - 1 issued after
-            // it may still be in flight
-            wait_vmcnt<2 * (mv::RPW - 1)>();
-            compute(j, wq[r], wh[r], acc[r]);
-            issue(r, j + 1, wq[r], wh[r]);
+        for (int jj = 0; jj < D; ++jj) {
+#pragma unroll
+            for (int r = 0; r < mv::RPW; ++r) {
+                // row r's instruction j0 + jj has landed once the RPW * D - 1
+                // issued after it may still be in flight
+                wait_vmcnt<2 * (mv::RPW * D - 1)>();
+                if (j0 + jj < ipr) compute(j0 + jj, wq[r][jj], wh[r][jj], acc[r]);  // uniform
+                issue(r, j0 + jj + D, wq[r][jj], wh[r][jj]);
+            }
         }
     }
 
@@ -1808,9 +1819,16 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             const dim3 grid((unsigned)((N + q4w::mv::RPG - 1) / q4w::mv::RPG)), block(64 * q4w::mv::NW);
             const int mt = mv_tokens(M);
             const size_t lds = (size_t)q4w::mv::lds_bytes(mt, M, K, a.nsb);
+            const bool deep = q4w::mv::depth_for(a.nsb / 8) == 2;
             switch (mt) {
-                case 1: hipLaunchKernelGGL(q4w::gemv_q4k_kernel<1>, grid, block, lds, stream, a); break;
-                default: hipLaunchKernelGGL(q4w::gemv_q4k_kernel<2>, grid, block, lds, stream, a); break;
+                case 1:
+                    if (deep) hipLaunchKernelGGL((q4w::gemv_q4k_kernel<1, 2>), grid, block, lds, stream, a);
+                    else hipLaunchKernelGGL((q4w::gemv_q4k_kernel<1, 1>), grid, block, lds, stream, a);
+                    break;
+                default:
+                    if (deep) hipLaunchKernelGGL((q4w::gemv_q4k_kernel<2, 2>), grid, block, lds, stream, a);
+                    else hipLaunchKernelGGL((q4w::gemv_q4k_kernel<2, 1>), grid, block, lds, stream, a);
+                    break;
             }
             break;
         }
