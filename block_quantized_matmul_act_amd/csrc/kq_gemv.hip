@@ -87,7 +87,7 @@ __device__ __forceinline__ void stage_acts(const Args &a, int8_t *s_qs, float *s
 // q - 32 is formed per byte without borrows: (q | 0x80) - 0x20, then bit 7
 // flipped back.
 // ---------------------------------------------------------------------------
-template <int MT>
+template <int MT, int D>
 __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
     extern __shared__ __attribute__((aligned(16))) int8_t s_gv[];
     const int lane = threadIdx.x & 63;
@@ -124,12 +124,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
         R.dd = ld4(rs_w, (base + 208) & ~3);
     };
     constexpr int LOADS = 8;  // per issue
-    Raw raw[RPW];
+    // D groups of loads in flight per row (past the last group a re-read of
+    // it, unused and drained at the end, so every step has the same loads in
+    // flight)
+    Raw raw[RPW][D];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) issue(r, 0, raw[r]);
+    for (int jj = 0; jj < D; ++jj)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) issue(r, jj, raw[r][jj]);
     // this wave's activation copies have landed once at most the weight loads
     // are in flight; the barrier covers the other waves' copies
-    wait_vmcnt<LOADS * RPW>();
+    wait_vmcnt<LOADS * RPW * D>();
     __builtin_amdgcn_s_barrier();
 
     float acc[RPW][MT];
@@ -181,14 +186,17 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
         }
     };
 
-    for (int j = 0; j < ipr; ++j) {
+    for (int j0 = 0; j0 < ipr; j0 += D) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            // row r's loads for group j have landed once the RPW - 1 issued
-            // after them may still be in flight
-            wait_vmcnt<LOADS * (RPW - 1)>();
-            compute(j, raw[r], acc[r]);
-            issue(r, j + 1, raw[r]);
+        for (int jj = 0; jj < D; ++jj) {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                // row r's loads for group j0 + jj have landed once the
+                // RPW * D - 1 groups issued after them may still be in flight
+                wait_vmcnt<LOADS * (RPW * D - 1)>();
+                if (j0 + jj < ipr) compute(j0 + jj, raw[r][jj], acc[r]);  // uniform
+                issue(r, j0 + jj + D, raw[r][jj]);
+            }
         }
     }
 
@@ -411,11 +419,20 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
     }
     const dim3 grid((unsigned)((N + gv::RPG - 1) / gv::RPG));
     const size_t lds = (size_t)gv::lds_bytes(mt, M, K);
-    switch (mt) {
-        case 1: hipLaunchKernelGGL(gv::gemv_q6k_kernel<1>, grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(gv::gemv_q6k_kernel<2>, grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(gv::gemv_q6k_kernel<4>, grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL(gv::gemv_q6k_kernel<8>, grid, block, lds, stream, a); break;
+    // two groups of loads in flight per row for four or eight tokens once a
+    // row has three or more groups (4096 x 14336: 16.7 against 17.7 us at 4
+    // tokens, 29.0 against 31.6 at 8; at one and two tokens one group in
+    // flight is faster, 12.8 against 14.5 us)
+    if (K / 2048 >= 3 && mt >= 4) {
+        if (mt == 4) hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 2>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((gv::gemv_q6k_kernel<8, 2>), grid, block, lds, stream, a);
+    } else {
+        switch (mt) {
+            case 1: hipLaunchKernelGGL((gv::gemv_q6k_kernel<1, 1>), grid, block, lds, stream, a); break;
+            case 2: hipLaunchKernelGGL((gv::gemv_q6k_kernel<2, 1>), grid, block, lds, stream, a); break;
+            case 4: hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 1>), grid, block, lds, stream, a); break;
+            default: hipLaunchKernelGGL((gv::gemv_q6k_kernel<8, 1>), grid, block, lds, stream, a); break;
+        }
     }
     return hipGetLastError();
 }
