@@ -12,7 +12,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kq {
+
+#define KQ_INLINE __attribute__((always_inline))
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{})
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

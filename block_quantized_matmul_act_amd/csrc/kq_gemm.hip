@@ -400,20 +400,6 @@ __device__ __forceinline__ int swz(int r, int c) { return r * MPITCH + 16 * c; }
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x020, SG_DSR = 0x100, SG_DSW = 0x200 };
 
-#define KQ_INLINE __attribute__((always_inline))
-
-template <int V>
-using IC = std::integral_constant<int, V>;
-
-// f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{})
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(IC<B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 // Per-thread registers of one chunk between its global loads and its unpack.
 template <int FMT>
 struct ChunkRegs;

@@ -1380,9 +1380,8 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
 // Step t multiplies superblock t (first half) and T + t (second half),
 // T = ceil(nsb / 2).  The activations of a step (values, scales, min-term
 // operands of both halves, all token rows) are copied global -> LDS into a
-// ring of 4 slots, RING_L = 3 steps ahead; each wave loads its strip's
-// weights for the same step into a register ring of 4 slots, in the same
-// issue.  Vector-memory loads complete in issue order, so the wait for a
+// ring of L + 1 slots, L steps ahead; each wave loads its strip's weights
+// for the same step into a register ring of L + 1 slots, in the same issue.  Vector-memory loads complete in issue order, so the wait for a
 // step's copies is also a wait for the weights issued before them, but
 // those are the weights of the same step or earlier: nothing is held up
 // that is not needed.  (The kernels above stage activations one step ahead
@@ -1397,14 +1396,20 @@ __global__ __launch_bounds__(64 * mv::NW) void gemv_q4k_kernel(Args a) {
 // superblock and uses each byte twice.  The A operand of K-step s is the 16
 // contiguous activation bytes at 64kg + 16s of the token row.
 // ---------------------------------------------------------------------------
-constexpr int RING_L = 3;              // steps of lead
-constexpr int RING_S = RING_L + 1;     // LDS slots and weight registers sets
 constexpr int RING_ZERO = 1024;        // zero bytes read as the min-term operand of lanes 32..63
 
 template <int TM>
 struct RingCfg {
     static_assert(TM == 16 || TM == 32 || TM == 64, "16, 32 or 64 token rows");
     static constexpr int MT = TM / 16;             // 16-row m-tiles
+    // steps of lead, and LDS slots / weight register sets.  Measured on
+    // 14336 weight rows, K = 2048 .. 8192: with 32 or 64 token rows a lead
+    // of two steps is 4-9% faster than three, and four is 10% slower than
+    // three; one step is up to 3% faster with 64 rows at K <= 3072 but
+    // 6-9% slower at K = 8192.  With 16 rows three steps are as fast as
+    // two or slightly faster, and one is 6-35% slower.
+    static constexpr int L = TM == 16 ? 3 : 2;
+    static constexpr int S = L + 1;
     static constexpr int ACTH = TM * ROW;          // values of one half: [row][256], swizzled
     static constexpr int DAH = 256;                // scales of one half (a 64-lane 4-byte copy)
     // min-term operands of one half: [part][row][16] (at TM = 16 the 1 KiB
@@ -1412,13 +1417,13 @@ struct RingCfg {
     static constexpr int ALH = 2 * TM * 16 > 1024 ? 2 * TM * 16 : 1024;
     static constexpr int O_DA = 2 * ACTH, O_AL = O_DA + 2 * DAH;
     static constexpr int SLOT = O_AL + 2 * ALH;
-    static constexpr int LDS = RING_S * SLOT + RING_ZERO;
+    static constexpr int LDS = S * SLOT + RING_ZERO;
     static constexpr int NA = ACTH / 1024;         // value copies per half
     static constexpr int NL = ALH / 1024;          // operand copies per half
     static_assert(NL <= 2 && NA % 4 == 0, "four value copies of a half per wave group, two operand parts");
     static constexpr int CPW = NA / 4 + 1;         // copies per wave and step
     static constexpr int LOADS = CPW + 3;          // vector-memory instructions per wave and step
-    static_assert(LOADS * (RING_L - 1) < 64, "vmcnt range");
+    static_assert(LOADS * (L - 1) < 64, "vmcnt range");
 };
 
 struct RingW {
@@ -1449,10 +1454,10 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     // loads of steps past the end, so that every step issues the same)
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
 
-    int8_t *const zero = s_lds + RING_S * C::SLOT;
+    int8_t *const zero = s_lds + C::S * C::SLOT;
     for (int i = tid; i < RING_ZERO / 4; i += 512) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
 
-    // ---- copies of step x into slot x % RING_S.  Wave w copies for its own
+    // ---- copies of step x into slot x % S.  Wave w copies for its own
     // K-half kh: value copies CPV*(w%4) .. +CPV-1 (copy r: rows 4r .. 4r+3;
     // lane l fills piece l%16 of row 4r + l/16 with piece (l%16) ^ row), and
     // one more by w%4: the scales (lane l: token l), the min-term operands
@@ -1476,7 +1481,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     const int x_lds = wq == 0 ? C::O_DA + kh * C::DAH
                               : C::O_AL + kh * C::ALH + (TM == 64 ? min(max(wq - 1, 0), 1) * 1024 : 0);
     auto copies = [&](int x) __attribute__((always_inline)) {
-        int8_t *S = s_lds + (x % RING_S) * C::SLOT;
+        int8_t *S = s_lds + (x % C::S) * C::SLOT;
         const int sb = kh ? T + x : x;
         const bool real = x < T && sb < nsb;
         const int sbr = real ? sb : 0;
@@ -1492,7 +1497,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     // check drops them)
     const int w_hdr = (int)((uint32_t)(n0 + r16) * (uint32_t)rowbytes);
     const int w_nib = w_hdr + 16 + 32 * kg;
-    RingW ring[RING_S];
+    RingW ring[C::S];
     auto wload = [&](int x, RingW &R) __attribute__((always_inline)) {
         const int sb = kh ? T + x : x;
         const bool real = x < T && sb < nsb;
@@ -1609,33 +1614,45 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
         }
     };
 
-    // step x: the copies and loads of step x + RING_L go out once every wave
-    // is past step x - 1 (their slot's last reader), then step x multiplies
+    // step x: the copies and loads of step x + L go out once every wave is
+    // past step x - 1 (their slot's last reader), then step x multiplies
     auto step = [&](auto KK, int x) __attribute__((always_inline)) {
         constexpr int k = decltype(KK)::value;
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<C::LOADS * (RING_L - 1)>();
+        wait_vmcnt<C::LOADS * (C::L - 1)>();
         barrier_nofence();
-        copies(x + RING_L);
-        wload(x + RING_L, ring[(k + RING_L) % RING_S]);
+        copies(x + C::L);
+        wload(x + C::L, ring[(k + C::L) % C::S]);
         __builtin_amdgcn_sched_barrier(0);
         const int sb = kh ? T + x : x;
         if (x < T && sb < nsb) compute(ring[k], (uint32_t)(k * C::SLOT));  // uniform
     };
 #pragma unroll
-    for (int x = 0; x < RING_L; ++x) {
+    for (int x = 0; x < C::L; ++x) {
         copies(x);
         wload(x, ring[x]);
     }
-    // (a whole number of ring turns: every step issues the same loads, so
-    // the waits stay partial)
-    const int npass = (T + RING_S - 1) / RING_S * RING_S;
-    for (int x0 = 0; x0 < npass; x0 += RING_S) {
-        step(std::integral_constant<int, 0>{}, x0);
-        step(std::integral_constant<int, 1>{}, x0 + 1);
-        step(std::integral_constant<int, 2>{}, x0 + 2);
-        step(std::integral_constant<int, 3>{}, x0 + 3);
-    }
+    // Whole ring turns (every step issues the same loads, so the waits stay
+    // partial), then the T mod S steps left over, which issue nothing: in
+    // tail step j the loads of steps x .. nfull - 1 + L are outstanding,
+    // L - j steps' worth, and step x's are the oldest.  (Padding T to whole
+    // turns instead cost about half a step per padded step.)
+    const int nfull = T / C::S * C::S;
+    for (int x0 = 0; x0 < nfull; x0 += C::S)
+        static_for<0, C::S>([&](auto KK) KQ_INLINE { step(KK, x0 + decltype(KK)::value); });
+    auto tail_step = [&](auto JJ) KQ_INLINE {
+        constexpr int j = decltype(JJ)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (C::L - 1 - j)>();
+        barrier_nofence();
+        __builtin_amdgcn_sched_barrier(0);
+        const int sb = kh ? T + nfull + j : nfull + j;
+        if (sb < nsb) compute(ring[j], (uint32_t)(j * C::SLOT));  // uniform
+    };
+    const int rem = T - nfull;
+    static_for<1, C::S>([&](auto RR) KQ_INLINE {
+        if (rem == decltype(RR)::value) static_for<0, decltype(RR)::value>(tail_step);
+    });
     // the copies and loads past the end (reading nothing) drain; then the
     // second half's sums go through LDS to the first half's waves
     wait_vmcnt<0>();
@@ -1666,7 +1683,6 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
         }
     }
 }
-static_assert(RING_S == 4, "the step loop above is unrolled for four slots");
 
 // out[0, n) = 0 (the product over an empty K); a kernel rather than a memset
 // so that the call stays capturable in a graph

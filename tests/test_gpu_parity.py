@@ -282,7 +282,10 @@ def test_q4k_few_token_ring(kq):
     products in full against the oracle at a ragged width (11016 columns:
     the last workgroup has two 16-row strips past N and 8 columns) for all
     three token-tile builds (16, 32 and 64 rows) and odd and even superblock
-    counts."""
+    counts.  Steps per K-half T = 2, 3, 5, 7 against rings of 3 slots (32
+    and 64 rows) and 4 (16 rows): tails of 1 .. 3 steps with and without
+    whole ring turns before them, and none; with an odd superblock count
+    the second half's last step is empty, in the turns or in the tail."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
     assert name(64, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert name(33, 10944, 1280) == "gemm_q4_k_m64_ring"
@@ -291,7 +294,7 @@ def test_q4k_few_token_ring(kq):
     assert name(16, 10880, 4096) == "gemm_q4_k_m16"
     N = 11016
     v = kq.kq_select_variant(Q4_K, 64, N, 768)
-    for K in (768, 1280):
+    for K in (768, 1280, 2304, 3584):
         W = datagen.make_weights(Q4_K, N, K, 5100 + K)
         x = datagen.draw_activations(64, K, 5200 + K)
         for M in (3, 16, 17, 32, 33, 64):
