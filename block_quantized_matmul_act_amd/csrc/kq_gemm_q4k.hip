@@ -1541,6 +1541,10 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
                 }
             }
         };
+        // The two waves on a SIMD (one per K-half) leave each step's barrier
+        // together; the one in its MFMA phase goes first, so the other's
+        // fold tends to fall under those MFMAs (2-3% at 48-64 tokens).
+        __builtin_amdgcn_s_setprio(1);
         rd(0, av[0]);
         rd(1, av[1]);
         // scales of sub-blocks 2kg (K-steps 0, 1) and 2kg + 1 (2, 3):
@@ -1590,6 +1594,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
                 for (int t = 0; t < MT; ++t) da[t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 64 * t));
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // fold: out += d_a[m] * (d[n] * float(8*acc_h + acc_l) - dmin[n] * M),
         // M = sum_j m_j B_j exact on one bf16 MFMA per m-tile (A row m =
         // both exact parts of B_0..B_7 in k-groups 0 and 1, k-groups 2 and 3
