@@ -1751,16 +1751,16 @@ int q4k_kernel_choice(int M, int N, int K) {
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
     const int cus = num_cus();
-    // the K-split ring kernel runs one 64-row workgroup per CU: it needs the
-    // weight rows to fill two thirds of the CUs.  Measured against the
-    // two-wave kernel (K = 4096): 14336 rows (224 workgroups) 12.5 against
-    // 14.6 us at 20 tokens, 13.9 against 15.7 at 32, 19.2 against 19.9 at
-    // 64; 11008 rows (172) 13.0 against 14.7 at 32, 17.6 against 18.1 at 64;
-    // 8192 rows (128) 12.7 against 11.4 at 32, 17.4 against 14.9 at 64.
-    // Its 16-row build against the four-wave split kernel on 14336 rows:
-    // 11.3 against 13.6 us at 16 tokens, 10.7 against 12.2 at 8, 10.4
-    // against 11.5 at 3
-    if (M <= 64 && 3 * ((N + 63) / 64) >= 2 * cus) return Q4K_FEW_RING;
+    // The K-split ring kernel (one 64-row workgroup per CU) once the 32-row
+    // workgroups of the split and two-wave kernels would need a second round
+    // on some CUs: those kernels jump by a quarter to a half there, and the
+    // ring kernel wins from that point on.  K = 4096, us, ring against the
+    // other: 9216 rows 10.0 / 11.0 at 3 tokens, 10.8 / 13.0 at 16, 11.6 /
+    // 14.6 at 32, 15.6 / 17.7 at 64; 14336 rows 11.2 / 13.6 at 16, 16.5 /
+    // 19.9 at 64; K = 2048 and 8192 alike (8448-10240 rows: 5-25% faster).
+    // At 8192 rows (one round) the other kernels win: 9.8 / 7.5 at 3 tokens,
+    // 15.4 / 14.3 at 64.
+    if (M <= 64 && (N + 31) / 32 > cus) return Q4K_FEW_RING;
     if (M <= 16) return Q4K_FEW_SPLIT;
     if (M <= 64) return Q4K_FEW_TOKENS;
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);

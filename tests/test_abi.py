@@ -178,12 +178,14 @@ def test_variants_and_counters(kq):
     assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(17, 4096, 4096) == "gemm_q4_k_m64"
     assert q4(16, 4096, 4096) == "gemm_q4_k_m16"
-    # 3 .. 64 tokens: the K-split ring kernel once its 64-row workgroups
-    # cover two thirds of the CUs
+    # 3 .. 64 tokens: the K-split ring kernel once the 32-row workgroups of
+    # the other few-token kernels would outnumber the CUs (256 here)
     assert q4(64, 14336, 4096) == "gemm_q4_k_m64_ring"
-    assert q4(17, 10944, 4096) == "gemm_q4_k_m64_ring"  # 171 workgroups
-    assert q4(17, 10880, 4096) == "gemm_q4_k_m64"       # 170
-    assert q4(16, 14336, 4096) == "gemm_q4_k_m64_ring"  # its 16-row build
+    assert q4(17, 8224, 4096) == "gemm_q4_k_m64_ring"   # 257 row pairs of 32
+    assert q4(17, 8192, 4096) == "gemm_q4_k_m64"        # 256
+    assert q4(16, 8224, 4096) == "gemm_q4_k_m64_ring"   # its 16-row build
+    assert q4(16, 8192, 4096) == "gemm_q4_k_m16"
+    assert q4(64, 10880, 4096) == "gemm_q4_k_m64_ring"
     assert q4(3, 14336, 4096) == "gemm_q4_k_m64_ring"
     # base-3 ternary: the register-unpack tile kernel when K is a multiple of
     # 256, the digit-plane tile kernel otherwise

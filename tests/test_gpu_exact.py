@@ -111,7 +111,7 @@ def assert_exact(out, want, what):
 # 8-wave 64 x 128 build takes the smaller counts (K = 768: an odd number of
 # superblocks, so one half of its waves sits out the last step); the
 # few-token kernel has a one- and a two-m-tile build; the K-split ring
-# kernel takes 3 .. 64 tokens when N / 64 reaches two thirds of the CUs, in
+# kernel takes 3 .. 64 tokens when N / 32 exceeds the CU count, in
 # 16-, 32- and 64-row builds (one superblock: the second K-half has none;
 # three: its second step is empty; 11016 columns: a ragged last workgroup); the matrix-vector kernel takes one
 # or two tokens with K a multiple of 2048

@@ -212,7 +212,7 @@ def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
 # (fmt, K, variant, token rows per launch, weight rows); the 128 x 128 Q4_K
 # kernel takes shapes of more than 256 such tiles, hence its 2100 weight rows,
 # the 4-wave 64 x 128 build more than 256 of its own (1100 rows), and the
-# K-split ring kernel at least 171 64-row workgroups (11016 rows, ragged)
+# K-split ring kernel more than 256 32-row pieces (11016 rows, ragged)
 IDENTITY_CASES = [
     (Q4_K, 2048, "gemm_q4_k_matvec", 2, 72),
     (Q4_K, 2048, "gemm_q4_k_m64", 64, 72),

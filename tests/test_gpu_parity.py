@@ -288,10 +288,10 @@ def test_q4k_few_token_ring(kq):
     the second half's last step is empty, in the turns or in the tail."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
     assert name(64, 14336, 4096) == "gemm_q4_k_m64_ring"
-    assert name(33, 10944, 1280) == "gemm_q4_k_m64_ring"
-    assert name(64, 10880, 4096) == "gemm_q4_k_m64"
+    assert name(33, 8224, 1280) == "gemm_q4_k_m64_ring"
+    assert name(64, 8192, 4096) == "gemm_q4_k_m64"
     assert name(3, 14336, 4096) == "gemm_q4_k_m64_ring"
-    assert name(16, 10880, 4096) == "gemm_q4_k_m16"
+    assert name(16, 8192, 4096) == "gemm_q4_k_m16"
     N = 11016
     v = kq.kq_select_variant(Q4_K, 64, N, 768)
     for K in (768, 1280, 2304, 3584):
