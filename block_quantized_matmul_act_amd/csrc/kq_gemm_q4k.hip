@@ -907,13 +907,6 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 constexpr int KWS = SWN + SHD;  // weight stage: nibbles of one half of 32 blocks, their headers
 constexpr int KFS = SDS + SLS;  // fold data of one superblock: scales and min-term parts of 64 rows
 
-__device__ __forceinline__ v4i mma16_i8(v4i a, v4i b, v4i c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v4f mma16_bf16(v8bf a, v8bf b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 template <int MT, int KW, int DW>
 struct SplitCfg {
     static_assert(MT == 1 || MT == 2 || MT == 4, "16-row m-tiles: up to 16, 32 or 64 tokens");

@@ -1,0 +1,393 @@
+// kq_gemm_q6k.hip -- the few-token Q6_K product (gfx950): more tokens than
+// the matrix-vector kernel takes, up to 64, against Q6_K weights (the tile
+// GEMM of vllm.cpp PR 3036 over Q6_K weights and BlockQ8_K activations, at
+// the small-batch end of the mul_mat_q / mat-vec crossover).
+//
+// The 128 x 128 tile kernel leaves most of the chip idle here: 4096 weight
+// rows are 32 tiles whatever the token count.  This kernel takes all tokens
+// (a 16-, 32- or 64-row token tile, TM) in one workgroup and splits the
+// weights over workgroups by rows and over waves by rows and K:
+//   * A workgroup of 8 waves owns 16 * (8 / KP) weight rows as 16-row strips;
+//     the superblocks are cut into KP contiguous K-parts (KP = 2, 4 or 8), and
+//     wave w takes strip w % (8 / KP) over K-part w / (8 / KP).  Narrow
+//     weights take more K-parts so that the grid still covers the CUs.
+//   * Step x multiplies superblock pT + x of every K-part p (T = ceil(nsb /
+//     KP)).  A step's activations (values and scales of every K-part, all
+//     token rows) are copied global -> LDS into a ring of L + 1 slots, L
+//     steps ahead; each wave loads its strip's weights for the same step into
+//     a register ring in the same issue.  Vector-memory loads complete in
+//     issue order, so the wait for a step's copies also waits for the weights
+//     issued before them: those of the same step or earlier.
+//   * The loop runs whole ring turns (steps past a part's end read through a
+//     buffer resource with no records: zeros, no memory access), then the
+//     T mod (L + 1) steps left over, which issue nothing.
+//   * The K-parts are summed through LDS at the end, in a fixed order.
+//
+// Operands (v_mfma_i32_16x16x64_i8): in K-step s of a superblock, lane group
+// kg (lane / 16) holds the 16 values 128h + 32u + 16(s % 2) + i with h = kg/2
+// and u = 2(kg % 2) + s/2, sub-block 4kg + s.  Those are
+//   * the low (kg even) or high (kg odd) nibbles of ql bytes 64h + 16s + i,
+//   * bits 4(kg % 2) + 2(s/2) of qh bytes 32h + 16(s % 2) + i,
+//   * scaled by scale byte 4kg + s,
+// so a lane reads 64 contiguous ql bytes, 32 contiguous qh bytes and 4
+// contiguous scale bytes per superblock, and its A operand in K-step s is the
+// 16 contiguous activation bytes at 64kg + 16s of the token row.  Blocks are
+// 210 bytes (2-byte aligned): a lane loads aligned dwords and shifts them into
+// place with v_alignbit.  W = sc (q - 32) = 64 h + l is split into two int8
+// digits (q6k_digits), two MFMAs per K-step and m-tile, and the superblock's
+// integer sum T = 64 acc_h + acc_l is folded once per superblock:
+// out += d_a * d * T.
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+#include "kq_tile.hpp"
+
+namespace kq {
+namespace q6r {
+using namespace tl;
+
+constexpr int QB = 210;    // Q6_K block bytes
+constexpr int ROW = 256;   // LDS bytes per staged activation row (one superblock)
+
+struct Args {
+    const uint8_t *W;
+    const int8_t *qs;
+    const float *da;  // [nsb][M]
+    float *out;
+    int M, N, K, nsb;
+};
+
+template <int TM, int KP>
+struct Cfg {
+    static_assert(TM == 16 || TM == 32 || TM == 64, "16, 32 or 64 token rows");
+    static_assert(KP == 2 || KP == 4 || KP == 8, "two, four or eight K-parts");
+    static constexpr int MT = TM / 16;            // 16-row m-tiles
+    static constexpr int NS = 8 / KP;             // 16-row strips per workgroup
+    static constexpr int ROWS = 16 * NS;          // weight rows per workgroup
+    static constexpr int ACT = TM * ROW;          // values of one K-part: [row][256], swizzled
+    static constexpr int PART = ACT + 256;        // ... then its scales (a 64-lane 4-byte copy)
+    static constexpr int SLOT = KP * PART;
+    // steps of lead: three with 16 token rows, two otherwise, one where two
+    // do not fit the LDS
+    static constexpr int L = TM == 16 ? 3 : (3 * SLOT <= 160 * 1024 ? 2 : 1);
+    static constexpr int S = L + 1;               // LDS slots and weight register sets
+    static constexpr int LDS = S * SLOT;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static constexpr int NA = ACT / 1024;         // value copies per K-part
+    static constexpr int CPV = NA / NS;           // ... per wave
+    static_assert(CPV * NS == NA, "value copies split evenly over a part's waves");
+    // vector-memory instructions per wave and step: value copies, the scale
+    // copy, 10 weight loads
+    static constexpr int LOADS = CPV + 1 + 10;
+    static_assert(LOADS * (L - 1) < 64, "vmcnt range");
+    // the K-parts' sums through LDS at the end
+    static_assert((KP - 1) * NS * MT * 4 * 64 * 4 <= LDS, "reduction space");
+};
+
+// one superblock of a lane's weights, as aligned dwords
+struct WRaw {
+    v4i l0, l1, l2, l3;   // ql: 68 bytes from the aligned start of its 64
+    uint32_t l4;
+    v4i h0, h1;           // qh: 36 bytes from the aligned start of its 32
+    uint32_t h2;
+    v2u sc;               // the dwords holding its 4 scale bytes
+    uint32_t dd;          // d (a 2-byte load: its aligned dword can pass the
+                          // buffer's end)
+};
+
+template <int TM, int KP>
+__global__ __launch_bounds__(512, 1) void gemm_q6k_ring_kernel(Args a) {
+    using C = Cfg<TM, KP>;
+    constexpr int MT = C::MT, NS = C::NS;
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int strip = w % NS, part = w / NS;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
+    const int T = (nsb + KP - 1) / KP;  // steps
+    const int n0 = blockIdx.x * C::ROWS + 16 * strip;
+    const int rowbytes = nsb * QB;
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+    // no records: reads return zero without a memory access (copies and
+    // loads of steps past a part's end, so that every step issues the same)
+    const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
+
+    // ---- copies of step x into slot x % S.  The NS waves of K-part p copy
+    // its values (copy r: rows 4r .. 4r+3; lane l fills piece l%16 of row
+    // 4r + l/16 with piece (l%16) ^ row), CPV copies each, and each copies
+    // the part's scales (lane l: token l; the same bytes to the same place),
+    // so every wave issues the same.  Token rows past M read other rows'
+    // data or zero; their outputs are dropped.
+    int a_vo[C::CPV];
+#pragma unroll
+    for (int i = 0; i < C::CPV; ++i) {
+        const int row = 4 * (C::CPV * strip + i) + (lane >> 4);
+        a_vo[i] = row * K + 16 * ((lane & 15) ^ (row & 15));
+    }
+    auto copies = [&](int x) __attribute__((always_inline)) {
+        int8_t *P = s_lds + (x % C::S) * C::SLOT + part * C::PART;
+        const int sb = part * T + x;
+        const bool real = x < T && sb < nsb;
+        const int sbr = real ? sb : 0;
+#pragma unroll
+        for (int i = 0; i < C::CPV; ++i)
+            copy16(real ? rs_a : rs_nul, P + (C::CPV * strip + i) * 1024, a_vo[i], sbr * ROW);
+        copy4(real ? rs_d : rs_nul, P + C::ACT, 4 * lane, sbr * M * 4);
+    };
+    // ---- this lane's weights: row n0 + r16 (row offsets as unsigned: rows
+    // past N may pass 2^31, and the range check drops them)
+    const uint32_t w_row = (uint32_t)(n0 + r16) * (uint32_t)rowbytes;
+    const int o_ql = 64 * (kg >> 1), o_qh = 128 + 32 * (kg >> 1), o_sc = 192 + 4 * kg;
+    WRaw ring[C::S];
+    auto wload = [&](int x, WRaw &R) __attribute__((always_inline)) {
+        const int sb = part * T + x;
+        const bool real = x < T && sb < nsb;
+        const auto rw = real ? rs_w : rs_nul;
+        // the block start, and the aligned dword at or below it (every field
+        // offset used with it is a multiple of 4)
+        const uint32_t b = w_row + (uint32_t)((real ? sb : 0) * QB);
+        const int b4 = (int)(b & ~3u);
+        R.l0 = ld16(rw, b4 + o_ql, 0);
+        R.l1 = ld16(rw, b4 + o_ql + 16, 0);
+        R.l2 = ld16(rw, b4 + o_ql + 32, 0);
+        R.l3 = ld16(rw, b4 + o_ql + 48, 0);
+        R.l4 = ld4(rw, b4 + o_ql + 64, 0);
+        R.h0 = ld16(rw, b4 + o_qh, 0);
+        R.h1 = ld16(rw, b4 + o_qh + 16, 0);
+        R.h2 = ld4(rw, b4 + o_qh + 32, 0);
+        R.sc = ld8(rw, b4 + o_sc, 0);
+        R.dd = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 208, 0, 0);
+    };
+
+    v4f out[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = v4f{};
+    // LDS addresses: K-step s of m-tile t reads row 16t + r16, piece
+    // (4kg + s) ^ r16 of this wave's K-part; the scales of tokens 4kg ..
+    // 4kg+3 of m-tile t follow the values
+    uint32_t a_ad[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a_ad[s] = lds_addr(s_lds) + part * C::PART + r16 * ROW + (((4 * kg + s) ^ r16) << 4);
+    const uint32_t d_ad = lds_addr(s_lds) + part * C::PART + C::ACT + 16 * kg;
+
+    auto compute = [&](const WRaw &R, uint32_t so, int sb) __attribute__((always_inline)) {
+        // LDS reads of K-step s (one per m-tile), two K-steps in flight; the
+        // scale reads go out under K-step 2
+        v4i av[2][MT];
+        auto rd = [&](int s, v4i(&dst)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                switch (t) {
+                    case 0: dst[t] = lds_read16<0>(a_ad[s] + so); break;
+                    case 1: dst[t] = lds_read16<16 * ROW>(a_ad[s] + so); break;
+                    case 2: dst[t] = lds_read16<32 * ROW>(a_ad[s] + so); break;
+                    default: dst[t] = lds_read16<48 * ROW>(a_ad[s] + so); break;
+                }
+            }
+        };
+        __builtin_amdgcn_s_setprio(1);
+        rd(0, av[0]);
+        rd(1, av[1]);
+        // the block's offset past the aligned dword (0 or 2 bytes)
+        const uint32_t sh = 8u * ((w_row + (uint32_t)(sb * QB)) & 3u);
+        const uint32_t ql[17] = {(uint32_t)R.l0[0], (uint32_t)R.l0[1], (uint32_t)R.l0[2], (uint32_t)R.l0[3],
+                                 (uint32_t)R.l1[0], (uint32_t)R.l1[1], (uint32_t)R.l1[2], (uint32_t)R.l1[3],
+                                 (uint32_t)R.l2[0], (uint32_t)R.l2[1], (uint32_t)R.l2[2], (uint32_t)R.l2[3],
+                                 (uint32_t)R.l3[0], (uint32_t)R.l3[1], (uint32_t)R.l3[2], (uint32_t)R.l3[3],
+                                 R.l4};
+        const uint32_t qhr[9] = {(uint32_t)R.h0[0], (uint32_t)R.h0[1], (uint32_t)R.h0[2], (uint32_t)R.h0[3],
+                                 (uint32_t)R.h1[0], (uint32_t)R.h1[1], (uint32_t)R.h1[2], (uint32_t)R.h1[3],
+                                 R.h2};
+        uint32_t qh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qh[e] = __builtin_amdgcn_alignbit(qhr[e + 1], qhr[e], sh);
+        const uint32_t scw = __builtin_amdgcn_alignbit(R.sc[1], R.sc[0], sh);
+        const uint32_t nib_sh = 4u * (uint32_t)(kg & 1);
+        v4i acc_h[MT], acc_l[MT];
+        v4f da[MT];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int sc = (int)(int8_t)(uint8_t)(scw >> (8 * s));
+            const uint32_t hsh = nib_sh + 2u * (uint32_t)(s >> 1);
+            v4i bh, bl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t l4 = (__builtin_amdgcn_alignbit(ql[4 * s + e + 1], ql[4 * s + e], sh) >> nib_sh) &
+                                    0x0F0F0F0Fu;
+                const uint32_t h2 = (qh[4 * (s & 1) + e] >> hsh) & 0x03030303u;
+                uint32_t dh, dl;
+                q6k_digits(l4 | (h2 << 4), sc, dh, dl);
+                bh[e] = (int)dh;
+                bl[e] = (int)dl;
+            }
+            // reads in flight behind m-tile t of K-step s: the rest of this
+            // K-step's, then the next K-step's or, under K-step 3, the
+            // scales' (MT)
+            v4i(&cur)[MT] = av[s & 1];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) lds_wait_n(2 * MT - 1 - t, cur[t]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                acc_h[t] = mma16_i8(cur[t], bh, s == 0 ? v4i{} : acc_h[t]);
+                acc_l[t] = mma16_i8(cur[t], bl, s == 0 ? v4i{} : acc_l[t]);
+            }
+            if (s < 2) {
+                rd(s + 2, av[s & 1]);
+            } else if (s == 2) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) da[t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 64 * t));
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // fold: out += d_a[m] * d[n] * (64 acc_h + acc_l)
+        const float dw = f16_bits_to_f32(R.dd);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            lds_wait_n(MT - 1 - t, da[t]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int Tq = (acc_h[t][i] << 6) + acc_l[t][i];
+                out[t][i] = fmaf((float)Tq * dw, da[t][i], out[t][i]);
+            }
+        }
+    };
+
+    // step x: the copies and loads of step x + L go out once every wave is
+    // past step x - 1 (their slot's last reader), then step x multiplies
+    auto step = [&](auto KK, int x) __attribute__((always_inline)) {
+        constexpr int k = decltype(KK)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (C::L - 1)>();
+        barrier_nofence();
+        copies(x + C::L);
+        wload(x + C::L, ring[(k + C::L) % C::S]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int sb = part * T + x;
+        if (x < T && sb < nsb) compute(ring[k], (uint32_t)(k * C::SLOT), sb);  // uniform
+    };
+#pragma unroll
+    for (int x = 0; x < C::L; ++x) {
+        copies(x);
+        wload(x, ring[x]);
+    }
+    // whole ring turns, then the T mod S steps left over, which issue
+    // nothing: in tail step j the loads of steps x .. nfull - 1 + L are
+    // outstanding, L - j steps' worth, and step x's are the oldest
+    const int nfull = T / C::S * C::S;
+    for (int x0 = 0; x0 < nfull; x0 += C::S)
+        static_for<0, C::S>([&](auto KK) KQ_INLINE { step(KK, x0 + decltype(KK)::value); });
+    auto tail_step = [&](auto JJ) KQ_INLINE {
+        constexpr int j = decltype(JJ)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (C::L - 1 - j)>();
+        barrier_nofence();
+        __builtin_amdgcn_sched_barrier(0);
+        const int sb = part * T + nfull + j;
+        if (sb < nsb) compute(ring[j], (uint32_t)(j * C::SLOT), sb);  // uniform
+    };
+    const int rem = T - nfull;
+    static_for<1, C::S>([&](auto RR) KQ_INLINE {
+        if (rem == decltype(RR)::value) static_for<0, decltype(RR)::value>(tail_step);
+    });
+    // the copies and loads past the end (reading nothing) drain; then the
+    // other parts' sums go through LDS to part 0's waves, added in part order
+    wait_vmcnt<0>();
+    barrier_nofence();
+    float *red = reinterpret_cast<float *>(s_lds);
+    if (part > 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[((((part - 1) * NS + strip) * MT + t) * 4 + i) * 64 + lane] = out[t][i];
+    }
+    barrier_nofence();
+    if (part == 0) {
+        // rows past M fall outside the resource; columns past N are sent out
+        // of range
+        const int n = n0 + r16;
+        const int voff = n < N ? (4 * kg * N + n) * 4 : OOB_VOFF;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            v4f sum = out[t];
+#pragma unroll
+            for (int p = 1; p < KP; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum[i] += red[((((p - 1) * NS + strip) * MT + t) * 4 + i) * 64 + lane];
+            const v4i bits = __builtin_bit_cast(v4i, sum);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(bits[i], rs_o, voff, (16 * t + i) * N * 4, 0);
+        }
+    }
+}
+
+}  // namespace q6r
+
+// Token counts this kernel takes: past the matrix-vector kernel, up to 64.
+bool q6k_ring_choice(int M, int N, int K) {
+    return M >= 1 && M <= 64 && N >= 1 && K >= 256 && K % 256 == 0 && !gemv_choice(2, M, N, K);
+}
+
+// K-parts: one workgroup per CU at a time, so the time goes as the rounds of
+// workgroups over the CUs times each one's share of K; the fewest parts
+// among the best, within what the token tile's LDS allows (64 rows: at most
+// four)
+int q6k_ring_parts(int M, int N) {
+    const int cus = num_cus();
+    const int kmax = M > 32 ? 4 : 8;
+    int best = 2;
+    int64_t best_num = 0, best_den = 1;  // rounds / parts as a fraction
+    for (int kp = 2; kp <= kmax; kp *= 2) {
+        const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp));
+        const int64_t rounds = (wgs + cus - 1) / cus;
+        if (kp == 2 || rounds * best_den < best_num * kp) {
+            best = kp;
+            best_num = rounds;
+            best_den = kp;
+        }
+    }
+    return best;
+}
+
+template <int TM, int KP>
+static void launch_q6r(const q6r::Args &a, hipStream_t stream) {
+    constexpr int R = q6r::Cfg<TM, KP>::ROWS;
+    hipLaunchKernelGGL((q6r::gemm_q6k_ring_kernel<TM, KP>), dim3((unsigned)((a.N + R - 1) / R)), dim3(512), 0,
+                       stream, a);
+}
+
+hipError_t launch_gemm_q6k_ring(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
+                                int K, hipStream_t stream) {
+    q6r::Args a;
+    a.W = static_cast<const uint8_t *>(W);
+    a.qs = qs;
+    a.da = da;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nsb = K / 256;
+    const int kp = q6k_ring_parts(M, N);
+    if (M <= 16) {
+        if (kp == 2) launch_q6r<16, 2>(a, stream);
+        else if (kp == 4) launch_q6r<16, 4>(a, stream);
+        else launch_q6r<16, 8>(a, stream);
+    } else if (M <= 32) {
+        if (kp == 2) launch_q6r<32, 2>(a, stream);
+        else if (kp == 4) launch_q6r<32, 4>(a, stream);
+        else launch_q6r<32, 8>(a, stream);
+    } else {
+        if (kp == 2) launch_q6r<64, 2>(a, stream);
+        else launch_q6r<64, 4>(a, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kq

@@ -23,6 +23,12 @@ __device__ __forceinline__ v16i mma_i8(v4i a, v4i b, v16i c) {
 __device__ __forceinline__ v16f mma_bf16(v8bf a, v8bf b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ v4i mma16_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mma16_bf16(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 // s_waitcnt on the vector-memory counter only (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -45,6 +51,12 @@ __device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rs, void *lds, int 
 }
 __device__ __forceinline__ v4i ld16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+__device__ __forceinline__ v2u ld8(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
 }
 
 // LDS reads of staged data, written as instructions of our own: the

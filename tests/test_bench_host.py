@@ -29,12 +29,12 @@ def test_kernel_source_hash_covers_each_format():
     hashes = {f: bench.kernel_source_hash(f) for f in bench.GEMM_SOURCES}
     for h in hashes.values():
         assert re.fullmatch(r"[0-9a-f]{16}", h)
-    # Q6_K and two-bit ternary run on the same generic kernel sources; base-3
-    # ternary adds its register-unpack tile kernel, Q4_K has its own
-    assert hashes["q6_k"] == hashes["tq2"]
-    assert hashes["tq"] != hashes["q6_k"]
-    assert hashes["q4_k"] != hashes["q6_k"]
+    # every format has its own set: the generic tile kernel plus, for Q6_K,
+    # its few-token ring kernel, for base-3 ternary its register-unpack tile
+    # kernel; Q4_K its own kernels
+    assert len(set(hashes.values())) == len(hashes)
     assert "kq_gemm_tq.hip" in bench.GEMM_SOURCES["tq"] and "kq_tile.hpp" in bench.GEMM_SOURCES["q4_k"]
+    assert "kq_gemm_q6k.hip" in bench.GEMM_SOURCES["q6_k"] and "kq_gemm_q6k.hip" not in bench.GEMM_SOURCES["tq2"]
     for srcs in bench.GEMM_SOURCES.values():
         for s in srcs:
             assert os.path.exists(os.path.join(bench.CSRC, s)), s

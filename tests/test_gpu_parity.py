@@ -304,6 +304,35 @@ def test_q4k_few_token_ring(kq):
             assert kq.kq_dispatch_count(v) == before + 1
 
 
+def test_q6k_few_token_ring(kq):
+    """The K-split Q6_K ring kernel (past the matrix-vector kernel, up to 64
+    tokens): products in full against the oracle for every token-tile build
+    (16, 32, 64 rows) and K-part count.  On 256 CUs, 14344 weight rows take
+    two K-parts (225 workgroups of 64 rows, the last with 8), 8192 rows four
+    and 4008 rows eight (four at 64 rows; the last workgroup ragged).  K =
+    2304 and 3584 (9 and 14 superblocks): tails after whole ring turns, steps
+    and whole K-parts past the end, blocks at both 4-byte phases.  Then the
+    FFN-down shape itself at 16 tokens."""
+    name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q6_K, M, N, K))
+    v = kq.kq_select_variant(Q6_K, 16, 4096, 2304)
+    assert kq.kq_variant_name(v) == "gemm_q6_k_ring"
+    for N in (14344, 8192, 4008):
+        for K in (2304, 3584):
+            W = datagen.make_weights(Q6_K, N, K, 6100 + K + N)
+            x = datagen.draw_activations(64, K, 6200 + K)
+            for M in (3, 9, 16, 17, 32, 33, 64):
+                assert name(M, N, K) == "gemm_q6_k_ring"
+                say(f"q6k ring M={M} N={N} K={K}")
+                before = kq.kq_dispatch_count(v)
+                gemm_vs_oracle(kq, Q6_K, W, np.ascontiguousarray(x[:M]), M, N, K,
+                               what=f"q6k ring M={M} N={N} K={K}")
+                assert kq.kq_dispatch_count(v) == before + 1
+    W = datagen.make_weights(Q6_K, 4096, 14336, 6300)
+    x = datagen.draw_activations(16, 14336, 6400)
+    say("q6k ring M=16 N=4096 K=14336")
+    gemm_vs_oracle(kq, Q6_K, W, x, 16, 4096, 14336, what="q6k ring FFN down")
+
+
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 5, 8)),
           TQ: ("gemm_tq_matvec", (1, 2, 3, 5, 8))}
 
@@ -343,9 +372,10 @@ def test_matvec_boundaries(kq):
     say("matvec M=2 N=48 K=14336")
     gemm_vs_oracle(kq, Q4_K, W, x, 2, 48, 14336)
     q6 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q6_K, M, N, K))
-    assert q6(9, 4096, 14336) == "gemm_q6_k_128x128"
-    assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_128x128"  # K not a multiple of 2048
+    assert q6(9, 4096, 14336) == "gemm_q6_k_ring"
+    assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_ring"  # K not a multiple of 2048
     assert q6(8, 4096, 14336) == "gemm_q6_k_matvec"
+    assert q6(65, 4096, 14336) == "gemm_q6_k_128x128"
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
     assert tq(9, 17408, 5120) == "gemm_tq_128x128"        # fewer 128 x 128 tiles than CUs
     assert tq(256, 17408, 5120) == "gemm_tq_128x128_reg"
