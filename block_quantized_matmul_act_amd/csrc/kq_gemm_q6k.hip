@@ -330,27 +330,31 @@ __global__ __launch_bounds__(512, 1) void gemm_q6k_ring_kernel(Args a) {
 
 }  // namespace q6r
 
-// Token counts this kernel takes: past the matrix-vector kernel, up to 64.
+// Token counts this kernel takes: past the matrix-vector kernel (up to 4
+// tokens), up to 64.
 bool q6k_ring_choice(int M, int N, int K) {
     return M >= 1 && M <= 64 && N >= 1 && K >= 256 && K % 256 == 0 && !gemv_choice(2, M, N, K);
 }
 
-// K-parts: one workgroup per CU at a time, so the time goes as the rounds of
-// workgroups over the CUs times each one's share of K; the fewest parts
-// among the best, within what the token tile's LDS allows (64 rows: at most
-// four)
-int q6k_ring_parts(int M, int N) {
+// K-parts: one workgroup runs per CU at a time, each costing a fixed part
+// (filling the rings, the reduction: about 4.5 us) plus its waves' share of
+// K (about 0.0085-0.010 us per K value at 16-64 tokens), so the time goes as
+// rounds * (512 + K / parts) in units of K.  The fewest parts among the
+// best, within what the token tile's LDS allows (64 rows: at most four).
+// Measured at 16 tokens, K = 4096, us for 2 / 4 / 8 parts: 4096 rows 21.4 /
+// 14.1 / 9.3; 8192 rows 22.0 / 14.9 / 17.1; 11008 rows 22.4 / 27.0 / 24.5;
+// 14336 rows 23.0 / 27.5 / 31.8; 28672 rows 44.2 / 53.1 / 55.4.
+int q6k_ring_parts(int M, int N, int K) {
     const int cus = num_cus();
     const int kmax = M > 32 ? 4 : 8;
     int best = 2;
-    int64_t best_num = 0, best_den = 1;  // rounds / parts as a fraction
+    int64_t best_cost = 0;
     for (int kp = 2; kp <= kmax; kp *= 2) {
         const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp));
-        const int64_t rounds = (wgs + cus - 1) / cus;
-        if (kp == 2 || rounds * best_den < best_num * kp) {
+        const int64_t cost = (wgs + cus - 1) / cus * (512 + K / kp);
+        if (kp == 2 || cost < best_cost) {
             best = kp;
-            best_num = rounds;
-            best_den = kp;
+            best_cost = cost;
         }
     }
     return best;
@@ -374,7 +378,7 @@ hipError_t launch_gemm_q6k_ring(const void *W, const int8_t *qs, const float *da
     a.N = N;
     a.K = K;
     a.nsb = K / 256;
-    const int kp = q6k_ring_parts(M, N);
+    const int kp = q6k_ring_parts(M, N, K);
     if (M <= 16) {
         if (kp == 2) launch_q6r<16, 2>(a, stream);
         else if (kp == 4) launch_q6r<16, 4>(a, stream);

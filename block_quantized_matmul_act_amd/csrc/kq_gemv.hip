@@ -382,14 +382,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
 
 static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
-// Which Q6_K / ternary shapes the matrix-vector kernels take: up to 8 tokens,
-// K a multiple of 2048 (Q6_K) or 1024 (ternary), so that a row is a whole
-// number of load instructions, and the staged activations within the LDS
-// budget.
+// Which Q6_K / ternary shapes the matrix-vector kernels take: up to 4 (Q6_K)
+// or 8 (ternary) tokens, K a multiple of 2048 (Q6_K) or 1024 (ternary), so
+// that a row is a whole number of load instructions, and the staged
+// activations within the LDS budget.  From 5 tokens the Q6_K ring kernel of
+// kq_gemm_q6k.hip is faster (4096 x 14336: 20.3 against 28.0 us at 5 tokens,
+// 20.7 against 29.0 at 8; at 4 tokens 16.5 against 20.1 us for this kernel).
 bool gemv_choice(int fmt, int M, int N, int K) {
     (void)N;
     if (M < 1 || M > 8) return false;
-    if (fmt == 2) return K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    if (fmt == 2) return M <= 4 && K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     if (fmt == 3) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     return false;
 }
@@ -419,19 +421,16 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
     }
     const dim3 grid((unsigned)((N + gv::RPG - 1) / gv::RPG));
     const size_t lds = (size_t)gv::lds_bytes(mt, M, K);
-    // two groups of loads in flight per row for four or eight tokens once a
-    // row has three or more groups (4096 x 14336: 16.7 against 17.7 us at 4
-    // tokens, 29.0 against 31.6 at 8; at one and two tokens one group in
-    // flight is faster, 12.8 against 14.5 us)
+    // two groups of loads in flight per row for four tokens once a row has
+    // three or more groups (4096 x 14336: 16.7 against 17.7 us; at one and
+    // two tokens one group in flight is faster, 12.8 against 14.5 us)
     if (K / 2048 >= 3 && mt >= 4) {
-        if (mt == 4) hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 2>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((gv::gemv_q6k_kernel<8, 2>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 2>), grid, block, lds, stream, a);
     } else {
         switch (mt) {
             case 1: hipLaunchKernelGGL((gv::gemv_q6k_kernel<1, 1>), grid, block, lds, stream, a); break;
             case 2: hipLaunchKernelGGL((gv::gemv_q6k_kernel<2, 1>), grid, block, lds, stream, a); break;
-            case 4: hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 1>), grid, block, lds, stream, a); break;
-            default: hipLaunchKernelGGL((gv::gemv_q6k_kernel<8, 1>), grid, block, lds, stream, a); break;
+            default: hipLaunchKernelGGL((gv::gemv_q6k_kernel<4, 1>), grid, block, lds, stream, a); break;
         }
     }
     return hipGetLastError();

@@ -37,7 +37,7 @@ hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da,
 // Q6_K products of up to 64 tokens past the matrix-vector kernel (and K a
 // multiple of 256): the K-split ring kernel of kq_gemm_q6k.hip.
 bool q6k_ring_choice(int M, int N, int K);
-int q6k_ring_parts(int M, int N);
+int q6k_ring_parts(int M, int N, int K);
 hipError_t launch_gemm_q6k_ring(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
                                 int K, hipStream_t stream);
 

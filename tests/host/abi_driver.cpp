@@ -62,7 +62,7 @@ hipError_t launch_subsums(int, const void *, const int8_t *, int32_t *, int, int
     ++rs.calls;
     return hipSuccess;
 }
-bool gemv_choice(int, int M, int, int) { return M <= 8; }
+bool gemv_choice(int fmt, int M, int, int) { return M <= (fmt == 2 ? 4 : 8); }
 hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
@@ -70,7 +70,7 @@ bool tq_tile_choice(int M, int, int K) { return M > 8 && K % 256 == 0; }
 hipError_t launch_gemm_tq_tile(const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
-bool q6k_ring_choice(int M, int, int K) { return M >= 1 && M <= 64 && K >= 256 && !(M <= 8 && K % 2048 == 0); }
+bool q6k_ring_choice(int M, int N, int K) { return M >= 1 && M <= 64 && K >= 256 && !gemv_choice(2, M, N, K); }
 int num_cus() { return 256; }
 int q4k_kernel_choice(int M, int, int) {
     return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;

@@ -187,14 +187,15 @@ def test_variants_and_counters(kq):
     assert q4(16, 8192, 4096) == "gemm_q4_k_m16"
     assert q4(64, 10880, 4096) == "gemm_q4_k_m64_ring"
     assert q4(3, 14336, 4096) == "gemm_q4_k_m64_ring"
-    # Q6_K: the matrix-vector kernel up to 8 tokens (K a multiple of 2048),
+    # Q6_K: the matrix-vector kernel up to 4 tokens (K a multiple of 2048),
     # the K-split ring kernel past it up to 64, the tile kernel above
     q6 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_Q6_K, M, N, K))
-    assert q6(8, 4096, 14336) == "gemm_q6_k_matvec"
+    assert q6(4, 4096, 14336) == "gemm_q6_k_matvec"
+    assert q6(5, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(9, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(64, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(65, 4096, 14336) == "gemm_q6_k_128x128"
-    assert q6(8, 4096, 14336 + 256) == "gemm_q6_k_ring"  # K not a multiple of 2048
+    assert q6(4, 4096, 14336 + 256) == "gemm_q6_k_ring"  # K not a multiple of 2048
     assert q6(1, 100, 256) == "gemm_q6_k_ring"
     # base-3 ternary: the register-unpack tile kernel when K is a multiple of
     # 256, the digit-plane tile kernel otherwise

@@ -209,12 +209,13 @@ Q6K_CASES = [
     ("gemm_q6_k_128x128", 70, 96, 512),
     ("gemm_q6_k_128x128", 130, 260, 256),
     ("gemm_q6_k_matvec", 1, 72, 2048),
-    ("gemm_q6_k_matvec", 8, 72, 2048),
+    ("gemm_q6_k_matvec", 4, 72, 2048),
     # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts
     # (72 rows), four (4104 rows and 64 tokens' 200 rows) and two (14344
     # rows); K-parts with no superblock; one to four superblocks
     ("gemm_q6_k_ring", 3, 72, 256),
     ("gemm_q6_k_ring", 9, 72, 512),
+    ("gemm_q6_k_ring", 5, 72, 2048),
     ("gemm_q6_k_ring", 20, 4104, 1024),
     ("gemm_q6_k_ring", 33, 200, 768),
     ("gemm_q6_k_ring", 16, 14344, 512),

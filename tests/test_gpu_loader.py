@@ -222,7 +222,7 @@ IDENTITY_CASES = [
     (Q4_K, 2048, "gemm_q4_k_64x128_k2", 2048, 72),
     (Q4_K, 2048, "gemm_q4_k_64x128", 2048, 1100),
     (Q4_K, 2048, "gemm_q4_k_128x128", 2048, 2100),
-    (Q6_K, 2048, "gemm_q6_k_matvec", 8, 72),
+    (Q6_K, 2048, "gemm_q6_k_matvec", 4, 72),
     (Q6_K, 2048, "gemm_q6_k_ring", 16, 72),
     (Q6_K, 2304, "gemm_q6_k_ring", 64, 4104),
     (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 72),
