@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kq_api.cpp", "kq_quant.hip", "kq_gemm.hip", "kq_gemm_q4k.hip", "kq_gemm_q6k.hip", "kq_gemm_tq.hip", "kq_gemv.hip", "kq_calib.hip"]
+SOURCES = ["kq_api.cpp", "kq_quant.hip", "kq_gemm.hip", "kq_gemm_q4k.hip", "kq_gemm_ring.hip", "kq_gemm_tq.hip", "kq_gemv.hip", "kq_calib.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

@@ -1,0 +1,495 @@
+// kq_gemm_ring.hip -- few-token products (gfx950) for Q6_K and two-bit
+// ternary weights: up to 64 tokens, past the matrix-vector kernels (the tile
+// GEMM of vllm.cpp PR 3036 over Q6_K weights and BlockQ8_K activations, and
+// the ternary MMQ path of llama.cpp PR 214, at the small-batch end of the
+// mul_mat_q / mat-vec crossover).
+//
+// The 128 x 128 tile kernel leaves most of the chip idle here: 4096 weight
+// rows are 32 tiles whatever the token count.  This kernel takes all tokens
+// (a 16-, 32- or 64-row token tile, TM) in one workgroup and splits the
+// weights over workgroups by rows and over waves by rows and K:
+//   * A workgroup of 8 waves owns 16 * (8 / KP) weight rows as 16-row strips;
+//     the K-chunks of 256 values are cut into KP contiguous K-parts (KP = 2, 4
+//     or 8), and wave w takes strip w % (8 / KP) over K-part w / (8 / KP).
+//     Narrow weights take more K-parts so that the grid still covers the CUs.
+//   * Step x multiplies chunk pT + x of every K-part p (T = ceil(chunks /
+//     KP)).  A step's activations (values and scales of every K-part, all
+//     token rows) are copied global -> LDS into a ring of L + 1 slots, L
+//     steps ahead; each wave loads its strip's weights for the same step into
+//     a register ring in the same issue.  Vector-memory loads complete in
+//     issue order, so the wait for a step's copies also waits for the weights
+//     issued before them: those of the same step or earlier.
+//   * The loop runs whole ring turns (steps past a part's end read through a
+//     buffer resource with no records: zeros, no memory access), then the
+//     T mod (L + 1) steps left over, which issue nothing.
+//   * The K-parts are summed through LDS at the end, in a fixed order.
+//
+// A chunk is four K-steps of v_mfma_i32_16x16x64_i8: in K-step s, lane group
+// kg (lane / 16) supplies 16 values of its token row (A) and of its weight
+// row (B) in the same K order.  Per format:
+//   * Q6_K (210 bytes per superblock of 256): lane group kg holds the values
+//     128h + 32u + 16(s % 2) + i with h = kg/2, u = 2(kg % 2) + s/2, sub-block
+//     4kg + s: the low (kg even) or high (kg odd) nibbles of ql bytes 64h +
+//     16s + i, bits 4(kg % 2) + 2(s/2) of qh bytes 32h + 16(s % 2) + i, and
+//     scale byte 4kg + s; so a lane reads 64 contiguous ql bytes, 32 qh bytes
+//     and 4 scale bytes per superblock, and its A operand is the 16
+//     activation bytes at 64kg + 16s.  W = sc (q - 32) = 64 h + l is split
+//     into two int8 digits (q6k_digits), two MFMAs per K-step and m-tile, and
+//     the superblock's sum T = 64 acc_h + acc_l is folded once:
+//     out += d_a * d * T.
+//   * Two-bit ternary (34 bytes per block of 128; a chunk is two blocks):
+//     K-steps 2b and 2b + 1 cover block b, lane group kg the values 64(s % 2)
+//     + 16kg + i of it: plane 2(s % 2) + kg/2 of code bytes 16(kg % 2) + i,
+//     so a lane reads 16 code bytes per block; its A operand is the 16
+//     activation bytes at 64s + 16kg.  The trits are int8 operands as they
+//     are (one MFMA per K-step and m-tile), and each block's sum is folded
+//     after its two K-steps with the block's weight and activation scales.
+// Blocks are 2-byte aligned: a lane loads aligned dwords and shifts them into
+// place with v_alignbit; the fp16 weight scales come in 2-byte loads (their
+// aligned dword can pass the buffer's end).
+#include "kq_device.hpp"
+#include "kq_launch.hpp"
+#include "kq_tile.hpp"
+
+namespace kq {
+namespace rk {
+using namespace tl;
+
+enum { F_Q6K = 2, F_TQ2 = 4 };  // the API's format numbers
+constexpr int ROW = 256;         // LDS bytes per staged activation row (one chunk)
+
+struct Args {
+    const uint8_t *W;
+    const int8_t *qs;
+    const float *da;  // [K / (256 / NBLK)][M]
+    float *out;
+    int M, N, K, nch;  // nch: 256-value chunks per row
+};
+
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<F_Q6K> {
+    static constexpr int CB = 210;      // weight bytes per chunk of a row
+    static constexpr int NBLK = 1;      // scale blocks per chunk
+    static constexpr int NDIG = 2;      // int8 digits per weight
+    static constexpr int WLOADS = 10;   // weight load instructions per lane and chunk
+    __device__ static int piece(int s, int kg) { return 4 * kg + s; }
+};
+template <>
+struct Fmt<F_TQ2> {
+    static constexpr int CB = 68;
+    static constexpr int NBLK = 2;
+    static constexpr int NDIG = 1;
+    static constexpr int WLOADS = 6;
+    __device__ static int piece(int s, int kg) { return 4 * s + kg; }
+};
+
+template <int F, int TM, int KP>
+struct Cfg {
+    static_assert(TM == 16 || TM == 32 || TM == 64, "16, 32 or 64 token rows");
+    static_assert(KP == 2 || KP == 4 || KP == 8, "two, four or eight K-parts");
+    using FM = Fmt<F>;
+    static constexpr int MT = TM / 16;            // 16-row m-tiles
+    static constexpr int NS = 8 / KP;             // 16-row strips per workgroup
+    static constexpr int ROWS = 16 * NS;          // weight rows per workgroup
+    static constexpr int ACT = TM * ROW;          // values of one K-part: [row][256], swizzled
+    static constexpr int PART = ACT + 256 * FM::NBLK;  // ... then its scales (64-lane 4-byte copies)
+    static constexpr int SLOT = KP * PART;
+    // steps of lead: three with 16 token rows, two otherwise, one where two
+    // do not fit the LDS
+    static constexpr int L = TM == 16 && 4 * SLOT <= 160 * 1024 ? 3 : (3 * SLOT <= 160 * 1024 ? 2 : 1);
+    static constexpr int S = L + 1;               // LDS slots and weight register sets
+    static constexpr int LDS = S * SLOT;
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static constexpr int NA = ACT / 1024;         // value copies per K-part
+    static constexpr int CPV = NA / NS;           // ... per wave
+    static_assert(CPV * NS == NA, "value copies split evenly over a part's waves");
+    // vector-memory instructions per wave and step: value copies, scale
+    // copies, weight loads
+    static constexpr int LOADS = CPV + FM::NBLK + FM::WLOADS;
+    static_assert(LOADS * (L - 1) < 64, "vmcnt range");
+    // the K-parts' sums through LDS at the end
+    static_assert((KP - 1) * NS * MT * 4 * 64 * 4 <= LDS, "reduction space");
+};
+
+// one chunk of a lane's weights, as loaded
+template <int F>
+struct WRaw;
+template <>
+struct WRaw<F_Q6K> {
+    v4i l0, l1, l2, l3;   // ql: 68 bytes from the aligned start of its 64
+    uint32_t l4;
+    v4i h0, h1;           // qh: 36 bytes from the aligned start of its 32
+    uint32_t h2;
+    v2u sc;               // the dwords holding its 4 scale bytes
+    uint32_t dd;          // d
+};
+template <>
+struct WRaw<F_TQ2> {
+    v4i c[2];             // per block: 20 bytes from the aligned start of its 16 code bytes
+    uint32_t c4[2];
+    uint32_t dd[2];       // per block: d
+};
+
+template <int F, int TM, int KP>
+__global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
+    using C = Cfg<F, TM, KP>;
+    using FM = Fmt<F>;
+    constexpr int MT = C::MT, NS = C::NS, NBLK = FM::NBLK, NDIG = FM::NDIG;
+    constexpr int KSB = 4 / NBLK;  // K-steps per scale block
+    __shared__ __attribute__((aligned(16))) int8_t s_lds[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int strip = w % NS, part = w / NS;
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int M = a.M, N = a.N, K = a.K, nch = a.nch;
+    const int T = (nch + KP - 1) / KP;  // steps
+    const int n0 = blockIdx.x * C::ROWS + 16 * strip;
+    const int rowbytes = nch * FM::CB;
+
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nch * NBLK * M * 4, RSRC_FLAGS);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+    // no records: reads return zero without a memory access (copies and
+    // loads of steps past a part's end, so that every step issues the same)
+    const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
+
+    // ---- copies of step x into slot x % S.  The NS waves of K-part p copy
+    // its values (copy r: rows 4r .. 4r+3; lane l fills piece l%16 of row
+    // 4r + l/16 with piece (l%16) ^ row), CPV copies each, and each copies
+    // the part's scales (lane l: token l; the same bytes to the same place),
+    // so every wave issues the same.  Token rows past M read other rows'
+    // data or zero; their outputs are dropped.
+    int a_vo[C::CPV];
+#pragma unroll
+    for (int i = 0; i < C::CPV; ++i) {
+        const int row = 4 * (C::CPV * strip + i) + (lane >> 4);
+        a_vo[i] = row * K + 16 * ((lane & 15) ^ (row & 15));
+    }
+    auto copies = [&](int x) __attribute__((always_inline)) {
+        int8_t *P = s_lds + (x % C::S) * C::SLOT + part * C::PART;
+        const int ch = part * T + x;
+        const bool real = x < T && ch < nch;
+        const int chr = real ? ch : 0;
+#pragma unroll
+        for (int i = 0; i < C::CPV; ++i)
+            copy16(real ? rs_a : rs_nul, P + (C::CPV * strip + i) * 1024, a_vo[i], chr * ROW);
+#pragma unroll
+        for (int bb = 0; bb < NBLK; ++bb)
+            copy4(real ? rs_d : rs_nul, P + C::ACT + 256 * bb, 4 * lane, (chr * NBLK + bb) * M * 4);
+    };
+    // ---- this lane's weights: row n0 + r16 (row offsets as unsigned: rows
+    // past N may pass 2^31, and the range check drops them)
+    const uint32_t w_row = (uint32_t)(n0 + r16) * (uint32_t)rowbytes;
+    WRaw<F> ring[C::S];
+    auto wload = [&](int x, WRaw<F> &R) __attribute__((always_inline)) {
+        const int ch = part * T + x;
+        const bool real = x < T && ch < nch;
+        const auto rw = real ? rs_w : rs_nul;
+        const uint32_t b = w_row + (uint32_t)((real ? ch : 0) * FM::CB);  // chunk start
+        if constexpr (F == F_Q6K) {
+            // the aligned dword at or below the block start (every field
+            // offset used with it is a multiple of 4)
+            const int b4 = (int)(b & ~3u);
+            const int o_ql = 64 * (kg >> 1), o_qh = 128 + 32 * (kg >> 1), o_sc = 192 + 4 * kg;
+            R.l0 = ld16(rw, b4 + o_ql, 0);
+            R.l1 = ld16(rw, b4 + o_ql + 16, 0);
+            R.l2 = ld16(rw, b4 + o_ql + 32, 0);
+            R.l3 = ld16(rw, b4 + o_ql + 48, 0);
+            R.l4 = ld4(rw, b4 + o_ql + 64, 0);
+            R.h0 = ld16(rw, b4 + o_qh, 0);
+            R.h1 = ld16(rw, b4 + o_qh + 16, 0);
+            R.h2 = ld4(rw, b4 + o_qh + 32, 0);
+            R.sc = ld8(rw, b4 + o_sc, 0);
+            R.dd = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 208, 0, 0);
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int c4 = (int)((b + 34u * bb + 16u * (kg & 1)) & ~3u);
+                R.c[bb] = ld16(rw, c4, 0);
+                R.c4[bb] = ld4(rw, c4 + 16, 0);
+                R.dd[bb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 34 * bb + 32, 0, 0);
+            }
+        }
+    };
+
+    v4f out[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = v4f{};
+    // LDS addresses: K-step s of m-tile t reads row 16t + r16 of this wave's
+    // K-part, piece piece(s, kg) ^ r16; the scales of tokens 4kg .. 4kg+3 of
+    // m-tile t and block bb follow the values
+    uint32_t a_ad[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a_ad[s] = lds_addr(s_lds) + part * C::PART + r16 * ROW + ((FM::piece(s, kg) ^ r16) << 4);
+    const uint32_t d_ad = lds_addr(s_lds) + part * C::PART + C::ACT + 16 * kg;
+
+    auto compute = [&](const WRaw<F> &R, uint32_t so, int ch) __attribute__((always_inline)) {
+        // LDS reads: the scales first, then K-step s (one per m-tile), two
+        // K-steps in flight
+        v4f da[NBLK][MT];
+        v4i av[2][MT];
+        auto rd = [&](int s, v4i(&dst)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                switch (t) {
+                    case 0: dst[t] = lds_read16<0>(a_ad[s] + so); break;
+                    case 1: dst[t] = lds_read16<16 * ROW>(a_ad[s] + so); break;
+                    case 2: dst[t] = lds_read16<32 * ROW>(a_ad[s] + so); break;
+                    default: dst[t] = lds_read16<48 * ROW>(a_ad[s] + so); break;
+                }
+            }
+        };
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int bb = 0; bb < NBLK; ++bb)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                da[bb][t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 256 * bb + 64 * t));
+        rd(0, av[0]);
+        rd(1, av[1]);
+        const uint32_t b = w_row + (uint32_t)(ch * FM::CB);  // chunk start
+        // ---- the chunk's weights, aligned, and the digits of K-step s
+        float dw[NBLK];
+        uint32_t q6l[17], q6h[8], q6s = 0, sh = 0;  // Q6_K
+        uint32_t t2w[2][4];                          // two-bit ternary
+        if constexpr (F == F_Q6K) {
+            // the block's offset past the aligned dword (0 or 2 bytes)
+            sh = 8u * (b & 3u);
+            const uint32_t l[17] = {(uint32_t)R.l0[0], (uint32_t)R.l0[1], (uint32_t)R.l0[2], (uint32_t)R.l0[3],
+                                    (uint32_t)R.l1[0], (uint32_t)R.l1[1], (uint32_t)R.l1[2], (uint32_t)R.l1[3],
+                                    (uint32_t)R.l2[0], (uint32_t)R.l2[1], (uint32_t)R.l2[2], (uint32_t)R.l2[3],
+                                    (uint32_t)R.l3[0], (uint32_t)R.l3[1], (uint32_t)R.l3[2], (uint32_t)R.l3[3],
+                                    R.l4};
+            const uint32_t h[9] = {(uint32_t)R.h0[0], (uint32_t)R.h0[1], (uint32_t)R.h0[2], (uint32_t)R.h0[3],
+                                   (uint32_t)R.h1[0], (uint32_t)R.h1[1], (uint32_t)R.h1[2], (uint32_t)R.h1[3],
+                                   R.h2};
+#pragma unroll
+            for (int e = 0; e < 17; ++e) q6l[e] = l[e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q6h[e] = __builtin_amdgcn_alignbit(h[e + 1], h[e], sh);
+            q6s = __builtin_amdgcn_alignbit(R.sc[1], R.sc[0], sh);
+            dw[0] = f16_bits_to_f32(R.dd);
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const uint32_t s2 = 8u * ((b + 34u * bb) & 3u);  // (16(kg % 2) keeps the phase)
+                const uint32_t c[5] = {(uint32_t)R.c[bb][0], (uint32_t)R.c[bb][1], (uint32_t)R.c[bb][2],
+                                       (uint32_t)R.c[bb][3], R.c4[bb]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t2w[bb][e] = __builtin_amdgcn_alignbit(c[e + 1], c[e], s2);
+                dw[bb] = f16_bits_to_f32(R.dd[bb]);
+            }
+        }
+        auto digits = [&](int s, v4i(&dg)[NDIG]) __attribute__((always_inline)) {
+            if constexpr (F == F_Q6K) {
+                const uint32_t nib_sh = 4u * (uint32_t)(kg & 1);
+                const int sc = (int)(int8_t)(uint8_t)(q6s >> (8 * s));
+                const uint32_t hsh = nib_sh + 2u * (uint32_t)(s >> 1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t l4 =
+                        (__builtin_amdgcn_alignbit(q6l[4 * s + e + 1], q6l[4 * s + e], sh) >> nib_sh) & 0x0F0F0F0Fu;
+                    const uint32_t h2 = (q6h[4 * (s & 1) + e] >> hsh) & 0x03030303u;
+                    uint32_t dh, dl;
+                    q6k_digits(l4 | (h2 << 4), sc, dh, dl);
+                    dg[0][e] = (int)dh;
+                    dg[NDIG - 1][e] = (int)dl;
+                }
+            } else {
+                // code c = t + 1 in plane 2(s % 2) + kg/2; t bytewise without
+                // borrows: (c | 0x80) - 1, bit 7 flipped back
+                const uint32_t psh = 2u * (uint32_t)(2 * (s & 1) + (kg >> 1));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t code = (t2w[s >> 1][e] >> psh) & 0x03030303u;
+                    dg[0][e] = (int)(((code | 0x80808080u) - 0x01010101u) ^ 0x80808080u);
+                }
+            }
+        };
+        v4i acc[NDIG][MT];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i dg[NDIG];
+            digits(s, dg);
+            // reads in flight behind m-tile t of K-step s: the rest of this
+            // K-step's, then the next K-step's (none after K-step 3)
+            v4i(&cur)[MT] = av[s & 1];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) lds_wait_n(MT - 1 - t + (s < 3 ? MT : 0), cur[t]);
+            const bool first = s % KSB == 0;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int d = 0; d < NDIG; ++d) acc[d][t] = mma16_i8(cur[t], dg[d], first ? v4i{} : acc[d][t]);
+            if (s < 2) rd(s + 2, av[s & 1]);
+            if (s % KSB == KSB - 1) {
+                // fold of block bb: out += d_a[m] * d[n] * T, T = 64 acc_h +
+                // acc_l (Q6_K) or acc (ternary).  Its scales were read before
+                // every K-step's values, all of which are in by K-step 1's wait
+                // but the last two K-steps' (2 MT)
+                const int bb = s / KSB;
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    lds_wait_n(s < 3 ? 2 * MT : 0, da[bb][t]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int Tq = NDIG == 2 ? (acc[0][t][i] << 6) + acc[NDIG - 1][t][i] : acc[0][t][i];
+                        out[t][i] = fmaf((float)Tq * dw[bb], da[bb][t][i], out[t][i]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // step x: the copies and loads of step x + L go out once every wave is
+    // past step x - 1 (their slot's last reader), then step x multiplies
+    auto step = [&](auto KK, int x) __attribute__((always_inline)) {
+        constexpr int k = decltype(KK)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (C::L - 1)>();
+        barrier_nofence();
+        copies(x + C::L);
+        wload(x + C::L, ring[(k + C::L) % C::S]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ch = part * T + x;
+        if (x < T && ch < nch) compute(ring[k], (uint32_t)(k * C::SLOT), ch);  // uniform
+    };
+#pragma unroll
+    for (int x = 0; x < C::L; ++x) {
+        copies(x);
+        wload(x, ring[x]);
+    }
+    // whole ring turns, then the T mod S steps left over, which issue
+    // nothing: in tail step j the loads of steps x .. nfull - 1 + L are
+    // outstanding, L - j steps' worth, and step x's are the oldest
+    const int nfull = T / C::S * C::S;
+    for (int x0 = 0; x0 < nfull; x0 += C::S)
+        static_for<0, C::S>([&](auto KK) KQ_INLINE { step(KK, x0 + decltype(KK)::value); });
+    auto tail_step = [&](auto JJ) KQ_INLINE {
+        constexpr int j = decltype(JJ)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<C::LOADS * (C::L - 1 - j)>();
+        barrier_nofence();
+        __builtin_amdgcn_sched_barrier(0);
+        const int ch = part * T + nfull + j;
+        if (ch < nch) compute(ring[j], (uint32_t)(j * C::SLOT), ch);  // uniform
+    };
+    const int rem = T - nfull;
+    static_for<1, C::S>([&](auto RR) KQ_INLINE {
+        if (rem == decltype(RR)::value) static_for<0, decltype(RR)::value>(tail_step);
+    });
+    // the copies and loads past the end (reading nothing) drain; then the
+    // other parts' sums go through LDS to part 0's waves, added in part order
+    wait_vmcnt<0>();
+    barrier_nofence();
+    float *red = reinterpret_cast<float *>(s_lds);
+    if (part > 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[((((part - 1) * NS + strip) * MT + t) * 4 + i) * 64 + lane] = out[t][i];
+    }
+    barrier_nofence();
+    if (part == 0) {
+        // rows past M fall outside the resource; columns past N are sent out
+        // of range
+        const int n = n0 + r16;
+        const int voff = n < N ? (4 * kg * N + n) * 4 : OOB_VOFF;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            v4f sum = out[t];
+#pragma unroll
+            for (int p = 1; p < KP; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum[i] += red[((((p - 1) * NS + strip) * MT + t) * 4 + i) * 64 + lane];
+            const v4i bits = __builtin_bit_cast(v4i, sum);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(bits[i], rs_o, voff, (16 * t + i) * N * 4, 0);
+        }
+    }
+}
+
+}  // namespace rk
+
+// Shapes this kernel takes: Q6_K past the matrix-vector kernel (up to 4
+// tokens) and two-bit ternary from one token, up to 64 tokens, K a multiple
+// of 256.
+bool ring_choice(int fmt, int M, int N, int K) {
+    if (fmt != rk::F_Q6K && fmt != rk::F_TQ2) return false;
+    if (M < 1 || M > 64 || N < 1 || K < 256 || K % 256 != 0) return false;
+    return fmt != rk::F_Q6K || !gemv_choice(fmt, M, N, K);
+}
+
+// K-parts: one workgroup runs per CU at a time, each costing a fixed part
+// (filling the rings, the reduction: about 4.5 us) plus its waves' share of
+// K (about 0.0085-0.010 us per K value at 16-64 tokens), so the time goes as
+// rounds * (512 + K / parts) in units of K.  The fewest parts among the
+// best, within what the token tile's LDS allows (64 rows: at most four).
+// Measured (Q6_K) at 16 tokens, K = 4096, us for 2 / 4 / 8 parts: 4096 rows
+// 21.4 / 14.1 / 9.3; 8192 rows 22.0 / 14.9 / 17.1; 11008 rows 22.4 / 27.0 /
+// 24.5; 14336 rows 23.0 / 27.5 / 31.8; 28672 rows 44.2 / 53.1 / 55.4.
+int ring_parts(int M, int N, int K) {
+    const int cus = num_cus();
+    const int kmax = M > 32 ? 4 : 8;
+    int best = 2;
+    int64_t best_cost = 0;
+    for (int kp = 2; kp <= kmax; kp *= 2) {
+        const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp));
+        const int64_t cost = (wgs + cus - 1) / cus * (512 + K / kp);
+        if (kp == 2 || cost < best_cost) {
+            best = kp;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+template <int F, int TM, int KP>
+static void launch_rk(const rk::Args &a, hipStream_t stream) {
+    constexpr int R = rk::Cfg<F, TM, KP>::ROWS;
+    hipLaunchKernelGGL((rk::gemm_ring_kernel<F, TM, KP>), dim3((unsigned)((a.N + R - 1) / R)), dim3(512), 0,
+                       stream, a);
+}
+
+template <int F>
+static void launch_rk_fmt(const rk::Args &a, int kp, hipStream_t stream) {
+    if (a.M <= 16) {
+        if (kp == 2) launch_rk<F, 16, 2>(a, stream);
+        else if (kp == 4) launch_rk<F, 16, 4>(a, stream);
+        else launch_rk<F, 16, 8>(a, stream);
+    } else if (a.M <= 32) {
+        if (kp == 2) launch_rk<F, 32, 2>(a, stream);
+        else if (kp == 4) launch_rk<F, 32, 4>(a, stream);
+        else launch_rk<F, 32, 8>(a, stream);
+    } else {
+        if (kp == 2) launch_rk<F, 64, 2>(a, stream);
+        else launch_rk<F, 64, 4>(a, stream);
+    }
+}
+
+hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
+                            int K, hipStream_t stream) {
+    rk::Args a;
+    a.W = static_cast<const uint8_t *>(W);
+    a.qs = qs;
+    a.da = da;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.nch = K / 256;
+    const int kp = ring_parts(M, N, K);
+    if (fmt == rk::F_Q6K) launch_rk_fmt<rk::F_Q6K>(a, kp, stream);
+    else launch_rk_fmt<rk::F_TQ2>(a, kp, stream);
+    return hipGetLastError();
+}
+
+}  // namespace kq

@@ -386,7 +386,7 @@ static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 // or 8 (ternary) tokens, K a multiple of 2048 (Q6_K) or 1024 (ternary), so
 // that a row is a whole number of load instructions, and the staged
 // activations within the LDS budget.  From 5 tokens the Q6_K ring kernel of
-// kq_gemm_q6k.hip is faster (4096 x 14336: 20.3 against 28.0 us at 5 tokens,
+// kq_gemm_ring.hip is faster (4096 x 14336: 20.3 against 28.0 us at 5 tokens,
 // 20.7 against 29.0 at 8; at 4 tokens 16.5 against 20.1 us for this kernel).
 bool gemv_choice(int fmt, int M, int N, int K) {
     (void)N;

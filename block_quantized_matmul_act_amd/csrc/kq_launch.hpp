@@ -34,12 +34,13 @@ bool tq_tile_choice(int M, int N, int K);
 hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
                                int K, hipStream_t stream);
 
-// Q6_K products of up to 64 tokens past the matrix-vector kernel (and K a
-// multiple of 256): the K-split ring kernel of kq_gemm_q6k.hip.
-bool q6k_ring_choice(int M, int N, int K);
-int q6k_ring_parts(int M, int N, int K);
-hipError_t launch_gemm_q6k_ring(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
-                                int K, hipStream_t stream);
+// Q6_K products of up to 64 tokens past the matrix-vector kernel, and
+// two-bit ternary products of up to 64 tokens (K a multiple of 256): the
+// K-split ring kernel of kq_gemm_ring.hip (fmt: the API's format number).
+bool ring_choice(int fmt, int M, int N, int K);
+int ring_parts(int M, int N, int K);
+hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
+                            int K, hipStream_t stream);
 
 // Compute units of the current device (cached per device; persistent grids
 // are sized from it).

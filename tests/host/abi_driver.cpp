@@ -70,7 +70,9 @@ bool tq_tile_choice(int M, int, int K) { return M > 8 && K % 256 == 0; }
 hipError_t launch_gemm_tq_tile(const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
-bool q6k_ring_choice(int M, int N, int K) { return M >= 1 && M <= 64 && K >= 256 && !gemv_choice(2, M, N, K); }
+bool ring_choice(int fmt, int M, int N, int K) {
+    return (fmt == 2 || fmt == 4) && M >= 1 && M <= 64 && K >= 256 && K % 256 == 0 && !gemv_choice(fmt, M, N, K);
+}
 int num_cus() { return 256; }
 int q4k_kernel_choice(int M, int, int) {
     return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;

@@ -202,9 +202,14 @@ def test_variants_and_counters(kq):
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ, M, N, K))
     assert tq(2048, 17408, 5120) == "gemm_tq_128x128_reg"
     assert tq(2048, 17408, 5248) == "gemm_tq_128x128"
-    # two-bit ternary always runs on the tile kernel
-    for M in (1, 8, 2048):
-        assert kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, 4096, 5120)) == "gemm_tq2_128x128"
+    # two-bit ternary: the K-split ring kernel up to 64 tokens (K a multiple
+    # of 256), the tile kernel otherwise
+    tq2 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, N, K))
+    for M in (1, 8, 64):
+        assert tq2(M, 4096, 5120) == "gemm_tq2_ring"
+    assert tq2(65, 4096, 5120) == "gemm_tq2_128x128"
+    assert tq2(2048, 4096, 5120) == "gemm_tq2_128x128"
+    assert tq2(8, 4096, 5120 + 128) == "gemm_tq2_128x128"
     assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT
     assert kq.kq_select_variant(kq.KQ_Q4_K, 1, 1, 100) == kq.KQ_ERR_SHAPE
 

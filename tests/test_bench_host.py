@@ -29,12 +29,15 @@ def test_kernel_source_hash_covers_each_format():
     hashes = {f: bench.kernel_source_hash(f) for f in bench.GEMM_SOURCES}
     for h in hashes.values():
         assert re.fullmatch(r"[0-9a-f]{16}", h)
-    # every format has its own set: the generic tile kernel plus, for Q6_K,
-    # its few-token ring kernel, for base-3 ternary its register-unpack tile
+    # every format has its own set: the generic tile kernel plus, for Q6_K
+    # and two-bit ternary, the few-token ring kernel (and for Q6_K its
+    # matrix-vector kernel), for base-3 ternary its register-unpack tile
     # kernel; Q4_K its own kernels
     assert len(set(hashes.values())) == len(hashes)
     assert "kq_gemm_tq.hip" in bench.GEMM_SOURCES["tq"] and "kq_tile.hpp" in bench.GEMM_SOURCES["q4_k"]
-    assert "kq_gemm_q6k.hip" in bench.GEMM_SOURCES["q6_k"] and "kq_gemm_q6k.hip" not in bench.GEMM_SOURCES["tq2"]
+    for f in ("q6_k", "tq2"):
+        assert "kq_gemm_ring.hip" in bench.GEMM_SOURCES[f]
+    assert "kq_gemv.hip" in bench.GEMM_SOURCES["q6_k"] and "kq_gemv.hip" not in bench.GEMM_SOURCES["tq2"]
     for srcs in bench.GEMM_SOURCES.values():
         for s in srcs:
             assert os.path.exists(os.path.join(bench.CSRC, s)), s

@@ -256,7 +256,14 @@ TQ_CASES = [
     ("gemm_tq_matvec", TQ, 1, 40, 1024),
     ("gemm_tq_matvec", TQ, 8, 40, 1024),
     ("gemm_tq2_128x128", TQ2, 67, 90, 640),
-    ("gemm_tq2_128x128", TQ2, 5, 40, 1024),
+    ("gemm_tq2_128x128", TQ2, 5, 40, 1152),
+    # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts
+    # (40 and 72 rows), four (4104 rows; 64 tokens' 200), two (14344 rows)
+    ("gemm_tq2_ring", TQ2, 1, 40, 256),
+    ("gemm_tq2_ring", TQ2, 5, 72, 1024),
+    ("gemm_tq2_ring", TQ2, 20, 4104, 768),
+    ("gemm_tq2_ring", TQ2, 64, 200, 512),
+    ("gemm_tq2_ring", TQ2, 16, 14344, 512),
 ]
 
 

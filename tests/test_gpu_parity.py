@@ -222,7 +222,7 @@ def test_shape_sweep(kq, fmt):
 
 
 @pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_1", "ffn_up_q4k_64", "ffn_up_q4k_2048",
-                                  "ffn_down_q6k_1", "tern_5120_1",
+                                  "ffn_down_q6k_1", "ffn_down_q6k_16", "tern_5120_1",
                                   "ffn_down_q6k_2048", "tern_5120_2048"])
 def test_workload_full_size_sampled(kq, workloads, name):
     """Full-size problem in the benchmarked launch; the oracle checks a sample
@@ -331,6 +331,27 @@ def test_q6k_few_token_ring(kq):
     x = datagen.draw_activations(16, 14336, 6400)
     say("q6k ring M=16 N=4096 K=14336")
     gemm_vs_oracle(kq, Q6_K, W, x, 16, 4096, 14336, what="q6k ring FFN down")
+
+
+def test_tq2_few_token_ring(kq):
+    """The K-split ring kernel for two-bit ternary (1 to 64 tokens, K a
+    multiple of 256): every token-tile build and K-part count as in the Q6_K
+    test (14344, 8192 and 4008 weight rows), K = 2304 and 3584 (9 and 14
+    chunks of two blocks), blocks at both 4-byte phases."""
+    name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ2, M, N, K))
+    v = kq.kq_select_variant(TQ2, 16, 4096, 2304)
+    assert kq.kq_variant_name(v) == "gemm_tq2_ring"
+    for N in (14344, 8192, 4008):
+        for K in (2304, 3584):
+            W = datagen.make_weights(TQ2, N, K, 7100 + K + N)
+            x = datagen.draw_activations(64, K, 7200 + K)
+            for M in (1, 3, 16, 17, 32, 33, 64):
+                assert name(M, N, K) == "gemm_tq2_ring"
+                say(f"tq2 ring M={M} N={N} K={K}")
+                before = kq.kq_dispatch_count(v)
+                gemm_vs_oracle(kq, TQ2, W, np.ascontiguousarray(x[:M]), M, N, K,
+                               what=f"tq2 ring M={M} N={N} K={K}")
+                assert kq.kq_dispatch_count(v) == before + 1
 
 
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 4)),
