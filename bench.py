@@ -64,7 +64,8 @@ CSRC = os.path.join(ROOT, "block_quantized_matmul_act_amd", "csrc")
 GEMM_SOURCES = {
     "q4_k": ("kq_gemm_q4k.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
     "q6_k": ("kq_gemm.hip", "kq_gemm_ring.hip", "kq_gemv.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
-    "tq": ("kq_gemm.hip", "kq_gemm_tq.hip", "kq_gemv.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
+    "tq": ("kq_gemm.hip", "kq_gemm_tq.hip", "kq_gemm_ring.hip", "kq_gemv.hip", "kq_tile.hpp", "kq_device.hpp",
+           "kq_launch.hpp"),
     "tq2": ("kq_gemm.hip", "kq_gemm_ring.hip", "kq_tile.hpp", "kq_device.hpp", "kq_launch.hpp"),
     # expert-indexed workloads: the gather mode of the Q4_K tile kernel
     # (kq_gemm_q4k.hip) or of the other formats' tile kernel (kq_gemm.hip)

@@ -1447,8 +1447,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     // loads of steps past the end, so that every step issues the same)
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
 
+    // (the stores complete before the first step's barrier, which carries no
+    // fence)
     int8_t *const zero = s_lds + C::S * C::SLOT;
     for (int i = tid; i < RING_ZERO / 4; i += 512) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     // ---- copies of step x into slot x % S.  Wave w copies for its own
     // K-half kh: value copies CPV*(w%4) .. +CPV-1 (copy r: rows 4r .. 4r+3;

@@ -1,5 +1,5 @@
-// kq_gemm_ring.hip -- few-token products (gfx950) for Q6_K and two-bit
-// ternary weights: up to 64 tokens, past the matrix-vector kernels (the tile
+// kq_gemm_ring.hip -- few-token products (gfx950) for Q6_K and ternary
+// weights: up to 64 tokens, past the matrix-vector kernels (the tile
 // GEMM of vllm.cpp PR 3036 over Q6_K weights and BlockQ8_K activations, and
 // the ternary MMQ path of llama.cpp PR 214, at the small-batch end of the
 // mul_mat_q / mat-vec crossover).
@@ -37,6 +37,14 @@
 //     into two int8 digits (q6k_digits), two MFMAs per K-step and m-tile, and
 //     the superblock's sum T = 64 acc_h + acc_l is folded once:
 //     out += d_a * d * T.
+//   * Base-3 ternary (28 bytes per block of 128, 4-byte aligned; a chunk is
+//     two blocks): K-steps 2b and 2b + 1 cover block b, lane group kg the
+//     trits 32kg + 16(s % 2) + i of it, which lie in 4 bytes starting at byte
+//     (32kg + 16(s % 2)) / 5, digit (32kg + 16(s % 2)) mod 5; a lane loads the
+//     3 dwords that hold both its windows.  Each byte goes through a 256-entry
+//     LDS table (its five trits as int8), the four 5-trit groups are packed
+//     into 20 bytes and the 16 wanted taken from the digit offset.  The A
+//     operand is the 16 activation bytes at 128b + 32kg + 16(s % 2).
 //   * Two-bit ternary (34 bytes per block of 128; a chunk is two blocks):
 //     K-steps 2b and 2b + 1 cover block b, lane group kg the values 64(s % 2)
 //     + 16kg + i of it: plane 2(s % 2) + kg/2 of code bytes 16(kg % 2) + i,
@@ -55,7 +63,7 @@ namespace kq {
 namespace rk {
 using namespace tl;
 
-enum { F_Q6K = 2, F_TQ2 = 4 };  // the API's format numbers
+enum { F_Q6K = 2, F_TQ = 3, F_TQ2 = 4 };  // the API's format numbers
 constexpr int ROW = 256;         // LDS bytes per staged activation row (one chunk)
 
 struct Args {
@@ -75,6 +83,14 @@ struct Fmt<F_Q6K> {
     static constexpr int NDIG = 2;      // int8 digits per weight
     static constexpr int WLOADS = 10;   // weight load instructions per lane and chunk
     __device__ static int piece(int s, int kg) { return 4 * kg + s; }
+};
+template <>
+struct Fmt<F_TQ> {
+    static constexpr int CB = 56;
+    static constexpr int NBLK = 2;
+    static constexpr int NDIG = 1;
+    static constexpr int WLOADS = 6;
+    __device__ static int piece(int s, int kg) { return 8 * (s >> 1) + (s & 1) + 2 * kg; }
 };
 template <>
 struct Fmt<F_TQ2> {
@@ -98,9 +114,10 @@ struct Cfg {
     static constexpr int SLOT = KP * PART;
     // steps of lead: three with 16 token rows, two otherwise, one where two
     // do not fit the LDS
-    static constexpr int L = TM == 16 && 4 * SLOT <= 160 * 1024 ? 3 : (3 * SLOT <= 160 * 1024 ? 2 : 1);
+    static constexpr int L = TM == 16 && 4 * SLOT <= 158 * 1024 ? 3 : (3 * SLOT <= 158 * 1024 ? 2 : 1);
     static constexpr int S = L + 1;               // LDS slots and weight register sets
-    static constexpr int LDS = S * SLOT;
+    static constexpr int LUT = F == F_TQ ? 256 * 8 : 0;  // base-3 decode table, after the slots
+    static constexpr int LDS = S * SLOT + LUT;
     static_assert(LDS <= 160 * 1024, "LDS");
     static constexpr int NA = ACT / 1024;         // value copies per K-part
     static constexpr int CPV = NA / NS;           // ... per wave
@@ -124,6 +141,12 @@ struct WRaw<F_Q6K> {
     uint32_t h2;
     v2u sc;               // the dwords holding its 4 scale bytes
     uint32_t dd;          // d
+};
+template <>
+struct WRaw<F_TQ> {
+    v2u w01[2];           // per block: the 3 dwords holding its trit windows
+    uint32_t w2[2];
+    uint32_t dd[2];       // per block: d
 };
 template <>
 struct WRaw<F_TQ2> {
@@ -156,6 +179,20 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     // no records: reads return zero without a memory access (copies and
     // loads of steps past a part's end, so that every step issues the same)
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
+
+    // base-3 decode table: entry v = the five trits of byte v (t0..t3 in the
+    // low word, t4 in the high word); the stores complete before the first
+    // step's barrier (which carries no fence), so every wave sees them after
+    uint32_t *const lut = reinterpret_cast<uint32_t *>(s_lds + C::S * C::SLOT);
+    if constexpr (F == F_TQ) {
+        if (tid < 256) {
+            uint32_t lo, hi;
+            tq_lut_entry((uint32_t)tid, lo, hi);
+            lut[2 * tid] = lo;
+            lut[2 * tid + 1] = hi;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 
     // ---- copies of step x into slot x % S.  The NS waves of K-part p copy
     // its values (copy r: rows 4r .. 4r+3; lane l fills piece l%16 of row
@@ -205,6 +242,15 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
             R.h2 = ld4(rw, b4 + o_qh + 32, 0);
             R.sc = ld8(rw, b4 + o_sc, 0);
             R.dd = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 208, 0, 0);
+        } else if constexpr (F == F_TQ) {
+            // dwords kg? {0, 1, 3, 4} .. +2 of each block
+            const int o3 = kg == 0 ? 0 : kg == 1 ? 4 : kg == 2 ? 12 : 16;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                R.w01[bb] = ld8(rw, (int)b + 28 * bb + o3, 0);
+                R.w2[bb] = ld4(rw, (int)b + 28 * bb + o3 + 8, 0);
+                R.dd[bb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 28 * bb + 26, 0, 0);
+            }
         } else {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
@@ -227,6 +273,18 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     for (int s = 0; s < 4; ++s)
         a_ad[s] = lds_addr(s_lds) + part * C::PART + r16 * ROW + ((FM::piece(s, kg) ^ r16) << 4);
     const uint32_t d_ad = lds_addr(s_lds) + part * C::PART + C::ACT + 16 * kg;
+    // base-3: per half h of a block, the window's first byte as (dword q,
+    // byte shift) within the lane's 3 dwords, and its first digit o
+    uint32_t tq_q[2], tq_sh[2], tq_o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int k0 = 32 * kg + 16 * h;
+        const int r = k0 / 5 - (kg == 0 ? 0 : kg == 1 ? 4 : kg == 2 ? 12 : 16);
+        tq_q[h] = (uint32_t)(r >> 2);
+        tq_sh[h] = (uint32_t)(r & 3);
+        tq_o[h] = (uint32_t)(k0 % 5);
+    }
+    const uint32_t lut_ad = lds_addr(lut);
 
     auto compute = [&](const WRaw<F> &R, uint32_t so, int ch) __attribute__((always_inline)) {
         // LDS reads: the scales first, then K-step s (one per m-tile), two
@@ -250,6 +308,43 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 da[bb][t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 256 * bb + 64 * t));
+        // base-3: the trits of all four K-steps through the decode table,
+        // waited for before the values are read
+        v4i tq_b[4];
+        if constexpr (F == F_TQ) {
+            v2u e[4][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int bb = s >> 1, h = s & 1;
+                const uint32_t w0 = R.w01[bb][0], w1 = R.w01[bb][1], w2 = R.w2[bb];
+                const uint32_t x = __builtin_amdgcn_alignbyte(tq_q[h] ? w2 : w1, tq_q[h] ? w1 : w0, tq_sh[h]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e[s][i] = lds_read8<0>(lut_ad + 8u * ((x >> (8 * i)) & 0xFFu));
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lds_wait_n(15 - 4 * s - i, e[s][i]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // 20 trits in order: D0 = t0..3, D1 = t4..7, ..., D4 = t16..19
+                uint32_t D[5];
+                D[0] = e[s][0].x;
+                D[1] = perm_b32(e[s][1].x, e[s][0].y, 0x06050400u);
+                D[2] = __builtin_amdgcn_alignbyte(e[s][1].y, e[s][1].x, 3) | (e[s][2].x << 16);
+                D[3] = __builtin_amdgcn_alignbyte(e[s][2].y, e[s][2].x, 2) | (e[s][3].x << 24);
+                D[4] = __builtin_amdgcn_alignbyte(e[s][3].y, e[s][3].x, 1);
+                // the 16 from digit o on (o = 4: one dword on)
+                const uint32_t o = tq_o[s & 1];
+                const bool o4 = o >= 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = o4 ? D[j + 1] : D[j];
+                    const uint32_t hi = o4 ? D[j + 2 < 5 ? j + 2 : 4] : D[j + 1];
+                    tq_b[s][j] = (int)__builtin_amdgcn_alignbyte(hi, lo, o & 3u);
+                }
+            }
+        }
         rd(0, av[0]);
         rd(1, av[1]);
         const uint32_t b = w_row + (uint32_t)(ch * FM::CB);  // chunk start
@@ -274,6 +369,9 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
             for (int e = 0; e < 8; ++e) q6h[e] = __builtin_amdgcn_alignbit(h[e + 1], h[e], sh);
             q6s = __builtin_amdgcn_alignbit(R.sc[1], R.sc[0], sh);
             dw[0] = f16_bits_to_f32(R.dd);
+        } else if constexpr (F == F_TQ) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) dw[bb] = f16_bits_to_f32(R.dd[bb]);
         } else {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
@@ -300,6 +398,9 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
                     dg[0][e] = (int)dh;
                     dg[NDIG - 1][e] = (int)dl;
                 }
+            } else if constexpr (F == F_TQ) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dg[0][e] = tq_b[s][e];
             } else {
                 // code c = t + 1 in plane 2(s % 2) + kg/2; t bytewise without
                 // borrows: (c | 0x80) - 1, bit 7 flipped back
@@ -419,13 +520,13 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 
 }  // namespace rk
 
-// Shapes this kernel takes: Q6_K past the matrix-vector kernel (up to 4
-// tokens) and two-bit ternary from one token, up to 64 tokens, K a multiple
-// of 256.
+// Shapes this kernel takes: Q6_K and base-3 ternary past the matrix-vector
+// kernels, two-bit ternary from one token, up to 64 tokens, K a multiple of
+// 256.
 bool ring_choice(int fmt, int M, int N, int K) {
-    if (fmt != rk::F_Q6K && fmt != rk::F_TQ2) return false;
+    if (fmt != rk::F_Q6K && fmt != rk::F_TQ && fmt != rk::F_TQ2) return false;
     if (M < 1 || M > 64 || N < 1 || K < 256 || K % 256 != 0) return false;
-    return fmt != rk::F_Q6K || !gemv_choice(fmt, M, N, K);
+    return fmt == rk::F_TQ2 || !gemv_choice(fmt, M, N, K);
 }
 
 // K-parts: one workgroup runs per CU at a time, each costing a fixed part
@@ -488,6 +589,7 @@ hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const floa
     a.nch = K / 256;
     const int kp = ring_parts(M, N, K);
     if (fmt == rk::F_Q6K) launch_rk_fmt<rk::F_Q6K>(a, kp, stream);
+    else if (fmt == rk::F_TQ) launch_rk_fmt<rk::F_TQ>(a, kp, stream);
     else launch_rk_fmt<rk::F_TQ2>(a, kp, stream);
     return hipGetLastError();
 }

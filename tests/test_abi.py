@@ -202,6 +202,13 @@ def test_variants_and_counters(kq):
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ, M, N, K))
     assert tq(2048, 17408, 5120) == "gemm_tq_128x128_reg"
     assert tq(2048, 17408, 5248) == "gemm_tq_128x128"
+    # ... and the K-split ring kernel past the matrix-vector kernel up to 64
+    # tokens (K a multiple of 256)
+    assert tq(8, 17408, 5120) == "gemm_tq_matvec"
+    assert tq(9, 17408, 5120) == "gemm_tq_ring"
+    assert tq(64, 17408, 5120) == "gemm_tq_ring"
+    assert tq(1, 17408, 5120 + 256) == "gemm_tq_ring"   # K not a multiple of 1024
+    assert tq(9, 17408, 5120 + 128) == "gemm_tq_128x128"
     # two-bit ternary: the K-split ring kernel up to 64 tokens (K a multiple
     # of 256), the tile kernel otherwise
     tq2 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, N, K))

@@ -255,6 +255,12 @@ TQ_CASES = [
     ("gemm_tq_128x128_reg", TQ, 300, 11000, 512), ("gemm_tq_128x128_reg", TQ, 129, 16500, 256),
     ("gemm_tq_matvec", TQ, 1, 40, 1024),
     ("gemm_tq_matvec", TQ, 8, 40, 1024),
+    # the K-split ring kernel (eight, four and two K-parts)
+    ("gemm_tq_ring", TQ, 9, 40, 1024),
+    ("gemm_tq_ring", TQ, 3, 72, 768),
+    ("gemm_tq_ring", TQ, 20, 4104, 768),
+    ("gemm_tq_ring", TQ, 64, 200, 512),
+    ("gemm_tq_ring", TQ, 16, 14344, 512),
     ("gemm_tq2_128x128", TQ2, 67, 90, 640),
     ("gemm_tq2_128x128", TQ2, 5, 40, 1152),
     # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts

@@ -228,6 +228,8 @@ IDENTITY_CASES = [
     (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 72),
     (TQ, 1024, "gemm_tq_matvec", 8, 72),
     (TQ, 1152, "gemm_tq_128x128", 1152, 72),
+    (TQ, 1024, "gemm_tq_ring", 16, 72),
+    (TQ, 1280, "gemm_tq_ring", 64, 4104),
     (TQ, 1024, "gemm_tq_128x128_reg", 1024, 4200),
     (TQ2, 1152, "gemm_tq2_128x128", 8, 72),
     (TQ2, 1024, "gemm_tq2_ring", 8, 72),

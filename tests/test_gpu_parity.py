@@ -333,6 +333,29 @@ def test_q6k_few_token_ring(kq):
     gemm_vs_oracle(kq, Q6_K, W, x, 16, 4096, 14336, what="q6k ring FFN down")
 
 
+def test_tq_few_token_ring(kq):
+    """The K-split ring kernel for base-3 ternary (past the matrix-vector
+    kernel, up to 64 tokens, K a multiple of 256): every token-tile build and
+    K-part count (14344, 8192 and 4008 weight rows), K = 2304 and 3584; with
+    K = 2304 the matrix-vector kernel declines even one token."""
+    name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
+    v = kq.kq_select_variant(TQ, 16, 4096, 2304)
+    assert kq.kq_variant_name(v) == "gemm_tq_ring"
+    for N in (14344, 8192, 4008):
+        for K in (2304, 3584):
+            W = datagen.make_weights(TQ, N, K, 8100 + K + N)
+            x = datagen.draw_activations(64, K, 8200 + K)
+            for M in (1, 3, 16, 17, 32, 33, 64):
+                if name(M, N, K) != "gemm_tq_ring":
+                    assert M <= 8 and K % 1024 == 0
+                    continue
+                say(f"tq ring M={M} N={N} K={K}")
+                before = kq.kq_dispatch_count(v)
+                gemm_vs_oracle(kq, TQ, W, np.ascontiguousarray(x[:M]), M, N, K,
+                               what=f"tq ring M={M} N={N} K={K}")
+                assert kq.kq_dispatch_count(v) == before + 1
+
+
 def test_tq2_few_token_ring(kq):
     """The K-split ring kernel for two-bit ternary (1 to 64 tokens, K a
     multiple of 256): every token-tile build and K-part count as in the Q6_K
@@ -398,7 +421,8 @@ def test_matvec_boundaries(kq):
     assert q6(4, 4096, 14336) == "gemm_q6_k_matvec"
     assert q6(65, 4096, 14336) == "gemm_q6_k_128x128"
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
-    assert tq(9, 17408, 5120) == "gemm_tq_128x128"        # fewer 128 x 128 tiles than CUs
+    assert tq(9, 17408, 5120) == "gemm_tq_ring"           # past the matrix-vector kernel
+    assert tq(65, 17408, 5120) == "gemm_tq_128x128"       # fewer 128 x 128 tiles than CUs
     assert tq(256, 17408, 5120) == "gemm_tq_128x128_reg"
     assert tq(8, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024 (nor of 256)
     assert tq(8, 17408, 5120) == "gemm_tq_matvec"
