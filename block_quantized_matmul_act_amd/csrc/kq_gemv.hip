@@ -380,18 +380,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
 
 }  // namespace gv
 
-static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
-// Which Q6_K / ternary shapes the matrix-vector kernels take: up to 4 (Q6_K)
-// or 8 (ternary) tokens, K a multiple of 2048 (Q6_K) or 1024 (ternary), so
-// that a row is a whole number of load instructions, and the staged
-// activations within the LDS budget.  From 5 tokens the Q6_K ring kernel of
-// kq_gemm_ring.hip is faster (4096 x 14336: 20.3 against 28.0 us at 5 tokens,
-// 20.7 against 29.0 at 8; at 4 tokens 16.5 against 20.1 us for this kernel).
+// Which Q6_K / ternary shapes the matrix-vector kernels take: up to 4
+// tokens, K a multiple of 2048 (Q6_K) or 1024 (ternary), so that a row is a
+// whole number of load instructions, and the staged activations within the
+// LDS budget.  From 5 tokens the ring kernel of kq_gemm_ring.hip is faster
+// (Q6_K 4096 x 14336: 20.3 against 28.0 us at 5 tokens, 20.7 against 29.0 at
+// 8, and 16.5 against 20.1 us for this kernel at 4; ternary 17408 x 5120:
+// 18.1 against 27.9 us at 5 tokens, 13.3 against 18.0 for this kernel at 4).
 bool gemv_choice(int fmt, int M, int N, int K) {
     (void)N;
-    if (M < 1 || M > 8) return false;
-    if (fmt == 2) return M <= 4 && K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    if (M < 1 || M > 4) return false;
+    if (fmt == 2) return K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     if (fmt == 3) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     return false;
 }
@@ -414,8 +415,7 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
         switch (mt) {
             case 1: hipLaunchKernelGGL(gv::gemv_tq_kernel<1>, grid, block, lds, stream, a); break;
             case 2: hipLaunchKernelGGL(gv::gemv_tq_kernel<2>, grid, block, lds, stream, a); break;
-            case 4: hipLaunchKernelGGL(gv::gemv_tq_kernel<4>, grid, block, lds, stream, a); break;
-            default: hipLaunchKernelGGL(gv::gemv_tq_kernel<8>, grid, block, lds, stream, a); break;
+            default: hipLaunchKernelGGL(gv::gemv_tq_kernel<4>, grid, block, lds, stream, a); break;
         }
         return hipGetLastError();
     }

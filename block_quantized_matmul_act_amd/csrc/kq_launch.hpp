@@ -28,8 +28,9 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
 // shapes of at most 256 such tiles) 64 x 128.
 // The 64-row tile also has an 8-wave build (one workgroup per CU, two
 // superblocks per step) for tile counts that balance better over CUs.
-// Ternary (base-3) products with K a multiple of 256 that the matrix-vector
-// kernel does not take run on the register-unpack tile kernel (kq_gemm_tq.hip).
+// Ternary (base-3) products with K a multiple of 256 that neither the
+// matrix-vector kernel nor the ring kernel (below) takes run on the
+// register-unpack tile kernel (kq_gemm_tq.hip).
 bool tq_tile_choice(int M, int N, int K);
 hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
                                int K, hipStream_t stream);

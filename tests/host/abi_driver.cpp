@@ -62,7 +62,7 @@ hipError_t launch_subsums(int, const void *, const int8_t *, int32_t *, int, int
     ++rs.calls;
     return hipSuccess;
 }
-bool gemv_choice(int fmt, int M, int, int) { return M <= (fmt == 2 ? 4 : 8); }
+bool gemv_choice(int fmt, int M, int, int) { return (fmt == 2 || fmt == 3) && M <= 4; }
 hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }

@@ -204,7 +204,8 @@ def test_variants_and_counters(kq):
     assert tq(2048, 17408, 5248) == "gemm_tq_128x128"
     # ... and the K-split ring kernel past the matrix-vector kernel up to 64
     # tokens (K a multiple of 256)
-    assert tq(8, 17408, 5120) == "gemm_tq_matvec"
+    assert tq(4, 17408, 5120) == "gemm_tq_matvec"
+    assert tq(5, 17408, 5120) == "gemm_tq_ring"
     assert tq(9, 17408, 5120) == "gemm_tq_ring"
     assert tq(64, 17408, 5120) == "gemm_tq_ring"
     assert tq(1, 17408, 5120 + 256) == "gemm_tq_ring"   # K not a multiple of 1024

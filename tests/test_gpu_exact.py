@@ -254,7 +254,7 @@ TQ_CASES = [
     ("gemm_tq_128x128", TQ, 67, 90, 640),
     ("gemm_tq_128x128_reg", TQ, 300, 11000, 512), ("gemm_tq_128x128_reg", TQ, 129, 16500, 256),
     ("gemm_tq_matvec", TQ, 1, 40, 1024),
-    ("gemm_tq_matvec", TQ, 8, 40, 1024),
+    ("gemm_tq_matvec", TQ, 4, 40, 1024),
     # the K-split ring kernel (eight, four and two K-parts)
     ("gemm_tq_ring", TQ, 9, 40, 1024),
     ("gemm_tq_ring", TQ, 3, 72, 768),

@@ -226,7 +226,7 @@ IDENTITY_CASES = [
     (Q6_K, 2048, "gemm_q6_k_ring", 16, 72),
     (Q6_K, 2304, "gemm_q6_k_ring", 64, 4104),
     (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 72),
-    (TQ, 1024, "gemm_tq_matvec", 8, 72),
+    (TQ, 1024, "gemm_tq_matvec", 4, 72),
     (TQ, 1152, "gemm_tq_128x128", 1152, 72),
     (TQ, 1024, "gemm_tq_ring", 16, 72),
     (TQ, 1280, "gemm_tq_ring", 64, 4104),

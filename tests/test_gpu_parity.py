@@ -347,7 +347,7 @@ def test_tq_few_token_ring(kq):
             x = datagen.draw_activations(64, K, 8200 + K)
             for M in (1, 3, 16, 17, 32, 33, 64):
                 if name(M, N, K) != "gemm_tq_ring":
-                    assert M <= 8 and K % 1024 == 0
+                    assert M <= 4 and K % 1024 == 0
                     continue
                 say(f"tq ring M={M} N={N} K={K}")
                 before = kq.kq_dispatch_count(v)
@@ -378,7 +378,7 @@ def test_tq2_few_token_ring(kq):
 
 
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 4)),
-          TQ: ("gemm_tq_matvec", (1, 2, 3, 5, 8))}
+          TQ: ("gemm_tq_matvec", (1, 2, 3, 4))}
 
 
 @pytest.mark.parametrize("fmt", sorted(MATVEC))
@@ -424,12 +424,13 @@ def test_matvec_boundaries(kq):
     assert tq(9, 17408, 5120) == "gemm_tq_ring"           # past the matrix-vector kernel
     assert tq(65, 17408, 5120) == "gemm_tq_128x128"       # fewer 128 x 128 tiles than CUs
     assert tq(256, 17408, 5120) == "gemm_tq_128x128_reg"
-    assert tq(8, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024 (nor of 256)
-    assert tq(8, 17408, 5120) == "gemm_tq_matvec"
+    assert tq(4, 17408, 5120 + 128) == "gemm_tq_128x128"  # K not a multiple of 1024 (nor of 256)
+    assert tq(4, 17408, 5120) == "gemm_tq_matvec"
+    assert tq(5, 17408, 5120) == "gemm_tq_ring"
     Wt = datagen.make_weights(TQ, 40, 5120, 4646)
-    xt = datagen.draw_activations(8, 5120, 4747)
-    say("matvec ternary M=8 N=40 K=5120")
-    gemm_vs_oracle(kq, TQ, Wt, xt, 8, 40, 5120)
+    xt = datagen.draw_activations(4, 5120, 4747)
+    say("matvec ternary M=4 N=40 K=5120")
+    gemm_vs_oracle(kq, TQ, Wt, xt, 4, 40, 5120)
     W6 = datagen.make_weights(Q6_K, 40, 14336, 4444)
     x6 = datagen.draw_activations(4, 14336, 4545)
     say("matvec Q6_K M=4 N=40 K=14336")
