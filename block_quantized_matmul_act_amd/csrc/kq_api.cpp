@@ -18,7 +18,6 @@ namespace {
 enum Variant {
     V_QUANT_Q8K = 0,
     V_QUANT_Q8_128,
-    V_GEMM_Q4K_M64,
     V_GEMM_Q4K_128x128,
     V_GEMM_Q4K_MATVEC,
     V_GEMM_Q6K_128x128,
@@ -40,15 +39,16 @@ enum Variant {
     V_GEMM_Q6K_RING,
     V_GEMM_TQ2_RING,
     V_GEMM_TQ_RING,
+    V_GEMM_Q4K_RING_KP,
     V_COUNT
 };
 
 const char *const kVariantNames[V_COUNT] = {
-    "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_m64", "gemm_q4_k_128x128", "gemm_q4_k_matvec",
+    "quant_q8_k",        "quant_q8_128",    "gemm_q4_k_128x128", "gemm_q4_k_matvec",
     "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
     "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",   "gemm_id_128x128", "gemm_q4_k_64x128",
     "gemm_id_q4_k_64x128", "gemm_q4_k_64x128_k2", "gemm_q4_k_m16", "gemm_tq_128x128_reg", "gemm_q4_k_m64_ring",
-    "gemm_q6_k_ring", "gemm_tq2_ring", "gemm_tq_ring",
+    "gemm_q6_k_ring", "gemm_tq2_ring", "gemm_tq_ring", "gemm_q4_k_ring_kp",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -125,8 +125,8 @@ int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
     if (fmt == KQ_Q4_K) {
         switch (kq::q4k_kernel_choice((int)M, (int)N, (int)K)) {
             case kq::Q4K_MATVEC: return V_GEMM_Q4K_MATVEC;
-            case kq::Q4K_FEW_TOKENS: return V_GEMM_Q4K_M64;
             case kq::Q4K_FEW_RING: return V_GEMM_Q4K_M64_RING;
+            case kq::Q4K_RING_KP: return V_GEMM_Q4K_RING_KP;
             case kq::Q4K_TILE64: return V_GEMM_Q4K_64x128;
             case kq::Q4K_TILE64_K2: return V_GEMM_Q4K_64x128_K2;
             case kq::Q4K_FEW_SPLIT: return V_GEMM_Q4K_M16;

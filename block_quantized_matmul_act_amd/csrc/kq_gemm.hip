@@ -1212,7 +1212,7 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
                        hipStream_t stream) {
     if (fmt == FMT_Q4K) return launch_gemm_q4k(W, qs, da, alpha, out, M, N, K, stream);
     if (gemv_choice(fmt, M, N, K)) return launch_gemv(fmt, W, qs, da, out, M, N, K, stream);
-    if (ring_choice(fmt, M, N, K)) return launch_gemm_ring(fmt, W, qs, da, out, M, N, K, stream);
+    if (ring_choice(fmt, M, N, K)) return launch_gemm_ring(fmt, W, qs, da, nullptr, out, M, N, K, stream);
     if (fmt == FMT_TQ && tq_tile_choice(M, N, K)) return launch_gemm_tq_tile(W, qs, da, out, M, N, K, stream);
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);

@@ -537,344 +537,12 @@ __global__ __launch_bounds__(NT * KS, KS == 1 ? TileCfg<BM>::WG_PER_CU : 1) void
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (M <= 64): the product is bound by streaming the weights from
-// HBM, so the work is cut along N and K instead of M.  A workgroup owns 32
-// weight rows and runs 2 independent waves, wave h taking superblock half h
-// for all token rows: SMT 32-row m-tiles (2 for M <= 64, so each weight
-// nibble is unpacked once for both; 1 for M <= 32).  Two (SMT = 2) or three
-// (SMT = 1) workgroups share a CU.
-// Each wave stages its own operands through LDS in half-superblocks (128
-// values), with coalesced buffer -> LDS copies (consecutive lanes read
-// consecutive bytes of a row, so a copy touches a handful of cache lines
-// instead of one per lane).  Activations (4 KiB per m-tile; the second half
-// also brings the superblock's scales and min-term operands) and weights
-// (the 64 nibble bytes of the half and the 16-byte headers of 32 blocks)
-// sit in separate rings, the weights staged further ahead.  Both scale
-// digits are multiplied as soon as a fragment arrives, into two int32 planes
-// combined at the superblock's end.  No barrier is needed until the two
-// K-halves are summed in LDS.
-//
-// K-step s (0..3) of half H uses nibble half n = s/2 of chunk pair cp = s%2:
-// lane group g holds weight chunk c = 2cp + g (nibble bytes 64H + 16c ..
-// +16), i.e. values k = 128H + 64cp + 32n + 16g + i, all of sub-block
-// j = 4H + 2cp + n; the activation fragment is the same 16 values of the
-// lane's row, piece p = 4cp + 2n + g of the half-row.
-// ---------------------------------------------------------------------------
-constexpr int SKH = 2;                      // K-split: superblock halves (one wave each)
-constexpr int SWN = 32 * 64;                // half the nibble bytes of 32 blocks
-constexpr int SHD = 32 * 16;                // block headers of 32 rows
-constexpr int SDS = 64 * 4;                 // activation scales of 64 rows
-constexpr int SLS = 2 * 64 * 16;            // min-term operands (hi, lo) of 64 rows
-// staging depths (half-superblocks ahead) of the few-token kernel: at 64
-// tokens the kernel is bound by its VALU work and depth makes no difference;
-// at up to 32 tokens weights six halves ahead beat four (12.6 vs 14.5 us for
-// 8 x 14336 x 4096)
-#ifndef Q4S_DA1
-#define Q4S_DA1 1
-#endif
-#ifndef Q4S_DW1
-#define Q4S_DW1 6
-#endif
-#ifndef Q4S_DA2
-#define Q4S_DA2 1
-#endif
-#ifndef Q4S_DW2
-#define Q4S_DW2 4
-#endif
-// SMT 32-token m-tiles (1: M <= 32, 2: M <= 64); activations are staged DA
-// half-superblocks ahead (they come from L2), weights DW > DA ahead (they
-// stream from HBM), in rings of DA + 1 and DW + 1 slots.
-template <int SMT, int DA, int DW>
-struct SmallCfg {
-    static_assert(DW > DA && DA >= 1, "weights must run ahead of activations");
-    static constexpr int SA = 32 * SMT * 128;                   // half-row activations
-    static constexpr int SAS = SA + SDS + SLS;                   // activation slot (+ scales)
-    static constexpr int SWS = SWN + SHD;                        // weight slot (+ headers)
-    static constexpr int LDS = (DA + 1) * SAS + (DW + 1) * SWS;  // per wave
-    static constexpr int WG_PER_CU = 163840 / (SKH * LDS);       // workgroups sharing a CU's LDS
-    // copies of an activation stage (second halves add the scales) and of a
-    // weight stage (first halves add the headers)
-    static constexpr int szA(int H) { return 4 * SMT + 3 * H; }
-    static constexpr int szW(int H) { return 2 + 2 * (1 - H); }
-    // Copies that may still be in flight when half j (parity H) starts: each
-    // half i issues activation stage i + DA, then weight stage i + DW.  The
-    // newest copies half j needs are activation stage j's (issued at half
-    // j - DA); after them came weight stage j - DA + DW and all copies of
-    // halves j - DA + 1 .. j - 1.
-    static constexpr int in_flight(int H) {
-        int n = szW((H - DA + DW) & 1);
-        for (int d = 1; d < DA; ++d) n += szA((H + d) & 1) + szW((H - DA + d + DW) & 1);
-        return n;
-    }
-};
-
-template <int SMT, int DA, int DW>
-__global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void gemm_q4k_small_kernel(Args a) {
-    using C = SmallCfg<SMT, DA, DW>;
-    constexpr int SA = C::SA, SAS = C::SAS, SWS = C::SWS;
-    __shared__ __attribute__((aligned(16))) int8_t s_lds[SKH][C::LDS];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ln = lane & 31, g = lane >> 5;
-    const int M = a.M, N = a.N, K = a.K, nsb = a.nsb;
-    const int n0 = blockIdx.x * 32;
-    const int rowbytes = nsb * BB;
-    const int sb0 = h * nsb / SKH, sb1 = (h + 1) * nsb / SKH;
-    const int nk = sb1 - sb0;
-
-    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
-    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nsb * M * 4, RSRC_FLAGS);
-    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nsb * 2 * M * 16, RSRC_FLAGS);
-    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
-    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
-
-    // Activation copy i (1 KiB) covers rows 8i .. 8i+7 (128 bytes each);
-    // lane l fills position l%8 of row 8i + l/8 with piece
-    // (l%8) ^ ((row/2) % 8) = ((l%8) ^ (l/16)) ^ 4(i%2): the i-dependent part
-    // is an XOR of 64*(i%2) on the byte offset.  The reads below are then free
-    // of bank conflicts.
-    const int a_vb = (lane >> 3) * K + 16 * ((lane & 7) ^ (lane >> 4));
-    // Nibble copy i: piece f = 64i + l is piece f%4 of row f/4 (64 bytes per
-    // row); header copy i: dword e = 64i + l is dword e%4 of row e/4.
-    // (unsigned: rows past N in the last strip may pass 2^31; the buffer
-    // range check drops them)
-    const uint32_t wr0 = (uint32_t)(n0 + (lane >> 2)) * (uint32_t)rowbytes;
-    const uint32_t wr1 = wr0 + 16u * (uint32_t)rowbytes;
-    const int w_vb0 = (int)(wr0 + 16 + 16 * (lane & 3));
-    const int w_vb1 = (int)(wr1 + 16 + 16 * (lane & 3));
-    const int h_vb0 = (int)(wr0 + 4 * (lane & 3));
-    const int h_vb1 = (int)(wr1 + 4 * (lane & 3));
-
-    int8_t *const myA = &s_lds[h][0];                    // activation ring
-    int8_t *const myW = &s_lds[h][(DA + 1) * SAS];       // weight ring
-    // Stage x: superblock sb0 + x/2 (clamped: past the end re-reads the last,
-    // unused), half x%2.  The copies are pinned between compiler memory
-    // barriers: the LDS reads are asm statements the compiler does not see as
-    // memory accesses, so without them a copy into a slot could be moved
-    // above the last reads of that slot.
-    auto issueA = [&](int x) __attribute__((always_inline)) {
-        asm volatile("" ::: "memory");
-        const int H = x & 1;
-        const int sb = sb0 + min(x >> 1, nk - 1);
-        int8_t *S = myA + (x % (DA + 1)) * SAS;
-#pragma unroll
-        for (int i = 0; i < 4 * SMT; ++i)
-            copy16(rs_a, S + 1024 * i, a_vb ^ (64 * (i & 1)), 8 * i * K + sb * ROW + 128 * H);
-        if (H == 1) {
-            // scales of rows 0..63 (lane = row) and min operands (lane = row)
-            copy4(rs_d, S + SA, 4 * lane, sb * M * 4);
-            copy16(rs_l, S + SA + SDS, 16 * lane, sb * 2 * M * 16);
-            copy16(rs_l, S + SA + SDS + 1024, 16 * lane, (sb * 2 + 1) * M * 16);
-        }
-        asm volatile("" ::: "memory");
-    };
-    auto issueW = [&](int x) __attribute__((always_inline)) {
-        asm volatile("" ::: "memory");
-        const int H = x & 1;
-        const int sb = sb0 + min(x >> 1, nk - 1);
-        int8_t *S = myW + (x % (DW + 1)) * SWS;
-        copy16(rs_w, S, w_vb0, sb * BB + 64 * H);
-        copy16(rs_w, S + 1024, w_vb1, sb * BB + 64 * H);
-        if (H == 0) {
-            copy4(rs_w, S + SWN, h_vb0, sb * BB);
-            copy4(rs_w, S + SWN + 256, h_vb1, sb * BB);
-        }
-        asm volatile("" ::: "memory");
-    };
-
-    const int afx = (ln >> 1) & 7;
-    v16f out[SMT];
-#pragma unroll
-    for (int t = 0; t < SMT; ++t) out[t] = v16f{};
-    v16i acc_h[SMT], acc_l[SMT];
-    v4i hdr;
-
-    // one half-superblock: H compile-time, slots runtime
-    auto half = [&](auto HH, int j) __attribute__((always_inline)) {
-        constexpr int H = decltype(HH)::value;
-        const uint32_t S = lds_addr(myA + (j % (DA + 1)) * SAS);
-        const uint32_t SW = lds_addr(myW + (j % (DW + 1)) * SWS);
-        const uint32_t arow = S + 128 * ln;
-        const uint32_t wrow = SW + 64 * ln + 16 * g;
-        if (H == 0) hdr = lds_read16<SWN>(SW + 16 * ln);
-        v4i wq0 = lds_read16<0>(wrow);
-        v4i wq1 = lds_read16<32>(wrow);
-        // fragments in K-step order, tile 0 then tile 1 within a step
-        v4i af[4][SMT];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int p = 4 * (s & 1) + 2 * (s >> 1) + g;
-            const uint32_t ad = arow + 16 * (p ^ afx);
-            af[s][0] = lds_read16<0>(ad);
-            if constexpr (SMT == 2) af[s][1] = lds_read16<32 * 128>(ad);
-        }
-        // reads in flight after each: header, two weight reads, 4*SMT fragments
-        if (H == 0) lds_wait_n(2 + 4 * SMT, hdr);
-        lds_wait_n(1 + 4 * SMT, wq0);
-        lds_wait_n(4 * SMT, wq1);
-        // scale digits of the four sub-blocks of this half
-        const uint32_t w1 = (uint32_t)hdr[1], w2 = (uint32_t)hdr[2];
-        const uint32_t x = H == 0 ? w1 : __builtin_amdgcn_alignbit(w2, w1, 24);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int cp = s & 1, n = s >> 1;
-            const uint32_t sc = (x >> (6 * (2 * cp + n))) & 63u;
-            const v4i &wq = cp ? wq1 : wq0;
-            v4i bh, bl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t q = (uint32_t)wq[e];
-                const uint32_t nib = n ? (q >> 4) & 0x0F0F0F0Fu : q & 0x0F0F0F0Fu;
-                bh[e] = mul_digit(nib, sc >> 3);
-                bl[e] = mul_digit(nib, sc & 7u);
-            }
-#pragma unroll
-            for (int t = 0; t < SMT; ++t) {
-                // reads newer than fragment (s, t): SMT*(3 - s) + (SMT - 1 - t)
-                lds_wait_n(SMT * (3 - s) + (SMT - 1 - t), af[s][t]);
-                if (H == 0 && s == 0) {
-                    acc_h[t] = mma_i8(af[s][t], bh, v16i{});
-                    acc_l[t] = mma_i8(af[s][t], bl, v16i{});
-                } else {
-                    acc_h[t] = mma_i8(af[s][t], bh, acc_h[t]);
-                    acc_l[t] = mma_i8(af[s][t], bl, acc_l[t]);
-                }
-            }
-        }
-        if (H == 1) {
-            // fold: out += d_a[m] * (d[n] * float(8*acc_h + acc_l) - dmin[n] * M)
-            // with M = sum_j m_j B_j exact (one bf16 MFMA per m-tile on the
-            // exact parts of B_j, as in the tile kernel); scales and min
-            // operands from this stage
-            const uint32_t sd = S + SA + 16 * g;
-            const uint32_t sl = S + SA + SDS + 16 * ln + 8 * g;
-            v4f da[SMT][4];
-            v2u ap0[SMT], ap1[SMT];
-            da[0][0] = __builtin_bit_cast(v4f, lds_read16<0>(sd));
-            da[0][1] = __builtin_bit_cast(v4f, lds_read16<32>(sd));
-            da[0][2] = __builtin_bit_cast(v4f, lds_read16<64>(sd));
-            da[0][3] = __builtin_bit_cast(v4f, lds_read16<96>(sd));
-            ap0[0] = lds_read8<0>(sl);
-            ap1[0] = lds_read8<1024>(sl);
-            if constexpr (SMT == 2) {
-                da[SMT - 1][0] = __builtin_bit_cast(v4f, lds_read16<128>(sd));
-                da[SMT - 1][1] = __builtin_bit_cast(v4f, lds_read16<160>(sd));
-                da[SMT - 1][2] = __builtin_bit_cast(v4f, lds_read16<192>(sd));
-                da[SMT - 1][3] = __builtin_bit_cast(v4f, lds_read16<224>(sd));
-                ap0[SMT - 1] = lds_read8<512>(sl);
-                ap1[SMT - 1] = lds_read8<1536>(sl);
-            }
-            // tile 0's six reads are followed by tile 1's six (if any)
-            lds_wait_n(6 * (SMT - 1), da[0][0]);
-            lds_wait_n(6 * (SMT - 1), da[0][1]);
-            lds_wait_n(6 * (SMT - 1), da[0][2]);
-            lds_wait_n(6 * (SMT - 1), da[0][3]);
-            lds_wait_n(6 * (SMT - 1), ap0[0]);
-            lds_wait_n(6 * (SMT - 1), ap1[0]);
-            if constexpr (SMT == 2) {
-                lds_wait<0>(da[SMT - 1][0]);
-                lds_wait<0>(da[SMT - 1][1]);
-                lds_wait<0>(da[SMT - 1][2]);
-                lds_wait<0>(da[SMT - 1][3]);
-                lds_wait<0>(ap0[SMT - 1]);
-                lds_wait<0>(ap1[SMT - 1]);
-            }
-            const float dw = f16_bits_to_f32((uint32_t)hdr[0]);
-            const float ndmin = -f16_bits_to_f32((uint32_t)hdr[0] >> 16);
-            const uint32_t w3 = (uint32_t)hdr[3];
-            const uint64_t hi64 = (uint64_t)w2 | ((uint64_t)w3 << 32);
-            const uint32_t mx = (uint32_t)(hi64 >> (16 + 24 * g));
-            v8bf bm;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const __bf16 m = (__bf16)(float)((mx >> (6 * i)) & 63u);
-                bm[i] = m;
-                bm[4 + i] = m;
-            }
-            v16f mt[SMT];
-#pragma unroll
-            for (int t = 0; t < SMT; ++t) {
-                const v4i avv = {(int)ap0[t].x, (int)ap0[t].y, (int)ap1[t].x, (int)ap1[t].y};
-                mt[t] = mma_bf16(__builtin_bit_cast(v8bf, avv), bm, v16f{});
-            }
-#pragma unroll
-            for (int t = 0; t < SMT; ++t) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * q + i;
-                        const int T = (acc_h[t][r] << 3) + acc_l[t][r];
-                        out[t][r] = fmaf(fmaf((float)T, dw, mt[t][r] * ndmin), da[t][q][i], out[t][r]);
-                    }
-            }
-        }
-    };
-
-    if (nk > 0) {
-        // Every iteration is one superblock (two halves) with no exit, so each
-        // wait below sees the same copies in flight on every pass
-        // (C::in_flight).  The prologue issues what halves -DW .. -1 would
-        // have, so half 0 starts in the same state.  Stages issued past the
-        // end re-read the last superblock and are drained unused.
-#pragma unroll
-        for (int i = -DW; i < 0; ++i) {
-            if (i + DA >= 0) issueA(i + DA);
-            issueW(i + DW);
-        }
-        for (int k = 0; k < nk; ++k) {
-            const int j = 2 * k;
-            wait_vmcnt<C::in_flight(0)>();
-            issueA(j + DA);
-            issueW(j + DW);
-            half(std::integral_constant<int, 0>{}, j);
-            wait_vmcnt<C::in_flight(1)>();
-            issueA(j + 1 + DA);
-            issueW(j + 1 + DW);
-            half(std::integral_constant<int, 1>{}, j + 1);
-        }
-    }
-    // no copy may still be writing this wave's stages
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-
-    // sum the two K-halves in a fixed order: wave 1 parks its sums in its own
-    // (now idle) stages
-    float *const red = reinterpret_cast<float *>(&s_lds[1][0]);
-    if (h == 1) {
-#pragma unroll
-        for (int t = 0; t < SMT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) red[(16 * t + r) * 64 + lane] = out[t][r];
-    }
-    __syncthreads();
-    if (h == 0) {
-        const int n = n0 + ln;
-        const int voff = n < N ? (4 * g * N + n) * 4 : OOB_VOFF;
-#pragma unroll
-        for (int t = 0; t < SMT; ++t) {
-            v16f sum = out[t];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sum[r] += red[(16 * t + r) * 64 + lane];
-            const v16i bits = __builtin_bit_cast(v16i, sum);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * t + 8 * (r >> 2) + (r & 3);  // minus the lane's 4g
-                __builtin_amdgcn_raw_buffer_store_b32(bits[r], rs_o, voff, row * N * 4, 0);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Few tokens, K split over the waves of a workgroup (M <= 16 in use).
 // A workgroup of KW waves owns 32 weight rows; wave w takes superblocks w,
 // w + KW, w + 2KW, ... for every token row (MT 16-row m-tiles), so the waves
 // of a workgroup read neighbouring bytes of the same weight rows.  At the end
 // the KW partial sums are added through LDS in a fixed order.  On 14336 x
-// 4096 weights that is 448 workgroups of 4 waves: two waves on most SIMDs,
-// where the two-wave kernel above leaves at most one.
+// 4096 weights that is 448 workgroups of 4 waves: two waves on most SIMDs.
 // Activation fragments go straight from memory into registers, half a
 // superblock ahead: every workgroup reads the same few token rows, so they
 // come from L2, and staging them in LDS per wave would cap the waves per CU.
@@ -887,7 +555,7 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 // The weights and the fold data (activation scales and min-term operands of
 // a superblock) stream through a small per-wave LDS ring with coalesced
 // buffer -> LDS copies.  No barrier is needed until the final sum.
-// Past 16 tokens the kernel loses to the two-wave kernel: its waves spend
+// Past 16 tokens the kernel loses to the ring kernels below: its waves spend
 // most of their time waiting on memory (the vector-memory counter counts in
 // issue order, so waiting for the next half's activation loads also waits
 // for every weight copy issued before them, and a weight stage gets at most
@@ -904,6 +572,10 @@ __global__ __launch_bounds__(64 * SKH, (SmallCfg<SMT, DA, DW>::WG_PER_CU)) void 
 // group) those are the low (kg < 2) or high (kg >= 2) nibbles of bytes 32s +
 // 16(kg % 2) + i: piece 2(s % 2) + kg % 2 of the 64 nibble bytes of half s/2.
 // ---------------------------------------------------------------------------
+constexpr int SWN = 32 * 64;    // half the nibble bytes of 32 blocks
+constexpr int SHD = 32 * 16;    // block headers of 32 rows
+constexpr int SDS = 64 * 4;     // activation scales of 64 rows
+constexpr int SLS = 2 * 64 * 16;  // min-term operands (hi, lo) of 64 rows
 constexpr int KWS = SWN + SHD;  // weight stage: nibbles of one half of 32 blocks, their headers
 constexpr int KFS = SDS + SLS;  // fold data of one superblock: scales and min-term parts of 64 rows
 
@@ -1716,11 +1388,9 @@ int num_cus() {
 static int mv_tokens(int M) { return M <= 1 ? 1 : 2; }
 constexpr int MV_LDS_BUDGET = 40 * 1024;  // four workgroups (16 waves) per CU
 
-// Which Q4_K kernel a shape gets: a handful of tokens -> the matrix-vector
-// kernel; up to 16 -> the four-wave K-split kernel; up to 64 -> the two-wave
-// few-token kernel (measured on 14336 x 4096 weights: 11.6 / 12.2 / 13.4 us
-// against 14.1 / 14.3 / 14.4 us at 4 / 8 / 16 tokens, but 17.5 and 26.6 us
-// against 15.1 and 19.0 us at 32 and 64 tokens); otherwise the
+// Which Q4_K kernel a shape gets: one or two tokens -> the matrix-vector
+// kernel; up to 64 -> a ring kernel or, on mid-width weights up to 16
+// tokens, the four-wave K-split kernel (the rules below); otherwise the
 // persistent tile kernel (two workgroups per CU), 128 x 128 when that tiling
 // has more tiles than the chip has CUs (256), else 64 x 128: below that the
 // taller tile leaves CUs idle, above it the shorter tile's extra unpacking
@@ -1748,17 +1418,25 @@ int q4k_kernel_choice(int M, int N, int K) {
         return Q4K_MATVEC;
     const int cus = num_cus();
     // The K-split ring kernel (one 64-row workgroup per CU) once the 32-row
-    // workgroups of the split and two-wave kernels would need a second round
-    // on some CUs: those kernels jump by a quarter to a half there, and the
-    // ring kernel wins from that point on.  K = 4096, us, ring against the
+    // workgroups of the split and (former) two-wave kernels would need a
+    // second round on some CUs: those kernels jump by a quarter to a half
+    // there, and the ring kernel wins from that point on.  K = 4096, us, ring against the
     // other: 9216 rows 10.0 / 11.0 at 3 tokens, 10.8 / 13.0 at 16, 11.6 /
     // 14.6 at 32, 15.6 / 17.7 at 64; 14336 rows 11.2 / 13.6 at 16, 16.5 /
     // 19.9 at 64; K = 2048 and 8192 alike (8448-10240 rows: 5-25% faster).
     // At 8192 rows (one round) the other kernels win: 9.8 / 7.5 at 3 tokens,
     // 15.4 / 14.3 at 64.
     if (M <= 64 && (N + 31) / 32 > cus) return Q4K_FEW_RING;
-    if (M <= 16) return Q4K_FEW_SPLIT;
-    if (M <= 64) return Q4K_FEW_TOKENS;
+    // Narrower weights: the four-wave split kernel up to 16 tokens while its
+    // 32-row workgroups cover more than half the CUs, else the ring kernel
+    // with K in 2, 4 or 8 parts (kq_gemm_ring.hip).  Paired runs, us, split
+    // / ring: 8192 x 4096 at 16 tokens 8.1 / 9.2, 5120 x 4096 7.5 / 8.7,
+    // 4096 x 4096 7.3 / 5.8, 4096 x 14336 at 3 tokens 17.1 / 12.1.  From 17
+    // tokens the ring kernel beat the former two-wave kernel at every width
+    // measured (8192 x 4096: 9.2 / 11.1 at 17 tokens, 12.6 / 14.1 at 64;
+    // 4096 x 14336: 18.0 / 31.9 at 32 tokens, 32.2 / 41.3 at 64).
+    if (M <= 16 && 2 * ((N + 31) / 32) > cus) return Q4K_FEW_SPLIT;
+    if (M <= 64) return Q4K_RING_KP;
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
@@ -1853,14 +1531,8 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
             hipLaunchKernelGGL((q4w::gemm_q4k_split_kernel<1, 4, 2>), dim3((unsigned)((N + 31) / 32)), dim3(64 * 4),
                                0, stream, a);
             break;
-        case Q4K_FEW_TOKENS:
-            if (M <= 32)
-                hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<1, Q4S_DA1, Q4S_DW1>),
-                                   dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
-            else
-                hipLaunchKernelGGL((q4w::gemm_q4k_small_kernel<2, Q4S_DA2, Q4S_DW2>),
-                                   dim3((unsigned)((N + 31) / 32)), dim3(64 * q4w::SKH), 0, stream, a);
-            break;
+        case Q4K_RING_KP:
+            return launch_gemm_ring(1, W, qs, da, alpha, out, M, N, K, stream);
         case Q4K_FEW_RING:
             if (M <= 16)
                 hipLaunchKernelGGL(q4w::gemm_q4k_ring_kernel<16>, dim3((unsigned)((N + 63) / 64)), dim3(512), 0,

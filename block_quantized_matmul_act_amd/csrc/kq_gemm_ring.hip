@@ -63,13 +63,14 @@ namespace kq {
 namespace rk {
 using namespace tl;
 
-enum { F_Q6K = 2, F_TQ = 3, F_TQ2 = 4 };  // the API's format numbers
+enum { F_Q4K = 1, F_Q6K = 2, F_TQ = 3, F_TQ2 = 4 };  // the API's format numbers
 constexpr int ROW = 256;         // LDS bytes per staged activation row (one chunk)
 
 struct Args {
     const uint8_t *W;
     const int8_t *qs;
-    const float *da;  // [K / (256 / NBLK)][M]
+    const float *da;        // [K / (256 / NBLK)][M]
+    const uint16_t *alpha;  // Q4_K: [K / 256][2][M][8] bf16, exact parts of the sub-block sums
     float *out;
     int M, N, K, nch;  // nch: 256-value chunks per row
 };
@@ -77,11 +78,21 @@ struct Args {
 template <int F>
 struct Fmt;
 template <>
-struct Fmt<F_Q6K> {
-    static constexpr int CB = 210;      // weight bytes per chunk of a row
+struct Fmt<F_Q4K> {
+    static constexpr int CB = 144;      // weight bytes per chunk of a row
     static constexpr int NBLK = 1;      // scale blocks per chunk
     static constexpr int NDIG = 2;      // int8 digits per weight
-    static constexpr int WLOADS = 10;   // weight load instructions per lane and chunk
+    static constexpr int SHIFT = 3;     // T = (digit-0 sum << SHIFT) + digit-1 sum
+    static constexpr int WLOADS = 3;    // weight load instructions per lane and chunk
+    __device__ static int piece(int s, int kg) { return 4 * kg + s; }
+};
+template <>
+struct Fmt<F_Q6K> {
+    static constexpr int CB = 210;
+    static constexpr int NBLK = 1;
+    static constexpr int NDIG = 2;
+    static constexpr int SHIFT = 6;
+    static constexpr int WLOADS = 10;
     __device__ static int piece(int s, int kg) { return 4 * kg + s; }
 };
 template <>
@@ -89,6 +100,7 @@ struct Fmt<F_TQ> {
     static constexpr int CB = 56;
     static constexpr int NBLK = 2;
     static constexpr int NDIG = 1;
+    static constexpr int SHIFT = 0;
     static constexpr int WLOADS = 6;
     __device__ static int piece(int s, int kg) { return 8 * (s >> 1) + (s & 1) + 2 * kg; }
 };
@@ -97,6 +109,7 @@ struct Fmt<F_TQ2> {
     static constexpr int CB = 68;
     static constexpr int NBLK = 2;
     static constexpr int NDIG = 1;
+    static constexpr int SHIFT = 0;
     static constexpr int WLOADS = 6;
     __device__ static int piece(int s, int kg) { return 4 * s + kg; }
 };
@@ -110,21 +123,27 @@ struct Cfg {
     static constexpr int NS = 8 / KP;             // 16-row strips per workgroup
     static constexpr int ROWS = 16 * NS;          // weight rows per workgroup
     static constexpr int ACT = TM * ROW;          // values of one K-part: [row][256], swizzled
-    static constexpr int PART = ACT + 256 * FM::NBLK;  // ... then its scales (64-lane 4-byte copies)
+    // Q4_K min-term operands of one K-part: [hi, lo][TM][16] in 1 KiB copies
+    static constexpr int NAL = F == F_Q4K ? (TM == 64 ? 2 : 1) : 0;
+    static constexpr int ALO = ACT + 256 * FM::NBLK;   // ... after the scales (64-lane 4-byte copies)
+    static constexpr int PART = ALO + 1024 * NAL;
     static constexpr int SLOT = KP * PART;
+    // after the slots: the base-3 decode table, or the zeros lanes of
+    // k-groups 2 and 3 read as their Q4_K min-term operand
+    static constexpr int EXTRA = F == F_TQ ? 256 * 8 : F == F_Q4K ? 1024 : 0;
+    static constexpr int LDS_MAX = 160 * 1024;
     // steps of lead: three with 16 token rows, two otherwise, one where two
     // do not fit the LDS
-    static constexpr int L = TM == 16 && 4 * SLOT <= 158 * 1024 ? 3 : (3 * SLOT <= 158 * 1024 ? 2 : 1);
+    static constexpr int L = TM == 16 && 4 * SLOT + EXTRA <= LDS_MAX ? 3 : (3 * SLOT + EXTRA <= LDS_MAX ? 2 : 1);
     static constexpr int S = L + 1;               // LDS slots and weight register sets
-    static constexpr int LUT = F == F_TQ ? 256 * 8 : 0;  // base-3 decode table, after the slots
-    static constexpr int LDS = S * SLOT + LUT;
+    static constexpr int LDS = S * SLOT + EXTRA;
     static_assert(LDS <= 160 * 1024, "LDS");
     static constexpr int NA = ACT / 1024;         // value copies per K-part
     static constexpr int CPV = NA / NS;           // ... per wave
     static_assert(CPV * NS == NA, "value copies split evenly over a part's waves");
     // vector-memory instructions per wave and step: value copies, scale
-    // copies, weight loads
-    static constexpr int LOADS = CPV + FM::NBLK + FM::WLOADS;
+    // copies, min-term operand copies, weight loads
+    static constexpr int LOADS = CPV + FM::NBLK + NAL + FM::WLOADS;
     static_assert(LOADS * (L - 1) < 64, "vmcnt range");
     // the K-parts' sums through LDS at the end
     static_assert((KP - 1) * NS * MT * 4 * 64 * 4 <= LDS, "reduction space");
@@ -133,6 +152,10 @@ struct Cfg {
 // one chunk of a lane's weights, as loaded
 template <int F>
 struct WRaw;
+template <>
+struct WRaw<F_Q4K> {
+    v4i hdr, q0, q1;      // block header; nibble bytes 32kg .. +15, 32kg + 16 .. +15
+};
 template <>
 struct WRaw<F_Q6K> {
     v4i l0, l1, l2, l3;   // ql: 68 bytes from the aligned start of its 64
@@ -176,9 +199,15 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nch * NBLK * M * 4, RSRC_FLAGS);
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nch * 2 * M * 16, RSRC_FLAGS);
     // no records: reads return zero without a memory access (copies and
     // loads of steps past a part's end, so that every step issues the same)
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
+    int8_t *const zero = s_lds + C::S * C::SLOT;
+    if constexpr (F == F_Q4K) {
+        for (int i = tid; i < 256; i += 512) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 
     // base-3 decode table: entry v = the five trits of byte v (t0..t3 in the
     // low word, t4 in the high word); the stores complete before the first
@@ -198,9 +227,17 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     // its values (copy r: rows 4r .. 4r+3; lane l fills piece l%16 of row
     // 4r + l/16 with piece (l%16) ^ row), CPV copies each, and each copies
     // the part's scales (lane l: token l; the same bytes to the same place),
-    // so every wave issues the same.  Token rows past M read other rows'
+    // so every wave issues the same; for Q4_K each also copies the part's
+    // min-term operands (TM = 64: copy j is part j, lane l token l; TM = 32:
+    // lane l part l/32, token l%32; TM = 16: lane l part (l/16)%2, token
+    // l%16, lanes 32..63 into padding).  Token rows past M read other rows'
     // data or zero; their outputs are dropped.
     int a_vo[C::CPV];
+    int l_vo[C::NAL > 0 ? C::NAL : 1];
+#pragma unroll
+    for (int j = 0; j < C::NAL; ++j)
+        l_vo[j] = TM == 64 ? (j * M + lane) * 16
+                           : TM == 32 ? ((lane >> 5) * M + (lane & 31)) * 16 : (((lane >> 4) & 1) * M + (lane & 15)) * 16;
 #pragma unroll
     for (int i = 0; i < C::CPV; ++i) {
         const int row = 4 * (C::CPV * strip + i) + (lane >> 4);
@@ -217,6 +254,8 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 #pragma unroll
         for (int bb = 0; bb < NBLK; ++bb)
             copy4(real ? rs_d : rs_nul, P + C::ACT + 256 * bb, 4 * lane, (chr * NBLK + bb) * M * 4);
+#pragma unroll
+        for (int j = 0; j < C::NAL; ++j) copy16(real ? rs_l : rs_nul, P + C::ALO + 1024 * j, l_vo[j], chr * 2 * M * 16);
     };
     // ---- this lane's weights: row n0 + r16 (row offsets as unsigned: rows
     // past N may pass 2^31, and the range check drops them)
@@ -227,7 +266,12 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
         const bool real = x < T && ch < nch;
         const auto rw = real ? rs_w : rs_nul;
         const uint32_t b = w_row + (uint32_t)((real ? ch : 0) * FM::CB);  // chunk start
-        if constexpr (F == F_Q6K) {
+        if constexpr (F == F_Q4K) {
+            // (blocks are 144 bytes: 16-byte aligned)
+            R.hdr = ld16(rw, (int)b, 0);
+            R.q0 = ld16(rw, (int)b + 16 + 32 * kg, 0);
+            R.q1 = ld16(rw, (int)b + 32 + 32 * kg, 0);
+        } else if constexpr (F == F_Q6K) {
             // the aligned dword at or below the block start (every field
             // offset used with it is a multiple of 4)
             const int b4 = (int)(b & ~3u);
@@ -243,7 +287,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
             R.sc = ld8(rw, b4 + o_sc, 0);
             R.dd = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (int)b + 208, 0, 0);
         } else if constexpr (F == F_TQ) {
-            // dwords kg? {0, 1, 3, 4} .. +2 of each block
+            // dwords {0, 1, 3, 4}[kg] .. +2 of each block
             const int o3 = kg == 0 ? 0 : kg == 1 ? 4 : kg == 2 ? 12 : 16;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
@@ -285,11 +329,17 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
         tq_o[h] = (uint32_t)(k0 % 5);
     }
     const uint32_t lut_ad = lds_addr(lut);
+    // Q4_K min-term operands of m-tile t: part kg (hi, lo) of token 16t + r16
+    // for kg < 2, zeros above (slot offsets apply to real operands only)
+    const uint32_t l_ad = kg < 2 ? lds_addr(s_lds) + part * C::PART + C::ALO + kg * (TM * 16) + 16 * r16
+                                 : lds_addr(zero) + 16 * r16;
+    const uint32_t l_slot = kg < 2 ? 1u : 0u;
 
     auto compute = [&](const WRaw<F> &R, uint32_t so, int ch) __attribute__((always_inline)) {
         // LDS reads: the scales first, then K-step s (one per m-tile), two
         // K-steps in flight
         v4f da[NBLK][MT];
+        v4i ap[MT];
         v4i av[2][MT];
         auto rd = [&](int s, v4i(&dst)[MT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -308,6 +358,17 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 da[bb][t] = __builtin_bit_cast(v4f, lds_read16<0>(d_ad + so + 256 * bb + 64 * t));
+        if constexpr (F == F_Q4K) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                switch (t) {
+                    case 0: ap[t] = lds_read16<0>(l_ad + l_slot * so); break;
+                    case 1: ap[t] = lds_read16<256>(l_ad + l_slot * so); break;
+                    case 2: ap[t] = lds_read16<512>(l_ad + l_slot * so); break;
+                    default: ap[t] = lds_read16<768>(l_ad + l_slot * so); break;
+                }
+            }
+        }
         // base-3: the trits of all four K-steps through the decode table,
         // waited for before the values are read
         v4i tq_b[4];
@@ -350,9 +411,23 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
         const uint32_t b = w_row + (uint32_t)(ch * FM::CB);  // chunk start
         // ---- the chunk's weights, aligned, and the digits of K-step s
         float dw[NBLK];
+        uint32_t q4x = 0;                            // Q4_K: this lane's scale fields
+        float ndmin = 0.0f;
+        v8bf bm;
         uint32_t q6l[17], q6h[8], q6s = 0, sh = 0;  // Q6_K
         uint32_t t2w[2][4];                          // two-bit ternary
-        if constexpr (F == F_Q6K) {
+        if constexpr (F == F_Q4K) {
+            // scales of sub-blocks 2kg (K-steps 0, 1) and 2kg + 1 (2, 3):
+            // fields 2kg, 2kg+1 of the 96-bit word, bits 12kg ..; mins m_j at
+            // bits 48 + 6j
+            const uint64_t f64 = (uint64_t)(uint32_t)R.hdr[1] | ((uint64_t)(uint32_t)R.hdr[2] << 32);
+            q4x = (uint32_t)(f64 >> (12 * kg));
+            dw[0] = f16_bits_to_f32((uint32_t)R.hdr[0]);
+            ndmin = -f16_bits_to_f32((uint32_t)R.hdr[0] >> 16);
+            const uint64_t mx = ((uint64_t)(uint32_t)R.hdr[2] | ((uint64_t)(uint32_t)R.hdr[3] << 32)) >> 16;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bm[i] = (__bf16)(float)(uint32_t)((mx >> (6 * i)) & 63u);
+        } else if constexpr (F == F_Q6K) {
             // the block's offset past the aligned dword (0 or 2 bytes)
             sh = 8u * (b & 3u);
             const uint32_t l[17] = {(uint32_t)R.l0[0], (uint32_t)R.l0[1], (uint32_t)R.l0[2], (uint32_t)R.l0[3],
@@ -384,7 +459,19 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
             }
         }
         auto digits = [&](int s, v4i(&dg)[NDIG]) __attribute__((always_inline)) {
-            if constexpr (F == F_Q6K) {
+            if constexpr (F == F_Q4K) {
+                // the low (s < 2) or high nibbles of bytes 32kg + 16(s % 2) + i
+                const uint32_t sc = (s < 2 ? q4x : q4x >> 6) & 63u;
+                const v4i qw = (s & 1) ? R.q1 : R.q0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t nib = s < 2 ? (uint32_t)qw[e] & 0x0F0F0F0Fu : ((uint32_t)qw[e] >> 4) & 0x0F0F0F0Fu;
+                    uint32_t dh, dl;
+                    q4k_digits(nib, sc, dh, dl);
+                    dg[0][e] = (int)dh;
+                    dg[NDIG - 1][e] = (int)dl;
+                }
+            } else if constexpr (F == F_Q6K) {
                 const uint32_t nib_sh = 4u * (uint32_t)(kg & 1);
                 const int sc = (int)(int8_t)(uint8_t)(q6s >> (8 * s));
                 const uint32_t hsh = nib_sh + 2u * (uint32_t)(s >> 1);
@@ -430,17 +517,31 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
             if (s < 2) rd(s + 2, av[s & 1]);
             if (s % KSB == KSB - 1) {
                 // fold of block bb: out += d_a[m] * d[n] * T, T = 64 acc_h +
-                // acc_l (Q6_K) or acc (ternary).  Its scales were read before
-                // every K-step's values, all of which are in by K-step 1's wait
-                // but the last two K-steps' (2 MT)
+                // acc_l (Q6_K) or acc (ternary); Q4_K: out += d_a[m] * (d[n] *
+                // (8 acc_h + acc_l) - dmin[n] * sum_j m_j B_j), the min term on
+                // one bf16 MFMA per m-tile (A row m = both exact parts of B_j
+                // in k-groups 0 and 1, zeros in 2 and 3; B column n = the
+                // mins).  Its operands were read before every K-step's values,
+                // all of which are in by K-step 1's wait but the last two
+                // K-steps' (2 MT)
                 const int bb = s / KSB;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     lds_wait_n(s < 3 ? 2 * MT : 0, da[bb][t]);
+                    if constexpr (F == F_Q4K) {
+                        lds_wait_n(0, ap[t]);
+                        const v4f mt = mma16_bf16(__builtin_bit_cast(v8bf, ap[t]), bm, v4f{});
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int Tq = NDIG == 2 ? (acc[0][t][i] << 6) + acc[NDIG - 1][t][i] : acc[0][t][i];
-                        out[t][i] = fmaf((float)Tq * dw[bb], da[bb][t][i], out[t][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int Tq = (acc[0][t][i] << FM::SHIFT) + acc[1][t][i];
+                            out[t][i] = fmaf(fmaf((float)Tq, dw[0], mt[i] * ndmin), da[0][t][i], out[t][i]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int Tq = NDIG == 2 ? (acc[0][t][i] << FM::SHIFT) + acc[NDIG - 1][t][i] : acc[0][t][i];
+                            out[t][i] = fmaf((float)Tq * dw[bb], da[bb][t][i], out[t][i]);
+                        }
                     }
                 }
             }
@@ -576,19 +677,21 @@ static void launch_rk_fmt(const rk::Args &a, int kp, hipStream_t stream) {
     }
 }
 
-hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
-                            int K, hipStream_t stream) {
+hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, const uint16_t *alpha,
+                            float *out, int M, int N, int K, hipStream_t stream) {
     rk::Args a;
     a.W = static_cast<const uint8_t *>(W);
     a.qs = qs;
     a.da = da;
+    a.alpha = alpha;
     a.out = out;
     a.M = M;
     a.N = N;
     a.K = K;
     a.nch = K / 256;
     const int kp = ring_parts(M, N, K);
-    if (fmt == rk::F_Q6K) launch_rk_fmt<rk::F_Q6K>(a, kp, stream);
+    if (fmt == rk::F_Q4K) launch_rk_fmt<rk::F_Q4K>(a, kp, stream);
+    else if (fmt == rk::F_Q6K) launch_rk_fmt<rk::F_Q6K>(a, kp, stream);
     else if (fmt == rk::F_TQ) launch_rk_fmt<rk::F_TQ>(a, kp, stream);
     else launch_rk_fmt<rk::F_TQ2>(a, kp, stream);
     return hipGetLastError();

@@ -22,9 +22,10 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
                        int M, int N, int K, hipStream_t stream);
 
 // Q4_K kernels: one or two tokens with K a multiple of 2048 (and the staged
-// activations within the LDS budget) -> matrix-vector kernel; M <= 16 -> the
-// few-token kernel with K split over four waves; M <= 64 -> the two-wave
-// few-token kernel; otherwise the persistent tile kernel, 128 x 128 or (for
+// activations within the LDS budget) -> matrix-vector kernel; up to 64 ->
+// the Q4_K ring kernel on wide weights, the few-token kernel with K split
+// over four waves (up to 16 tokens, mid widths) or the ring kernel of
+// kq_gemm_ring.hip; otherwise the persistent tile kernel, 128 x 128 or (for
 // shapes of at most 256 such tiles) 64 x 128.
 // The 64-row tile also has an 8-wave build (one workgroup per CU, two
 // superblocks per step) for tile counts that balance better over CUs.
@@ -40,21 +41,22 @@ hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da,
 // K-split ring kernel of kq_gemm_ring.hip (fmt: the API's format number).
 bool ring_choice(int fmt, int M, int N, int K);
 int ring_parts(int M, int N, int K);
-hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
-                            int K, hipStream_t stream);
+// (alpha: the Q4_K min-term operands of the activations; unused otherwise)
+hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, const uint16_t *alpha,
+                            float *out, int M, int N, int K, hipStream_t stream);
 
 // Compute units of the current device (cached per device; persistent grids
 // are sized from it).
 int num_cus();
 
 enum Q4KKernel {
-    Q4K_FEW_TOKENS = 0,
     Q4K_TILE128 = 1,
     Q4K_MATVEC = 2,
     Q4K_TILE64 = 3,
     Q4K_TILE64_K2 = 4,
     Q4K_FEW_SPLIT = 5,
-    Q4K_FEW_RING = 6
+    Q4K_FEW_RING = 6,
+    Q4K_RING_KP = 7
 };
 int q4k_kernel_choice(int M, int N, int K);
 

@@ -76,7 +76,7 @@ bool ring_choice(int fmt, int M, int N, int K) {
 }
 int num_cus() { return 256; }
 int q4k_kernel_choice(int M, int, int) {
-    return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_FEW_TOKENS : Q4K_TILE128;
+    return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_RING_KP : Q4K_TILE128;
 }
 hipError_t launch_calib(int, int, const void *, int64_t, int, double *work, hipStream_t) {
     *work = 1.0;

@@ -175,14 +175,17 @@ def test_variants_and_counters(kq):
     assert q4(576, 4096, 4096) == "gemm_q4_k_64x128"     # 9 x 32
     assert q4(2048, 14336, 4096) == "gemm_q4_k_128x128"
     assert q4(65, 4096, 4096) == "gemm_q4_k_64x128_k2"
-    assert q4(64, 4096, 4096) == "gemm_q4_k_m64"
-    assert q4(17, 4096, 4096) == "gemm_q4_k_m64"
-    assert q4(16, 4096, 4096) == "gemm_q4_k_m16"
-    # 3 .. 64 tokens: the K-split ring kernel once the 32-row workgroups of
-    # the other few-token kernels would outnumber the CUs (256 here)
+    # 3 .. 64 tokens: the Q4_K ring kernel once 32-row workgroups would
+    # outnumber the CUs (256 here); below that the four-wave split kernel up
+    # to 16 tokens while 32-row workgroups cover more than half the CUs, and
+    # the ring kernel with 2, 4 or 8 K-parts otherwise
+    assert q4(64, 4096, 4096) == "gemm_q4_k_ring_kp"
+    assert q4(17, 4096, 4096) == "gemm_q4_k_ring_kp"
+    assert q4(16, 4096, 4096) == "gemm_q4_k_ring_kp"    # 128 workgroups of 32 rows
+    assert q4(16, 4128, 4096) == "gemm_q4_k_m16"        # 129
     assert q4(64, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert q4(17, 8224, 4096) == "gemm_q4_k_m64_ring"   # 257 row pairs of 32
-    assert q4(17, 8192, 4096) == "gemm_q4_k_m64"        # 256
+    assert q4(17, 8192, 4096) == "gemm_q4_k_ring_kp"    # 256
     assert q4(16, 8224, 4096) == "gemm_q4_k_m64_ring"   # its 16-row build
     assert q4(16, 8192, 4096) == "gemm_q4_k_m16"
     assert q4(64, 10880, 4096) == "gemm_q4_k_m64_ring"

@@ -109,23 +109,27 @@ def assert_exact(out, want, what):
 # (variant, M, N, K): the 128 x 128 tile needs more than 256 such tiles
 # (3 x 86); the 4-wave 64 x 128 tile more than 256 of its own (3 x 100); the
 # 8-wave 64 x 128 build takes the smaller counts (K = 768: an odd number of
-# superblocks, so one half of its waves sits out the last step); the
-# few-token kernel has a one- and a two-m-tile build; the K-split ring
-# kernel takes 3 .. 64 tokens when N / 32 exceeds the CU count, in
-# 16-, 32- and 64-row builds (one superblock: the second K-half has none;
-# three: its second step is empty; 11016 columns: a ragged last workgroup); the matrix-vector kernel takes one
-# or two tokens with K a multiple of 2048
+# superblocks, so one half of its waves sits out the last step); the Q4_K
+# ring kernel takes 3 .. 64 tokens when N / 32 exceeds the CU count, in 16-,
+# 32- and 64-row builds (one superblock: the second K-half has none; three:
+# its second step is empty; 11016 columns: a ragged last workgroup); below
+# that the four-wave split kernel takes up to 16 tokens while N / 32 is more
+# than half the CU count (4104-4200 rows), and the ring kernel with K-parts
+# the rest (K-parts without a superblock at 200 and 100 rows); the
+# matrix-vector kernel takes one or two tokens with K a multiple of 2048
 Q4K_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 256),
     ("gemm_q4_k_64x128", 192, 12800, 256),
     ("gemm_q4_k_64x128_k2", 70, 96, 256),
     ("gemm_q4_k_64x128_k2", 129, 200, 768),
-    ("gemm_q4_k_m64", 64, 200, 256),
-    ("gemm_q4_k_m64", 20, 200, 512),
+    ("gemm_q4_k_ring_kp", 64, 200, 256),
+    ("gemm_q4_k_ring_kp", 20, 200, 512),
+    ("gemm_q4_k_ring_kp", 3, 100, 256),
+    ("gemm_q4_k_ring_kp", 20, 4104, 768),
     ("gemm_q4_k_m64_ring", 64, 11008, 256),
     ("gemm_q4_k_m64_ring", 20, 11016, 768),
     ("gemm_q4_k_m64_ring", 9, 11008, 512),
-    ("gemm_q4_k_m16", 16, 200, 512), ("gemm_q4_k_m16", 3, 100, 256), ("gemm_q4_k_m16", 9, 96, 1280),
+    ("gemm_q4_k_m16", 16, 4200, 512), ("gemm_q4_k_m16", 3, 4200, 256), ("gemm_q4_k_m16", 9, 4104, 1280),
     ("gemm_q4_k_matvec", 1, 100, 2048),
     ("gemm_q4_k_matvec", 2, 100, 2048),
 ]
@@ -320,10 +324,11 @@ def stress_weights(N, K, seed, kind):
 HEADROOM_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 512),
     ("gemm_q4_k_64x128_k2", 129, 640, 1024),
-    ("gemm_q4_k_m64", 64, 640, 1024),
+    ("gemm_q4_k_ring_kp", 64, 640, 1024),
     ("gemm_q4_k_m64_ring", 64, 11008, 1024),
     ("gemm_q4_k_m64_ring", 16, 11008, 1024),
-    ("gemm_q4_k_m16", 16, 640, 1024),
+    ("gemm_q4_k_m16", 16, 4200, 1024),
+    ("gemm_q4_k_ring_kp", 16, 640, 1024),
     ("gemm_q4_k_matvec", 2, 640, 2048),
 ]
 

@@ -215,10 +215,11 @@ def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
 # K-split ring kernel more than 256 32-row pieces (11016 rows, ragged)
 IDENTITY_CASES = [
     (Q4_K, 2048, "gemm_q4_k_matvec", 2, 72),
-    (Q4_K, 2048, "gemm_q4_k_m64", 64, 72),
+    (Q4_K, 2048, "gemm_q4_k_ring_kp", 64, 72),
+    (Q4_K, 2048, "gemm_q4_k_ring_kp", 32, 4104),
     (Q4_K, 2048, "gemm_q4_k_m64_ring", 64, 11016),
     (Q4_K, 2048, "gemm_q4_k_m64_ring", 16, 11016),
-    (Q4_K, 2048, "gemm_q4_k_m16", 16, 72),
+    (Q4_K, 2048, "gemm_q4_k_m16", 16, 4200),
     (Q4_K, 2048, "gemm_q4_k_64x128_k2", 2048, 72),
     (Q4_K, 2048, "gemm_q4_k_64x128", 2048, 1100),
     (Q4_K, 2048, "gemm_q4_k_128x128", 2048, 2100),

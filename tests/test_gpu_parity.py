@@ -289,7 +289,7 @@ def test_q4k_few_token_ring(kq):
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
     assert name(64, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert name(33, 8224, 1280) == "gemm_q4_k_m64_ring"
-    assert name(64, 8192, 4096) == "gemm_q4_k_m64"
+    assert name(64, 8192, 4096) == "gemm_q4_k_ring_kp"
     assert name(3, 14336, 4096) == "gemm_q4_k_m64_ring"
     assert name(16, 8192, 4096) == "gemm_q4_k_m16"
     N = 11016
@@ -302,6 +302,30 @@ def test_q4k_few_token_ring(kq):
             before = kq.kq_dispatch_count(v)
             gemm_vs_oracle(kq, Q4_K, W, np.ascontiguousarray(x[:M]), M, N, K, what=f"ring M={M} K={K}")
             assert kq.kq_dispatch_count(v) == before + 1
+
+
+def test_q4k_ring_kparts(kq):
+    """The ring kernel of kq_gemm_ring.hip on Q4_K (narrower weights, up to
+    64 tokens): every token-tile build; on 256 CUs 4008 weight rows take
+    eight K-parts (four at 64 rows) and 8192 rows four.  K = 2304 and 3584:
+    tails after whole ring turns, empty K-parts; one token with K not a
+    multiple of 2048 (the matrix-vector kernel declines it)."""
+    name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
+    v = kq.kq_select_variant(Q4_K, 64, 4008, 2304)
+    assert kq.kq_variant_name(v) == "gemm_q4_k_ring_kp"
+    for N in (4008, 8192):
+        for K in (2304, 3584):
+            W = datagen.make_weights(Q4_K, N, K, 9100 + K + N)
+            x = datagen.draw_activations(64, K, 9200 + K)
+            for M in (1, 3, 16, 17, 32, 33, 64):
+                if name(M, N, K) != "gemm_q4_k_ring_kp":
+                    assert M <= 16 and N == 8192
+                    continue
+                say(f"q4k ring_kp M={M} N={N} K={K}")
+                before = kq.kq_dispatch_count(v)
+                gemm_vs_oracle(kq, Q4_K, W, np.ascontiguousarray(x[:M]), M, N, K,
+                               what=f"q4k ring_kp M={M} N={N} K={K}")
+                assert kq.kq_dispatch_count(v) == before + 1
 
 
 def test_q6k_few_token_ring(kq):
@@ -405,11 +429,16 @@ def test_matvec_boundaries(kq):
     """Shapes just outside the matrix-vector kernels' rules go to the
     tile kernels; inside them the long-K projection still takes them."""
     name = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(Q4_K, M, N, K))
-    assert name(3, 4096, 4096) == "gemm_q4_k_m16"
-    assert name(2, 4096, 1792) == "gemm_q4_k_m16"      # K not a multiple of 2048
-    assert name(2, 4096, 2048 * 9) == "gemm_q4_k_m16"  # staged activations past the budget
-    assert name(16, 4096, 4096) == "gemm_q4_k_m16"
-    assert name(17, 4096, 4096) == "gemm_q4_k_m64"
+    assert name(3, 4200, 4096) == "gemm_q4_k_m16"
+    assert name(2, 4200, 1792) == "gemm_q4_k_m16"      # K not a multiple of 2048
+    assert name(2, 4200, 2048 * 9) == "gemm_q4_k_m16"  # staged activations past the budget
+    assert name(2, 4096, 1792) == "gemm_q4_k_ring_kp"  # ... on narrower weights
+    assert name(16, 4200, 4096) == "gemm_q4_k_m16"
+    assert name(17, 4200, 4096) == "gemm_q4_k_ring_kp"
+    Ws = datagen.make_weights(Q4_K, 4200, 4096, 4141)
+    xs = datagen.draw_activations(16, 4096, 4040)
+    say("split M=16 N=4200 K=4096")
+    gemm_vs_oracle(kq, Q4_K, Ws, xs, 16, 4200, 4096)
     assert name(2, 4096, 14336) == "gemm_q4_k_matvec"
     W = datagen.make_weights(Q4_K, 48, 14336, 4242)
     x = datagen.draw_activations(2, 14336, 4343)
