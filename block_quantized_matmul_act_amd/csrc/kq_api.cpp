@@ -40,6 +40,7 @@ enum Variant {
     V_GEMM_TQ2_RING,
     V_GEMM_TQ_RING,
     V_GEMM_Q4K_RING_KP,
+    V_GEMM_TQ2_MATVEC,
     V_COUNT
 };
 
@@ -48,7 +49,7 @@ const char *const kVariantNames[V_COUNT] = {
     "gemm_q6_k_128x128", "gemm_q6_k_matvec", "gemm_tq_128x128", "gemm_tq_matvec", "subsums_q4_k",  "subsums_q6_k",
     "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",   "gemm_id_128x128", "gemm_q4_k_64x128",
     "gemm_id_q4_k_64x128", "gemm_q4_k_64x128_k2", "gemm_q4_k_m16", "gemm_tq_128x128_reg", "gemm_q4_k_m64_ring",
-    "gemm_q6_k_ring", "gemm_tq2_ring", "gemm_tq_ring", "gemm_q4_k_ring_kp",
+    "gemm_q6_k_ring", "gemm_tq2_ring", "gemm_tq_ring", "gemm_q4_k_ring_kp", "gemm_tq2_matvec",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -133,11 +134,11 @@ int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
             default: return V_GEMM_Q4K_128x128;
         }
     }
+    if (kq::gemv_choice(fmt, (int)M, (int)N, (int)K))
+        return fmt == KQ_Q6_K ? V_GEMM_Q6K_MATVEC : fmt == KQ_TQ ? V_GEMM_TQ_MATVEC : V_GEMM_TQ2_MATVEC;
     if (kq::ring_choice(fmt, (int)M, (int)N, (int)K))
         return fmt == KQ_Q6_K ? V_GEMM_Q6K_RING : fmt == KQ_TQ ? V_GEMM_TQ_RING : V_GEMM_TQ2_RING;
     if (fmt == KQ_TQ2) return V_GEMM_TQ2_128x128;
-    if (kq::gemv_choice(fmt, (int)M, (int)N, (int)K))
-        return fmt == KQ_Q6_K ? V_GEMM_Q6K_MATVEC : V_GEMM_TQ_MATVEC;
     if (fmt == KQ_TQ && kq::tq_tile_choice((int)M, (int)N, (int)K)) return V_GEMM_TQ_128x128_REG;
     return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
 }

@@ -621,13 +621,12 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 
 }  // namespace rk
 
-// Shapes this kernel takes: Q6_K and base-3 ternary past the matrix-vector
-// kernels, two-bit ternary from one token, up to 64 tokens, K a multiple of
-// 256.
+// Shapes this kernel takes: Q6_K and ternary past the matrix-vector kernels,
+// up to 64 tokens, K a multiple of 256 (Q4_K comes through its own choice).
 bool ring_choice(int fmt, int M, int N, int K) {
     if (fmt != rk::F_Q6K && fmt != rk::F_TQ && fmt != rk::F_TQ2) return false;
     if (M < 1 || M > 64 || N < 1 || K < 256 || K % 256 != 0) return false;
-    return fmt == rk::F_TQ2 || !gemv_choice(fmt, M, N, K);
+    return !gemv_choice(fmt, M, N, K);
 }
 
 // K-parts: one workgroup runs per CU at a time, each costing a fixed part

@@ -217,7 +217,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Ternary.  Blocks are 28 bytes (26 trit bytes, fp16 scale), 4-byte aligned.
+// Ternary (TWO = false: base-3; TWO = true: two bits per trit).
+// Base-3 blocks are 28 bytes (26 trit bytes, fp16 scale), 4-byte aligned.
 // A load instruction covers 8 consecutive blocks of each of the wave's 8 rows:
 // lane l takes block l%8 of row l/8, all 128 values.  Byte b holds the digits
 // e = t + 1 of values 5b .. 5b+4 (value 5b + p at base-3 position p).  The
@@ -226,11 +227,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_q6k_kernel(Args a) {
 // b's values start at byte 5b of the block's natural order, i.e. at offset
 // 5b mod 4 = b mod 4 of dword floor(5b/4), so the phase-(b mod 4) entry ORs
 // straight into natural-order dwords 5b/4 and 5b/4 + 1 (the two padding
-// positions past value 127 are dropped).  Then 32 v_dot4 per token, one fold
-// per block with the block scale.  The 8 lanes of a row are summed at the
-// end in a fixed order.
+// positions past value 127 are dropped).
+// Two-bit blocks are 34 bytes (32 code bytes, fp16 scale), 2-byte aligned;
+// a lane loads the 9 aligned dwords around its block and shifts them into
+// place with v_alignbit (rows are a multiple of 8 blocks, so an odd block
+// ends 4-aligned and no dword it needs passes the buffer's end).  Code byte
+// j holds weights j + 32p in bits 2p, 2p+1, so natural-order dword d (values
+// 4d .. 4d+3) is plane d/8 of code dword d % 8, trits bytewise without
+// borrows: (c | 0x80) - 1, bit 7 flipped back.
+// Then 32 v_dot4 per token, one fold per block with the block scale.  The 8
+// lanes of a row are summed at the end in a fixed order.
 // ---------------------------------------------------------------------------
-constexpr int TQB = 28;         // ternary block bytes
+constexpr int TQB = 28;         // ternary block bytes (base-3)
+constexpr int TQ2B = 34;        // ... (two bits per trit)
 constexpr int TRPW = 8;         // rows per wave
 constexpr int TRPG = NW * TRPW; // rows per workgroup
 #ifndef GV_TQ_DEPTH
@@ -239,17 +248,18 @@ constexpr int TRPG = NW * TRPW; // rows per workgroup
 constexpr int TQ_DEPTH = GV_TQ_DEPTH;  // load instructions in flight per wave
 constexpr int LUT_BYTES = 4 * 256 * 8;
 __host__ __device__ constexpr int tq_lds_d(int M, int nblk) { return (nblk * M * 4 + 1023) / 1024 * 1024; }
-__host__ __device__ constexpr int tq_lds_bytes(int MT, int M, int K) {
-    return MT * K + tq_lds_d(M, K / 128) + LUT_BYTES + 256;
+__host__ __device__ constexpr int tq_lds_bytes(int MT, int M, int K, bool two = false) {
+    return MT * K + tq_lds_d(M, K / 128) + (two ? 0 : LUT_BYTES) + 256;
 }
 
-template <int MT>
+template <int MT, bool TWO>
 __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
+    constexpr int BB = TWO ? TQ2B : TQB;
     extern __shared__ __attribute__((aligned(16))) int8_t s_gv[];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int M = a.M, N = a.N, K = a.K, nblk = K / 128;
-    const int rowbytes = nblk * TQB;
+    const int rowbytes = nblk * BB;
     const int ipr = nblk >> 3;  // load instructions per row
     const int r = lane >> 3, bl = lane & 7;
     const int row = blockIdx.x * TRPG + w * TRPW + r;
@@ -271,20 +281,30 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
     struct Raw {
         v4i w0;
-        v3u w1;
+        v3u w1;   // base-3: dwords 4..6
+        v4i w1b;  // two bits per trit: dwords 4..7, then w3
+        uint32_t w3;
     };
     // (rows past N: offsets stay below (N + 256) rows, the host's limit)
     auto issue = [&](int j, Raw &R) __attribute__((always_inline)) {
-        const int off = row * rowbytes + (8 * min(j, ipr - 1) + bl) * TQB;
-        R.w0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0));
-        R.w1 = __builtin_bit_cast(v3u, __builtin_amdgcn_raw_buffer_load_b96(rs_w, off + 16, 0, 0));
+        const int off = row * rowbytes + (8 * min(j, ipr - 1) + bl) * BB;
+        if constexpr (TWO) {
+            const int off4 = off & ~3;
+            R.w0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off4, 0, 0));
+            R.w1b = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off4 + 16, 0, 0));
+            R.w3 = __builtin_amdgcn_raw_buffer_load_b32(rs_w, off4 + 32, 0, 0);
+        } else {
+            R.w0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0));
+            R.w1 = __builtin_bit_cast(v3u, __builtin_amdgcn_raw_buffer_load_b96(rs_w, off + 16, 0, 0));
+        }
     };
+    constexpr int WLOADS = TWO ? 3 : 2;  // load instructions per issue
     Raw raw[TQ_DEPTH];
 #pragma unroll
     for (int s = 0; s < TQ_DEPTH; ++s) issue(s, raw[s]);
 
     // ---- the trit table: entry (phi, v), 8 bytes, at 8 * (256 phi + v) ----
-    for (int e = threadIdx.x; e < 4 * 256; e += 64 * NW) {
+    for (int e = threadIdx.x; !TWO && e < 4 * 256; e += 64 * NW) {
         const int phi = e >> 8, v = e & 255;
         uint64_t ent = 0;
         if (v < 243) {
@@ -301,7 +321,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
     // this wave's activation copies have landed once at most the weight loads
     // are in flight, and its table entries once its LDS writes are done; the
     // barrier covers the other waves'
-    wait_vmcnt<2 * TQ_DEPTH>();
+    wait_vmcnt<WLOADS * TQ_DEPTH>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
 
@@ -312,28 +332,47 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
 
     auto compute = [&](int j, const Raw &R) __attribute__((always_inline)) {
         const int b = 8 * j + bl;
-        const uint32_t wv[7] = {(uint32_t)R.w0[0], (uint32_t)R.w0[1], (uint32_t)R.w0[2], (uint32_t)R.w0[3],
-                                R.w1[0], R.w1[1], R.w1[2]};
-        // table lookups for the 26 trit bytes
-        uint64_t ent[26];
-#pragma unroll
-        for (int by = 0; by < 26; ++by) {
-            const uint32_t v = (wv[by >> 2] >> (8 * (by & 3))) & 0xFFu;
-            const uint32_t addr = lut + 2048u * (uint32_t)(by & 3) + 8u * v;
-            ent[by] = *reinterpret_cast<const __attribute__((address_space(3))) uint64_t *>(
-                (__attribute__((address_space(3))) void *)(uintptr_t)addr);
-        }
-        // natural-order int8 trits: byte by ORs into dwords 5by/4 and 5by/4 + 1
         int nat[32];
+        float dw;
+        if constexpr (TWO) {
+            // the block's offset past the aligned dword: 2 bytes for odd
+            // blocks (rows start 4-aligned)
+            const uint32_t sh = 16u * (uint32_t)(b & 1);
+            const uint32_t wv[9] = {(uint32_t)R.w0[0],  (uint32_t)R.w0[1],  (uint32_t)R.w0[2],
+                                    (uint32_t)R.w0[3],  (uint32_t)R.w1b[0], (uint32_t)R.w1b[1],
+                                    (uint32_t)R.w1b[2], (uint32_t)R.w1b[3], R.w3};
+            uint32_t cw[8];
 #pragma unroll
-        for (int d = 0; d < 32; ++d) nat[d] = 0;
+            for (int e = 0; e < 8; ++e) cw[e] = __builtin_amdgcn_alignbit(wv[e + 1], wv[e], sh);
 #pragma unroll
-        for (int by = 0; by < 26; ++by) {
-            const int d0 = (5 * by) >> 2;
-            nat[d0] |= (int)(uint32_t)ent[by];
-            if (d0 + 1 < 32) nat[d0 + 1] |= (int)(uint32_t)(ent[by] >> 32);
+            for (int d = 0; d < 32; ++d) {
+                const uint32_t c = (cw[d & 7] >> (2 * (d >> 3))) & 0x03030303u;
+                nat[d] = (int)(((c | 0x80808080u) - 0x01010101u) ^ 0x80808080u);
+            }
+            dw = f16_bits_to_f32((R.w3 >> sh) & 0xFFFFu);
+        } else {
+            const uint32_t wv[7] = {(uint32_t)R.w0[0], (uint32_t)R.w0[1], (uint32_t)R.w0[2], (uint32_t)R.w0[3],
+                                    R.w1[0], R.w1[1], R.w1[2]};
+            // table lookups for the 26 trit bytes
+            uint64_t ent[26];
+#pragma unroll
+            for (int by = 0; by < 26; ++by) {
+                const uint32_t v = (wv[by >> 2] >> (8 * (by & 3))) & 0xFFu;
+                const uint32_t addr = lut + 2048u * (uint32_t)(by & 3) + 8u * v;
+                ent[by] = *reinterpret_cast<const __attribute__((address_space(3))) uint64_t *>(
+                    (__attribute__((address_space(3))) void *)(uintptr_t)addr);
+            }
+            // natural-order int8 trits: byte by ORs into dwords 5by/4 and 5by/4 + 1
+#pragma unroll
+            for (int d = 0; d < 32; ++d) nat[d] = 0;
+#pragma unroll
+            for (int by = 0; by < 26; ++by) {
+                const int d0 = (5 * by) >> 2;
+                nat[d0] |= (int)(uint32_t)ent[by];
+                if (d0 + 1 < 32) nat[d0 + 1] |= (int)(uint32_t)(ent[by] >> 32);
+            }
+            dw = f16_bits_to_f32(wv[6] >> 16);
         }
-        const float dw = f16_bits_to_f32(wv[6] >> 16);
         const int kb = b * 128;
         v4i av[MT][8];
         float da[MT];
@@ -360,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_tq_kernel(Args a) {
         for (int s = 0; s < TQ_DEPTH; ++s) {
             // instruction j0 + s has landed once the TQ_DEPTH - 1 issued after
             // it may still be in flight (past the last, re-reads are harmless)
-            wait_vmcnt<2 * (TQ_DEPTH - 1)>();
+            wait_vmcnt<WLOADS * (TQ_DEPTH - 1)>();
             if (j0 + s < ipr) compute(j0 + s, raw[s]);
             issue(j0 + s + TQ_DEPTH, raw[s]);
         }
@@ -394,6 +433,7 @@ bool gemv_choice(int fmt, int M, int N, int K) {
     if (M < 1 || M > 4) return false;
     if (fmt == 2) return K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     if (fmt == 3) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
+    if (fmt == 4) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K, true) <= gv::LDS_BUDGET;
     return false;
 }
 
@@ -409,13 +449,23 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
     a.K = K;
     const dim3 block(64 * gv::NW);
     const int mt = gv_tokens(M);
-    if (fmt == 3) {
+    if (fmt == 3 || fmt == 4) {
         const dim3 grid((unsigned)((N + gv::TRPG - 1) / gv::TRPG));
-        const size_t lds = (size_t)gv::tq_lds_bytes(mt, M, K);
+        const bool two = fmt == 4;
+        const size_t lds = (size_t)gv::tq_lds_bytes(mt, M, K, two);
         switch (mt) {
-            case 1: hipLaunchKernelGGL(gv::gemv_tq_kernel<1>, grid, block, lds, stream, a); break;
-            case 2: hipLaunchKernelGGL(gv::gemv_tq_kernel<2>, grid, block, lds, stream, a); break;
-            default: hipLaunchKernelGGL(gv::gemv_tq_kernel<4>, grid, block, lds, stream, a); break;
+            case 1:
+                if (two) hipLaunchKernelGGL((gv::gemv_tq_kernel<1, true>), grid, block, lds, stream, a);
+                else hipLaunchKernelGGL((gv::gemv_tq_kernel<1, false>), grid, block, lds, stream, a);
+                break;
+            case 2:
+                if (two) hipLaunchKernelGGL((gv::gemv_tq_kernel<2, true>), grid, block, lds, stream, a);
+                else hipLaunchKernelGGL((gv::gemv_tq_kernel<2, false>), grid, block, lds, stream, a);
+                break;
+            default:
+                if (two) hipLaunchKernelGGL((gv::gemv_tq_kernel<4, true>), grid, block, lds, stream, a);
+                else hipLaunchKernelGGL((gv::gemv_tq_kernel<4, false>), grid, block, lds, stream, a);
+                break;
         }
         return hipGetLastError();
     }

@@ -62,7 +62,7 @@ hipError_t launch_subsums(int, const void *, const int8_t *, int32_t *, int, int
     ++rs.calls;
     return hipSuccess;
 }
-bool gemv_choice(int fmt, int M, int, int) { return (fmt == 2 || fmt == 3) && M <= 4; }
+bool gemv_choice(int fmt, int M, int, int) { return fmt >= 2 && fmt <= 4 && M <= 4; }
 hipError_t launch_gemv(int, const void *, const int8_t *, const float *, float *, int, int, int, hipStream_t) {
     return hipSuccess;
 }
@@ -71,8 +71,7 @@ hipError_t launch_gemm_tq_tile(const void *, const int8_t *, const float *, floa
     return hipSuccess;
 }
 bool ring_choice(int fmt, int M, int N, int K) {
-    return fmt >= 2 && fmt <= 4 && M >= 1 && M <= 64 && K >= 256 && K % 256 == 0 &&
-           (fmt == 4 || !gemv_choice(fmt, M, N, K));
+    return fmt >= 2 && fmt <= 4 && M >= 1 && M <= 64 && K >= 256 && K % 256 == 0 && !gemv_choice(fmt, M, N, K);
 }
 int num_cus() { return 256; }
 int q4k_kernel_choice(int M, int, int) {

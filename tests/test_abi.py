@@ -213,11 +213,15 @@ def test_variants_and_counters(kq):
     assert tq(64, 17408, 5120) == "gemm_tq_ring"
     assert tq(1, 17408, 5120 + 256) == "gemm_tq_ring"   # K not a multiple of 1024
     assert tq(9, 17408, 5120 + 128) == "gemm_tq_128x128"
-    # two-bit ternary: the K-split ring kernel up to 64 tokens (K a multiple
-    # of 256), the tile kernel otherwise
+    # two-bit ternary: the matrix-vector kernel up to 4 tokens (K a multiple
+    # of 1024), the K-split ring kernel up to 64 (K a multiple of 256), the
+    # tile kernel otherwise
     tq2 = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(kq.KQ_TQ2, M, N, K))
-    for M in (1, 8, 64):
+    for M in (1, 4):
+        assert tq2(M, 4096, 5120) == "gemm_tq2_matvec"
+    for M in (5, 8, 64):
         assert tq2(M, 4096, 5120) == "gemm_tq2_ring"
+    assert tq2(1, 4096, 5120 + 256) == "gemm_tq2_ring"
     assert tq2(65, 4096, 5120) == "gemm_tq2_128x128"
     assert tq2(2048, 4096, 5120) == "gemm_tq2_128x128"
     assert tq2(8, 4096, 5120 + 128) == "gemm_tq2_128x128"

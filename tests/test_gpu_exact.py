@@ -269,6 +269,8 @@ TQ_CASES = [
     ("gemm_tq2_128x128", TQ2, 5, 40, 1152),
     # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts
     # (40 and 72 rows), four (4104 rows; 64 tokens' 200), two (14344 rows)
+    ("gemm_tq2_matvec", TQ2, 1, 40, 1024),
+    ("gemm_tq2_matvec", TQ2, 4, 40, 2048),
     ("gemm_tq2_ring", TQ2, 1, 40, 256),
     ("gemm_tq2_ring", TQ2, 5, 72, 1024),
     ("gemm_tq2_ring", TQ2, 20, 4104, 768),

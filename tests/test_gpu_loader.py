@@ -233,6 +233,7 @@ IDENTITY_CASES = [
     (TQ, 1280, "gemm_tq_ring", 64, 4104),
     (TQ, 1024, "gemm_tq_128x128_reg", 1024, 4200),
     (TQ2, 1152, "gemm_tq2_128x128", 8, 72),
+    (TQ2, 1024, "gemm_tq2_matvec", 4, 72),
     (TQ2, 1024, "gemm_tq2_ring", 8, 72),
     (TQ2, 1280, "gemm_tq2_ring", 64, 4104),
     (TQ2, 1024, "gemm_tq2_128x128", 1024, 72),

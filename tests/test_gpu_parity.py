@@ -402,7 +402,7 @@ def test_tq2_few_token_ring(kq):
 
 
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 4)),
-          TQ: ("gemm_tq_matvec", (1, 2, 3, 4))}
+          TQ: ("gemm_tq_matvec", (1, 2, 3, 4)), TQ2: ("gemm_tq2_matvec", (1, 2, 3, 4))}
 
 
 @pytest.mark.parametrize("fmt", sorted(MATVEC))
