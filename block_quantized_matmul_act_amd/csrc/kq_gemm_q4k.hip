@@ -1434,9 +1434,12 @@ int q4k_kernel_choice(int M, int N, int K) {
     // 4096 x 4096 7.3 / 5.8, 4096 x 14336 at 3 tokens 17.1 / 12.1.  From 17
     // tokens the ring kernel beat the former two-wave kernel at every width
     // measured (8192 x 4096: 9.2 / 11.1 at 17 tokens, 12.6 / 14.1 at 64;
-    // 4096 x 14336: 18.0 / 31.9 at 32 tokens, 32.2 / 41.3 at 64).
+    // 4096 x 14336: 18.0 / 31.9 at 32 tokens, 32.2 / 41.3 at 64).  Past 64
+    // tokens, the ring kernel in 64-token slices where the tile kernels
+    // would leave most CUs idle (4096 x 14336 at 128 tokens: 33 against 77
+    // us).
     if (M <= 16 && 2 * ((N + 31) / 32) > cus) return Q4K_FEW_SPLIT;
-    if (M <= 64) return Q4K_RING_KP;
+    if (M <= 64 || ring_slices_pay(1, M, N, K)) return Q4K_RING_KP;
     const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);

@@ -195,11 +195,18 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     const int n0 = blockIdx.x * C::ROWS + 16 * strip;
     const int rowbytes = nch * FM::CB;
 
-    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)a.qs, (short)0, M * K, RSRC_FLAGS);
-    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)a.da, (short)0, nch * NBLK * M * 4, RSRC_FLAGS);
+    // token slice: rows m0 .. m0 + TM - 1 (the resources start at row m0,
+    // strides stay those of the whole M)
+    const int m0 = blockIdx.y * TM;
+    const auto rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)(a.qs + (size_t)m0 * K), (short)0, (M - m0) * K,
+                                                        RSRC_FLAGS);
+    const auto rs_d = __builtin_amdgcn_make_buffer_rsrc((void *)(a.da + m0), (short)0, (nch * NBLK * M - m0) * 4,
+                                                        RSRC_FLAGS);
     const auto rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, N * rowbytes, RSRC_FLAGS);
-    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)a.out, (short)0, M * N * 4, RSRC_FLAGS);
-    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)a.alpha, (short)0, nch * 2 * M * 16, RSRC_FLAGS);
+    const auto rs_o = __builtin_amdgcn_make_buffer_rsrc((void *)(a.out + (size_t)m0 * N), (short)0, (M - m0) * N * 4,
+                                                        RSRC_FLAGS);
+    const auto rs_l = __builtin_amdgcn_make_buffer_rsrc((void *)(F == F_Q4K ? a.alpha + (size_t)m0 * 8 : a.alpha), (short)0,
+                                                        (nch * 2 * M - m0) * 16, RSRC_FLAGS);
     // no records: reads return zero without a memory access (copies and
     // loads of steps past a part's end, so that every step issues the same)
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
@@ -621,43 +628,84 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
 
 }  // namespace rk
 
-// Shapes this kernel takes: Q6_K and ternary past the matrix-vector kernels,
-// up to 64 tokens, K a multiple of 256 (Q4_K comes through its own choice).
-bool ring_choice(int fmt, int M, int N, int K) {
-    if (fmt != rk::F_Q6K && fmt != rk::F_TQ && fmt != rk::F_TQ2) return false;
-    if (M < 1 || M > 64 || N < 1 || K < 256 || K % 256 != 0) return false;
-    return !gemv_choice(fmt, M, N, K);
-}
-
 // K-parts: one workgroup runs per CU at a time, each costing a fixed part
 // (filling the rings, the reduction: about 4.5 us) plus its waves' share of
 // K (about 0.0085-0.010 us per K value at 16-64 tokens), so the time goes as
-// rounds * (512 + K / parts) in units of K.  The fewest parts among the
-// best, within what the token tile's LDS allows (64 rows: at most four).
-// Measured (Q6_K) at 16 tokens, K = 4096, us for 2 / 4 / 8 parts: 4096 rows
-// 21.4 / 14.1 / 9.3; 8192 rows 22.0 / 14.9 / 17.1; 11008 rows 22.4 / 27.0 /
-// 24.5; 14336 rows 23.0 / 27.5 / 31.8; 28672 rows 44.2 / 53.1 / 55.4.
-int ring_parts(int M, int N, int K) {
+// rounds * (512 + K / parts) in units of K, the workgroups of every 64-token
+// slice counted.  The fewest parts among the best, within what the token
+// tile's LDS allows (64 rows: at most four).  Measured (Q6_K) at 16 tokens,
+// K = 4096, us for 2 / 4 / 8 parts: 4096 rows 21.4 / 14.1 / 9.3; 8192 rows
+// 22.0 / 14.9 / 17.1; 11008 rows 22.4 / 27.0 / 24.5; 14336 rows 23.0 / 27.5 /
+// 31.8; 28672 rows 44.2 / 53.1 / 55.4.
+static int64_t ring_plan(int M, int N, int K, int *parts) {
     const int cus = num_cus();
     const int kmax = M > 32 ? 4 : 8;
+    const int64_t slices = M > 64 ? (M + 63) / 64 : 1;
     int best = 2;
     int64_t best_cost = 0;
     for (int kp = 2; kp <= kmax; kp *= 2) {
-        const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp));
+        const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp)) * slices;
         const int64_t cost = (wgs + cus - 1) / cus * (512 + K / kp);
         if (kp == 2 || cost < best_cost) {
             best = kp;
             best_cost = cost;
         }
     }
-    return best;
+    *parts = best;
+    return best_cost;
+}
+
+int ring_parts(int M, int N, int K) {
+    int kp;
+    ring_plan(M, N, K, &kp);
+    return kp;
+}
+
+// Past 64 tokens the ring kernel runs one 64-token slice per grid row, each
+// reading the whole weight matrix again (from L2 and the last-level cache
+// when the slices run together).  It pays where the 128 x 128 tile kernels
+// leave most CUs idle: narrow weights with a long K.  The tile kernels' time
+// goes as rounds * K, their rounds counted in 128 x 128 tiles; the two
+// models are weighed with the ratio of their fitted costs per unit (ring /
+// tile: Q4_K 6/5, Q6_K 19/20, base-3 5/6, two-bit 4/5).  Paired runs, us,
+// tile / ring: Q6_K 4096 x 14336 at 65 tokens 142 / 44, 128 144 / 45.5, 256
+// 143 / 77, 384 143 / 124, 512 144 / 143, 1024 172 / 291; 4096 x 4096 at
+// 128 45 / 15.8, 256 45 / 25, 512 45.6 / 45.6; 14336 x 4096 at 128 46.8 /
+// 46.9, 256 51 / 90.  Base-3 4096 x 14336 at 128 / 256 / 512 tokens 111 /
+// 31, 111 / 49, 112 / 91; 17408 x 5120 at 128 44 / 55.  Two-bit 4096 x
+// 14336 101 / 33, 101 / 48, 102 / 86.5; 17408 x 5120 at 128 40 / 52.  Q4_K
+// 4096 x 14336 at 65 / 128 / 256 / 512 tokens 71 / 31, 77 / 33, 77 / 50, 79
+// / 93; 4096 x 4096 at 128 24 / 11.6, 256 24 / 16.8; 14336 x 4096 at 128 26
+// / 31.
+bool ring_slices_pay(int fmt, int M, int N, int K) {
+    if (M <= 64 || M > 512) return false;
+    const int cus = num_cus();
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t tile_units = (tiles + cus - 1) / cus * K;
+    int kp;
+    const int64_t ring_units = ring_plan(M, N, K, &kp);
+    int num = 4, den = 5;  // two-bit ternary
+    if (fmt == rk::F_Q4K) num = 6, den = 5;
+    else if (fmt == rk::F_Q6K) num = 19, den = 20;
+    else if (fmt == rk::F_TQ) num = 5, den = 6;
+    return ring_units * num < tile_units * den;
+}
+
+// Shapes this kernel takes: Q6_K and ternary past the matrix-vector kernels,
+// up to 64 tokens, and in 64-token slices where that pays; K a multiple of
+// 256 (Q4_K comes through its own choice).
+bool ring_choice(int fmt, int M, int N, int K) {
+    if (fmt != rk::F_Q6K && fmt != rk::F_TQ && fmt != rk::F_TQ2) return false;
+    if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return false;
+    if (M > 64) return ring_slices_pay(fmt, M, N, K);
+    return !gemv_choice(fmt, M, N, K);
 }
 
 template <int F, int TM, int KP>
 static void launch_rk(const rk::Args &a, hipStream_t stream) {
     constexpr int R = rk::Cfg<F, TM, KP>::ROWS;
-    hipLaunchKernelGGL((rk::gemm_ring_kernel<F, TM, KP>), dim3((unsigned)((a.N + R - 1) / R)), dim3(512), 0,
-                       stream, a);
+    hipLaunchKernelGGL((rk::gemm_ring_kernel<F, TM, KP>),
+                       dim3((unsigned)((a.N + R - 1) / R), (unsigned)((a.M + TM - 1) / TM)), dim3(512), 0, stream, a);
 }
 
 template <int F>

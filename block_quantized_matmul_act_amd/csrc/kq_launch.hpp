@@ -36,11 +36,13 @@ bool tq_tile_choice(int M, int N, int K);
 hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
                                int K, hipStream_t stream);
 
-// Q6_K products of up to 64 tokens past the matrix-vector kernel, and
-// two-bit ternary products of up to 64 tokens (K a multiple of 256): the
-// K-split ring kernel of kq_gemm_ring.hip (fmt: the API's format number).
+// Q6_K and ternary products of up to 64 tokens past the matrix-vector
+// kernels, and of 65-512 tokens where 64-token slices beat the tile kernels
+// (K a multiple of 256): the K-split ring kernel of kq_gemm_ring.hip (fmt:
+// the API's format number; ring_slices_pay also takes Q4_K).
 bool ring_choice(int fmt, int M, int N, int K);
 int ring_parts(int M, int N, int K);
+bool ring_slices_pay(int fmt, int M, int N, int K);
 // (alpha: the Q4_K min-term operands of the activations; unused otherwise)
 hipError_t launch_gemm_ring(int fmt, const void *W, const int8_t *qs, const float *da, const uint16_t *alpha,
                             float *out, int M, int N, int K, hipStream_t stream);

@@ -174,7 +174,7 @@ def test_variants_and_counters(kq):
     assert q4(512, 4096, 4096) == "gemm_q4_k_64x128_k2"  # 8 x 32 tiles of 64 rows
     assert q4(576, 4096, 4096) == "gemm_q4_k_64x128"     # 9 x 32
     assert q4(2048, 14336, 4096) == "gemm_q4_k_128x128"
-    assert q4(65, 4096, 4096) == "gemm_q4_k_64x128_k2"
+    assert q4(65, 4000, 512) == "gemm_q4_k_64x128_k2"
     # 3 .. 64 tokens: the Q4_K ring kernel once 32-row workgroups would
     # outnumber the CUs (256 here); below that the four-wave split kernel up
     # to 16 tokens while 32-row workgroups cover more than half the CUs, and
@@ -197,7 +197,19 @@ def test_variants_and_counters(kq):
     assert q6(5, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(9, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(64, 4096, 14336) == "gemm_q6_k_ring"
-    assert q6(65, 4096, 14336) == "gemm_q6_k_128x128"
+    # 65 .. 512 tokens: the ring kernel in 64-token slices where the 128 x
+    # 128 tile kernels leave most CUs idle (narrow weights, long K)
+    for M in (65, 128, 200, 384):
+        assert q6(M, 4096, 14336) == "gemm_q6_k_ring"
+    assert q6(512, 4096, 14336) == "gemm_q6_k_128x128"  # 128 tiles over 14336 of K
+    assert q6(513, 1024, 4096) == "gemm_q6_k_128x128"   # past 512 tokens
+    assert q6(512, 1024, 4096) == "gemm_q6_k_ring"
+    assert q6(128, 14336, 4096) == "gemm_q6_k_128x128"  # 112 tiles already
+    assert q6(130, 72, 512) == "gemm_q6_k_128x128"      # one tile, short K
+    assert q4(128, 4096, 14336) == "gemm_q4_k_ring_kp"
+    assert q4(256, 4096, 14336) == "gemm_q4_k_ring_kp"
+    assert q4(384, 4096, 14336) == "gemm_q4_k_64x128_k2"
+    assert q4(128, 14336, 4096) != "gemm_q4_k_ring_kp"
     assert q6(4, 4096, 14336 + 256) == "gemm_q6_k_ring"  # K not a multiple of 2048
     assert q6(1, 100, 256) == "gemm_q6_k_ring"
     # base-3 ternary: the register-unpack tile kernel when K is a multiple of
@@ -213,6 +225,9 @@ def test_variants_and_counters(kq):
     assert tq(64, 17408, 5120) == "gemm_tq_ring"
     assert tq(1, 17408, 5120 + 256) == "gemm_tq_ring"   # K not a multiple of 1024
     assert tq(9, 17408, 5120 + 128) == "gemm_tq_128x128"
+    for M in (65, 256, 512):
+        assert tq(M, 4096, 14336) == "gemm_tq_ring"
+    assert tq(128, 17408, 5120) != "gemm_tq_ring"
     # two-bit ternary: the matrix-vector kernel up to 4 tokens (K a multiple
     # of 1024), the K-split ring kernel up to 64 (K a multiple of 256), the
     # tile kernel otherwise
@@ -222,7 +237,9 @@ def test_variants_and_counters(kq):
     for M in (5, 8, 64):
         assert tq2(M, 4096, 5120) == "gemm_tq2_ring"
     assert tq2(1, 4096, 5120 + 256) == "gemm_tq2_ring"
-    assert tq2(65, 4096, 5120) == "gemm_tq2_128x128"
+    assert tq2(65, 4096, 5120) == "gemm_tq2_ring"
+    assert tq2(512, 4096, 14336) == "gemm_tq2_ring"
+    assert tq2(128, 17408, 5120) == "gemm_tq2_128x128"
     assert tq2(2048, 4096, 5120) == "gemm_tq2_128x128"
     assert tq2(8, 4096, 5120 + 128) == "gemm_tq2_128x128"
     assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT

@@ -126,6 +126,10 @@ Q4K_CASES = [
     ("gemm_q4_k_ring_kp", 20, 200, 512),
     ("gemm_q4_k_ring_kp", 3, 100, 256),
     ("gemm_q4_k_ring_kp", 20, 4104, 768),
+    # ... in 64-token slices (two, three ragged, five)
+    ("gemm_q4_k_ring_kp", 128, 72, 2048),
+    ("gemm_q4_k_ring_kp", 150, 200, 2048),
+    ("gemm_q4_k_ring_kp", 300, 72, 2048),
     ("gemm_q4_k_m64_ring", 64, 11008, 256),
     ("gemm_q4_k_m64_ring", 20, 11016, 768),
     ("gemm_q4_k_m64_ring", 9, 11008, 512),
@@ -223,6 +227,10 @@ Q6K_CASES = [
     ("gemm_q6_k_ring", 20, 4104, 1024),
     ("gemm_q6_k_ring", 33, 200, 768),
     ("gemm_q6_k_ring", 16, 14344, 512),
+    # ... in 64-token slices (two, three ragged, five)
+    ("gemm_q6_k_ring", 128, 72, 2048),
+    ("gemm_q6_k_ring", 150, 200, 2048),
+    ("gemm_q6_k_ring", 300, 72, 2048),
 ]
 
 
@@ -265,6 +273,7 @@ TQ_CASES = [
     ("gemm_tq_ring", TQ, 20, 4104, 768),
     ("gemm_tq_ring", TQ, 64, 200, 512),
     ("gemm_tq_ring", TQ, 16, 14344, 512),
+    ("gemm_tq_ring", TQ, 150, 200, 2048),  # three 64-token slices, ragged
     ("gemm_tq2_128x128", TQ2, 67, 90, 640),
     ("gemm_tq2_128x128", TQ2, 5, 40, 1152),
     # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts
@@ -276,6 +285,7 @@ TQ_CASES = [
     ("gemm_tq2_ring", TQ2, 20, 4104, 768),
     ("gemm_tq2_ring", TQ2, 64, 200, 512),
     ("gemm_tq2_ring", TQ2, 16, 14344, 512),
+    ("gemm_tq2_ring", TQ2, 150, 200, 2048),
 ]
 
 
@@ -325,7 +335,8 @@ def stress_weights(N, K, seed, kind):
 
 HEADROOM_CASES = [
     ("gemm_q4_k_128x128", 300, 11000, 512),
-    ("gemm_q4_k_64x128_k2", 129, 640, 1024),
+    ("gemm_q4_k_64x128_k2", 129, 4000, 1024),
+    ("gemm_q4_k_ring_kp", 129, 640, 1024),  # three 64-token slices
     ("gemm_q4_k_ring_kp", 64, 640, 1024),
     ("gemm_q4_k_m64_ring", 64, 11008, 1024),
     ("gemm_q4_k_m64_ring", 16, 11008, 1024),

@@ -401,6 +401,39 @@ def test_tq2_few_token_ring(kq):
                 assert kq.kq_dispatch_count(v) == before + 1
 
 
+SLICE_RING = {Q4_K: "gemm_q4_k_ring_kp", Q6_K: "gemm_q6_k_ring", TQ: "gemm_tq_ring", TQ2: "gemm_tq2_ring"}
+
+
+@pytest.mark.parametrize("fmt", sorted(SLICE_RING))
+def test_ring_token_slices(kq, fmt):
+    """Past 64 tokens the ring kernel runs one 64-token slice per grid row,
+    each slice's activations, scales, min-term operands and output rows at
+    its own offset: full products against the oracle at 65 tokens (one in
+    the second slice), 128, 200 (ragged), 320 and 512, on 1000 weight rows
+    (ragged against the 32- and 64-row workgroups) and 1024, K = 2304 (a
+    tail after whole ring turns) and 4096.  Then 128 tokens on the FFN-down
+    shape 4096 x 14336."""
+    name = SLICE_RING[fmt]
+    for N in (1000, 1024):
+        for K in (2304, 4096):
+            W = datagen.make_weights(fmt, N, K, 9100 + N + K + fmt)
+            x = datagen.draw_activations(512, K, 9200 + K + fmt)
+            for M in (65, 128, 200, 320, 512):
+                v = kq.kq_select_variant(fmt, M, N, K)
+                assert kq.kq_variant_name(v) == name, (M, N, K)
+                say(f"{name} slices M={M} N={N} K={K}")
+                before = kq.kq_dispatch_count(v)
+                gemm_vs_oracle(kq, fmt, W, np.ascontiguousarray(x[:M]), M, N, K,
+                               what=f"{name} slices M={M} N={N} K={K}")
+                assert kq.kq_dispatch_count(v) == before + 1
+    M, N, K = 128, 4096, 14336
+    assert kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)) == name
+    W = datagen.make_weights(fmt, N, K, 9300 + fmt)
+    x = datagen.draw_activations(M, K, 9400 + fmt)
+    say(f"{name} slices M={M} N={N} K={K}")
+    gemm_vs_oracle(kq, fmt, W, x, M, N, K, what=f"{name} slices FFN down")
+
+
 MATVEC = {Q4_K: ("gemm_q4_k_matvec", (1, 2)), Q6_K: ("gemm_q6_k_matvec", (1, 2, 3, 4)),
           TQ: ("gemm_tq_matvec", (1, 2, 3, 4)), TQ2: ("gemm_tq2_matvec", (1, 2, 3, 4))}
 
@@ -448,7 +481,8 @@ def test_matvec_boundaries(kq):
     assert q6(5, 4096, 14336) == "gemm_q6_k_ring"
     assert q6(4, 4096, 14336 + 256) == "gemm_q6_k_ring"  # K not a multiple of 2048
     assert q6(4, 4096, 14336) == "gemm_q6_k_matvec"
-    assert q6(65, 4096, 14336) == "gemm_q6_k_128x128"
+    assert q6(65, 4096, 14336) == "gemm_q6_k_ring"       # 64-token slices
+    assert q6(520, 4096, 14336) == "gemm_q6_k_128x128"
     tq = lambda M, N, K: kq.kq_variant_name(kq.kq_select_variant(TQ, M, N, K))
     assert tq(9, 17408, 5120) == "gemm_tq_ring"           # past the matrix-vector kernel
     assert tq(65, 17408, 5120) == "gemm_tq_128x128"       # fewer 128 x 128 tiles than CUs
