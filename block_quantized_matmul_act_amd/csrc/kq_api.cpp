@@ -41,6 +41,9 @@ enum Variant {
     V_GEMM_TQ_RING,
     V_GEMM_Q4K_RING_KP,
     V_GEMM_TQ2_MATVEC,
+    V_GEMM_Q6K_128x128_K2,
+    V_GEMM_TQ_128x128_K2,
+    V_GEMM_TQ2_128x128_K2,
     V_COUNT
 };
 
@@ -50,6 +53,7 @@ const char *const kVariantNames[V_COUNT] = {
     "subsums_tq",        "gemm_tq2_128x128", "subsums_tq2",   "gemm_id_128x128", "gemm_q4_k_64x128",
     "gemm_id_q4_k_64x128", "gemm_q4_k_64x128_k2", "gemm_q4_k_m16", "gemm_tq_128x128_reg", "gemm_q4_k_m64_ring",
     "gemm_q6_k_ring", "gemm_tq2_ring", "gemm_tq_ring", "gemm_q4_k_ring_kp", "gemm_tq2_matvec",
+    "gemm_q6_k_128x128_k2", "gemm_tq_128x128_k2", "gemm_tq2_128x128_k2",
 };
 
 std::atomic<uint64_t> g_count[V_COUNT];
@@ -138,8 +142,10 @@ int variant_for(int fmt, int64_t M, int64_t N, int64_t K) {
         return fmt == KQ_Q6_K ? V_GEMM_Q6K_MATVEC : fmt == KQ_TQ ? V_GEMM_TQ_MATVEC : V_GEMM_TQ2_MATVEC;
     if (kq::ring_choice(fmt, (int)M, (int)N, (int)K))
         return fmt == KQ_Q6_K ? V_GEMM_Q6K_RING : fmt == KQ_TQ ? V_GEMM_TQ_RING : V_GEMM_TQ2_RING;
-    if (fmt == KQ_TQ2) return V_GEMM_TQ2_128x128;
     if (fmt == KQ_TQ && kq::tq_tile_choice((int)M, (int)N, (int)K)) return V_GEMM_TQ_128x128_REG;
+    if (kq::tile_split_choice(fmt, (int)M, (int)N, (int)K))
+        return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128_K2 : fmt == KQ_TQ ? V_GEMM_TQ_128x128_K2 : V_GEMM_TQ2_128x128_K2;
+    if (fmt == KQ_TQ2) return V_GEMM_TQ2_128x128;
     return fmt == KQ_Q6_K ? V_GEMM_Q6K_128x128 : V_GEMM_TQ_128x128;
 }
 

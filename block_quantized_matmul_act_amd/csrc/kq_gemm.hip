@@ -436,7 +436,12 @@ struct ChunkRegs<FMT_TQ2> {
     uint32_t d;     // fp16 d
 };
 
-template <int FMT, bool GATHER = false>
+// SPLIT: K in two parts on blockIdx.y (for shapes with at most half as many
+// tiles as CUs), each a whole number of four-chunk groups so that both start
+// at phase 0; each part adds its sums into the output, zeroed before the
+// launch.  With exactly two addends onto zero the result does not depend on
+// their order (0 + a + b = 0 + b + a in fp32), so it is deterministic.
+template <int FMT, bool GATHER = false, bool SPLIT = false>
 __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     constexpr int BM = MBM, BN = MBN, KCH = MKC;
     constexpr int NDIG = Fmt<FMT>::NDIG;
@@ -520,7 +525,10 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
         const int t = a.rows[idx];
         return min(max(t, 0), M - 1);
     };
-    const int nch = (K + KCH - 1) / KCH;                    // chunks
+    const int nch_all = (K + KCH - 1) / KCH;                // chunks
+    const int cpp = SPLIT ? ((nch_all + 1) / 2 + 3) / 4 * 4 : nch_all;
+    const int cb = SPLIT ? (int)blockIdx.y * cpp : 0;      // first chunk of this part
+    const int nch = SPLIT ? max(min(nch_all - cb, cpp), 0) : nch_all;  // chunks of this part
     const int nsa = TRI ? a.nblk : a.nchunks;               // activation scale blocks per row
 
     const int lrow = lane & 31, kgrp = lane >> 5;
@@ -578,10 +586,12 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
     // global loads of chunk c (c % 2 == H) into R
     auto prefetch = [&](auto HH, ChunkRegs<FMT> &R, int c) KQ_INLINE {
         constexpr int H = decltype(HH)::value;
-        const int sblk = c / CPS;
+        // (c counts this part's chunks; the global chunk is cb + c)
+        const int cg = cb + c;
+        const int sblk = cg / CPS;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            R.act[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (int)a_off[i], c * KCH, 0));
+            R.act[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (int)a_off[i], cg * KCH, 0));
         R.da = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_d, (int)d_off, sblk * M * 4, 0));
         const int wsoff = sblk * Fmt<FMT>::BB;
         if constexpr (Q4) {
@@ -1057,7 +1067,10 @@ __global__ __launch_bounds__(MNT) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int ml = 64 * wm + 32 * i + mfma32_row(r, lane);
-            if (full || (ml < mrows && n < N)) out[(orow0 + ml) * N + n] = acc_f[i][r];
+            if (full || (ml < mrows && n < N)) {
+                if constexpr (SPLIT) unsafeAtomicAdd(&out[(orow0 + ml) * N + n], acc_f[i][r]);
+                else out[(orow0 + ml) * N + n] = acc_f[i][r];
+            }
         }
     }
 }
@@ -1207,6 +1220,30 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
                            const uint16_t *alpha, float *out, int M, int N, int K,
                            hipStream_t stream);
 
+// K in two parts where the tiles cover at most half the CUs (one round
+// either way) and half of K outweighs the split's own cost: the zero fill
+// and two atomic adds per output, which the L2 takes at about 0.3 per ns,
+// modelled as M * N / 1536 in units of K (plus 256 for the second launch).
+// Paired runs, us, whole K / split: Q6_K 512 x 4096 x 14336 143 / 96; 512 x
+// 4096 x 4096 44.8 / 42.1; 128 x 14336 x 4096 46.5 / 41.0; 300 x 4000 x
+// 2048 25.9 / 23.7; base-3 9 x 4096 x 5248 42.7 / 28.7; the whole-K kernel
+// at half K (one part's share) on Q6_K 512 x 4096 x 14336: 76.
+static int64_t split_units(int M, int N, int K) { return K / 2 + 256 + (int64_t)M * N / 1536; }
+
+bool tile_split_choice(int fmt, int M, int N, int K) {
+    if (fmt != FMT_Q6K && fmt != FMT_TQ && fmt != FMT_TQ2) return false;
+    if (M <= 0 || N <= 0 || K < 1024) return false;
+    const int64_t tiles = ((int64_t)M + MBM - 1) / MBM * (((int64_t)N + MBN - 1) / MBN);
+    return 2 * tiles <= num_cus() && split_units(M, N, K) < K;
+}
+
+int64_t tile_units(int fmt, int M, int N, int K) {
+    if (tile_split_choice(fmt, M, N, K)) return split_units(M, N, K);
+    const int cus = num_cus();
+    const int64_t tiles = ((int64_t)M + MBM - 1) / MBM * (((int64_t)N + MBN - 1) / MBN);
+    return (tiles + cus - 1) / cus * K;
+}
+
 hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da,
                        const uint16_t *alpha, float *out, int M, int N, int K,
                        hipStream_t stream) {
@@ -1216,6 +1253,15 @@ hipError_t launch_gemm(int fmt, const void *W, const int8_t *qs, const float *da
     if (fmt == FMT_TQ && tq_tile_choice(M, N, K)) return launch_gemm_tq_tile(W, qs, da, out, M, N, K, stream);
     GemmArgs a = make_args(fmt, W, qs, da, alpha, out, M, N, K, MBM, MBN);
     const unsigned grid = (unsigned)(a.tiles_m * a.tiles_n);
+    if (tile_split_choice(fmt, M, N, K)) {
+        const hipError_t e = launch_zero_fill(out, (int64_t)M * N, stream);
+        if (e != hipSuccess) return e;
+        const dim3 g2(grid, 2);
+        if (fmt == FMT_Q6K) hipLaunchKernelGGL((gemm_kernel<FMT_Q6K, false, true>), g2, dim3(MNT), 0, stream, a);
+        else if (fmt == FMT_TQ2) hipLaunchKernelGGL((gemm_kernel<FMT_TQ2, false, true>), g2, dim3(MNT), 0, stream, a);
+        else hipLaunchKernelGGL((gemm_kernel<FMT_TQ, false, true>), g2, dim3(MNT), 0, stream, a);
+        return hipGetLastError();
+    }
     switch (fmt) {
         case FMT_Q6K:
             hipLaunchKernelGGL(gemm_kernel<FMT_Q6K>, dim3(grid), dim3(MNT), 0, stream, a);

@@ -1413,7 +1413,7 @@ static bool split_pays(int64_t tiles, int cus) {
     return r2 < 2 * r1;
 }
 int q4k_kernel_choice(int M, int N, int K) {
-    if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 &&
+    if (M <= q4w::mv::MAX_TOKENS && K % 2048 == 0 && K <= (1 << 20) &&
         q4w::mv::lds_bytes(mv_tokens(M), M, K, K / 256) <= MV_LDS_BUDGET)
         return Q4K_MATVEC;
     const int cus = num_cus();
@@ -1426,7 +1426,7 @@ int q4k_kernel_choice(int M, int N, int K) {
     // 19.9 at 64; K = 2048 and 8192 alike (8448-10240 rows: 5-25% faster).
     // At 8192 rows (one round) the other kernels win: 9.8 / 7.5 at 3 tokens,
     // 15.4 / 14.3 at 64.
-    if (M <= 64 && (N + 31) / 32 > cus) return Q4K_FEW_RING;
+    if (M <= 64 && ((int64_t)N + 31) / 32 > cus) return Q4K_FEW_RING;
     // Narrower weights: the four-wave split kernel up to 16 tokens while its
     // 32-row workgroups cover more than half the CUs, else the ring kernel
     // with K in 2, 4 or 8 parts (kq_gemm_ring.hip).  Paired runs, us, split
@@ -1438,12 +1438,18 @@ int q4k_kernel_choice(int M, int N, int K) {
     // tokens, the ring kernel in 64-token slices where the tile kernels
     // would leave most CUs idle (4096 x 14336 at 128 tokens: 33 against 77
     // us).
-    if (M <= 16 && 2 * ((N + 31) / 32) > cus) return Q4K_FEW_SPLIT;
+    if (M <= 16 && 2 * (((int64_t)N + 31) / 32) > cus) return Q4K_FEW_SPLIT;
     if (M <= 64 || ring_slices_pay(1, M, N, K)) return Q4K_RING_KP;
-    const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t tiles128 = (((int64_t)M + 127) / 128) * (((int64_t)N + 127) / 128);
     if (tiles128 > TILE64_MAX_TILES128) return Q4K_TILE128;
-    const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+    const int64_t tiles64 = (((int64_t)M + 63) / 64) * (((int64_t)N + 127) / 128);
     return split_pays(tiles64, cus) ? Q4K_TILE64_K2 : Q4K_TILE64;
+}
+
+hipError_t launch_zero_fill(float *out, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, n);
+    return hipGetLastError();
 }
 
 bool q4k_id_tile_ok(int N, int K) {

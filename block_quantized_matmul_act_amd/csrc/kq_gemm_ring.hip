@@ -644,7 +644,7 @@ static int64_t ring_plan(int M, int N, int K, int *parts) {
     int best = 2;
     int64_t best_cost = 0;
     for (int kp = 2; kp <= kmax; kp *= 2) {
-        const int64_t wgs = (N + 16 * (8 / kp) - 1) / (16 * (8 / kp)) * slices;
+        const int64_t wgs = ((int64_t)N + 16 * (8 / kp) - 1) / (16 * (8 / kp)) * slices;
         const int64_t cost = (wgs + cus - 1) / cus * (512 + K / kp);
         if (kp == 2 || cost < best_cost) {
             best = kp;
@@ -680,15 +680,16 @@ int ring_parts(int M, int N, int K) {
 bool ring_slices_pay(int fmt, int M, int N, int K) {
     if (M <= 64 || M > 512) return false;
     const int cus = num_cus();
-    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t tile_units = (tiles + cus - 1) / cus * K;
+    const int64_t tiles = (int64_t)((M + 127) / 128) * (((int64_t)N + 127) / 128);
+    // Q4_K's tile kernels take K whole; the others' split it where it pays
+    const int64_t tile_cost = fmt == rk::F_Q4K ? (tiles + cus - 1) / cus * K : tile_units(fmt, M, N, K);
     int kp;
     const int64_t ring_units = ring_plan(M, N, K, &kp);
     int num = 4, den = 5;  // two-bit ternary
     if (fmt == rk::F_Q4K) num = 6, den = 5;
     else if (fmt == rk::F_Q6K) num = 19, den = 20;
     else if (fmt == rk::F_TQ) num = 5, den = 6;
-    return ring_units * num < tile_units * den;
+    return ring_units * num < tile_cost * den;
 }
 
 // Shapes this kernel takes: Q6_K and ternary past the matrix-vector kernels,

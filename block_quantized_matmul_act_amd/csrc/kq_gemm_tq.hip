@@ -364,7 +364,7 @@ bool tq_tile_choice(int M, int N, int K) {
     // the digit-plane kernel's eight waves per tile win (200 x 4096 x 5120:
     // 43 against 48 us).
     if (M <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || gemv_choice(3, M, N, K)) return false;
-    const int64_t tiles = (int64_t)((M + tqt::BM - 1) / tqt::BM) * ((N + tqt::BN - 1) / tqt::BN);
+    const int64_t tiles = (((int64_t)M + tqt::BM - 1) / tqt::BM) * (((int64_t)N + tqt::BN - 1) / tqt::BN);
     return tiles >= num_cus() && tiles * (K / 256) <= INT32_MAX;
 }
 

@@ -430,7 +430,9 @@ static int gv_tokens(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 // 18.1 against 27.9 us at 5 tokens, 13.3 against 18.0 for this kernel at 4).
 bool gemv_choice(int fmt, int M, int N, int K) {
     (void)N;
-    if (M < 1 || M > 4) return false;
+    // (the staged activations cap K far below 2^20; the bound keeps the LDS
+    // arithmetic below in int range for any K the API accepts)
+    if (M < 1 || M > 4 || K > (1 << 20)) return false;
     if (fmt == 2) return K % 2048 == 0 && gv::lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     if (fmt == 3) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K) <= gv::LDS_BUDGET;
     if (fmt == 4) return K % 1024 == 0 && gv::tq_lds_bytes(gv_tokens(M), M, K, true) <= gv::LDS_BUDGET;

@@ -33,6 +33,16 @@ hipError_t launch_gemv(int fmt, const void *W, const int8_t *qs, const float *da
 // matrix-vector kernel nor the ring kernel (below) takes run on the
 // register-unpack tile kernel (kq_gemm_tq.hip).
 bool tq_tile_choice(int M, int N, int K);
+// The 128 x 128 tile kernel with K in two parts on the grid's second
+// dimension, each part adding into the zeroed output (Q6_K and ternary):
+// shapes with at most half as many tiles as CUs, K of at least 1024, and
+// half of K worth more than the zero fill and atomic adds.
+bool tile_split_choice(int fmt, int M, int N, int K);
+// Modelled cost of the 128 x 128 tile route (split or whole), in units of K:
+// rounds x K, or the split's half K plus its zero fill and atomics.
+int64_t tile_units(int fmt, int M, int N, int K);
+// out[0, n) = 0, as a kernel (capturable in a graph)
+hipError_t launch_zero_fill(float *out, int64_t n, hipStream_t stream);
 hipError_t launch_gemm_tq_tile(const void *W, const int8_t *qs, const float *da, float *out, int M, int N,
                                int K, hipStream_t stream);
 

@@ -74,6 +74,11 @@ bool ring_choice(int fmt, int M, int N, int K) {
     return fmt >= 2 && fmt <= 4 && M >= 1 && M <= 64 && K >= 256 && K % 256 == 0 && !gemv_choice(fmt, M, N, K);
 }
 int num_cus() { return 256; }
+bool tile_split_choice(int fmt, int M, int N, int K) {
+    return fmt >= 2 && fmt <= 4 && M > 0 && K >= 1024 &&
+           2 * (((int64_t)M + 127) / 128) * (((int64_t)N + 127) / 128) <= 256 &&
+           K / 2 + 256 + (int64_t)M * N / 1536 < K;
+}
 int q4k_kernel_choice(int M, int, int) {
     return M <= 2 ? Q4K_MATVEC : M <= 16 ? Q4K_FEW_SPLIT : M <= 64 ? Q4K_RING_KP : Q4K_TILE128;
 }

@@ -199,12 +199,18 @@ def test_variants_and_counters(kq):
     assert q6(64, 4096, 14336) == "gemm_q6_k_ring"
     # 65 .. 512 tokens: the ring kernel in 64-token slices where the 128 x
     # 128 tile kernels leave most CUs idle (narrow weights, long K)
-    for M in (65, 128, 200, 384):
+    for M in (65, 128, 200, 256):
         assert q6(M, 4096, 14336) == "gemm_q6_k_ring"
-    assert q6(512, 4096, 14336) == "gemm_q6_k_128x128"  # 128 tiles over 14336 of K
-    assert q6(513, 1024, 4096) == "gemm_q6_k_128x128"   # past 512 tokens
+    # ... and the tile kernel with K in two parts where its tiles cover at
+    # most half the CUs and the ring kernel would need more rounds
+    assert q6(512, 4096, 14336) == "gemm_q6_k_128x128_k2"  # 128 tiles over 14336 of K
+    assert q6(513, 1024, 4096) == "gemm_q6_k_128x128_k2"   # past 512 tokens (40 tiles)
+    assert q6(1024, 4096, 14336) == "gemm_q6_k_128x128"    # 256 tiles
     assert q6(512, 1024, 4096) == "gemm_q6_k_ring"
-    assert q6(128, 14336, 4096) == "gemm_q6_k_128x128"  # 112 tiles already
+    assert q6(128, 14336, 4096) == "gemm_q6_k_128x128_k2"  # 112 tiles
+    assert q6(256, 14336, 4096) == "gemm_q6_k_128x128"     # 224 tiles
+    assert q6(300, 4000, 512) == "gemm_q6_k_128x128"       # K under 1024
+    assert q6(300, 4000, 2048) == "gemm_q6_k_128x128"      # half of K under the split's cost
     assert q6(130, 72, 512) == "gemm_q6_k_128x128"      # one tile, short K
     assert q4(128, 4096, 14336) == "gemm_q4_k_ring_kp"
     assert q4(256, 4096, 14336) == "gemm_q4_k_ring_kp"
@@ -225,9 +231,11 @@ def test_variants_and_counters(kq):
     assert tq(64, 17408, 5120) == "gemm_tq_ring"
     assert tq(1, 17408, 5120 + 256) == "gemm_tq_ring"   # K not a multiple of 1024
     assert tq(9, 17408, 5120 + 128) == "gemm_tq_128x128"
-    for M in (65, 256, 512):
+    for M in (65, 256):
         assert tq(M, 4096, 14336) == "gemm_tq_ring"
-    assert tq(128, 17408, 5120) != "gemm_tq_ring"
+    assert tq(128, 17408, 5120) == "gemm_tq_128x128"     # 136 tiles: whole K
+    assert tq(512, 4096, 14336) == "gemm_tq_128x128_k2"
+    assert tq(9, 4096, 5120 + 128) == "gemm_tq_128x128_k2"
     # two-bit ternary: the matrix-vector kernel up to 4 tokens (K a multiple
     # of 1024), the K-split ring kernel up to 64 (K a multiple of 256), the
     # tile kernel otherwise
@@ -238,10 +246,13 @@ def test_variants_and_counters(kq):
         assert tq2(M, 4096, 5120) == "gemm_tq2_ring"
     assert tq2(1, 4096, 5120 + 256) == "gemm_tq2_ring"
     assert tq2(65, 4096, 5120) == "gemm_tq2_ring"
-    assert tq2(512, 4096, 14336) == "gemm_tq2_ring"
+    assert tq2(256, 4096, 14336) == "gemm_tq2_ring"
+    assert tq2(512, 4096, 14336) == "gemm_tq2_128x128_k2"
     assert tq2(128, 17408, 5120) == "gemm_tq2_128x128"
     assert tq2(2048, 4096, 5120) == "gemm_tq2_128x128"
-    assert tq2(8, 4096, 5120 + 128) == "gemm_tq2_128x128"
+    assert tq2(8, 4096, 5120 + 128) == "gemm_tq2_128x128_k2"  # 32 tiles: K in two parts
+    assert tq2(8, 16384, 5120 + 128) == "gemm_tq2_128x128_k2"  # 128 tiles: two parts fill the CUs
+    assert tq2(8, 16512, 5120 + 128) == "gemm_tq2_128x128"     # 129 tiles
     assert kq.kq_select_variant(0, 1, 1, 256) == kq.KQ_ERR_FMT
     assert kq.kq_select_variant(kq.KQ_Q4_K, 1, 1, 100) == kq.KQ_ERR_SHAPE
 

@@ -231,6 +231,9 @@ Q6K_CASES = [
     ("gemm_q6_k_ring", 128, 72, 2048),
     ("gemm_q6_k_ring", 150, 200, 2048),
     ("gemm_q6_k_ring", 300, 72, 2048),
+    # the tile kernel with K in two parts (4 / 4 and 8 / 2 chunks of 128)
+    ("gemm_q6_k_128x128_k2", 600, 130, 1024),
+    ("gemm_q6_k_128x128_k2", 600, 130, 1280),
 ]
 
 
@@ -275,7 +278,7 @@ TQ_CASES = [
     ("gemm_tq_ring", TQ, 16, 14344, 512),
     ("gemm_tq_ring", TQ, 150, 200, 2048),  # three 64-token slices, ragged
     ("gemm_tq2_128x128", TQ2, 67, 90, 640),
-    ("gemm_tq2_128x128", TQ2, 5, 40, 1152),
+    ("gemm_tq2_128x128_k2", TQ2, 5, 40, 1152),
     # the K-split ring kernel: 16-, 32- and 64-row token tiles; eight K-parts
     # (40 and 72 rows), four (4104 rows; 64 tokens' 200), two (14344 rows)
     ("gemm_tq2_matvec", TQ2, 1, 40, 1024),
@@ -286,6 +289,9 @@ TQ_CASES = [
     ("gemm_tq2_ring", TQ2, 64, 200, 512),
     ("gemm_tq2_ring", TQ2, 16, 14344, 512),
     ("gemm_tq2_ring", TQ2, 150, 200, 2048),
+    # the tile kernel with K in two parts (8 / 1 chunks of 128)
+    ("gemm_tq_128x128_k2", TQ, 600, 130, 1152),
+    ("gemm_tq2_128x128_k2", TQ2, 600, 130, 1152),
 ]
 
 

@@ -212,7 +212,9 @@ def finite_weights(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
 # (fmt, K, variant, token rows per launch, weight rows); the 128 x 128 Q4_K
 # kernel takes shapes of more than 256 such tiles, hence its 2100 weight rows,
 # the 4-wave 64 x 128 build more than 256 of its own (1100 rows), and the
-# K-split ring kernel more than 256 32-row pieces (11016 rows, ragged)
+# K-split ring kernel more than 256 32-row pieces (11016 rows, ragged); the
+# 128 x 128 tile kernel of the other formats takes K in two parts where its
+# tiles cover at most half the CUs (72 rows) and whole at 4200 rows
 IDENTITY_CASES = [
     (Q4_K, 2048, "gemm_q4_k_matvec", 2, 72),
     (Q4_K, 2048, "gemm_q4_k_ring_kp", 64, 72),
@@ -226,17 +228,20 @@ IDENTITY_CASES = [
     (Q6_K, 2048, "gemm_q6_k_matvec", 4, 72),
     (Q6_K, 2048, "gemm_q6_k_ring", 16, 72),
     (Q6_K, 2304, "gemm_q6_k_ring", 64, 4104),
-    (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 72),
+    (Q6_K, 2048, "gemm_q6_k_128x128_k2", 2048, 72),
+    (Q6_K, 2048, "gemm_q6_k_128x128", 2048, 4200),
     (TQ, 1024, "gemm_tq_matvec", 4, 72),
-    (TQ, 1152, "gemm_tq_128x128", 1152, 72),
+    (TQ, 1152, "gemm_tq_128x128_k2", 1152, 72),
+    (TQ, 1152, "gemm_tq_128x128", 1152, 4200),
     (TQ, 1024, "gemm_tq_ring", 16, 72),
     (TQ, 1280, "gemm_tq_ring", 64, 4104),
     (TQ, 1024, "gemm_tq_128x128_reg", 1024, 4200),
-    (TQ2, 1152, "gemm_tq2_128x128", 8, 72),
+    (TQ2, 1152, "gemm_tq2_128x128_k2", 8, 72),
     (TQ2, 1024, "gemm_tq2_matvec", 4, 72),
     (TQ2, 1024, "gemm_tq2_ring", 8, 72),
     (TQ2, 1280, "gemm_tq2_ring", 64, 4104),
-    (TQ2, 1024, "gemm_tq2_128x128", 1024, 72),
+    (TQ2, 1024, "gemm_tq2_128x128_k2", 1024, 72),
+    (TQ2, 1024, "gemm_tq2_128x128", 1024, 4200),
 ]
 
 

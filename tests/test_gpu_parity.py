@@ -401,6 +401,52 @@ def test_tq2_few_token_ring(kq):
                 assert kq.kq_dispatch_count(v) == before + 1
 
 
+SPLIT_TILE = {Q6_K: "gemm_q6_k_128x128_k2", TQ: "gemm_tq_128x128_k2", TQ2: "gemm_tq2_128x128_k2"}
+SPLIT_SHAPES = {
+    # (M, N, K): chunks of 128 values per part in the comments
+    Q6_K: ((300, 4000, 4096),    # 16 / 16
+           (300, 4000, 2304),    # 12 / 6
+           (65, 4100, 1280)),    # 8 / 2
+    TQ: ((300, 4000, 4096), (129, 2000, 1152),   # 8 / 1
+         (70, 4000, 5248),                        # 24 / 17
+         (5, 4096, 5248)),                        # a few tokens, K not a multiple of 256
+}
+SPLIT_SHAPES[TQ2] = SPLIT_SHAPES[TQ]
+
+
+@pytest.mark.parametrize("fmt", sorted(SPLIT_TILE))
+def test_tile_split_k(kq, fmt):
+    """The 128 x 128 tile kernel with K in two parts (grid row 0 and 1),
+    each adding into the zeroed output, on shapes whose tiles cover at most
+    half the CUs: full products against the oracle (the output starts as NaN,
+    so a missed zero fill fails) with parts of equal and unequal length, a
+    part of one chunk, ragged M and N; then sampled columns of 512 x 4096 x
+    14336; and the same product twice, bit for bit (two addends onto zero
+    commute in fp32)."""
+    name = SPLIT_TILE[fmt]
+    for M, N, K in SPLIT_SHAPES[fmt]:
+        v = kq.kq_select_variant(fmt, M, N, K)
+        assert kq.kq_variant_name(v) == name, (M, N, K)
+        W = datagen.make_weights(fmt, N, K, 9500 + N + K + fmt)
+        x = datagen.draw_activations(M, K, 9600 + K + fmt)
+        say(f"{name} M={M} N={N} K={K}")
+        before = kq.kq_dispatch_count(v)
+        gemm_vs_oracle(kq, fmt, W, x, M, N, K, what=f"{name} M={M} N={N} K={K}")
+        assert kq.kq_dispatch_count(v) == before + 1
+    M, N, K = 512, 4096, 14336
+    assert kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)) == name
+    W = datagen.make_weights(fmt, N, K, 9700 + fmt)
+    x = datagen.draw_activations(M, K, 9800 + fmt)
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], np.random.default_rng(9900).choice(N, 48, replace=False)]))
+    say(f"{name} M={M} N={N} K={K}, {len(rows)} sampled columns")
+    gemm_vs_oracle(kq, fmt, W, x, M, N, K, rows=rows, what=f"{name} 512 x 4096 x 14336")
+    a_q8 = kq.quantize_act(dev(x), kq.kq_act_fmt_for(fmt))
+    Wd = dev(W)
+    o1 = run_gemm(kq, fmt, Wd, a_q8, M, N, K)
+    o2 = run_gemm(kq, fmt, Wd, a_q8, M, N, K)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), f"{name}: two runs differ"
+
+
 SLICE_RING = {Q4_K: "gemm_q4_k_ring_kp", Q6_K: "gemm_q6_k_ring", TQ: "gemm_tq_ring", TQ2: "gemm_tq2_ring"}
 
 
