@@ -1357,12 +1357,19 @@ __global__ __launch_bounds__(512, 1) void gemm_q4k_ring_kernel(Args a) {
     }
 }
 
-// out[0, n) = 0 (the product over an empty K); a kernel rather than a memset
-// so that the call stays capturable in a graph
+// out[0, n) = 0 (the product over an empty K, or before the two K-parts of
+// the tile kernel add into it); a kernel rather than a memset so that the
+// call stays capturable in a graph.  out is 16-byte aligned: four floats per
+// lane, the last lane's group cut at n.
 __global__ __launch_bounds__(256) void zero_fill_kernel(float *out, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) out[i] = 0.0f;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i + 4 <= n) {
+        *reinterpret_cast<v4f *>(out + i) = v4f{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t j = i; j < n; ++j) out[j] = 0.0f;
+    }
 }
+static unsigned zero_fill_blocks(int64_t n) { return (unsigned)((n + 1023) / 1024); }
 
 }  // namespace q4w
 
@@ -1448,7 +1455,7 @@ int q4k_kernel_choice(int M, int N, int K) {
 
 hipError_t launch_zero_fill(float *out, int64_t n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, n);
+    hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3(q4w::zero_fill_blocks(n)), dim3(256), 0, stream, out, n);
     return hipGetLastError();
 }
 
@@ -1465,7 +1472,7 @@ hipError_t launch_gemm_q4k_id(const void *W, int n_experts, int64_t expert_bytes
     const int cus = num_cus();
     if (K == 0) {
         const int64_t n = (int64_t)R * N;
-        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3(q4w::zero_fill_blocks(n)), dim3(256), 0,
                            stream, out, n);
         return hipGetLastError();
     }
@@ -1499,7 +1506,7 @@ hipError_t launch_gemm_q4k(const void *W, const int8_t *qs, const float *da,
     const int cus = num_cus();
     if (K == 0) {
         const int64_t n = (int64_t)M * N;
-        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(q4w::zero_fill_kernel, dim3(q4w::zero_fill_blocks(n)), dim3(256), 0,
                            stream, out, n);
         return hipGetLastError();
     }

@@ -78,6 +78,9 @@ WORKLOADS = {
     "ffn_down_q6k_16": Workload("ffn_down_q6k_16", Q6_K, 16, 4096, 14336, 1004,
                                 "plain", "Q6_K x Q8_K FFN down, 16 tokens (a small decode batch; "
                                 "first 16 token rows of the 2048-token draw)"),
+    "ffn_down_q6k_512": Workload("ffn_down_q6k_512", Q6_K, 512, 4096, 14336, 1004,
+                                 "plain", "Q6_K x Q8_K FFN down, 512 tokens (a prefill chunk; "
+                                 "first 512 token rows of the 2048-token draw)"),
     "tern_5120_1": Workload("tern_5120_1", TQ, 1, 17408, 5120, 1005,
                             "plain", "ternary x Q8_128, one token (decode; first token row "
                             "of the 2048-token draw), 17408x5120"),
@@ -327,7 +330,7 @@ def make_weights(fmt: int, N: int, K: int, seed: int, dist: str = "plain") -> np
 
 # token-prefix workloads: their activations are the first rows of the 2048-token draw
 _PREFIX_OF_2048 = ("ffn_up_q4k_2048", "ffn_up_q4k_64", "ffn_up_q4k_1", "ffn_down_q6k_1", "ffn_down_q6k_16",
-                   "tern_5120_1")
+                   "ffn_down_q6k_512", "tern_5120_1")
 
 
 def make_workload(wl: Workload | str, n_rows: int | None = None, m_rows: int | None = None):

@@ -222,7 +222,7 @@ def test_shape_sweep(kq, fmt):
 
 
 @pytest.mark.parametrize("name", ["proj_q4k_4096", "ffn_up_q4k_1", "ffn_up_q4k_64", "ffn_up_q4k_2048",
-                                  "ffn_down_q6k_1", "ffn_down_q6k_16", "tern_5120_1",
+                                  "ffn_down_q6k_1", "ffn_down_q6k_16", "ffn_down_q6k_512", "tern_5120_1",
                                   "ffn_down_q6k_2048", "tern_5120_2048"])
 def test_workload_full_size_sampled(kq, workloads, name):
     """Full-size problem in the benchmarked launch; the oracle checks a sample
@@ -406,10 +406,10 @@ SPLIT_SHAPES = {
     # (M, N, K): chunks of 128 values per part in the comments
     Q6_K: ((300, 4000, 4096),    # 16 / 16
            (300, 4000, 2304),    # 12 / 6
-           (65, 4100, 1280)),    # 8 / 2
+           (65, 4099, 1280)),    # 8 / 2; an output count that is not a multiple of 4
     TQ: ((300, 4000, 4096), (129, 2000, 1152),   # 8 / 1
          (70, 4000, 5248),                        # 24 / 17
-         (5, 4096, 5248)),                        # a few tokens, K not a multiple of 256
+         (5, 4095, 5248)),                        # a few tokens, K not a multiple of 256
 }
 SPLIT_SHAPES[TQ2] = SPLIT_SHAPES[TQ]
 
