@@ -152,7 +152,12 @@ int kq_quantize_act(int act_fmt, const float *x, int64_t M, int64_t K, void *a_q
  * the tile GEMM of vllm.cpp PR 3036 (per-sub-block int8 dot products with the
  * Q4_K/Q6_K scales and mins folded in) and the PTQ1_0 MMQ path of llama.cpp
  * PR 214.  The fp32 result agrees with the exact product of the dequantized
- * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element.  The kernels
+ * operands to within 1e-4 * sum_k |W^ A^| + 1e-6 per element, and the same
+ * call on the same inputs gives the same bits (where a product runs K in two
+ * parts, each adds into out, zeroed first, and two addends onto zero round
+ * alike in either order; out is written in full whatever it held).  Calls
+ * on one stream run in order; out must not be read or written by other work
+ * until the call completes.  The kernels
  * address every operand with 32-bit byte offsets: shapes where the weight
  * tensor plus 256 rows, or an activation section (qs, d, alpha) or the
  * output plus 128 (scales: 256) rows, reaches 2^31 bytes are declined with
