@@ -75,12 +75,13 @@ WEIGHT_CASES = [
     (Q4_K, 4096, (1, 40, 200)),     # matrix-vector, few-token, 128 x 128
     (Q4_K, 131072, (100,)),         # 64 x 128 (226 column tiles)
     (Q6_K, 4096, (1, 40)),          # matrix-vector, 128 x 128 tile
+    (Q6_K, 589824, (128, 200)),     # ring kernel in 64-token slices, tile kernel with K in two parts
     (TQ, 5120, (1, 40)),            # matrix-vector, 128 x 128 tile
     (TQ2, 5120, (1, 40)),           # 128 x 128 tile
 ]
 
 
-@pytest.mark.parametrize("fmt,K,Ms", WEIGHT_CASES, ids=["q4_k", "q4_k_long_k", "q6_k", "tq", "tq2"])
+@pytest.mark.parametrize("fmt,K,Ms", WEIGHT_CASES, ids=["q4_k", "q4_k_long_k", "q6_k", "q6_k_long_k", "tq", "tq2"])
 def test_weights_just_below_2gib(kq, fmt, K, Ms):
     rowbytes = (K // QK[fmt]) * BB[fmt]
     N = LIMIT // rowbytes - 256           # largest N with (N + 256) * rowbytes < 2^31
