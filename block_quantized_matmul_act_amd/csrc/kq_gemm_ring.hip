@@ -114,13 +114,15 @@ struct Fmt<F_TQ2> {
     __device__ static int piece(int s, int kg) { return 4 * s + kg; }
 };
 
-template <int F, int TM, int KP>
+template <int F, int TM, int KP, int NW = 8>
 struct Cfg {
     static_assert(TM == 16 || TM == 32 || TM == 64, "16, 32 or 64 token rows");
     static_assert(KP == 2 || KP == 4 || KP == 8, "two, four or eight K-parts");
+    static_assert(NW == 8 || NW == 4, "eight or four waves");
     using FM = Fmt<F>;
     static constexpr int MT = TM / 16;            // 16-row m-tiles
-    static constexpr int NS = 8 / KP;             // 16-row strips per workgroup
+    static constexpr int NS = NW / KP;            // 16-row strips per workgroup
+    static_assert(NS >= 1, "a strip per K-part at least");
     static constexpr int ROWS = 16 * NS;          // weight rows per workgroup
     static constexpr int ACT = TM * ROW;          // values of one K-part: [row][256], swizzled
     // Q4_K min-term operands of one K-part: [hi, lo][TM][16] in 1 KiB copies
@@ -178,9 +180,9 @@ struct WRaw<F_TQ2> {
     uint32_t dd[2];       // per block: d
 };
 
-template <int F, int TM, int KP>
-__global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
-    using C = Cfg<F, TM, KP>;
+template <int F, int TM, int KP, int NW = 8>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(Args a) {
+    using C = Cfg<F, TM, KP, NW>;
     using FM = Fmt<F>;
     constexpr int MT = C::MT, NS = C::NS, NBLK = FM::NBLK, NDIG = FM::NDIG;
     constexpr int KSB = 4 / NBLK;  // K-steps per scale block
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void gemm_ring_kernel(Args a) {
     const auto rs_nul = __builtin_amdgcn_make_buffer_rsrc((void *)a.W, (short)0, 0, RSRC_FLAGS);
     int8_t *const zero = s_lds + C::S * C::SLOT;
     if constexpr (F == F_Q4K) {
-        for (int i = tid; i < 256; i += 512) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
+        for (int i = tid; i < 256; i += 64 * NW) reinterpret_cast<uint32_t *>(zero)[i] = 0u;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
@@ -702,11 +704,23 @@ bool ring_choice(int fmt, int M, int N, int K) {
     return !gemv_choice(fmt, M, N, K);
 }
 
-template <int F, int TM, int KP>
+template <int F, int TM, int KP, int NW = 8>
 static void launch_rk(const rk::Args &a, hipStream_t stream) {
-    constexpr int R = rk::Cfg<F, TM, KP>::ROWS;
-    hipLaunchKernelGGL((rk::gemm_ring_kernel<F, TM, KP>),
-                       dim3((unsigned)((a.N + R - 1) / R), (unsigned)((a.M + TM - 1) / TM)), dim3(512), 0, stream, a);
+    constexpr int R = rk::Cfg<F, TM, KP, NW>::ROWS;
+    hipLaunchKernelGGL((rk::gemm_ring_kernel<F, TM, KP, NW>),
+                       dim3((unsigned)((a.N + R - 1) / R), (unsigned)((a.M + TM - 1) / TM)), dim3(64 * NW), 0,
+                       stream, a);
+}
+
+// Four-wave workgroups (one strip per K-part) for 64-row token tiles in four
+// K-parts where the eight-wave ones would leave CUs idle and the four-wave
+// ones take one round: twice the workgroups, each CU one of them.
+static bool ring_four_waves(int M, int N, int kp) {
+    if (M <= 32 || kp != 4) return false;
+    const int64_t slices = M > 64 ? (M + 63) / 64 : 1;
+    const int64_t wgs8 = ((int64_t)N + 31) / 32 * slices, wgs4 = ((int64_t)N + 15) / 16 * slices;
+    const int cus = num_cus();
+    return wgs8 < cus && wgs4 <= cus;
 }
 
 template <int F>
@@ -721,6 +735,7 @@ static void launch_rk_fmt(const rk::Args &a, int kp, hipStream_t stream) {
         else launch_rk<F, 32, 8>(a, stream);
     } else {
         if (kp == 2) launch_rk<F, 64, 2>(a, stream);
+        else if (ring_four_waves(a.M, a.N, kp)) launch_rk<F, 64, 4, 4>(a, stream);
         else launch_rk<F, 64, 4>(a, stream);
     }
 }
