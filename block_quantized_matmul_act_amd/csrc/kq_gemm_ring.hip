@@ -8,10 +8,12 @@
 // rows are 32 tiles whatever the token count.  This kernel takes all tokens
 // (a 16-, 32- or 64-row token tile, TM) in one workgroup and splits the
 // weights over workgroups by rows and over waves by rows and K:
-//   * A workgroup of 8 waves owns 16 * (8 / KP) weight rows as 16-row strips;
-//     the K-chunks of 256 values are cut into KP contiguous K-parts (KP = 2, 4
-//     or 8), and wave w takes strip w % (8 / KP) over K-part w / (8 / KP).
-//     Narrow weights take more K-parts so that the grid still covers the CUs.
+//   * A workgroup of NW = 8 waves owns 16 * (NW / KP) weight rows as 16-row
+//     strips; the K-chunks of 256 values are cut into KP contiguous K-parts
+//     (KP = 2, 4 or 8), and wave w takes strip w % (NW / KP) over K-part
+//     w / (NW / KP).  Narrow weights take more K-parts so that the grid still
+//     covers the CUs; where the LDS of 64 token rows stops at four K-parts, a
+//     four-wave build (NW = 4, one strip per K-part) doubles the workgroups.
 //   * Step x multiplies chunk pT + x of every K-part p (T = ceil(chunks /
 //     KP)).  A step's activations (values and scales of every K-part, all
 //     token rows) are copied global -> LDS into a ring of L + 1 slots, L
