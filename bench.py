@@ -75,8 +75,9 @@ GEMM_SOURCES = {
 
 # the other configurations, reported beside the main one in the same line:
 # the 64-token case of the same FFN projection (bound by the weight stream),
-# the 512-token projection, the Q6_K down projection, the ternary projection
-SIDE_WORKLOADS = ("ffn_up_q4k_64", "proj_q4k_4096", "ffn_down_q6k_2048", "tern_5120_2048")
+# the 512-token projection, the Q6_K down projection at 2048 and at 512 tokens
+# (a prefill chunk, K in two parts), the ternary projection
+SIDE_WORKLOADS = ("ffn_up_q4k_64", "proj_q4k_4096", "ffn_down_q6k_2048", "ffn_down_q6k_512", "tern_5120_2048")
 
 
 def log(*a):
