@@ -29,6 +29,10 @@
  *     global state is a set of atomic per-variant dispatch counters and a
  *     per-device cache of the compute-unit count (atomic; it sizes the
  *     persistent grids).
+ *   - Every launch goes to the caller's stream and the library records no
+ *     memset (outputs that must start at zero are cleared by a kernel), so
+ *     kq_quantize_act, kq_gemm and kq_gemm_id can be captured in a HIP graph;
+ *     dispatch counters count the capture, not the replays.
  *
  * Data layouts (this library's own; the pages fix only the block sizes:
  * 292 bytes per 256 activations for BlockQ8_K in vllm.cpp PR 3036, a 28-byte

@@ -447,6 +447,54 @@ def test_tile_split_k(kq, fmt):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), f"{name}: two runs differ"
 
 
+GRAPH_CASES = [
+    (Q4_K, 300, 11000, 512, "gemm_q4_k_128x128"),
+    (Q4_K, 64, 11008, 512, "gemm_q4_k_m64_ring"),
+    (Q4_K, 2, 1000, 2048, "gemm_q4_k_matvec"),
+    (Q4_K, 40, 1000, 2048, "gemm_q4_k_ring_kp"),      # four-wave build
+    (Q6_K, 300, 4000, 4096, "gemm_q6_k_128x128_k2"),  # zero fill, then two parts adding
+    (Q6_K, 128, 1024, 4096, "gemm_q6_k_ring"),         # two 64-token slices
+    (TQ, 1, 1000, 2048, "gemm_tq_matvec"),
+    (TQ2, 600, 130, 1152, "gemm_tq2_128x128_k2"),
+]
+
+
+def test_graph_capture_replays(kq):
+    """Quantize + product captured in one HIP graph (the library records no
+    memset and allocates nothing), replayed three times with eager work
+    between the replays (the buffers refilled, the device synchronized): every
+    replay equals the eager call bit for bit, on each kernel family,
+    including the two-part tile kernel with its zero fill."""
+    import torch
+    for fmt, M, N, K, name in GRAPH_CASES:
+        assert kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K)) == name, (fmt, M, N, K)
+        act = kq.kq_act_fmt_for(fmt)
+        W = dev(datagen.make_weights(fmt, N, K, 9950 + fmt + M))
+        x = dev(datagen.draw_activations(M, K, 9960 + fmt + M))
+        a_q8 = torch.empty(kq.kq_act_bytes(act, M, K), dtype=torch.uint8, device=DEV)
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        kq.kq_quantize_act(act, x, M, K, a_q8)
+        kq.kq_gemm(fmt, W, a_q8, M, N, K, out)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        say(f"graph {name} M={M} N={N} K={K}")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            kq.kq_quantize_act(act, x, M, K, a_q8)
+            kq.kq_gemm(fmt, W, a_q8, M, N, K, out)
+        torch.cuda.synchronize()
+        for r in range(3):
+            out.fill_(float("nan"))
+            a_q8.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"{name}: replay {r} differs"
+        del g
+
+
 SLICE_RING = {Q4_K: "gemm_q4_k_ring_kp", Q6_K: "gemm_q6_k_ring", TQ: "gemm_tq_ring", TQ2: "gemm_tq2_ring"}
 
 
