@@ -447,6 +447,33 @@ def test_tile_split_k(kq, fmt):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), f"{name}: two runs differ"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_random_shapes_every_route(kq, fmt):
+    """Seeded random shapes across the routing boundaries (mat-vec, ring
+    kernels with and without slices and in both wave counts, tile kernels
+    whole and with K in two parts): 16 products per format with M in 1..700,
+    N in 1..8000 and K up to 8192, the oracle's work bounded, each against
+    the oracle in full; the variants reached are printed."""
+    rng = np.random.default_rng(4242 + fmt)
+    qk = 256 if fmt in (Q4_K, Q6_K) else 128
+    seen = {}
+    done = 0
+    while done < 16:
+        M = int(rng.choice([rng.integers(1, 5), rng.integers(5, 65), rng.integers(65, 700)]))
+        N = int(rng.integers(1, 8000))
+        K = qk * int(rng.integers(1, 8192 // qk + 1))
+        if M * N * K > 2e9:
+            continue
+        name = kq.kq_variant_name(kq.kq_select_variant(fmt, M, N, K))
+        W = datagen.make_weights(fmt, N, K, 7700 + 31 * done + fmt)
+        x = datagen.draw_activations(M, K, 7800 + 31 * done + fmt)
+        say(f"random {name} M={M} N={N} K={K}")
+        gemm_vs_oracle(kq, fmt, W, x, M, N, K, what=f"random {name} M={M} N={N} K={K}")
+        seen[name] = seen.get(name, 0) + 1
+        done += 1
+    say(f"  variants reached: {seen}")
+
+
 GRAPH_CASES = [
     (Q4_K, 300, 11000, 512, "gemm_q4_k_128x128"),
     (Q4_K, 64, 11008, 512, "gemm_q4_k_m64_ring"),
